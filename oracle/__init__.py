@@ -1,0 +1,176 @@
+"""fp64 CPU oracle for paged decode attention (test infrastructure).
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may
+import this package. The HIP library never calls it and shares no code with it. The
+arithmetic lives in ``oracle.c`` (plain C, fp64, OpenMP over rows); this module only builds
+that file with gcc and marshals numpy arrays into it.
+
+Every function takes the problem as the dict that ``workloads.generate`` returns (numpy
+arrays: q, k_pages, v_pages, k_scales, v_scales, page_table, kv_len; ints: q_per_seq; float:
+sm_scale). Strides are read from the arrays themselves, in elements.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+class OracleProblem(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("q_per_seq", ctypes.c_int32),
+        ("num_qo_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
+        ("kv_int8", ctypes.c_int32), ("pad0", ctypes.c_int32),
+        ("sm_scale", ctypes.c_double),
+        ("q", ctypes.c_void_p), ("q_tok_stride", ctypes.c_int64), ("q_head_stride", ctypes.c_int64),
+        ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+        ("page_stride", ctypes.c_int64), ("tok_stride", ctypes.c_int64), ("head_stride", ctypes.c_int64),
+        ("s_page_stride", ctypes.c_int64), ("s_tok_stride", ctypes.c_int64), ("s_head_stride", ctypes.c_int64),
+        ("table", ctypes.c_void_p), ("table_stride", ctypes.c_int64),
+        ("kv_len", ctypes.c_void_p),
+    ]
+
+
+def build(out_path: str = _LIB_PATH, mutant: int = 0) -> str:
+    """Compile oracle.c with gcc (-O2 -fopenmp, no fast-math). mutant > 0 plants the
+    numbered deliberate mistake (used only to show that the pins catch it)."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", "-Wall",
+           f"-DORACLE_MUTANT={int(mutant)}", _SRC, "-o", out_path + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out_path + ".tmp", out_path)
+    return out_path
+
+
+def load(path: str | None = None):
+    """Load the oracle library (building it if it is missing)."""
+    global _lib
+    if path is None and _lib is not None:
+        return _lib
+    p = path or _LIB_PATH
+    if not os.path.exists(p) or (path is None and os.path.getmtime(p) < os.path.getmtime(_SRC)):
+        build(p)
+    lib = ctypes.CDLL(p)
+    P = ctypes.POINTER(OracleProblem)
+    lib.oracle_decode.argtypes = [P, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                  ctypes.c_void_p, ctypes.c_int]
+    lib.oracle_decode.restype = ctypes.c_int
+    lib.oracle_decode_blocked.argtypes = [P, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                          ctypes.c_void_p, ctypes.c_void_p]
+    lib.oracle_decode_blocked.restype = ctypes.c_int
+    lib.oracle_gather.argtypes = [P, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                  ctypes.c_void_p, ctypes.c_void_p]
+    lib.oracle_gather.restype = ctypes.c_int
+    lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
+    lib.oracle_half_to_double.restype = ctypes.c_double
+    lib.oracle_num_threads.restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _problem(prob: dict):
+    """Build the ctypes problem struct; returns (struct, keep-alive list)."""
+    q, k, v = prob["q"], prob["k_pages"], prob["v_pages"]
+    int8 = k.dtype == np.int8
+    assert q.dtype == np.float16 and q.ndim == 3 and q.strides[2] == 2
+    assert k.shape == v.shape and k.strides == v.strides and k.ndim == 4
+    table = np.ascontiguousarray(prob["page_table"], dtype=np.int32)
+    kv_len = np.ascontiguousarray(prob["kv_len"], dtype=np.int32)
+    es = k.itemsize
+    B = kv_len.shape[0]
+    T = int(prob["q_per_seq"])
+    s = OracleProblem()
+    s.batch, s.q_per_seq = B, T
+    s.num_qo_heads, s.num_kv_heads, s.head_dim = q.shape[1], k.shape[2], k.shape[3]
+    s.page_size = k.shape[1]
+    s.kv_int8 = int(int8)
+    s.sm_scale = float(np.float32(prob["sm_scale"]))
+    s.q = q.ctypes.data
+    s.q_tok_stride, s.q_head_stride = q.strides[0] // 2, q.strides[1] // 2
+    s.k, s.v = k.ctypes.data, v.ctypes.data
+    s.page_stride, s.tok_stride, s.head_stride = (k.strides[0] // es, k.strides[1] // es,
+                                                  k.strides[2] // es)
+    keep = [q, k, v, table, kv_len]
+    if int8:
+        ks, vs = prob["k_scales"], prob["v_scales"]
+        assert ks.dtype == np.float16 and ks.strides == vs.strides
+        s.k_scale, s.v_scale = ks.ctypes.data, vs.ctypes.data
+        s.s_page_stride, s.s_tok_stride, s.s_head_stride = (ks.strides[0] // 2, ks.strides[1] // 2,
+                                                            ks.strides[2] // 2)
+        keep += [ks, vs]
+    s.table = table.ctypes.data
+    s.table_stride = table.shape[1]
+    s.kv_len = kv_len.ctypes.data
+    return s, keep
+
+
+def decode(prob: dict, rows=None, nthreads: int = 0, lib=None):
+    """fp64 o [nrows, D] and lse [nrows] for the given flat rows r = (b*T + t)*Hq + h
+    (all rows when None)."""
+    lib = lib or load()
+    s, keep = _problem(prob)
+    D = s.head_dim
+    total = s.batch * s.q_per_seq * s.num_qo_heads
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    n = total if r is None else r.shape[0]
+    o = np.empty((n, D), np.float64)
+    lse = np.empty((n,), np.float64)
+    rc = lib.oracle_decode(ctypes.byref(s), _ptr(r), n, o.ctypes.data, lse.ctypes.data, nthreads)
+    if rc != 0:
+        raise RuntimeError("oracle_decode failed")
+    return o, lse
+
+
+def decode_blocked(prob: dict, block: int, rows=None, lib=None):
+    """The same rows in split form over blocks of `block` tokens (self-check of the merge)."""
+    lib = lib or load()
+    s, keep = _problem(prob)
+    D = s.head_dim
+    total = s.batch * s.q_per_seq * s.num_qo_heads
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    n = total if r is None else r.shape[0]
+    o = np.empty((n, D), np.float64)
+    lse = np.empty((n,), np.float64)
+    rc = lib.oracle_decode_blocked(ctypes.byref(s), _ptr(r), n, int(block), o.ctypes.data,
+                                   lse.ctypes.data)
+    if rc != 0:
+        raise RuntimeError("oracle_decode_blocked failed")
+    return o, lse
+
+
+def gather(prob: dict, max_len: int, lib=None):
+    """Raw dense copies of every visible K/V row: (dense_k, dense_v, dense_ks, dense_vs) of
+    shape [B, max_len, Hkv, D] (and [B, max_len, Hkv, D/32] scales for int8); positions at or
+    beyond kv_len are zero."""
+    lib = lib or load()
+    s, keep = _problem(prob)
+    B, Hkv, D = s.batch, s.num_kv_heads, s.head_dim
+    dt = prob["k_pages"].dtype
+    dk = np.zeros((B, max_len, Hkv, D), dt)
+    dv = np.zeros((B, max_len, Hkv, D), dt)
+    dks = dvs = None
+    if s.kv_int8:
+        dks = np.zeros((B, max_len, Hkv, D // 32), np.float16)
+        dvs = np.zeros((B, max_len, Hkv, D // 32), np.float16)
+    rc = lib.oracle_gather(ctypes.byref(s), int(max_len), dk.ctypes.data, dv.ctypes.data,
+                           _ptr(dks), _ptr(dvs))
+    if rc != 0:
+        raise RuntimeError("oracle_gather failed")
+    return dk, dv, dks, dvs
+
+
+def num_threads() -> int:
+    return int(load().oracle_num_threads())

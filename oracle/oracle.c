@@ -1,0 +1,331 @@
+/*
+ * oracle.c - plain fp64 CPU oracle for paged decode attention.
+ *
+ * TEST INFRASTRUCTURE. Only the tests, the smoke check and the CPU-baseline leg of the
+ * benchmark load this library. The HIP library never calls it, and the two share no code:
+ * no headers, no helpers, no tables, no constants.
+ *
+ * What it computes
+ * ----------------
+ * The split-KV decode of the pages computes exactly (up to rounding order) plain softmax
+ * attention over the cached positions of each sequence: cutting the KV length into 64-token
+ * partial blocks and merging the per-block partials with a log-sum-exp reduction is an
+ * algebraic identity (1bit-MONSTER/engine issue #115, "HRX: flash-attention decode-split
+ * template resolution fails", comments "Root-caused" and "Closing the remaining half of this
+ * issue": the producer writes one partial per 64-token block and reduce_fused merges them).
+ * So this oracle is that plain definition, written out in fp64, step by step:
+ *
+ *   O1 gather  For sequence b and logical position j, the page is table[b][j / P] and the
+ *              slot j % P; the K row of KV head g is read at
+ *              page*page_stride + slot*tok_stride + g*head_stride (elements). V is read with
+ *              the same page shape and strides as K, and only pages named by the table are
+ *              read (AMD-Ecosystem/flashinfer PR #397, "Stop declaring the paged KV cache
+ *              mutated on read-only attention ops", section "What changed": K and V share page
+ *              shape and strides; page counts may differ; only indexed pages are read).
+ *              An f16 element widens to f64 exactly. An int8 element is value = int8 * scale
+ *              with one f16 scale per 32 contiguous head_dim elements; the product is exact
+ *              in f64.
+ *   O2 heads   Query head h reads KV head floor(h / G), G = Hq / Hkv (consecutive grouping;
+ *              the pages give only the head counts).
+ *   O3 length  Query token t of a sequence with T query tokens and kv_len L sees positions
+ *              j < L - T + t + 1 (the T query tokens are the last T cached positions: the
+ *              multi-token decode that the routing threshold of llama-cpp-turboquant PR #176,
+ *              section "Changes", keeps on the decode path for MTP spec-decode). T = 1 sees L.
+ *   O4 logits  s_j = sm_scale * sum_d q[d] * K[j][d], all in fp64.
+ *   O5 result  m = max_j s_j, w_j = exp(s_j - m), S = sum_j w_j,
+ *              o[d] = sum_j w_j V[j][d] / S, lse = m + ln S (natural log, scale included).
+ *              A row that sees no position gets o = 0 and lse = -inf.
+ *   O6         (self-check only) the same result in split form: blocks of a given number of
+ *              tokens, each with its own (m_i, S_i, o_i), merged with M = max m_i,
+ *              S = sum S_i e^(m_i - M), o = sum e^(m_i - M) o_i / S, lse = M + ln S.
+ *
+ * Layouts: q is [B*T, Hq, D] f16 (row b*T + t; token and head strides in elements, D dense);
+ * K and V pools are [pages, P, Hkv, D] with the given element strides; int8 scales are
+ * [pages, P, Hkv, D/32] f16 with their own strides; table is [B, table_stride] int32;
+ * kv_len is [B] int32. Outputs are fp64 [nrows, D] and [nrows].
+ *
+ * Build: gcc -O2 -fopenmp -fPIC -shared (no fast-math).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* A mutant build plants one deliberate mistake so that the tests can show a pin catches
+ * it. The default build (ORACLE_MUTANT undefined or 0) is the oracle. */
+#ifndef ORACLE_MUTANT
+#define ORACLE_MUTANT 0
+#endif
+
+typedef struct {
+  int32_t batch;        /* B */
+  int32_t q_per_seq;    /* T */
+  int32_t num_qo_heads; /* Hq */
+  int32_t num_kv_heads; /* Hkv */
+  int32_t head_dim;     /* D */
+  int32_t page_size;    /* P */
+  int32_t kv_int8;      /* 0: f16 K/V; 1: int8 K/V with f16 scales per 32 elements */
+  int32_t pad0;
+  double sm_scale;      /* the f32 scale the caller passes, widened */
+  const uint16_t *q;    /* f16 bits */
+  int64_t q_tok_stride, q_head_stride;
+  const void *k, *v;    /* f16 bits or int8 */
+  const uint16_t *k_scale, *v_scale;
+  int64_t page_stride, tok_stride, head_stride;
+  int64_t s_page_stride, s_tok_stride, s_head_stride;
+  const int32_t *table;
+  int64_t table_stride;
+  const int32_t *kv_len;
+} oracle_problem;
+
+/* IEEE-754 binary16 -> binary64, exact. */
+double oracle_half_to_double(uint16_t h) {
+  int sign = h >> 15, e = (h >> 10) & 0x1f, m = h & 0x3ff;
+  double v;
+  if (e == 0)
+    v = ldexp((double)m, -24); /* subnormal: m * 2^-24 */
+  else if (e == 31)
+    v = m ? NAN : INFINITY;
+  else
+    v = ldexp((double)(m + 1024), e - 25); /* (1024 + m) * 2^(e - 15 - 10) */
+  return sign ? -v : v;
+}
+
+/* O1: element offset of position j's row for KV head g, and of its scale row. */
+static int64_t row_offset(const oracle_problem *p, int b, int64_t j, int g, int64_t *scale_off) {
+  int64_t page_idx = j / p->page_size;
+  int64_t slot = j % p->page_size;
+#if ORACLE_MUTANT == 4
+  slot = (j + 1) % p->page_size; /* planted: wrong slot */
+#endif
+  int64_t page = p->table[(int64_t)b * p->table_stride + page_idx];
+  if (scale_off)
+    *scale_off = page * p->s_page_stride + slot * p->s_tok_stride + (int64_t)g * p->s_head_stride;
+  return page * p->page_stride + slot * p->tok_stride + (int64_t)g * p->head_stride;
+}
+
+/* O1: dequantized element d of a gathered row, in fp64. */
+static double kv_elem(const oracle_problem *p, const void *base, const uint16_t *scales,
+                      int64_t off, int64_t soff, int d) {
+  if (!p->kv_int8) return oracle_half_to_double(((const uint16_t *)base)[off + d]);
+  int group = d / 32;
+#if ORACLE_MUTANT == 5
+  group = d / 16; /* planted: wrong scale group */
+  if (group >= p->head_dim / 32) group = p->head_dim / 32 - 1;
+#endif
+  double s = oracle_half_to_double(scales[soff + group]);
+  return (double)((const int8_t *)base)[off + d] * s;
+}
+
+/* O3: number of positions row (b, t) sees. */
+static int64_t visible_len(const oracle_problem *p, int b, int t) {
+  int64_t L = p->kv_len[b];
+  int64_t n = L - p->q_per_seq + t + 1;
+#if ORACLE_MUTANT == 3
+  n = L - p->q_per_seq + t; /* planted: causal off by one */
+#endif
+  if (n > L) n = L;
+  return n < 0 ? 0 : n;
+}
+
+/* O2 */
+static int kv_head_of(const oracle_problem *p, int h) {
+#if ORACLE_MUTANT == 1
+  return h % p->num_kv_heads; /* planted: interleaved head map */
+#else
+  return h / (p->num_qo_heads / p->num_kv_heads);
+#endif
+}
+
+/* O4 for one (row, position). */
+static double logit(const oracle_problem *p, const uint16_t *qrow, int b, int64_t j, int g) {
+  int64_t soff = 0;
+  int64_t off = row_offset(p, b, j, g, &soff);
+#if ORACLE_MUTANT == 8
+  const void *kb = p->v; const uint16_t *ks = p->v_scale; /* planted: V used as K */
+#else
+  const void *kb = p->k; const uint16_t *ks = p->k_scale;
+#endif
+  double dot = 0.0;
+  for (int d = 0; d < p->head_dim; ++d)
+    dot += oracle_half_to_double(qrow[d]) * kv_elem(p, kb, ks, off, soff, d);
+#if ORACLE_MUTANT == 2
+  return dot; /* planted: scale dropped */
+#else
+  return p->sm_scale * dot;
+#endif
+}
+
+static void row_coords(const oracle_problem *p, int64_t r, int *b, int *t, int *h) {
+  int64_t Hq = p->num_qo_heads, T = p->q_per_seq;
+  *h = (int)(r % Hq);
+  int64_t bt = r / Hq;
+  *t = (int)(bt % T);
+  *b = (int)(bt / T);
+}
+
+static const uint16_t *q_row(const oracle_problem *p, int b, int t, int h) {
+  int tt = t;
+#if ORACLE_MUTANT == 10
+  tt = 0; /* planted: every query token reads token 0's q */
+#endif
+  return p->q + ((int64_t)b * p->q_per_seq + tt) * p->q_tok_stride + (int64_t)h * p->q_head_stride;
+}
+
+/* O1-O5 for one row; s is scratch of at least n doubles. */
+static void decode_row(const oracle_problem *p, int64_t r, double *o, double *lse, double *s) {
+  int b, t, h;
+  row_coords(p, r, &b, &t, &h);
+  int D = p->head_dim, g = kv_head_of(p, h);
+  int64_t n = visible_len(p, b, t);
+  for (int d = 0; d < D; ++d) o[d] = 0.0;
+  if (n <= 0) { *lse = -INFINITY; return; }
+  const uint16_t *qrow = q_row(p, b, t, h);
+  double m = -INFINITY;
+  for (int64_t j = 0; j < n; ++j) {
+    s[j] = logit(p, qrow, b, j, g);
+    if (s[j] > m) m = s[j];
+  }
+  double S = 0.0;
+  for (int64_t j = 0; j < n; ++j) {
+#if ORACLE_MUTANT == 9
+    double w = exp(m - s[j]); /* planted: sign flipped */
+#else
+    double w = exp(s[j] - m);
+#endif
+    S += w;
+    int64_t soff = 0;
+    int64_t off = row_offset(p, b, j, g, &soff);
+    for (int d = 0; d < D; ++d) o[d] += w * kv_elem(p, p->v, p->v_scale, off, soff, d);
+  }
+#if ORACLE_MUTANT != 7
+  for (int d = 0; d < D; ++d) o[d] /= S;
+#endif
+#if ORACLE_MUTANT == 6
+  *lse = log(S); /* planted: max dropped from lse */
+#else
+  *lse = m + log(S);
+#endif
+}
+
+static int64_t max_visible(const oracle_problem *p) {
+  int64_t mx = 1;
+  for (int b = 0; b < p->batch; ++b)
+    if (p->kv_len[b] > mx) mx = p->kv_len[b];
+  return mx;
+}
+
+/* Decode the given rows (r = (b*T + t)*Hq + h), or all B*T*Hq rows when rows is NULL.
+ * o is [nrows, D] and lse [nrows], fp64. nthreads <= 0 uses the OpenMP default. */
+int oracle_decode(const oracle_problem *p, const int64_t *rows, int64_t nrows, double *o,
+                  double *lse, int nthreads) {
+  int64_t total = (int64_t)p->batch * p->q_per_seq * p->num_qo_heads;
+  if (!rows) nrows = total;
+  int64_t smax = max_visible(p);
+  int D = p->head_dim;
+  int bad = 0;
+#ifdef _OPENMP
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads) reduction(| : bad)
+#endif
+  {
+    double *s = (double *)malloc(sizeof(double) * (size_t)smax);
+    if (!s) bad = 1;
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+    for (int64_t i = 0; i < nrows; ++i) {
+      int64_t r = rows ? rows[i] : i;
+      if (!s || r < 0 || r >= total) { bad = 1; continue; }
+      decode_row(p, r, o + i * D, lse + i, s);
+    }
+    free(s);
+  }
+  return bad ? -1 : 0;
+}
+
+/* O6 (self-check): the same rows in split form over blocks of `block` tokens. */
+int oracle_decode_blocked(const oracle_problem *p, const int64_t *rows, int64_t nrows,
+                          int64_t block, double *o, double *lse) {
+  int64_t total = (int64_t)p->batch * p->q_per_seq * p->num_qo_heads;
+  if (!rows) nrows = total;
+  if (block <= 0) return -1;
+  int D = p->head_dim;
+  double *oi = (double *)malloc(sizeof(double) * (size_t)D);
+  if (!oi) return -1;
+  for (int64_t i = 0; i < nrows; ++i) {
+    int64_t r = rows ? rows[i] : i;
+    if (r < 0 || r >= total) { free(oi); return -1; }
+    int b, t, h;
+    row_coords(p, r, &b, &t, &h);
+    int g = kv_head_of(p, h);
+    int64_t n = visible_len(p, b, t);
+    const uint16_t *qrow = q_row(p, b, t, h);
+    double *orow = o + i * D;
+    double M = -INFINITY, S = 0.0;
+    for (int d = 0; d < D; ++d) orow[d] = 0.0;
+    for (int64_t j0 = 0; j0 < n; j0 += block) {
+      int64_t j1 = j0 + block < n ? j0 + block : n;
+      double mi = -INFINITY, Si = 0.0;
+      for (int64_t j = j0; j < j1; ++j) {
+        double s = logit(p, qrow, b, j, g);
+        if (s > mi) mi = s;
+      }
+      for (int d = 0; d < D; ++d) oi[d] = 0.0;
+      for (int64_t j = j0; j < j1; ++j) {
+        double w = exp(logit(p, qrow, b, j, g) - mi);
+        Si += w;
+        int64_t soff = 0;
+        int64_t off = row_offset(p, b, j, g, &soff);
+        for (int d = 0; d < D; ++d) oi[d] += w * kv_elem(p, p->v, p->v_scale, off, soff, d);
+      }
+      /* merge block i into the running state */
+      double Mn = mi > M ? mi : M;
+      double a = (M == -INFINITY) ? 0.0 : exp(M - Mn), c = exp(mi - Mn);
+      S = S * a + Si * c;
+      for (int d = 0; d < D; ++d) orow[d] = orow[d] * a + oi[d] * c;
+      M = Mn;
+    }
+    if (n <= 0) { lse[i] = -INFINITY; continue; }
+    for (int d = 0; d < D; ++d) orow[d] /= S;
+    lse[i] = M + log(S);
+  }
+  free(oi);
+  return 0;
+}
+
+/* O1 alone: copy the raw elements (and, for int8, the raw f16 scale bits) of every visible
+ * position j < kv_len[b] into dense [B, max_len, Hkv, D] (and [B, max_len, Hkv, D/32])
+ * arrays. Positions at or beyond kv_len are left untouched. */
+int oracle_gather(const oracle_problem *p, int64_t max_len, void *dense_k, void *dense_v,
+                  uint16_t *dense_ks, uint16_t *dense_vs) {
+  int D = p->head_dim, Hkv = p->num_kv_heads, es = p->kv_int8 ? 1 : 2, ng = D / 32;
+  for (int b = 0; b < p->batch; ++b) {
+    int64_t L = p->kv_len[b];
+    if (L > max_len) return -1;
+    for (int64_t j = 0; j < L; ++j)
+      for (int g = 0; g < Hkv; ++g) {
+        int64_t soff = 0;
+        int64_t off = row_offset(p, b, j, g, &soff);
+        int64_t dst = (((int64_t)b * max_len + j) * Hkv + g);
+        memcpy((char *)dense_k + dst * D * es, (const char *)p->k + off * es, (size_t)D * es);
+        memcpy((char *)dense_v + dst * D * es, (const char *)p->v + off * es, (size_t)D * es);
+        if (p->kv_int8) {
+          memcpy(dense_ks + dst * ng, p->k_scale + soff, sizeof(uint16_t) * ng);
+          memcpy(dense_vs + dst * ng, p->v_scale + soff, sizeof(uint16_t) * ng);
+        }
+      }
+  }
+  return 0;
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
