@@ -1,0 +1,203 @@
+#!/usr/bin/env python3
+"""Benchmark: split-KV paged decode on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config 2] [--gpus 1] [--no-cpu]
+
+A step is one decode call (partial kernel + reducer) over one batch of the workload, with
+all inputs resident in HBM. The default workload is the GQA batch decode (B=32, 32 query /
+8 KV heads, head_dim 128, page 16, kv_len uniform in [1024, 4096], f16 cache). Enough copies
+of the pools and tables rotate that the working set exceeds twice the 256 MB Infinity Cache.
+
+Prints one JSON line: value = K+V bytes read per call / time per call (GB/s), plus
+roofline (the partial kernel's algorithmic K+V bytes per launch over its average launch time,
+timed with HIP events on the launching stream, against 8 TB/s) and cpu_baseline (the fp64
+oracle on the host cores over a bounded sample of the same workload).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode µs/call and achieved HBM GB/s (K+V bytes read) vs roofline"
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 * 2 ** 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("kernels.hip", "plan.cpp"):
+        with open(os.path.join(ROOT, "quantized_kv_cache_page_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per partial-kernel launch from the committed rocprofv3 --pmc summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "partial_kernel_traffic.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = d.get(workload)
+    if not e or e.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(prob, budget_s=12.0):
+    """The oracle as it stands, on all host cores, over whole decodes of the same batch
+    (K+V bytes per decode / wall time), repeated until about budget_s of CPU work."""
+    import numpy as np
+    import oracle
+    import workloads
+    nthreads = oracle.num_threads()
+    times = []
+    t_end = time.time() + budget_s
+    while True:
+        t0 = time.time()
+        oracle.decode(prob)
+        times.append(time.time() - t0)
+        if time.time() > t_end or len(times) >= 30:
+            break
+    t = float(np.median(times))
+    gbs = workloads.kv_bytes(prob) / t / 1e9
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"{len(times)} whole decodes of the same batch (all {prob['q'].shape[0]} "
+                      f"query tokens x {prob['q'].shape[1]} heads), median {t:.3f} s each, fp64"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--bps", type=int, default=0, help="force 64-token blocks per split")
+    ap.add_argument("--reducer", default="auto")
+    ap.add_argument("--copies", type=int, default=0, help="pool copies to rotate (0: auto)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (the decode "
+              f"is single-GPU; the multi-GPU sharding is described, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import quantized_kv_cache_page_amd as skvd
+    import workloads
+
+    spec = workloads.config(args.config)
+    seed = args.config if args.seed is None else args.seed
+    t0 = time.time()
+    prob = workloads.generate(spec, seed)
+    log(f"[bench] generated config {args.config} ({spec.name}) in {time.time() - t0:.1f}s")
+    kvb = workloads.kv_bytes(prob)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def up(x):
+        return None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    q = up(prob["q"])
+    table = up(prob["page_table"])
+    kv_len = up(prob["kv_len"])
+    pools = [up(prob[k]) for k in ("k_pages", "v_pages", "k_scales", "v_scales")]
+    pool_bytes = sum(p.numel() * p.element_size() for p in pools if p is not None)
+    copies = args.copies or max(1, math.ceil(2 * MALL_BYTES / max(kvb, 1)) + 1)
+    sets = [pools] + [[None if p is None else p.clone() for p in pools] for _ in range(copies - 1)]
+    log(f"[bench] K+V bytes/call {kvb / 2**20:.1f} MiB, pools {pool_bytes / 2**20:.1f} MiB x "
+        f"{copies} copies")
+
+    plan = skvd.Plan(spec.num_qo_heads, spec.num_kv_heads, spec.head_dim, spec.page_size,
+                     spec.kv_dtype, spec.batch, spec.q_per_seq, spec.max_kv_len, device=0,
+                     force_blocks_per_split=args.bps, force_reducer=args.reducer)
+    plan.ensure_workspace()
+    log(f"[bench] {plan.describe()}")
+    out = torch.empty(q.shape, dtype=torch.float16, device=dev)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+
+    def call(i, stage="all"):
+        k, v, ks, vs = sets[i % copies]
+        plan.run(q, k, v, table, kv_len, prob["sm_scale"], ks, vs, out=out, lse=lse,
+                 q_per_seq=spec.q_per_seq, stage=stage)
+
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+
+    # Timed region: K steps, each one decode = partial stage + merge stage, with events on the
+    # launching (current) stream around the partial kernel.
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(K):
+        ev[i][0].record()
+        call(i, "partial")
+        ev[i][1].record()
+        call(i, "merge")
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_step = total_ms / K
+    part_ms = [a.elapsed_time(b) for a, b in ev]
+    part_avg = float(np.mean(part_ms))
+
+    # A second timed pass of whole skvd_decode calls (no events in between) for µs/call.
+    start2, stop2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start2.record()
+    for i in range(K):
+        call(i)
+    stop2.record()
+    torch.cuda.synchronize()
+    ms_call = start2.elapsed_time(stop2) / K
+    log(f"[bench] decode {ms_call * 1e3:.2f} us/call (staged {ms_step * 1e3:.2f}), partial "
+        f"kernel avg {part_avg * 1e3:.2f} us (min {min(part_ms) * 1e3:.2f})")
+
+    gbs = kvb / (ms_call * 1e-3) / 1e9
+    achieved = kvb / (part_avg * 1e-3) / 1e9
+    workload = (f"{spec.name} (config {args.config}): B={spec.batch} T={spec.q_per_seq} "
+                f"Hq={spec.num_qo_heads} Hkv={spec.num_kv_heads} D={spec.head_dim} "
+                f"P={spec.page_size} kv={spec.kv_dtype} lens={spec.lens}")
+    traffic = measured_traffic(spec.name)
+    res = {
+        "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_call, 5),
+        "us_per_call": round(ms_call * 1e3, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": workload, "seed": seed, "kv_bytes_per_call": kvb,
+                   "pool_copies_rotated": copies, "plan": plan.describe()},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "partial_kernel",
+                     "kernel_avg_us": round(part_avg * 1e3, 3),
+                     "algorithmic_bytes_per_launch": kvb},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        log("[bench] timing the CPU oracle ...")
+        res["cpu_baseline"] = cpu_baseline(prob)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

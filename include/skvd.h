@@ -1,0 +1,213 @@
+/*
+ * skvd.h - split-KV paged decode attention for MI355X (gfx950): the C ABI.
+ *
+ * What the library computes
+ * -------------------------
+ * Batch decode attention over a paged KV cache. Each sequence b has T query tokens (T <= 8)
+ * and kv_len[b] cached positions held in pages of P tokens; query head h reads KV head
+ * h / G (G = Hq / Hkv). For query token t of sequence b the visible positions are
+ * j < kv_len[b] - T + t + 1 (the T query tokens are the last T cached positions, so T = 1
+ * sees all of kv_len[b]); the result is
+ *     o   = softmax(sm_scale * q K^T) V          (f16, dense [B*T, Hq, D])
+ *     lse = ln sum_j exp(sm_scale * q . k_j)     (f32, [B*T, Hq]; natural log)
+ * A row that sees no position gets o = 0 and lse = -inf.
+ *
+ * The method is the split-KV decode of 1bit-MONSTER/engine issue #115 ("HRX:
+ * flash-attention decode-split template resolution fails ("all_rejected") at longer
+ * context"): the KV length is cut into 64-token blocks (key_value_capacity is kv_len rounded
+ * up to a multiple of 64, comment "Closing the remaining half of this issue"), each run of
+ * blocks yields an online-softmax partial (running max, sum and f32 output), and the
+ * partials are merged by a log-sum-exp reduction. The reducers here are direct,
+ * cooperative (one lane per partial), multipass (lane-strided, any count) and hierarchical
+ * (two levels); no capacity ceiling exists at 32 blocks / 2048 tokens or anywhere else.
+ *
+ * The call follows the statement of a read-only decode op in AMD-Ecosystem/flashinfer PR
+ * #397 ("Stop declaring the paged KV cache mutated on read-only attention ops", sections
+ * "Summary" and "What changed"): it takes q, separate K and V page pools that share page
+ * shape and strides (their page counts may differ; only pages named by the table are read),
+ * a page table and per-sequence lengths, and writes only o and lse, densely. The int8 cache
+ * (one f16 scale per 32 contiguous head_dim elements, value = int8 * scale) is dequantized
+ * inline with no f16 temporary, as the graph-safe VEC decode path of llama-cpp-turboquant
+ * PR #176 ("HIP: fix turbo KV decode crash under graph capture; batch-aware VEC/TILE FA
+ * routing", section "Changes") does; that PR's routing threshold (Q->ne[1] <= 8) is why this
+ * decode call accepts at most 8 query tokens per sequence.
+ *
+ * Conventions
+ * -----------
+ * - Ownership: every pointer in skvd_decode_args is caller-owned device memory on the plan's
+ *   device. The library keeps none of them after a call returns. A plan is a host object;
+ *   the workspace is caller-provided device memory of skvd_plan_workspace_bytes() bytes,
+ *   256-byte aligned, used by one call at a time (one plan per stream at a time).
+ * - Const-correctness is the declaration: q, both pools, both scale pools, the table and
+ *   kv_len are read only. skvd_decode writes o, lse and the workspace, nothing else.
+ * - Graph capture: skvd_decode performs no allocation, no synchronization and no device-to-
+ *   host read; kernels read kv_len on the device. It may be called inside hipStreamBegin-
+ *   Capture, including as the first call of a plan. Plans are created outside capture.
+ * - Errors: every call returns a status. Host-checkable faults (shapes, dtypes, strides,
+ *   alignment, batch above the plan, workspace too small) are reported before anything is
+ *   launched. A launch failure returns SKVD_ERR_HIP after reading and clearing the HIP
+ *   error. skvd_last_error() gives a thread-local message. No exception or abort crosses
+ *   the ABI.
+ * - Device-data contracts (page ids in range, q_per_seq <= kv_len[b] <= max_kv_len) are not
+ *   checked with a synchronization: kernels clamp page ids into [0, num_pages) and kv_len
+ *   into [0, max_kv_len], so a violation cannot read or write out of range; plans made with
+ *   debug != 0 also set bits in the workspace status word (skvd_plan_info.status_offset).
+ * - Strides are in elements of the array they index. head_dim is dense (stride 1).
+ */
+#ifndef SKVD_H
+#define SKVD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SKVD_ABI_VERSION 1
+
+typedef enum {
+  SKVD_OK = 0,
+  SKVD_ERR_NULL = 1,        /* a required pointer is NULL */
+  SKVD_ERR_SHAPE = 2,       /* a size is out of range or inconsistent with the plan */
+  SKVD_ERR_LAYOUT = 3,      /* a stride or alignment the kernels cannot address */
+  SKVD_ERR_DTYPE = 4,       /* unknown kv_dtype, or scales present/absent against it */
+  SKVD_ERR_WORKSPACE = 5,   /* workspace missing, too small or misaligned */
+  SKVD_ERR_DEVICE = 6,      /* device query failed or the current device is not the plan's */
+  SKVD_ERR_PLAN = 7,        /* invalid plan parameters (e.g. a forced reducer that cannot
+                               cover the plan's partial count) */
+  SKVD_ERR_HIP = 8          /* a HIP call or launch failed; detail in skvd_last_error() */
+} skvd_status;
+
+typedef enum {
+  SKVD_KV_F16 = 0,          /* K/V pools hold f16 */
+  SKVD_KV_I8_F16SCALE32 = 1 /* K/V pools hold int8; scale pools hold one f16 per 32 elements */
+} skvd_kv_dtype;
+
+typedef enum {
+  SKVD_REDUCER_AUTO = 0,
+  SKVD_REDUCER_DIRECT = 1,       /* one wave per row walks the partials serially */
+  SKVD_REDUCER_COOPERATIVE = 2,  /* one lane per partial (at most 64 partials) */
+  SKVD_REDUCER_MULTIPASS = 3,    /* lane-strided over any number of partials */
+  SKVD_REDUCER_HIERARCHICAL = 4, /* groups of 64 partials per workgroup, then a second merge */
+  SKVD_REDUCER_NONE = 5          /* one split: the partial kernel writes o and lse itself */
+} skvd_reducer;
+
+/* Static shape of a plan. All sizes are upper bounds of what skvd_decode may be given. */
+typedef struct {
+  int32_t num_qo_heads;   /* Hq; Hq % Hkv == 0 */
+  int32_t num_kv_heads;   /* Hkv >= 1 */
+  int32_t head_dim;       /* D: 128 or 256 */
+  int32_t page_size;      /* P: power of two, 1..1024 */
+  int32_t max_batch;      /* B upper bound, >= 1 */
+  int32_t max_q_per_seq;  /* T upper bound: 1..8, and G * T <= 16 */
+  int32_t max_kv_len;     /* kv_len upper bound, >= 1 */
+  int32_t kv_dtype;       /* skvd_kv_dtype */
+  int32_t device;         /* HIP device ordinal the calls run on */
+  int32_t num_cus;        /* 0: query the device; > 0: plan for this many compute units
+                             without touching HIP (host-only planning) */
+  int32_t force_blocks_per_split; /* 0: heuristic; > 0: 64-token blocks per split */
+  int32_t force_reducer;  /* skvd_reducer; 0 = choose by partial count */
+  int32_t debug;          /* != 0: kernels record contract violations in the status word */
+} skvd_plan_params;
+
+/* What a plan resolved to (for logs and tests). */
+typedef struct {
+  int32_t blocks_per_split; /* 64-token blocks each split covers */
+  int32_t splits_cap;       /* partials per row at max_kv_len (partial stride) */
+  int32_t reducer;          /* skvd_reducer actually used */
+  int32_t hier_groups_cap;  /* first-level groups of the hierarchical reducer, else 0 */
+  int32_t rows_per_group;   /* G * max_q_per_seq rows one workgroup serves */
+  int32_t num_cus;          /* compute units planned for */
+  int64_t rows_cap;         /* max_batch * max_q_per_seq * Hq */
+  uint64_t workspace_bytes;
+  uint64_t status_offset;   /* byte offset of the uint32 status word in the workspace */
+} skvd_plan_info;
+
+/* Status-word bits (debug plans). */
+#define SKVD_STATUS_KV_LEN_CLAMPED 0x1u  /* some kv_len[b] was < 0 or > max_kv_len */
+#define SKVD_STATUS_PAGE_CLAMPED 0x2u    /* some page id read was outside [0, num_pages) */
+
+typedef struct skvd_plan skvd_plan;
+
+/* Arguments of one decode. Element strides; every array lives on the plan's device. */
+typedef struct {
+  const void *q;             /* f16 [B*T, Hq, D]; row b*T + t; D dense; 16-byte aligned */
+  int64_t q_tok_stride;      /* elements between rows b*T + t and b*T + t + 1 (multiple of 8) */
+  int64_t q_head_stride;     /* elements between heads (multiple of 8) */
+  const void *k_pages;       /* [num_k_pages, P, Hkv, D] f16 or int8; 16-byte aligned */
+  const void *v_pages;       /* [num_v_pages, P, Hkv, D], same strides as K */
+  int64_t page_stride;       /* elements between pages (shared by K and V) */
+  int64_t tok_stride;        /* elements between slots of a page */
+  int64_t head_stride;       /* elements between KV heads */
+  int64_t num_k_pages;       /* pages in the K pool (>= 1); ids are clamped below it */
+  int64_t num_v_pages;       /* pages in the V pool (>= 1) */
+  const void *k_scales;      /* int8 only: f16 [num_k_pages, P, Hkv, D/32]; else NULL */
+  const void *v_scales;      /* int8 only: f16 [num_v_pages, P, Hkv, D/32]; else NULL */
+  int64_t scale_page_stride; /* elements; shared by both scale pools */
+  int64_t scale_tok_stride;
+  int64_t scale_head_stride;
+  const int32_t *page_table; /* [B, table_stride]; entry i of row b is the page holding
+                                positions i*P .. i*P+P-1; entries past ceil(kv_len/P) are
+                                never read */
+  int64_t table_stride;      /* >= ceil(max_kv_len / P) */
+  const int32_t *kv_len;     /* [B] device int32 */
+  int32_t batch;             /* B, 0..max_batch (0 launches nothing) */
+  int32_t q_per_seq;         /* T, 1..max_q_per_seq */
+  float sm_scale;            /* softmax scale applied to q . k (finite) */
+  int32_t reserved;          /* must be 0 */
+  void *o;                   /* f16 [B*T, Hq, D] dense, written */
+  float *lse;                /* f32 [B*T, Hq] dense, written; may be NULL (not written) */
+} skvd_decode_args;
+
+/* Plan: validate the static shape, choose blocks per split and the reducer, and size the
+ * workspace. Host only: no device allocation; with num_cus > 0 no HIP call at all. The
+ * environment variable SKVD_LOG_DISPATCH=1 prints the resolved plan to stderr here (never
+ * in a launch). On success *out owns a plan to free with skvd_plan_destroy. */
+skvd_status skvd_plan_create(const skvd_plan_params *params, skvd_plan **out);
+void skvd_plan_destroy(skvd_plan *plan);
+/* Workspace bytes skvd_decode needs for this plan (0 for a NULL plan). */
+size_t skvd_plan_workspace_bytes(const skvd_plan *plan);
+skvd_status skvd_plan_get_info(const skvd_plan *plan, skvd_plan_info *info);
+/* NUL-terminated one-line description (blocks per split, splits, reducer, bytes). */
+skvd_status skvd_plan_describe(const skvd_plan *plan, char *buf, size_t buf_len);
+
+/* Validation alone: the checks skvd_decode makes before launching, with no HIP call. */
+skvd_status skvd_decode_check(const skvd_plan *plan, const skvd_decode_args *args,
+                              size_t workspace_bytes);
+
+/* Decode: partial kernel, then the plan's reducer, enqueued on `stream` (a hipStream_t;
+ * NULL is the null stream). Asynchronous; writes o, lse and the workspace only. The
+ * current HIP device must be the plan's device. */
+skvd_status skvd_decode(const skvd_plan *plan, const skvd_decode_args *args, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+/* The two stages of skvd_decode, for callers that time or compose them. The partial stage
+ * writes one (max, sum, f32 output) partial per split into the workspace, or o and lse
+ * directly when the plan's reducer is SKVD_REDUCER_NONE; the merge stage reads those
+ * partials and writes o and lse (and does nothing for SKVD_REDUCER_NONE). Running
+ * skvd_decode_partial then skvd_decode_merge on one stream equals skvd_decode. */
+skvd_status skvd_decode_partial(const skvd_plan *plan, const skvd_decode_args *args,
+                                void *workspace, size_t workspace_bytes, void *stream);
+skvd_status skvd_decode_merge(const skvd_plan *plan, const skvd_decode_args *args,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/* Test aid: copy the raw elements of every visible K/V row (position j < kv_len[b]) into
+ * dense [B, max_len, Hkv, D] arrays (element size 2 for f16, 1 for int8), and for int8 the
+ * raw f16 scales into dense [B, max_len, Hkv, D/32] arrays (dense_ks/dense_vs; NULL for f16).
+ * The row address comes from the same device function the decode kernels use. Rows at or
+ * beyond kv_len[b] are not written. max_len >= every kv_len[b]. o, lse are ignored. */
+skvd_status skvd_gather_debug(const skvd_plan *plan, const skvd_decode_args *args,
+                              int32_t max_len, void *dense_k, void *dense_v, void *dense_ks,
+                              void *dense_vs, void *stream);
+
+const char *skvd_status_string(skvd_status status);
+/* Message of the last failed call on this thread ("" if none). */
+const char *skvd_last_error(void);
+int32_t skvd_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SKVD_H */

@@ -1,0 +1,348 @@
+"""ctypes binding of libskvd.so: the C-ABI functions under the same names, and `Plan`, which
+marshals torch tensors (device memory and streams only) into those calls.
+
+Nothing here computes any part of the decode: every step runs in the HIP kernels of
+libskvd.so. Importing fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # imported first: libskvd.so then binds to the HIP runtime torch already loaded
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libskvd.so")
+
+SKVD_KV_F16 = 0
+SKVD_KV_I8_F16SCALE32 = 1
+REDUCERS = {"auto": 0, "direct": 1, "cooperative": 2, "multipass": 3, "hierarchical": 4,
+            "none": 5}
+REDUCER_NAMES = {v: k for k, v in REDUCERS.items()}
+STATUS_KV_LEN_CLAMPED = 0x1
+STATUS_PAGE_CLAMPED = 0x2
+
+
+class SkvdError(RuntimeError):
+    def __init__(self, status: int, where: str, msg: str):
+        super().__init__(f"{where}: status {status} ({status_string(status)}): {msg}")
+        self.status = status
+
+
+class skvd_plan_params(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_qo_heads", "num_kv_heads", "head_dim", "page_size", "max_batch", "max_q_per_seq",
+        "max_kv_len", "kv_dtype", "device", "num_cus", "force_blocks_per_split",
+        "force_reducer", "debug")]
+
+
+class skvd_plan_info(ctypes.Structure):
+    _fields_ = [("blocks_per_split", ctypes.c_int32), ("splits_cap", ctypes.c_int32),
+                ("reducer", ctypes.c_int32), ("hier_groups_cap", ctypes.c_int32),
+                ("rows_per_group", ctypes.c_int32), ("num_cus", ctypes.c_int32),
+                ("rows_cap", ctypes.c_int64), ("workspace_bytes", ctypes.c_uint64),
+                ("status_offset", ctypes.c_uint64)]
+
+
+class skvd_decode_args(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("q_tok_stride", ctypes.c_int64), ("q_head_stride", ctypes.c_int64),
+        ("k_pages", ctypes.c_void_p), ("v_pages", ctypes.c_void_p),
+        ("page_stride", ctypes.c_int64), ("tok_stride", ctypes.c_int64),
+        ("head_stride", ctypes.c_int64), ("num_k_pages", ctypes.c_int64),
+        ("num_v_pages", ctypes.c_int64),
+        ("k_scales", ctypes.c_void_p), ("v_scales", ctypes.c_void_p),
+        ("scale_page_stride", ctypes.c_int64), ("scale_tok_stride", ctypes.c_int64),
+        ("scale_head_stride", ctypes.c_int64),
+        ("page_table", ctypes.c_void_p), ("table_stride", ctypes.c_int64),
+        ("kv_len", ctypes.c_void_p),
+        ("batch", ctypes.c_int32), ("q_per_seq", ctypes.c_int32),
+        ("sm_scale", ctypes.c_float), ("reserved", ctypes.c_int32),
+        ("o", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+    ]
+
+
+# Every symbol include/skvd.h declares, with its ctypes signature.
+_PLAN_P = ctypes.c_void_p
+SIGNATURES = {
+    "skvd_plan_create": (ctypes.c_int, [ctypes.POINTER(skvd_plan_params), ctypes.POINTER(ctypes.c_void_p)]),
+    "skvd_plan_destroy": (None, [_PLAN_P]),
+    "skvd_plan_workspace_bytes": (ctypes.c_size_t, [_PLAN_P]),
+    "skvd_plan_get_info": (ctypes.c_int, [_PLAN_P, ctypes.POINTER(skvd_plan_info)]),
+    "skvd_plan_describe": (ctypes.c_int, [_PLAN_P, ctypes.c_char_p, ctypes.c_size_t]),
+    "skvd_decode_check": (ctypes.c_int, [_PLAN_P, ctypes.POINTER(skvd_decode_args), ctypes.c_size_t]),
+    "skvd_decode": (ctypes.c_int, [_PLAN_P, ctypes.POINTER(skvd_decode_args), ctypes.c_void_p,
+                                   ctypes.c_size_t, ctypes.c_void_p]),
+    "skvd_decode_partial": (ctypes.c_int, [_PLAN_P, ctypes.POINTER(skvd_decode_args),
+                                           ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "skvd_decode_merge": (ctypes.c_int, [_PLAN_P, ctypes.POINTER(skvd_decode_args),
+                                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "skvd_gather_debug": (ctypes.c_int, [_PLAN_P, ctypes.POINTER(skvd_decode_args), ctypes.c_int32,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_void_p]),
+    "skvd_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "skvd_last_error": (ctypes.c_char_p, []),
+    "skvd_abi_version": (ctypes.c_int32, []),
+}
+
+_lib = None
+
+
+def _hip_runtimes_mapped():
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln})
+    except OSError:
+        return []
+
+
+def lib():
+    """Load libskvd.so once. Raises if it is missing or if two HIP runtimes end up mapped."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run `python -m quantized_kv_cache_page_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    rts = _hip_runtimes_mapped()
+    if len(rts) > 1:
+        raise ImportError(f"two HIP runtimes are mapped ({rts}); import torch before libskvd")
+    if L.skvd_abi_version() != 1:
+        raise ImportError("libskvd ABI version mismatch")
+    _lib = L
+    return L
+
+
+def status_string(st: int) -> str:
+    return lib().skvd_status_string(st).decode()
+
+
+def last_error() -> str:
+    return lib().skvd_last_error().decode()
+
+
+def _check(st: int, where: str):
+    if st != 0:
+        raise SkvdError(st, where, last_error())
+
+
+# ---------------------------------------------------------------- thin C-ABI wrappers
+def skvd_plan_create(params: skvd_plan_params) -> int:
+    h = ctypes.c_void_p()
+    _check(lib().skvd_plan_create(ctypes.byref(params), ctypes.byref(h)), "skvd_plan_create")
+    return h.value
+
+
+def skvd_plan_destroy(plan: int) -> None:
+    lib().skvd_plan_destroy(plan)
+
+
+def skvd_plan_workspace_bytes(plan: int) -> int:
+    return int(lib().skvd_plan_workspace_bytes(plan))
+
+
+def skvd_plan_get_info(plan: int) -> skvd_plan_info:
+    info = skvd_plan_info()
+    _check(lib().skvd_plan_get_info(plan, ctypes.byref(info)), "skvd_plan_get_info")
+    return info
+
+
+def skvd_plan_describe(plan: int) -> str:
+    buf = ctypes.create_string_buffer(512)
+    _check(lib().skvd_plan_describe(plan, buf, 512), "skvd_plan_describe")
+    return buf.value.decode()
+
+
+def skvd_decode_check(plan: int, args: skvd_decode_args, workspace_bytes: int) -> int:
+    return int(lib().skvd_decode_check(plan, ctypes.byref(args), workspace_bytes))
+
+
+def skvd_decode(plan, args, workspace, workspace_bytes, stream) -> int:
+    return int(lib().skvd_decode(plan, ctypes.byref(args), workspace, workspace_bytes, stream))
+
+
+def skvd_decode_partial(plan, args, workspace, workspace_bytes, stream) -> int:
+    return int(lib().skvd_decode_partial(plan, ctypes.byref(args), workspace, workspace_bytes,
+                                         stream))
+
+
+def skvd_decode_merge(plan, args, workspace, workspace_bytes, stream) -> int:
+    return int(lib().skvd_decode_merge(plan, ctypes.byref(args), workspace, workspace_bytes,
+                                       stream))
+
+
+def skvd_gather_debug(plan, args, max_len, dk, dv, dks, dvs, stream) -> int:
+    return int(lib().skvd_gather_debug(plan, ctypes.byref(args), max_len, dk, dv, dks, dvs,
+                                       stream))
+
+
+# ---------------------------------------------------------------- torch-facing plan
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+class Plan:
+    """A decode plan and its workspace.
+
+    Plan(num_qo_heads, num_kv_heads, head_dim, page_size, kv_dtype, max_batch, max_q_per_seq,
+         max_kv_len, device) sizes everything once, outside any capture; run() then launches
+    the decode on the current stream with no allocation other than the default outputs.
+    kv_dtype is "f16" or "i8" (int8 with one f16 scale per 32 elements)."""
+
+    def __init__(self, num_qo_heads, num_kv_heads, head_dim, page_size, kv_dtype="f16",
+                 max_batch=1, max_q_per_seq=1, max_kv_len=1, device=0, num_cus=0,
+                 force_blocks_per_split=0, force_reducer="auto", debug=False):
+        dev = torch.device("cuda", device) if isinstance(device, int) else torch.device(device)
+        self.device = dev
+        idx = dev.index if dev.index is not None else torch.cuda.current_device()
+        red = REDUCERS[force_reducer] if isinstance(force_reducer, str) else int(force_reducer)
+        self.params = skvd_plan_params(
+            int(num_qo_heads), int(num_kv_heads), int(head_dim), int(page_size), int(max_batch),
+            int(max_q_per_seq), int(max_kv_len),
+            SKVD_KV_F16 if kv_dtype in ("f16", torch.float16) else SKVD_KV_I8_F16SCALE32,
+            int(idx), int(num_cus), int(force_blocks_per_split), red, int(bool(debug)))
+        self.kv_dtype = "f16" if self.params.kv_dtype == SKVD_KV_F16 else "i8"
+        self.handle = skvd_plan_create(self.params)
+        self.info = skvd_plan_get_info(self.handle)
+        self.workspace_bytes = int(self.info.workspace_bytes)
+        self.workspace = None
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h:
+            try:
+                skvd_plan_destroy(h)
+            except Exception:
+                pass
+            self.handle = None
+
+    def describe(self) -> str:
+        return skvd_plan_describe(self.handle)
+
+    @property
+    def reducer(self) -> str:
+        return REDUCER_NAMES[self.info.reducer]
+
+    def ensure_workspace(self):
+        """Allocate the workspace (once; call it outside graph capture)."""
+        if self.workspace is None:
+            self.workspace = torch.zeros(self.workspace_bytes + 256, dtype=torch.uint8,
+                                         device=self.device)
+            off = (-self.workspace.data_ptr()) % 256
+            self.workspace = self.workspace[off:off + self.workspace_bytes]
+        return self.workspace
+
+    def status_word(self) -> int:
+        """Debug status bits recorded by the kernels (reads device memory: synchronizes)."""
+        ws = self.ensure_workspace()
+        o = int(self.info.status_offset)
+        return int(ws[o:o + 4].view(torch.int32).item())
+
+    def clear_status(self):
+        ws = self.ensure_workspace()
+        o = int(self.info.status_offset)
+        ws[o:o + 4].zero_()
+
+    def make_args(self, q, k_pages, v_pages, page_table, kv_len, sm_scale, k_scales=None,
+                  v_scales=None, out=None, lse=None, q_per_seq=1) -> skvd_decode_args:
+        if q.dtype != torch.float16:
+            raise TypeError("q must be float16")
+        want = torch.float16 if self.kv_dtype == "f16" else torch.int8
+        if k_pages.dtype != want or v_pages.dtype != want:
+            raise TypeError(f"k_pages and v_pages must be {want}")
+        if k_pages.stride() != v_pages.stride() or k_pages.shape[1:] != v_pages.shape[1:]:
+            raise SkvdError(3, "Plan.run", "K and V must share page shape and strides")
+        if page_table.dtype != torch.int32 or kv_len.dtype != torch.int32:
+            raise TypeError("page_table and kv_len must be int32")
+        if page_table.dim() != 2 or page_table.stride(1) != 1:
+            raise SkvdError(3, "Plan.run", "page_table must be [B, n] with unit inner stride")
+        if q.dim() != 3 or k_pages.dim() != 4:
+            raise SkvdError(2, "Plan.run", "q must be [B*T, Hq, D] and pools [pages, P, Hkv, D]")
+        if q.stride(2) != 1 or k_pages.stride(3) != 1:
+            raise SkvdError(3, "Plan.run", "head_dim must be dense in q and the pools")
+        B = int(kv_len.shape[0])
+        a = skvd_decode_args()
+        a.q = q.data_ptr()
+        a.q_tok_stride, a.q_head_stride = q.stride(0), q.stride(1)
+        a.k_pages, a.v_pages = k_pages.data_ptr(), v_pages.data_ptr()
+        a.page_stride, a.tok_stride, a.head_stride = k_pages.stride(0), k_pages.stride(1), k_pages.stride(2)
+        a.num_k_pages, a.num_v_pages = k_pages.shape[0], v_pages.shape[0]
+        if k_scales is not None:
+            if k_scales.dtype != torch.float16 or v_scales is None or v_scales.stride() != k_scales.stride():
+                raise SkvdError(4, "Plan.run", "k_scales/v_scales must be f16 with equal strides")
+            a.k_scales, a.v_scales = k_scales.data_ptr(), v_scales.data_ptr()
+            a.scale_page_stride, a.scale_tok_stride, a.scale_head_stride = (
+                k_scales.stride(0), k_scales.stride(1), k_scales.stride(2))
+        elif v_scales is not None:
+            raise SkvdError(4, "Plan.run", "v_scales given without k_scales")
+        a.page_table = page_table.data_ptr()
+        a.table_stride = page_table.stride(0)
+        a.kv_len = kv_len.data_ptr()
+        a.batch, a.q_per_seq = B, int(q_per_seq)
+        a.sm_scale = float(sm_scale)
+        a.reserved = 0
+        a.o = _ptr(out)
+        a.lse = _ptr(lse)
+        return a
+
+    def _outputs(self, q, out, lse):
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float16, device=q.device)  # dense
+        if lse is None:
+            lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+        if not out.is_contiguous() or (lse is not None and not lse.is_contiguous()):
+            raise SkvdError(3, "Plan.run", "o and lse are written densely: pass contiguous tensors")
+        return out, lse
+
+    def _stream(self, stream):
+        s = stream if stream is not None else torch.cuda.current_stream(self.device)
+        return s.cuda_stream
+
+    def run(self, q, k_pages, v_pages, page_table, kv_len, sm_scale, k_scales=None,
+            v_scales=None, out=None, lse=None, q_per_seq=1, stream=None, stage="all"):
+        """Decode. q [B*T, Hq, D] f16 (token and head strides free, D dense); pools
+        [pages, P, Hkv, D]; page_table [B, n] int32; kv_len [B] int32 on the device.
+        Returns (o [B*T, Hq, D] f16 dense, lse [B*T, Hq] f32). stage: "all", "partial" or
+        "merge" (the two halves of one decode, for timing)."""
+        out, lse = self._outputs(q, out, lse)
+        ws = self.ensure_workspace()
+        a = self.make_args(q, k_pages, v_pages, page_table, kv_len, sm_scale, k_scales, v_scales,
+                           out, lse, q_per_seq)
+        fn = {"all": skvd_decode, "partial": skvd_decode_partial, "merge": skvd_decode_merge}[stage]
+        _check(fn(self.handle, a, ws.data_ptr(), self.workspace_bytes, self._stream(stream)),
+               f"skvd_decode[{stage}]")
+        return out, lse
+
+    def check(self, q, k_pages, v_pages, page_table, kv_len, sm_scale, k_scales=None,
+              v_scales=None, out=None, lse=None, q_per_seq=1, workspace_bytes=None) -> int:
+        """skvd_decode_check: the validation alone, no HIP call. Returns the status."""
+        a = self.make_args(q, k_pages, v_pages, page_table, kv_len, sm_scale, k_scales, v_scales,
+                           out, lse, q_per_seq)
+        return skvd_decode_check(self.handle, a, self.workspace_bytes if workspace_bytes is None
+                                 else workspace_bytes)
+
+    def gather_debug(self, q, k_pages, v_pages, page_table, kv_len, max_len, k_scales=None,
+                     v_scales=None, q_per_seq=1, stream=None):
+        """skvd_gather_debug: dense raw copies of the visible K/V rows (zeros elsewhere)."""
+        B = int(kv_len.shape[0])
+        Hkv, D = k_pages.shape[2], k_pages.shape[3]
+        dk = torch.zeros((B, max_len, Hkv, D), dtype=k_pages.dtype, device=k_pages.device)
+        dv = torch.zeros_like(dk)
+        dks = dvs = None
+        if k_scales is not None:
+            dks = torch.zeros((B, max_len, Hkv, D // 32), dtype=torch.float16, device=k_pages.device)
+            dvs = torch.zeros_like(dks)
+        o = torch.empty(q.shape, dtype=torch.float16, device=q.device)
+        a = self.make_args(q, k_pages, v_pages, page_table, kv_len, 1.0, k_scales, v_scales, o,
+                           None, q_per_seq)
+        _check(skvd_gather_debug(self.handle, a, int(max_len), dk.data_ptr(), dv.data_ptr(),
+                                 _ptr(dks), _ptr(dvs), self._stream(stream)), "skvd_gather_debug")
+        return dk, dv, dks, dvs
+
+
+def skvd_abi_version_py() -> int:
+    return int(lib().skvd_abi_version())

@@ -1,0 +1,246 @@
+// Host-only planning and validation: no HIP calls in this file.
+//
+// The plan fixes, from static shape bounds, everything a launch needs: the 64-token partial
+// block (1bit-MONSTER/engine issue #115, comment "Closing the remaining half of this issue":
+// key_value_capacity = ceil_div(kv_len, 64) * 64), how many blocks one split covers, the
+// partial stride (from the capacity at max_kv_len, while the loop bounds stay runtime values
+// read from kv_len on the device: the same issue, comments "Deep-context decode failures
+// were JIT SGPR exhaustion" and "Residual >2048 fault root-caused and fixed"), the reducer,
+// and the exact workspace layout, so that a decode call allocates nothing (llama-cpp-
+// turboquant PR #176, problem statement: allocation inside a captured stream fails).
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "skvd_internal.h"
+
+namespace skvd {
+
+static skvd_status fail(char *err, size_t n, skvd_status st, const char *fmt, ...) {
+  if (err && n) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(err, n, fmt, ap);
+    va_end(ap);
+  }
+  return st;
+}
+
+static size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+const char *reducer_name(int r) {
+  switch (r) {
+    case SKVD_REDUCER_DIRECT: return "direct";
+    case SKVD_REDUCER_COOPERATIVE: return "cooperative";
+    case SKVD_REDUCER_MULTIPASS: return "multipass";
+    case SKVD_REDUCER_HIERARCHICAL: return "hierarchical";
+    case SKVD_REDUCER_NONE: return "none";
+    default: return "auto";
+  }
+}
+
+static bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char *err,
+                      size_t errn) {
+  const int Hq = prm.num_qo_heads, Hkv = prm.num_kv_heads, D = prm.head_dim;
+  if (Hkv < 1 || Hq < 1 || Hq % Hkv != 0)
+    return fail(err, errn, SKVD_ERR_SHAPE, "num_qo_heads=%d must be a positive multiple of "
+                "num_kv_heads=%d", Hq, Hkv);
+  if (D != 128 && D != 256)
+    return fail(err, errn, SKVD_ERR_SHAPE, "head_dim=%d unsupported (128 or 256)", D);
+  if (!is_pow2(prm.page_size) || prm.page_size > 1024)
+    return fail(err, errn, SKVD_ERR_SHAPE, "page_size=%d must be a power of two <= 1024",
+                prm.page_size);
+  if (prm.max_batch > 65535 || Hkv > 65535)
+    return fail(err, errn, SKVD_ERR_SHAPE, "max_batch=%d and num_kv_heads=%d must be <= 65535 "
+                "(grid dimensions)", prm.max_batch, Hkv);
+  if (prm.max_batch < 1 || prm.max_kv_len < 1)
+    return fail(err, errn, SKVD_ERR_SHAPE, "max_batch=%d and max_kv_len=%d must be >= 1",
+                prm.max_batch, prm.max_kv_len);
+  if (prm.max_q_per_seq < 1 || prm.max_q_per_seq > 8)
+    return fail(err, errn, SKVD_ERR_SHAPE, "max_q_per_seq=%d must be in 1..8",
+                prm.max_q_per_seq);
+  const int G = Hq / Hkv;
+  const int R = G * prm.max_q_per_seq;
+  if (R > 16)
+    return fail(err, errn, SKVD_ERR_SHAPE, "group*max_q_per_seq=%d exceeds 16 rows", R);
+  if (prm.kv_dtype != SKVD_KV_F16 && prm.kv_dtype != SKVD_KV_I8_F16SCALE32)
+    return fail(err, errn, SKVD_ERR_DTYPE, "kv_dtype=%d unknown", prm.kv_dtype);
+  if (num_cus < 1) return fail(err, errn, SKVD_ERR_DEVICE, "num_cus=%d", num_cus);
+  if (prm.force_reducer < 0 || prm.force_reducer > SKVD_REDUCER_NONE)
+    return fail(err, errn, SKVD_ERR_PLAN, "force_reducer=%d unknown", prm.force_reducer);
+  if (prm.force_blocks_per_split < 0)
+    return fail(err, errn, SKVD_ERR_PLAN, "force_blocks_per_split=%d",
+                prm.force_blocks_per_split);
+
+  Plan p{};
+  p.prm = prm;
+  p.group = G;
+  p.rows_per_wg = R;
+  p.row_blocks = R <= 4 ? 1 : (R <= 8 ? 2 : 4);
+  p.num_cus = num_cus;
+  p.max_blocks = (prm.max_kv_len + kBlockTokens - 1) / kBlockTokens;
+  p.rows_cap = (int64_t)prm.max_batch * prm.max_q_per_seq * Hq;
+
+  // Blocks per split. Two pressures: enough workgroups to fill the chip (about 16 per CU
+  // when every sequence is at max_kv_len), and partial traffic (one (m, l, D floats) per row
+  // and split, written then read back) at most ~3% of the split's K+V bytes.
+  const double row_bytes = prm.kv_dtype == SKVD_KV_F16 ? 4.0 * D : 2.0 * (D + 2 * (D / 32));
+  const double partial_bytes = 2.0 * R * (D + 2) * 4.0;
+  int bps_min = (int)std::ceil(partial_bytes / (0.03 * kBlockTokens * row_bytes));
+  if (bps_min < 1) bps_min = 1;
+  const int64_t units = (int64_t)prm.max_batch * Hkv * p.max_blocks;
+  int64_t bps = units / (16LL * num_cus);
+  if (bps < bps_min) bps = bps_min;
+  if (bps > 4LL * bps_min) bps = 4LL * bps_min;
+  if (p.max_blocks <= 4) bps = p.max_blocks;  // short contexts: one split, one launch
+  if (prm.force_blocks_per_split > 0) bps = prm.force_blocks_per_split;
+  if (bps > p.max_blocks) bps = p.max_blocks;
+  if (bps < 1) bps = 1;
+  p.bps = (int)bps;
+  p.splits_cap = (p.max_blocks + p.bps - 1) / p.bps;
+
+  // Reducer: total over every partial count.
+  int red = prm.force_reducer;
+  if (red == SKVD_REDUCER_AUTO) {
+    if (p.splits_cap == 1) red = SKVD_REDUCER_NONE;
+    else if (p.splits_cap <= 4) red = SKVD_REDUCER_DIRECT;
+    else if (p.splits_cap <= 64) red = SKVD_REDUCER_COOPERATIVE;
+    else if (p.rows_cap >= 2LL * num_cus) red = SKVD_REDUCER_MULTIPASS;
+    else red = SKVD_REDUCER_HIERARCHICAL;
+  }
+  if (red == SKVD_REDUCER_NONE && p.splits_cap != 1)
+    return fail(err, errn, SKVD_ERR_PLAN, "reducer none needs one split, plan has %d",
+                p.splits_cap);
+  if (red == SKVD_REDUCER_COOPERATIVE && p.splits_cap > 64)
+    return fail(err, errn, SKVD_ERR_PLAN, "cooperative reducer covers at most 64 partials, "
+                "plan has %d", p.splits_cap);
+  p.reducer = red;
+  p.hier_groups_cap = red == SKVD_REDUCER_HIERARCHICAL
+                          ? (p.splits_cap + kHierGroup - 1) / kHierGroup : 0;
+
+  // Workspace: status word, then partials (and hierarchical intermediates).
+  size_t off = 0;
+  p.off_status = off;
+  off = align_up(off + sizeof(uint32_t));
+  const size_t parts = red == SKVD_REDUCER_NONE ? 0 : (size_t)p.rows_cap * p.splits_cap;
+  p.off_ml = off;
+  off = align_up(off + parts * 2 * sizeof(float));
+  p.off_o = off;
+  off = align_up(off + parts * (size_t)D * sizeof(float));
+  const size_t hparts = (size_t)p.rows_cap * p.hier_groups_cap;
+  p.off_hml = off;
+  off = align_up(off + hparts * 2 * sizeof(float));
+  p.off_ho = off;
+  off = align_up(off + hparts * (size_t)D * sizeof(float));
+  p.ws_bytes = off;
+  *out = p;
+  return SKVD_OK;
+}
+
+static bool aligned(const void *ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+skvd_status check_args(const Plan &p, const skvd_decode_args *a, size_t ws_bytes, char *err,
+                       size_t errn) {
+  if (!a) return fail(err, errn, SKVD_ERR_NULL, "args is NULL");
+  const int D = p.prm.head_dim;
+  const bool i8 = p.prm.kv_dtype == SKVD_KV_I8_F16SCALE32;
+  if (a->reserved != 0) return fail(err, errn, SKVD_ERR_SHAPE, "reserved must be 0");
+  if (a->batch < 0 || a->batch > p.prm.max_batch)
+    return fail(err, errn, SKVD_ERR_SHAPE, "batch=%d outside 0..max_batch=%d", a->batch,
+                p.prm.max_batch);
+  if (a->q_per_seq < 1 || a->q_per_seq > p.prm.max_q_per_seq)
+    return fail(err, errn, SKVD_ERR_SHAPE, "q_per_seq=%d outside 1..max_q_per_seq=%d",
+                a->q_per_seq, p.prm.max_q_per_seq);
+  if (!a->q || !a->k_pages || !a->v_pages || !a->page_table || !a->kv_len || !a->o)
+    return fail(err, errn, SKVD_ERR_NULL, "q, k_pages, v_pages, page_table, kv_len and o "
+                "must be non-NULL");
+  if (i8 && (!a->k_scales || !a->v_scales))
+    return fail(err, errn, SKVD_ERR_DTYPE, "int8 cache needs k_scales and v_scales");
+  if (!i8 && (a->k_scales || a->v_scales))
+    return fail(err, errn, SKVD_ERR_DTYPE, "f16 cache takes no scales");
+  if (!std::isfinite(a->sm_scale))
+    return fail(err, errn, SKVD_ERR_SHAPE, "sm_scale is not finite");
+  // Vector loads: 16 bytes of q, o and f16 K/V rows; 8 bytes of int8 K/V rows.
+  const int64_t kv_vec = i8 ? 8 : 8;  // elements per vector load (16 B f16, 8 B int8)
+  if (!aligned(a->q, 16) || a->q_tok_stride % 8 || a->q_head_stride % 8 || a->q_tok_stride < 0 ||
+      a->q_head_stride < 0)
+    return fail(err, errn, SKVD_ERR_LAYOUT, "q must be 16-byte aligned with token/head "
+                "strides that are non-negative multiples of 8 elements");
+  if (!aligned(a->k_pages, i8 ? 8 : 16) || !aligned(a->v_pages, i8 ? 8 : 16) ||
+      a->page_stride % kv_vec || a->tok_stride % kv_vec || a->head_stride % kv_vec ||
+      a->page_stride < 0 || a->tok_stride < 0 || a->head_stride < 0)
+    return fail(err, errn, SKVD_ERR_LAYOUT, "K/V pools must be aligned to their vector load "
+                "and have page/token/head strides that are non-negative multiples of 8 "
+                "elements (head_dim dense, same strides for K and V)");
+  if (i8 && (!aligned(a->k_scales, 2) || !aligned(a->v_scales, 2) || a->scale_page_stride < 0 ||
+             a->scale_tok_stride < 0 || a->scale_head_stride < 0))
+    return fail(err, errn, SKVD_ERR_LAYOUT, "scale pools must be 2-byte aligned with "
+                "non-negative strides");
+  if (a->num_k_pages < 1 || a->num_v_pages < 1)
+    return fail(err, errn, SKVD_ERR_SHAPE, "num_k_pages and num_v_pages must be >= 1");
+  const int64_t need_pages = (p.prm.max_kv_len + p.prm.page_size - 1) / p.prm.page_size;
+  if (a->table_stride < need_pages)
+    return fail(err, errn, SKVD_ERR_LAYOUT, "table_stride=%lld below ceil(max_kv_len/P)=%lld",
+                (long long)a->table_stride, (long long)need_pages);
+  if (!aligned(a->o, 16)) return fail(err, errn, SKVD_ERR_LAYOUT, "o must be 16-byte aligned");
+  if (a->lse && !aligned(a->lse, 4))
+    return fail(err, errn, SKVD_ERR_LAYOUT, "lse must be 4-byte aligned");
+  if (ws_bytes < p.ws_bytes)
+    return fail(err, errn, SKVD_ERR_WORKSPACE, "workspace of %zu bytes below the plan's %zu",
+                ws_bytes, p.ws_bytes);
+  (void)D;
+  return SKVD_OK;
+}
+
+void fill_launch_args(const Plan &p, const skvd_decode_args &a, void *ws, LaunchArgs *la) {
+  LaunchArgs l{};
+  l.q = a.q;
+  l.q_tok_stride = a.q_tok_stride;
+  l.q_head_stride = a.q_head_stride;
+  l.k = a.k_pages;
+  l.v = a.v_pages;
+  l.page_stride = a.page_stride;
+  l.tok_stride = a.tok_stride;
+  l.head_stride = a.head_stride;
+  l.num_k_pages = a.num_k_pages;
+  l.num_v_pages = a.num_v_pages;
+  l.ks = a.k_scales;
+  l.vs = a.v_scales;
+  l.s_page_stride = a.scale_page_stride;
+  l.s_tok_stride = a.scale_tok_stride;
+  l.s_head_stride = a.scale_head_stride;
+  l.table = a.page_table;
+  l.table_stride = a.table_stride;
+  l.kv_len = a.kv_len;
+  l.batch = a.batch;
+  l.T = a.q_per_seq;
+  l.Hq = p.prm.num_qo_heads;
+  l.Hkv = p.prm.num_kv_heads;
+  l.G = p.group;
+  l.D = p.prm.head_dim;
+  int sh = 0;
+  while ((1 << sh) < p.prm.page_size) ++sh;
+  l.page_shift = sh;
+  l.scale_log2 = a.sm_scale * 1.4426950408889634f;
+  l.bps = p.bps;
+  l.splits_cap = p.splits_cap;
+  l.max_kv_len = p.prm.max_kv_len;
+  l.hier_groups_cap = p.hier_groups_cap;
+  l.int8 = p.prm.kv_dtype == SKVD_KV_I8_F16SCALE32;
+  l.debug = p.prm.debug;
+  char *w = (char *)ws;
+  l.status = w ? (unsigned *)(w + p.off_status) : nullptr;
+  l.ws_ml = w ? (float *)(w + p.off_ml) : nullptr;
+  l.ws_o = w ? (float *)(w + p.off_o) : nullptr;
+  l.ws_hml = w ? (float *)(w + p.off_hml) : nullptr;
+  l.ws_ho = w ? (float *)(w + p.off_ho) : nullptr;
+  l.o = a.o;
+  l.lse = a.lse;
+  l.single = p.reducer == SKVD_REDUCER_NONE;
+  *la = l;
+}
+
+}  // namespace skvd

@@ -1,0 +1,70 @@
+// Internal declarations shared by the host runtime (plan, validation, launch sequencing)
+// and the HIP kernels. Not part of the ABI.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/skvd.h"
+
+namespace skvd {
+
+constexpr int kBlockTokens = 64;  // one partial block: 64 consecutive KV positions
+constexpr int kHierGroup = 64;    // partials merged by one first-level hierarchical workgroup
+constexpr size_t kAlign = 256;
+
+struct Plan {
+  skvd_plan_params prm;
+  int group;          // G = Hq / Hkv
+  int rows_per_wg;    // G * max_q_per_seq
+  int row_blocks;     // ceil(rows_per_wg / 4): 16x16 MFMA row quarters in use (1, 2 or 4)
+  int num_cus;
+  int max_blocks;     // ceil(max_kv_len / 64)
+  int bps;            // 64-token blocks per split
+  int splits_cap;     // ceil(max_blocks / bps): partial stride per row
+  int reducer;        // resolved skvd_reducer
+  int hier_groups_cap;
+  int64_t rows_cap;
+  size_t off_status, off_ml, off_o, off_hml, off_ho, ws_bytes;
+};
+
+// Everything a kernel launch needs, resolved on the host from the plan and the args.
+struct LaunchArgs {
+  const void *q;
+  int64_t q_tok_stride, q_head_stride;
+  const void *k, *v;
+  int64_t page_stride, tok_stride, head_stride;
+  int64_t num_k_pages, num_v_pages;
+  const void *ks, *vs;
+  int64_t s_page_stride, s_tok_stride, s_head_stride;
+  const int32_t *table;
+  int64_t table_stride;
+  const int32_t *kv_len;
+  int batch, T, Hq, Hkv, G, D, page_shift;
+  float scale_log2;  // sm_scale * log2(e): scores are kept in base 2
+  int bps, splits_cap, max_kv_len, hier_groups_cap;
+  int int8, debug;
+  float *ws_ml;      // [rows_cap][splits_cap][2]  (max in log2 units, sum)
+  float *ws_o;       // [rows_cap][splits_cap][D]  unnormalized f32 output
+  float *ws_hml;     // [rows_cap][hier_groups_cap][2]
+  float *ws_ho;      // [rows_cap][hier_groups_cap][D]
+  unsigned *status;
+  void *o;
+  float *lse;
+  int single;        // the partial kernel writes o/lse (reducer NONE)
+};
+
+// plan.cpp (pure host)
+skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char *err, size_t errn);
+skvd_status check_args(const Plan &p, const skvd_decode_args *a, size_t ws_bytes, char *err,
+                       size_t errn);
+const char *reducer_name(int r);
+void fill_launch_args(const Plan &p, const skvd_decode_args &a, void *ws, LaunchArgs *la);
+
+// kernels.hip (return a hipError_t as int; 0 = success)
+int launch_partial(const Plan &p, const LaunchArgs &la, void *stream);
+int launch_merge(const Plan &p, const LaunchArgs &la, void *stream);
+int launch_gather(const Plan &p, const LaunchArgs &la, int max_len, void *dk, void *dv, void *dks,
+                  void *dvs, void *stream);
+
+}  // namespace skvd

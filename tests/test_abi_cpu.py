@@ -1,0 +1,165 @@
+"""The C ABI on the CPU: the library loads and exports every declared symbol, plans resolve
+as specified, and every host-checkable error path returns its status without any HIP call
+(skvd_decode_check and plan creation with an explicit CU count touch no GPU)."""
+import math
+import os
+import re
+
+import pytest
+
+import quantized_kv_cache_page_amd as skvd
+from quantized_kv_cache_page_amd import _binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    txt = open(os.path.join(ROOT, "include", "skvd.h")).read()
+    return sorted(set(re.findall(r"^\S[^\n(]*?\b(skvd_\w+)\(", txt, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    L = skvd.lib()
+    syms = declared_symbols()
+    assert len(syms) >= 12
+    for s in syms:
+        assert hasattr(L, s), s
+    assert set(syms) == set(bd.SIGNATURES), set(syms) ^ set(bd.SIGNATURES)
+    assert L.skvd_abi_version() == 1
+
+
+def plan(**kw):
+    base = dict(num_qo_heads=32, num_kv_heads=8, head_dim=128, page_size=16, kv_dtype="f16",
+                max_batch=32, max_q_per_seq=1, max_kv_len=4096, device=0, num_cus=256)
+    base.update(kw)
+    return skvd.Plan(**base)
+
+
+def test_golden_capacity_blocks():
+    """Forced one block per split, the partial count is the page's capacity / 64."""
+    path = os.path.join(ROOT, "tests", "golden", "capacity_blocks.txt")
+    for ln in open(path):
+        if ln.startswith("#") or not ln.strip():
+            continue
+        n, cap, blocks = map(int, ln.split())
+        assert cap == -(-n // 64) * 64 and blocks == cap // 64
+        p = plan(max_batch=1, max_kv_len=n, force_blocks_per_split=1, force_reducer="multipass")
+        assert p.info.splits_cap == blocks
+
+
+@pytest.mark.parametrize("maxlen", [1, 63, 64, 65, 256, 257, 2047, 2048, 2049, 4096, 4864,
+                                    131072, 262144, 262208])
+@pytest.mark.parametrize("bps", [0, 1, 3, 8])
+def test_plan_splits_and_total_reducer(maxlen, bps):
+    p = plan(max_kv_len=maxlen, force_blocks_per_split=bps)
+    i = p.info
+    blocks = -(-maxlen // 64)
+    assert 1 <= i.blocks_per_split <= blocks
+    if bps:
+        assert i.blocks_per_split == min(bps, blocks)
+    assert i.splits_cap == -(-blocks // i.blocks_per_split)
+    # the reducer choice is total: every partial count has one
+    assert p.reducer in ("none", "direct", "cooperative", "multipass", "hierarchical")
+    if i.splits_cap == 1:
+        assert p.reducer == "none"
+    if p.reducer == "cooperative":
+        assert i.splits_cap <= 64
+    if p.reducer == "hierarchical":
+        assert i.hier_groups_cap == -(-i.splits_cap // 64)
+    # workspace holds the status word plus (m, l, D floats) per row and split
+    rows = 32 * 1 * 32
+    need = 0 if p.reducer == "none" else rows * i.splits_cap * (2 + 128) * 4
+    assert i.workspace_bytes >= need + 4
+
+
+@pytest.mark.parametrize("red", ["direct", "multipass", "hierarchical"])
+def test_forced_reducers_cover_any_count(red):
+    p = plan(max_kv_len=262208, force_blocks_per_split=1, force_reducer=red)
+    assert p.info.splits_cap == 4097 and p.reducer == red
+
+
+def test_heuristic_configs():
+    """The workloads' plans: one split for 256 tokens; no 2048/32-block ceiling anywhere."""
+    c1 = plan(num_qo_heads=8, num_kv_heads=8, max_batch=1, max_kv_len=256)
+    assert c1.reducer == "none"
+    c3 = plan(max_batch=1, page_size=64, max_kv_len=131072)
+    assert c3.info.splits_cap > 64 and c3.reducer in ("multipass", "hierarchical")
+    for p in (plan(), c3, plan(num_kv_heads=16, head_dim=256, max_batch=8, max_q_per_seq=4,
+                               max_kv_len=32768), plan(kv_dtype="i8", max_batch=64,
+                                                       max_kv_len=65536)):
+        i = p.info
+        assert i.blocks_per_split * 64 * i.splits_cap >= p.params.max_kv_len
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=64), 2), (dict(num_qo_heads=30), 2), (dict(page_size=24), 2),
+    (dict(max_q_per_seq=9), 2), (dict(max_q_per_seq=8, num_qo_heads=32, num_kv_heads=8), 2),
+    (dict(max_batch=0), 2), (dict(max_kv_len=0), 2), (dict(kv_dtype=7), 4),
+    (dict(force_reducer="cooperative", max_kv_len=131072, max_batch=1, force_blocks_per_split=1), 7),
+    (dict(force_reducer="none", max_kv_len=4096), 7),
+])
+def test_plan_errors(kw, status):
+    with pytest.raises(skvd.SkvdError) as e:
+        if kw.get("kv_dtype") == 7:
+            prm = bd.skvd_plan_params(32, 8, 128, 16, 32, 1, 4096, 7, 0, 256, 0, 0, 0)
+            bd.skvd_plan_create(prm)
+        else:
+            plan(**kw)
+    assert e.value.status == status
+    assert skvd.last_error()
+
+
+FAKE = 1 << 40  # an aligned address; skvd_decode_check never dereferences it
+
+
+def good_args(p, i8=False, **over):
+    a = bd.skvd_decode_args()
+    a.q, a.q_tok_stride, a.q_head_stride = FAKE, 32 * 128, 128
+    a.k_pages, a.v_pages = FAKE, FAKE + (1 << 30)
+    a.page_stride, a.tok_stride, a.head_stride = 16 * 8 * 128, 8 * 128, 128
+    a.num_k_pages = a.num_v_pages = 100
+    if i8:
+        a.k_scales, a.v_scales = FAKE + (2 << 30), FAKE + (3 << 30)
+        a.scale_page_stride, a.scale_tok_stride, a.scale_head_stride = 16 * 8 * 4, 8 * 4, 4
+    a.page_table, a.table_stride, a.kv_len = FAKE, 256, FAKE
+    a.batch, a.q_per_seq, a.sm_scale = 32, 1, 1 / math.sqrt(128)
+    a.o, a.lse = FAKE, FAKE
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("over,status", [
+    ({}, 0), (dict(lse=None), 0), (dict(batch=0), 0),
+    (dict(q=None), 1), (dict(o=None), 1), (dict(kv_len=None), 1), (dict(page_table=None), 1),
+    (dict(batch=33), 2), (dict(batch=-1), 2), (dict(q_per_seq=2), 2), (dict(q_per_seq=0), 2),
+    (dict(sm_scale=float("nan")), 2), (dict(reserved=1), 2), (dict(num_v_pages=0), 2),
+    (dict(q=FAKE + 2), 3), (dict(q_head_stride=100), 3), (dict(tok_stride=1020), 3),
+    (dict(k_pages=FAKE + 8), 3), (dict(table_stride=255), 3), (dict(o=FAKE + 4), 3),
+    (dict(page_stride=-8), 3),
+    (dict(k_scales=FAKE), 4),
+])
+def test_decode_check_f16(over, status):
+    p = plan()
+    assert bd.skvd_decode_check(p.handle, good_args(p, **over), p.workspace_bytes) == status
+
+
+@pytest.mark.parametrize("over,status", [
+    ({}, 0), (dict(k_scales=None), 4), (dict(v_scales=None), 4), (dict(k_pages=FAKE + 8), 0),
+    (dict(k_pages=FAKE + 4), 3), (dict(k_scales=FAKE + 1), 3),
+])
+def test_decode_check_int8(over, status):
+    p = plan(kv_dtype="i8")
+    assert bd.skvd_decode_check(p.handle, good_args(p, i8=True, **over), p.workspace_bytes) == status
+
+
+def test_workspace_too_small():
+    p = plan()
+    assert bd.skvd_decode_check(p.handle, good_args(p), p.workspace_bytes - 1) == 5
+    assert "workspace" in skvd.last_error()
+
+
+def test_status_strings():
+    for s in range(9):
+        assert skvd.status_string(s)
+    assert skvd.status_string(0) == "ok"

@@ -1,0 +1,319 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle on seeded inputs.
+
+Small and mid-size problems are compared on every output; the full-size workloads on sampled
+rows. Tolerances: max|do| <= 2e-3, max|dlse| <= 1e-3; page gather bit-exact.
+"""
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.gpu_util import compare, make_plan, run, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import quantized_kv_cache_page_amd as skvd
+    skvd.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def spec(**kw):
+    return workloads.spec(**kw)
+
+
+def check(s, seed, plan_kw=None, rows=None, what=None):
+    prob = workloads.generate(s, seed)
+    what = what or f"{s.name} seed={seed} {plan_kw or ''}"
+    say(f"case {what}: B={s.batch} T={s.q_per_seq} Hq={s.num_qo_heads} Hkv={s.num_kv_heads} "
+        f"D={s.head_dim} P={s.page_size} kv={s.kv_dtype} L={list(prob['kv_len'])[:8]}")
+    dev = to_dev(prob)
+    plan = make_plan(prob, **(plan_kw or {}))
+    say(f"  {plan.describe()}")
+    o, lse = run(plan, prob, dev)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode(prob, rows=rows)
+    compare(o, lse, ro, rl, rows=rows, what=what)
+    return prob, dev, plan, o, lse
+
+
+# ------------------------------------------------------------------ small/mid shapes, all rows
+SMALL = [
+    # (name, batch, T, Hq, Hkv, D, P, kv, lens)
+    ("mha_one_tile", 1, 1, 8, 8, 128, 16, "f16", ("list", (256,))),
+    ("gqa4_ragged", 5, 1, 32, 8, 128, 16, "f16", ("list", (1, 63, 64, 65, 1000))),
+    ("gqa4_p1", 3, 1, 8, 2, 128, 1, "f16", ("list", (17, 130, 300))),
+    ("gqa4_p4", 3, 1, 8, 2, 128, 4, "f16", ("list", (5, 64, 257))),
+    ("gqa2_t4_d256", 3, 4, 8, 4, 256, 16, "f16", ("list", (4, 100, 700))),
+    ("gqa2_t4_d256_p2", 2, 4, 4, 2, 256, 2, "f16", ("list", (9, 333))),
+    ("mha_t2_d256", 2, 2, 4, 4, 256, 64, "f16", ("list", (2, 1500))),
+    ("gqa8_t2", 2, 2, 16, 2, 128, 16, "f16", ("list", (40, 900))),
+    ("int8_gqa4", 4, 1, 32, 8, 128, 16, "i8", ("list", (1, 65, 512, 2049))),
+    ("int8_p1", 2, 1, 8, 2, 128, 1, "i8", ("list", (33, 200))),
+    ("int8_t4_d256", 2, 4, 8, 4, 256, 16, "i8", ("list", (4, 600))),
+    ("int8_t3_g2", 2, 3, 4, 2, 128, 8, "i8", ("list", (3, 400))),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_all_rows(case):
+    name, B, T, Hq, Hkv, D, P, kv, lens = case
+    check(spec(name=name, batch=B, q_per_seq=T, num_qo_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+               page_size=P, kv_dtype=kv, lens=lens), seed=zlib.crc32(name.encode()) % 1000)
+
+
+@pytest.mark.parametrize("kv", ["f16", "i8"])
+@pytest.mark.parametrize("red,bps", [("direct", 1), ("cooperative", 1), ("multipass", 1),
+                                     ("hierarchical", 1), ("direct", 3), ("multipass", 7),
+                                     ("hierarchical", 2), ("none", 1000)])
+def test_forced_reducers_and_splits(kv, red, bps):
+    s = spec(name="forced", batch=3, q_per_seq=1, num_qo_heads=16, num_kv_heads=4, head_dim=128,
+             page_size=16, kv_dtype=kv, lens=("list", (70, 1300, 5000)))
+    if red == "cooperative":
+        s = spec(name="forced", batch=3, q_per_seq=1, num_qo_heads=16, num_kv_heads=4,
+                 head_dim=128, page_size=16, kv_dtype=kv, lens=("list", (70, 1300, 4000)))
+    check(s, seed=7, plan_kw=dict(force_reducer=red, force_blocks_per_split=bps))
+
+
+@pytest.mark.parametrize("L", [2047, 2048, 2049, 4095, 4096, 4097])
+def test_2048_4096_boundaries(L):
+    """Partial counts 32/33/64/65 around the pages' cooperative ceiling, at one block per
+    split, with every reducer that covers them."""
+    s = spec(name=f"boundary{L}", batch=2, q_per_seq=1, num_qo_heads=32, num_kv_heads=8,
+             head_dim=128, page_size=16, lens=("list", (L, L - 1000)))
+    for red in ("multipass", "hierarchical", "direct"):
+        check(s, seed=L, plan_kw=dict(force_blocks_per_split=1, force_reducer=red),
+              what=f"L={L} {red}")
+
+
+def test_no_ceiling_262208():
+    """One sequence of 262208 tokens = 4097 blocks, above the pages' 262144 cap."""
+    s = spec(name="beyond_cap", batch=1, q_per_seq=1, num_qo_heads=8, num_kv_heads=2,
+             head_dim=128, page_size=64, lens=("list", (262208,)))
+    rows = np.arange(8)
+    check(s, seed=11, plan_kw=dict(force_blocks_per_split=1, force_reducer="hierarchical"),
+          rows=rows)
+    check(s, seed=11, plan_kw=dict(force_blocks_per_split=1, force_reducer="multipass"),
+          rows=rows)
+
+
+def test_split_invariance():
+    """Same input, every split size and reducer: all within tolerance of the oracle and of
+    each other (LSE merge of partials = one-pass softmax)."""
+    s = spec(name="inv", batch=2, q_per_seq=2, num_qo_heads=8, num_kv_heads=4, head_dim=128,
+             page_size=16, lens=("list", (3000, 777)), q_mult=2.0)
+    outs = []
+    for bps, red in [(1, "multipass"), (2, "hierarchical"), (8, "cooperative"), (0, "auto"),
+                     (47, "direct"), (1000, "none")]:
+        _, _, _, o, lse = check(s, seed=3, plan_kw=dict(force_blocks_per_split=bps,
+                                                         force_reducer=red))
+        outs.append((o.float().cpu(), lse.cpu()))
+    for o, l in outs[1:]:
+        assert (o - outs[0][0]).abs().max().item() <= 2e-3
+        assert (l - outs[0][1]).abs().max().item() <= 1e-3
+
+
+def test_gather_bit_exact():
+    for kv, P in (("f16", 16), ("f16", 1), ("i8", 4), ("i8", 64)):
+        s = spec(name="gather", batch=3, q_per_seq=1, num_qo_heads=4, num_kv_heads=2,
+                 head_dim=128, page_size=P, kv_dtype=kv, lens=("list", (1, 190, 700)))
+        prob = workloads.generate(s, 5)
+        dev = to_dev(prob)
+        plan = make_plan(prob)
+        maxl = int(prob["kv_len"].max())
+        dk, dv, dks, dvs = plan.gather_debug(dev["q"], dev["k_pages"], dev["v_pages"],
+                                             dev["page_table"], dev["kv_len"], maxl,
+                                             dev["k_scales"], dev["v_scales"])
+        ok, ov, oks, ovs = oracle.gather(prob, maxl)
+        assert np.array_equal(dk.cpu().numpy().view(np.uint8), ok.view(np.uint8))
+        assert np.array_equal(dv.cpu().numpy().view(np.uint8), ov.view(np.uint8))
+        if kv == "i8":
+            assert np.array_equal(dks.cpu().numpy().view(np.uint16), oks.view(np.uint16))
+            assert np.array_equal(dvs.cpu().numpy().view(np.uint16), ovs.view(np.uint16))
+        say(f"  gather {kv} P={P}: bit-exact")
+
+
+def test_single_position_exact():
+    """kv_len 1: o is exactly the V row (weight 1), on the single-split and merged paths."""
+    for kw in (dict(), dict(force_blocks_per_split=1, force_reducer="multipass")):
+        s = spec(name="one", batch=3, q_per_seq=1, num_qo_heads=8, num_kv_heads=2, head_dim=128,
+                 page_size=16, lens=("list", (1, 1, 1)))
+        prob, dev, plan, o, lse = check(s, seed=9, plan_kw=kw)
+        v = prob["v_pages"]
+        for b in range(3):
+            pg = prob["page_table"][b, 0]
+            for h in range(8):
+                assert np.array_equal(o[b, h].cpu().numpy().view(np.uint16),
+                                      v[pg, 0, h // 4].view(np.uint16))
+
+
+def test_empty_sequence():
+    s = spec(name="empty", batch=3, q_per_seq=1, num_qo_heads=8, num_kv_heads=2, head_dim=128,
+             page_size=16, lens=("list", (0, 50, 0)))
+    for kw in (dict(max_kv_len=64), dict(force_blocks_per_split=1, force_reducer="cooperative")):
+        prob, dev, plan, o, lse = check(s, seed=2, plan_kw=kw)
+        assert torch.all(o[0] == 0) and torch.all(torch.isneginf(lse[0]))
+
+
+def test_strided_q_and_shorter_v_pool():
+    """q sliced from a fused QKV buffer (token stride > Hq*D) and a V pool with fewer pages
+    than K (only indexed pages are read)."""
+    s = spec(name="strided", batch=3, q_per_seq=1, num_qo_heads=16, num_kv_heads=4,
+             head_dim=128, page_size=16, lens=("list", (33, 500, 1200)), spare_frac=0.0)
+    prob = workloads.generate(s, 4)
+    ref_o, ref_l = oracle.decode(prob)
+    dev = to_dev(prob)
+    qkv = torch.zeros((3, 16 + 8, 128), dtype=torch.float16, device="cuda")
+    qkv[:, :16] = dev["q"]
+    dev["q"] = qkv[:, :16]
+    extra = torch.full((7,) + tuple(dev["k_pages"].shape[1:]), float("nan"),
+                       dtype=torch.float16, device="cuda")
+    dev["k_pages"] = torch.cat([dev["k_pages"], extra])  # K pool longer than V pool
+    plan = make_plan(prob)
+    o, lse = run(plan, prob, dev)
+    torch.cuda.synchronize()
+    compare(o, lse, ref_o, ref_l, what="strided q, unequal pools")
+
+
+def test_read_only_and_canaries():
+    """Inputs bit-identical after the call; nothing written outside o and lse."""
+    s = spec(name="ro", batch=4, q_per_seq=2, num_qo_heads=8, num_kv_heads=4, head_dim=128,
+             page_size=16, lens=("list", (5, 300, 2500, 64)))
+    prob = workloads.generate(s, 8)
+    dev = to_dev(prob)
+    before = {k: (v.clone() if v is not None else None) for k, v in dev.items()}
+    plan = make_plan(prob, force_blocks_per_split=2)
+    n = 8 * 8
+    canary = torch.full((n * 128 + 2 * 4096,), 12345.0, dtype=torch.float16, device="cuda")
+    out = canary[4096:4096 + n * 128].view(8, 8, 128)
+    lcan = torch.full((n + 2 * 64,), -7.0, dtype=torch.float32, device="cuda")
+    lse = lcan[64:64 + n].view(8, 8)
+    run(plan, prob, dev, out=out, lse=lse)
+    torch.cuda.synchronize()
+    for k, v in dev.items():
+        if v is not None:
+            assert torch.equal(v.view(torch.uint8) if v.dtype != torch.int32 else v,
+                               before[k].view(torch.uint8) if v.dtype != torch.int32 else before[k]), k
+    assert torch.all(canary[:4096] == 12345.0) and torch.all(canary[4096 + n * 128:] == 12345.0)
+    assert torch.all(lcan[:64] == -7.0) and torch.all(lcan[64 + n:] == -7.0)
+    ro, rl = oracle.decode(prob)
+    compare(out, lse, ro, rl, what="canaries")
+
+
+def test_deterministic():
+    s = spec(name="det", batch=4, q_per_seq=1, num_qo_heads=32, num_kv_heads=8, head_dim=128,
+             page_size=16, lens=("list", (100, 3000, 5000, 9000)))
+    prob = workloads.generate(s, 12)
+    dev = to_dev(prob)
+    plan = make_plan(prob)
+    o1, l1 = run(plan, prob, dev)
+    o1, l1 = o1.clone(), l1.clone()
+    for _ in range(3):
+        o2, l2 = run(plan, prob, dev)
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_debug_status_clamps():
+    """kv_len above max_kv_len and out-of-range page ids are clamped, flagged, never faulted."""
+    import quantized_kv_cache_page_amd as skvd
+    s = spec(name="dbg", batch=2, q_per_seq=1, num_qo_heads=8, num_kv_heads=2, head_dim=128,
+             page_size=16, lens=("list", (100, 200)))
+    prob = workloads.generate(s, 6)
+    dev = to_dev(prob)
+    plan = make_plan(prob, debug=True, max_kv_len=256)
+    plan.clear_status()
+    dev["kv_len"][1] = 100000  # above max_kv_len: clamped to 256
+    t = torch.full((2, 16), -1, dtype=torch.int32, device="cuda")
+    t[:, :dev["page_table"].shape[1]] = dev["page_table"]
+    t[0, 3] = 10 ** 6          # beyond the pool: clamped into it
+    dev["page_table"] = t
+    run(plan, prob, dev)
+    torch.cuda.synchronize()
+    st = plan.status_word()
+    assert st & skvd.STATUS_KV_LEN_CLAMPED and st & skvd.STATUS_PAGE_CLAMPED
+
+
+# ------------------------------------------------------------------ graph capture
+def test_graph_capture_replay():
+    """First call made under capture; replays equal the eager result bit for bit, with eager
+    work between replays; a new plan re-records at a new shape."""
+    for lens in ((700, 3000, 20), (64, 128, 4100)):
+        s = spec(name="graph", batch=3, q_per_seq=1, num_qo_heads=16, num_kv_heads=4,
+                 head_dim=128, page_size=16, lens=("list", lens))
+        prob = workloads.generate(s, 21)
+        dev = to_dev(prob)
+        plan = make_plan(prob)
+        plan.ensure_workspace()
+        out = torch.empty((3, 16, 128), dtype=torch.float16, device="cuda")
+        lse = torch.empty((3, 16), dtype=torch.float32, device="cuda")
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run(plan, prob, dev, out=out, lse=lse)
+        eo, el = run(plan, prob, dev)
+        torch.cuda.synchronize()
+        eo, el = eo.clone(), el.clone()
+        for i in range(4):
+            out.zero_()
+            lse.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int16), eo.view(torch.int16)), f"replay {i}"
+            assert torch.equal(lse, el)
+            _ = run(plan, prob, dev)  # eager work between replays
+        ro, rl = oracle.decode(prob)
+        compare(out, lse, ro, rl, what=f"graph {lens}")
+
+
+# ------------------------------------------------------------------ the workloads
+def sample_rows(prob, n, seed):
+    total = prob["q"].shape[0] * prob["q"].shape[1]
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([rng.choice(total, size=min(n, total), replace=False),
+                                     [0, total - 1]]))
+
+
+def test_config1_all_rows():
+    check(workloads.config(1), 1)
+
+
+def test_config2_all_rows():
+    check(workloads.config(2), 2)
+
+
+def test_config3_sampled():
+    prob = workloads.generate(workloads.config(3), 3)
+    check_full(prob, 3)
+
+
+def test_config4_sampled():
+    prob = workloads.generate(workloads.config(4), 4)
+    check_full(prob, 4)
+
+
+def test_config5_sampled():
+    prob = workloads.generate(workloads.config(5), 5)
+    check_full(prob, 5)
+
+
+def check_full(prob, cfg):
+    s = prob["spec"]
+    say(f"case config {cfg} ({s.name}): L={list(prob['kv_len'])[:8]}...")
+    dev = to_dev(prob)
+    plan = make_plan(prob, max_kv_len=s.max_kv_len)
+    say(f"  {plan.describe()}")
+    o, lse = run(plan, prob, dev)
+    torch.cuda.synchronize()
+    rows = sample_rows(prob, 96, cfg)
+    ro, rl = oracle.decode(prob, rows=rows)
+    compare(o, lse, ro, rl, rows=rows, what=f"config {cfg} sampled {len(rows)} rows")
+    # every row finite
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
