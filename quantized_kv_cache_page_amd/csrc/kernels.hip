@@ -264,23 +264,24 @@ __global__ __launch_bounds__(64) void partial_kernel(LaunchArgs a) {
     }
 
     // ---- scores: S[t] = rows x 16 tokens of tile t (lane: token c16, rows 4*g4 + e)
+    // The MFMA chains run for every tile, also the ones past the split (their K is zero and
+    // their scores are masked): a branch between an MFMA and the reads of its result let the
+    // compiler's wait-state insertion miss the taken path, which read a stale accumulator.
     float4v S[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       S[t] = (float4v)0.f;
-      if (c0 + 16 * t < tok_end) {
-        if constexpr (I8) {
+      if constexpr (I8) {
 #pragma unroll
-          for (int k = 0; k < KS; ++k) {
-            float4v part = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[k], i8x8_to_h8(kb[t][k]),
-                                                                  (float4v)0.f, 0, 0, 0);
-            S[t] += part * ks_tok[t][k];
-          }
-        } else {
-#pragma unroll
-          for (int k = 0; k < KS; ++k)
-            S[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[k], kb[t][k], S[t], 0, 0, 0);
+        for (int k = 0; k < KS; ++k) {
+          float4v part = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[k], i8x8_to_h8(kb[t][k]),
+                                                                (float4v)0.f, 0, 0, 0);
+          S[t] += part * ks_tok[t][k];
         }
+      } else {
+#pragma unroll
+        for (int k = 0; k < KS; ++k)
+          S[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[k], kb[t][k], S[t], 0, 0, 0);
       }
     }
 
