@@ -91,7 +91,20 @@ def main():
     ap.add_argument("--bps", type=int, default=0, help="force 64-token blocks per split")
     ap.add_argument("--reducer", default="auto")
     ap.add_argument("--copies", type=int, default=0, help="pool copies to rotate (0: auto)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB, 5 times (reference "
+                         "for scaling the HBM byte counters)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        n = args.calibrate_copy * 2 ** 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "repeats": 5}), flush=True)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (the decode "
               f"is single-GPU; the multi-GPU sharding is described, not built)", file=sys.stderr)

@@ -102,6 +102,14 @@ __device__ __forceinline__ float readlane_f(float x, int lane) {
 }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// LDS hand-off between the lanes of a one-wave workgroup: a wavefront-scope fence and wave
+// barrier order the LDS accesses without waiting on outstanding global loads.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // 8 signed bytes -> 8 f16 (exact).
 __device__ __forceinline__ half8 i8x8_to_h8(uint2v w) {
   half8 r;
@@ -198,75 +206,99 @@ __global__ __launch_bounds__(64) void partial_kernel(LaunchArgs a) {
   bool clamped_any = false;
   const int vlane_tok = lane / LPR, vlane_el = 8 * (lane % LPR);
 
-  for (int c0 = tok0; c0 < tok_end; c0 += CH) {
-    // ---- gather: K tiles (MFMA B operand layout) and V steps (P.V layout)
-    Vec kb[NT][KS];
-    float ks_tok[NT][KS];
-    Vec vb[NS];
-    float vs_tok[NS];
+  // Loads are branch-free: a token past the split is clamped to the split's last token
+  // (a re-read of lines already fetched, masked out of the softmax), so every load of a chunk
+  // is issued unconditionally and the in-order load counter can be waited on precisely.
+  // FAST: the page of each 16-token tile is wave-uniform; a chunk's page ids are read from the
+  // table through the constant address space (scalar loads, counted apart from the vector
+  // loads) one chunk ahead of their use.
+  const int last_tile = (tok_end - 1) & ~15;
+  typedef const __attribute__((address_space(4))) int32_t *ctable_t;
+  const ctable_t trow = (ctable_t)(a.table + (int64_t)b * a.table_stride);
+  auto chunk_pages = [&](int c0, int *pg) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) pg[t] = trow[min(c0 + 16 * t, last_tile) >> a.page_shift];
+  };
+  auto clamp_page = [&](int pg, int64_t npages) -> int64_t {
+    const bool bad = pg < 0 || pg >= npages;
+    clamped_any |= bad;
+    return bad ? (pg < 0 ? 0 : npages - 1) : (int64_t)pg;
+  };
+
+  Vec kb[NT][KS];
+  float ks_tok[NT][KS];
+  Vec vb[NS];
+  float vs_tok[NS];
+
+  // K rows of chunk c0 in the MFMA B-operand layout: tile t, lane (g4, c16) holds elements
+  // 32k + 8*g4 .. +7 of token 16t + c16.
+  auto load_k = [&](int c0, const int *pgs) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int jt = c0 + 16 * t;
-      if (jt < tok_end) {
-        const int j = min(jt + c16, tok_end - 1);
-        bool cl;
-        int64_t pg;
-        if (FAST) {
-          pg = lookup_page(a.table, a.table_stride, b, jt, a.page_shift, a.num_k_pages, &cl);
-        } else {
-          pg = lookup_page(a.table, a.table_stride, b, j, a.page_shift, a.num_k_pages, &cl);
-        }
-        clamped_any |= cl;
-        const int64_t off = row_offset(pg, j & P1, kvh, a.page_stride, a.tok_stride,
-                                       a.head_stride);
-        const char *kp = kbase + (off + 8 * g4) * ES;
-#pragma unroll
-        for (int k = 0; k < KS; ++k) kb[t][k] = *(const Vec *)(kp + 32 * k * ES);
-        if constexpr (I8) {
-          const int64_t so = row_offset(pg, j & P1, kvh, a.s_page_stride, a.s_tok_stride,
-                                        a.s_head_stride);
-#pragma unroll
-          for (int k = 0; k < KS; ++k) ks_tok[t][k] = (float)ksc[so + k];
-        }
+      const int j = min(jt + c16, tok_end - 1);
+      int64_t pg;
+      if constexpr (FAST) {
+        pg = clamp_page(pgs[t], a.num_k_pages);
       } else {
+        bool cl;
+        pg = lookup_page(a.table, a.table_stride, b, j, a.page_shift, a.num_k_pages, &cl);
+        clamped_any |= cl;
+      }
+      const int64_t off = row_offset(pg, j & P1, kvh, a.page_stride, a.tok_stride, a.head_stride);
+      const char *kp = kbase + (off + 8 * g4) * ES;
 #pragma unroll
-        for (int k = 0; k < KS; ++k) {
-          kb[t][k] = Vec{};
-          ks_tok[t][k] = 0.f;
-        }
+      for (int k = 0; k < KS; ++k) kb[t][k] = *(const Vec *)(kp + 32 * k * ES);
+      if constexpr (I8) {
+        const int64_t so = row_offset(pg, j & P1, kvh, a.s_page_stride, a.s_tok_stride,
+                                      a.s_head_stride);
+#pragma unroll
+        for (int k = 0; k < KS; ++k) ks_tok[t][k] = (float)ksc[so + k];
       }
     }
+  };
+  // V rows of chunk c0 in the P.V layout: step s, lane holds elements vlane_el .. +7 of
+  // token TPS*s + vlane_tok.
+  auto load_v = [&](int c0, const int *pgs) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const int js = c0 + TPS * s;
-      if (js < tok_end) {
-        const int j = min(js + vlane_tok, tok_end - 1);
-        bool cl;
-        int64_t pg;
-        if (FAST) {
-          pg = lookup_page(a.table, a.table_stride, b, js, a.page_shift, a.num_v_pages, &cl);
-        } else {
-          pg = lookup_page(a.table, a.table_stride, b, j, a.page_shift, a.num_v_pages, &cl);
-        }
-        clamped_any |= cl;
-        const int64_t off = row_offset(pg, j & P1, kvh, a.page_stride, a.tok_stride,
-                                       a.head_stride);
-        vb[s] = *(const Vec *)(vbase + (off + vlane_el) * ES);
-        if constexpr (I8) {
-          const int64_t so = row_offset(pg, j & P1, kvh, a.s_page_stride, a.s_tok_stride,
-                                        a.s_head_stride);
-          vs_tok[s] = (float)vsc[so + vlane_el / 32];
-        }
+    for (int s2 = 0; s2 < NS; ++s2) {
+      const int js = c0 + TPS * s2;
+      const int j = min(js + vlane_tok, tok_end - 1);
+      int64_t pg;
+      if constexpr (FAST) {
+        pg = clamp_page(pgs[(TPS * s2) >> 4], a.num_v_pages);
       } else {
-        vb[s] = Vec{};
-        vs_tok[s] = 0.f;
+        bool cl;
+        pg = lookup_page(a.table, a.table_stride, b, j, a.page_shift, a.num_v_pages, &cl);
+        clamped_any |= cl;
+      }
+      const int64_t off = row_offset(pg, j & P1, kvh, a.page_stride, a.tok_stride, a.head_stride);
+      vb[s2] = *(const Vec *)(vbase + (off + vlane_el) * ES);
+      if constexpr (I8) {
+        const int64_t so = row_offset(pg, j & P1, kvh, a.s_page_stride, a.s_tok_stride,
+                                      a.s_head_stride);
+        vs_tok[s2] = (float)vsc[so + vlane_el / 32];
       }
     }
+  };
 
+  int pg_cur[NT], pg_next[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) pg_cur[t] = pg_next[t] = 0;
+  if (tok0 < tok_end) {
+    if constexpr (FAST) chunk_pages(tok0, pg_cur);
+    load_k(tok0, pg_cur);
+    __builtin_amdgcn_sched_barrier(0);
+    load_v(tok0, pg_cur);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int c0 = tok0; c0 < tok_end; c0 += CH) {
+    const int c1 = c0 + CH;
+    if constexpr (FAST) chunk_pages(c1, pg_next);
     // ---- scores: S[t] = rows x 16 tokens of tile t (lane: token c16, rows 4*g4 + e)
-    // The MFMA chains run for every tile, also the ones past the split (their K is zero and
-    // their scores are masked): a branch between an MFMA and the reads of its result let the
-    // compiler's wait-state insertion miss the taken path, which read a stale accumulator.
+    // The MFMA chains run for every tile, also the ones past the split (their K is a clamped
+    // re-read and their scores are masked): a branch between an MFMA and the reads of its
+    // result let the compiler's wait-state insertion miss the taken path.
     float4v S[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -284,6 +316,11 @@ __global__ __launch_bounds__(64) void partial_kernel(LaunchArgs a) {
           S[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[k], kb[t][k], S[t], 0, 0, 0);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- prefetch the next chunk's K while this chunk's softmax and P.V run (past the end
+    // of the split this re-reads the last token: cached, and never used)
+    load_k(c1, pg_next);
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- mask, online softmax (base 2)
     float alpha[4];
@@ -293,9 +330,9 @@ __global__ __launch_bounds__(64) void partial_kernel(LaunchArgs a) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const int j = c0 + 16 * t + c16;
-        const float s = j < nvis[e] ? S[t][e] * a.scale_log2 : kNegInf;
-        S[t][e] = s;
-        cmax = fmaxf(cmax, s);
+        const float sc = j < nvis[e] ? S[t][e] * a.scale_log2 : kNegInf;
+        S[t][e] = sc;
+        cmax = fmaxf(cmax, sc);
       }
       cmax = row16_max(cmax);
       const float mnew = fmaxf(m[e], cmax);
@@ -318,7 +355,7 @@ __global__ __launch_bounds__(64) void partial_kernel(LaunchArgs a) {
     float al[RM];
 #pragma unroll
     for (int r = 0; r < RM; ++r) al[r] = readlane_f(alpha[r & 3], 16 * (r >> 2));
-    __syncthreads();
+    wave_sync();
 
     // ---- P.V
     bool rescale = false;
@@ -331,25 +368,31 @@ __global__ __launch_bounds__(64) void partial_kernel(LaunchArgs a) {
         for (int i = 0; i < 8; ++i) acc[r][i] *= al[r];
     }
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const int tk = TPS * s + vlane_tok;
+    for (int s2 = 0; s2 < NS; ++s2) {
+      const int tk = TPS * s2 + vlane_tok;
       float4v pr[RB];
 #pragma unroll
       for (int q = 0; q < RB; ++q) pr[q] = p_lds[tk][q];
       float v[8];
       if constexpr (I8) {
-        i8x8_to_f(vb[s], v);
+        i8x8_to_f(vb[s2], v);
 #pragma unroll
-        for (int q = 0; q < RB; ++q) pr[q] *= vs_tok[s];
+        for (int q = 0; q < RB; ++q) pr[q] *= vs_tok[s2];
       } else {
-        h8_to_f(vb[s], v);
+        h8_to_f(vb[s2], v);
       }
 #pragma unroll
       for (int r = 0; r < RM; ++r)
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[r][i] = fmaf(pr[r >> 2][r & 3], v[i], acc[r][i]);
     }
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- prefetch the next chunk's V while the next chunk's scores run
+    load_v(c1, pg_next);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) pg_cur[t] = pg_next[t];
+    wave_sync();
   }
   if (a.debug && clamped_any) atomicOr(a.status, (unsigned)SKVD_STATUS_PAGE_CLAMPED);
 
