@@ -91,6 +91,10 @@ def main():
     ap.add_argument("--bps", type=int, default=0, help="force 64-token blocks per split")
     ap.add_argument("--reducer", default="auto")
     ap.add_argument("--copies", type=int, default=0, help="pool copies to rotate (0: auto)")
+    ap.add_argument("--layout", choices=["nhd", "hnd"], default="nhd",
+                    help="pool layout: nhd = [pages, P, Hkv, D] (the workload's); hnd = each KV "
+                         "head's page rows contiguous, passed through the same strides")
+    ap.add_argument("--no-stream-ref", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB, 5 times (reference "
                          "for scaling the HBM byte counters)")
@@ -131,6 +135,9 @@ def main():
     table = up(prob["page_table"])
     kv_len = up(prob["kv_len"])
     pools = [up(prob[k]) for k in ("k_pages", "v_pages", "k_scales", "v_scales")]
+    if args.layout == "hnd":
+        pools = [None if p is None else p.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+                 for p in pools]
     pool_bytes = sum(p.numel() * p.element_size() for p in pools if p is not None)
     copies = args.copies or max(1, math.ceil(2 * MALL_BYTES / max(kvb, 1)) + 1)
     sets = [pools] + [[None if p is None else p.clone() for p in pools] for _ in range(copies - 1)]
@@ -186,9 +193,25 @@ def main():
     log(f"[bench] decode {ms_call * 1e3:.2f} us/call (staged {ms_step * 1e3:.2f}), partial "
         f"kernel avg {part_avg * 1e3:.2f} us (min {min(part_ms) * 1e3:.2f})")
 
+    stream_gbs = None
+    if not args.no_stream_ref:
+        # Reference: a plain streaming read (torch's sum over 2 GiB of f16) on the same GPU.
+        buf = torch.ones(2 ** 30, dtype=torch.float16, device=dev)
+        for _ in range(3):
+            buf.sum(dtype=torch.float32)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            buf.sum(dtype=torch.float32)
+        e1.record()
+        torch.cuda.synchronize()
+        stream_gbs = buf.numel() * 2 / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9
+        del buf
+        log(f"[bench] streaming-read reference: {stream_gbs:.0f} GB/s")
     gbs = kvb / (ms_call * 1e-3) / 1e9
     achieved = kvb / (part_avg * 1e-3) / 1e9
-    workload = (f"{spec.name} (config {args.config}): B={spec.batch} T={spec.q_per_seq} "
+    workload = (f"{spec.name} (config {args.config}, {args.layout.upper()} pools): B={spec.batch} T={spec.q_per_seq} "
                 f"Hq={spec.num_qo_heads} Hkv={spec.num_kv_heads} D={spec.head_dim} "
                 f"P={spec.page_size} kv={spec.kv_dtype} lens={spec.lens}")
     traffic = measured_traffic(spec.name)
@@ -203,6 +226,7 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "partial_kernel",
                      "kernel_avg_us": round(part_avg * 1e3, 3),
+                     "stream_read_ref_gbs": None if stream_gbs is None else round(stream_gbs, 1),
                      "algorithmic_bytes_per_launch": kvb},
         "cpu_baseline": None,
     }

@@ -138,9 +138,11 @@ __device__ __forceinline__ void i8x8_to_f(uint2v w, float *f) {
 // D: head_dim (128/256). RB: 4-row quarters of the 16 MFMA rows in use (rows = G*T <= 4*RB).
 // I8: int8 cache with f16 scales per 32 elements. FAST: page_size >= 16, so each 16-token
 // tile lies in one page and its page id is wave-uniform.
-template <int D, int RB, bool I8, bool FAST>
+template <int D, int RB, bool I8, bool FAST, int CH>
 __global__ __launch_bounds__(64) void partial_kernel(LaunchArgs a) {
-  constexpr int CH = 8192 / D;   // tokens per chunk (64 for D=128, 32 for D=256)
+  // CH: tokens per chunk (16, 32 or 64). The K and V registers of a chunk (CH*D*4 bytes per
+  // wave) bound how many waves fit on a SIMD; residency, not ALU work, sets the bandwidth.
+  static_assert(CH == 16 || CH == 32 || CH == 64, "chunk");
   constexpr int NT = CH / 16;    // 16-token MFMA tiles per chunk
   constexpr int KS = D / 32;     // MFMA contraction steps of 32 head_dim elements
   constexpr int LPR = D / 8;     // P.V lanes per V row, 8 elements each
@@ -215,11 +217,11 @@ __global__ __launch_bounds__(64) void partial_kernel(LaunchArgs a) {
   const int last_tile = (tok_end - 1) & ~15;
   typedef const __attribute__((address_space(4))) int32_t *ctable_t;
   const ctable_t trow = (ctable_t)(a.table + (int64_t)b * a.table_stride);
-  auto chunk_pages = [&](int c0, int *pg) {
+  auto chunk_pages = [&](int c0, int *pg) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) pg[t] = trow[min(c0 + 16 * t, last_tile) >> a.page_shift];
   };
-  auto clamp_page = [&](int pg, int64_t npages) -> int64_t {
+  auto clamp_page = [&](int pg, int64_t npages) __attribute__((always_inline)) -> int64_t {
     const bool bad = pg < 0 || pg >= npages;
     clamped_any |= bad;
     return bad ? (pg < 0 ? 0 : npages - 1) : (int64_t)pg;
@@ -232,7 +234,7 @@ __global__ __launch_bounds__(64) void partial_kernel(LaunchArgs a) {
 
   // K rows of chunk c0 in the MFMA B-operand layout: tile t, lane (g4, c16) holds elements
   // 32k + 8*g4 .. +7 of token 16t + c16.
-  auto load_k = [&](int c0, const int *pgs) {
+  auto load_k = [&](int c0, const int *pgs) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int jt = c0 + 16 * t;
@@ -259,7 +261,7 @@ __global__ __launch_bounds__(64) void partial_kernel(LaunchArgs a) {
   };
   // V rows of chunk c0 in the P.V layout: step s, lane holds elements vlane_el .. +7 of
   // token TPS*s + vlane_tok.
-  auto load_v = [&](int c0, const int *pgs) {
+  auto load_v = [&](int c0, const int *pgs) __attribute__((always_inline)) {
 #pragma unroll
     for (int s2 = 0; s2 < NS; ++s2) {
       const int js = c0 + TPS * s2;
@@ -292,7 +294,11 @@ __global__ __launch_bounds__(64) void partial_kernel(LaunchArgs a) {
     load_v(tok0, pg_cur);
     __builtin_amdgcn_sched_barrier(0);
   }
-  for (int c0 = tok0; c0 < tok_end; c0 += CH) {
+  // One chunk: scores of the chunk's K (loaded one step ahead), prefetch of the next K,
+  // softmax, P.V with the chunk's V, prefetch of the next V. The first call is peeled off
+  // the loop so that the loop is entered with the same load order as its back edge (K
+  // before V) and the in-order load counter is waited on for K alone at the loop top.
+  auto chunk = [&](int c0) __attribute__((always_inline)) {
     const int c1 = c0 + CH;
     if constexpr (FAST) chunk_pages(c1, pg_next);
     // ---- scores: S[t] = rows x 16 tokens of tile t (lane: token c16, rows 4*g4 + e)
@@ -393,6 +399,10 @@ __global__ __launch_bounds__(64) void partial_kernel(LaunchArgs a) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) pg_cur[t] = pg_next[t];
     wave_sync();
+  };
+  if (tok0 < tok_end) {
+    chunk(tok0);
+    for (int c0 = tok0 + CH; c0 < tok_end; c0 += CH) chunk(c0);
   }
   if (a.debug && clamped_any) atomicOr(a.status, (unsigned)SKVD_STATUS_PAGE_CLAMPED);
 
@@ -626,12 +636,20 @@ __global__ __launch_bounds__(64) void gather_kernel(LaunchArgs a, int max_len, c
 }
 
 // ----------------------------------------------------------------------------- launchers
+// Tokens per chunk for each variant, chosen so that the kernel keeps at most 168 registers
+// (three waves per SIMD) where the row count allows.
+template <int D, int RB>
+constexpr int chunk_tokens() {
+  return D == 128 ? (RB <= 2 ? 32 : 16) : 16;
+}
+
 template <int D, int RB, bool I8>
 static void launch_partial_t(const LaunchArgs &la, dim3 grid, hipStream_t st, bool fast) {
+  constexpr int CH = chunk_tokens<D, RB>();
   if (fast)
-    partial_kernel<D, RB, I8, true><<<grid, 64, 0, st>>>(la);
+    partial_kernel<D, RB, I8, true, CH><<<grid, 64, 0, st>>>(la);
   else
-    partial_kernel<D, RB, I8, false><<<grid, 64, 0, st>>>(la);
+    partial_kernel<D, RB, I8, false, CH><<<grid, 64, 0, st>>>(la);
 }
 
 template <int D, bool I8>
