@@ -201,6 +201,13 @@ skvd_status skvd_gather_debug(const skvd_plan *plan, const skvd_decode_args *arg
                               int32_t max_len, void *dense_k, void *dense_v, void *dense_ks,
                               void *dense_vs, void *stream);
 
+/* Measurement aid (not part of the decode): read `bytes` bytes at `buf` once with 16-byte
+ * loads spread over the whole chip, so that a benchmark can report the HBM read bandwidth this
+ * GPU actually sustains next to the decode's. buf is device memory, 16-byte aligned; bytes is
+ * a multiple of 16; sink is a device uint32 that the kernel may write (keeps the loads live).
+ * Asynchronous on `stream`. */
+skvd_status skvd_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *stream);
+
 const char *skvd_status_string(skvd_status status);
 /* Message of the last failed call on this thread ("" if none). */
 const char *skvd_last_error(void);

@@ -10,5 +10,6 @@ from ._binding import (  # noqa: F401
     skvd_decode, skvd_decode_check, skvd_decode_merge, skvd_decode_partial, skvd_gather_debug,
     skvd_plan_create, skvd_plan_describe, skvd_plan_destroy, skvd_plan_get_info,
     skvd_plan_params, skvd_plan_workspace_bytes, skvd_decode_args, status_string,
+    skvd_stream_read, stream_read,
     STATUS_KV_LEN_CLAMPED, STATUS_PAGE_CLAMPED,
 )

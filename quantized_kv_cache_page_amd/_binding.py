@@ -80,6 +80,8 @@ SIGNATURES = {
     "skvd_gather_debug": (ctypes.c_int, [_PLAN_P, ctypes.POINTER(skvd_decode_args), ctypes.c_int32,
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_void_p, ctypes.c_void_p]),
+    "skvd_stream_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                        ctypes.c_void_p]),
     "skvd_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "skvd_last_error": (ctypes.c_char_p, []),
     "skvd_abi_version": (ctypes.c_int32, []),
@@ -178,6 +180,17 @@ def skvd_decode_merge(plan, args, workspace, workspace_bytes, stream) -> int:
 def skvd_gather_debug(plan, args, max_len, dk, dv, dks, dvs, stream) -> int:
     return int(lib().skvd_gather_debug(plan, ctypes.byref(args), max_len, dk, dv, dks, dvs,
                                        stream))
+
+
+def skvd_stream_read(buf: int, nbytes: int, sink: int, stream) -> int:
+    return int(lib().skvd_stream_read(buf, nbytes, sink, stream))
+
+
+def stream_read(t, sink, stream=None):
+    """Read tensor t once (measurement aid; see skvd_stream_read)."""
+    s = (stream if stream is not None else torch.cuda.current_stream(t.device)).cuda_stream
+    _check(skvd_stream_read(t.data_ptr(), t.numel() * t.element_size(), sink.data_ptr(), s),
+           "skvd_stream_read")
 
 
 # ---------------------------------------------------------------- torch-facing plan

@@ -203,4 +203,13 @@ skvd_status skvd_gather_debug(const skvd_plan *plan, const skvd_decode_args *arg
   return e ? hip_err(e, "gather kernel launch") : SKVD_OK;
 }
 
+skvd_status skvd_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *stream) {
+  g_err[0] = 0;
+  if (!buf || !sink) return set_err(SKVD_ERR_NULL, "buf and sink must be non-NULL");
+  if ((uintptr_t)buf % 16 || bytes % 16)
+    return set_err(SKVD_ERR_LAYOUT, "buf must be 16-byte aligned and bytes a multiple of 16");
+  int e = skvd::launch_stream_read(buf, bytes / 16, sink, stream);
+  return e ? hip_err(e, "stream-read kernel launch") : SKVD_OK;
+}
+
 }  // extern "C"

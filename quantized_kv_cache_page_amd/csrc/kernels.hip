@@ -635,6 +635,26 @@ __global__ __launch_bounds__(64) void gather_kernel(LaunchArgs a, int max_len, c
   }
 }
 
+// ----------------------------------------------------------------------------- stream read (measurement aid)
+// Every thread reads one 16-byte word per step with a grid-wide stride, so at any moment the
+// chip sweeps one contiguous window: the plainest way to run HBM at its sustainable rate.
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4v *p, size_t n, uint32_t *sink) {
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  unsigned acc = 0;
+  for (; i < n; i += stride) {
+    const uint4v v = p[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
+int launch_stream_read(const void *buf, size_t n16, uint32_t *sink, void *stream) {
+  if (n16 == 0) return 0;
+  stream_read_kernel<<<2048, 256, 0, (hipStream_t)stream>>>((const uint4v *)buf, n16, sink);
+  return (int)hipGetLastError();
+}
+
 // ----------------------------------------------------------------------------- launchers
 // Tokens per chunk for each variant, chosen so that the kernel keeps at most 168 registers
 // (three waves per SIMD) where the row count allows.

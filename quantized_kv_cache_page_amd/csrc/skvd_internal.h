@@ -64,6 +64,7 @@ void fill_launch_args(const Plan &p, const skvd_decode_args &a, void *ws, Launch
 // kernels.hip (return a hipError_t as int; 0 = success)
 int launch_partial(const Plan &p, const LaunchArgs &la, void *stream);
 int launch_merge(const Plan &p, const LaunchArgs &la, void *stream);
+int launch_stream_read(const void *buf, size_t n16, uint32_t *sink, void *stream);
 int launch_gather(const Plan &p, const LaunchArgs &la, int max_len, void *dk, void *dv, void *dks,
                   void *dvs, void *stream);
 
