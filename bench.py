@@ -86,6 +86,82 @@ def cpu_baseline(prob, budget_s=12.0):
                       f"query tokens x {prob['q'].shape[1]} heads), median {t:.3f} s each, fp64"}
 
 
+CLIFF_LENS = [1024, 1470, 1900, 2000, 2047, 2048, 2049, 2100, 3000, 4096, 4097, 4800, 8192,
+              16384, 32768]
+LONG_LENS = [8192, 16384, 32768, 65536, 131072]
+
+
+def time_decode(spec, seed, steps, warmup, bps=0, reducer="auto"):
+    """Generate one problem, rotate pool copies past the Infinity Cache, and return
+    (us per decode call, us per partial kernel, K+V bytes, plan description)."""
+    import numpy as np
+    import torch
+    import quantized_kv_cache_page_amd as skvd
+    import workloads
+    prob = workloads.generate(spec, seed)
+    kvb = workloads.kv_bytes(prob)
+    dev = torch.device("cuda:0")
+
+    def up(x):
+        return None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    q, table, kv_len = up(prob["q"]), up(prob["page_table"]), up(prob["kv_len"])
+    pools = [up(prob[k]) for k in ("k_pages", "v_pages", "k_scales", "v_scales")]
+    copies = max(1, math.ceil(2 * MALL_BYTES / max(kvb, 1)) + 1)
+    sets = [pools] + [[None if p is None else p.clone() for p in pools] for _ in range(copies - 1)]
+    plan = skvd.Plan(spec.num_qo_heads, spec.num_kv_heads, spec.head_dim, spec.page_size,
+                     spec.kv_dtype, spec.batch, spec.q_per_seq, spec.max_kv_len, device=0,
+                     force_blocks_per_split=bps, force_reducer=reducer)
+    plan.ensure_workspace()
+    out = torch.empty(q.shape, dtype=torch.float16, device=dev)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+
+    def call(i, stage="all"):
+        k, v, ks, vs = sets[i % copies]
+        plan.run(q, k, v, table, kv_len, prob["sm_scale"], ks, vs, out=out, lse=lse,
+                 q_per_seq=spec.q_per_seq, stage=stage)
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        call(i, "partial")
+        ev[i][1].record()
+        call(i, "merge")
+    torch.cuda.synchronize()
+    part_us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        call(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps * 1e3, part_us, kvb, plan.describe()
+
+
+def sweep(args):
+    import workloads
+    lens = CLIFF_LENS if args.sweep == "cliff" else LONG_LENS
+    for L in lens:
+        if args.sweep == "cliff":
+            s = workloads.spec(name=f"cliff_{L}", batch=32, q_per_seq=1, num_qo_heads=32,
+                               num_kv_heads=8, head_dim=128, page_size=16, lens=("fixed", L))
+        else:
+            s = workloads.spec(name=f"long_{L}", batch=1, q_per_seq=1, num_qo_heads=32,
+                               num_kv_heads=8, head_dim=128, page_size=64, lens=("fixed", L),
+                               q_mult=2.0)
+        us, part_us, kvb, plan = time_decode(s, 100 + L % 97, args.steps, args.warmup,
+                                             args.bps, args.reducer)
+        print(json.dumps({"sweep": args.sweep, "kv_len": L, "us_per_call": round(us, 2),
+                          "partial_us": round(part_us, 2), "kv_bytes": kvb,
+                          "gbs": round(kvb / (us * 1e-6) / 1e9, 1),
+                          "partial_gbs": round(kvb / (part_us * 1e-6) / 1e9, 1),
+                          "plan": plan}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -101,6 +177,10 @@ def main():
                     help="pool layout: nhd = [pages, P, Hkv, D] (the workload's); hnd = each KV "
                          "head's page rows contiguous, passed through the same strides")
     ap.add_argument("--no-stream-ref", action="store_true")
+    ap.add_argument("--sweep", choices=["cliff", "long"], default=None,
+                    help="instead of the bench line: cliff = B=32, 32/8 heads, D=128, P=16 at "
+                         "uniform kv_len across the 2048-token boundary; long = B=1, the long-"
+                         "context shape, kv_len 8192..131072. One JSON line per point.")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB, 5 times (reference "
                          "for scaling the HBM byte counters)")
@@ -115,6 +195,8 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n, "repeats": 5}), flush=True)
         return
+    if args.sweep:
+        return sweep(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (the decode "
               f"is single-GPU; the multi-GPU sharding is described, not built)", file=sys.stderr)

@@ -110,51 +110,112 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// 8 signed bytes -> 8 f16 (exact).
+// ----------------------------------------------------------------------------- int8 -> f16
+// Exact int8 -> f16 without conversion instructions: flip the sign bit of each byte (x + 128
+// as an unsigned byte u), put u under the f16 exponent of 1024 with a byte permute (the f16
+// with bits 0x64uu is 1024 + u, exact) and subtract 1152 with one packed f16 add per pair.
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+constexpr unsigned kExp1024 = 0x64646464u;  // every byte 0x64: f16 high byte of 1024
+
+__device__ __forceinline__ half2v magic_pair(unsigned flipped, unsigned sel) {
+  return __builtin_bit_cast(half2v, __builtin_amdgcn_perm(kExp1024, flipped, sel)) -
+         (half2v)(_Float16)1152;
+}
+
+// 8 signed bytes (elements 0..7 in byte order) -> 8 f16.
 __device__ __forceinline__ half8 i8x8_to_h8(uint2v w) {
   half8 r;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const unsigned word = i < 4 ? w.x : w.y;
-    const int v = (int)(signed char)((word >> (8 * (i & 3))) & 0xff);
-    r[i] = (_Float16)v;
+  for (int k = 0; k < 2; ++k) {
+    const unsigned x = w[k] ^ 0x80808080u;
+    const half2v lo = magic_pair(x, 0x04010400u), hi = magic_pair(x, 0x04030402u);
+    r[4 * k + 0] = lo[0];
+    r[4 * k + 1] = lo[1];
+    r[4 * k + 2] = hi[0];
+    r[4 * k + 3] = hi[1];
   }
   return r;
 }
 
-__device__ __forceinline__ void h8_to_f(const half8 &h, float *f) {
+// Two int8 rows a (token t) and b (token t + 16), 8 elements each -> the 8 f16 pairs
+// (a_i, b_i): the bytes are interleaved first, then converted two elements per permute.
+__device__ __forceinline__ void i8_pairs(uint2v a, uint2v b, half2v *out) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) f[i] = (float)h[i];
+  for (int w = 0; w < 2; ++w) {
+    const unsigned lo = __builtin_amdgcn_perm(b[w], a[w], 0x05010400u) ^ 0x80808080u;
+    const unsigned hi = __builtin_amdgcn_perm(b[w], a[w], 0x07030602u) ^ 0x80808080u;
+    out[4 * w + 0] = magic_pair(lo, 0x04010400u);
+    out[4 * w + 1] = magic_pair(lo, 0x04030402u);
+    out[4 * w + 2] = magic_pair(hi, 0x04010400u);
+    out[4 * w + 3] = magic_pair(hi, 0x04030402u);
+  }
 }
-__device__ __forceinline__ void i8x8_to_f(uint2v w, float *f) {
+
+// Two f16 rows a (token t) and b (token t + 16) -> the 8 pairs (a_i, b_i).
+__device__ __forceinline__ void h16_pairs(const half8 &a, const half8 &b, half2v *out) {
+  const uint4v aw = __builtin_bit_cast(uint4v, a), bw = __builtin_bit_cast(uint4v, b);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const unsigned word = i < 4 ? w.x : w.y;
-    f[i] = (float)(int)(signed char)((word >> (8 * (i & 3))) & 0xff);
+  for (int k = 0; k < 4; ++k) {
+    out[2 * k] = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(bw[k], aw[k], 0x05040100u));
+    out[2 * k + 1] = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(bw[k], aw[k], 0x07060302u));
   }
 }
 
 // ----------------------------------------------------------------------------- partial kernel
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4v *lds_s4_ptr;
+
+// Byte offset of 16-byte chunk c of row r in a row-major LDS tile with rows of RB bytes: the
+// chunk index is XOR-swizzled by the row so that the transposed reads of 16 consecutive rows
+// at one column fall in different banks.
+template <int ROWB>
+__device__ __forceinline__ int swz(int r, int c) {
+  return r * ROWB + ((c ^ (r & 15)) << 4);
+}
+
 // D: head_dim (128/256). RB: 4-row quarters of the 16 MFMA rows in use (rows = G*T <= 4*RB).
 // I8: int8 cache with f16 scales per 32 elements. FAST: page_size >= 16, so each 16-token
-// tile lies in one page and its page id is wave-uniform.
-template <int D, int RB, bool I8, bool FAST, int CH>
+// tile lies in one page and its page id is wave-uniform. CH: tokens per chunk (32 at D=128,
+// 16 at D=256): the K and V registers of a chunk bound how many waves fit on a SIMD.
+// PVM: P.V on the MFMA through an LDS copy of the chunk's V (dense when several query rows
+// share the KV head); otherwise P.V on the vector ALU as f16 pair dot products
+// (v_dot2_f32_f16) from the V registers, pairing token t with token t + 16.
+template <int D, int RB, bool I8, bool FAST, int CH, bool PVM>
 __global__ __launch_bounds__(64) void partial_kernel(LaunchArgs a) {
-  // CH: tokens per chunk (16, 32 or 64). The K and V registers of a chunk (CH*D*4 bytes per
-  // wave) bound how many waves fit on a SIMD; residency, not ALU work, sets the bandwidth.
-  static_assert(CH == 16 || CH == 32 || CH == 64, "chunk");
-  constexpr int NT = CH / 16;    // 16-token MFMA tiles per chunk
-  constexpr int KS = D / 32;     // MFMA contraction steps of 32 head_dim elements
-  constexpr int LPR = D / 8;     // P.V lanes per V row, 8 elements each
-  constexpr int TPS = 64 / LPR;  // tokens per P.V step
-  constexpr int NS = CH / TPS;   // P.V steps per chunk
+  static_assert(CH == 16 || CH == 32, "chunk");
+  static_assert(PVM || CH == 32, "the vector P.V pairs the two 16-token tiles of a chunk");
+  constexpr int NT = CH / 16;    // 16-token score tiles per chunk
+  constexpr int KS = D / 32;     // score MFMA steps of 32 head_dim elements
+  constexpr int LPR = D / 8;     // lanes per V row in the load layout, 8 elements each
+  constexpr int TPS = 64 / LPR;  // V rows per load step
+  constexpr int NS = CH / TPS;   // V load steps per chunk
+  constexpr int NDT = D / 16;    // 16-wide head_dim tiles of the P.V MFMA
+  constexpr int KPL = CH / 4;    // P.V contraction elements per lane (8: 16x16x32, 4: 16x16x16)
   constexpr int RM = 4 * RB;     // query rows held (padded)
+  constexpr int PSTR = CH + 4;   // row stride of the probability tile, floats
+  constexpr int ROWB = 2 * D;    // bytes per V row in LDS (f16)
   using Vec = std::conditional_t<I8, uint2v, half8>;  // one lane's 8 elements of a row
+  using PvOp = std::conditional_t<CH == 32, half8, half4>;
 
-  __shared__ float4v p_lds[CH][RB];  // probabilities of each chunk token, 4 rows per float4
+  __shared__ __attribute__((aligned(16))) char v_lds[PVM ? CH * ROWB : 16];  // chunk V, f16
+  __shared__ __attribute__((aligned(16))) float p_lds[PVM ? RM * PSTR : 4];  // [row][token]
+  __shared__ float vs_lds[PVM && I8 ? CH * (D / 32) : 1];  // int8 V scales [token][group]
+  // vector P.V: probabilities as f16 pairs (token tp, token tp + 16) per row: [tp][row]
+  __shared__ __attribute__((aligned(16))) unsigned p2_lds[PVM ? 4 : 16 * RM];
 
+  // Workgroup order: split fastest, then KV head, then sequence, with an odd split stride.
+  // Consecutive workgroups go to the eight XCDs in turn; with an even stride split s of
+  // every (head, sequence) would land on the same XCD, and the live splits of a ragged batch
+  // (short sequences have few) would pile onto the XCDs of the low split indices. The odd
+  // stride rotates each row's start over all eight. Indices past splits_cap are padding.
   const int lane = threadIdx.x;
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int Hkv = a.Hkv;
+  const int wg = blockIdx.x;
+  const int split = wg % a.split_stride;
+  const int head_seq = wg / a.split_stride;
+  const int kvh = head_seq % Hkv, b = head_seq / Hkv;
+  if (split >= a.splits_cap) return;
   const int T = a.T, G = a.G, R = G * T;
   const int L = clamp_len(a.kv_len[b], a.max_kv_len, a.status, a.debug);
   const int nblk = (L + 63) >> 6;
@@ -170,8 +231,8 @@ __global__ __launch_bounds__(64) void partial_kernel(LaunchArgs a) {
   const _Float16 *ksc = (const _Float16 *)a.ks;
   const _Float16 *vsc = (const _Float16 *)a.vs;
 
-  // Query rows as the MFMA A operand: lane holds row (lane & 15), elements 8*(lane>>4)..+7
-  // of each 32-element contraction step.
+  // Query rows as the score MFMA A operand: lane holds row (lane & 15), elements
+  // 8*(lane>>4)..+7 of each 32-element contraction step.
   const int g4 = lane >> 4, c16 = lane & 15;
   half8 qa[KS];
   {
@@ -187,7 +248,7 @@ __global__ __launch_bounds__(64) void partial_kernel(LaunchArgs a) {
       for (int k = 0; k < KS; ++k) qa[k] = (half8)(_Float16)0;
     }
   }
-  // Rows of this lane's MFMA outputs: 4*g4 + e. Positions a row sees: j < L - T + t + 1.
+  // This lane's MFMA output rows: 4*g4 + e. Row r sees positions j < L - T + t + 1.
   int nvis[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -199,11 +260,17 @@ __global__ __launch_bounds__(64) void partial_kernel(LaunchArgs a) {
   float m[4], lsum[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) { m[e] = kNegInf; lsum[e] = 0.f; }
-  float acc[RM][8];
+  // MFMA P.V output: lane holds head_dim column 16*dt + c16 of rows 4*g4 + e.
+  float4v acc[PVM ? NDT : 1];
 #pragma unroll
-  for (int r = 0; r < RM; ++r)
+  for (int dt = 0; dt < (PVM ? NDT : 1); ++dt) acc[dt] = (float4v)0.f;
+  // Vector P.V output: lane holds elements vlane_el .. +7 of every row, summed over the
+  // tokens of its load slot (reduced across slots at the end).
+  float accv[PVM ? 1 : RM][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[r][i] = 0.f;
+  for (int r = 0; r < (PVM ? 1 : RM); ++r)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) accv[r][i] = 0.f;
 
   bool clamped_any = false;
   const int vlane_tok = lane / LPR, vlane_el = 8 * (lane % LPR);
@@ -230,56 +297,84 @@ __global__ __launch_bounds__(64) void partial_kernel(LaunchArgs a) {
   Vec kb[NT][KS];
   float ks_tok[NT][KS];
   Vec vb[NS];
-  float vs_tok[NS];
+  _Float16 vs_h[NS];
 
-  // K rows of chunk c0 in the MFMA B-operand layout: tile t, lane (g4, c16) holds elements
-  // 32k + 8*g4 .. +7 of token 16t + c16.
+  // K rows of chunk c0 in the score MFMA B-operand layout: tile t, lane (g4, c16) holds
+  // elements 32k + 8*g4 .. +7 of token 16t + c16.
   auto load_k = [&](int c0, const int *pgs) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int jt = c0 + 16 * t;
-      const int j = min(jt + c16, tok_end - 1);
-      int64_t pg;
       if constexpr (FAST) {
-        pg = clamp_page(pgs[t], a.num_k_pages);
+        // wave-uniform base of the (clamped) tile on the scalar unit + 32-bit lane offset
+        const int jte = min(jt, last_tile);
+        const int64_t pg = clamp_page(pgs[t], a.num_k_pages);
+        const char *base = kbase + row_offset(pg, jte & P1, kvh, a.page_stride, a.tok_stride,
+                                              a.head_stride) * ES;
+        const int tk = min(c16, tok_end - 1 - jte);
+        const unsigned off = (unsigned)((tk * (int)a.tok_stride + 8 * g4) * ES);
+#pragma unroll
+        for (int k = 0; k < KS; ++k) kb[t][k] = *(const Vec *)(base + off + 32 * k * ES);
+        if constexpr (I8) {
+          const _Float16 *sb = ksc + row_offset(pg, jte & P1, kvh, a.s_page_stride,
+                                                a.s_tok_stride, a.s_head_stride);
+          const unsigned so = (unsigned)(tk * (int)a.s_tok_stride);
+#pragma unroll
+          for (int k = 0; k < KS; ++k) ks_tok[t][k] = (float)sb[so + k];
+        }
       } else {
+        const int j = min(jt + c16, tok_end - 1);
         bool cl;
-        pg = lookup_page(a.table, a.table_stride, b, j, a.page_shift, a.num_k_pages, &cl);
+        const int64_t pg = lookup_page(a.table, a.table_stride, b, j, a.page_shift,
+                                       a.num_k_pages, &cl);
         clamped_any |= cl;
-      }
-      const int64_t off = row_offset(pg, j & P1, kvh, a.page_stride, a.tok_stride, a.head_stride);
-      const char *kp = kbase + (off + 8 * g4) * ES;
+        const int64_t off = row_offset(pg, j & P1, kvh, a.page_stride, a.tok_stride,
+                                       a.head_stride);
+        const char *kp = kbase + (off + 8 * g4) * ES;
 #pragma unroll
-      for (int k = 0; k < KS; ++k) kb[t][k] = *(const Vec *)(kp + 32 * k * ES);
-      if constexpr (I8) {
-        const int64_t so = row_offset(pg, j & P1, kvh, a.s_page_stride, a.s_tok_stride,
-                                      a.s_head_stride);
+        for (int k = 0; k < KS; ++k) kb[t][k] = *(const Vec *)(kp + 32 * k * ES);
+        if constexpr (I8) {
+          const int64_t so = row_offset(pg, j & P1, kvh, a.s_page_stride, a.s_tok_stride,
+                                        a.s_head_stride);
 #pragma unroll
-        for (int k = 0; k < KS; ++k) ks_tok[t][k] = (float)ksc[so + k];
+          for (int k = 0; k < KS; ++k) ks_tok[t][k] = (float)ksc[so + k];
+        }
       }
     }
   };
-  // V rows of chunk c0 in the P.V layout: step s, lane holds elements vlane_el .. +7 of
+  // V rows of chunk c0 in the load layout: step s, lane holds elements vlane_el .. +7 of
   // token TPS*s + vlane_tok.
   auto load_v = [&](int c0, const int *pgs) __attribute__((always_inline)) {
 #pragma unroll
     for (int s2 = 0; s2 < NS; ++s2) {
       const int js = c0 + TPS * s2;
-      const int j = min(js + vlane_tok, tok_end - 1);
-      int64_t pg;
       if constexpr (FAST) {
-        pg = clamp_page(pgs[(TPS * s2) >> 4], a.num_v_pages);
+        const int jte = min(js & ~15, last_tile);
+        const int64_t pg = clamp_page(pgs[(TPS * s2) >> 4], a.num_v_pages);
+        const char *base = vbase + row_offset(pg, jte & P1, kvh, a.page_stride, a.tok_stride,
+                                              a.head_stride) * ES;
+        const int tk = min((js & 15) + vlane_tok, tok_end - 1 - jte);
+        const unsigned off = (unsigned)((tk * (int)a.tok_stride + vlane_el) * ES);
+        vb[s2] = *(const Vec *)(base + off);
+        if constexpr (I8) {
+          const _Float16 *sb = vsc + row_offset(pg, jte & P1, kvh, a.s_page_stride,
+                                                a.s_tok_stride, a.s_head_stride);
+          vs_h[s2] = sb[(unsigned)(tk * (int)a.s_tok_stride) + vlane_el / 32];
+        }
       } else {
+        const int j = min(js + vlane_tok, tok_end - 1);
         bool cl;
-        pg = lookup_page(a.table, a.table_stride, b, j, a.page_shift, a.num_v_pages, &cl);
+        const int64_t pg = lookup_page(a.table, a.table_stride, b, j, a.page_shift,
+                                       a.num_v_pages, &cl);
         clamped_any |= cl;
-      }
-      const int64_t off = row_offset(pg, j & P1, kvh, a.page_stride, a.tok_stride, a.head_stride);
-      vb[s2] = *(const Vec *)(vbase + (off + vlane_el) * ES);
-      if constexpr (I8) {
-        const int64_t so = row_offset(pg, j & P1, kvh, a.s_page_stride, a.s_tok_stride,
-                                      a.s_head_stride);
-        vs_tok[s2] = (float)vsc[so + vlane_el / 32];
+        const int64_t off = row_offset(pg, j & P1, kvh, a.page_stride, a.tok_stride,
+                                       a.head_stride);
+        vb[s2] = *(const Vec *)(vbase + (off + vlane_el) * ES);
+        if constexpr (I8) {
+          const int64_t so = row_offset(pg, j & P1, kvh, a.s_page_stride, a.s_tok_stride,
+                                        a.s_head_stride);
+          vs_h[s2] = vsc[so + vlane_el / 32];
+        }
       }
     }
   };
@@ -294,10 +389,11 @@ __global__ __launch_bounds__(64) void partial_kernel(LaunchArgs a) {
     load_v(tok0, pg_cur);
     __builtin_amdgcn_sched_barrier(0);
   }
+
   // One chunk: scores of the chunk's K (loaded one step ahead), prefetch of the next K,
-  // softmax, P.V with the chunk's V, prefetch of the next V. The first call is peeled off
-  // the loop so that the loop is entered with the same load order as its back edge (K
-  // before V) and the in-order load counter is waited on for K alone at the loop top.
+  // softmax, P.V with the chunk's V, prefetch of the next V. The first call is peeled off the
+  // loop so that the loop is entered with the same load order as its back edge (K before V):
+  // the in-order load counter is then waited on for K alone at the loop top.
   auto chunk = [&](int c0) __attribute__((always_inline)) {
     const int c1 = c0 + CH;
     if constexpr (FAST) chunk_pages(c1, pg_next);
@@ -354,43 +450,129 @@ __global__ __launch_bounds__(64) void partial_kernel(LaunchArgs a) {
       lsum[e] = lsum[e] * alpha[e] + ps;
       m[e] = mnew;
     }
-    if (g4 < RB) {
-#pragma unroll
-      for (int t = 0; t < NT; ++t) p_lds[16 * t + c16][g4] = S[t];
-    }
-    float al[RM];
-#pragma unroll
-    for (int r = 0; r < RM; ++r) al[r] = readlane_f(alpha[r & 3], 16 * (r >> 2));
-    wave_sync();
 
-    // ---- P.V
-    bool rescale = false;
+    if constexpr (PVM) {
+      // ---- probabilities to LDS as [row][token]; the chunk's V rows to LDS (int8 widened
+      // exactly to f16, scales to vs_lds)
+      if (g4 < RB) {
 #pragma unroll
-    for (int r = 0; r < RM; ++r) rescale |= al[r] != 1.f;
-    if (rescale) {
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int r = 0; r < RM; ++r)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[r][i] *= al[r];
-    }
-#pragma unroll
-    for (int s2 = 0; s2 < NS; ++s2) {
-      const int tk = TPS * s2 + vlane_tok;
-      float4v pr[RB];
-#pragma unroll
-      for (int q = 0; q < RB; ++q) pr[q] = p_lds[tk][q];
-      float v[8];
-      if constexpr (I8) {
-        i8x8_to_f(vb[s2], v);
-#pragma unroll
-        for (int q = 0; q < RB; ++q) pr[q] *= vs_tok[s2];
-      } else {
-        h8_to_f(vb[s2], v);
+          for (int e = 0; e < 4; ++e) p_lds[(4 * g4 + e) * PSTR + 16 * t + c16] = S[t][e];
       }
 #pragma unroll
-      for (int r = 0; r < RM; ++r)
+      for (int s2 = 0; s2 < NS; ++s2) {
+        const int row = TPS * s2 + vlane_tok;
+        half8 h;
+        if constexpr (I8) {
+          h = i8x8_to_h8(vb[s2]);
+          if ((lane % LPR) % 4 == 0) vs_lds[row * (D / 32) + vlane_el / 32] = (float)vs_h[s2];
+        } else {
+          h = vb[s2];
+        }
+        *(half8 *)(v_lds + swz<ROWB>(row, lane % LPR)) = h;
+      }
+      wave_sync();
+
+      // ---- P.V on the MFMA: A = probabilities (row c16, tokens KPL*g4 ..), B = V^T tiles
+      // read transposed from LDS (column 16*dt + c16, the same tokens)
+      bool rescale = false;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[r][i] = fmaf(pr[r >> 2][r & 3], v[i], acc[r][i]);
+      for (int e = 0; e < 4; ++e) rescale |= alpha[e] != 1.f;
+      if (__builtin_amdgcn_read_exec() && rescale) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[dt][e] *= alpha[e];
+      }
+      float pv[KPL];
+#pragma unroll
+      for (int i = 0; i < KPL; ++i) pv[i] = c16 < RM ? p_lds[c16 * PSTR + KPL * g4 + i] : 0.f;
+      PvOp pa[I8 ? D / 32 : 1];
+      if constexpr (I8) {
+#pragma unroll
+        for (int gg = 0; gg < D / 32; ++gg)
+#pragma unroll
+          for (int i = 0; i < KPL; ++i)
+            pa[gg][i] = (_Float16)(pv[i] * vs_lds[(KPL * g4 + i) * (D / 32) + gg]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) pa[0][i] = (_Float16)pv[i];
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        // lane (g4, c16) of read h receives column 16*dt + c16 of tokens KPL*g4 + 4h + 0..3
+        PvOp vt;
+#pragma unroll
+        for (int h = 0; h < KPL / 4; ++h) {
+          const int row = KPL * g4 + 4 * h + (c16 >> 2);
+          const int col = 16 * dt + 4 * (c16 & 3);
+          const short4v r4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s4_ptr)(v_lds + swz<ROWB>(row, col >> 3) + ((col & 7) << 1)));
+          const half4 hv = __builtin_bit_cast(half4, r4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) vt[4 * h + i] = hv[i];
+        }
+        const PvOp &pop = pa[I8 ? dt / 2 : 0];
+        if constexpr (CH == 32)
+          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pop, vt, acc[dt], 0, 0, 0);
+        else
+          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(pop, vt, acc[dt], 0, 0, 0);
+      }
+    } else {
+      // ---- probabilities to LDS as f16 pairs (token c16, token 16 + c16) per row
+      if (g4 < RB) {
+        uint4v w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w[e] = __builtin_bit_cast(unsigned, half2v{(_Float16)S[0][e], (_Float16)S[1][e]});
+        *(uint4v *)&p2_lds[c16 * RM + 4 * g4] = w;
+      }
+      // per-row rescale factors (row-uniform within the 16 lanes of a DPP row)
+      float al[RM];
+#pragma unroll
+      for (int r = 0; r < RM; ++r) al[r] = readlane_f(alpha[r & 3], 16 * (r >> 2));
+      wave_sync();
+      bool rescale = false;
+#pragma unroll
+      for (int r = 0; r < RM; ++r) rescale |= al[r] != 1.f;
+      if (rescale) {
+#pragma unroll
+        for (int r = 0; r < RM; ++r)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) accv[r][i] *= al[r];
+      }
+      // ---- P.V: load steps s and s + NS/2 hold tokens tp and tp + 16 of the lane's slot
+#pragma unroll
+      for (int s2 = 0; s2 < NS / 2; ++s2) {
+        const int tp = TPS * s2 + vlane_tok;
+        half2v pp[RM];
+#pragma unroll
+        for (int q = 0; q < RB; ++q) {
+          const uint4v w = *(const uint4v *)&p2_lds[tp * RM + 4 * q];
+          // (bit_cast of a vector element would cast element 0: copy the element out first)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const unsigned we = w[e];
+            pp[4 * q + e] = __builtin_bit_cast(half2v, we);
+          }
+        }
+        half2v vp[8];
+        if constexpr (I8) {
+          // int8 V: the pair's per-32 scales fold into the probabilities
+          const half2v sc = {vs_h[s2], vs_h[s2 + NS / 2]};
+#pragma unroll
+          for (int r = 0; r < RM; ++r) pp[r] *= sc;
+          i8_pairs(vb[s2], vb[s2 + NS / 2], vp);
+        } else {
+          h16_pairs(vb[s2], vb[s2 + NS / 2], vp);
+        }
+#pragma unroll
+        for (int r = 0; r < RM; ++r)
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            accv[r][i] = __builtin_amdgcn_fdot2(pp[r], vp[i], accv[r][i], false);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     // ---- prefetch the next chunk's V while the next chunk's scores run
@@ -406,49 +588,78 @@ __global__ __launch_bounds__(64) void partial_kernel(LaunchArgs a) {
   }
   if (a.debug && clamped_any) atomicOr(a.status, (unsigned)SKVD_STATUS_PAGE_CLAMPED);
 
-  // ---- per-row max and sum (wave-uniform)
-  float mr[RM], lr[RM];
+  // ---- per-row sum over the tokens of the lane's DPP row; max is already row-uniform
 #pragma unroll
   for (int e = 0; e < 4; ++e) lsum[e] = row16_sum(lsum[e]);
-#pragma unroll
-  for (int r = 0; r < RM; ++r) {
-    mr[r] = readlane_f(m[r & 3], 16 * (r >> 2));
-    lr[r] = readlane_f(lsum[r & 3], 16 * (r >> 2));
-  }
-  // ---- sum the token groups of the P.V lanes: lanes l, l^LPR, ... share head_dim elements
-#pragma unroll
-  for (int r = 0; r < RM; ++r)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float x = acc[r][i];
-      if constexpr (TPS >= 4) x += __shfl_xor(x, 16);
-      if constexpr (TPS >= 2) x += __shfl_xor(x, 32);
-      acc[r][i] = x;
-    }
-  if (lane >= LPR) return;
-
   const int Hq = a.Hq;
+
+  if constexpr (PVM) {
+    // ---- output: lanes of group g4 hold rows 4*g4 + e, column 16*dt + c16
+    if (g4 >= RB) return;
 #pragma unroll
-  for (int r = 0; r < RM; ++r) {
-    if (r >= R) continue;
-    const int t = r / G, hg = r - (r / G) * G;
-    const int64_t row = ((int64_t)b * T + t) * Hq + kvh * G + hg;
-    if (a.single) {
-      const float l = lr[r];
-      const float inv = l > 0.f ? 1.f / l : 0.f;
-      half8 out;
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * g4 + e;
+      if (r >= R) continue;
+      const int t = r / G, hg = r - (r / G) * G;
+      const int64_t row = ((int64_t)b * T + t) * Hq + kvh * G + hg;
+      if (a.single) {
+        const float l = lsum[e];
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        _Float16 *o = (_Float16 *)a.o + row * D + c16;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) out[i] = (_Float16)(acc[r][i] * inv);
-      *(half8 *)((_Float16 *)a.o + row * D + vlane_el) = out;
-      if (a.lse && lane == 0) a.lse[row] = l > 0.f ? (mr[r] + __log2f(l)) * kLn2 : kNegInf;
-    } else {
-      float *dst = a.ws_o + (row * a.splits_cap + split) * D + vlane_el;
-      *(float4v *)dst = float4v{acc[r][0], acc[r][1], acc[r][2], acc[r][3]};
-      *(float4v *)(dst + 4) = float4v{acc[r][4], acc[r][5], acc[r][6], acc[r][7]};
-      if (lane == 0) {
-        float *ml = a.ws_ml + (row * a.splits_cap + split) * 2;
-        ml[0] = mr[r];
-        ml[1] = lr[r];
+        for (int dt = 0; dt < NDT; ++dt) o[16 * dt] = (_Float16)(acc[dt][e] * inv);
+        if (a.lse && c16 == 0) a.lse[row] = l > 0.f ? (m[e] + __log2f(l)) * kLn2 : kNegInf;
+      } else {
+        float *dst = a.ws_o + (row * a.splits_cap + split) * D + c16;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) dst[16 * dt] = acc[dt][e];
+        if (c16 == 0) {
+          float *ml = a.ws_ml + (row * a.splits_cap + split) * 2;
+          ml[0] = m[e];
+          ml[1] = lsum[e];
+        }
+      }
+    }
+  } else {
+    // ---- sum the load slots: lanes l, l ^ LPR, ... hold the same head_dim elements
+#pragma unroll
+    for (int r = 0; r < RM; ++r)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float x = accv[r][i];
+#pragma unroll
+        for (int sh = LPR; sh < 64; sh <<= 1) x += __shfl_xor(x, sh);
+        accv[r][i] = x;
+      }
+    float mr[RM], lr[RM];
+#pragma unroll
+    for (int r = 0; r < RM; ++r) {
+      mr[r] = readlane_f(m[r & 3], 16 * (r >> 2));
+      lr[r] = readlane_f(lsum[r & 3], 16 * (r >> 2));
+    }
+    if (lane >= LPR) return;
+#pragma unroll
+    for (int r = 0; r < RM; ++r) {
+      if (r >= R) continue;
+      const int t = r / G, hg = r - (r / G) * G;
+      const int64_t row = ((int64_t)b * T + t) * Hq + kvh * G + hg;
+      if (a.single) {
+        const float l = lr[r];
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        half8 out;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) out[i] = (_Float16)(accv[r][i] * inv);
+        *(half8 *)((_Float16 *)a.o + row * D + vlane_el) = out;
+        if (a.lse && lane == 0) a.lse[row] = l > 0.f ? (mr[r] + __log2f(l)) * kLn2 : kNegInf;
+      } else {
+        float *dst = a.ws_o + (row * a.splits_cap + split) * D + vlane_el;
+        *(float4v *)dst = float4v{accv[r][0], accv[r][1], accv[r][2], accv[r][3]};
+        *(float4v *)(dst + 4) = float4v{accv[r][4], accv[r][5], accv[r][6], accv[r][7]};
+        if (lane == 0) {
+          float *ml = a.ws_ml + (row * a.splits_cap + split) * 2;
+          ml[0] = mr[r];
+          ml[1] = lr[r];
+        }
       }
     }
   }
@@ -656,20 +867,26 @@ int launch_stream_read(const void *buf, size_t n16, uint32_t *sink, void *stream
 }
 
 // ----------------------------------------------------------------------------- launchers
-// Tokens per chunk for each variant, chosen so that the kernel keeps at most 168 registers
-// (three waves per SIMD) where the row count allows.
+// Tokens per chunk and P.V unit per variant. D=128 chunks hold 32 tokens; D=256 chunks 16
+// (register bound). One query row quarter at D=128 takes the vector P.V (pair dot products
+// from registers, no LDS copy of V); more rows, or D=256, make P.V a dense tile for the MFMA.
 template <int D, int RB>
 constexpr int chunk_tokens() {
-  return D == 128 ? (RB <= 2 ? 32 : 16) : 16;
+  return D == 128 ? 32 : 16;
+}
+template <int D, int RB>
+constexpr bool pv_on_mfma() {
+  return !(D == 128 && RB == 1);
 }
 
 template <int D, int RB, bool I8>
 static void launch_partial_t(const LaunchArgs &la, dim3 grid, hipStream_t st, bool fast) {
   constexpr int CH = chunk_tokens<D, RB>();
+  constexpr bool PVM = pv_on_mfma<D, RB>();
   if (fast)
-    partial_kernel<D, RB, I8, true, CH><<<grid, 64, 0, st>>>(la);
+    partial_kernel<D, RB, I8, true, CH, PVM><<<grid, 64, 0, st>>>(la);
   else
-    partial_kernel<D, RB, I8, false, CH><<<grid, 64, 0, st>>>(la);
+    partial_kernel<D, RB, I8, false, CH, PVM><<<grid, 64, 0, st>>>(la);
 }
 
 template <int D, bool I8>
@@ -684,7 +901,8 @@ static void launch_partial_rb(const Plan &p, const LaunchArgs &la, dim3 grid, hi
 
 int launch_partial(const Plan &p, const LaunchArgs &la, void *stream) {
   hipStream_t st = (hipStream_t)stream;
-  dim3 grid(p.splits_cap, la.Hkv, la.batch);
+  // one-dimensional grid, split fastest (the plan keeps the count below 2^31)
+  dim3 grid((unsigned)((int64_t)la.split_stride * la.Hkv * la.batch));
   const bool i8 = la.int8;
   if (la.D == 128) {
     if (i8) launch_partial_rb<128, true>(p, la, grid, st);

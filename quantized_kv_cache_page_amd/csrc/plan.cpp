@@ -99,6 +99,20 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
   if (prm.force_blocks_per_split > 0) bps = prm.force_blocks_per_split;
   if (bps > p.max_blocks) bps = p.max_blocks;
   if (bps < 1) bps = 1;
+  // The partial kernel's one-dimensional grid holds split_stride x KV heads x sequences
+  // < 2^31 workgroups, split_stride being splits_cap rounded up to odd.
+  const int64_t per_split = (int64_t)Hkv * prm.max_batch;
+  const int64_t max_splits = INT32_MAX / per_split - 1;
+  if (max_splits < 1)
+    return fail(err, errn, SKVD_ERR_SHAPE, "num_kv_heads x max_batch = %lld exceeds the grid",
+                (long long)per_split);
+  const int64_t bps_grid = (p.max_blocks + max_splits - 1) / max_splits;
+  if (bps < bps_grid) {
+    if (prm.force_blocks_per_split > 0)
+      return fail(err, errn, SKVD_ERR_PLAN, "force_blocks_per_split=%d gives more than 2^31 "
+                  "partial workgroups", prm.force_blocks_per_split);
+    bps = bps_grid;
+  }
   p.bps = (int)bps;
   p.splits_cap = (p.max_blocks + p.bps - 1) / p.bps;
 
@@ -179,6 +193,11 @@ skvd_status check_args(const Plan &p, const skvd_decode_args *a, size_t ws_bytes
              a->scale_tok_stride < 0 || a->scale_head_stride < 0))
     return fail(err, errn, SKVD_ERR_LAYOUT, "scale pools must be 2-byte aligned with "
                 "non-negative strides");
+  // Within a 16-token tile the kernels address rows with 32-bit byte offsets.
+  const int64_t es = i8 ? 1 : 2;
+  if ((16 * a->tok_stride + D) * es >= (int64_t(1) << 31) ||
+      (i8 && 16 * a->scale_tok_stride + D / 32 >= (int64_t(1) << 30)))
+    return fail(err, errn, SKVD_ERR_LAYOUT, "token stride too large for 32-bit in-tile offsets");
   if (a->num_k_pages < 1 || a->num_v_pages < 1)
     return fail(err, errn, SKVD_ERR_SHAPE, "num_k_pages and num_v_pages must be >= 1");
   const int64_t need_pages = (p.prm.max_kv_len + p.prm.page_size - 1) / p.prm.page_size;
@@ -191,7 +210,6 @@ skvd_status check_args(const Plan &p, const skvd_decode_args *a, size_t ws_bytes
   if (ws_bytes < p.ws_bytes)
     return fail(err, errn, SKVD_ERR_WORKSPACE, "workspace of %zu bytes below the plan's %zu",
                 ws_bytes, p.ws_bytes);
-  (void)D;
   return SKVD_OK;
 }
 
@@ -227,6 +245,7 @@ void fill_launch_args(const Plan &p, const skvd_decode_args &a, void *ws, Launch
   l.scale_log2 = a.sm_scale * 1.4426950408889634f;
   l.bps = p.bps;
   l.splits_cap = p.splits_cap;
+  l.split_stride = p.splits_cap | 1;
   l.max_kv_len = p.prm.max_kv_len;
   l.hier_groups_cap = p.hier_groups_cap;
   l.int8 = p.prm.kv_dtype == SKVD_KV_I8_F16SCALE32;

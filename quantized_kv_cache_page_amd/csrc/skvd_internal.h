@@ -42,7 +42,7 @@ struct LaunchArgs {
   const int32_t *kv_len;
   int batch, T, Hq, Hkv, G, D, page_shift;
   float scale_log2;  // sm_scale * log2(e): scores are kept in base 2
-  int bps, splits_cap, max_kv_len, hier_groups_cap;
+  int bps, splits_cap, split_stride, max_kv_len, hier_groups_cap;  // stride: odd, >= cap
   int int8, debug;
   float *ws_ml;      // [rows_cap][splits_cap][2]  (max in log2 units, sum)
   float *ws_o;       // [rows_cap][splits_cap][D]  unnormalized f32 output
