@@ -91,7 +91,8 @@ CLIFF_LENS = [1024, 1470, 1900, 2000, 2047, 2048, 2049, 2100, 3000, 4096, 4097, 
 LONG_LENS = [8192, 16384, 32768, 65536, 131072]
 
 
-def time_decode(spec, seed, steps, warmup, bps=0, reducer="auto"):
+def time_decode(spec, seed, steps, warmup, bps=0, reducer="auto", schedule="auto",
+                wgs_per_cu=0):
     """Generate one problem, rotate pool copies past the Infinity Cache, and return
     (us per decode call, us per partial kernel, K+V bytes, plan description)."""
     import numpy as np
@@ -111,7 +112,8 @@ def time_decode(spec, seed, steps, warmup, bps=0, reducer="auto"):
     sets = [pools] + [[None if p is None else p.clone() for p in pools] for _ in range(copies - 1)]
     plan = skvd.Plan(spec.num_qo_heads, spec.num_kv_heads, spec.head_dim, spec.page_size,
                      spec.kv_dtype, spec.batch, spec.q_per_seq, spec.max_kv_len, device=0,
-                     force_blocks_per_split=bps, force_reducer=reducer)
+                     force_blocks_per_split=bps, force_reducer=reducer, schedule=schedule,
+                     wgs_per_cu=wgs_per_cu)
     plan.ensure_workspace()
     out = torch.empty(q.shape, dtype=torch.float16, device=dev)
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
@@ -154,7 +156,8 @@ def sweep(args):
                                num_kv_heads=8, head_dim=128, page_size=64, lens=("fixed", L),
                                q_mult=2.0)
         us, part_us, kvb, plan = time_decode(s, 100 + L % 97, args.steps, args.warmup,
-                                             args.bps, args.reducer)
+                                             args.bps, args.reducer, args.schedule,
+                                             args.wgs_per_cu)
         print(json.dumps({"sweep": args.sweep, "kv_len": L, "us_per_call": round(us, 2),
                           "partial_us": round(part_us, 2), "kv_bytes": kvb,
                           "gbs": round(kvb / (us * 1e-6) / 1e9, 1),
@@ -172,6 +175,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--bps", type=int, default=0, help="force 64-token blocks per split")
     ap.add_argument("--reducer", default="auto")
+    ap.add_argument("--schedule", choices=["auto", "static", "balanced"], default="auto")
+    ap.add_argument("--wgs-per-cu", type=int, default=0,
+                    help="balanced schedule: partial-kernel workgroups per CU (0: plan default)")
     ap.add_argument("--copies", type=int, default=0, help="pool copies to rotate (0: auto)")
     ap.add_argument("--layout", choices=["nhd", "hnd"], default="nhd",
                     help="pool layout: nhd = [pages, P, Hkv, D] (the workload's); hnd = each KV "
@@ -234,7 +240,8 @@ def main():
 
     plan = skvd.Plan(spec.num_qo_heads, spec.num_kv_heads, spec.head_dim, spec.page_size,
                      spec.kv_dtype, spec.batch, spec.q_per_seq, spec.max_kv_len, device=0,
-                     force_blocks_per_split=args.bps, force_reducer=args.reducer)
+                     force_blocks_per_split=args.bps, force_reducer=args.reducer,
+                     schedule=args.schedule, wgs_per_cu=args.wgs_per_cu)
     plan.ensure_workspace()
     log(f"[bench] {plan.describe()}")
     out = torch.empty(q.shape, dtype=torch.float16, device=dev)

@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define SKVD_ABI_VERSION 1
+#define SKVD_ABI_VERSION 2
 
 typedef enum {
   SKVD_OK = 0,
@@ -93,6 +93,18 @@ typedef enum {
   SKVD_REDUCER_NONE = 5          /* one split: the partial kernel writes o and lse itself */
 } skvd_reducer;
 
+/* How the partial kernel's workgroups divide the batch's 64-token blocks. */
+typedef enum {
+  SKVD_SCHEDULE_AUTO = 0,     /* balanced when the plan splits and max_batch <= 64, else static */
+  SKVD_SCHEDULE_STATIC = 1,   /* one workgroup per (split of blocks_per_split blocks, KV head,
+                                 sequence); splits past a sequence's length exit at once */
+  SKVD_SCHEDULE_BALANCED = 2  /* the launch's blocks, in (sequence, KV head, block) order, cut
+                                 on the device into W equal contiguous shares, W = min(grid,
+                                 blocks / blocks_per_split); a share may cover parts of several
+                                 (sequence, KV head) rows and writes one partial per part.
+                                 Needs max_batch <= 64 and more than one split. */
+} skvd_schedule;
+
 /* Static shape of a plan. All sizes are upper bounds of what skvd_decode may be given. */
 typedef struct {
   int32_t num_qo_heads;   /* Hq; Hq % Hkv == 0 */
@@ -109,6 +121,9 @@ typedef struct {
   int32_t force_blocks_per_split; /* 0: heuristic; > 0: 64-token blocks per split */
   int32_t force_reducer;  /* skvd_reducer; 0 = choose by partial count */
   int32_t debug;          /* != 0: kernels record contract violations in the status word */
+  int32_t schedule;       /* skvd_schedule; 0 = auto */
+  int32_t wgs_per_cu;     /* balanced schedule: workgroups launched per compute unit (0: 4;
+                             3 at head_dim 256; 8 for int8 at head_dim 128 with G*T <= 4) */
 } skvd_plan_params;
 
 /* What a plan resolved to (for logs and tests). */
@@ -122,6 +137,11 @@ typedef struct {
   int64_t rows_cap;         /* max_batch * max_q_per_seq * Hq */
   uint64_t workspace_bytes;
   uint64_t status_offset;   /* byte offset of the uint32 status word in the workspace */
+  int32_t schedule;         /* skvd_schedule actually used */
+  int32_t part_stride;      /* partial slots per row in the workspace (splits_cap, + 1 when
+                               balanced: a row may straddle one more share boundary) */
+  int32_t grid_wgs;         /* partial-kernel workgroups launched (upper bound) */
+  int32_t reserved;
 } skvd_plan_info;
 
 /* Status-word bits (debug plans). */
@@ -144,7 +164,9 @@ typedef struct {
   int64_t num_v_pages;       /* pages in the V pool (>= 1) */
   const void *k_scales;      /* int8 only: f16 [num_k_pages, P, Hkv, D/32]; else NULL */
   const void *v_scales;      /* int8 only: f16 [num_v_pages, P, Hkv, D/32]; else NULL */
-  int64_t scale_page_stride; /* elements; shared by both scale pools */
+  int64_t scale_page_stride; /* elements; shared by both scale pools; the D/32 scales of a
+                                token-head are contiguous; pools 8-byte aligned and all three
+                                strides multiples of 4 elements (else SKVD_ERR_LAYOUT) */
   int64_t scale_tok_stride;
   int64_t scale_head_stride;
   const int32_t *page_table; /* [B, table_stride]; entry i of row b is the page holding

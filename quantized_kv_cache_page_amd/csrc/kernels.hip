@@ -161,6 +161,43 @@ __device__ __forceinline__ void h16_pairs(const half8 &a, const half8 &b, half2v
   }
 }
 
+// ----------------------------------------------------------------------------- balanced schedule
+// The batch's 64-token blocks in (sequence, KV head, block) order, cut into n_shares equal
+// contiguous shares: share w covers [w N / W, (w + 1) N / W). One sequence per lane (the plan
+// limits the batch to 64); every lane of the wave must be active. Per lane: the sequence's
+// clamped length, its block count and the blocks of all earlier sequences.
+struct Shares {
+  int len_l;
+  unsigned nb_l, pre_l;
+  int64_t n_blocks;  // N = Hkv * sum of block counts
+  int n_shares;      // W = min(grid, N / bps), at least 1 when N > 0
+};
+
+__device__ __forceinline__ Shares balanced_shares(const LaunchArgs &a, int debug) {
+  const int lane = threadIdx.x;
+  Shares sh;
+  sh.len_l = lane < a.batch ? clamp_len(a.kv_len[lane], a.max_kv_len, a.status, debug) : 0;
+  sh.nb_l = (unsigned)(sh.len_l + 63) >> 6;
+  unsigned inc = sh.nb_l;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const unsigned up = __shfl_up(inc, d);
+    if (lane >= d) inc += up;
+  }
+  sh.pre_l = inc - sh.nb_l;
+  // (readlane: the total is wave-uniform, so it and everything derived from it stay scalar)
+  sh.n_blocks = (int64_t)(unsigned)__builtin_amdgcn_readlane((int)inc, 63) * a.Hkv;
+  sh.n_shares = sh.n_blocks == 0
+                    ? 0
+                    : (int)max((int64_t)1, min((int64_t)a.grid_wgs, sh.n_blocks / a.bps));
+  return sh;
+}
+
+// The share holding global block x (0 <= x < N): the largest w with floor(w N / W) <= x.
+__device__ __forceinline__ int share_of(int64_t x, int64_t n_blocks, int n_shares) {
+  return (int)(((x + 1) * n_shares - 1) / n_blocks);
+}
+
 // ----------------------------------------------------------------------------- partial kernel
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef short short4v __attribute__((ext_vector_type(4)));
@@ -176,15 +213,26 @@ __device__ __forceinline__ int swz(int r, int c) {
 
 // D: head_dim (128/256). RB: 4-row quarters of the 16 MFMA rows in use (rows = G*T <= 4*RB).
 // I8: int8 cache with f16 scales per 32 elements. FAST: page_size >= 16, so each 16-token
-// tile lies in one page and its page id is wave-uniform. CH: tokens per chunk (32 at D=128,
-// 16 at D=256): the K and V registers of a chunk bound how many waves fit on a SIMD.
+// tile lies in one page and its page id is wave-uniform. CH: tokens per chunk (16, 32 or
+// 64): the K and V registers of a chunk bound how many waves fit on a SIMD.
 // PVM: P.V on the MFMA through an LDS copy of the chunk's V (dense when several query rows
 // share the KV head); otherwise P.V on the vector ALU as f16 pair dot products
 // (v_dot2_f32_f16) from the V registers, pairing token t with token t + 16.
+// Minimum waves per SIMD the register allocator must leave room for. int8 at D=128 is vector-
+// ALU heavy and runs several waves per SIMD (the plan launches 8 workgroups per CU): three,
+// at the cost of three values spilled and reloaded once per segment. f16 single-quarter
+// variants run one wave per SIMD under the balanced schedule and gain more from registers
+// spent on instruction-level parallelism than from occupancy: no floor.
+template <int D, int RB, bool I8>
+constexpr int partial_waves() {
+  return D == 128 ? (RB == 1 ? (I8 ? 3 : 1) : 2) : 1;
+}
+
 template <int D, int RB, bool I8, bool FAST, int CH, bool PVM>
-__global__ __launch_bounds__(64) void partial_kernel(LaunchArgs a) {
-  static_assert(CH == 16 || CH == 32, "chunk");
-  static_assert(PVM || CH == 32, "the vector P.V pairs the two 16-token tiles of a chunk");
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>())))
+void partial_kernel(LaunchArgs a) {
+  static_assert(CH == 16 || CH == 32 || (CH == 64 && !PVM), "chunk");
+  static_assert(PVM || CH % 32 == 0, "the vector P.V pairs 16-token tiles 2h and 2h + 1");
   constexpr int NT = CH / 16;    // 16-token score tiles per chunk
   constexpr int KS = D / 32;     // score MFMA steps of 32 head_dim elements
   constexpr int LPR = D / 8;     // lanes per V row in the load layout, 8 elements each
@@ -200,30 +248,79 @@ __global__ __launch_bounds__(64) void partial_kernel(LaunchArgs a) {
 
   __shared__ __attribute__((aligned(16))) char v_lds[PVM ? CH * ROWB : 16];  // chunk V, f16
   __shared__ __attribute__((aligned(16))) float p_lds[PVM ? RM * PSTR : 4];  // [row][token]
-  __shared__ float vs_lds[PVM && I8 ? CH * (D / 32) : 1];  // int8 V scales [token][group]
+  // int8 V scales of the chunk, [token][group] f16, staged through LDS from one load per lane
+  __shared__ __attribute__((aligned(16))) uint2v vsc_lds[I8 ? CH * (D / 128) : 1];
+  const _Float16 *vsh = (const _Float16 *)vsc_lds;
   // vector P.V: probabilities as f16 pairs (token tp, token tp + 16) per row: [tp][row]
-  __shared__ __attribute__((aligned(16))) unsigned p2_lds[PVM ? 4 : 16 * RM];
+  __shared__ __attribute__((aligned(16))) unsigned p2_lds[PVM ? 4 : (CH / 2) * RM];
 
-  // Workgroup order: split fastest, then KV head, then sequence, with an odd split stride.
-  // Consecutive workgroups go to the eight XCDs in turn; with an even stride split s of
-  // every (head, sequence) would land on the same XCD, and the live splits of a ragged batch
-  // (short sequences have few) would pile onto the XCDs of the low split indices. The odd
-  // stride rotates each row's start over all eight. Indices past splits_cap are padding.
   const int lane = threadIdx.x;
   const int Hkv = a.Hkv;
-  const int wg = blockIdx.x;
-  const int split = wg % a.split_stride;
-  const int head_seq = wg / a.split_stride;
-  const int kvh = head_seq % Hkv, b = head_seq / Hkv;
-  if (split >= a.splits_cap) return;
   const int T = a.T, G = a.G, R = G * T;
-  const int L = clamp_len(a.kv_len[b], a.max_kv_len, a.status, a.debug);
-  const int nblk = (L + 63) >> 6;
-  const int blk0 = split * a.bps;
-  if (!a.single && blk0 >= nblk) return;  // beyond this sequence: no partial is read
-  const int tok0 = blk0 * 64;
-  const int tok_end = min(min(blk0 + a.bps, nblk) * 64, L);
   const int P1 = (1 << a.page_shift) - 1;
+
+  // ---- this workgroup's segments: (sequence, KV head, block range, partial slot)
+  // Static: workgroup order split fastest, then KV head, then sequence, with an odd split
+  // stride. Consecutive workgroups go to the eight XCDs in turn; with an even stride split s
+  // of every (head, sequence) would land on the same XCD, and the live splits of a ragged
+  // batch would pile onto the XCDs of the low split indices. The odd stride rotates each
+  // row's start over all eight. Indices past splits_cap are padding. One segment.
+  // Balanced: the batch's blocks in (sequence, KV head, block) order are cut into W equal
+  // contiguous shares; workgroup w takes share w, which may cover the end of one row and the
+  // start of the next ones: one segment per row, its partial in slot w - (first share of the
+  // row). Sequence lengths, one per lane, come from kv_len on the device.
+  int st_b = 0, st_kvh = 0, st_split = 0;
+  Shares sh{};
+  int64_t x_cur = 0, x_end = 0;  // balanced: this workgroup's share
+  const int share = blockIdx.x;
+  if (a.balanced) {
+    sh = balanced_shares(a, a.debug);
+    if (share >= sh.n_shares) return;
+    x_cur = share * sh.n_blocks / sh.n_shares;
+    x_end = (share + 1) * sh.n_blocks / sh.n_shares;
+  } else {
+    const int wg = blockIdx.x;
+    st_split = wg % a.split_stride;
+    const int head_seq = wg / a.split_stride;
+    st_kvh = head_seq % Hkv;
+    st_b = head_seq / Hkv;
+    if (st_split >= a.splits_cap) return;
+  }
+  bool pending = true;
+  for (;;) {
+  int b, kvh, slot, L, blk_lo, blk_hi;
+  if (a.balanced) {
+    if (x_cur >= x_end) break;
+    // the sequence holding global block x_cur: Hkv*pre <= x_cur < Hkv*(pre + nb), that is
+    // pre <= x_cur / Hkv < pre + nb (one scalar division, 32-bit lane compares)
+    const unsigned xq = (unsigned)(x_cur / Hkv);
+    const bool mine = sh.pre_l <= xq && xq < sh.pre_l + sh.nb_l;
+    b = __builtin_ctzll(__ballot(mine));
+    const unsigned pre_b = (unsigned)__builtin_amdgcn_readlane((int)sh.pre_l, b);
+    const int nb_b = __builtin_amdgcn_readlane((int)sh.nb_l, b);
+    L = __builtin_amdgcn_readlane(sh.len_l, b);
+    const int64_t off = x_cur - (int64_t)Hkv * pre_b;
+    kvh = (int)(off / nb_b);
+    blk_lo = (int)(off - (int64_t)kvh * nb_b);
+    const int64_t row0 = (int64_t)Hkv * pre_b + (int64_t)kvh * nb_b;  // the row's first block
+    const int64_t seg_end = min(x_end, row0 + nb_b);
+    blk_hi = blk_lo + (int)(seg_end - x_cur);
+    slot = share - share_of(row0, sh.n_blocks, sh.n_shares);
+    x_cur = seg_end;
+  } else {
+    if (!pending) break;
+    pending = false;
+    b = st_b;
+    kvh = st_kvh;
+    slot = st_split;
+    L = clamp_len(a.kv_len[b], a.max_kv_len, a.status, a.debug);
+    const int nblk = (L + 63) >> 6;
+    blk_lo = st_split * a.bps;
+    if (!a.single && blk_lo >= nblk) break;  // beyond this sequence: no partial is read
+    blk_hi = min(blk_lo + a.bps, nblk);
+  }
+  const int tok0 = blk_lo * 64;
+  const int tok_end = min(blk_hi * 64, L);
 
   const char *kbase = (const char *)a.k;
   const char *vbase = (const char *)a.v;
@@ -295,9 +392,12 @@ __global__ __launch_bounds__(64) void partial_kernel(LaunchArgs a) {
   };
 
   Vec kb[NT][KS];
-  float ks_tok[NT][KS];
   Vec vb[NS];
-  _Float16 vs_h[NS];
+  // int8 scales, two f16 per register. K: tile t, groups 2k and 2k + 1 of the lane's token,
+  // from 8-byte loads (each token-head's D/32 scales are contiguous). V: the D/32 scales of
+  // chunk token (lane % CH), one load per lane, handed to the P.V lanes through LDS.
+  half2v ks2[NT][KS / 2];
+  uint2v vsr[D / 128];
 
   // K rows of chunk c0 in the score MFMA B-operand layout: tile t, lane (g4, c16) holds
   // elements 32k + 8*g4 .. +7 of token 16t + c16.
@@ -320,7 +420,12 @@ __global__ __launch_bounds__(64) void partial_kernel(LaunchArgs a) {
                                                 a.s_tok_stride, a.s_head_stride);
           const unsigned so = (unsigned)(tk * (int)a.s_tok_stride);
 #pragma unroll
-          for (int k = 0; k < KS; ++k) ks_tok[t][k] = (float)sb[so + k];
+          for (int k4 = 0; k4 < KS / 4; ++k4) {
+            const uint2v w = *(const uint2v *)(sb + so + 4 * k4);
+            const unsigned w0 = w[0], w1 = w[1];
+            ks2[t][2 * k4] = __builtin_bit_cast(half2v, w0);
+            ks2[t][2 * k4 + 1] = __builtin_bit_cast(half2v, w1);
+          }
         }
       } else {
         const int j = min(jt + c16, tok_end - 1);
@@ -337,7 +442,12 @@ __global__ __launch_bounds__(64) void partial_kernel(LaunchArgs a) {
           const int64_t so = row_offset(pg, j & P1, kvh, a.s_page_stride, a.s_tok_stride,
                                         a.s_head_stride);
 #pragma unroll
-          for (int k = 0; k < KS; ++k) ks_tok[t][k] = (float)ksc[so + k];
+          for (int k4 = 0; k4 < KS / 4; ++k4) {
+            const uint2v w = *(const uint2v *)(ksc + so + 4 * k4);
+            const unsigned w0 = w[0], w1 = w[1];
+            ks2[t][2 * k4] = __builtin_bit_cast(half2v, w0);
+            ks2[t][2 * k4 + 1] = __builtin_bit_cast(half2v, w1);
+          }
         }
       }
     }
@@ -356,11 +466,6 @@ __global__ __launch_bounds__(64) void partial_kernel(LaunchArgs a) {
         const int tk = min((js & 15) + vlane_tok, tok_end - 1 - jte);
         const unsigned off = (unsigned)((tk * (int)a.tok_stride + vlane_el) * ES);
         vb[s2] = *(const Vec *)(base + off);
-        if constexpr (I8) {
-          const _Float16 *sb = vsc + row_offset(pg, jte & P1, kvh, a.s_page_stride,
-                                                a.s_tok_stride, a.s_head_stride);
-          vs_h[s2] = sb[(unsigned)(tk * (int)a.s_tok_stride) + vlane_el / 32];
-        }
       } else {
         const int j = min(js + vlane_tok, tok_end - 1);
         bool cl;
@@ -370,12 +475,27 @@ __global__ __launch_bounds__(64) void partial_kernel(LaunchArgs a) {
         const int64_t off = row_offset(pg, j & P1, kvh, a.page_stride, a.tok_stride,
                                        a.head_stride);
         vb[s2] = *(const Vec *)(vbase + (off + vlane_el) * ES);
-        if constexpr (I8) {
-          const int64_t so = row_offset(pg, j & P1, kvh, a.s_page_stride, a.s_tok_stride,
-                                        a.s_head_stride);
-          vs_h[s2] = vsc[so + vlane_el / 32];
-        }
       }
+    }
+    if constexpr (I8) {
+      // scales of chunk token (lane % CH); a token past the split reads the last one's
+      const int jl = min(c0 + lane % CH, tok_end - 1);
+      int64_t pg;
+      if constexpr (FAST) {
+        const int tl = (jl - c0) >> 4;  // the lane's 16-token tile (its page is wave-uniform)
+        int pgl = pgs[0];
+#pragma unroll
+        for (int t = 1; t < NT; ++t) pgl = tl == t ? pgs[t] : pgl;
+        pg = clamp_page(pgl, a.num_v_pages);
+      } else {
+        bool cl;
+        pg = lookup_page(a.table, a.table_stride, b, jl, a.page_shift, a.num_v_pages, &cl);
+        clamped_any |= cl;
+      }
+      const _Float16 *sp = vsc + row_offset(pg, jl & P1, kvh, a.s_page_stride, a.s_tok_stride,
+                                            a.s_head_stride);
+#pragma unroll
+      for (int k4 = 0; k4 < D / 128; ++k4) vsr[k4] = *(const uint2v *)(sp + 4 * k4);
     }
   };
 
@@ -410,7 +530,7 @@ __global__ __launch_bounds__(64) void partial_kernel(LaunchArgs a) {
         for (int k = 0; k < KS; ++k) {
           float4v part = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[k], i8x8_to_h8(kb[t][k]),
                                                                 (float4v)0.f, 0, 0, 0);
-          S[t] += part * ks_tok[t][k];
+          S[t] += part * (float)ks2[t][k >> 1][k & 1];
         }
       } else {
 #pragma unroll
@@ -453,7 +573,7 @@ __global__ __launch_bounds__(64) void partial_kernel(LaunchArgs a) {
 
     if constexpr (PVM) {
       // ---- probabilities to LDS as [row][token]; the chunk's V rows to LDS (int8 widened
-      // exactly to f16, scales to vs_lds)
+      // exactly to f16; int8 V scales to vsc_lds)
       if (g4 < RB) {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
@@ -466,11 +586,16 @@ __global__ __launch_bounds__(64) void partial_kernel(LaunchArgs a) {
         half8 h;
         if constexpr (I8) {
           h = i8x8_to_h8(vb[s2]);
-          if ((lane % LPR) % 4 == 0) vs_lds[row * (D / 32) + vlane_el / 32] = (float)vs_h[s2];
         } else {
           h = vb[s2];
         }
         *(half8 *)(v_lds + swz<ROWB>(row, lane % LPR)) = h;
+      }
+      if constexpr (I8) {
+        if (lane < CH) {
+#pragma unroll
+          for (int k4 = 0; k4 < D / 128; ++k4) vsc_lds[lane * (D / 128) + k4] = vsr[k4];
+        }
       }
       wave_sync();
 
@@ -494,7 +619,7 @@ __global__ __launch_bounds__(64) void partial_kernel(LaunchArgs a) {
         for (int gg = 0; gg < D / 32; ++gg)
 #pragma unroll
           for (int i = 0; i < KPL; ++i)
-            pa[gg][i] = (_Float16)(pv[i] * vs_lds[(KPL * g4 + i) * (D / 32) + gg]);
+            pa[gg][i] = (_Float16)(pv[i] * (float)vsh[(KPL * g4 + i) * (D / 32) + gg]);
       } else {
 #pragma unroll
         for (int i = 0; i < KPL; ++i) pa[0][i] = (_Float16)pv[i];
@@ -520,18 +645,28 @@ __global__ __launch_bounds__(64) void partial_kernel(LaunchArgs a) {
           acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(pop, vt, acc[dt], 0, 0, 0);
       }
     } else {
-      // ---- probabilities to LDS as f16 pairs (token c16, token 16 + c16) per row
+      // ---- probabilities to LDS as f16 pairs (token 32h + c16, token 32h + 16 + c16) per row
       if (g4 < RB) {
-        uint4v w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          w[e] = __builtin_bit_cast(unsigned, half2v{(_Float16)S[0][e], (_Float16)S[1][e]});
-        *(uint4v *)&p2_lds[c16 * RM + 4 * g4] = w;
+        for (int h = 0; h < NT / 2; ++h) {
+          uint4v w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            w[e] = __builtin_bit_cast(unsigned,
+                                      half2v{(_Float16)S[2 * h][e], (_Float16)S[2 * h + 1][e]});
+          *(uint4v *)&p2_lds[(16 * h + c16) * RM + 4 * g4] = w;
+        }
       }
       // per-row rescale factors (row-uniform within the 16 lanes of a DPP row)
       float al[RM];
 #pragma unroll
       for (int r = 0; r < RM; ++r) al[r] = readlane_f(alpha[r & 3], 16 * (r >> 2));
+      if constexpr (I8) {
+        if (lane < CH) {
+#pragma unroll
+          for (int k4 = 0; k4 < D / 128; ++k4) vsc_lds[lane * (D / 128) + k4] = vsr[k4];
+        }
+      }
       wave_sync();
       bool rescale = false;
 #pragma unroll
@@ -542,10 +677,13 @@ __global__ __launch_bounds__(64) void partial_kernel(LaunchArgs a) {
 #pragma unroll
           for (int i = 0; i < 8; ++i) accv[r][i] *= al[r];
       }
-      // ---- P.V: load steps s and s + NS/2 hold tokens tp and tp + 16 of the lane's slot
+      // ---- P.V: in the 32 tokens from 32h, load steps s and s + SPT hold tokens tp and
+      // tp + 16 of the lane's slot (SPT load steps per 16-token tile)
+      constexpr int SPT = 16 / TPS;
 #pragma unroll
-      for (int s2 = 0; s2 < NS / 2; ++s2) {
-        const int tp = TPS * s2 + vlane_tok;
+      for (int ps = 0; ps < NS / 2; ++ps) {
+        const int h = ps / SPT, s2 = 2 * SPT * h + ps % SPT, s3 = s2 + SPT;
+        const int tp = 16 * h + TPS * (ps % SPT) + vlane_tok;
         half2v pp[RM];
 #pragma unroll
         for (int q = 0; q < RB; ++q) {
@@ -560,12 +698,13 @@ __global__ __launch_bounds__(64) void partial_kernel(LaunchArgs a) {
         half2v vp[8];
         if constexpr (I8) {
           // int8 V: the pair's per-32 scales fold into the probabilities
-          const half2v sc = {vs_h[s2], vs_h[s2 + NS / 2]};
+          const int ta = TPS * s2 + vlane_tok, g = vlane_el / 32;
+          const half2v sc = {vsh[ta * (D / 32) + g], vsh[(ta + 16) * (D / 32) + g]};
 #pragma unroll
           for (int r = 0; r < RM; ++r) pp[r] *= sc;
-          i8_pairs(vb[s2], vb[s2 + NS / 2], vp);
+          i8_pairs(vb[s2], vb[s3], vp);
         } else {
-          h16_pairs(vb[s2], vb[s2 + NS / 2], vp);
+          h16_pairs(vb[s2], vb[s3], vp);
         }
 #pragma unroll
         for (int r = 0; r < RM; ++r)
@@ -595,11 +734,10 @@ __global__ __launch_bounds__(64) void partial_kernel(LaunchArgs a) {
 
   if constexpr (PVM) {
     // ---- output: lanes of group g4 hold rows 4*g4 + e, column 16*dt + c16
-    if (g4 >= RB) return;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 4 * g4 + e;
-      if (r >= R) continue;
+      if (g4 >= RB || r >= R) continue;
       const int t = r / G, hg = r - (r / G) * G;
       const int64_t row = ((int64_t)b * T + t) * Hq + kvh * G + hg;
       if (a.single) {
@@ -610,11 +748,11 @@ __global__ __launch_bounds__(64) void partial_kernel(LaunchArgs a) {
         for (int dt = 0; dt < NDT; ++dt) o[16 * dt] = (_Float16)(acc[dt][e] * inv);
         if (a.lse && c16 == 0) a.lse[row] = l > 0.f ? (m[e] + __log2f(l)) * kLn2 : kNegInf;
       } else {
-        float *dst = a.ws_o + (row * a.splits_cap + split) * D + c16;
+        float *dst = a.ws_o + (row * a.part_stride + slot) * D + c16;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) dst[16 * dt] = acc[dt][e];
         if (c16 == 0) {
-          float *ml = a.ws_ml + (row * a.splits_cap + split) * 2;
+          float *ml = a.ws_ml + (row * a.part_stride + slot) * 2;
           ml[0] = m[e];
           ml[1] = lsum[e];
         }
@@ -637,10 +775,9 @@ __global__ __launch_bounds__(64) void partial_kernel(LaunchArgs a) {
       mr[r] = readlane_f(m[r & 3], 16 * (r >> 2));
       lr[r] = readlane_f(lsum[r & 3], 16 * (r >> 2));
     }
-    if (lane >= LPR) return;
 #pragma unroll
     for (int r = 0; r < RM; ++r) {
-      if (r >= R) continue;
+      if (lane >= LPR || r >= R) continue;
       const int t = r / G, hg = r - (r / G) * G;
       const int64_t row = ((int64_t)b * T + t) * Hq + kvh * G + hg;
       if (a.single) {
@@ -652,28 +789,39 @@ __global__ __launch_bounds__(64) void partial_kernel(LaunchArgs a) {
         *(half8 *)((_Float16 *)a.o + row * D + vlane_el) = out;
         if (a.lse && lane == 0) a.lse[row] = l > 0.f ? (mr[r] + __log2f(l)) * kLn2 : kNegInf;
       } else {
-        float *dst = a.ws_o + (row * a.splits_cap + split) * D + vlane_el;
+        float *dst = a.ws_o + (row * a.part_stride + slot) * D + vlane_el;
         *(float4v *)dst = float4v{accv[r][0], accv[r][1], accv[r][2], accv[r][3]};
         *(float4v *)(dst + 4) = float4v{accv[r][4], accv[r][5], accv[r][6], accv[r][7]};
         if (lane == 0) {
-          float *ml = a.ws_ml + (row * a.splits_cap + split) * 2;
+          float *ml = a.ws_ml + (row * a.part_stride + slot) * 2;
           ml[0] = mr[r];
           ml[1] = lr[r];
         }
       }
     }
   }
+  }  // segments
 }
 
 // ----------------------------------------------------------------------------- merge kernels
-__device__ __forceinline__ void row_coords(const LaunchArgs &a, int64_t row, int *b) {
-  *b = (int)(row / ((int64_t)a.T * a.Hq));
-}
-
-__device__ __forceinline__ int splits_of(const LaunchArgs &a, int b) {
-  const int L = clamp_len(a.kv_len[b], a.max_kv_len, a.status, 0);
-  const int nblk = (L + 63) >> 6;
-  return (nblk + a.bps - 1) / a.bps;
+// Partials of output row `row` (sequence b, query head -> KV head): static, the splits that
+// cover the sequence's blocks; balanced, the shares the (sequence, KV head) row's blocks meet,
+// by the partial kernel's own integer arithmetic. Called by the whole wave.
+__device__ __forceinline__ int parts_of_row(const LaunchArgs &a, int64_t row) {
+  const int b = (int)(row / ((int64_t)a.T * a.Hq));
+  if (!a.balanced) {
+    const int L = clamp_len(a.kv_len[b], a.max_kv_len, a.status, 0);
+    const int nblk = (L + 63) >> 6;
+    return (nblk + a.bps - 1) / a.bps;
+  }
+  const int kvh = (int)(row % a.Hq) / a.G;
+  const Shares sh = balanced_shares(a, 0);
+  const int64_t pre_b = (unsigned)__builtin_amdgcn_readlane((int)sh.pre_l, b);
+  const int64_t nb_b = __builtin_amdgcn_readlane((int)sh.nb_l, b);
+  if (nb_b == 0) return 0;
+  const int64_t row0 = a.Hkv * pre_b + kvh * nb_b;
+  return share_of(row0 + nb_b - 1, sh.n_blocks, sh.n_shares) -
+         share_of(row0, sh.n_blocks, sh.n_shares) + 1;
 }
 
 // Final write of one row from a normalized accumulator.
@@ -700,11 +848,9 @@ template <int D>
 __global__ __launch_bounds__(64) void merge_direct(LaunchArgs a) {
   constexpr int PER = D / 64;
   const int64_t row = blockIdx.x;
-  int b;
-  row_coords(a, row, &b);
-  const int n = splits_of(a, b);
-  const float *ml = a.ws_ml + row * a.splits_cap * 2;
-  const float *po = a.ws_o + row * a.splits_cap * D + PER * threadIdx.x;
+  const int n = parts_of_row(a, row);
+  const float *ml = a.ws_ml + row * a.part_stride * 2;
+  const float *po = a.ws_o + row * a.part_stride * D + PER * threadIdx.x;
   float M = kNegInf;
   for (int s = 0; s < n; ++s) M = fmaxf(M, ml[2 * s]);
   float S = 0.f, acc[PER] = {};
@@ -763,11 +909,9 @@ template <int D>
 __global__ __launch_bounds__(64) void merge_rows(LaunchArgs a) {
   constexpr int PER = D / 64;
   const int64_t row = blockIdx.x;
-  int b;
-  row_coords(a, row, &b);
-  const int n = splits_of(a, b);
+  const int n = parts_of_row(a, row);
   float M, S, acc[PER];
-  merge_span<D>(a.ws_ml + row * a.splits_cap * 2, a.ws_o + row * a.splits_cap * D, n, &M, &S,
+  merge_span<D>(a.ws_ml + row * a.part_stride * 2, a.ws_o + row * a.part_stride * D, n, &M, &S,
                 acc);
   write_row<D>(a, row, acc, M, S);
 }
@@ -779,14 +923,12 @@ __global__ __launch_bounds__(64) void merge_hier1(LaunchArgs a) {
   constexpr int PER = D / 64;
   const int64_t row = blockIdx.x;
   const int g = blockIdx.y;
-  int b;
-  row_coords(a, row, &b);
-  const int n = splits_of(a, b);
+  const int n = parts_of_row(a, row);
   const int s0 = g * kHierGroup;
   if (s0 >= n) return;
   const int cnt = min(kHierGroup, n - s0);
   float M, S, acc[PER];
-  merge_span<D>(a.ws_ml + (row * a.splits_cap + s0) * 2, a.ws_o + (row * a.splits_cap + s0) * D,
+  merge_span<D>(a.ws_ml + (row * a.part_stride + s0) * 2, a.ws_o + (row * a.part_stride + s0) * D,
                 cnt, &M, &S, acc);
   float *dst = a.ws_ho + (row * a.hier_groups_cap + g) * D + PER * threadIdx.x;
 #pragma unroll
@@ -803,9 +945,7 @@ template <int D>
 __global__ __launch_bounds__(64) void merge_hier2(LaunchArgs a) {
   constexpr int PER = D / 64;
   const int64_t row = blockIdx.x;
-  int b;
-  row_coords(a, row, &b);
-  const int n = splits_of(a, b);
+  const int n = parts_of_row(a, row);
   const int ng = (n + kHierGroup - 1) / kHierGroup;
   float M, S, acc[PER];
   merge_span<D>(a.ws_hml + row * a.hier_groups_cap * 2, a.ws_ho + row * a.hier_groups_cap * D,
@@ -867,21 +1007,22 @@ int launch_stream_read(const void *buf, size_t n16, uint32_t *sink, void *stream
 }
 
 // ----------------------------------------------------------------------------- launchers
-// Tokens per chunk and P.V unit per variant. D=128 chunks hold 32 tokens; D=256 chunks 16
-// (register bound). One query row quarter at D=128 takes the vector P.V (pair dot products
-// from registers, no LDS copy of V); more rows, or D=256, make P.V a dense tile for the MFMA.
-template <int D, int RB>
-constexpr int chunk_tokens() {
-  return D == 128 ? 32 : 16;
-}
+// Tokens per chunk and P.V unit per variant. D=128 chunks hold 32 tokens, D=256 chunks 16
+// (register bound; 64 int8 tokens at D=128 measured slower: two waves per SIMD). One query
+// row quarter at D=128 takes the vector P.V (pair dot products from registers, no LDS copy
+// of V); more rows, or D=256, make P.V a dense tile for the MFMA.
 template <int D, int RB>
 constexpr bool pv_on_mfma() {
   return !(D == 128 && RB == 1);
 }
+template <int D, int RB, bool I8>
+constexpr int chunk_tokens() {
+  return D == 128 ? 32 : 16;
+}
 
 template <int D, int RB, bool I8>
 static void launch_partial_t(const LaunchArgs &la, dim3 grid, hipStream_t st, bool fast) {
-  constexpr int CH = chunk_tokens<D, RB>();
+  constexpr int CH = chunk_tokens<D, RB, I8>();
   constexpr bool PVM = pv_on_mfma<D, RB>();
   if (fast)
     partial_kernel<D, RB, I8, true, CH, PVM><<<grid, 64, 0, st>>>(la);
@@ -901,8 +1042,10 @@ static void launch_partial_rb(const Plan &p, const LaunchArgs &la, dim3 grid, hi
 
 int launch_partial(const Plan &p, const LaunchArgs &la, void *stream) {
   hipStream_t st = (hipStream_t)stream;
-  // one-dimensional grid, split fastest (the plan keeps the count below 2^31)
-  dim3 grid((unsigned)((int64_t)la.split_stride * la.Hkv * la.batch));
+  // one-dimensional grid: balanced, the plan's share count bound; static, split fastest over
+  // (split, KV head, sequence) (the plan keeps the count below 2^31)
+  dim3 grid(la.balanced ? (unsigned)la.grid_wgs
+                        : (unsigned)((int64_t)la.split_stride * la.Hkv * la.batch));
   const bool i8 = la.int8;
   if (la.D == 128) {
     if (i8) launch_partial_rb<128, true>(p, la, grid, st);

@@ -74,6 +74,10 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
   if (prm.force_blocks_per_split < 0)
     return fail(err, errn, SKVD_ERR_PLAN, "force_blocks_per_split=%d",
                 prm.force_blocks_per_split);
+  if (prm.schedule < SKVD_SCHEDULE_AUTO || prm.schedule > SKVD_SCHEDULE_BALANCED)
+    return fail(err, errn, SKVD_ERR_PLAN, "schedule=%d unknown", prm.schedule);
+  if (prm.wgs_per_cu < 0 || prm.wgs_per_cu > 64)
+    return fail(err, errn, SKVD_ERR_PLAN, "wgs_per_cu=%d outside 0..64", prm.wgs_per_cu);
 
   Plan p{};
   p.prm = prm;
@@ -116,30 +120,58 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
   p.bps = (int)bps;
   p.splits_cap = (p.max_blocks + p.bps - 1) / p.bps;
 
+  // Schedule. Static: workgroups are (split, KV head, sequence) at fixed block offsets, so a
+  // ragged batch leaves some compute units with more work than others once the grid fits the
+  // chip in one round. Balanced: equal shares of the blocks actually present, cut on the device
+  // from kv_len (one sequence per lane, hence the batch limit); every share is at least
+  // bps blocks, so a row meets at most splits_cap + 1 shares.
+  int sched = prm.schedule;
+  const bool can_balance = p.splits_cap > 1 && prm.max_batch <= kBalancedMaxBatch &&
+                           prm.force_reducer != SKVD_REDUCER_NONE;
+  if (sched == SKVD_SCHEDULE_AUTO)
+    sched = can_balance ? SKVD_SCHEDULE_BALANCED : SKVD_SCHEDULE_STATIC;
+  if (sched == SKVD_SCHEDULE_BALANCED && !can_balance)
+    return fail(err, errn, SKVD_ERR_PLAN, "balanced schedule needs more than one split, "
+                "max_batch <= %d and a reducer (plan: %d splits, max_batch %d)",
+                kBalancedMaxBatch, p.splits_cap, prm.max_batch);
+  p.schedule = sched;
+  if (sched == SKVD_SCHEDULE_BALANCED) {
+    p.part_stride = p.splits_cap + 1;
+    // Workgroups per CU (measured on MI355X): about three resident waves per CU saturate the
+    // memory pipes of an f16 stream; int8 at D=128 also needs vector-ALU throughput, so more
+    // waves; D=256 workgroups are the largest (one wave per SIMD fits).
+    const bool i8 = prm.kv_dtype == SKVD_KV_I8_F16SCALE32;
+    const int auto_wpc = D == 256 ? 3 : (i8 && p.row_blocks == 1 ? 8 : kDefaultWgsPerCu);
+    p.grid_wgs = (prm.wgs_per_cu ? prm.wgs_per_cu : auto_wpc) * num_cus;
+  } else {
+    p.part_stride = p.splits_cap;
+    p.grid_wgs = (int)((int64_t)(p.splits_cap | 1) * per_split);
+  }
+
   // Reducer: total over every partial count.
   int red = prm.force_reducer;
   if (red == SKVD_REDUCER_AUTO) {
-    if (p.splits_cap == 1) red = SKVD_REDUCER_NONE;
-    else if (p.splits_cap <= 4) red = SKVD_REDUCER_DIRECT;
-    else if (p.splits_cap <= 64) red = SKVD_REDUCER_COOPERATIVE;
+    if (p.part_stride == 1) red = SKVD_REDUCER_NONE;
+    else if (p.part_stride <= 4) red = SKVD_REDUCER_DIRECT;
+    else if (p.part_stride <= 64) red = SKVD_REDUCER_COOPERATIVE;
     else if (p.rows_cap >= 2LL * num_cus) red = SKVD_REDUCER_MULTIPASS;
     else red = SKVD_REDUCER_HIERARCHICAL;
   }
-  if (red == SKVD_REDUCER_NONE && p.splits_cap != 1)
+  if (red == SKVD_REDUCER_NONE && p.part_stride != 1)
     return fail(err, errn, SKVD_ERR_PLAN, "reducer none needs one split, plan has %d",
-                p.splits_cap);
-  if (red == SKVD_REDUCER_COOPERATIVE && p.splits_cap > 64)
+                p.part_stride);
+  if (red == SKVD_REDUCER_COOPERATIVE && p.part_stride > 64)
     return fail(err, errn, SKVD_ERR_PLAN, "cooperative reducer covers at most 64 partials, "
-                "plan has %d", p.splits_cap);
+                "plan has %d", p.part_stride);
   p.reducer = red;
   p.hier_groups_cap = red == SKVD_REDUCER_HIERARCHICAL
-                          ? (p.splits_cap + kHierGroup - 1) / kHierGroup : 0;
+                          ? (p.part_stride + kHierGroup - 1) / kHierGroup : 0;
 
   // Workspace: status word, then partials (and hierarchical intermediates).
   size_t off = 0;
   p.off_status = off;
   off = align_up(off + sizeof(uint32_t));
-  const size_t parts = red == SKVD_REDUCER_NONE ? 0 : (size_t)p.rows_cap * p.splits_cap;
+  const size_t parts = red == SKVD_REDUCER_NONE ? 0 : (size_t)p.rows_cap * p.part_stride;
   p.off_ml = off;
   off = align_up(off + parts * 2 * sizeof(float));
   p.off_o = off;
@@ -189,10 +221,12 @@ skvd_status check_args(const Plan &p, const skvd_decode_args *a, size_t ws_bytes
     return fail(err, errn, SKVD_ERR_LAYOUT, "K/V pools must be aligned to their vector load "
                 "and have page/token/head strides that are non-negative multiples of 8 "
                 "elements (head_dim dense, same strides for K and V)");
-  if (i8 && (!aligned(a->k_scales, 2) || !aligned(a->v_scales, 2) || a->scale_page_stride < 0 ||
-             a->scale_tok_stride < 0 || a->scale_head_stride < 0))
-    return fail(err, errn, SKVD_ERR_LAYOUT, "scale pools must be 2-byte aligned with "
-                "non-negative strides");
+  // Scales: the D/32 scales of one token-head are read with 8-byte loads.
+  if (i8 && (!aligned(a->k_scales, 8) || !aligned(a->v_scales, 8) || a->scale_page_stride < 0 ||
+             a->scale_tok_stride < 0 || a->scale_head_stride < 0 || a->scale_page_stride % 4 ||
+             a->scale_tok_stride % 4 || a->scale_head_stride % 4))
+    return fail(err, errn, SKVD_ERR_LAYOUT, "scale pools must be 8-byte aligned with "
+                "non-negative strides that are multiples of 4 elements");
   // Within a 16-token tile the kernels address rows with 32-bit byte offsets.
   const int64_t es = i8 ? 1 : 2;
   if ((16 * a->tok_stride + D) * es >= (int64_t(1) << 31) ||
@@ -246,6 +280,9 @@ void fill_launch_args(const Plan &p, const skvd_decode_args &a, void *ws, Launch
   l.bps = p.bps;
   l.splits_cap = p.splits_cap;
   l.split_stride = p.splits_cap | 1;
+  l.balanced = p.schedule == SKVD_SCHEDULE_BALANCED;
+  l.grid_wgs = p.grid_wgs;
+  l.part_stride = p.part_stride;
   l.max_kv_len = p.prm.max_kv_len;
   l.hier_groups_cap = p.hier_groups_cap;
   l.int8 = p.prm.kv_dtype == SKVD_KV_I8_F16SCALE32;

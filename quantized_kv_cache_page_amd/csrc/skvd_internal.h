@@ -12,6 +12,8 @@ namespace skvd {
 constexpr int kBlockTokens = 64;  // one partial block: 64 consecutive KV positions
 constexpr int kHierGroup = 64;    // partials merged by one first-level hierarchical workgroup
 constexpr size_t kAlign = 256;
+constexpr int kBalancedMaxBatch = 64;  // balanced schedule: one sequence per lane of a wave
+constexpr int kDefaultWgsPerCu = 4;
 
 struct Plan {
   skvd_plan_params prm;
@@ -21,7 +23,10 @@ struct Plan {
   int num_cus;
   int max_blocks;     // ceil(max_kv_len / 64)
   int bps;            // 64-token blocks per split
-  int splits_cap;     // ceil(max_blocks / bps): partial stride per row
+  int splits_cap;     // ceil(max_blocks / bps): static splits per row at max_kv_len
+  int schedule;       // resolved skvd_schedule
+  int part_stride;    // partial slots per row: splits_cap (+ 1 when balanced)
+  int grid_wgs;       // partial-kernel grid (static: split_stride * Hkv * max_batch)
   int reducer;        // resolved skvd_reducer
   int hier_groups_cap;
   int64_t rows_cap;
@@ -43,9 +48,10 @@ struct LaunchArgs {
   int batch, T, Hq, Hkv, G, D, page_shift;
   float scale_log2;  // sm_scale * log2(e): scores are kept in base 2
   int bps, splits_cap, split_stride, max_kv_len, hier_groups_cap;  // stride: odd, >= cap
+  int balanced, grid_wgs, part_stride;
   int int8, debug;
-  float *ws_ml;      // [rows_cap][splits_cap][2]  (max in log2 units, sum)
-  float *ws_o;       // [rows_cap][splits_cap][D]  unnormalized f32 output
+  float *ws_ml;      // [rows_cap][part_stride][2]  (max in log2 units, sum)
+  float *ws_o;       // [rows_cap][part_stride][D]  unnormalized f32 output
   float *ws_hml;     // [rows_cap][hier_groups_cap][2]
   float *ws_ho;      // [rows_cap][hier_groups_cap][D]
   unsigned *status;

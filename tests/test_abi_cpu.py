@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol():
     for s in syms:
         assert hasattr(L, s), s
     assert set(syms) == set(bd.SIGNATURES), set(syms) ^ set(bd.SIGNATURES)
-    assert L.skvd_abi_version() == 1
+    assert L.skvd_abi_version() == bd.ABI_VERSION == 2
 
 
 def plan(**kw):
@@ -61,21 +61,40 @@ def test_plan_splits_and_total_reducer(maxlen, bps):
     # the reducer choice is total: every partial count has one
     assert p.reducer in ("none", "direct", "cooperative", "multipass", "hierarchical")
     if i.splits_cap == 1:
-        assert p.reducer == "none"
+        assert p.reducer == "none" and p.schedule == "static" and i.part_stride == 1
+    else:  # max_batch 32 <= 64: the balanced schedule, one more slot per row
+        assert p.schedule == "balanced" and i.part_stride == i.splits_cap + 1
+        assert i.grid_wgs == 4 * 256
     if p.reducer == "cooperative":
-        assert i.splits_cap <= 64
+        assert i.part_stride <= 64
     if p.reducer == "hierarchical":
-        assert i.hier_groups_cap == -(-i.splits_cap // 64)
-    # workspace holds the status word plus (m, l, D floats) per row and split
+        assert i.hier_groups_cap == -(-i.part_stride // 64)
+    # workspace holds the status word plus (m, l, D floats) per row and partial slot
     rows = 32 * 1 * 32
-    need = 0 if p.reducer == "none" else rows * i.splits_cap * (2 + 128) * 4
+    need = 0 if p.reducer == "none" else rows * i.part_stride * (2 + 128) * 4
     assert i.workspace_bytes >= need + 4
+
+
+def test_schedule_choice():
+    assert plan(max_batch=64).schedule == "balanced"
+    p = plan(max_batch=65)
+    assert p.schedule == "static" and p.info.part_stride == p.info.splits_cap
+    assert p.info.grid_wgs == (p.info.splits_cap | 1) * 8 * 65
+    s = plan(schedule="static")
+    assert s.schedule == "static" and s.info.part_stride == s.info.splits_cap
+    w = plan(wgs_per_cu=7, num_cus=100)
+    assert w.schedule == "balanced" and w.info.grid_wgs == 700
+    assert "schedule=balanced" in w.describe()
+    # defaults per variant: 4 per CU, 3 at head_dim 256, 8 for int8 single-quarter tiles
+    assert plan(head_dim=256, num_kv_heads=16).info.grid_wgs == 3 * 256
+    assert plan(kv_dtype="i8").info.grid_wgs == 8 * 256
+    assert plan(kv_dtype="i8", max_q_per_seq=2).info.grid_wgs == 4 * 256
 
 
 @pytest.mark.parametrize("red", ["direct", "multipass", "hierarchical"])
 def test_forced_reducers_cover_any_count(red):
     p = plan(max_kv_len=262208, force_blocks_per_split=1, force_reducer=red)
-    assert p.info.splits_cap == 4097 and p.reducer == red
+    assert p.info.splits_cap == 4097 and p.info.part_stride == 4098 and p.reducer == red
 
 
 def test_heuristic_configs():
@@ -97,6 +116,9 @@ def test_heuristic_configs():
     (dict(max_batch=0), 2), (dict(max_kv_len=0), 2), (dict(kv_dtype=7), 4),
     (dict(force_reducer="cooperative", max_kv_len=131072, max_batch=1, force_blocks_per_split=1), 7),
     (dict(force_reducer="none", max_kv_len=4096), 7),
+    (dict(schedule="balanced", max_batch=65), 7), (dict(schedule="balanced", max_kv_len=256), 7),
+    (dict(schedule="balanced", force_reducer="none", max_kv_len=200), 7),
+    (dict(schedule=3), 7), (dict(wgs_per_cu=65), 7), (dict(wgs_per_cu=-1), 7),
 ])
 def test_plan_errors(kw, status):
     with pytest.raises(skvd.SkvdError) as e:
@@ -146,7 +168,9 @@ def test_decode_check_f16(over, status):
 
 @pytest.mark.parametrize("over,status", [
     ({}, 0), (dict(k_scales=None), 4), (dict(v_scales=None), 4), (dict(k_pages=FAKE + 8), 0),
-    (dict(k_pages=FAKE + 4), 3), (dict(k_scales=FAKE + 1), 3),
+    (dict(k_pages=FAKE + 4), 3), (dict(k_scales=FAKE + 1), 3), (dict(v_scales=FAKE + 4), 3),
+    (dict(scale_tok_stride=34), 3), (dict(scale_head_stride=2), 3),
+    (dict(scale_page_stride=16 * 8 * 4 + 2), 3), (dict(scale_tok_stride=36), 0),
 ])
 def test_decode_check_int8(over, status):
     p = plan(kv_dtype="i8")

@@ -64,11 +64,54 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("schedule", ["auto", "static"])
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
-def test_small_all_rows(case):
+def test_small_all_rows(case, schedule):
     name, B, T, Hq, Hkv, D, P, kv, lens = case
-    check(spec(name=name, batch=B, q_per_seq=T, num_qo_heads=Hq, num_kv_heads=Hkv, head_dim=D,
-               page_size=P, kv_dtype=kv, lens=lens), seed=zlib.crc32(name.encode()) % 1000)
+    s = spec(name=name, batch=B, q_per_seq=T, num_qo_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+             page_size=P, kv_dtype=kv, lens=lens)
+    check(s, seed=zlib.crc32(name.encode()) % 1000, plan_kw=dict(schedule=schedule))
+
+
+_rng = np.random.default_rng(2024)
+BALANCED = [
+    # (name, B, T, Hq, Hkv, D, kv, lens, plan kw): shares that cover many short rows, empty
+    # sequences, one long row among short ones, tiny and large grids
+    ("tiny_rows", 64, 1, 8, 2, 128, "f16", tuple(int(x) for x in _rng.integers(0, 140, 64)),
+     dict(force_blocks_per_split=1, wgs_per_cu=1, num_cus=8)),
+    ("tiny_rows_i8", 64, 1, 8, 2, 128, "i8", tuple(int(x) for x in _rng.integers(0, 140, 64)),
+     dict(force_blocks_per_split=2, wgs_per_cu=1, num_cus=5)),
+    ("half_empty", 64, 1, 16, 4, 128, "f16", tuple([0, 333] * 32), dict(force_blocks_per_split=1)),
+    ("one_long", 17, 2, 8, 4, 128, "f16", (5000,) + (70,) * 16, dict(force_blocks_per_split=2)),
+    ("big_grid", 3, 1, 16, 16, 128, "f16", (64, 1000, 129), dict(force_blocks_per_split=1,
+                                                                 wgs_per_cu=64)),
+    ("mqa_d256", 9, 1, 4, 1, 256, "f16", (1, 300, 64, 65, 1200, 7, 0, 640, 2),
+     dict(force_blocks_per_split=1, wgs_per_cu=2, num_cus=3)),
+    ("t4_i8_d256", 5, 4, 8, 4, 256, "i8", (700, 4, 129, 1100, 64), dict(force_blocks_per_split=3)),
+]
+
+
+@pytest.mark.parametrize("case", BALANCED, ids=[c[0] for c in BALANCED])
+def test_balanced_schedule_edges(case):
+    name, B, T, Hq, Hkv, D, kv, lens, kw = case
+    s = spec(name=name, batch=B, q_per_seq=T, num_qo_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+             page_size=16, kv_dtype=kv, lens=("list", lens))
+    _, _, plan, _, _ = check(s, seed=zlib.crc32(name.encode()) % 1000,
+                             plan_kw=dict(schedule="balanced", **kw))
+    assert plan.schedule == "balanced"
+
+
+def test_balanced_all_empty():
+    s = spec(name="all_empty", batch=4, q_per_seq=1, num_qo_heads=8, num_kv_heads=2,
+             head_dim=128, page_size=16, lens=("list", (0, 0, 0, 0)))
+    prob = workloads.generate(s, 1)
+    prob["page_table"] = np.zeros((4, 300), np.int32)  # plan for up to 300 pages per row
+    dev = to_dev(prob)
+    plan = make_plan(prob, schedule="balanced")
+    o, lse = run(plan, prob, dev)
+    torch.cuda.synchronize()
+    assert plan.schedule == "balanced"
+    assert (o.float() == 0).all() and torch.isneginf(lse).all()
 
 
 @pytest.mark.parametrize("kv", ["f16", "i8"])
@@ -112,10 +155,12 @@ def test_split_invariance():
     s = spec(name="inv", batch=2, q_per_seq=2, num_qo_heads=8, num_kv_heads=4, head_dim=128,
              page_size=16, lens=("list", (3000, 777)), q_mult=2.0)
     outs = []
-    for bps, red in [(1, "multipass"), (2, "hierarchical"), (8, "cooperative"), (0, "auto"),
-                     (47, "direct"), (1000, "none")]:
+    for bps, red, sch in [(1, "multipass", "auto"), (2, "hierarchical", "auto"),
+                          (8, "cooperative", "auto"), (0, "auto", "auto"), (47, "direct", "auto"),
+                          (1000, "none", "auto"), (1, "multipass", "static"),
+                          (3, "auto", "static")]:
         _, _, _, o, lse = check(s, seed=3, plan_kw=dict(force_blocks_per_split=bps,
-                                                         force_reducer=red))
+                                                         force_reducer=red, schedule=sch))
         outs.append((o.float().cpu(), lse.cpu()))
     for o, l in outs[1:]:
         assert (o - outs[0][0]).abs().max().item() <= 2e-3
