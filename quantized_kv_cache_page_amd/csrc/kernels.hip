@@ -174,7 +174,7 @@ struct Shares {
 };
 
 __device__ __forceinline__ Shares balanced_shares(const LaunchArgs &a, int debug) {
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   Shares sh;
   sh.len_l = lane < a.batch ? clamp_len(a.kv_len[lane], a.max_kv_len, a.status, debug) : 0;
   sh.nb_l = (unsigned)(sh.len_l + 63) >> 6;
@@ -824,12 +824,12 @@ __device__ __forceinline__ int parts_of_row(const LaunchArgs &a, int64_t row) {
          share_of(row0, sh.n_blocks, sh.n_shares) + 1;
 }
 
-// Final write of one row from a normalized accumulator.
+// Final write of one row from an unnormalized accumulator (wave 0's lanes hold D/64 each).
 template <int D>
 __device__ __forceinline__ void write_row(const LaunchArgs &a, int64_t row, const float *acc,
                                           float M, float S) {
   constexpr int PER = D / 64;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const bool empty = !(S > 0.f) || M == kNegInf;
   _Float16 *o = (_Float16 *)a.o + row * D + PER * lane;
   const float inv = empty ? 0.f : 1.f / S;
@@ -843,10 +843,126 @@ __device__ __forceinline__ float part_weight(float m, float M) {
   return m == kNegInf ? 0.f : fast_exp2(m - M);
 }
 
-// Direct: every lane walks all n partials (few partials).
+// A running merge state (max in log2 units, sum relative to it, PER accumulator elements).
+template <int PER>
+struct MergeAcc {
+  float M = kNegInf, S = 0.f;
+  float acc[PER] = {};
+  // fold in another state of the same form: the log-sum-exp combination
+  __device__ __forceinline__ void fold(float M2, float S2, const float *acc2) {
+    const float Mn = fmaxf(M, M2);
+    if (Mn == kNegInf) return;
+    const float wa = part_weight(M, Mn), wb = part_weight(M2, Mn);
+    S = S * wa + S2 * wb;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) acc[i] = acc[i] * wa + acc2[i] * wb;
+    M = Mn;
+  }
+};
+
+template <int PER>
+struct PerVecT;
+template <>
+struct PerVecT<2> {
+  typedef float __attribute__((ext_vector_type(2))) type;
+};
+template <>
+struct PerVecT<4> {
+  typedef float4v type;
+};
+
+// Cooperative step: up to 64 partials first, first + stride, ... one per lane of this wave.
+// Each lane's (m, l) gives the wave max and sum; the lanes then walk the partials' output
+// slices (PER elements per lane), eight loads in flight, each weight broadcast from the lane
+// that owns the partial. The loads of the first eight slices and of every lane's (m, l) are
+// issued for the first min(cap, 64) slots before the count is known (count() is evaluated
+// after them, so its own loads overlap); slots at or past the count are ignored.
+template <int D, class CountFn>
+__device__ __forceinline__ void merge_lanes(const float *ml, const float *po, int64_t first,
+                                            int stride, int cap, CountFn count,
+                                            MergeAcc<D / 64> *out) {
+  constexpr int PER = D / 64;
+  using PerVec = typename PerVecT<PER>::type;
+  typedef float float2v __attribute__((ext_vector_type(2)));
+  const int lane = threadIdx.x & 63;
+  const int64_t sl = first + (int64_t)stride * lane;
+  float2v mlv = {kNegInf, 0.f};
+  if (lane < cap) mlv = *(const float2v *)(ml + 2 * sl);
+  PerVec ov[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    ov[j] = j < cap ? *(const PerVec *)(po + (first + (int64_t)stride * j) * D + PER * lane)
+                    : (PerVec)0.f;
+  const int cnt = min(count(), cap);
+  const float m = lane < cnt ? mlv[0] : kNegInf;
+  const float M = wave_max(m);
+  const float w = M == kNegInf ? 0.f : part_weight(m, M);
+  const float S = wave_sum(lane < cnt ? w * mlv[1] : 0.f);
+  float acc[PER] = {};
+  for (int k0 = 0; k0 < cnt; k0 += 8) {
+    if (k0 > 0) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        ov[j] = k0 + j < cnt ? *(const PerVec *)(po + (first + (int64_t)stride * (k0 + j)) * D +
+                                                PER * lane)
+                             : (PerVec)0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float wj = k0 + j < cnt ? readlane_f(w, k0 + j) : 0.f;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) acc[i] = fmaf(wj, ov[j][i], acc[i]);
+    }
+  }
+  out->fold(M, S, acc);
+}
+
+// Multipass: the NW waves of the workgroup take partials w, w + NW, ... in rounds of 64 per
+// wave; the per-wave states are combined through LDS. Wave 0 returns the row's state. cap
+// bounds the partial count (the row's slots) and count() gives it.
+template <int D, int NW, class CountFn>
+__device__ __forceinline__ MergeAcc<D / 64> merge_waves(const float *ml, const float *po, int cap,
+                                                        CountFn count) {
+  constexpr int PER = D / 64;
+  __shared__ float st_lds[NW][2 + D];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  MergeAcc<PER> r;
+  const int capw = cap > wave ? (cap - wave + NW - 1) / NW : 0;  // this wave's slots
+  int n = 0;
+  merge_lanes<D>(ml, po, wave, NW, min(64, capw), [&]() { n = count(); return
+                 n > wave ? (n - wave + NW - 1) / NW : 0; }, &r);
+  const int nw = n > wave ? (n - wave + NW - 1) / NW : 0;
+  for (int c0 = 64; c0 < nw; c0 += 64)
+    merge_lanes<D>(ml, po, wave + (int64_t)NW * c0, NW, min(64, nw - c0),
+                   [&]() { return 64; }, &r);
+  if constexpr (NW > 1) {
+    if (lane == 0) {
+      st_lds[wave][0] = r.M;
+      st_lds[wave][1] = r.S;
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) st_lds[wave][2 + PER * lane + i] = r.acc[i];
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int v = 1; v < NW; ++v) {
+        float a2[PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) a2[i] = st_lds[v][2 + PER * lane + i];
+        r.fold(st_lds[v][0], st_lds[v][1], a2);
+      }
+    }
+  }
+  return r;
+}
+
+constexpr int kMergeWaves = 4;
+
+// Direct: one wave; every lane walks all n partials in order (few partials).
 template <int D>
 __global__ __launch_bounds__(64) void merge_direct(LaunchArgs a) {
   constexpr int PER = D / 64;
+  using PerVec = typename PerVecT<PER>::type;
   const int64_t row = blockIdx.x;
   const int n = parts_of_row(a, row);
   const float *ml = a.ws_ml + row * a.part_stride * 2;
@@ -854,103 +970,68 @@ __global__ __launch_bounds__(64) void merge_direct(LaunchArgs a) {
   float M = kNegInf;
   for (int s = 0; s < n; ++s) M = fmaxf(M, ml[2 * s]);
   float S = 0.f, acc[PER] = {};
-  for (int s = 0; s < n; ++s) {
-    const float w = part_weight(ml[2 * s], M);
-    S += w * ml[2 * s + 1];
+  for (int s0 = 0; s0 < n; s0 += 4) {
+    PerVec ov[4];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) acc[i] = fmaf(w, po[(int64_t)s * D + i], acc[i]);
+    for (int j = 0; j < 4; ++j)
+      ov[j] = s0 + j < n ? *(const PerVec *)(po + (int64_t)(s0 + j) * D) : (PerVec)0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (s0 + j >= n) continue;
+      const float w = part_weight(ml[2 * (s0 + j)], M);
+      S += w * ml[2 * (s0 + j) + 1];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) acc[i] = fmaf(w, ov[j][i], acc[i]);
+    }
   }
   write_row<D>(a, row, acc, M, S);
 }
 
-// Lane-strided merge of n partials at (ml, po) with stride D between partials. Produces the
-// row max M, the sum S relative to M, and the unnormalized accumulator. Cooperative when
-// n <= 64 (one lane per partial, one pass); multipass otherwise.
-template <int D>
-__device__ __forceinline__ void merge_span(const float *ml, const float *po, int n, float *M_out,
-                                           float *S_out, float *acc) {
-  constexpr int PER = D / 64;
-  __shared__ float w_lds[64];
-  const int lane = threadIdx.x;
-  // pass 1: running (max, sum) per lane over partials lane, lane+64, ...
-  float mloc = kNegInf, sloc = 0.f;
-  for (int s = lane; s < n; s += 64) {
-    const float ms = ml[2 * s], ls = ml[2 * s + 1];
-    const float mn = fmaxf(mloc, ms);
-    if (mn != kNegInf) {
-      sloc = sloc * part_weight(mloc, mn) + ls * part_weight(ms, mn);
-      mloc = mn;
-    }
-  }
-  const float M = wave_max(mloc);
-  const float S = wave_sum(M == kNegInf ? 0.f : sloc * part_weight(mloc, M));
-#pragma unroll
-  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-  // pass 2: weights of 64 partials at a time through LDS, lanes over head_dim
-  for (int base = 0; base < n; base += 64) {
-    const int s = base + lane;
-    w_lds[lane] = (s < n && M != kNegInf) ? part_weight(ml[2 * s], M) : 0.f;
-    __syncthreads();
-    const int cnt = min(64, n - base);
-    for (int i2 = 0; i2 < cnt; ++i2) {
-      const float w = w_lds[i2];
-      const float *src = po + (int64_t)(base + i2) * D + PER * lane;
-#pragma unroll
-      for (int i = 0; i < PER; ++i) acc[i] = fmaf(w, src[i], acc[i]);
-    }
-    __syncthreads();
-  }
-  *M_out = M;
-  *S_out = S;
-}
-
-// Cooperative / multipass: one wave per row over all of the row's partials.
-template <int D>
-__global__ __launch_bounds__(64) void merge_rows(LaunchArgs a) {
-  constexpr int PER = D / 64;
+// Cooperative (one lane per partial, <= 64) and multipass (NW waves, lane-strided rounds):
+// one workgroup per row.
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void merge_rows(LaunchArgs a) {
   const int64_t row = blockIdx.x;
-  const int n = parts_of_row(a, row);
-  float M, S, acc[PER];
-  merge_span<D>(a.ws_ml + row * a.part_stride * 2, a.ws_o + row * a.part_stride * D, n, &M, &S,
-                acc);
-  write_row<D>(a, row, acc, M, S);
+  const MergeAcc<D / 64> r =
+      merge_waves<D, NW>(a.ws_ml + row * a.part_stride * 2, a.ws_o + row * a.part_stride * D,
+                         a.part_stride, [&]() { return parts_of_row(a, row); });
+  if (threadIdx.x < 64) write_row<D>(a, row, r.acc, r.M, r.S);
 }
 
-// Hierarchical level 1: workgroup (row, g) merges partials 64g .. 64g+63 into one
-// unnormalized partial of the same form.
+// Hierarchical level 1: workgroup (row, g) merges partials 64g .. 64g+63 (cooperatively) into
+// one unnormalized partial of the same form.
 template <int D>
 __global__ __launch_bounds__(64) void merge_hier1(LaunchArgs a) {
   constexpr int PER = D / 64;
   const int64_t row = blockIdx.x;
   const int g = blockIdx.y;
-  const int n = parts_of_row(a, row);
   const int s0 = g * kHierGroup;
+  int n = 0;
+  MergeAcc<PER> r;
+  merge_lanes<D>(a.ws_ml + row * a.part_stride * 2, a.ws_o + row * a.part_stride * D, s0, 1,
+                 min(kHierGroup, a.part_stride - s0), [&]() {
+                   n = parts_of_row(a, row);
+                   return max(0, min(kHierGroup, n - s0));
+                 }, &r);
   if (s0 >= n) return;
-  const int cnt = min(kHierGroup, n - s0);
-  float M, S, acc[PER];
-  merge_span<D>(a.ws_ml + (row * a.part_stride + s0) * 2, a.ws_o + (row * a.part_stride + s0) * D,
-                cnt, &M, &S, acc);
   float *dst = a.ws_ho + (row * a.hier_groups_cap + g) * D + PER * threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) dst[i] = acc[i];
+  for (int i = 0; i < PER; ++i) dst[i] = r.acc[i];
   if (threadIdx.x == 0) {
     float *hm = a.ws_hml + (row * a.hier_groups_cap + g) * 2;
-    hm[0] = M;
-    hm[1] = S;
+    hm[0] = r.M;
+    hm[1] = r.S;
   }
 }
 
 // Hierarchical level 2: multipass over the row's groups.
 template <int D>
-__global__ __launch_bounds__(64) void merge_hier2(LaunchArgs a) {
-  constexpr int PER = D / 64;
+__global__ __launch_bounds__(64 * kMergeWaves) void merge_hier2(LaunchArgs a) {
   const int64_t row = blockIdx.x;
-  const int n = parts_of_row(a, row);
-  const int ng = (n + kHierGroup - 1) / kHierGroup;
-  float M, S, acc[PER];
-  merge_span<D>(a.ws_hml + row * a.hier_groups_cap * 2, a.ws_ho + row * a.hier_groups_cap * D,
-                ng, &M, &S, acc);
-  write_row<D>(a, row, acc, M, S);
+  const MergeAcc<D / 64> r = merge_waves<D, kMergeWaves>(
+      a.ws_hml + row * a.hier_groups_cap * 2, a.ws_ho + row * a.hier_groups_cap * D,
+      a.hier_groups_cap, [&]() { return (parts_of_row(a, row) + kHierGroup - 1) / kHierGroup; });
+  if (threadIdx.x < 64) write_row<D>(a, row, r.acc, r.M, r.S);
 }
 
 // ----------------------------------------------------------------------------- gather (test aid)
@@ -1062,11 +1143,13 @@ static void launch_merge_t(const Plan &p, const LaunchArgs &la, hipStream_t st) 
   const unsigned rows = (unsigned)((int64_t)la.batch * la.T * la.Hq);
   switch (p.reducer) {
     case SKVD_REDUCER_DIRECT: merge_direct<D><<<rows, 64, 0, st>>>(la); break;
-    case SKVD_REDUCER_COOPERATIVE:
-    case SKVD_REDUCER_MULTIPASS: merge_rows<D><<<rows, 64, 0, st>>>(la); break;
+    case SKVD_REDUCER_COOPERATIVE: merge_rows<D, 1><<<rows, 64, 0, st>>>(la); break;
+    case SKVD_REDUCER_MULTIPASS:
+      merge_rows<D, kMergeWaves><<<rows, 64 * kMergeWaves, 0, st>>>(la);
+      break;
     case SKVD_REDUCER_HIERARCHICAL:
       merge_hier1<D><<<dim3(rows, p.hier_groups_cap), 64, 0, st>>>(la);
-      merge_hier2<D><<<rows, 64, 0, st>>>(la);
+      merge_hier2<D><<<rows, 64 * kMergeWaves, 0, st>>>(la);
       break;
     default: break;
   }

@@ -154,7 +154,8 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
     if (p.part_stride == 1) red = SKVD_REDUCER_NONE;
     else if (p.part_stride <= 4) red = SKVD_REDUCER_DIRECT;
     else if (p.part_stride <= 64) red = SKVD_REDUCER_COOPERATIVE;
-    else if (p.rows_cap >= 2LL * num_cus) red = SKVD_REDUCER_MULTIPASS;
+    // hierarchical only pays for its second launch when few rows hold very many partials
+    else if (p.part_stride <= 1024 || p.rows_cap >= 2LL * num_cus) red = SKVD_REDUCER_MULTIPASS;
     else red = SKVD_REDUCER_HIERARCHICAL;
   }
   if (red == SKVD_REDUCER_NONE && p.part_stride != 1)
