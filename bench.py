@@ -176,6 +176,8 @@ def main():
     ap.add_argument("--bps", type=int, default=0, help="force 64-token blocks per split")
     ap.add_argument("--reducer", default="auto")
     ap.add_argument("--schedule", choices=["auto", "static", "balanced"], default="auto")
+    ap.add_argument("--heads-per-wg", type=int, default=0,
+                    help="KV heads per partial-kernel workgroup (0: plan default)")
     ap.add_argument("--wgs-per-cu", type=int, default=0,
                     help="balanced schedule: partial-kernel workgroups per CU (0: plan default)")
     ap.add_argument("--copies", type=int, default=0, help="pool copies to rotate (0: auto)")
@@ -241,7 +243,8 @@ def main():
     plan = skvd.Plan(spec.num_qo_heads, spec.num_kv_heads, spec.head_dim, spec.page_size,
                      spec.kv_dtype, spec.batch, spec.q_per_seq, spec.max_kv_len, device=0,
                      force_blocks_per_split=args.bps, force_reducer=args.reducer,
-                     schedule=args.schedule, wgs_per_cu=args.wgs_per_cu)
+                     schedule=args.schedule, wgs_per_cu=args.wgs_per_cu,
+                     heads_per_wg=args.heads_per_wg)
     plan.ensure_workspace()
     log(f"[bench] {plan.describe()}")
     out = torch.empty(q.shape, dtype=torch.float16, device=dev)

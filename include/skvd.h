@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define SKVD_ABI_VERSION 2
+#define SKVD_ABI_VERSION 3
 
 typedef enum {
   SKVD_OK = 0,
@@ -123,7 +123,13 @@ typedef struct {
   int32_t debug;          /* != 0: kernels record contract violations in the status word */
   int32_t schedule;       /* skvd_schedule; 0 = auto */
   int32_t wgs_per_cu;     /* balanced schedule: workgroups launched per compute unit (0: 4;
-                             3 at head_dim 256; 8 for int8 at head_dim 128 with G*T <= 4) */
+                             3 at head_dim 256; 8 / heads_per_wg for int8 at head_dim 128 with
+                             G*T <= 4) */
+  int32_t heads_per_wg;   /* KV heads one partial-kernel workgroup serves, one wave each
+                             (0: 4, else 2, else 1 -- whichever divides Hkv -- for int8 at
+                             head_dim 128 with G*T <= 4, where the waves of a CU then share
+                             each token's scale cache line; 1 otherwise). Values > 1 only for
+                             that variant and must divide Hkv (else SKVD_ERR_PLAN). */
 } skvd_plan_params;
 
 /* What a plan resolved to (for logs and tests). */
@@ -141,7 +147,7 @@ typedef struct {
   int32_t part_stride;      /* partial slots per row in the workspace (splits_cap, + 1 when
                                balanced: a row may straddle one more share boundary) */
   int32_t grid_wgs;         /* partial-kernel workgroups launched (upper bound) */
-  int32_t reserved;
+  int32_t heads_per_wg;     /* KV heads (waves) per partial-kernel workgroup */
 } skvd_plan_info;
 
 /* Status-word bits (debug plans). */

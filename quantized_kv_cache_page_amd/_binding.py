@@ -21,7 +21,7 @@ REDUCERS = {"auto": 0, "direct": 1, "cooperative": 2, "multipass": 3, "hierarchi
 REDUCER_NAMES = {v: k for k, v in REDUCERS.items()}
 SCHEDULES = {"auto": 0, "static": 1, "balanced": 2}
 SCHEDULE_NAMES = {v: k for k, v in SCHEDULES.items()}
-ABI_VERSION = 2
+ABI_VERSION = 3
 STATUS_KV_LEN_CLAMPED = 0x1
 STATUS_PAGE_CLAMPED = 0x2
 
@@ -36,7 +36,7 @@ class skvd_plan_params(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_qo_heads", "num_kv_heads", "head_dim", "page_size", "max_batch", "max_q_per_seq",
         "max_kv_len", "kv_dtype", "device", "num_cus", "force_blocks_per_split",
-        "force_reducer", "debug", "schedule", "wgs_per_cu")]
+        "force_reducer", "debug", "schedule", "wgs_per_cu", "heads_per_wg")]
 
 
 class skvd_plan_info(ctypes.Structure):
@@ -46,7 +46,7 @@ class skvd_plan_info(ctypes.Structure):
                 ("rows_cap", ctypes.c_int64), ("workspace_bytes", ctypes.c_uint64),
                 ("status_offset", ctypes.c_uint64), ("schedule", ctypes.c_int32),
                 ("part_stride", ctypes.c_int32), ("grid_wgs", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("heads_per_wg", ctypes.c_int32)]
 
 
 class skvd_decode_args(ctypes.Structure):
@@ -214,7 +214,7 @@ class Plan:
     def __init__(self, num_qo_heads, num_kv_heads, head_dim, page_size, kv_dtype="f16",
                  max_batch=1, max_q_per_seq=1, max_kv_len=1, device=0, num_cus=0,
                  force_blocks_per_split=0, force_reducer="auto", debug=False,
-                 schedule="auto", wgs_per_cu=0):
+                 schedule="auto", wgs_per_cu=0, heads_per_wg=0):
         dev = torch.device("cuda", device) if isinstance(device, int) else torch.device(device)
         self.device = dev
         idx = dev.index if dev.index is not None else torch.cuda.current_device()
@@ -225,7 +225,7 @@ class Plan:
             int(max_q_per_seq), int(max_kv_len),
             SKVD_KV_F16 if kv_dtype in ("f16", torch.float16) else SKVD_KV_I8_F16SCALE32,
             int(idx), int(num_cus), int(force_blocks_per_split), red, int(bool(debug)), sch,
-            int(wgs_per_cu))
+            int(wgs_per_cu), int(heads_per_wg))
         self.kv_dtype = "f16" if self.params.kv_dtype == SKVD_KV_F16 else "i8"
         self.handle = skvd_plan_create(self.params)
         self.info = skvd_plan_get_info(self.handle)

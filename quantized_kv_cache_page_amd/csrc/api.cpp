@@ -128,7 +128,7 @@ skvd_status skvd_plan_get_info(const skvd_plan *plan, skvd_plan_info *info) {
   info->schedule = p.schedule;
   info->part_stride = p.part_stride;
   info->grid_wgs = p.grid_wgs;
-  info->reserved = 0;
+  info->heads_per_wg = p.heads_per_wg;
   return SKVD_OK;
 }
 
@@ -138,12 +138,13 @@ skvd_status skvd_plan_describe(const skvd_plan *plan, char *buf, size_t n) {
   const skvd::Plan &p = plan->p;
   snprintf(buf, n,
            "plan Hq=%d Hkv=%d D=%d P=%d kv=%s max_batch=%d max_T=%d max_kv_len=%d cus=%d: "
-           "blocks_per_split=%d splits=%d schedule=%s grid=%d reducer=%s hier_groups=%d "
-           "rows_per_wg=%d workspace=%zu B",
+           "blocks_per_split=%d splits=%d schedule=%s grid=%d heads_per_wg=%d reducer=%s "
+           "hier_groups=%d rows_per_wg=%d workspace=%zu B",
            p.prm.num_qo_heads, p.prm.num_kv_heads, p.prm.head_dim, p.prm.page_size,
            p.prm.kv_dtype == SKVD_KV_F16 ? "f16" : "int8", p.prm.max_batch, p.prm.max_q_per_seq,
            p.prm.max_kv_len, p.num_cus, p.bps, p.splits_cap,
            p.schedule == SKVD_SCHEDULE_BALANCED ? "balanced" : "static", p.grid_wgs,
+           p.heads_per_wg,
            skvd::reducer_name(p.reducer),
            p.hier_groups_cap, p.rows_per_wg, p.ws_bytes);
   return SKVD_OK;

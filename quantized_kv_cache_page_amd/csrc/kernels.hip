@@ -169,7 +169,7 @@ __device__ __forceinline__ void h16_pairs(const half8 &a, const half8 &b, half2v
 struct Shares {
   int len_l;
   unsigned nb_l, pre_l;
-  int64_t n_blocks;  // N = Hkv * sum of block counts
+  int64_t n_blocks;  // N = (Hkv / heads per workgroup) * sum of block counts
   int n_shares;      // W = min(grid, N / bps), at least 1 when N > 0
 };
 
@@ -186,7 +186,8 @@ __device__ __forceinline__ Shares balanced_shares(const LaunchArgs &a, int debug
   }
   sh.pre_l = inc - sh.nb_l;
   // (readlane: the total is wave-uniform, so it and everything derived from it stay scalar)
-  sh.n_blocks = (int64_t)(unsigned)__builtin_amdgcn_readlane((int)inc, 63) * a.Hkv;
+  sh.n_blocks = (int64_t)(unsigned)__builtin_amdgcn_readlane((int)inc, 63) *
+                (a.Hkv / a.heads_per_wg);
   sh.n_shares = sh.n_blocks == 0
                     ? 0
                     : (int)max((int64_t)1, min((int64_t)a.grid_wgs, sh.n_blocks / a.bps));
@@ -228,9 +229,9 @@ constexpr int partial_waves() {
   return D == 128 ? (RB == 1 ? (I8 ? 3 : 1) : 2) : 1;
 }
 
-template <int D, int RB, bool I8, bool FAST, int CH, bool PVM>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>())))
-void partial_kernel(LaunchArgs a) {
+template <int D, int RB, bool I8, bool FAST, int CH, bool PVM, int HW>
+__global__ __launch_bounds__(64 * HW)
+__attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_kernel(LaunchArgs a) {
   static_assert(CH == 16 || CH == 32 || (CH == 64 && !PVM), "chunk");
   static_assert(PVM || CH % 32 == 0, "the vector P.V pairs 16-token tiles 2h and 2h + 1");
   constexpr int NT = CH / 16;    // 16-token score tiles per chunk
@@ -246,20 +247,30 @@ void partial_kernel(LaunchArgs a) {
   using Vec = std::conditional_t<I8, uint2v, half8>;  // one lane's 8 elements of a row
   using PvOp = std::conditional_t<CH == 32, half8, half4>;
 
-  __shared__ __attribute__((aligned(16))) char v_lds[PVM ? CH * ROWB : 16];  // chunk V, f16
-  __shared__ __attribute__((aligned(16))) float p_lds[PVM ? RM * PSTR : 4];  // [row][token]
-  // int8 V scales of the chunk, [token][group] f16, staged through LDS from one load per lane
-  __shared__ __attribute__((aligned(16))) uint2v vsc_lds[I8 ? CH * (D / 128) : 1];
+  // LDS, one slice per wave (each wave serves its own KV head):
+  constexpr int VL = PVM ? CH * ROWB : 16;          // chunk V rows, f16
+  constexpr int PL = PVM ? RM * PSTR : 4;           // probabilities [row][token]
+  constexpr int SL = I8 ? CH * (D / 128) : 1;       // int8 V scales [token][group], f16
+  constexpr int QL = PVM ? 4 : (CH / 2) * RM;       // vector P.V: f16 pairs (tp, tp+16) [tp][row]
+  __shared__ __attribute__((aligned(16))) char v_lds_all[HW * VL];
+  __shared__ __attribute__((aligned(16))) float p_lds_all[HW * PL];
+  __shared__ __attribute__((aligned(16))) uint2v vsc_lds_all[HW * SL];
+  __shared__ __attribute__((aligned(16))) unsigned p2_lds_all[HW * QL];
+  const int wave = HW > 1 ? (int)(threadIdx.x >> 6) : 0;
+  char *const v_lds = v_lds_all + wave * VL;
+  float *const p_lds = p_lds_all + wave * PL;
+  uint2v *const vsc_lds = vsc_lds_all + wave * SL;
   const _Float16 *vsh = (const _Float16 *)vsc_lds;
-  // vector P.V: probabilities as f16 pairs (token tp, token tp + 16) per row: [tp][row]
-  __shared__ __attribute__((aligned(16))) unsigned p2_lds[PVM ? 4 : (CH / 2) * RM];
+  unsigned *const p2_lds = p2_lds_all + wave * QL;
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int Hkv = a.Hkv;
+  const int Hg = Hkv / HW;  // head groups: the rows of the schedule
   const int T = a.T, G = a.G, R = G * T;
   const int P1 = (1 << a.page_shift) - 1;
 
-  // ---- this workgroup's segments: (sequence, KV head, block range, partial slot)
+  // ---- this workgroup's segments: (sequence, KV head group, block range, partial slot); wave
+  // w of the workgroup serves KV head HW * group + w over the same block range
   // Static: workgroup order split fastest, then KV head, then sequence, with an odd split
   // stride. Consecutive workgroups go to the eight XCDs in turn; with an even stride split s
   // of every (head, sequence) would land on the same XCD, and the live splits of a ragged
@@ -269,7 +280,7 @@ void partial_kernel(LaunchArgs a) {
   // contiguous shares; workgroup w takes share w, which may cover the end of one row and the
   // start of the next ones: one segment per row, its partial in slot w - (first share of the
   // row). Sequence lengths, one per lane, come from kv_len on the device.
-  int st_b = 0, st_kvh = 0, st_split = 0;
+  int st_b = 0, st_grp = 0, st_split = 0;
   Shares sh{};
   int64_t x_cur = 0, x_end = 0;  // balanced: this workgroup's share
   const int share = blockIdx.x;
@@ -282,27 +293,27 @@ void partial_kernel(LaunchArgs a) {
     const int wg = blockIdx.x;
     st_split = wg % a.split_stride;
     const int head_seq = wg / a.split_stride;
-    st_kvh = head_seq % Hkv;
-    st_b = head_seq / Hkv;
+    st_grp = head_seq % Hg;
+    st_b = head_seq / Hg;
     if (st_split >= a.splits_cap) return;
   }
   bool pending = true;
   for (;;) {
-  int b, kvh, slot, L, blk_lo, blk_hi;
+  int b, grp, slot, L, blk_lo, blk_hi;
   if (a.balanced) {
     if (x_cur >= x_end) break;
-    // the sequence holding global block x_cur: Hkv*pre <= x_cur < Hkv*(pre + nb), that is
-    // pre <= x_cur / Hkv < pre + nb (one scalar division, 32-bit lane compares)
-    const unsigned xq = (unsigned)(x_cur / Hkv);
+    // the sequence holding global block x_cur: Hg*pre <= x_cur < Hg*(pre + nb), that is
+    // pre <= x_cur / Hg < pre + nb (one scalar division, 32-bit lane compares)
+    const unsigned xq = (unsigned)(x_cur / Hg);
     const bool mine = sh.pre_l <= xq && xq < sh.pre_l + sh.nb_l;
     b = __builtin_ctzll(__ballot(mine));
     const unsigned pre_b = (unsigned)__builtin_amdgcn_readlane((int)sh.pre_l, b);
     const int nb_b = __builtin_amdgcn_readlane((int)sh.nb_l, b);
     L = __builtin_amdgcn_readlane(sh.len_l, b);
-    const int64_t off = x_cur - (int64_t)Hkv * pre_b;
-    kvh = (int)(off / nb_b);
-    blk_lo = (int)(off - (int64_t)kvh * nb_b);
-    const int64_t row0 = (int64_t)Hkv * pre_b + (int64_t)kvh * nb_b;  // the row's first block
+    const int64_t off = x_cur - (int64_t)Hg * pre_b;
+    grp = (int)(off / nb_b);
+    blk_lo = (int)(off - (int64_t)grp * nb_b);
+    const int64_t row0 = (int64_t)Hg * pre_b + (int64_t)grp * nb_b;  // the row's first block
     const int64_t seg_end = min(x_end, row0 + nb_b);
     blk_hi = blk_lo + (int)(seg_end - x_cur);
     slot = share - share_of(row0, sh.n_blocks, sh.n_shares);
@@ -311,7 +322,7 @@ void partial_kernel(LaunchArgs a) {
     if (!pending) break;
     pending = false;
     b = st_b;
-    kvh = st_kvh;
+    grp = st_grp;
     slot = st_split;
     L = clamp_len(a.kv_len[b], a.max_kv_len, a.status, a.debug);
     const int nblk = (L + 63) >> 6;
@@ -319,6 +330,7 @@ void partial_kernel(LaunchArgs a) {
     if (!a.single && blk_lo >= nblk) break;  // beyond this sequence: no partial is read
     blk_hi = min(blk_lo + a.bps, nblk);
   }
+  const int kvh = HW * grp + wave;
   const int tok0 = blk_lo * 64;
   const int tok_end = min(blk_hi * 64, L);
 
@@ -814,12 +826,12 @@ __device__ __forceinline__ int parts_of_row(const LaunchArgs &a, int64_t row) {
     const int nblk = (L + 63) >> 6;
     return (nblk + a.bps - 1) / a.bps;
   }
-  const int kvh = (int)(row % a.Hq) / a.G;
+  const int grp = (int)(row % a.Hq) / a.G / a.heads_per_wg;  // the KV head's group
   const Shares sh = balanced_shares(a, 0);
   const int64_t pre_b = (unsigned)__builtin_amdgcn_readlane((int)sh.pre_l, b);
   const int64_t nb_b = __builtin_amdgcn_readlane((int)sh.nb_l, b);
   if (nb_b == 0) return 0;
-  const int64_t row0 = a.Hkv * pre_b + kvh * nb_b;
+  const int64_t row0 = (a.Hkv / a.heads_per_wg) * pre_b + grp * nb_b;
   return share_of(row0 + nb_b - 1, sh.n_blocks, sh.n_shares) -
          share_of(row0, sh.n_blocks, sh.n_shares) + 1;
 }
@@ -1101,14 +1113,25 @@ constexpr int chunk_tokens() {
   return D == 128 ? 32 : 16;
 }
 
-template <int D, int RB, bool I8>
-static void launch_partial_t(const LaunchArgs &la, dim3 grid, hipStream_t st, bool fast) {
+template <int D, int RB, bool I8, int HW>
+static void launch_partial_hw(const LaunchArgs &la, dim3 grid, hipStream_t st, bool fast) {
   constexpr int CH = chunk_tokens<D, RB, I8>();
   constexpr bool PVM = pv_on_mfma<D, RB>();
   if (fast)
-    partial_kernel<D, RB, I8, true, CH, PVM><<<grid, 64, 0, st>>>(la);
+    partial_kernel<D, RB, I8, true, CH, PVM, HW><<<grid, 64 * HW, 0, st>>>(la);
   else
-    partial_kernel<D, RB, I8, false, CH, PVM><<<grid, 64, 0, st>>>(la);
+    partial_kernel<D, RB, I8, false, CH, PVM, HW><<<grid, 64 * HW, 0, st>>>(la);
+}
+
+// KV heads per workgroup (one wave each): int8 D=128 single-quarter variants share each
+// token's scale line among the waves of a CU (heads_per_wg 4 or 2); every other variant 1.
+template <int D, int RB, bool I8>
+static void launch_partial_t(const LaunchArgs &la, dim3 grid, hipStream_t st, bool fast) {
+  if constexpr (I8 && D == 128 && RB == 1) {
+    if (la.heads_per_wg == 4) return launch_partial_hw<D, RB, I8, 4>(la, grid, st, fast);
+    if (la.heads_per_wg == 2) return launch_partial_hw<D, RB, I8, 2>(la, grid, st, fast);
+  }
+  launch_partial_hw<D, RB, I8, 1>(la, grid, st, fast);
 }
 
 template <int D, bool I8>
@@ -1126,7 +1149,8 @@ int launch_partial(const Plan &p, const LaunchArgs &la, void *stream) {
   // one-dimensional grid: balanced, the plan's share count bound; static, split fastest over
   // (split, KV head, sequence) (the plan keeps the count below 2^31)
   dim3 grid(la.balanced ? (unsigned)la.grid_wgs
-                        : (unsigned)((int64_t)la.split_stride * la.Hkv * la.batch));
+                        : (unsigned)((int64_t)la.split_stride * (la.Hkv / la.heads_per_wg) *
+                                     la.batch));
   const bool i8 = la.int8;
   if (la.D == 128) {
     if (i8) launch_partial_rb<128, true>(p, la, grid, st);

@@ -78,6 +78,14 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
     return fail(err, errn, SKVD_ERR_PLAN, "schedule=%d unknown", prm.schedule);
   if (prm.wgs_per_cu < 0 || prm.wgs_per_cu > 64)
     return fail(err, errn, SKVD_ERR_PLAN, "wgs_per_cu=%d outside 0..64", prm.wgs_per_cu);
+  // KV heads per workgroup: the int8 single-quarter variant at D=128 comes in 1, 2 and 4.
+  const bool multi_head_ok = prm.kv_dtype == SKVD_KV_I8_F16SCALE32 && D == 128 &&
+                             G * prm.max_q_per_seq <= 4;
+  int hw = prm.heads_per_wg;
+  if (hw == 0) hw = !multi_head_ok ? 1 : (Hkv % 4 == 0 ? 4 : (Hkv % 2 == 0 ? 2 : 1));
+  if (hw != 1 && (!multi_head_ok || (hw != 2 && hw != 4) || Hkv % hw != 0))
+    return fail(err, errn, SKVD_ERR_PLAN, "heads_per_wg=%d: only 1, or 2 / 4 dividing Hkv=%d "
+                "for int8 at head_dim 128 with G*T <= 4", prm.heads_per_wg, Hkv);
 
   Plan p{};
   p.prm = prm;
@@ -87,6 +95,7 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
   p.num_cus = num_cus;
   p.max_blocks = (prm.max_kv_len + kBlockTokens - 1) / kBlockTokens;
   p.rows_cap = (int64_t)prm.max_batch * prm.max_q_per_seq * Hq;
+  p.heads_per_wg = hw;
 
   // Blocks per split. Two pressures: enough workgroups to fill the chip (about 16 per CU
   // when every sequence is at max_kv_len), and partial traffic (one (m, l, D floats) per row
@@ -105,7 +114,7 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
   if (bps < 1) bps = 1;
   // The partial kernel's one-dimensional grid holds split_stride x KV heads x sequences
   // < 2^31 workgroups, split_stride being splits_cap rounded up to odd.
-  const int64_t per_split = (int64_t)Hkv * prm.max_batch;
+  const int64_t per_split = (int64_t)(Hkv / hw) * prm.max_batch;
   const int64_t max_splits = INT32_MAX / per_split - 1;
   if (max_splits < 1)
     return fail(err, errn, SKVD_ERR_SHAPE, "num_kv_heads x max_batch = %lld exceeds the grid",
@@ -141,7 +150,7 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
     // memory pipes of an f16 stream; int8 at D=128 also needs vector-ALU throughput, so more
     // waves; D=256 workgroups are the largest (one wave per SIMD fits).
     const bool i8 = prm.kv_dtype == SKVD_KV_I8_F16SCALE32;
-    const int auto_wpc = D == 256 ? 3 : (i8 && p.row_blocks == 1 ? 8 : kDefaultWgsPerCu);
+    const int auto_wpc = D == 256 ? 3 : (i8 && p.row_blocks == 1 ? 8 / hw : kDefaultWgsPerCu);
     p.grid_wgs = (prm.wgs_per_cu ? prm.wgs_per_cu : auto_wpc) * num_cus;
   } else {
     p.part_stride = p.splits_cap;
@@ -283,6 +292,7 @@ void fill_launch_args(const Plan &p, const skvd_decode_args &a, void *ws, Launch
   l.split_stride = p.splits_cap | 1;
   l.balanced = p.schedule == SKVD_SCHEDULE_BALANCED;
   l.grid_wgs = p.grid_wgs;
+  l.heads_per_wg = p.heads_per_wg;
   l.part_stride = p.part_stride;
   l.max_kv_len = p.prm.max_kv_len;
   l.hier_groups_cap = p.hier_groups_cap;

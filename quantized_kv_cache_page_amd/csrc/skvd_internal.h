@@ -26,7 +26,8 @@ struct Plan {
   int splits_cap;     // ceil(max_blocks / bps): static splits per row at max_kv_len
   int schedule;       // resolved skvd_schedule
   int part_stride;    // partial slots per row: splits_cap (+ 1 when balanced)
-  int grid_wgs;       // partial-kernel grid (static: split_stride * Hkv * max_batch)
+  int grid_wgs;       // partial-kernel grid (static: split_stride * Hkv / hw * max_batch)
+  int heads_per_wg;   // hw: KV heads served by one workgroup, one wave each
   int reducer;        // resolved skvd_reducer
   int hier_groups_cap;
   int64_t rows_cap;
@@ -49,6 +50,7 @@ struct LaunchArgs {
   float scale_log2;  // sm_scale * log2(e): scores are kept in base 2
   int bps, splits_cap, split_stride, max_kv_len, hier_groups_cap;  // stride: odd, >= cap
   int balanced, grid_wgs, part_stride;
+  int heads_per_wg;  // KV heads (waves) per partial-kernel workgroup; divides Hkv
   int int8, debug;
   float *ws_ml;      // [rows_cap][part_stride][2]  (max in log2 units, sum)
   float *ws_o;       // [rows_cap][part_stride][D]  unnormalized f32 output
