@@ -1123,11 +1123,12 @@ static void launch_partial_hw(const LaunchArgs &la, dim3 grid, hipStream_t st, b
     partial_kernel<D, RB, I8, false, CH, PVM, HW><<<grid, 64 * HW, 0, st>>>(la);
 }
 
-// KV heads per workgroup (one wave each): int8 D=128 single-quarter variants share each
-// token's scale line among the waves of a CU (heads_per_wg 4 or 2); every other variant 1.
+// KV heads per workgroup (one wave each): the D=128 single-quarter variants read each token's
+// rows of 4 (or 2) KV heads from one CU together (int8: and share the token's scale line);
+// every other variant serves one head.
 template <int D, int RB, bool I8>
 static void launch_partial_t(const LaunchArgs &la, dim3 grid, hipStream_t st, bool fast) {
-  if constexpr (I8 && D == 128 && RB == 1) {
+  if constexpr (D == 128 && RB == 1) {
     if (la.heads_per_wg == 4) return launch_partial_hw<D, RB, I8, 4>(la, grid, st, fast);
     if (la.heads_per_wg == 2) return launch_partial_hw<D, RB, I8, 2>(la, grid, st, fast);
   }

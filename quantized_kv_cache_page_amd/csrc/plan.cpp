@@ -78,14 +78,13 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
     return fail(err, errn, SKVD_ERR_PLAN, "schedule=%d unknown", prm.schedule);
   if (prm.wgs_per_cu < 0 || prm.wgs_per_cu > 64)
     return fail(err, errn, SKVD_ERR_PLAN, "wgs_per_cu=%d outside 0..64", prm.wgs_per_cu);
-  // KV heads per workgroup: the int8 single-quarter variant at D=128 comes in 1, 2 and 4.
-  const bool multi_head_ok = prm.kv_dtype == SKVD_KV_I8_F16SCALE32 && D == 128 &&
-                             G * prm.max_q_per_seq <= 4;
+  // KV heads per workgroup: the single-quarter variants at D=128 come in 1, 2 and 4.
+  const bool multi_head_ok = D == 128 && G * prm.max_q_per_seq <= 4;
   int hw = prm.heads_per_wg;
   if (hw == 0) hw = !multi_head_ok ? 1 : (Hkv % 4 == 0 ? 4 : (Hkv % 2 == 0 ? 2 : 1));
   if (hw != 1 && (!multi_head_ok || (hw != 2 && hw != 4) || Hkv % hw != 0))
     return fail(err, errn, SKVD_ERR_PLAN, "heads_per_wg=%d: only 1, or 2 / 4 dividing Hkv=%d "
-                "for int8 at head_dim 128 with G*T <= 4", prm.heads_per_wg, Hkv);
+                "at head_dim 128 with G*T <= 4", prm.heads_per_wg, Hkv);
 
   Plan p{};
   p.prm = prm;
@@ -146,11 +145,14 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
   p.schedule = sched;
   if (sched == SKVD_SCHEDULE_BALANCED) {
     p.part_stride = p.splits_cap + 1;
-    // Workgroups per CU (measured on MI355X): about three resident waves per CU saturate the
-    // memory pipes of an f16 stream; int8 at D=128 also needs vector-ALU throughput, so more
-    // waves; D=256 workgroups are the largest (one wave per SIMD fits).
+    // Workgroups per CU (measured on MI355X): one wave per SIMD saturates the memory pipes of
+    // an f16 stream, best as one workgroup of 4 KV heads reading each token row's heads
+    // together; int8 at D=128 also needs vector-ALU throughput, so two waves per SIMD; D=256
+    // workgroups are the largest (3 per CU measured best).
     const bool i8 = prm.kv_dtype == SKVD_KV_I8_F16SCALE32;
-    const int auto_wpc = D == 256 ? 3 : (i8 && p.row_blocks == 1 ? 8 / hw : kDefaultWgsPerCu);
+    const int auto_wpc = D == 256 ? 3
+                         : p.row_blocks == 1 ? (i8 ? 8 : kDefaultWgsPerCu) / hw
+                                             : kDefaultWgsPerCu;
     p.grid_wgs = (prm.wgs_per_cu ? prm.wgs_per_cu : auto_wpc) * num_cus;
   } else {
     p.part_stride = p.splits_cap;

@@ -64,7 +64,7 @@ def test_plan_splits_and_total_reducer(maxlen, bps):
         assert p.reducer == "none" and p.schedule == "static" and i.part_stride == 1
     else:  # max_batch 32 <= 64: the balanced schedule, one more slot per row
         assert p.schedule == "balanced" and i.part_stride == i.splits_cap + 1
-        assert i.grid_wgs == 4 * 256
+        assert i.grid_wgs == 256 and i.heads_per_wg == 4  # 4 KV heads per workgroup, 1 per CU
     if p.reducer == "cooperative":
         assert i.part_stride <= 64
     if p.reducer == "hierarchical":
@@ -79,11 +79,11 @@ def test_schedule_choice():
     assert plan(max_batch=64).schedule == "balanced"
     p = plan(max_batch=65)
     assert p.schedule == "static" and p.info.part_stride == p.info.splits_cap
-    assert p.info.grid_wgs == (p.info.splits_cap | 1) * 8 * 65
+    assert p.info.grid_wgs == (p.info.splits_cap | 1) * (8 // p.info.heads_per_wg) * 65
     s = plan(schedule="static")
     assert s.schedule == "static" and s.info.part_stride == s.info.splits_cap
     w = plan(wgs_per_cu=7, num_cus=100)
-    assert w.schedule == "balanced" and w.info.grid_wgs == 700
+    assert w.schedule == "balanced" and w.info.grid_wgs == 700 and w.info.heads_per_wg == 4
     assert "schedule=balanced" in w.describe()
     # defaults per variant: 4 per CU, 3 at head_dim 256, 8 waves per CU for int8 single-quarter
     # tiles, whose workgroups serve 4 (else 2) KV heads
@@ -95,7 +95,9 @@ def test_schedule_choice():
     assert plan(kv_dtype="i8", heads_per_wg=1).info.grid_wgs == 8 * 256
     assert plan(kv_dtype="i8", max_q_per_seq=2).info.grid_wgs == 4 * 256
     assert plan(kv_dtype="i8", max_q_per_seq=2).info.heads_per_wg == 1
-    assert plan().info.heads_per_wg == 1
+    assert plan().info.heads_per_wg == 4 and plan().info.grid_wgs == 256
+    assert plan(heads_per_wg=1).info.grid_wgs == 4 * 256
+    assert plan(num_kv_heads=2, num_qo_heads=8).info.grid_wgs == 2 * 256
     st = plan(kv_dtype="i8", schedule="static")
     assert st.info.grid_wgs == (st.info.splits_cap | 1) * 2 * 32
 
@@ -128,7 +130,7 @@ def test_heuristic_configs():
     (dict(schedule="balanced", max_batch=65), 7), (dict(schedule="balanced", max_kv_len=256), 7),
     (dict(schedule="balanced", force_reducer="none", max_kv_len=200), 7),
     (dict(schedule=3), 7), (dict(wgs_per_cu=65), 7), (dict(wgs_per_cu=-1), 7),
-    (dict(heads_per_wg=2), 7), (dict(kv_dtype="i8", heads_per_wg=3), 7),
+    (dict(heads_per_wg=2, max_q_per_seq=2), 7), (dict(kv_dtype="i8", heads_per_wg=3), 7),
     (dict(kv_dtype="i8", heads_per_wg=8), 7), (dict(kv_dtype="i8", heads_per_wg=4, num_kv_heads=2,
                                                    num_qo_heads=8), 7),
     (dict(kv_dtype="i8", heads_per_wg=2, head_dim=256), 7),

@@ -101,13 +101,14 @@ def test_balanced_schedule_edges(case):
     assert plan.schedule == "balanced"
 
 
+@pytest.mark.parametrize("kv", ["i8", "f16"])
 @pytest.mark.parametrize("hw", [1, 2, 4])
 @pytest.mark.parametrize("schedule", ["balanced", "static"])
 @pytest.mark.parametrize("P", [16, 1])
-def test_int8_heads_per_workgroup(hw, schedule, P):
-    """int8 workgroups serving 1, 2 or 4 KV heads (one wave each) over the same blocks."""
-    s = spec(name="i8hw", batch=5, q_per_seq=1, num_qo_heads=32, num_kv_heads=8, head_dim=128,
-             page_size=P, kv_dtype="i8", lens=("list", (1, 700, 64, 2100, 333)))
+def test_heads_per_workgroup(kv, hw, schedule, P):
+    """Workgroups serving 1, 2 or 4 KV heads (one wave each) over the same blocks."""
+    s = spec(name="hw", batch=5, q_per_seq=1, num_qo_heads=32, num_kv_heads=8, head_dim=128,
+             page_size=P, kv_dtype=kv, lens=("list", (1, 700, 64, 2100, 333)))
     _, _, plan, _, _ = check(s, seed=hw * 10 + P, plan_kw=dict(heads_per_wg=hw, schedule=schedule,
                                                               force_blocks_per_split=2))
     assert plan.info.heads_per_wg == hw
