@@ -170,7 +170,7 @@ struct Shares {
   int len_l;
   unsigned nb_l, pre_l;
   int64_t n_blocks;  // N = (Hkv / heads per workgroup) * sum of block counts
-  int n_shares;      // W = min(grid, N / bps), at least 1 when N > 0
+  int n_shares;      // W = min(grid, N / piece_min), at least 1 when N > 0
 };
 
 __device__ __forceinline__ Shares balanced_shares(const LaunchArgs &a, int debug) {
@@ -190,7 +190,7 @@ __device__ __forceinline__ Shares balanced_shares(const LaunchArgs &a, int debug
                 (a.Hkv / a.heads_per_wg);
   sh.n_shares = sh.n_blocks == 0
                     ? 0
-                    : (int)max((int64_t)1, min((int64_t)a.grid_wgs, sh.n_blocks / a.bps));
+                    : (int)max((int64_t)1, min((int64_t)a.grid_wgs, sh.n_blocks / a.piece_min));
   return sh;
 }
 
@@ -316,7 +316,8 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
     const int64_t row0 = (int64_t)Hg * pre_b + (int64_t)grp * nb_b;  // the row's first block
     const int64_t seg_end = min(x_end, row0 + nb_b);
     blk_hi = blk_lo + (int)(seg_end - x_cur);
-    slot = share - share_of(row0, sh.n_blocks, sh.n_shares);
+    // compact slot of (schedule row b*Hg + grp, share): unique, below rows + shares
+    slot = b * Hg + grp + share;
     x_cur = seg_end;
   } else {
     if (!pending) break;
@@ -743,6 +744,11 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
 #pragma unroll
   for (int e = 0; e < 4; ++e) lsum[e] = row16_sum(lsum[e]);
   const int Hq = a.Hq;
+  // Partial index of output row `orow` (query row rr of this wave's KV head): static, the
+  // split slot of the row; balanced, the compact slot's entry for this head and row.
+  auto part_index = [&](int64_t orow, int rr) __attribute__((always_inline)) -> int64_t {
+    return a.balanced ? ((int64_t)slot * HW + wave) * R + rr : orow * a.part_stride + slot;
+  };
 
   if constexpr (PVM) {
     // ---- output: lanes of group g4 hold rows 4*g4 + e, column 16*dt + c16
@@ -760,11 +766,11 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
         for (int dt = 0; dt < NDT; ++dt) o[16 * dt] = (_Float16)(acc[dt][e] * inv);
         if (a.lse && c16 == 0) a.lse[row] = l > 0.f ? (m[e] + __log2f(l)) * kLn2 : kNegInf;
       } else {
-        float *dst = a.ws_o + (row * a.part_stride + slot) * D + c16;
+        float *dst = a.ws_o + part_index(row, hg + G * t) * D + c16;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) dst[16 * dt] = acc[dt][e];
         if (c16 == 0) {
-          float *ml = a.ws_ml + (row * a.part_stride + slot) * 2;
+          float *ml = a.ws_ml + part_index(row, hg + G * t) * 2;
           ml[0] = m[e];
           ml[1] = lsum[e];
         }
@@ -801,11 +807,11 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
         *(half8 *)((_Float16 *)a.o + row * D + vlane_el) = out;
         if (a.lse && lane == 0) a.lse[row] = l > 0.f ? (mr[r] + __log2f(l)) * kLn2 : kNegInf;
       } else {
-        float *dst = a.ws_o + (row * a.part_stride + slot) * D + vlane_el;
+        float *dst = a.ws_o + part_index(row, hg + G * t) * D + vlane_el;
         *(float4v *)dst = float4v{accv[r][0], accv[r][1], accv[r][2], accv[r][3]};
         *(float4v *)(dst + 4) = float4v{accv[r][4], accv[r][5], accv[r][6], accv[r][7]};
         if (lane == 0) {
-          float *ml = a.ws_ml + (row * a.part_stride + slot) * 2;
+          float *ml = a.ws_ml + part_index(row, hg + G * t) * 2;
           ml[0] = mr[r];
           ml[1] = lr[r];
         }
@@ -816,24 +822,40 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
 }
 
 // ----------------------------------------------------------------------------- merge kernels
-// Partials of output row `row` (sequence b, query head -> KV head): static, the splits that
-// cover the sequence's blocks; balanced, the shares the (sequence, KV head) row's blocks meet,
-// by the partial kernel's own integer arithmetic. Called by the whole wave.
-__device__ __forceinline__ int parts_of_row(const LaunchArgs &a, int64_t row) {
-  const int b = (int)(row / ((int64_t)a.T * a.Hq));
+// The partials of output row `row` (sequence b, query head -> KV head): their count, the
+// index of the first and the index step between consecutive ones. Static: the splits covering
+// the sequence's blocks, contiguous at row * part_stride. Balanced: the shares the (sequence,
+// head group) schedule row r meets, w_first .. w_last, in compact slots r + w, by the partial
+// kernel's own integer arithmetic. Called by the whole wave.
+struct RowParts {
+  int64_t first;
+  int64_t stride;
+  int count;
+};
+
+__device__ __forceinline__ RowParts row_parts(const LaunchArgs &a, int64_t row) {
+  const int64_t per_seq = (int64_t)a.T * a.Hq;
+  const int b = (int)(row / per_seq);
   if (!a.balanced) {
     const int L = clamp_len(a.kv_len[b], a.max_kv_len, a.status, 0);
     const int nblk = (L + 63) >> 6;
-    return (nblk + a.bps - 1) / a.bps;
+    return {row * a.part_stride, 1, (nblk + a.bps - 1) / a.bps};
   }
-  const int grp = (int)(row % a.Hq) / a.G / a.heads_per_wg;  // the KV head's group
+  const int rem = (int)(row - b * per_seq);
+  const int t = rem / a.Hq, qh = rem - t * a.Hq;
+  const int kvh = qh / a.G, hg = qh - kvh * a.G;
+  const int HW = a.heads_per_wg, Hg = a.Hkv / HW;
+  const int grp = kvh / HW, wave = kvh - grp * HW;
+  const int RT = a.G * a.T;
   const Shares sh = balanced_shares(a, 0);
   const int64_t pre_b = (unsigned)__builtin_amdgcn_readlane((int)sh.pre_l, b);
   const int64_t nb_b = __builtin_amdgcn_readlane((int)sh.nb_l, b);
-  if (nb_b == 0) return 0;
-  const int64_t row0 = (a.Hkv / a.heads_per_wg) * pre_b + grp * nb_b;
-  return share_of(row0 + nb_b - 1, sh.n_blocks, sh.n_shares) -
-         share_of(row0, sh.n_blocks, sh.n_shares) + 1;
+  if (nb_b == 0) return {0, 1, 0};
+  const int64_t row0 = Hg * pre_b + grp * nb_b;
+  const int w0 = share_of(row0, sh.n_blocks, sh.n_shares);
+  const int w1 = share_of(row0 + nb_b - 1, sh.n_blocks, sh.n_shares);
+  const int64_t r = (int64_t)b * Hg + grp;
+  return {((r + w0) * HW + wave) * RT + hg + a.G * t, (int64_t)HW * RT, w1 - w0 + 1};
 }
 
 // Final write of one row from an unnormalized accumulator (wave 0's lanes hold D/64 each).
@@ -883,42 +905,29 @@ struct PerVecT<4> {
   typedef float4v type;
 };
 
-// Cooperative step: up to 64 partials first, first + stride, ... one per lane of this wave.
-// Each lane's (m, l) gives the wave max and sum; the lanes then walk the partials' output
+// Cooperative step: up to 64 partials (indices first, first + stride, ...) one per lane of this
+// wave. Each lane's (m, l) gives the wave max and sum; the lanes then walk the partials' output
 // slices (PER elements per lane), eight loads in flight, each weight broadcast from the lane
-// that owns the partial. The loads of the first eight slices and of every lane's (m, l) are
-// issued for the first min(cap, 64) slots before the count is known (count() is evaluated
-// after them, so its own loads overlap); slots at or past the count are ignored.
-template <int D, class CountFn>
+// that owns the partial.
+template <int D>
 __device__ __forceinline__ void merge_lanes(const float *ml, const float *po, int64_t first,
-                                            int stride, int cap, CountFn count,
-                                            MergeAcc<D / 64> *out) {
+                                            int64_t stride, int cnt, MergeAcc<D / 64> *out) {
   constexpr int PER = D / 64;
   using PerVec = typename PerVecT<PER>::type;
   typedef float float2v __attribute__((ext_vector_type(2)));
   const int lane = threadIdx.x & 63;
-  const int64_t sl = first + (int64_t)stride * lane;
   float2v mlv = {kNegInf, 0.f};
-  if (lane < cap) mlv = *(const float2v *)(ml + 2 * sl);
-  PerVec ov[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    ov[j] = j < cap ? *(const PerVec *)(po + (first + (int64_t)stride * j) * D + PER * lane)
-                    : (PerVec)0.f;
-  const int cnt = min(count(), cap);
-  const float m = lane < cnt ? mlv[0] : kNegInf;
-  const float M = wave_max(m);
-  const float w = M == kNegInf ? 0.f : part_weight(m, M);
-  const float S = wave_sum(lane < cnt ? w * mlv[1] : 0.f);
+  if (lane < cnt) mlv = *(const float2v *)(ml + 2 * (first + stride * lane));
+  const float M = wave_max(mlv[0]);
+  const float w = M == kNegInf ? 0.f : part_weight(mlv[0], M);
+  const float S = wave_sum(w * mlv[1]);
   float acc[PER] = {};
   for (int k0 = 0; k0 < cnt; k0 += 8) {
-    if (k0 > 0) {
+    PerVec ov[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        ov[j] = k0 + j < cnt ? *(const PerVec *)(po + (first + (int64_t)stride * (k0 + j)) * D +
-                                                PER * lane)
-                             : (PerVec)0.f;
-    }
+    for (int j = 0; j < 8; ++j)
+      ov[j] = k0 + j < cnt ? *(const PerVec *)(po + (first + stride * (k0 + j)) * D + PER * lane)
+                           : (PerVec)0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float wj = k0 + j < cnt ? readlane_f(w, k0 + j) : 0.f;
@@ -930,23 +939,18 @@ __device__ __forceinline__ void merge_lanes(const float *ml, const float *po, in
 }
 
 // Multipass: the NW waves of the workgroup take partials w, w + NW, ... in rounds of 64 per
-// wave; the per-wave states are combined through LDS. Wave 0 returns the row's state. cap
-// bounds the partial count (the row's slots) and count() gives it.
-template <int D, int NW, class CountFn>
-__device__ __forceinline__ MergeAcc<D / 64> merge_waves(const float *ml, const float *po, int cap,
-                                                        CountFn count) {
+// wave; the per-wave states are combined through LDS. Wave 0 returns the row's state.
+template <int D, int NW>
+__device__ __forceinline__ MergeAcc<D / 64> merge_waves(const float *ml, const float *po,
+                                                        int64_t first, int64_t stride, int n) {
   constexpr int PER = D / 64;
   __shared__ float st_lds[NW][2 + D];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   MergeAcc<PER> r;
-  const int capw = cap > wave ? (cap - wave + NW - 1) / NW : 0;  // this wave's slots
-  int n = 0;
-  merge_lanes<D>(ml, po, wave, NW, min(64, capw), [&]() { n = count(); return
-                 n > wave ? (n - wave + NW - 1) / NW : 0; }, &r);
-  const int nw = n > wave ? (n - wave + NW - 1) / NW : 0;
-  for (int c0 = 64; c0 < nw; c0 += 64)
-    merge_lanes<D>(ml, po, wave + (int64_t)NW * c0, NW, min(64, nw - c0),
-                   [&]() { return 64; }, &r);
+  const int nw = n > wave ? (n - wave + NW - 1) / NW : 0;  // this wave's partials
+  for (int c0 = 0; c0 < nw; c0 += 64)
+    merge_lanes<D>(ml, po, first + stride * (wave + (int64_t)NW * c0), stride * NW,
+                   min(64, nw - c0), &r);
   if constexpr (NW > 1) {
     if (lane == 0) {
       st_lds[wave][0] = r.M;
@@ -976,22 +980,24 @@ __global__ __launch_bounds__(64) void merge_direct(LaunchArgs a) {
   constexpr int PER = D / 64;
   using PerVec = typename PerVecT<PER>::type;
   const int64_t row = blockIdx.x;
-  const int n = parts_of_row(a, row);
-  const float *ml = a.ws_ml + row * a.part_stride * 2;
-  const float *po = a.ws_o + row * a.part_stride * D + PER * threadIdx.x;
+  const RowParts rp = row_parts(a, row);
+  const int n = rp.count;
   float M = kNegInf;
-  for (int s = 0; s < n; ++s) M = fmaxf(M, ml[2 * s]);
+  for (int s = 0; s < n; ++s) M = fmaxf(M, a.ws_ml[2 * (rp.first + rp.stride * s)]);
   float S = 0.f, acc[PER] = {};
   for (int s0 = 0; s0 < n; s0 += 4) {
     PerVec ov[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      ov[j] = s0 + j < n ? *(const PerVec *)(po + (int64_t)(s0 + j) * D) : (PerVec)0.f;
+      ov[j] = s0 + j < n ? *(const PerVec *)(a.ws_o + (rp.first + rp.stride * (s0 + j)) * D +
+                                             PER * threadIdx.x)
+                         : (PerVec)0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if (s0 + j >= n) continue;
-      const float w = part_weight(ml[2 * (s0 + j)], M);
-      S += w * ml[2 * (s0 + j) + 1];
+      const float *mlj = a.ws_ml + 2 * (rp.first + rp.stride * (s0 + j));
+      const float w = part_weight(mlj[0], M);
+      S += w * mlj[1];
 #pragma unroll
       for (int i = 0; i < PER; ++i) acc[i] = fmaf(w, ov[j][i], acc[i]);
     }
@@ -1004,28 +1010,24 @@ __global__ __launch_bounds__(64) void merge_direct(LaunchArgs a) {
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) void merge_rows(LaunchArgs a) {
   const int64_t row = blockIdx.x;
-  const MergeAcc<D / 64> r =
-      merge_waves<D, NW>(a.ws_ml + row * a.part_stride * 2, a.ws_o + row * a.part_stride * D,
-                         a.part_stride, [&]() { return parts_of_row(a, row); });
+  const RowParts rp = row_parts(a, row);
+  const MergeAcc<D / 64> r = merge_waves<D, NW>(a.ws_ml, a.ws_o, rp.first, rp.stride, rp.count);
   if (threadIdx.x < 64) write_row<D>(a, row, r.acc, r.M, r.S);
 }
 
-// Hierarchical level 1: workgroup (row, g) merges partials 64g .. 64g+63 (cooperatively) into
-// one unnormalized partial of the same form.
+// Hierarchical level 1: workgroup (row, g) merges the row's partials 64g .. 64g+63
+// (cooperatively) into one unnormalized partial of the same form.
 template <int D>
 __global__ __launch_bounds__(64) void merge_hier1(LaunchArgs a) {
   constexpr int PER = D / 64;
   const int64_t row = blockIdx.x;
   const int g = blockIdx.y;
+  const RowParts rp = row_parts(a, row);
   const int s0 = g * kHierGroup;
-  int n = 0;
+  if (s0 >= rp.count) return;
   MergeAcc<PER> r;
-  merge_lanes<D>(a.ws_ml + row * a.part_stride * 2, a.ws_o + row * a.part_stride * D, s0, 1,
-                 min(kHierGroup, a.part_stride - s0), [&]() {
-                   n = parts_of_row(a, row);
-                   return max(0, min(kHierGroup, n - s0));
-                 }, &r);
-  if (s0 >= n) return;
+  merge_lanes<D>(a.ws_ml, a.ws_o, rp.first + rp.stride * s0, rp.stride,
+                 min(kHierGroup, rp.count - s0), &r);
   float *dst = a.ws_ho + (row * a.hier_groups_cap + g) * D + PER * threadIdx.x;
 #pragma unroll
   for (int i = 0; i < PER; ++i) dst[i] = r.acc[i];
@@ -1040,9 +1042,9 @@ __global__ __launch_bounds__(64) void merge_hier1(LaunchArgs a) {
 template <int D>
 __global__ __launch_bounds__(64 * kMergeWaves) void merge_hier2(LaunchArgs a) {
   const int64_t row = blockIdx.x;
+  const int ng = (row_parts(a, row).count + kHierGroup - 1) / kHierGroup;
   const MergeAcc<D / 64> r = merge_waves<D, kMergeWaves>(
-      a.ws_hml + row * a.hier_groups_cap * 2, a.ws_ho + row * a.hier_groups_cap * D,
-      a.hier_groups_cap, [&]() { return (parts_of_row(a, row) + kHierGroup - 1) / kHierGroup; });
+      a.ws_hml, a.ws_ho, row * a.hier_groups_cap, 1, ng);
   if (threadIdx.x < 64) write_row<D>(a, row, r.acc, r.M, r.S);
 }
 

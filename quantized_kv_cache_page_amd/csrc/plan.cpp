@@ -8,6 +8,7 @@
 // were JIT SGPR exhaustion" and "Residual >2048 fault root-caused and fixed"), the reducer,
 // and the exact workspace layout, so that a decode call allocates nothing (llama-cpp-
 // turboquant PR #176, problem statement: allocation inside a captured stream fails).
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -131,8 +132,9 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
   // Schedule. Static: workgroups are (split, KV head, sequence) at fixed block offsets, so a
   // ragged batch leaves some compute units with more work than others once the grid fits the
   // chip in one round. Balanced: equal shares of the blocks actually present, cut on the device
-  // from kv_len (one sequence per lane, hence the batch limit); every share is at least
-  // bps blocks, so a row meets at most splits_cap + 1 shares.
+  // from kv_len (one sequence per lane, hence the batch limit); partials go to compact slots,
+  // one per (schedule row, share) pair that meet — at most rows + shares — so the workspace does
+  // not grow with the context and shares can be as small as one block.
   int sched = prm.schedule;
   const bool can_balance = p.splits_cap > 1 && prm.max_batch <= kBalancedMaxBatch &&
                            prm.force_reducer != SKVD_REDUCER_NONE;
@@ -144,7 +146,6 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
                 kBalancedMaxBatch, p.splits_cap, prm.max_batch);
   p.schedule = sched;
   if (sched == SKVD_SCHEDULE_BALANCED) {
-    p.part_stride = p.splits_cap + 1;
     // Workgroups per CU (measured on MI355X): one wave per SIMD saturates the memory pipes of
     // an f16 stream, best as one workgroup of 4 KV heads reading each token row's heads
     // together; int8 at D=128 also needs vector-ALU throughput, so two waves per SIMD; D=256
@@ -154,8 +155,16 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
                          : p.row_blocks == 1 ? (i8 ? 8 : kDefaultWgsPerCu) / hw
                                              : kDefaultWgsPerCu;
     p.grid_wgs = (prm.wgs_per_cu ? prm.wgs_per_cu : auto_wpc) * num_cus;
+    // a forced split size becomes the balanced shares' minimum
+    p.piece_min = prm.force_blocks_per_split > 0 ? p.bps : 1;
+    const int64_t per_row = std::min<int64_t>(p.grid_wgs,
+                                              (p.max_blocks + p.piece_min - 1) / p.piece_min + 1);
+    p.part_stride = (int)per_row;
+    p.slots_cap = (int64_t)prm.max_batch * (Hkv / hw) + p.grid_wgs;
   } else {
     p.part_stride = p.splits_cap;
+    p.piece_min = p.bps;
+    p.slots_cap = 0;
     p.grid_wgs = (int)((int64_t)(p.splits_cap | 1) * per_split);
   }
 
@@ -183,7 +192,10 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
   size_t off = 0;
   p.off_status = off;
   off = align_up(off + sizeof(uint32_t));
-  const size_t parts = red == SKVD_REDUCER_NONE ? 0 : (size_t)p.rows_cap * p.part_stride;
+  const size_t parts = red == SKVD_REDUCER_NONE ? 0
+                       : sched == SKVD_SCHEDULE_BALANCED
+                           ? (size_t)p.slots_cap * hw * R
+                           : (size_t)p.rows_cap * p.part_stride;
   p.off_ml = off;
   off = align_up(off + parts * 2 * sizeof(float));
   p.off_o = off;
@@ -296,6 +308,7 @@ void fill_launch_args(const Plan &p, const skvd_decode_args &a, void *ws, Launch
   l.grid_wgs = p.grid_wgs;
   l.heads_per_wg = p.heads_per_wg;
   l.part_stride = p.part_stride;
+  l.piece_min = p.piece_min;
   l.max_kv_len = p.prm.max_kv_len;
   l.hier_groups_cap = p.hier_groups_cap;
   l.int8 = p.prm.kv_dtype == SKVD_KV_I8_F16SCALE32;

@@ -25,7 +25,10 @@ struct Plan {
   int bps;            // 64-token blocks per split
   int splits_cap;     // ceil(max_blocks / bps): static splits per row at max_kv_len
   int schedule;       // resolved skvd_schedule
-  int part_stride;    // partial slots per row: splits_cap (+ 1 when balanced)
+  int part_stride;    // partials per output row at most: static splits_cap (the row's slot
+                      // stride); balanced min(grid, max_blocks / piece_min + 1)
+  int piece_min;      // balanced: fewest 64-token blocks in a share
+  int64_t slots_cap;  // balanced: compact slots (schedule rows + shares)
   int grid_wgs;       // partial-kernel grid (static: split_stride * Hkv / hw * max_batch)
   int heads_per_wg;   // hw: KV heads served by one workgroup, one wave each
   int reducer;        // resolved skvd_reducer
@@ -49,11 +52,12 @@ struct LaunchArgs {
   int batch, T, Hq, Hkv, G, D, page_shift;
   float scale_log2;  // sm_scale * log2(e): scores are kept in base 2
   int bps, splits_cap, split_stride, max_kv_len, hier_groups_cap;  // stride: odd, >= cap
-  int balanced, grid_wgs, part_stride;
+  int balanced, grid_wgs, part_stride, piece_min;
   int heads_per_wg;  // KV heads (waves) per partial-kernel workgroup; divides Hkv
   int int8, debug;
-  float *ws_ml;      // [rows_cap][part_stride][2]  (max in log2 units, sum)
-  float *ws_o;       // [rows_cap][part_stride][D]  unnormalized f32 output
+  // partials (static: [rows_cap][part_stride]; balanced: [slots][heads_per_wg][G*T]):
+  float *ws_ml;      // [..][2]  (max in log2 units, sum)
+  float *ws_o;       // [..][D]  unnormalized f32 output
   float *ws_hml;     // [rows_cap][hier_groups_cap][2]
   float *ws_ho;      // [rows_cap][hier_groups_cap][D]
   unsigned *status;

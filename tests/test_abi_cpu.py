@@ -62,16 +62,25 @@ def test_plan_splits_and_total_reducer(maxlen, bps):
     assert p.reducer in ("none", "direct", "cooperative", "multipass", "hierarchical")
     if i.splits_cap == 1:
         assert p.reducer == "none" and p.schedule == "static" and i.part_stride == 1
-    else:  # max_batch 32 <= 64: the balanced schedule, one more slot per row
-        assert p.schedule == "balanced" and i.part_stride == i.splits_cap + 1
-        assert i.grid_wgs == 256 and i.heads_per_wg == 4  # 4 KV heads per workgroup, 1 per CU
+    else:  # max_batch 32 <= 64: the balanced schedule; a row meets at most min(grid, pieces + 1)
+        # shares, a piece being one block (or the forced split size)
+        assert p.schedule == "balanced" and i.heads_per_wg == 4
+        assert i.grid_wgs == 256  # 4 KV heads per workgroup, one workgroup per CU
+        piece = min(bps, blocks) if bps else 1
+        assert i.part_stride == min(i.grid_wgs, -(-blocks // piece) + 1)
     if p.reducer == "cooperative":
         assert i.part_stride <= 64
     if p.reducer == "hierarchical":
         assert i.hier_groups_cap == -(-i.part_stride // 64)
-    # workspace holds the status word plus (m, l, D floats) per row and partial slot
+    # workspace holds the status word plus (m, l, D floats) per partial: static, per output row
+    # and split; balanced, per compact slot (schedule rows + shares), head and query row
     rows = 32 * 1 * 32
-    need = 0 if p.reducer == "none" else rows * i.part_stride * (2 + 128) * 4
+    if p.reducer == "none":
+        need = 0
+    elif p.schedule == "static":
+        need = rows * i.part_stride * (2 + 128) * 4
+    else:
+        need = (32 * 2 + i.grid_wgs) * 4 * 4 * (2 + 128) * 4
     assert i.workspace_bytes >= need + 4
 
 
@@ -104,8 +113,11 @@ def test_schedule_choice():
 
 @pytest.mark.parametrize("red", ["direct", "multipass", "hierarchical"])
 def test_forced_reducers_cover_any_count(red):
-    p = plan(max_kv_len=262208, force_blocks_per_split=1, force_reducer=red)
-    assert p.info.splits_cap == 4097 and p.info.part_stride == 4098 and p.reducer == red
+    p = plan(max_kv_len=262208, force_blocks_per_split=1, force_reducer=red, schedule="static")
+    assert p.info.splits_cap == 4097 and p.info.part_stride == 4097 and p.reducer == red
+    b = plan(max_kv_len=262208, force_blocks_per_split=1, force_reducer=red)
+    assert b.schedule == "balanced" and b.info.part_stride == b.info.grid_wgs == 256
+    assert b.reducer == red
 
 
 def test_heuristic_configs():

@@ -131,13 +131,15 @@ def test_balanced_all_empty():
 @pytest.mark.parametrize("red,bps", [("direct", 1), ("cooperative", 1), ("multipass", 1),
                                      ("hierarchical", 1), ("direct", 3), ("multipass", 7),
                                      ("hierarchical", 2), ("none", 1000)])
-def test_forced_reducers_and_splits(kv, red, bps):
+@pytest.mark.parametrize("schedule", ["auto", "static"])
+def test_forced_reducers_and_splits(kv, red, bps, schedule):
     s = spec(name="forced", batch=3, q_per_seq=1, num_qo_heads=16, num_kv_heads=4, head_dim=128,
              page_size=16, kv_dtype=kv, lens=("list", (70, 1300, 5000)))
     if red == "cooperative":
         s = spec(name="forced", batch=3, q_per_seq=1, num_qo_heads=16, num_kv_heads=4,
                  head_dim=128, page_size=16, kv_dtype=kv, lens=("list", (70, 1300, 4000)))
-    check(s, seed=7, plan_kw=dict(force_reducer=red, force_blocks_per_split=bps))
+    check(s, seed=7, plan_kw=dict(force_reducer=red, force_blocks_per_split=bps,
+                                  schedule=schedule))
 
 
 @pytest.mark.parametrize("L", [2047, 2048, 2049, 4095, 4096, 4097])
@@ -147,8 +149,9 @@ def test_2048_4096_boundaries(L):
     s = spec(name=f"boundary{L}", batch=2, q_per_seq=1, num_qo_heads=32, num_kv_heads=8,
              head_dim=128, page_size=16, lens=("list", (L, L - 1000)))
     for red in ("multipass", "hierarchical", "direct"):
-        check(s, seed=L, plan_kw=dict(force_blocks_per_split=1, force_reducer=red),
-              what=f"L={L} {red}")
+        check(s, seed=L, plan_kw=dict(force_blocks_per_split=1, force_reducer=red,
+                                      schedule="static"), what=f"L={L} {red} static")
+    check(s, seed=L, plan_kw=dict(force_blocks_per_split=1), what=f"L={L} balanced")
 
 
 def test_no_ceiling_262208():
@@ -156,10 +159,12 @@ def test_no_ceiling_262208():
     s = spec(name="beyond_cap", batch=1, q_per_seq=1, num_qo_heads=8, num_kv_heads=2,
              head_dim=128, page_size=64, lens=("list", (262208,)))
     rows = np.arange(8)
-    check(s, seed=11, plan_kw=dict(force_blocks_per_split=1, force_reducer="hierarchical"),
-          rows=rows)
-    check(s, seed=11, plan_kw=dict(force_blocks_per_split=1, force_reducer="multipass"),
-          rows=rows)
+    check(s, seed=11, plan_kw=dict(force_blocks_per_split=1, force_reducer="hierarchical",
+                                   schedule="static"), rows=rows)
+    check(s, seed=11, plan_kw=dict(force_blocks_per_split=1, force_reducer="multipass",
+                                   schedule="static"), rows=rows)
+    check(s, seed=11, plan_kw=dict(force_reducer="hierarchical"), rows=rows)
+    check(s, seed=11, rows=rows)
 
 
 def test_split_invariance():
