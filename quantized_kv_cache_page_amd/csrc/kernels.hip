@@ -111,10 +111,12 @@ __device__ __forceinline__ void wave_sync() {
 }
 
 // ----------------------------------------------------------------------------- int8 -> f16
-// Exact int8 -> f16 without conversion instructions: flip the sign bit of each byte (x + 128
-// as an unsigned byte u), put u under the f16 exponent of 1024 with a byte permute (the f16
-// with bits 0x64uu is 1024 + u, exact) and subtract 1152 with one packed f16 add per pair.
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// K operand (feeds the score MFMA, so compiler-visible code only: the MFMA's operand hazards are
+// tracked for the compiler's own instructions): flip the sign bit of each byte (x + 128 as an
+// unsigned byte u), put u under the f16 exponent of 1024 with a byte permute (the f16 with bits
+// 0x64uu is 1024 + u, exact) and subtract 1152 with one packed f16 add per pair.
 constexpr unsigned kExp1024 = 0x64646464u;  // every byte 0x64: f16 high byte of 1024
 
 __device__ __forceinline__ half2v magic_pair(unsigned flipped, unsigned sel) {
@@ -137,17 +139,44 @@ __device__ __forceinline__ half8 i8x8_to_h8(uint2v w) {
   return r;
 }
 
+// V pairs (feed v_dot2, vector ALU only): v_cvt_f16_i16 with SDWA operand selection takes byte
+// k of a dword sign-extended and writes either the low half of the result (clearing the high
+// half) or the high half (keeping the low half) -- a packed f16 pair in two instructions, one
+// per element, with no shifts, permutes or packs.
+template <int B>
+__device__ __forceinline__ unsigned cvt_i8_lo(unsigned src);
+template <int B>
+__device__ __forceinline__ unsigned cvt_i8_hi(unsigned dst, unsigned src);
+#define SKVD_CVT_I8(B)                                                                         \
+  template <>                                                                                  \
+  __device__ __forceinline__ unsigned cvt_i8_lo<B>(unsigned src) {                             \
+    unsigned r;                                                                                \
+    asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_" \
+        #B : "=v"(r) : "v"(src));                                                              \
+    return r;                                                                                  \
+  }                                                                                            \
+  template <>                                                                                  \
+  __device__ __forceinline__ unsigned cvt_i8_hi<B>(unsigned dst, unsigned src) {               \
+    asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE "           \
+        "src0_sel:BYTE_" #B : "+v"(dst) : "v"(src));                                           \
+    return dst;                                                                                \
+  }
+SKVD_CVT_I8(0)
+SKVD_CVT_I8(1)
+SKVD_CVT_I8(2)
+SKVD_CVT_I8(3)
+#undef SKVD_CVT_I8
+
 // Two int8 rows a (token t) and b (token t + 16), 8 elements each -> the 8 f16 pairs
-// (a_i, b_i): the bytes are interleaved first, then converted two elements per permute.
+// (a_i, b_i).
 __device__ __forceinline__ void i8_pairs(uint2v a, uint2v b, half2v *out) {
 #pragma unroll
   for (int w = 0; w < 2; ++w) {
-    const unsigned lo = __builtin_amdgcn_perm(b[w], a[w], 0x05010400u) ^ 0x80808080u;
-    const unsigned hi = __builtin_amdgcn_perm(b[w], a[w], 0x07030602u) ^ 0x80808080u;
-    out[4 * w + 0] = magic_pair(lo, 0x04010400u);
-    out[4 * w + 1] = magic_pair(lo, 0x04030402u);
-    out[4 * w + 2] = magic_pair(hi, 0x04010400u);
-    out[4 * w + 3] = magic_pair(hi, 0x04030402u);
+    const unsigned x = a[w], y = b[w];
+    out[4 * w + 0] = __builtin_bit_cast(half2v, cvt_i8_hi<0>(cvt_i8_lo<0>(x), y));
+    out[4 * w + 1] = __builtin_bit_cast(half2v, cvt_i8_hi<1>(cvt_i8_lo<1>(x), y));
+    out[4 * w + 2] = __builtin_bit_cast(half2v, cvt_i8_hi<2>(cvt_i8_lo<2>(x), y));
+    out[4 * w + 3] = __builtin_bit_cast(half2v, cvt_i8_hi<3>(cvt_i8_lo<3>(x), y));
   }
 }
 
