@@ -229,6 +229,18 @@ __device__ __forceinline__ int share_of(int64_t x, int64_t n_blocks, int n_share
 }
 
 // ----------------------------------------------------------------------------- partial kernel
+// K and V rows are read once: non-temporal loads (evict-first in L2, no Infinity Cache
+// allocation) when each load instruction covers whole 128-byte lines between the lanes that
+// share them (f16 K: half lines, consumed by the next instruction; f16 and int8 V: whole
+// lines). int8 K instructions cover a quarter of each line, whose other quarters are read by
+// the next three instructions: cached loads (measured: evict-first loses them).
+template <bool STREAM, class T>
+__device__ __forceinline__ T kv_load(const char *p) {
+  if constexpr (STREAM) return __builtin_nontemporal_load((const T *)p);
+  else return *(const T *)p;
+}
+
+// ----------------------------------------------------------------------------- partial kernel (body)
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4v *lds_s4_ptr;
@@ -456,7 +468,7 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
         const int tk = min(c16, tok_end - 1 - jte);
         const unsigned off = (unsigned)((tk * (int)a.tok_stride + 8 * g4) * ES);
 #pragma unroll
-        for (int k = 0; k < KS; ++k) kb[t][k] = *(const Vec *)(base + off + 32 * k * ES);
+        for (int k = 0; k < KS; ++k) kb[t][k] = kv_load<!I8, Vec>(base + off + 32 * k * ES);
         if constexpr (I8) {
           const _Float16 *sb = ksc + row_offset(pg, jte & P1, kvh, a.s_page_stride,
                                                 a.s_tok_stride, a.s_head_stride);
@@ -479,7 +491,7 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
                                        a.head_stride);
         const char *kp = kbase + (off + 8 * g4) * ES;
 #pragma unroll
-        for (int k = 0; k < KS; ++k) kb[t][k] = *(const Vec *)(kp + 32 * k * ES);
+        for (int k = 0; k < KS; ++k) kb[t][k] = kv_load<!I8, Vec>(kp + 32 * k * ES);
         if constexpr (I8) {
           const int64_t so = row_offset(pg, j & P1, kvh, a.s_page_stride, a.s_tok_stride,
                                         a.s_head_stride);
@@ -507,7 +519,7 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
                                               a.head_stride) * ES;
         const int tk = min((js & 15) + vlane_tok, tok_end - 1 - jte);
         const unsigned off = (unsigned)((tk * (int)a.tok_stride + vlane_el) * ES);
-        vb[s2] = *(const Vec *)(base + off);
+        vb[s2] = kv_load<true, Vec>(base + off);
       } else {
         const int j = min(js + vlane_tok, tok_end - 1);
         bool cl;
@@ -516,7 +528,7 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
         clamped_any |= cl;
         const int64_t off = row_offset(pg, j & P1, kvh, a.page_stride, a.tok_stride,
                                        a.head_stride);
-        vb[s2] = *(const Vec *)(vbase + (off + vlane_el) * ES);
+        vb[s2] = kv_load<true, Vec>(vbase + (off + vlane_el) * ES);
       }
     }
     if constexpr (I8) {
