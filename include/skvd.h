@@ -164,7 +164,9 @@ typedef struct {
   int64_t q_head_stride;     /* elements between heads (multiple of 8) */
   const void *k_pages;       /* [num_k_pages, P, Hkv, D] f16 or int8; 16-byte aligned */
   const void *v_pages;       /* [num_v_pages, P, Hkv, D], same strides as K */
-  int64_t page_stride;       /* elements between pages (shared by K and V) */
+  int64_t page_stride;       /* elements between pages (shared by K and V); the three strides
+                                are non-negative multiples of 16 bytes (8 f16 / 16 int8
+                                elements), else SKVD_ERR_LAYOUT */
   int64_t tok_stride;        /* elements between slots of a page */
   int64_t head_stride;       /* elements between KV heads */
   int64_t num_k_pages;       /* pages in the K pool (>= 1); ids are clamped below it */

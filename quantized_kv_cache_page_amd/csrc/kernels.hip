@@ -385,6 +385,12 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
   // Query rows as the score MFMA A operand: lane holds row (lane & 15), elements
   // 8*(lane>>4)..+7 of each 32-element contraction step.
   const int g4 = lane >> 4, c16 = lane & 15;
+  // head_dim element of step k's first lane element (the contraction order is free as long as
+  // q and K agree): f16, 32k + 8*g4; int8, group g4 + 4*(k/4) at offset 8*(k%4), so that each
+  // lane's elements of a group are 32 contiguous bytes under one scale
+  auto kelem = [&](int k) __attribute__((always_inline)) {
+    return I8 ? 32 * (g4 + 4 * (k >> 2)) + 8 * (k & 3) : 32 * k + 8 * g4;
+  };
   half8 qa[KS];
   {
     const int r = c16;
@@ -393,7 +399,7 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
       const _Float16 *qp = (const _Float16 *)a.q + ((int64_t)b * T + t) * a.q_tok_stride +
                            (int64_t)(kvh * G + hg) * a.q_head_stride + 8 * g4;
 #pragma unroll
-      for (int k = 0; k < KS; ++k) qa[k] = *(const half8 *)(qp + 32 * k);
+      for (int k = 0; k < KS; ++k) qa[k] = *(const half8 *)(qp + kelem(k) - 8 * g4);
     } else {
 #pragma unroll
       for (int k = 0; k < KS; ++k) qa[k] = (half8)(_Float16)0;
@@ -445,12 +451,12 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
     return bad ? (pg < 0 ? 0 : npages - 1) : (int64_t)pg;
   };
 
-  Vec kb[NT][KS];
+  Vec kb[NT][I8 ? 1 : KS];                   // f16 K: step k's 8 elements
+  uint4v kq[NT][I8 ? KS / 4 : 1][2];         // int8 K: the lane's 32 bytes of group g4 + 4m
+  _Float16 ksh[NT][I8 ? KS / 4 : 1];         // int8 K: the token's scale of group g4 + 4m
   Vec vb[NS];
-  // int8 scales, two f16 per register. K: tile t, groups 2k and 2k + 1 of the lane's token,
-  // from 8-byte loads (each token-head's D/32 scales are contiguous). V: the D/32 scales of
-  // chunk token (lane % CH), one load per lane, handed to the P.V lanes through LDS.
-  half2v ks2[NT][KS / 2];
+  // int8 V scales: the D/32 scales of chunk token (lane % CH), one 8-byte load per lane (a
+  // token-head's scales are contiguous), handed to the P.V lanes through LDS.
   uint2v vsr[D / 128];
 
   // K rows of chunk c0 in the score MFMA B-operand layout: tile t, lane (g4, c16) holds
@@ -466,20 +472,22 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
         const char *base = kbase + row_offset(pg, jte & P1, kvh, a.page_stride, a.tok_stride,
                                               a.head_stride) * ES;
         const int tk = min(c16, tok_end - 1 - jte);
-        const unsigned off = (unsigned)((tk * (int)a.tok_stride + 8 * g4) * ES);
-#pragma unroll
-        for (int k = 0; k < KS; ++k) kb[t][k] = kv_load<!I8, Vec>(base + off + 32 * k * ES);
         if constexpr (I8) {
+          const unsigned off = (unsigned)(tk * (int)a.tok_stride + 32 * g4);
+#pragma unroll
+          for (int m = 0; m < KS / 4; ++m)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+              kq[t][m][h] = kv_load<true, uint4v>(base + off + 128 * m + 16 * h);
           const _Float16 *sb = ksc + row_offset(pg, jte & P1, kvh, a.s_page_stride,
                                                 a.s_tok_stride, a.s_head_stride);
-          const unsigned so = (unsigned)(tk * (int)a.s_tok_stride);
+          const unsigned so = (unsigned)(tk * (int)a.s_tok_stride) + g4;
 #pragma unroll
-          for (int k4 = 0; k4 < KS / 4; ++k4) {
-            const uint2v w = *(const uint2v *)(sb + so + 4 * k4);
-            const unsigned w0 = w[0], w1 = w[1];
-            ks2[t][2 * k4] = __builtin_bit_cast(half2v, w0);
-            ks2[t][2 * k4 + 1] = __builtin_bit_cast(half2v, w1);
-          }
+          for (int m = 0; m < KS / 4; ++m) ksh[t][m] = sb[so + 4 * m];
+        } else {
+          const unsigned off = (unsigned)((tk * (int)a.tok_stride + 8 * g4) * ES);
+#pragma unroll
+          for (int k = 0; k < KS; ++k) kb[t][k] = kv_load<true, Vec>(base + off + 32 * k * ES);
         }
       } else {
         const int j = min(jt + c16, tok_end - 1);
@@ -489,19 +497,20 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
         clamped_any |= cl;
         const int64_t off = row_offset(pg, j & P1, kvh, a.page_stride, a.tok_stride,
                                        a.head_stride);
-        const char *kp = kbase + (off + 8 * g4) * ES;
-#pragma unroll
-        for (int k = 0; k < KS; ++k) kb[t][k] = kv_load<!I8, Vec>(kp + 32 * k * ES);
         if constexpr (I8) {
-          const int64_t so = row_offset(pg, j & P1, kvh, a.s_page_stride, a.s_tok_stride,
-                                        a.s_head_stride);
+          const char *kp = kbase + off + 32 * g4;
 #pragma unroll
-          for (int k4 = 0; k4 < KS / 4; ++k4) {
-            const uint2v w = *(const uint2v *)(ksc + so + 4 * k4);
-            const unsigned w0 = w[0], w1 = w[1];
-            ks2[t][2 * k4] = __builtin_bit_cast(half2v, w0);
-            ks2[t][2 * k4 + 1] = __builtin_bit_cast(half2v, w1);
-          }
+          for (int m = 0; m < KS / 4; ++m)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) kq[t][m][h] = kv_load<true, uint4v>(kp + 128 * m + 16 * h);
+          const int64_t so = row_offset(pg, j & P1, kvh, a.s_page_stride, a.s_tok_stride,
+                                        a.s_head_stride) + g4;
+#pragma unroll
+          for (int m = 0; m < KS / 4; ++m) ksh[t][m] = ksc[so + 4 * m];
+        } else {
+          const char *kp = kbase + (off + 8 * g4) * ES;
+#pragma unroll
+          for (int k = 0; k < KS; ++k) kb[t][k] = kv_load<true, Vec>(kp + 32 * k * ES);
         }
       }
     }
@@ -580,11 +589,14 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
     for (int t = 0; t < NT; ++t) {
       S[t] = (float4v)0.f;
       if constexpr (I8) {
+        // int8: step k's 8 elements are bytes 8(k%4) .. +7 of the lane's 32-byte group slice,
+        // widened exactly and scaled in f16 (one rounding of int8 * scale)
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
-          float4v part = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[k], i8x8_to_h8(kb[t][k]),
-                                                                (float4v)0.f, 0, 0, 0);
-          S[t] += part * (float)ks2[t][k >> 1][k & 1];
+          const uint4v &q4 = kq[t][k >> 2][(k & 3) >> 1];
+          const unsigned w0 = q4[2 * (k & 1)], w1 = q4[2 * (k & 1) + 1];
+          const half8 kh = i8x8_to_h8(uint2v{w0, w1}) * (half8)ksh[t][k >> 2];
+          S[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[k], kh, S[t], 0, 0, 0);
         }
       } else {
 #pragma unroll

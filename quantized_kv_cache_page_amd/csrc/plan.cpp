@@ -233,18 +233,18 @@ skvd_status check_args(const Plan &p, const skvd_decode_args *a, size_t ws_bytes
     return fail(err, errn, SKVD_ERR_DTYPE, "f16 cache takes no scales");
   if (!std::isfinite(a->sm_scale))
     return fail(err, errn, SKVD_ERR_SHAPE, "sm_scale is not finite");
-  // Vector loads: 16 bytes of q, o and f16 K/V rows; 8 bytes of int8 K/V rows.
-  const int64_t kv_vec = i8 ? 8 : 8;  // elements per vector load (16 B f16, 8 B int8)
+  // Vector loads: 16 bytes of q, o, K and f16 V rows; 8 bytes of int8 V rows.
+  const int64_t kv_vec = i8 ? 16 : 8;  // elements per 16-byte load
   if (!aligned(a->q, 16) || a->q_tok_stride % 8 || a->q_head_stride % 8 || a->q_tok_stride < 0 ||
       a->q_head_stride < 0)
     return fail(err, errn, SKVD_ERR_LAYOUT, "q must be 16-byte aligned with token/head "
                 "strides that are non-negative multiples of 8 elements");
-  if (!aligned(a->k_pages, i8 ? 8 : 16) || !aligned(a->v_pages, i8 ? 8 : 16) ||
+  if (!aligned(a->k_pages, 16) || !aligned(a->v_pages, 16) ||
       a->page_stride % kv_vec || a->tok_stride % kv_vec || a->head_stride % kv_vec ||
       a->page_stride < 0 || a->tok_stride < 0 || a->head_stride < 0)
-    return fail(err, errn, SKVD_ERR_LAYOUT, "K/V pools must be aligned to their vector load "
-                "and have page/token/head strides that are non-negative multiples of 8 "
-                "elements (head_dim dense, same strides for K and V)");
+    return fail(err, errn, SKVD_ERR_LAYOUT, "K/V pools must be 16-byte aligned and have "
+                "page/token/head strides that are non-negative multiples of 16 bytes "
+                "(head_dim dense, same strides for K and V)");
   // Scales: the D/32 scales of one token-head are read with 8-byte loads.
   if (i8 && (!aligned(a->k_scales, 8) || !aligned(a->v_scales, 8) || a->scale_page_stride < 0 ||
              a->scale_tok_stride < 0 || a->scale_head_stride < 0 || a->scale_page_stride % 4 ||

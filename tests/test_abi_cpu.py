@@ -194,8 +194,10 @@ def test_decode_check_f16(over, status):
 
 
 @pytest.mark.parametrize("over,status", [
-    ({}, 0), (dict(k_scales=None), 4), (dict(v_scales=None), 4), (dict(k_pages=FAKE + 8), 0),
+    ({}, 0), (dict(k_scales=None), 4), (dict(v_scales=None), 4), (dict(k_pages=FAKE + 8), 3),
+    (dict(k_pages=FAKE + 16), 0),
     (dict(k_pages=FAKE + 4), 3), (dict(k_scales=FAKE + 1), 3), (dict(v_scales=FAKE + 4), 3),
+    (dict(tok_stride=8 * 128 + 8), 3), (dict(tok_stride=8 * 128 + 16), 0),
     (dict(scale_tok_stride=34), 3), (dict(scale_head_stride=2), 3),
     (dict(scale_page_stride=16 * 8 * 4 + 2), 3), (dict(scale_tok_stride=36), 0),
 ])
