@@ -88,7 +88,7 @@ typedef enum {
   SKVD_REDUCER_AUTO = 0,
   SKVD_REDUCER_DIRECT = 1,       /* one wave per row walks the partials serially */
   SKVD_REDUCER_COOPERATIVE = 2,  /* one lane per partial (at most 64 partials) */
-  SKVD_REDUCER_MULTIPASS = 3,    /* lane-strided over any number of partials */
+  SKVD_REDUCER_MULTIPASS = 3,    /* lane-strided over any count (one wave when <= 64) */
   SKVD_REDUCER_HIERARCHICAL = 4, /* groups of 64 partials per workgroup, then a second merge */
   SKVD_REDUCER_NONE = 5          /* one split: the partial kernel writes o and lse itself */
 } skvd_reducer;

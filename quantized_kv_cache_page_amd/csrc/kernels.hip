@@ -1058,12 +1058,22 @@ __global__ __launch_bounds__(64) void merge_direct(LaunchArgs a) {
   write_row<D>(a, row, acc, M, S);
 }
 
-// Cooperative (one lane per partial, <= 64) and multipass (NW waves, lane-strided rounds):
-// one workgroup per row.
+// Cooperative (one wave, lane per partial, rounds of 64) and multipass (NW waves, lane-strided
+// rounds): one workgroup per row. A multipass row with at most 64 partials is merged by wave 0
+// alone (the count is uniform over the workgroup, so no wave reaches the LDS barrier).
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) void merge_rows(LaunchArgs a) {
   const int64_t row = blockIdx.x;
   const RowParts rp = row_parts(a, row);
+  if constexpr (NW > 1) {
+    if (rp.count <= 64) {
+      if (threadIdx.x >= 64) return;
+      MergeAcc<D / 64> r;
+      merge_lanes<D>(a.ws_ml, a.ws_o, rp.first, rp.stride, rp.count, &r);
+      write_row<D>(a, row, r.acc, r.M, r.S);
+      return;
+    }
+  }
   const MergeAcc<D / 64> r = merge_waves<D, NW>(a.ws_ml, a.ws_o, rp.first, rp.stride, rp.count);
   if (threadIdx.x < 64) write_row<D>(a, row, r.acc, r.M, r.S);
 }
@@ -1224,9 +1234,17 @@ static void launch_merge_t(const Plan &p, const LaunchArgs &la, hipStream_t st) 
   switch (p.reducer) {
     case SKVD_REDUCER_DIRECT: merge_direct<D><<<rows, 64, 0, st>>>(la); break;
     case SKVD_REDUCER_COOPERATIVE: merge_rows<D, 1><<<rows, 64, 0, st>>>(la); break;
-    case SKVD_REDUCER_MULTIPASS:
-      merge_rows<D, kMergeWaves><<<rows, 64 * kMergeWaves, 0, st>>>(la);
+    case SKVD_REDUCER_MULTIPASS: {
+      // Balanced: a schedule row (sequence, head group) meets on average at most
+      // shares / rows + 1 partials; while that fits one wave's lanes, one wave per output row
+      // (rounds of 64 cover the outliers) beats four.
+      const int64_t sched_rows = (int64_t)la.batch * (la.Hkv / la.heads_per_wg);
+      if (la.balanced && la.grid_wgs / sched_rows + 1 <= 64)
+        merge_rows<D, 1><<<rows, 64, 0, st>>>(la);
+      else
+        merge_rows<D, kMergeWaves><<<rows, 64 * kMergeWaves, 0, st>>>(la);
       break;
+    }
     case SKVD_REDUCER_HIERARCHICAL:
       merge_hier1<D><<<dim3(rows, p.hier_groups_cap), 64, 0, st>>>(la);
       merge_hier2<D><<<rows, 64 * kMergeWaves, 0, st>>>(la);
