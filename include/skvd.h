@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define SKVD_ABI_VERSION 3
+#define SKVD_ABI_VERSION 4
 
 typedef enum {
   SKVD_OK = 0,
@@ -222,6 +222,16 @@ skvd_status skvd_decode_partial(const skvd_plan *plan, const skvd_decode_args *a
                                 void *workspace, size_t workspace_bytes, void *stream);
 skvd_status skvd_decode_merge(const skvd_plan *plan, const skvd_decode_args *args,
                               void *workspace, size_t workspace_bytes, void *stream);
+
+/* Measurement aid: skvd_decode_partial whose kernel dispatch itself records its begin time in
+ * start_event and its end time in stop_event (hipExtLaunchKernel), so that
+ * hipEventElapsedTime(start_event, stop_event) is the partial kernel's execution alone, with no
+ * marker packets around it. Both are hipEvent_t that the caller created, with timing enabled,
+ * on the plan's device; either may be NULL. With batch 0 nothing is launched and the events are
+ * left untouched. */
+skvd_status skvd_decode_partial_timed(const skvd_plan *plan, const skvd_decode_args *args,
+                                      void *workspace, size_t workspace_bytes, void *stream,
+                                      void *start_event, void *stop_event);
 
 /* Test aid: copy the raw elements of every visible K/V row (position j < kv_len[b]) into
  * dense [B, max_len, Hkv, D] arrays (element size 2 for f16, 1 for int8), and for int8 the

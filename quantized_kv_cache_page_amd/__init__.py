@@ -7,7 +7,8 @@ package is its thin Python face: ``Plan`` marshals torch tensors into those call
 """
 from ._binding import (  # noqa: F401
     LIB_PATH, REDUCERS, SIGNATURES, Plan, SkvdError, last_error, lib, skvd_abi_version_py,
-    skvd_decode, skvd_decode_check, skvd_decode_merge, skvd_decode_partial, skvd_gather_debug,
+    skvd_decode, skvd_decode_check, skvd_decode_merge, skvd_decode_partial,
+    skvd_decode_partial_timed, skvd_gather_debug,
     skvd_plan_create, skvd_plan_describe, skvd_plan_destroy, skvd_plan_get_info,
     skvd_plan_params, skvd_plan_workspace_bytes, skvd_decode_args, status_string,
     skvd_stream_read, stream_read,

@@ -21,7 +21,7 @@ REDUCERS = {"auto": 0, "direct": 1, "cooperative": 2, "multipass": 3, "hierarchi
 REDUCER_NAMES = {v: k for k, v in REDUCERS.items()}
 SCHEDULES = {"auto": 0, "static": 1, "balanced": 2}
 SCHEDULE_NAMES = {v: k for k, v in SCHEDULES.items()}
-ABI_VERSION = 3
+ABI_VERSION = 4
 STATUS_KV_LEN_CLAMPED = 0x1
 STATUS_PAGE_CLAMPED = 0x2
 
@@ -82,6 +82,10 @@ SIGNATURES = {
                                            ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "skvd_decode_merge": (ctypes.c_int, [_PLAN_P, ctypes.POINTER(skvd_decode_args),
                                          ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "skvd_decode_partial_timed": (ctypes.c_int, [_PLAN_P, ctypes.POINTER(skvd_decode_args),
+                                                 ctypes.c_void_p, ctypes.c_size_t,
+                                                 ctypes.c_void_p, ctypes.c_void_p,
+                                                 ctypes.c_void_p]),
     "skvd_gather_debug": (ctypes.c_int, [_PLAN_P, ctypes.POINTER(skvd_decode_args), ctypes.c_int32,
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_void_p, ctypes.c_void_p]),
@@ -175,6 +179,12 @@ def skvd_decode(plan, args, workspace, workspace_bytes, stream) -> int:
 def skvd_decode_partial(plan, args, workspace, workspace_bytes, stream) -> int:
     return int(lib().skvd_decode_partial(plan, ctypes.byref(args), workspace, workspace_bytes,
                                          stream))
+
+
+def skvd_decode_partial_timed(plan, args, workspace, workspace_bytes, stream, start_event,
+                              stop_event) -> int:
+    return int(lib().skvd_decode_partial_timed(plan, ctypes.byref(args), workspace,
+                                               workspace_bytes, stream, start_event, stop_event))
 
 
 def skvd_decode_merge(plan, args, workspace, workspace_bytes, stream) -> int:
@@ -328,15 +338,28 @@ class Plan:
         return s.cuda_stream
 
     def run(self, q, k_pages, v_pages, page_table, kv_len, sm_scale, k_scales=None,
-            v_scales=None, out=None, lse=None, q_per_seq=1, stream=None, stage="all"):
+            v_scales=None, out=None, lse=None, q_per_seq=1, stream=None, stage="all",
+            events=None):
         """Decode. q [B*T, Hq, D] f16 (token and head strides free, D dense); pools
         [pages, P, Hkv, D]; page_table [B, n] int32; kv_len [B] int32 on the device.
         Returns (o [B*T, Hq, D] f16 dense, lse [B*T, Hq] f32). stage: "all", "partial" or
-        "merge" (the two halves of one decode, for timing)."""
+        "merge" (the two halves of one decode, for timing). events: with stage "partial", a
+        (start, stop) pair of already recorded torch.cuda.Event(enable_timing=True) that the
+        partial kernel's dispatch stamps with its own begin and end (skvd_decode_partial_timed)."""
         out, lse = self._outputs(q, out, lse)
         ws = self.ensure_workspace()
         a = self.make_args(q, k_pages, v_pages, page_table, kv_len, sm_scale, k_scales, v_scales,
                            out, lse, q_per_seq)
+        if events is not None:
+            if stage != "partial":
+                raise ValueError("events time the partial stage only")
+            e0, e1 = (ctypes.c_void_p(e.cuda_event) for e in events)
+            if not e0.value or not e1.value:
+                raise ValueError("record each event once before passing it (HIP creates it then)")
+            _check(skvd_decode_partial_timed(self.handle, a, ws.data_ptr(), self.workspace_bytes,
+                                             self._stream(stream), e0, e1),
+                   "skvd_decode_partial_timed")
+            return out, lse
         fn = {"all": skvd_decode, "partial": skvd_decode_partial, "merge": skvd_decode_merge}[stage]
         _check(fn(self.handle, a, ws.data_ptr(), self.workspace_bytes, self._stream(stream)),
                f"skvd_decode[{stage}]")

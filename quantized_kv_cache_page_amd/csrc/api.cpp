@@ -167,6 +167,17 @@ skvd_status skvd_decode_partial(const skvd_plan *plan, const skvd_decode_args *a
   return e ? hip_err(e, "partial kernel launch") : SKVD_OK;
 }
 
+skvd_status skvd_decode_partial_timed(const skvd_plan *plan, const skvd_decode_args *args,
+                                      void *workspace, size_t workspace_bytes, void *stream,
+                                      void *start_event, void *stop_event) {
+  skvd_status st = common_checks(plan, args, workspace, workspace_bytes);
+  if (st != SKVD_OK || args->batch == 0) return st;
+  skvd::LaunchArgs la;
+  skvd::fill_launch_args(plan->p, *args, workspace, &la);
+  int e = skvd::launch_partial(plan->p, la, stream, start_event, stop_event);
+  return e ? hip_err(e, "partial kernel launch") : SKVD_OK;
+}
+
 skvd_status skvd_decode_merge(const skvd_plan *plan, const skvd_decode_args *args,
                               void *workspace, size_t workspace_bytes, void *stream) {
   skvd_status st = common_checks(plan, args, workspace, workspace_bytes);

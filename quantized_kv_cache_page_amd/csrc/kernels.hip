@@ -22,6 +22,7 @@
 // as direct (serial), cooperative (one lane per partial, <= 64), multipass (lane-strided,
 // any count) and hierarchical (64 partials per workgroup, then a multipass over groups).
 // Loop bounds come from kv_len on the device; the partial stride is the plan's capacity.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -1178,40 +1179,61 @@ constexpr int chunk_tokens() {
   return D == 128 ? 32 : 16;
 }
 
+// Events: optional pair that the dispatch itself stamps with the kernel's begin and end.
+struct KernelEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
+template <typename K>
+static void launch_one(K kernel, dim3 grid, unsigned threads, hipStream_t st,
+                       const KernelEvents &ev, const LaunchArgs &la) {
+  if (ev.start || ev.stop)
+    hipExtLaunchKernelGGL(kernel, grid, dim3(threads), 0, st, ev.start, ev.stop, 0, la);
+  else
+    kernel<<<grid, threads, 0, st>>>(la);
+}
+
 template <int D, int RB, bool I8, int HW>
-static void launch_partial_hw(const LaunchArgs &la, dim3 grid, hipStream_t st, bool fast) {
+static void launch_partial_hw(const LaunchArgs &la, dim3 grid, hipStream_t st, bool fast,
+                              const KernelEvents &ev) {
   constexpr int CH = chunk_tokens<D, RB, I8>();
   constexpr bool PVM = pv_on_mfma<D, RB>();
   if (fast)
-    partial_kernel<D, RB, I8, true, CH, PVM, HW><<<grid, 64 * HW, 0, st>>>(la);
+    launch_one(partial_kernel<D, RB, I8, true, CH, PVM, HW>, grid, 64 * HW, st, ev, la);
   else
-    partial_kernel<D, RB, I8, false, CH, PVM, HW><<<grid, 64 * HW, 0, st>>>(la);
+    launch_one(partial_kernel<D, RB, I8, false, CH, PVM, HW>, grid, 64 * HW, st, ev, la);
 }
 
 // KV heads per workgroup (one wave each): the D=128 single-quarter variants read each token's
 // rows of 4 (or 2) KV heads from one CU together (int8: and share the token's scale line);
 // every other variant serves one head.
 template <int D, int RB, bool I8>
-static void launch_partial_t(const LaunchArgs &la, dim3 grid, hipStream_t st, bool fast) {
+static void launch_partial_t(const LaunchArgs &la, dim3 grid, hipStream_t st, bool fast,
+                             const KernelEvents &ev) {
   if constexpr (D == 128 && RB == 1) {
-    if (la.heads_per_wg == 4) return launch_partial_hw<D, RB, I8, 4>(la, grid, st, fast);
-    if (la.heads_per_wg == 2) return launch_partial_hw<D, RB, I8, 2>(la, grid, st, fast);
+    if (la.heads_per_wg == 4) return launch_partial_hw<D, RB, I8, 4>(la, grid, st, fast, ev);
+    if (la.heads_per_wg == 2) return launch_partial_hw<D, RB, I8, 2>(la, grid, st, fast, ev);
   }
-  launch_partial_hw<D, RB, I8, 1>(la, grid, st, fast);
+  launch_partial_hw<D, RB, I8, 1>(la, grid, st, fast, ev);
 }
 
 template <int D, bool I8>
-static void launch_partial_rb(const Plan &p, const LaunchArgs &la, dim3 grid, hipStream_t st) {
+static void launch_partial_rb(const Plan &p, const LaunchArgs &la, dim3 grid, hipStream_t st,
+                              const KernelEvents &ev) {
   const bool fast = p.prm.page_size >= 16;
   switch (p.row_blocks) {
-    case 1: launch_partial_t<D, 1, I8>(la, grid, st, fast); break;
-    case 2: launch_partial_t<D, 2, I8>(la, grid, st, fast); break;
-    default: launch_partial_t<D, 4, I8>(la, grid, st, fast); break;
+    case 1: launch_partial_t<D, 1, I8>(la, grid, st, fast, ev); break;
+    case 2: launch_partial_t<D, 2, I8>(la, grid, st, fast, ev); break;
+    default: launch_partial_t<D, 4, I8>(la, grid, st, fast, ev); break;
   }
 }
 
-int launch_partial(const Plan &p, const LaunchArgs &la, void *stream) {
+int launch_partial(const Plan &p, const LaunchArgs &la, void *stream, void *start_event,
+                   void *stop_event) {
   hipStream_t st = (hipStream_t)stream;
+  KernelEvents ev;
+  ev.start = (hipEvent_t)start_event;
+  ev.stop = (hipEvent_t)stop_event;
   // one-dimensional grid: balanced, the plan's share count bound; static, split fastest over
   // (split, KV head, sequence) (the plan keeps the count below 2^31)
   dim3 grid(la.balanced ? (unsigned)la.grid_wgs
@@ -1219,11 +1241,11 @@ int launch_partial(const Plan &p, const LaunchArgs &la, void *stream) {
                                      la.batch));
   const bool i8 = la.int8;
   if (la.D == 128) {
-    if (i8) launch_partial_rb<128, true>(p, la, grid, st);
-    else launch_partial_rb<128, false>(p, la, grid, st);
+    if (i8) launch_partial_rb<128, true>(p, la, grid, st, ev);
+    else launch_partial_rb<128, false>(p, la, grid, st, ev);
   } else {
-    if (i8) launch_partial_rb<256, true>(p, la, grid, st);
-    else launch_partial_rb<256, false>(p, la, grid, st);
+    if (i8) launch_partial_rb<256, true>(p, la, grid, st, ev);
+    else launch_partial_rb<256, false>(p, la, grid, st, ev);
   }
   return (int)hipGetLastError();
 }

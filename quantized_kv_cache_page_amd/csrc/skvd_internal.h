@@ -74,7 +74,10 @@ const char *reducer_name(int r);
 void fill_launch_args(const Plan &p, const skvd_decode_args &a, void *ws, LaunchArgs *la);
 
 // kernels.hip (return a hipError_t as int; 0 = success)
-int launch_partial(const Plan &p, const LaunchArgs &la, void *stream);
+// start_event/stop_event: NULL, or hipEvent_t that the partial kernel's dispatch stamps with its
+// begin and end (hipExtLaunchKernel).
+int launch_partial(const Plan &p, const LaunchArgs &la, void *stream, void *start_event = nullptr,
+                   void *stop_event = nullptr);
 int launch_merge(const Plan &p, const LaunchArgs &la, void *stream);
 int launch_stream_read(const void *buf, size_t n16, uint32_t *sink, void *stream);
 int launch_gather(const Plan &p, const LaunchArgs &la, int max_len, void *dk, void *dv, void *dks,

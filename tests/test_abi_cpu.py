@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol():
     for s in syms:
         assert hasattr(L, s), s
     assert set(syms) == set(bd.SIGNATURES), set(syms) ^ set(bd.SIGNATURES)
-    assert L.skvd_abi_version() == bd.ABI_VERSION == 3
+    assert L.skvd_abi_version() == bd.ABI_VERSION == 4
 
 
 def plan(**kw):

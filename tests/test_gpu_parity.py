@@ -285,6 +285,38 @@ def test_deterministic():
         assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
 
 
+def test_partial_timed_matches_partial():
+    """skvd_decode_partial_timed writes what skvd_decode_partial writes, and its kernel-stamped
+    events bound a positive duration no longer than a marker pair around the same launch."""
+    s = spec(name="timed", batch=4, q_per_seq=1, num_qo_heads=32, num_kv_heads=8, head_dim=128,
+             page_size=16, lens=("list", (100, 3000, 5000, 9000)))
+    prob = workloads.generate(s, 13)
+    dev = to_dev(prob)
+    plan = make_plan(prob)
+    o1, l1 = run(plan, prob, dev, stage="partial")
+    run(plan, prob, dev, out=o1, lse=l1, stage="merge")
+    o1, l1 = o1.clone(), l1.clone()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    e1.record()
+    torch.cuda.synchronize()
+    for _ in range(2):
+        m0.record()
+        o2, l2 = plan.run(dev["q"], dev["k_pages"], dev["v_pages"], dev["page_table"],
+                          dev["kv_len"], prob["sm_scale"], stage="partial", events=(e0, e1))
+        m1.record()
+        run(plan, prob, dev, out=o2, lse=l2, stage="merge")
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+        t_kernel, t_marker = e0.elapsed_time(e1), m0.elapsed_time(m1)
+        say(f"  kernel-stamped {t_kernel * 1e3:.1f} us, marker pair {t_marker * 1e3:.1f} us")
+        assert 0 < t_kernel <= t_marker * 1.05 + 1e-3
+    with pytest.raises(ValueError):
+        plan.run(dev["q"], dev["k_pages"], dev["v_pages"], dev["page_table"], dev["kv_len"],
+                 prob["sm_scale"], stage="all", events=(e0, e1))
+
+
 def test_debug_status_clamps():
     """kv_len above max_kv_len and out-of-range page ids are clamped, flagged, never faulted."""
     import quantized_kv_cache_page_amd as skvd
