@@ -298,7 +298,9 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
   __shared__ __attribute__((aligned(16))) float p_lds_all[HW * PL];
   __shared__ __attribute__((aligned(16))) uint2v vsc_lds_all[HW * SL];
   __shared__ __attribute__((aligned(16))) unsigned p2_lds_all[HW * QL];
-  const int wave = HW > 1 ? (int)(threadIdx.x >> 6) : 0;
+  // (readfirstlane: the wave index is uniform in the wave, and saying so keeps the KV head and
+  // every row base derived from it in SGPRs, so loads take a scalar base + 32-bit lane offset)
+  const int wave = HW > 1 ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) : 0;
   char *const v_lds = v_lds_all + wave * VL;
   float *const p_lds = p_lds_all + wave * PL;
   uint2v *const vsc_lds = vsc_lds_all + wave * SL;
@@ -325,12 +327,23 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
   int st_b = 0, st_grp = 0, st_split = 0;
   Shares sh{};
   int64_t x_cur = 0, x_end = 0;  // balanced: this workgroup's share
+  // Progress priority (int8, whose waves share SIMDs): waves of a SIMD are served oldest
+  // first, so a co-resident workgroup started later falls behind and finishes alone, with fewer
+  // loads in flight. Each wave instead sets its issue priority from the fraction of its work
+  // done (3 in the first quarter down to 0 in the last), so the waves of a SIMD advance
+  // together. Blocks done so far: done_base (earlier segments) + the segment's own; quarters
+  // at pq1, pq2, pq3.
+  int done_base = 0, pq1 = 0, pq2 = 0, pq3 = 0;
   const int share = blockIdx.x;
   if (a.balanced) {
     sh = balanced_shares(a, a.debug);
     if (share >= sh.n_shares) return;
     x_cur = share * sh.n_blocks / sh.n_shares;
     x_end = (share + 1) * sh.n_blocks / sh.n_shares;
+    const int total = (int)(x_end - x_cur);
+    pq1 = total / 4;
+    pq2 = total / 2;
+    pq3 = 3 * total / 4;
   } else {
     const int wg = blockIdx.x;
     st_split = wg % a.split_stride;
@@ -372,6 +385,10 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
     blk_lo = st_split * a.bps;
     if (!a.single && blk_lo >= nblk) break;  // beyond this sequence: no partial is read
     blk_hi = min(blk_lo + a.bps, nblk);
+    const int total = blk_hi - blk_lo;
+    pq1 = total / 4;
+    pq2 = total / 2;
+    pq3 = 3 * total / 4;
   }
   const int kvh = HW * grp + wave;
   const int tok0 = blk_lo * 64;
@@ -452,6 +469,12 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
     return bad ? (pg < 0 ? 0 : npages - 1) : (int64_t)pg;
   };
 
+  // Per-lane token offsets within a 16-token tile, hoisted: with a non-negative stride,
+  // min(token, limit) * stride = min(token * stride, limit * stride), the limit being scalar.
+  const unsigned c16_tok = (unsigned)(c16 * (int)a.tok_stride);
+  const unsigned c16_stok = I8 ? (unsigned)(c16 * (int)a.s_tok_stride) : 0u;
+  const unsigned vt_tok = (unsigned)(vlane_tok * (int)a.tok_stride);
+
   Vec kb[NT][I8 ? 1 : KS];                   // f16 K: step k's 8 elements
   uint4v kq[NT][I8 ? KS / 4 : 1][2];         // int8 K: the lane's 32 bytes of group g4 + 4m
   _Float16 ksh[NT][I8 ? KS / 4 : 1];         // int8 K: the token's scale of group g4 + 4m
@@ -472,9 +495,9 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
         const int64_t pg = clamp_page(pgs[t], a.num_k_pages);
         const char *base = kbase + row_offset(pg, jte & P1, kvh, a.page_stride, a.tok_stride,
                                               a.head_stride) * ES;
-        const int tk = min(c16, tok_end - 1 - jte);
+        const int lim = min(tok_end - 1 - jte, 15);  // last valid token of the tile
         if constexpr (I8) {
-          const unsigned off = (unsigned)(tk * (int)a.tok_stride + 32 * g4);
+          const unsigned off = min(c16_tok, (unsigned)(lim * (int)a.tok_stride)) + 32 * g4;
 #pragma unroll
           for (int m = 0; m < KS / 4; ++m)
 #pragma unroll
@@ -482,11 +505,12 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
               kq[t][m][h] = kv_load<true, uint4v>(base + off + 128 * m + 16 * h);
           const _Float16 *sb = ksc + row_offset(pg, jte & P1, kvh, a.s_page_stride,
                                                 a.s_tok_stride, a.s_head_stride);
-          const unsigned so = (unsigned)(tk * (int)a.s_tok_stride) + g4;
+          const unsigned so = 2u * (min(c16_stok, (unsigned)(lim * (int)a.s_tok_stride)) + g4);
 #pragma unroll
-          for (int m = 0; m < KS / 4; ++m) ksh[t][m] = sb[so + 4 * m];
+          for (int m = 0; m < KS / 4; ++m)
+            ksh[t][m] = *(const _Float16 *)((const char *)sb + so + 8 * m);
         } else {
-          const unsigned off = (unsigned)((tk * (int)a.tok_stride + 8 * g4) * ES);
+          const unsigned off = (min(c16_tok, (unsigned)(lim * (int)a.tok_stride)) + 8 * g4) * ES;
 #pragma unroll
           for (int k = 0; k < KS; ++k) kb[t][k] = kv_load<true, Vec>(base + off + 32 * k * ES);
         }
@@ -527,8 +551,11 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
         const int64_t pg = clamp_page(pgs[(TPS * s2) >> 4], a.num_v_pages);
         const char *base = vbase + row_offset(pg, jte & P1, kvh, a.page_stride, a.tok_stride,
                                               a.head_stride) * ES;
-        const int tk = min((js & 15) + vlane_tok, tok_end - 1 - jte);
-        const unsigned off = (unsigned)((tk * (int)a.tok_stride + vlane_el) * ES);
+        // token (js & 15) + vlane_tok of the tile, clamped to its last valid token
+        const int ts = (int)a.tok_stride;
+        const unsigned tko = min(vt_tok + (unsigned)((js & 15) * ts),
+                                 (unsigned)(min(tok_end - 1 - jte, 15) * ts));
+        const unsigned off = (tko + vlane_el) * ES;
         vb[s2] = kv_load<true, Vec>(base + off);
       } else {
         const int j = min(js + vlane_tok, tok_end - 1);
@@ -788,10 +815,23 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
     for (int t = 0; t < NT; ++t) pg_cur[t] = pg_next[t];
     wave_sync();
   };
+  auto set_priority = [&](int c0) __attribute__((always_inline)) {
+    if constexpr (!I8) return;  // f16 runs one wave per SIMD: nothing to arbitrate
+    const int done = done_base + ((c0 - tok0) >> 6);
+    if (done < pq1) __builtin_amdgcn_s_setprio(3);
+    else if (done < pq2) __builtin_amdgcn_s_setprio(2);
+    else if (done < pq3) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+  };
   if (tok0 < tok_end) {
+    set_priority(tok0);
     chunk(tok0);
-    for (int c0 = tok0 + CH; c0 < tok_end; c0 += CH) chunk(c0);
+    for (int c0 = tok0 + CH; c0 < tok_end; c0 += CH) {
+      set_priority(c0);
+      chunk(c0);
+    }
   }
+  done_base += blk_hi - blk_lo;
   if (a.debug && clamped_any) atomicOr(a.status, (unsigned)SKVD_STATUS_PAGE_CLAMPED);
 
   // ---- per-row sum over the tokens of the lane's DPP row; max is already row-uniform
@@ -1211,6 +1251,7 @@ template <int D, int RB, bool I8>
 static void launch_partial_t(const LaunchArgs &la, dim3 grid, hipStream_t st, bool fast,
                              const KernelEvents &ev) {
   if constexpr (D == 128 && RB == 1) {
+    if (la.heads_per_wg == 8) return launch_partial_hw<D, RB, I8, 8>(la, grid, st, fast, ev);
     if (la.heads_per_wg == 4) return launch_partial_hw<D, RB, I8, 4>(la, grid, st, fast, ev);
     if (la.heads_per_wg == 2) return launch_partial_hw<D, RB, I8, 2>(la, grid, st, fast, ev);
   }

@@ -79,12 +79,18 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
     return fail(err, errn, SKVD_ERR_PLAN, "schedule=%d unknown", prm.schedule);
   if (prm.wgs_per_cu < 0 || prm.wgs_per_cu > 64)
     return fail(err, errn, SKVD_ERR_PLAN, "wgs_per_cu=%d outside 0..64", prm.wgs_per_cu);
-  // KV heads per workgroup: the single-quarter variants at D=128 come in 1, 2 and 4.
+  // KV heads per workgroup: the single-quarter variants at D=128 come in 1, 2, 4 and 8.
   const bool multi_head_ok = D == 128 && G * prm.max_q_per_seq <= 4;
+  const bool i8_kv = prm.kv_dtype == SKVD_KV_I8_F16SCALE32;
   int hw = prm.heads_per_wg;
-  if (hw == 0) hw = !multi_head_ok ? 1 : (Hkv % 4 == 0 ? 4 : (Hkv % 2 == 0 ? 2 : 1));
-  if (hw != 1 && (!multi_head_ok || (hw != 2 && hw != 4) || Hkv % hw != 0))
-    return fail(err, errn, SKVD_ERR_PLAN, "heads_per_wg=%d: only 1, or 2 / 4 dividing Hkv=%d "
+  if (hw == 0)
+    hw = !multi_head_ok ? 1
+         : (i8_kv && Hkv % 8 == 0) ? 8
+         : Hkv % 4 == 0 ? 4
+         : Hkv % 2 == 0 ? 2
+         : 1;
+  if (hw != 1 && (!multi_head_ok || (hw != 2 && hw != 4 && hw != 8) || Hkv % hw != 0))
+    return fail(err, errn, SKVD_ERR_PLAN, "heads_per_wg=%d: only 1, or 2 / 4 / 8 dividing Hkv=%d "
                 "at head_dim 128 with G*T <= 4", prm.heads_per_wg, Hkv);
 
   Plan p{};
@@ -148,11 +154,14 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
   if (sched == SKVD_SCHEDULE_BALANCED) {
     // Workgroups per CU (measured on MI355X): one wave per SIMD saturates the memory pipes of
     // an f16 stream, best as one workgroup of 4 KV heads reading each token row's heads
-    // together; int8 at D=128 also needs vector-ALU throughput, so two waves per SIMD; D=256
-    // workgroups are the largest (3 per CU measured best).
+    // together; int8 at D=128 also needs vector-ALU throughput, so two waves per SIMD: one
+    // workgroup of 8 KV heads at a time, two per CU in two rounds (the registers hold one), so
+    // that the dispatcher hands each CU its second share when it frees up; D=256 workgroups
+    // are the largest (3 per CU measured best).
     const bool i8 = prm.kv_dtype == SKVD_KV_I8_F16SCALE32;
     const int auto_wpc = D == 256 ? 3
-                         : p.row_blocks == 1 ? (i8 ? 8 : kDefaultWgsPerCu) / hw
+                         : p.row_blocks == 1 ? (i8 ? (hw == 8 ? 2 : 8 / hw)
+                                                   : std::max(1, kDefaultWgsPerCu / hw))
                                              : kDefaultWgsPerCu;
     p.grid_wgs = (prm.wgs_per_cu ? prm.wgs_per_cu : auto_wpc) * num_cus;
     // a forced split size becomes the balanced shares' minimum

@@ -94,12 +94,16 @@ def test_schedule_choice():
     w = plan(wgs_per_cu=7, num_cus=100)
     assert w.schedule == "balanced" and w.info.grid_wgs == 700 and w.info.heads_per_wg == 4
     assert "schedule=balanced" in w.describe()
-    # defaults per variant: 4 per CU, 3 at head_dim 256, 8 waves per CU for int8 single-quarter
-    # tiles, whose workgroups serve 4 (else 2) KV heads
+    # defaults per variant: 4 per CU, 3 at head_dim 256; int8 single-quarter tiles: workgroups
+    # of 8 KV heads, two per CU (else 4 or 2 heads, 8 waves per CU)
     assert plan(head_dim=256, num_kv_heads=16).info.grid_wgs == 3 * 256
     i8 = plan(kv_dtype="i8")
-    assert i8.info.heads_per_wg == 4 and i8.info.grid_wgs == 2 * 256
+    assert i8.info.heads_per_wg == 8 and i8.info.grid_wgs == 2 * 256
+    i8_4 = plan(kv_dtype="i8", num_kv_heads=4, num_qo_heads=16)
+    assert i8_4.info.heads_per_wg == 4 and i8_4.info.grid_wgs == 2 * 256
+    assert plan(kv_dtype="i8", heads_per_wg=4).info.grid_wgs == 2 * 256
     assert plan(kv_dtype="i8", num_kv_heads=2, num_qo_heads=8).info.heads_per_wg == 2
+    assert plan(heads_per_wg=8).info.grid_wgs == 256
     assert plan(kv_dtype="i8", num_kv_heads=3, num_qo_heads=12).info.heads_per_wg == 1
     assert plan(kv_dtype="i8", heads_per_wg=1).info.grid_wgs == 8 * 256
     assert plan(kv_dtype="i8", max_q_per_seq=2).info.grid_wgs == 4 * 256
@@ -108,7 +112,7 @@ def test_schedule_choice():
     assert plan(heads_per_wg=1).info.grid_wgs == 4 * 256
     assert plan(num_kv_heads=2, num_qo_heads=8).info.grid_wgs == 2 * 256
     st = plan(kv_dtype="i8", schedule="static")
-    assert st.info.grid_wgs == (st.info.splits_cap | 1) * 2 * 32
+    assert st.info.grid_wgs == (st.info.splits_cap | 1) * (8 // st.info.heads_per_wg) * 32
 
 
 @pytest.mark.parametrize("red", ["direct", "multipass", "hierarchical"])
@@ -143,7 +147,7 @@ def test_heuristic_configs():
     (dict(schedule="balanced", force_reducer="none", max_kv_len=200), 7),
     (dict(schedule=3), 7), (dict(wgs_per_cu=65), 7), (dict(wgs_per_cu=-1), 7),
     (dict(heads_per_wg=2, max_q_per_seq=2), 7), (dict(kv_dtype="i8", heads_per_wg=3), 7),
-    (dict(kv_dtype="i8", heads_per_wg=8), 7), (dict(kv_dtype="i8", heads_per_wg=4, num_kv_heads=2,
+    (dict(kv_dtype="i8", heads_per_wg=8, num_kv_heads=4, num_qo_heads=16), 7), (dict(kv_dtype="i8", heads_per_wg=4, num_kv_heads=2,
                                                    num_qo_heads=8), 7),
     (dict(kv_dtype="i8", heads_per_wg=2, head_dim=256), 7),
 ])

@@ -102,11 +102,11 @@ def test_balanced_schedule_edges(case):
 
 
 @pytest.mark.parametrize("kv", ["i8", "f16"])
-@pytest.mark.parametrize("hw", [1, 2, 4])
+@pytest.mark.parametrize("hw", [1, 2, 4, 8])
 @pytest.mark.parametrize("schedule", ["balanced", "static"])
 @pytest.mark.parametrize("P", [16, 1])
 def test_heads_per_workgroup(kv, hw, schedule, P):
-    """Workgroups serving 1, 2 or 4 KV heads (one wave each) over the same blocks."""
+    """Workgroups serving 1, 2, 4 or 8 KV heads (one wave each) over the same blocks."""
     s = spec(name="hw", batch=5, q_per_seq=1, num_qo_heads=32, num_kv_heads=8, head_dim=128,
              page_size=P, kv_dtype=kv, lens=("list", (1, 700, 64, 2100, 333)))
     _, _, plan, _, _ = check(s, seed=hw * 10 + P, plan_kw=dict(heads_per_wg=hw, schedule=schedule,
