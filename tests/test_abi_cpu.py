@@ -125,9 +125,15 @@ def test_forced_reducers_cover_any_count(red):
 
 
 def test_heuristic_configs():
-    """The workloads' plans: one split for 256 tokens; no 2048/32-block ceiling anywhere."""
+    """The workloads' plans: one split up to 128 tokens; small decodes spread one KV head per
+    workgroup; no 2048/32-block ceiling anywhere."""
+    assert plan(num_qo_heads=8, num_kv_heads=8, max_batch=1, max_kv_len=128).reducer == "none"
     c1 = plan(num_qo_heads=8, num_kv_heads=8, max_batch=1, max_kv_len=256)
-    assert c1.reducer == "none"
+    assert c1.reducer in ("direct", "cooperative") and c1.schedule == "balanced"
+    assert c1.info.heads_per_wg == 1 and c1.info.blocks_per_split == 2
+    # (sequence, KV head, block) units <= CUs: one head per workgroup; beyond, four
+    assert plan(max_batch=1, max_kv_len=1024).info.heads_per_wg == 1
+    assert plan(max_batch=1, max_kv_len=8192).info.heads_per_wg == 4
     c3 = plan(max_batch=1, page_size=64, max_kv_len=131072)
     assert c3.info.splits_cap > 64 and c3.reducer in ("multipass", "hierarchical")
     for p in (plan(), c3, plan(num_kv_heads=16, head_dim=256, max_batch=8, max_q_per_seq=4,
