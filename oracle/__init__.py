@@ -1,13 +1,15 @@
-"""fp64 CPU oracle for paged decode attention (test infrastructure).
+"""fp64 CPU oracle for paged decode attention, and for appending to the paged cache (test
+infrastructure).
 
 Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may
 import this package. The HIP library never calls it and shares no code with it. The
 arithmetic lives in ``oracle.c`` (plain C, fp64, OpenMP over rows); this module only builds
 that file with gcc and marshals numpy arrays into it.
 
-Every function takes the problem as the dict that ``workloads.generate`` returns (numpy
+The decode functions take the problem as the dict that ``workloads.generate`` returns (numpy
 arrays: q, k_pages, v_pages, k_scales, v_scales, page_table, kv_len; ints: q_per_seq; float:
-sm_scale). Strides are read from the arrays themselves, in elements.
+sm_scale). ``append`` takes new K/V rows and their (sequence, position) pairs and returns
+written copies of the pools. Strides are read from the arrays themselves, in elements.
 """
 from __future__ import annotations
 
@@ -37,6 +39,24 @@ class OracleProblem(ctypes.Structure):
         ("s_page_stride", ctypes.c_int64), ("s_tok_stride", ctypes.c_int64), ("s_head_stride", ctypes.c_int64),
         ("table", ctypes.c_void_p), ("table_stride", ctypes.c_int64),
         ("kv_len", ctypes.c_void_p),
+    ]
+
+
+class OracleAppendProblem(ctypes.Structure):
+    _fields_ = [
+        ("num_tokens", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
+        ("kv_int8", ctypes.c_int32), ("batch", ctypes.c_int32),
+        ("max_len", ctypes.c_int32), ("pad0", ctypes.c_int32),
+        ("k_new", ctypes.c_void_p), ("v_new", ctypes.c_void_p),
+        ("new_tok_stride", ctypes.c_int64), ("new_head_stride", ctypes.c_int64),
+        ("batch_idx", ctypes.c_void_p), ("positions", ctypes.c_void_p),
+        ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+        ("page_stride", ctypes.c_int64), ("tok_stride", ctypes.c_int64), ("head_stride", ctypes.c_int64),
+        ("num_k_pages", ctypes.c_int64), ("num_v_pages", ctypes.c_int64),
+        ("s_page_stride", ctypes.c_int64), ("s_tok_stride", ctypes.c_int64), ("s_head_stride", ctypes.c_int64),
+        ("table", ctypes.c_void_p), ("table_stride", ctypes.c_int64),
     ]
 
 
@@ -72,6 +92,13 @@ def load(path: str | None = None):
     lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
     lib.oracle_half_to_double.restype = ctypes.c_double
     lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_append.argtypes = [ctypes.POINTER(OracleAppendProblem)]
+    lib.oracle_append.restype = ctypes.c_int64
+    lib.oracle_float_to_half.argtypes = [ctypes.c_float]
+    lib.oracle_float_to_half.restype = ctypes.c_uint16
+    lib.oracle_quantize_group.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                          ctypes.c_void_p]
+    lib.oracle_quantize_group.restype = None
     if path is None:
         _lib = lib
     return lib
@@ -174,3 +201,57 @@ def gather(prob: dict, max_len: int, lib=None):
 
 def num_threads() -> int:
     return int(load().oracle_num_threads())
+
+
+def append(k_new, v_new, batch_idx, positions, page_table, max_len, k_pages, v_pages,
+           k_scales=None, v_scales=None, batch=None, lib=None):
+    """Write new K/V rows into copies of the pools. k_new, v_new: f16 [N, Hkv, D] (same
+    strides); batch_idx, positions: int [N]; page_table [B, stride] int32; pools as in the
+    decode problem (int8 pools take f16 scale pools). Returns (k, v, ks, vs, skipped): the
+    written copies (ks, vs None for f16) and the number of tokens skipped."""
+    lib = lib or load()
+    kn, vn = k_new, v_new
+    assert kn.dtype == np.float16 and kn.shape == vn.shape and kn.strides == vn.strides
+    assert kn.ndim == 3 and kn.strides[2] == 2
+    int8 = k_pages.dtype == np.int8
+    k, v = k_pages.copy(), v_pages.copy()
+    bi = np.ascontiguousarray(batch_idx, dtype=np.int32)
+    ps = np.ascontiguousarray(positions, dtype=np.int32)
+    table = np.ascontiguousarray(page_table, dtype=np.int32)
+    es = k.itemsize
+    s = OracleAppendProblem()
+    s.num_tokens, s.num_kv_heads, s.head_dim = kn.shape[0], k.shape[2], k.shape[3]
+    s.page_size, s.kv_int8 = k.shape[1], int(int8)
+    s.batch = table.shape[0] if batch is None else int(batch)
+    s.max_len = int(max_len)
+    s.k_new, s.v_new = kn.ctypes.data, vn.ctypes.data
+    s.new_tok_stride, s.new_head_stride = kn.strides[0] // 2, kn.strides[1] // 2
+    s.batch_idx, s.positions = bi.ctypes.data, ps.ctypes.data
+    s.k, s.v = k.ctypes.data, v.ctypes.data
+    s.page_stride, s.tok_stride, s.head_stride = (k.strides[0] // es, k.strides[1] // es,
+                                                  k.strides[2] // es)
+    s.num_k_pages, s.num_v_pages = k.shape[0], v.shape[0]
+    ks = vs = None
+    if int8:
+        ks, vs = k_scales.copy(), v_scales.copy()
+        s.k_scale, s.v_scale = ks.ctypes.data, vs.ctypes.data
+        s.s_page_stride, s.s_tok_stride, s.s_head_stride = (ks.strides[0] // 2, ks.strides[1] // 2,
+                                                            ks.strides[2] // 2)
+    s.table, s.table_stride = table.ctypes.data, table.shape[1]
+    skipped = lib.oracle_append(ctypes.byref(s))
+    return k, v, ks, vs, int(skipped)
+
+
+def float_to_half_bits(x: float, lib=None) -> int:
+    """f32 -> f16 bits, nearest even (the oracle's own conversion)."""
+    return int((lib or load()).oracle_float_to_half(float(np.float32(x))))
+
+
+def quantize_group(x, lib=None):
+    """One group of f16 elements -> (int8 codes, f16 scale) by the oracle's int8 append rule."""
+    lib = lib or load()
+    xb = np.ascontiguousarray(x, dtype=np.float16)
+    codes = np.empty(xb.shape[0], np.int8)
+    sb = np.empty(1, np.uint16)
+    lib.oracle_quantize_group(xb.ctypes.data, xb.shape[0], codes.ctypes.data, sb.ctypes.data)
+    return codes, sb.view(np.float16)[0]

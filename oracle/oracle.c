@@ -329,3 +329,142 @@ int oracle_num_threads(void) {
   return 1;
 #endif
 }
+
+/* ============================================================================ append
+ * Writing new tokens into the paged cache: the step before a decode, and the one operation
+ * that writes the cache (AMD-Ecosystem/flashinfer PR #397, section "What changed": append
+ * genuinely writes the cache and keeps declaring it written, unlike the read-only decode).
+ * The pages give no further definition, so this is the plainest reading, stated in the
+ * library's own terms:
+ *
+ *   W1 place   New token i belongs to sequence b = batch_idx[i] at logical position
+ *              j = positions[i]. Its K row of KV head g goes to slot j % P of page
+ *              table[b][j / P], at page*page_stride + slot*tok_stride + g*head_stride
+ *              (elements) - the address O1 reads - and its V row to the same place in V.
+ *              A token whose b is outside [0, batch) or j outside [0, max_len) is skipped;
+ *              a page id outside a pool skips that pool's write. Nothing else is written.
+ *   W2 f16     An f16 cache receives the f16 elements verbatim.
+ *   W3 int8    An int8 cache (value = int8 * scale, one f16 scale per 32 contiguous head_dim
+ *              elements: the q8_0-style KV type that the pages name, 1bit-MONSTER/engine issue
+ *              #115 "Fixed" and llama-cpp-turboquant PR #176 "Results") quantizes each group
+ *              of 32 on write, symmetric, with the largest magnitude mapped to 127:
+ *                a = max |x| over the group (exact),
+ *                s = f16(a / 127): the quotient in f32, rounded once to f16 (nearest even),
+ *                c = clip(rint(x / s), -127, 127), x / s in f32, rint to nearest even;
+ *                s = 0 (an all-zero group, or a below f16's range) gives c = 0.
+ *              The pages fix no precision for these decisions; f32 is the kernel's.
+ * ============================================================================ */
+
+typedef struct {
+  int32_t num_tokens;   /* N */
+  int32_t num_kv_heads; /* Hkv */
+  int32_t head_dim;     /* D */
+  int32_t page_size;    /* P */
+  int32_t kv_int8;      /* 0: f16 cache; 1: int8 cache with f16 scales per 32 elements */
+  int32_t batch;        /* rows of the page table */
+  int32_t max_len;      /* positions are < max_len */
+  int32_t pad0;
+  const uint16_t *k_new, *v_new; /* f16 bits [N, Hkv, D] */
+  int64_t new_tok_stride, new_head_stride;
+  const int32_t *batch_idx, *positions;
+  void *k, *v;                   /* written: f16 bits or int8 */
+  uint16_t *k_scale, *v_scale;   /* written: f16 bits (int8 cache only) */
+  int64_t page_stride, tok_stride, head_stride;
+  int64_t num_k_pages, num_v_pages;
+  int64_t s_page_stride, s_tok_stride, s_head_stride;
+  const int32_t *table;
+  int64_t table_stride;
+} oracle_append_problem;
+
+/* IEEE-754 binary32 -> binary16, rounded to nearest, ties to even (the default IEEE rounding).
+ * Written from the format's definition: the result is the f16 value nearest to x, so scale x
+ * to the integer significand grid of its binade and round that once. */
+uint16_t oracle_float_to_half(float x) {
+  uint16_t sign = signbit(x) ? 0x8000 : 0;
+  double a = fabs((double)x);
+  if (isnan(x)) return (uint16_t)(sign | 0x7e00);
+  if (a == 0.0) return sign;
+  int e2;
+  frexp(a, &e2);          /* a = f * 2^e2, f in [0.5, 1): the binade is [2^(e2-1), 2^e2) */
+  int e = e2 - 1;         /* unbiased exponent of a */
+  if (e < -14) e = -14;   /* subnormal range: the grid step stays 2^-24 */
+  double q = rint(ldexp(a, 10 - e)); /* significand with 10 fraction bits, nearest even */
+  if (q >= 2048.0) { q /= 2.0; e += 1; } /* rounded up into the next binade (exact) */
+  if (e > 15) return (uint16_t)(sign | 0x7c00); /* overflow: infinity */
+  if (q < 1024.0) return (uint16_t)(sign | (uint16_t)q); /* subnormal (exponent field 0) */
+  return (uint16_t)(sign | (uint16_t)((e + 15) << 10) | (uint16_t)(q - 1024.0));
+}
+
+/* W3 for one group of n (= 32) f16 elements. */
+void oracle_quantize_group(const uint16_t *x, int n, int8_t *codes, uint16_t *scale_bits) {
+  float a = 0.0f;
+  for (int d = 0; d < n; ++d) {
+    float v = fabsf((float)oracle_half_to_double(x[d]));
+    if (v > a) a = v;
+  }
+#if ORACLE_MUTANT == 11
+  float sq = a / 128.0f; /* planted: wrong divisor */
+#else
+  float sq = a / 127.0f;
+#endif
+  uint16_t sb = oracle_float_to_half(sq);
+  float s = (float)oracle_half_to_double(sb);
+  *scale_bits = sb;
+  for (int d = 0; d < n; ++d) {
+    float v = (float)oracle_half_to_double(x[d]);
+    float c = 0.0f;
+    if (s > 0.0f) {
+#if ORACLE_MUTANT == 12
+      c = truncf(v / s); /* planted: truncation instead of rounding */
+#else
+      c = rintf(v / s);
+#endif
+      if (c > 127.0f) c = 127.0f;
+      if (c < -127.0f) c = -127.0f;
+    }
+    codes[d] = (int8_t)c;
+  }
+}
+
+/* W1-W3 for one row of one pool. */
+static void append_row(const oracle_append_problem *p, const uint16_t *src, void *pool,
+                       uint16_t *scales, int64_t page, int64_t slot, int g) {
+  int D = p->head_dim;
+  int64_t off = page * p->page_stride + slot * p->tok_stride + (int64_t)g * p->head_stride;
+  if (!p->kv_int8) {
+    memcpy((uint16_t *)pool + off, src, sizeof(uint16_t) * (size_t)D);
+    return;
+  }
+  int64_t soff = page * p->s_page_stride + slot * p->s_tok_stride + (int64_t)g * p->s_head_stride;
+  for (int grp = 0; grp < D / 32; ++grp) {
+    int sg = grp;
+#if ORACLE_MUTANT == 13
+    sg = (grp + 1) % (D / 32); /* planted: scale stored in the wrong group's slot */
+#endif
+    oracle_quantize_group(src + grp * 32, 32, (int8_t *)pool + off + grp * 32, scales + soff + sg);
+  }
+}
+
+/* Append every new token (W1-W3), in token order. Returns the number of tokens skipped. */
+int64_t oracle_append(const oracle_append_problem *p) {
+  int64_t skipped = 0;
+  int P = p->page_size;
+  for (int64_t i = 0; i < p->num_tokens; ++i) {
+    int b = p->batch_idx[i];
+    int64_t j = p->positions[i];
+    if (b < 0 || b >= p->batch || j < 0 || j >= p->max_len) { ++skipped; continue; }
+    int64_t page = p->table[(int64_t)b * p->table_stride + j / P];
+    int64_t slot = j % P;
+    for (int g = 0; g < p->num_kv_heads; ++g) {
+      int gg = g;
+#if ORACLE_MUTANT == 14
+      gg = (g + 1) % p->num_kv_heads; /* planted: row written under the next KV head */
+#endif
+      const uint16_t *kr = p->k_new + i * p->new_tok_stride + (int64_t)g * p->new_head_stride;
+      const uint16_t *vr = p->v_new + i * p->new_tok_stride + (int64_t)g * p->new_head_stride;
+      if (page >= 0 && page < p->num_k_pages) append_row(p, kr, p->k, p->k_scale, page, slot, gg);
+      if (page >= 0 && page < p->num_v_pages) append_row(p, vr, p->v, p->v_scale, page, slot, gg);
+    }
+  }
+  return skipped;
+}
