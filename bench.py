@@ -2,6 +2,7 @@
 """Benchmark: split-KV paged decode on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--config 2] [--gpus 1] [--no-cpu]
+    python bench.py --op append [--append prefill_i8|prefill_f16|decode_i8]
 
 A step is one decode call (partial kernel + reducer) over one batch of the workload, with
 all inputs resident in HBM. The default workload is the GQA batch decode (B=32, 32 query /
@@ -11,7 +12,9 @@ of the pools and tables rotate that the working set exceeds twice the 256 MB Inf
 Prints one JSON line: value = K+V bytes read per call / time per call (GB/s), plus
 roofline (the partial kernel's algorithmic K+V bytes per launch over its average launch time,
 timed with HIP events on the launching stream, against 8 TB/s) and cpu_baseline (the fp64
-oracle on the host cores over a bounded sample of the same workload).
+oracle on the host cores over a bounded sample of the same workload). The default line also
+carries an "append" object: the int8 prefill-chunk append (32 sequences x 1024 new tokens
+quantized into the int8 cache) timed the same way. `--op append` prints the append's own line.
 """
 from __future__ import annotations
 
@@ -166,9 +169,122 @@ def sweep(args):
                           "plan": plan}), flush=True)
 
 
+APPEND_METRIC = "append µs/call and achieved HBM GB/s (new K/V rows read + cache written) vs roofline"
+
+
+def time_append(name, seed, steps, warmup):
+    """Time skvd_append on one append workload: pools and new rows resident in HBM, copies
+    rotated past the Infinity Cache. Returns a dict of measurements and the problem."""
+    import numpy as np
+    import torch
+    import quantized_kv_cache_page_amd as skvd
+    import workloads
+    spec, n = workloads.APPEND_CONFIGS[name]
+    prob = workloads.generate(spec, seed)
+    new = workloads.append_tokens(prob, seed, n)
+    nbytes = workloads.append_bytes(prob, new)
+    dev = torch.device("cuda:0")
+
+    def up(x):
+        return None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    table = up(prob["page_table"])
+    base = [up(new[k]) for k in ("k_new", "v_new")] + \
+        [up(prob[k]) for k in ("k_pages", "v_pages", "k_scales", "v_scales")]
+    copies = max(1, math.ceil(2 * MALL_BYTES / max(nbytes, 1)) + 1)
+    sets = [base] + [[None if t is None else t.clone() for t in base] for _ in range(copies - 1)]
+    bi, pos = up(new["batch_idx"]), up(new["positions"])
+    plan = skvd.Plan(spec.num_qo_heads, spec.num_kv_heads, spec.head_dim, spec.page_size,
+                     spec.kv_dtype, spec.batch, spec.q_per_seq, spec.max_kv_len, device=0)
+
+    def call(i):
+        kn, vn, k, v, ks, vs = sets[i % copies]
+        plan.append(kn, vn, bi, pos, k, v, table, ks, vs)
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    # per-launch event pairs on the launching stream (torch's current stream) ...
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        call(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    k_us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    # ... and back-to-back calls for us/call
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        call(i)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / steps * 1e3
+    workload = (f"{spec.name}: {new['k_new'].shape[0]} new tokens ({n} per sequence x "
+                f"{spec.batch}) Hkv={spec.num_kv_heads} D={spec.head_dim} P={spec.page_size} "
+                f"kv={spec.kv_dtype}, random order, permuted pages")
+    return dict(workload=workload, us_per_call=us, kernel_avg_us=k_us, bytes=nbytes,
+                gbs=nbytes / (us * 1e-6) / 1e9, achieved=nbytes / (k_us * 1e-6) / 1e9,
+                copies=copies, seed=seed), prob, new
+
+
+def cpu_baseline_append(prob, new, max_len, budget_s=8.0):
+    """The oracle's append on all host cores (it runs on one), whole workloads, repeated until
+    about budget_s; bytes as for the GPU figure."""
+    import numpy as np
+    import oracle
+    import workloads
+    times = []
+    t_end = time.time() + budget_s
+    while True:
+        t0 = time.time()
+        oracle.append(new["k_new"], new["v_new"], new["batch_idx"], new["positions"],
+                      prob["page_table"], max_len, prob["k_pages"], prob["v_pages"],
+                      prob["k_scales"], prob["v_scales"])
+        times.append(time.time() - t0)
+        if time.time() > t_end or len(times) >= 20:
+            break
+    t = float(np.median(times))
+    return {"value": round(workloads.append_bytes(prob, new) / t / 1e9, 3), "unit": "GB/s",
+            "cores": 1, "kind": "oracle",
+            "sample": f"{len(times)} whole appends of the workload ({new['k_new'].shape[0]} "
+                      f"tokens), median {t:.3f} s each (pool copies included)"}
+
+
+def bench_append(args):
+    import workloads
+    seed = 40 if args.seed is None else args.seed
+    r, prob, new = time_append(args.append, seed, args.steps, args.warmup)
+    spec = workloads.APPEND_CONFIGS[args.append][0]
+    res = {
+        "metric": APPEND_METRIC, "value": round(r["gbs"], 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["us_per_call"] / 1e3, 5),
+        "us_per_call": round(r["us_per_call"], 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "i8" if spec.kv_dtype == "i8" else "f16",
+        "data": "synthetic",
+        "config": {"workload": r["workload"], "seed": seed, "bytes_per_call": r["bytes"],
+                   "copies_rotated": r["copies"]},
+        "roofline": {"bound": "hbm", "achieved": round(r["achieved"], 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(r["achieved"] / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "append_kernel",
+                     "kernel_avg_us": round(r["kernel_avg_us"], 3),
+                     "algorithmic_bytes_per_launch": r["bytes"]},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline_append(prob, new, spec.max_kv_len)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--op", choices=["decode", "append"], default="decode")
+    ap.add_argument("--append", default="prefill_i8",
+                    help="append workload for --op append: prefill_i8, prefill_f16, decode_i8")
+    ap.add_argument("--no-append", action="store_true",
+                    help="leave the append object out of the decode line")
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2)
@@ -204,12 +320,14 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n, "repeats": 5}), flush=True)
         return
-    if args.sweep:
-        return sweep(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (the decode "
               f"is single-GPU; the multi-GPU sharding is described, not built)", file=sys.stderr)
         sys.exit(2)
+    if args.sweep:
+        return sweep(args)
+    if args.op == "append":
+        return bench_append(args)
 
     import numpy as np
     import torch
@@ -334,6 +452,13 @@ def main():
                      "algorithmic_bytes_per_launch": kvb},
         "cpu_baseline": None,
     }
+    if not args.no_append:
+        r, _, _ = time_append("prefill_i8", 40, min(K, 100), min(args.warmup, 10))
+        res["append"] = {"workload": r["workload"], "us_per_call": round(r["us_per_call"], 3),
+                         "gbs": round(r["gbs"], 1), "kernel_avg_us": round(r["kernel_avg_us"], 3),
+                         "roofline_frac": round(r["achieved"] / HBM_PEAK_GBS, 4),
+                         "bytes_per_call": r["bytes"]}
+        log(f"[bench] append {r['us_per_call']:.2f} us/call, {r['gbs']:.0f} GB/s")
     if not args.no_cpu:
         log("[bench] timing the CPU oracle ...")
         res["cpu_baseline"] = cpu_baseline(prob)

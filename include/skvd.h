@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define SKVD_ABI_VERSION 4
+#define SKVD_ABI_VERSION 5
 
 typedef enum {
   SKVD_OK = 0,
@@ -250,6 +250,68 @@ skvd_status skvd_gather_debug(const skvd_plan *plan, const skvd_decode_args *arg
  * a multiple of 16; sink is a device uint32 that the kernel may write (keeps the loads live).
  * Asynchronous on `stream`. */
 skvd_status skvd_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *stream);
+
+/* ---------------------------------------------------------------------------- append
+ * Writing new tokens into the paged cache: the step right before a decode, and the one
+ * operation that writes the cache (AMD-Ecosystem/flashinfer PR #397, "Stop declaring the paged
+ * KV cache mutated on read-only attention ops", section "What changed": append genuinely writes
+ * the cache and keeps declaring it written; the decode above only reads it). New token i belongs
+ * to sequence b = batch_idx[i] at logical position j = positions[i]; its K row of KV head g is
+ * written to slot j % P of page page_table[b][j / P] -- the address the decode reads -- and its
+ * V row to the same place in the V pool. An f16 cache receives the f16 elements verbatim. An
+ * int8 cache (value = int8 * scale, one f16 scale per 32 contiguous head_dim elements: the
+ * q8_0-style KV type named in 1bit-MONSTER/engine issue #115, comment "Fixed") is quantized on
+ * write, symmetric, the largest magnitude of each group of 32 mapped to 127:
+ *     s = f16(max|x| / 127)             (quotient in f32, rounded once to f16, nearest even)
+ *     c = clip(rint(x / s), -127, 127)  (quotient in f32, rint to nearest even; s = 0 -> c = 0)
+ * with no f16 temporary: each row is read once and written once.
+ *
+ * - Written: exactly the K/V elements (and, int8, the scales) of the slots the tokens name.
+ *   Nothing else; no workspace. k_new, v_new, batch_idx, positions and the table are read only.
+ * - Skips (device-data contract, not checked with a synchronization): a token whose batch_idx is
+ *   outside [0, batch) or whose position is outside [0, the plan's max_kv_len) writes nothing; a
+ *   page id outside [0, num_k_pages) (or num_v_pages) skips that pool's write. Two tokens naming
+ *   the same slot leave it undefined (no ordering between them). Inputs must be finite.
+ * - The pools may be any views the strides describe (K and V share page shape and strides, as
+ *   for the decode), but must not overlap each other or the inputs.
+ * - Graph capture: no allocation, synchronization or device-to-host read; one kernel launch.
+ * The plan supplies Hkv, D, P, the cache type, max_kv_len and the device; other plan fields are
+ * not used. */
+typedef struct {
+  const void *k_new;          /* f16 [N, Hkv, D]; D dense; 16-byte aligned (k_new, v_new,
+                                 batch_idx and positions may be NULL when N is 0) */
+  const void *v_new;          /* f16 [N, Hkv, D], same strides as k_new; 16-byte aligned */
+  int64_t new_tok_stride;     /* elements between tokens (non-negative multiple of 8) */
+  int64_t new_head_stride;    /* elements between KV heads (non-negative multiple of 8) */
+  const int32_t *batch_idx;   /* [N] device: sequence (page-table row) of each new token */
+  const int32_t *positions;   /* [N] device: logical position of each new token */
+  int32_t num_tokens;         /* N >= 0 (0 launches nothing) */
+  int32_t batch;              /* rows of page_table, >= 0 */
+  void *k_pages;              /* [num_k_pages, P, Hkv, D] f16 or int8, written; layout rules
+                                 as in skvd_decode_args */
+  void *v_pages;              /* [num_v_pages, P, Hkv, D], same strides as K, written */
+  int64_t page_stride;        /* elements; shared by K and V */
+  int64_t tok_stride;
+  int64_t head_stride;
+  int64_t num_k_pages;        /* >= 1 */
+  int64_t num_v_pages;        /* >= 1 */
+  void *k_scales;             /* int8 only: f16 [num_k_pages, P, Hkv, D/32], written; else NULL */
+  void *v_scales;             /* int8 only: f16 [num_v_pages, P, Hkv, D/32], written; else NULL */
+  int64_t scale_page_stride;  /* elements; layout rules as in skvd_decode_args */
+  int64_t scale_tok_stride;
+  int64_t scale_head_stride;
+  const int32_t *page_table;  /* [batch, table_stride] */
+  int64_t table_stride;       /* >= ceil(max_kv_len / P) */
+} skvd_append_args;
+
+/* Validation alone: the checks skvd_append makes before launching, with no HIP call. */
+skvd_status skvd_append_check(const skvd_plan *plan, const skvd_append_args *args);
+
+/* Append: one kernel on `stream` (a hipStream_t; NULL is the null stream), asynchronous. The
+ * current HIP device must be the plan's device. Host-checkable faults (NULL pointers, strides,
+ * alignment, scales present/absent against the cache type, table_stride) return an error before
+ * anything is launched; a launch failure returns SKVD_ERR_HIP. */
+skvd_status skvd_append(const skvd_plan *plan, const skvd_append_args *args, void *stream);
 
 const char *skvd_status_string(skvd_status status);
 /* Message of the last failed call on this thread ("" if none). */

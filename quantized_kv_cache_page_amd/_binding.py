@@ -21,7 +21,7 @@ REDUCERS = {"auto": 0, "direct": 1, "cooperative": 2, "multipass": 3, "hierarchi
 REDUCER_NAMES = {v: k for k, v in REDUCERS.items()}
 SCHEDULES = {"auto": 0, "static": 1, "balanced": 2}
 SCHEDULE_NAMES = {v: k for k, v in SCHEDULES.items()}
-ABI_VERSION = 4
+ABI_VERSION = 5
 STATUS_KV_LEN_CLAMPED = 0x1
 STATUS_PAGE_CLAMPED = 0x2
 
@@ -67,6 +67,23 @@ class skvd_decode_args(ctypes.Structure):
     ]
 
 
+class skvd_append_args(ctypes.Structure):
+    _fields_ = [
+        ("k_new", ctypes.c_void_p), ("v_new", ctypes.c_void_p),
+        ("new_tok_stride", ctypes.c_int64), ("new_head_stride", ctypes.c_int64),
+        ("batch_idx", ctypes.c_void_p), ("positions", ctypes.c_void_p),
+        ("num_tokens", ctypes.c_int32), ("batch", ctypes.c_int32),
+        ("k_pages", ctypes.c_void_p), ("v_pages", ctypes.c_void_p),
+        ("page_stride", ctypes.c_int64), ("tok_stride", ctypes.c_int64),
+        ("head_stride", ctypes.c_int64), ("num_k_pages", ctypes.c_int64),
+        ("num_v_pages", ctypes.c_int64),
+        ("k_scales", ctypes.c_void_p), ("v_scales", ctypes.c_void_p),
+        ("scale_page_stride", ctypes.c_int64), ("scale_tok_stride", ctypes.c_int64),
+        ("scale_head_stride", ctypes.c_int64),
+        ("page_table", ctypes.c_void_p), ("table_stride", ctypes.c_int64),
+    ]
+
+
 # Every symbol include/skvd.h declares, with its ctypes signature.
 _PLAN_P = ctypes.c_void_p
 SIGNATURES = {
@@ -91,6 +108,8 @@ SIGNATURES = {
                                          ctypes.c_void_p, ctypes.c_void_p]),
     "skvd_stream_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                         ctypes.c_void_p]),
+    "skvd_append_check": (ctypes.c_int, [_PLAN_P, ctypes.POINTER(skvd_append_args)]),
+    "skvd_append": (ctypes.c_int, [_PLAN_P, ctypes.POINTER(skvd_append_args), ctypes.c_void_p]),
     "skvd_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "skvd_last_error": (ctypes.c_char_p, []),
     "skvd_abi_version": (ctypes.c_int32, []),
@@ -195,6 +214,14 @@ def skvd_decode_merge(plan, args, workspace, workspace_bytes, stream) -> int:
 def skvd_gather_debug(plan, args, max_len, dk, dv, dks, dvs, stream) -> int:
     return int(lib().skvd_gather_debug(plan, ctypes.byref(args), max_len, dk, dv, dks, dvs,
                                        stream))
+
+
+def skvd_append_check(plan, args) -> int:
+    return int(lib().skvd_append_check(plan, ctypes.byref(args)))
+
+
+def skvd_append(plan, args, stream) -> int:
+    return int(lib().skvd_append(plan, ctypes.byref(args), stream))
 
 
 def skvd_stream_read(buf: int, nbytes: int, sink: int, stream) -> int:
@@ -372,6 +399,65 @@ class Plan:
                            out, lse, q_per_seq)
         return skvd_decode_check(self.handle, a, self.workspace_bytes if workspace_bytes is None
                                  else workspace_bytes)
+
+    def make_append_args(self, k_new, v_new, batch_idx, positions, k_pages, v_pages, page_table,
+                         k_scales=None, v_scales=None, batch=None) -> skvd_append_args:
+        if k_new.dtype != torch.float16 or v_new.dtype != torch.float16:
+            raise TypeError("k_new and v_new must be float16")
+        if k_new.shape != v_new.shape or k_new.stride() != v_new.stride() or k_new.dim() != 3:
+            raise SkvdError(3, "Plan.append", "k_new and v_new must be [N, Hkv, D] with equal strides")
+        empty = k_new.shape[0] == 0  # torch may give an empty tensor any strides
+        if (not empty and k_new.stride(2) != 1) or k_pages.stride(3) != 1:
+            raise SkvdError(3, "Plan.append", "head_dim must be dense in the new rows and the pools")
+        want = torch.float16 if self.kv_dtype == "f16" else torch.int8
+        if k_pages.dtype != want or v_pages.dtype != want:
+            raise TypeError(f"k_pages and v_pages must be {want}")
+        if k_pages.stride() != v_pages.stride() or k_pages.shape[1:] != v_pages.shape[1:]:
+            raise SkvdError(3, "Plan.append", "K and V must share page shape and strides")
+        if batch_idx.dtype != torch.int32 or positions.dtype != torch.int32 or \
+                page_table.dtype != torch.int32:
+            raise TypeError("batch_idx, positions and page_table must be int32")
+        if batch_idx.shape != (k_new.shape[0],) or positions.shape != (k_new.shape[0],) or \
+                (not empty and (not batch_idx.is_contiguous() or not positions.is_contiguous())):
+            raise SkvdError(2, "Plan.append", "batch_idx and positions must be dense [N]")
+        if page_table.dim() != 2 or page_table.stride(1) != 1:
+            raise SkvdError(3, "Plan.append", "page_table must be [B, n] with unit inner stride")
+        if k_new.shape[1] != self.params.num_kv_heads or k_new.shape[2] != self.params.head_dim:
+            raise SkvdError(2, "Plan.append", "new rows must be [N, Hkv, D] of the plan")
+        a = skvd_append_args()
+        a.k_new, a.v_new = k_new.data_ptr(), v_new.data_ptr()
+        a.new_tok_stride, a.new_head_stride = ((k_new.shape[1] * k_new.shape[2], k_new.shape[2])
+                                               if empty else (k_new.stride(0), k_new.stride(1)))
+        a.batch_idx, a.positions = batch_idx.data_ptr(), positions.data_ptr()
+        a.num_tokens = int(k_new.shape[0])
+        a.batch = int(page_table.shape[0] if batch is None else batch)
+        a.k_pages, a.v_pages = k_pages.data_ptr(), v_pages.data_ptr()
+        a.page_stride, a.tok_stride, a.head_stride = k_pages.stride(0), k_pages.stride(1), k_pages.stride(2)
+        a.num_k_pages, a.num_v_pages = k_pages.shape[0], v_pages.shape[0]
+        if k_scales is not None:
+            if k_scales.dtype != torch.float16 or v_scales is None or v_scales.stride() != k_scales.stride():
+                raise SkvdError(4, "Plan.append", "k_scales/v_scales must be f16 with equal strides")
+            a.k_scales, a.v_scales = k_scales.data_ptr(), v_scales.data_ptr()
+            a.scale_page_stride, a.scale_tok_stride, a.scale_head_stride = (
+                k_scales.stride(0), k_scales.stride(1), k_scales.stride(2))
+        elif v_scales is not None:
+            raise SkvdError(4, "Plan.append", "v_scales given without k_scales")
+        a.page_table = page_table.data_ptr()
+        a.table_stride = page_table.stride(0)
+        return a
+
+    def append(self, k_new, v_new, batch_idx, positions, k_pages, v_pages, page_table,
+               k_scales=None, v_scales=None, batch=None, stream=None):
+        """skvd_append: write new rows k_new, v_new [N, Hkv, D] f16 of tokens (batch_idx[i],
+        positions[i]) into the pools in place (int8 pools: quantized, scales written). Only the
+        named slots are written; nothing is allocated."""
+        a = self.make_append_args(k_new, v_new, batch_idx, positions, k_pages, v_pages,
+                                  page_table, k_scales, v_scales, batch)
+        _check(skvd_append(self.handle, a, self._stream(stream)), "skvd_append")
+
+    def append_check(self, *args, **kw) -> int:
+        """skvd_append_check: the validation alone, no HIP call. Returns the status."""
+        return skvd_append_check(self.handle, self.make_append_args(*args, **kw))
 
     def gather_debug(self, q, k_pages, v_pages, page_table, kv_len, max_len, k_scales=None,
                      v_scales=None, q_per_seq=1, stream=None):

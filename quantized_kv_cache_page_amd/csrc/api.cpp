@@ -54,6 +54,54 @@ skvd_status common_checks(const skvd_plan *plan, const skvd_decode_args *args, v
   return SKVD_OK;
 }
 
+// skvd_append's host checks (shapes and layout the append kernel addresses; no HIP call).
+skvd_status check_append(const skvd_plan *plan, const skvd_append_args *a) {
+  g_err[0] = 0;
+  if (!plan) return set_err(SKVD_ERR_NULL, "plan is NULL");
+  if (!a) return set_err(SKVD_ERR_NULL, "args is NULL");
+  const skvd::Plan &p = plan->p;
+  const bool i8 = p.prm.kv_dtype == SKVD_KV_I8_F16SCALE32;
+  const auto al = [](const void *ptr, uintptr_t n) { return (uintptr_t)ptr % n == 0; };
+  if (a->num_tokens < 0 || a->batch < 0)
+    return set_err(SKVD_ERR_SHAPE, "num_tokens=%d and batch=%d must be >= 0", a->num_tokens,
+                   a->batch);
+  if (a->num_tokens > 0 && (!a->k_new || !a->v_new || !a->batch_idx || !a->positions))
+    return set_err(SKVD_ERR_NULL, "k_new, v_new, batch_idx and positions must be non-NULL "
+                   "when num_tokens > 0");
+  if (!a->k_pages || !a->v_pages || !a->page_table)
+    return set_err(SKVD_ERR_NULL, "k_pages, v_pages and page_table must be non-NULL");
+  if (i8 && (!a->k_scales || !a->v_scales))
+    return set_err(SKVD_ERR_DTYPE, "int8 cache needs k_scales and v_scales");
+  if (!i8 && (a->k_scales || a->v_scales))
+    return set_err(SKVD_ERR_DTYPE, "f16 cache takes no scales");
+  if (!al(a->k_new, 16) || !al(a->v_new, 16) || a->new_tok_stride < 0 || a->new_head_stride < 0 ||
+      a->new_tok_stride % 8 || a->new_head_stride % 8)
+    return set_err(SKVD_ERR_LAYOUT, "k_new/v_new must be 16-byte aligned with token/head strides "
+                   "that are non-negative multiples of 8 elements");
+  const int64_t kv_vec = i8 ? 16 : 8;  // the decode's rule: 16-byte rows in both cache types
+  if (!al(a->k_pages, 16) || !al(a->v_pages, 16) || a->page_stride < 0 || a->tok_stride < 0 ||
+      a->head_stride < 0 || a->page_stride % kv_vec || a->tok_stride % kv_vec ||
+      a->head_stride % kv_vec)
+    return set_err(SKVD_ERR_LAYOUT, "K/V pools must be 16-byte aligned and have page/token/head "
+                   "strides that are non-negative multiples of 16 bytes");
+  if (i8 && (!al(a->k_scales, 8) || !al(a->v_scales, 8) || a->scale_page_stride < 0 ||
+             a->scale_tok_stride < 0 || a->scale_head_stride < 0 || a->scale_page_stride % 4 ||
+             a->scale_tok_stride % 4 || a->scale_head_stride % 4))
+    return set_err(SKVD_ERR_LAYOUT, "scale pools must be 8-byte aligned with non-negative "
+                   "strides that are multiples of 4 elements");
+  if (a->num_k_pages < 1 || a->num_v_pages < 1)
+    return set_err(SKVD_ERR_SHAPE, "num_k_pages and num_v_pages must be >= 1");
+  const int64_t need = (p.prm.max_kv_len + p.prm.page_size - 1) / p.prm.page_size;
+  if (a->table_stride < need)
+    return set_err(SKVD_ERR_LAYOUT, "table_stride=%lld below ceil(max_kv_len/P)=%lld",
+                   (long long)a->table_stride, (long long)need);
+  // The append kernel numbers its lanes (num_tokens * Hkv * D / 8) in 32 bits.
+  if ((int64_t)a->num_tokens * p.prm.num_kv_heads * (p.prm.head_dim / 8) >= (int64_t(1) << 31))
+    return set_err(SKVD_ERR_SHAPE, "num_tokens=%d too large for one append (split the call)",
+                   a->num_tokens);
+  return SKVD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -219,6 +267,76 @@ skvd_status skvd_gather_debug(const skvd_plan *plan, const skvd_decode_args *arg
   la.debug = 0;
   int e = skvd::launch_gather(plan->p, la, max_len, dense_k, dense_v, dense_ks, dense_vs, stream);
   return e ? hip_err(e, "gather kernel launch") : SKVD_OK;
+}
+
+skvd_status skvd_append_check(const skvd_plan *plan, const skvd_append_args *args) {
+  return check_append(plan, args);
+}
+
+skvd_status skvd_append(const skvd_plan *plan, const skvd_append_args *a, void *stream) {
+  skvd_status st = check_append(plan, a);
+  if (st != SKVD_OK) return st;
+  const skvd::Plan &p = plan->p;
+  int dev = -1;
+  hipError_t he = hipGetDevice(&dev);
+  if (he != hipSuccess) {
+    (void)hipGetLastError();
+    return set_err(SKVD_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(he));
+  }
+  if (dev != p.prm.device)
+    return set_err(SKVD_ERR_DEVICE, "current device %d is not the plan's device %d", dev,
+                   p.prm.device);
+  skvd::AppendLaunch l{};
+  l.k_new = a->k_new;
+  l.v_new = a->v_new;
+  l.new_tok_stride = a->new_tok_stride;
+  l.new_head_stride = a->new_head_stride;
+  l.batch_idx = a->batch_idx;
+  l.positions = a->positions;
+  l.k = a->k_pages;
+  l.v = a->v_pages;
+  l.page_stride = a->page_stride;
+  l.tok_stride = a->tok_stride;
+  l.head_stride = a->head_stride;
+  l.num_k_pages = a->num_k_pages;
+  l.num_v_pages = a->num_v_pages;
+  l.ks = a->k_scales;
+  l.vs = a->v_scales;
+  l.s_page_stride = a->scale_page_stride;
+  l.s_tok_stride = a->scale_tok_stride;
+  l.s_head_stride = a->scale_head_stride;
+  l.table = a->page_table;
+  l.table_stride = a->table_stride;
+  l.num_tokens = a->num_tokens;
+  l.batch = a->batch;
+  l.Hkv = p.prm.num_kv_heads;
+  l.D = p.prm.head_dim;
+  l.rows = (int64_t)a->num_tokens * l.Hkv;
+  int sh = 0;
+  while ((1 << sh) < p.prm.page_size) ++sh;
+  l.page_shift = sh;
+  l.max_len = p.prm.max_kv_len;
+  l.int8 = p.prm.kv_dtype == SKVD_KV_I8_F16SCALE32;
+  // Grid: a whole number of tokens' lanes (so a lane keeps its head and part while it strides),
+  // each lane serving up to skvd::kAppendTokensPerLane tokens per round; at most one round of
+  // resident 256-lane workgroups, fewer for a small append.
+  l.lanes_per_token = l.Hkv * l.D / 8;
+  int64_t g0 = 1;
+  {
+    int64_t x = l.lanes_per_token, y = 256;
+    while (y) { const int64_t t = x % y; x = y; y = t; }
+    g0 = l.lanes_per_token / x;  // workgroups per whole number of tokens
+  }
+  const int64_t toks = (a->num_tokens + skvd::kAppendTokensPerLane - 1) / skvd::kAppendTokensPerLane;
+  const int64_t want = (toks * l.lanes_per_token + 255) / 256;
+  // resident workgroups per CU: int8 77 VGPRs -> 6 waves per SIMD; f16 58 -> 8
+  const int64_t cap = (l.int8 ? 6LL : 8LL) * p.num_cus;
+  int64_t blocks = want < cap ? want : cap;
+  blocks = (blocks + g0 - 1) / g0 * g0;
+  l.blocks = (unsigned)blocks;
+  l.tok_step = (int)(blocks * 256 / l.lanes_per_token);
+  int e = skvd::launch_append(l, stream);
+  return e ? hip_err(e, "append kernel launch") : SKVD_OK;
 }
 
 skvd_status skvd_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *stream) {

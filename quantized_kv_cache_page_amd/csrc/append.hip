@@ -1,0 +1,178 @@
+// Append kernel: new K/V rows into the paged cache, f16 verbatim or int8 quantized on write.
+//
+// The slot of new token i is (page_table[b][j / P], j % P) for b = batch_idx[i], j =
+// positions[i]: the address the decode reads. Each lane owns 8 consecutive head_dim elements of
+// one (token, KV head) row, in K and in V: one 16-byte load of each and one store of each (16
+// bytes of f16, or 8 bytes of int8 codes), so a row of D elements is D/8 lanes and a wave covers
+// 64*8/D rows; consecutive rows of a [N, Hkv, D] input are consecutive memory, so a wave's loads
+// are one contiguous run. The kernel is a pure stream (read the new rows once, write the slots
+// once); it is bound by HBM, or by launch latency for a decode step's handful of tokens.
+//
+// int8 (one f16 scale per 32 elements; AMD-Ecosystem/flashinfer PR #397 names append as the op
+// that writes the cache, 1bit-MONSTER/engine issue #115 comment "Fixed" names the q8_0-style KV
+// type): the four lanes of a 32-element group take the group's largest magnitude with two
+// quad-permute DPP steps, then
+//     s = f16(amax / 127)                 f32 quotient, rounded once to f16 (nearest even)
+//     c = clip(rint(x / s), -127, 127)    f32 quotient, nearest even; s = 0 gives c = 0
+// and the group's first lane writes s. The scale's quotient is an IEEE-correctly rounded f32
+// division; the codes take the correctly rounded quotient's decision through a reciprocal
+// multiply checked against the rounding boundary (code_of), so they are those of any correctly
+// rounded f32 evaluation of the same rule.
+#include <hip/hip_runtime.h>
+
+#include "skvd_internal.h"
+
+namespace skvd {
+namespace {
+
+typedef _Float16 half8a __attribute__((ext_vector_type(8)));
+typedef unsigned uint2a __attribute__((ext_vector_type(2)));
+
+template <int CTRL>
+__device__ __forceinline__ float quad_dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// The 8 codes of one lane and the f16 scale of its 32-element group (all four lanes of the
+// group run this together: the DPP steps read within the lane quad).
+//
+// Codes: rint(x / s) with x / s the correctly rounded f32 quotient, clipped to [-127, 127]. The
+// product q = x * rcp(s) (rcp to 1 ulp) is within 1.5 ulp-relative of x / s, i.e. within 6e-5 of
+// it for |x / s| < 256 (always: s is max|x| / 127 rounded to f16), so rint(q) is the quotient's
+// integer unless q lies within 2^-12 of a half-integer. Lanes holding such an element (rare)
+// redo it with the division, so the decision is that of the correctly rounded quotient while
+// nearly every element costs one multiply.
+__device__ __forceinline__ uint2a quantize8(half8a x, _Float16 *scale) {
+  constexpr float kNear = 0.5f - 0x1p-12f;
+  float f[8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    f[e] = (float)x[e];
+    amax = fmaxf(amax, fabsf(f[e]));
+  }
+  amax = fmaxf(amax, quad_dpp<0xB1>(amax));  // quad_perm [1,0,3,2]: lane xor 1
+  amax = fmaxf(amax, quad_dpp<0x4E>(amax));  // quad_perm [2,3,0,1]: lane xor 2
+  const _Float16 sh = (_Float16)(amax / 127.0f);
+  const float s = (float)sh;
+  const float rs = __builtin_amdgcn_rcpf(s);
+  float c[8];
+  bool near = false;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float q = f[e] * rs;
+    c[e] = rintf(q);
+    near |= fabsf(q - c[e]) > kNear;
+  }
+  if (near && s > 0.0f) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float q = f[e] * rs;
+      if (fabsf(q - rintf(q)) > kNear) c[e] = rintf(f[e] / s);
+    }
+  }
+  unsigned w[2] = {0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float cc = s > 0.0f ? __builtin_amdgcn_fmed3f(c[e], -127.0f, 127.0f) : 0.0f;
+    w[e >> 2] |= ((unsigned)(int)cc & 0xFFu) << (8 * (e & 3));
+  }
+  *scale = sh;
+  uint2a r;
+  r[0] = w[0];
+  r[1] = w[1];
+  return r;
+}
+
+template <int D, bool I8>
+__device__ __forceinline__ void store_row(const AppendLaunch &a, half8a x, void *pool,
+                                          void *scales, int64_t page, int slot, int kvh,
+                                          int part) {
+  const int64_t off = page * a.page_stride + (int64_t)slot * a.tok_stride +
+                      (int64_t)kvh * a.head_stride + part * 8;
+  if constexpr (!I8) {
+    *(half8a *)((_Float16 *)pool + off) = x;
+  } else {
+    _Float16 sh;
+    const uint2a codes = quantize8(x, &sh);
+    *(uint2a *)((int8_t *)pool + off) = codes;
+    if ((part & 3) == 0) {
+      const int64_t soff = page * a.s_page_stride + (int64_t)slot * a.s_tok_stride +
+                           (int64_t)kvh * a.s_head_stride + (part >> 2);
+      ((_Float16 *)scales)[soff] = sh;
+    }
+  }
+}
+
+// A lane owns one 8-element part of one KV-head row and serves kTokensPerLane tokens that are
+// tok_step apart (the grid holds a whole number of tokens' lanes, so a lane keeps its head and
+// part; one division at entry). All of a round's loads -- new K and V rows, sequence indices,
+// positions -- are issued together, then all of its page-table reads, then the quantization and
+// stores: two dependent memory round trips per kTokensPerLane tokens. Loads are branch-free
+// (token indices clamped into the batch, invalid tokens masked), so nothing waits early.
+constexpr int kTokensPerLane = kAppendTokensPerLane;
+
+template <int D, bool I8>
+__global__ __launch_bounds__(256) void append_kernel(AppendLaunch a) {
+  constexpr int kLanesPerRow = D / 8;
+  constexpr int U = kTokensPerLane;
+  const unsigned gid = blockIdx.x * 256u + threadIdx.x;
+  const unsigned lpt = (unsigned)a.lanes_per_token;
+  const int tok0 = (int)(gid / lpt);
+  if (tok0 >= a.tok_step) return;
+  const unsigned rem = gid - (unsigned)tok0 * lpt;
+  const int kvh = (int)(rem / kLanesPerRow);   // lanes of one row (and quad) share every branch
+  const int part = (int)(rem % kLanesPerRow);
+  const int64_t head_off = (int64_t)kvh * a.new_head_stride + part * 8;
+  const _Float16 *kn = (const _Float16 *)a.k_new;
+  const _Float16 *vn = (const _Float16 *)a.v_new;
+  const int slot_mask = (1 << a.page_shift) - 1;
+  const int last = a.num_tokens - 1;
+  for (int base = tok0; base < a.num_tokens; base += U * a.tok_step) {
+    half8a xk[U], xv[U];
+    int b[U], j[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = min(base + u * a.tok_step, last);
+      const int64_t src = (int64_t)t * a.new_tok_stride + head_off;
+      xk[u] = __builtin_nontemporal_load((const half8a *)(kn + src));
+      xv[u] = __builtin_nontemporal_load((const half8a *)(vn + src));
+      b[u] = a.batch_idx[t];
+      j[u] = a.positions[t];
+    }
+    int64_t page[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool ok = base + u * a.tok_step <= last && b[u] >= 0 && b[u] < a.batch &&
+                      j[u] >= 0 && j[u] < a.max_len;
+      const int bb = ok ? b[u] : 0, jj = ok ? j[u] : 0;  // row 0, entry 0 exist (batch >= 1)
+      const int64_t pg = a.table[(int64_t)bb * a.table_stride + (jj >> a.page_shift)];
+      page[u] = ok ? pg : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (page[u] < 0) continue;
+      const int slot = j[u] & slot_mask;
+      if (page[u] < a.num_k_pages) store_row<D, I8>(a, xk[u], a.k, a.ks, page[u], slot, kvh, part);
+      if (page[u] < a.num_v_pages) store_row<D, I8>(a, xv[u], a.v, a.vs, page[u], slot, kvh, part);
+    }
+  }
+}
+
+template <int D>
+void launch_d(const AppendLaunch &a, hipStream_t st) {
+  if (a.int8) append_kernel<D, true><<<a.blocks, 256, 0, st>>>(a);
+  else append_kernel<D, false><<<a.blocks, 256, 0, st>>>(a);
+}
+
+}  // namespace
+
+int launch_append(const AppendLaunch &a, void *stream) {
+  if (a.rows == 0 || a.batch == 0) return 0;  // nothing to write (and no table row to read)
+  hipStream_t st = (hipStream_t)stream;
+  if (a.D == 128) launch_d<128>(a, st);
+  else launch_d<256>(a, st);
+  return (int)hipGetLastError();
+}
+
+}  // namespace skvd

@@ -83,4 +83,27 @@ int launch_stream_read(const void *buf, size_t n16, uint32_t *sink, void *stream
 int launch_gather(const Plan &p, const LaunchArgs &la, int max_len, void *dk, void *dv, void *dks,
                   void *dvs, void *stream);
 
+// Append launch (append.hip): resolved on the host from the plan and skvd_append_args.
+struct AppendLaunch {
+  const void *k_new, *v_new;
+  int64_t new_tok_stride, new_head_stride;
+  const int32_t *batch_idx, *positions;
+  void *k, *v;
+  int64_t page_stride, tok_stride, head_stride;
+  int64_t num_k_pages, num_v_pages;
+  void *ks, *vs;
+  int64_t s_page_stride, s_tok_stride, s_head_stride;
+  const int32_t *table;
+  int64_t table_stride;
+  int64_t rows;        // num_tokens * Hkv
+  int num_tokens, batch, Hkv, D, page_shift, max_len, int8;
+  int lanes_per_token;  // Hkv * D / 8: one lane per 8 elements of a row, K and V together
+  int tok_step;         // tokens the whole grid covers per step (grid lanes / lanes_per_token)
+  unsigned blocks;      // 256-lane workgroups launched
+};
+
+// append.hip
+constexpr int kAppendTokensPerLane = 4;  // tokens one append lane serves per round
+int launch_append(const AppendLaunch &a, void *stream);
+
 }  // namespace skvd

@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol():
     for s in syms:
         assert hasattr(L, s), s
     assert set(syms) == set(bd.SIGNATURES), set(syms) ^ set(bd.SIGNATURES)
-    assert L.skvd_abi_version() == bd.ABI_VERSION == 4
+    assert L.skvd_abi_version() == bd.ABI_VERSION == 5
 
 
 def plan(**kw):
@@ -226,3 +226,50 @@ def test_status_strings():
     for s in range(9):
         assert skvd.status_string(s)
     assert skvd.status_string(0) == "ok"
+
+
+def good_append_args(i8=False, **over):
+    a = bd.skvd_append_args()
+    a.k_new, a.v_new = FAKE, FAKE + (1 << 29)
+    a.new_tok_stride, a.new_head_stride = 8 * 128, 128
+    a.batch_idx, a.positions = FAKE + (1 << 28), FAKE + (1 << 27)
+    a.num_tokens, a.batch = 64, 32
+    a.k_pages, a.v_pages = FAKE + (1 << 31), FAKE + (1 << 32)
+    a.page_stride, a.tok_stride, a.head_stride = 16 * 8 * 128, 8 * 128, 128
+    a.num_k_pages = a.num_v_pages = 100
+    if i8:
+        a.k_scales, a.v_scales = FAKE + (2 << 32), FAKE + (3 << 32)
+        a.scale_page_stride, a.scale_tok_stride, a.scale_head_stride = 16 * 8 * 4, 8 * 4, 4
+    a.page_table, a.table_stride = FAKE, 256
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("over,status", [
+    ({}, 0), (dict(num_tokens=0), 0), (dict(batch=0), 0),
+    (dict(num_tokens=0, k_new=None, v_new=None, batch_idx=None, positions=None), 0),
+    (dict(k_new=None), 1), (dict(v_new=None), 1), (dict(batch_idx=None), 1),
+    (dict(positions=None), 1), (dict(k_pages=None), 1), (dict(page_table=None), 1),
+    (dict(num_tokens=-1), 2), (dict(batch=-1), 2), (dict(num_k_pages=0), 2),
+    (dict(k_new=FAKE + 8), 3), (dict(new_head_stride=100), 3), (dict(new_tok_stride=-8), 3),
+    (dict(v_pages=FAKE + 8), 3), (dict(tok_stride=1020), 3), (dict(table_stride=255), 3),
+    (dict(k_scales=FAKE), 4),
+])
+def test_append_check_f16(over, status):
+    p = plan()
+    assert bd.skvd_append_check(p.handle, good_append_args(**over)) == status
+
+
+@pytest.mark.parametrize("over,status", [
+    ({}, 0), (dict(k_scales=None), 4), (dict(v_scales=None), 4), (dict(k_pages=FAKE + 8), 3),
+    (dict(tok_stride=8 * 128 + 8), 3), (dict(tok_stride=8 * 128 + 16), 0),
+    (dict(k_scales=FAKE + 2), 3), (dict(scale_tok_stride=34), 3),
+])
+def test_append_check_int8(over, status):
+    p = plan(kv_dtype="i8")
+    assert bd.skvd_append_check(p.handle, good_append_args(i8=True, **over)) == status
+
+
+def test_append_check_null_plan():
+    assert bd.skvd_append_check(None, good_append_args()) == 1

@@ -1,0 +1,251 @@
+"""GPU parity of the append (new K/V rows into the paged cache, int8 quantized on write): the HIP
+kernel through the C ABI against the oracle's append on the same seeded inputs.
+
+Append is byte work (f16 rows copied, int8 codes and f16 scales decided in f32 on both sides),
+so every comparison is bit-exact over the whole pools, written slots and untouched ones alike.
+The decode over an appended cache is compared with the fp64 oracle at the decode's tolerance.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.gpu_util import compare, make_plan, run, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import quantized_kv_cache_page_amd as skvd
+    skvd.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _dev(x):
+    return None if x is None else torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def _pool_dev(x, layout):
+    """A pool [N, P, Hkv, X] on the device in NHD (as given) or HND memory order (the same
+    logical view over [N, Hkv, P, X] storage)."""
+    if x is None:
+        return None
+    if layout == "nhd":
+        return torch.from_numpy(x).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x.transpose(0, 2, 1, 3))).cuda().permute(0, 2, 1, 3)
+
+
+def gpu_append(plan, prob, new, layout="nhd", batch=None, table=None):
+    """Append on the GPU into device copies of the problem's pools; returns them on the host."""
+    k = _pool_dev(prob["k_pages"], layout)
+    v = _pool_dev(prob["v_pages"], layout)
+    ks = _pool_dev(prob["k_scales"], layout)
+    vs = _pool_dev(prob["v_scales"], layout)
+    tab = _dev(prob["page_table"] if table is None else table)
+    plan.append(_dev(new["k_new"]), _dev(new["v_new"]), _dev(new["batch_idx"]),
+                _dev(new["positions"]), k, v, tab, ks, vs, batch=batch)
+    torch.cuda.synchronize()
+    return [None if t is None else t.cpu().numpy() for t in (k, v, ks, vs)]
+
+
+def oracle_append(prob, new, max_len, batch=None, table=None):
+    k, v, ks, vs, _ = oracle.append(new["k_new"], new["v_new"], new["batch_idx"],
+                                    new["positions"],
+                                    prob["page_table"] if table is None else table, max_len,
+                                    prob["k_pages"], prob["v_pages"], prob["k_scales"],
+                                    prob["v_scales"], batch=batch)
+    return [k, v, ks, vs]
+
+
+def assert_pools_equal(got, want, what):
+    for name, g, w in zip(("K", "V", "K scales", "V scales"), got, want):
+        if w is None:
+            assert g is None
+            continue
+        gb, wb = np.ascontiguousarray(g).view(np.uint8), np.ascontiguousarray(w).view(np.uint8)
+        bad = int((gb != wb).sum())
+        assert bad == 0, f"{what}: {name} differs in {bad} bytes"
+    say(f"  {what}: pools bit-identical")
+
+
+CASES = [
+    # (name, B, Hkv, D, P, kv, lens, new per sequence, layout)
+    ("f16_d128_p16", 3, 8, 128, 16, "f16", (17, 300, 64), 40, "nhd"),
+    ("f16_d256_p1", 2, 2, 256, 1, "f16", (9, 130), 130, "nhd"),
+    ("f16_d128_p64_hnd", 3, 4, 128, 64, "f16", (1, 200, 129), 70, "hnd"),
+    ("i8_d128_p16", 4, 8, 128, 16, "i8", (1, 65, 512, 33), 64, "nhd"),
+    ("i8_d256_p4", 2, 2, 256, 4, "i8", (7, 300), 300, "nhd"),
+    ("i8_d128_p1_mha", 2, 1, 128, 1, "i8", (50, 3), 50, "nhd"),
+    ("i8_d128_p16_hnd", 3, 8, 128, 16, "i8", (40, 16, 100), 25, "hnd"),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_append_matches_oracle(case):
+    name, B, Hkv, D, P, kv, lens, n, layout = case
+    s = workloads.spec(name=name, batch=B, num_qo_heads=2 * Hkv, num_kv_heads=Hkv, head_dim=D,
+                       page_size=P, kv_dtype=kv, lens=("list", lens))
+    prob = workloads.generate(s, 31)
+    new = workloads.append_tokens(prob, 31, n)
+    say(f"case {name}: N={new['k_new'].shape[0]} B={B} Hkv={Hkv} D={D} P={P} {kv} {layout}")
+    plan = make_plan(prob)
+    got = gpu_append(plan, prob, new, layout)
+    want = oracle_append(prob, new, plan.params.max_kv_len)
+    assert_pools_equal(got, want, name)
+
+
+def test_append_special_values():
+    """Groups that stress the int8 rule: exact multiples of powers of two, quotients halfway
+    between integers, all-zero groups, groups whose scale underflows f16, f16 subnormals and
+    values near f16's maximum."""
+    B, Hkv, D, P = 1, 2, 128, 16
+    s = workloads.spec(name="special", batch=B, num_qo_heads=4, num_kv_heads=Hkv, head_dim=D,
+                       page_size=P, kv_dtype="i8", lens=("list", (64,)))
+    prob = workloads.generate(s, 32)
+    rng = np.random.default_rng(32)
+    N = 64
+    x = np.zeros((N, Hkv, D // 32, 32), np.float64)
+    for i in range(N):
+        for h in range(Hkv):
+            for g in range(D // 32):
+                kind = (i * 7 + h * 3 + g) % 8
+                c = rng.integers(-127, 128, size=32).astype(np.float64)
+                if kind == 0:    # exact: c * 2^e with |c| = 127 present
+                    c[rng.integers(32)] = 127
+                    x[i, h, g] = c * 2.0 ** rng.integers(-12, 3)
+                elif kind == 1:  # halfway quotients at scale 1
+                    x[i, h, g] = np.round(c) + 0.5
+                    x[i, h, g, 0] = 127
+                elif kind == 2:  # all zero
+                    x[i, h, g] = 0
+                elif kind == 3:  # scale below f16's range
+                    x[i, h, g] = 0
+                    x[i, h, g, 3] = 2.0 ** -24
+                elif kind == 4:  # subnormal inputs
+                    x[i, h, g] = c * 2.0 ** -24
+                elif kind == 5:  # near f16's maximum
+                    x[i, h, g] = rng.uniform(-65504, 65504, 32)
+                else:            # wide dynamic range in one group
+                    x[i, h, g] = rng.standard_normal(32) * 10.0 ** rng.uniform(-4, 4, 32)
+    kn = x.reshape(N, Hkv, D).astype(np.float16)
+    vn = (-x[:, ::-1]).reshape(N, Hkv, D).astype(np.float16)
+    new = dict(k_new=kn, v_new=np.ascontiguousarray(vn), batch_idx=np.zeros(N, np.int32),
+               positions=rng.permutation(64).astype(np.int32))
+    plan = make_plan(prob)
+    got = gpu_append(plan, prob, new)
+    want = oracle_append(prob, new, plan.params.max_kv_len)
+    assert_pools_equal(got, want, "special values")
+
+
+def test_append_skips_invalid_tokens():
+    """Tokens naming a sequence outside [0, batch), a position outside [0, max_kv_len), or a page
+    id outside the pool write nothing (the kernel's own bounds checks); the rest are written."""
+    s = workloads.spec(name="skips", batch=3, num_qo_heads=8, num_kv_heads=4, head_dim=128,
+                       page_size=16, kv_dtype="i8", lens=("list", (40, 64, 20)))
+    prob = workloads.generate(s, 33)
+    new = workloads.append_tokens(prob, 33, 20)
+    N = new["k_new"].shape[0]
+    bi, pos = new["batch_idx"].copy(), new["positions"].copy()
+    bi[0], bi[1], pos[2], pos[3] = -1, 3, -7, 64  # 64 = max_kv_len of the plan below
+    table = prob["page_table"].copy()
+    table[2, 0] = prob["k_pages"].shape[0]        # one past the pool
+    table[2, 1] = -3
+    new = dict(new, batch_idx=bi, positions=pos)
+    plan = make_plan(prob, max_kv_len=64)
+    got = gpu_append(plan, prob, new, table=table)
+    want = oracle_append(prob, new, 64, table=table)
+    say(f"  N={N}")
+    assert_pools_equal(got, want, "skips")
+
+
+def test_append_empty_launches_nothing():
+    s = workloads.spec(name="empty", batch=1, num_qo_heads=2, num_kv_heads=1, head_dim=128,
+                       page_size=16, kv_dtype="f16", lens=("list", (32,)))
+    prob = workloads.generate(s, 34)
+    new = dict(k_new=np.zeros((0, 1, 128), np.float16), v_new=np.zeros((0, 1, 128), np.float16),
+               batch_idx=np.zeros(0, np.int32), positions=np.zeros(0, np.int32))
+    plan = make_plan(prob)
+    got = gpu_append(plan, prob, new)
+    assert_pools_equal(got, [prob["k_pages"], prob["v_pages"], None, None], "empty")
+
+
+@pytest.mark.parametrize("name", sorted(workloads.APPEND_CONFIGS))
+def test_append_workloads_full_size(name):
+    """The benchmark's append workloads at full size, in its launch configuration."""
+    s, n = workloads.APPEND_CONFIGS[name]
+    prob = workloads.generate(s, 35)
+    new = workloads.append_tokens(prob, 35, n)
+    say(f"case {name}: N={new['k_new'].shape[0]}")
+    plan = make_plan(prob, max_kv_len=s.max_kv_len)
+    got = gpu_append(plan, prob, new)
+    want = oracle_append(prob, new, s.max_kv_len)
+    assert_pools_equal(got, want, name)
+
+
+@pytest.mark.parametrize("kv", ["f16", "i8"])
+def test_append_then_decode(kv):
+    """A decode step: append T new tokens per sequence at the end of each cache, then decode
+    over the result on the GPU; the pools match the oracle's append bit for bit and the decode
+    matches the fp64 oracle on those pools."""
+    s = workloads.spec(name=f"step_{kv}", batch=6, q_per_seq=2, num_qo_heads=32, num_kv_heads=8,
+                       head_dim=128, page_size=16, kv_dtype=kv,
+                       lens=("list", (2, 70, 1000, 2049, 31, 4096)))
+    prob = workloads.generate(s, 36)
+    new = workloads.append_tokens(prob, 36, 2)
+    plan = make_plan(prob)
+    dev = to_dev(prob)
+    plan.append(_dev(new["k_new"]), _dev(new["v_new"]), _dev(new["batch_idx"]),
+                _dev(new["positions"]), dev["k_pages"], dev["v_pages"], dev["page_table"],
+                dev["k_scales"], dev["v_scales"])
+    o, lse = run(plan, prob, dev)
+    torch.cuda.synchronize()
+    want = oracle_append(prob, new, plan.params.max_kv_len)
+    got = [None if dev[k] is None else dev[k].cpu().numpy()
+           for k in ("k_pages", "v_pages", "k_scales", "v_scales")]
+    assert_pools_equal(got, want, f"append {kv}")
+    p2 = dict(prob, k_pages=want[0], v_pages=want[1], k_scales=want[2], v_scales=want[3])
+    ro, rl = oracle.decode(p2)
+    compare(o, lse, ro, rl, what=f"decode after append {kv}")
+
+
+def test_append_graph_capture_replay():
+    """Append + decode captured into one HIP graph (first calls of the plan under capture);
+    replays with eager work between them give the eager results bit for bit."""
+    s = workloads.spec(name="graph_append", batch=3, q_per_seq=1, num_qo_heads=16,
+                       num_kv_heads=4, head_dim=128, page_size=16, kv_dtype="i8",
+                       lens=("list", (100, 1500, 3000)))
+    prob = workloads.generate(s, 37)
+    new = workloads.append_tokens(prob, 37, 1)
+    args = [_dev(new[k]) for k in ("k_new", "v_new", "batch_idx", "positions")]
+    plan = make_plan(prob)
+    plan.ensure_workspace()
+    dev = to_dev(prob)
+    out = torch.empty(dev["q"].shape, dtype=torch.float16, device="cuda")
+    lse = torch.empty(dev["q"].shape[:2], dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        plan.append(*args, dev["k_pages"], dev["v_pages"], dev["page_table"], dev["k_scales"],
+                    dev["v_scales"])
+        run(plan, prob, dev, out=out, lse=lse)
+    want = oracle_append(prob, new, plan.params.max_kv_len)
+    p2 = dict(prob, k_pages=want[0], v_pages=want[1], k_scales=want[2], v_scales=want[3])
+    ro, rl = oracle.decode(p2)
+    ref = None
+    for i in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [dev[k].cpu().numpy() for k in ("k_pages", "v_pages", "k_scales", "v_scales")]
+        assert_pools_equal(got, want, f"replay {i}")
+        compare(out, lse, ro, rl, what=f"replay {i}")
+        if ref is None:
+            ref = (out.clone(), lse.clone())
+        else:
+            assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1])
+        torch.ones(1 << 20, device="cuda").sum()  # eager work between replays

@@ -241,6 +241,43 @@ def poison_unread(k, v, ks, vs, table, L, P, spare_pages):
                 vs[last, L[b] % P:] = nan
 
 
+def append_tokens(prob: dict, seed: int, new_per_seq: int):
+    """New K/V rows for an append: the last new_per_seq positions of every sequence (positions
+    kv_len_b - n .. kv_len_b - 1 that exist), visited in a random order. Values are N(0,1)
+    rounded to f16 from streams 6 (K) and 7 (V) of `seed`; the order comes from
+    default_rng((seed, 7)). Returns dict(k_new, v_new [N, Hkv, D] f16, batch_idx, positions
+    [N] int32)."""
+    k = prob["k_pages"]
+    Hkv, D = k.shape[2], k.shape[3]
+    L = np.asarray(prob["kv_len"], np.int64)
+    n = np.minimum(L, int(new_per_seq))
+    bi = np.concatenate([np.full(int(n[b]), b) for b in range(L.shape[0])] + [np.zeros(0)])
+    pos = np.concatenate([np.arange(L[b] - n[b], L[b]) for b in range(L.shape[0])] + [np.zeros(0)])
+    order = np.random.default_rng((seed, 7)).permutation(bi.shape[0])
+    N = int(bi.shape[0])
+    return dict(k_new=_normal_f16(seed, 6, (N, Hkv, D)), v_new=_normal_f16(seed, 7, (N, Hkv, D)),
+                batch_idx=bi[order].astype(np.int32), positions=pos[order].astype(np.int32))
+
+
+# Append workloads: (cache spec, new tokens per sequence). A prefill chunk of 1024 tokens for
+# each of 32 sequences (the GQA batch's cache shape), and one decode step (one token for each
+# of 64 sequences, the int8 batch's cache shape).
+APPEND_CONFIGS = {
+    "prefill_i8": (Spec("append_prefill_i8", 32, 1, 32, 8, 128, 16, "i8", ("fixed", 1024)), 1024),
+    "prefill_f16": (Spec("append_prefill_f16", 32, 1, 32, 8, 128, 16, "f16", ("fixed", 1024)), 1024),
+    "decode_i8": (Spec("append_decode_i8", 64, 1, 32, 8, 128, 16, "i8", ("fixed", 1024)), 1),
+}
+
+
+def append_bytes(prob: dict, new: dict) -> int:
+    """Algorithmic bytes of one append: the new K and V rows read (2*D*2 bytes per token-head)
+    plus the cache written (2*D*2 bytes for f16; 2*(D + 2*D/32) for int8 with f16 scales)."""
+    k = prob["k_pages"]
+    Hkv, D = k.shape[2], k.shape[3]
+    written = 4 * D if k.dtype == np.float16 else 2 * (D + 2 * (D // 32))
+    return int(new["k_new"].shape[0]) * Hkv * (4 * D + written)
+
+
 def kv_bytes(prob: dict) -> int:
     """Algorithmic K+V bytes one decode reads: sum_b kv_len_b * Hkv * row bytes, where a row
     pair is 2*D*2 bytes for f16 and 2*(D + 2*D/32) bytes for int8 with f16 scales."""
