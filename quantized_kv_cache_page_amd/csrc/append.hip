@@ -6,7 +6,9 @@
 // bytes of f16, or 8 bytes of int8 codes), so a row of D elements is D/8 lanes and a wave covers
 // 64*8/D rows; consecutive rows of a [N, Hkv, D] input are consecutive memory, so a wave's loads
 // are one contiguous run. The kernel is a pure stream (read the new rows once, write the slots
-// once); it is bound by HBM, or by launch latency for a decode step's handful of tokens.
+// once, both non-temporal: neither is read again by this kernel, and the decode that reads the
+// slots later comes after many other launches); it is bound by HBM, or by launch latency for a
+// decode step's handful of tokens.
 //
 // int8 (one f16 scale per 32 elements; AMD-Ecosystem/flashinfer PR #397 names append as the op
 // that writes the cache, 1bit-MONSTER/engine issue #115 comment "Fixed" names the q8_0-style KV
@@ -91,11 +93,11 @@ __device__ __forceinline__ void store_row(const AppendLaunch &a, half8a x, void 
   const int64_t off = page * a.page_stride + (int64_t)slot * a.tok_stride +
                       (int64_t)kvh * a.head_stride + part * 8;
   if constexpr (!I8) {
-    *(half8a *)((_Float16 *)pool + off) = x;
+    __builtin_nontemporal_store(x, (half8a *)((_Float16 *)pool + off));
   } else {
     _Float16 sh;
     const uint2a codes = quantize8(x, &sh);
-    *(uint2a *)((int8_t *)pool + off) = codes;
+    __builtin_nontemporal_store(codes, (uint2a *)((int8_t *)pool + off));
     if ((part & 3) == 0) {
       const int64_t soff = page * a.s_page_stride + (int64_t)slot * a.s_tok_stride +
                            (int64_t)kvh * a.s_head_stride + (part >> 2);
