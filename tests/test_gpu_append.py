@@ -249,3 +249,62 @@ def test_append_graph_capture_replay():
         else:
             assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1])
         torch.ones(1 << 20, device="cuda").sum()  # eager work between replays
+
+
+@pytest.mark.parametrize("kv", ["f16", "i8"])
+@pytest.mark.parametrize("form", ["halves", "interleaved", "layer"])
+def test_cache_views(kv, form):
+    """K and V as views of one tensor -- the two halves of [2, pages, ...], the interleaved
+    [pages, 2, ...], layer 1 of a [layers, 2, pages, ...] pool (the layouts AMD-Ecosystem/
+    flashinfer PR #397 tests under "Test plan") -- are addressed through their strides: an
+    append into the views and a decode over them match the oracle, and the other layer and
+    the unused halves keep their bytes."""
+    s = workloads.spec(name=f"views_{form}_{kv}", batch=3, q_per_seq=1, num_qo_heads=16,
+                       num_kv_heads=4, head_dim=128, page_size=16, kv_dtype=kv,
+                       lens=("list", (33, 700, 1500)))
+    prob = workloads.generate(s, 38)
+    new = workloads.append_tokens(prob, 38, 3)
+
+    def combined(k, v):
+        if k is None:
+            return None, None, None
+        if form == "halves":
+            big = np.stack([k, v])                       # [2, N, P, H, X]
+            return big, big[0], big[1]
+        if form == "interleaved":
+            big = np.ascontiguousarray(np.stack([k, v], axis=1))  # [N, 2, P, H, X]
+            return big, big[:, 0], big[:, 1]
+        big = np.stack([np.stack([v, k]), np.stack([k, v])])     # [layers=2, 2, N, P, H, X]
+        return big, big[1, 0], big[1, 1]
+
+    bkv, kview, vview = combined(prob["k_pages"], prob["v_pages"])
+    bsc, ksview, vsview = combined(prob["k_scales"], prob["v_scales"])
+    tk = torch.from_numpy(bkv).cuda()
+    ts = None if bsc is None else torch.from_numpy(bsc).cuda()
+
+    def dev_view(t, npview, base):
+        if t is None:
+            return None
+        off = (npview.__array_interface__["data"][0] - base.__array_interface__["data"][0])
+        st = [x // npview.itemsize for x in npview.strides]
+        return torch.as_strided(t, npview.shape, st, off // npview.itemsize)
+
+    dk, dv = dev_view(tk, kview, bkv), dev_view(tk, vview, bkv)
+    dks = None if ts is None else dev_view(ts, ksview, bsc)
+    dvs = None if ts is None else dev_view(ts, vsview, bsc)
+    plan = make_plan(prob)
+    tab, kvl, q = _dev(prob["page_table"]), _dev(prob["kv_len"]), _dev(prob["q"])
+    plan.append(_dev(new["k_new"]), _dev(new["v_new"]), _dev(new["batch_idx"]),
+                _dev(new["positions"]), dk, dv, tab, dks, dvs)
+    o, lse = plan.run(q, dk, dv, tab, kvl, prob["sm_scale"], dks, dvs)
+    torch.cuda.synchronize()
+    want = oracle_append(prob, new, plan.params.max_kv_len)
+    got = [None if t is None else t.cpu().numpy() for t in (dk, dv, dks, dvs)]
+    assert_pools_equal(got, want, f"views {form} {kv}")
+    if form == "layer":  # layer 0 untouched
+        assert np.array_equal(tk[0].cpu().numpy().view(np.uint8), bkv[0].view(np.uint8))
+        if ts is not None:
+            assert np.array_equal(ts[0].cpu().numpy().view(np.uint8), bsc[0].view(np.uint8))
+    p2 = dict(prob, k_pages=want[0], v_pages=want[1], k_scales=want[2], v_scales=want[3])
+    ro, rl = oracle.decode(p2)
+    compare(o, lse, ro, rl, what=f"decode over views {form} {kv}")
