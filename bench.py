@@ -3,6 +3,7 @@
 
     python bench.py [--steps K] [--warmup W] [--config 2] [--gpus 1] [--no-cpu]
     python bench.py --op append [--append prefill_i8|prefill_f16|decode_i8]
+    python bench.py --op prefill [--prefill prompt_i8|prompt_f16]
 
 A step is one decode call (partial kernel + reducer) over one batch of the workload, with
 all inputs resident in HBM. The default workload is the GQA batch decode (B=32, 32 query /
@@ -285,6 +286,106 @@ def cpu_baseline_append(prob, new, max_len, budget_s=8.0):
                       f"tokens), median {t:.3f} s each (pool copies included)"}
 
 
+PREFILL_METRIC = ("prefill µs/call and achieved TFLOP/s (causal attention FLOPs, 4*D per visible "
+                  "query-position pair) vs MFMA roofline")
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense f16 matrix peak
+
+
+def time_prefill(name, seed, steps, warmup):
+    """Time skvd_prefill on one prefill workload (inputs resident in HBM; compute-bound, so no
+    copies rotate). Returns measurements and the problem."""
+    import numpy as np
+    import torch
+    import quantized_kv_cache_page_amd as skvd
+    import workloads
+    spec = workloads.PREFILL_CONFIGS[name]
+    prob = workloads.generate(spec, seed)
+    flops = workloads.attention_flops(prob)
+    dev = torch.device("cuda:0")
+
+    def up(x):
+        return None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    t = {k: up(prob[k]) for k in ("q", "k_pages", "v_pages", "k_scales", "v_scales",
+                                  "page_table", "kv_len")}
+    plan = skvd.Plan(spec.num_qo_heads, spec.num_kv_heads, spec.head_dim, spec.page_size,
+                     spec.kv_dtype, spec.batch, 1, spec.max_kv_len, device=0)
+    out = torch.empty(t["q"].shape, dtype=torch.float16, device=dev)
+    lse = torch.empty(t["q"].shape[:2], dtype=torch.float32, device=dev)
+
+    def call():
+        plan.prefill(t["q"], t["k_pages"], t["v_pages"], t["page_table"], t["kv_len"],
+                     prob["sm_scale"], t["k_scales"], t["v_scales"], out=out, lse=lse,
+                     q_per_seq=spec.q_per_seq)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    # one event pair on the launching stream around back-to-back calls (one kernel each)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / steps * 1e3
+    workload = (f"{spec.name}: B={spec.batch} prompts of T={spec.q_per_seq} tokens over "
+                f"kv_len={spec.lens[1]} (full causal), Hq={spec.num_qo_heads} "
+                f"Hkv={spec.num_kv_heads} D={spec.head_dim} P={spec.page_size} kv={spec.kv_dtype}")
+    return dict(workload=workload, us_per_call=us, flops=flops,
+                tflops=flops / (us * 1e-6) / 1e12, seed=seed), prob
+
+
+def cpu_baseline_prefill(prob, budget_s=10.0, nrows=256):
+    """The oracle on all host cores over a bounded sample of rows of the same workload; FLOPs
+    of those rows (4*D per visible position) per second."""
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(0)
+    total = prob["q"].shape[0] * prob["q"].shape[1]
+    rows = rng.choice(total, size=min(nrows, total), replace=False)
+    Hq, T, D = prob["q"].shape[1], int(prob["q_per_seq"]), prob["k_pages"].shape[3]
+    L = np.asarray(prob["kv_len"], np.int64)
+    bt = rows // Hq
+    vis = np.clip(L[bt // T] - T + (bt % T) + 1, 0, None)
+    flops = 4 * D * int(vis.sum())
+    times = []
+    t_end = time.time() + budget_s
+    while True:
+        t0 = time.time()
+        oracle.decode(prob, rows=rows)
+        times.append(time.time() - t0)
+        if time.time() > t_end or len(times) >= 20:
+            break
+    t = float(np.median(times))
+    return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "sample": f"{len(rows)} random rows of the workload, median "
+                                        f"{t:.3f} s per pass, fp64"}
+
+
+def bench_prefill(args):
+    seed = 50 if args.seed is None else args.seed
+    r, prob = time_prefill(args.prefill, seed, args.steps, args.warmup)
+    import workloads
+    spec = workloads.PREFILL_CONFIGS[args.prefill]
+    res = {
+        "metric": PREFILL_METRIC, "value": round(r["tflops"], 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["us_per_call"] / 1e3, 5),
+        "us_per_call": round(r["us_per_call"], 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": r["workload"], "seed": seed, "flops_per_call": r["flops"]},
+        "roofline": {"bound": "mfma", "achieved": round(r["tflops"], 2),
+                     "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(r["tflops"] / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "prefill_kernel", "kernel_avg_us": round(r["us_per_call"], 3),
+                     "algorithmic_flops_per_launch": r["flops"]},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline_prefill(prob)
+    print(json.dumps(res), flush=True)
+
+
 def bench_append(args):
     import workloads
     seed = 40 if args.seed is None else args.seed
@@ -315,7 +416,9 @@ def bench_append(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--op", choices=["decode", "append"], default="decode")
+    ap.add_argument("--op", choices=["decode", "append", "prefill"], default="decode")
+    ap.add_argument("--prefill", default="prompt_i8",
+                    help="prefill workload for --op prefill: prompt_i8, prompt_f16")
     ap.add_argument("--append", default="prefill_i8",
                     help="append workload for --op append: prefill_i8, prefill_f16, decode_i8")
     ap.add_argument("--no-append", action="store_true",
@@ -363,6 +466,8 @@ def main():
         return sweep(args)
     if args.op == "append":
         return bench_append(args)
+    if args.op == "prefill":
+        return bench_prefill(args)
 
     import numpy as np
     import torch

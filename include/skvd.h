@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define SKVD_ABI_VERSION 5
+#define SKVD_ABI_VERSION 6
 
 typedef enum {
   SKVD_OK = 0,
@@ -250,6 +250,32 @@ skvd_status skvd_gather_debug(const skvd_plan *plan, const skvd_decode_args *arg
  * a multiple of 16; sink is a device uint32 that the kernel may write (keeps the loads live).
  * Asynchronous on `stream`. */
 skvd_status skvd_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *stream);
+
+/* --------------------------------------------------------------------------- prefill
+ * The multi-token route: any number T >= 1 of query tokens per sequence (prompt processing,
+ * long speculative drafts) over the same paged cache, with the same arguments, result, causal
+ * reading and output layout as skvd_decode (the T query tokens are the last T cached positions;
+ * token t sees positions j <= kv_len[b] - T + t). llama-cpp-turboquant PR #176 ("HIP: fix turbo
+ * KV decode crash under graph capture; batch-aware VEC/TILE FA routing", section "Changes")
+ * keeps the vector decode for at most 8 query tokens and routes larger batches to a tiled
+ * matrix-core kernel; its tiled path first dequantized the quantized cache into f16 buffers.
+ * This route is one tiled MFMA kernel that reads the pages itself and widens int8 (value =
+ * int8 * f16 scale per 32 elements) on the way into LDS: no f16 temporary, no workspace.
+ *
+ * - args: as skvd_decode_args, with q_per_seq = T in 1..max_kv_len (not bounded by the plan's
+ *   max_q_per_seq); batch <= max_batch; o [B*T, Hq, D] f16 dense and lse [B*T, Hq] f32 (may be
+ *   NULL) are written, nothing else. The plan's Hq / Hkv must be <= 64.
+ * - Device-data contract: T <= kv_len[b] <= max_kv_len. Rows that see no position (kv_len[b] <
+ *   T) get o = 0 and lse = -inf; kv_len is clamped and page ids are clamped into the pools as in
+ *   the decode.
+ * - Graph capture: no allocation, synchronization or device-to-host read; one kernel launch. */
+
+/* Validation alone: the checks skvd_prefill makes before launching, with no HIP call. */
+skvd_status skvd_prefill_check(const skvd_plan *plan, const skvd_decode_args *args);
+
+/* Prefill: one kernel on `stream` (a hipStream_t; NULL is the null stream), asynchronous. The
+ * current HIP device must be the plan's device. Errors as for skvd_decode. */
+skvd_status skvd_prefill(const skvd_plan *plan, const skvd_decode_args *args, void *stream);
 
 /* ---------------------------------------------------------------------------- append
  * Writing new tokens into the paged cache: the step right before a decode, and the one

@@ -1,7 +1,7 @@
 """Split-KV paged decode attention for MI355X (gfx950).
 
-The decode, and the append that writes new tokens into the cache, run in hand-written HIP
-kernels behind the C ABI of ``include/skvd.h`` (``libskvd.so``, built in-tree by
+The decode, the multi-token (prefill) route and the append that writes new tokens into the
+cache run in hand-written HIP kernels behind the C ABI of ``include/skvd.h`` (``libskvd.so``, built in-tree by
 ``python -m quantized_kv_cache_page_amd.build``). This package is its thin Python face: ``Plan`` marshals torch tensors into those calls, and the
 ``skvd_*`` functions are the C-ABI entry points under the same names.
 """
@@ -12,5 +12,6 @@ from ._binding import (  # noqa: F401
     skvd_plan_create, skvd_plan_describe, skvd_plan_destroy, skvd_plan_get_info,
     skvd_plan_params, skvd_plan_workspace_bytes, skvd_decode_args, status_string,
     skvd_stream_read, stream_read, skvd_append, skvd_append_check, skvd_append_args,
+    skvd_prefill, skvd_prefill_check,
     STATUS_KV_LEN_CLAMPED, STATUS_PAGE_CLAMPED,
 )

@@ -21,7 +21,7 @@ REDUCERS = {"auto": 0, "direct": 1, "cooperative": 2, "multipass": 3, "hierarchi
 REDUCER_NAMES = {v: k for k, v in REDUCERS.items()}
 SCHEDULES = {"auto": 0, "static": 1, "balanced": 2}
 SCHEDULE_NAMES = {v: k for k, v in SCHEDULES.items()}
-ABI_VERSION = 5
+ABI_VERSION = 6
 STATUS_KV_LEN_CLAMPED = 0x1
 STATUS_PAGE_CLAMPED = 0x2
 
@@ -108,6 +108,8 @@ SIGNATURES = {
                                          ctypes.c_void_p, ctypes.c_void_p]),
     "skvd_stream_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                         ctypes.c_void_p]),
+    "skvd_prefill_check": (ctypes.c_int, [_PLAN_P, ctypes.POINTER(skvd_decode_args)]),
+    "skvd_prefill": (ctypes.c_int, [_PLAN_P, ctypes.POINTER(skvd_decode_args), ctypes.c_void_p]),
     "skvd_append_check": (ctypes.c_int, [_PLAN_P, ctypes.POINTER(skvd_append_args)]),
     "skvd_append": (ctypes.c_int, [_PLAN_P, ctypes.POINTER(skvd_append_args), ctypes.c_void_p]),
     "skvd_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -214,6 +216,14 @@ def skvd_decode_merge(plan, args, workspace, workspace_bytes, stream) -> int:
 def skvd_gather_debug(plan, args, max_len, dk, dv, dks, dvs, stream) -> int:
     return int(lib().skvd_gather_debug(plan, ctypes.byref(args), max_len, dk, dv, dks, dvs,
                                        stream))
+
+
+def skvd_prefill_check(plan, args) -> int:
+    return int(lib().skvd_prefill_check(plan, ctypes.byref(args)))
+
+
+def skvd_prefill(plan, args, stream) -> int:
+    return int(lib().skvd_prefill(plan, ctypes.byref(args), stream))
 
 
 def skvd_append_check(plan, args) -> int:
@@ -399,6 +409,23 @@ class Plan:
                            out, lse, q_per_seq)
         return skvd_decode_check(self.handle, a, self.workspace_bytes if workspace_bytes is None
                                  else workspace_bytes)
+
+    def prefill(self, q, k_pages, v_pages, page_table, kv_len, sm_scale, k_scales=None,
+                v_scales=None, out=None, lse=None, q_per_seq=1, stream=None):
+        """skvd_prefill: the multi-token route (any q_per_seq = T >= 1; same arguments, causal
+        reading and outputs as run()). Returns (o [B*T, Hq, D] f16, lse [B*T, Hq] f32)."""
+        out, lse = self._outputs(q, out, lse)
+        a = self.make_args(q, k_pages, v_pages, page_table, kv_len, sm_scale, k_scales, v_scales,
+                           out, lse, q_per_seq)
+        _check(skvd_prefill(self.handle, a, self._stream(stream)), "skvd_prefill")
+        return out, lse
+
+    def prefill_check(self, q, k_pages, v_pages, page_table, kv_len, sm_scale, k_scales=None,
+                      v_scales=None, out=None, lse=None, q_per_seq=1) -> int:
+        """skvd_prefill_check: the validation alone, no HIP call. Returns the status."""
+        a = self.make_args(q, k_pages, v_pages, page_table, kv_len, sm_scale, k_scales, v_scales,
+                           out, lse, q_per_seq)
+        return skvd_prefill_check(self.handle, a)
 
     def make_append_args(self, k_new, v_new, batch_idx, positions, k_pages, v_pages, page_table,
                          k_scales=None, v_scales=None, batch=None) -> skvd_append_args:

@@ -102,6 +102,23 @@ skvd_status check_append(const skvd_plan *plan, const skvd_append_args *a) {
   return SKVD_OK;
 }
 
+// skvd_prefill's host checks: the decode's layout and shape checks with any number of query
+// tokens per sequence (1..max_kv_len) and no workspace; G <= 64 (a workgroup's 64 rows).
+skvd_status check_prefill(const skvd_plan *plan, const skvd_decode_args *a) {
+  g_err[0] = 0;
+  if (!plan) return set_err(SKVD_ERR_NULL, "plan is NULL");
+  if (!a) return set_err(SKVD_ERR_NULL, "args is NULL");
+  const skvd::Plan &p = plan->p;
+  if (a->q_per_seq < 1 || a->q_per_seq > p.prm.max_kv_len)
+    return set_err(SKVD_ERR_SHAPE, "q_per_seq=%d outside 1..max_kv_len=%d", a->q_per_seq,
+                   p.prm.max_kv_len);
+  if (p.group > 64)
+    return set_err(SKVD_ERR_SHAPE, "prefill needs Hq/Hkv <= 64 (got %d)", p.group);
+  skvd_decode_args one = *a;
+  one.q_per_seq = 1;  // the remaining checks do not depend on the token count
+  return skvd::check_args(p, &one, p.ws_bytes, g_err, sizeof g_err);
+}
+
 }  // namespace
 
 extern "C" {
@@ -267,6 +284,28 @@ skvd_status skvd_gather_debug(const skvd_plan *plan, const skvd_decode_args *arg
   la.debug = 0;
   int e = skvd::launch_gather(plan->p, la, max_len, dense_k, dense_v, dense_ks, dense_vs, stream);
   return e ? hip_err(e, "gather kernel launch") : SKVD_OK;
+}
+
+skvd_status skvd_prefill_check(const skvd_plan *plan, const skvd_decode_args *args) {
+  return check_prefill(plan, args);
+}
+
+skvd_status skvd_prefill(const skvd_plan *plan, const skvd_decode_args *args, void *stream) {
+  skvd_status st = check_prefill(plan, args);
+  if (st != SKVD_OK) return st;
+  int dev = -1;
+  hipError_t he = hipGetDevice(&dev);
+  if (he != hipSuccess) {
+    (void)hipGetLastError();
+    return set_err(SKVD_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(he));
+  }
+  if (dev != plan->p.prm.device)
+    return set_err(SKVD_ERR_DEVICE, "current device %d is not the plan's device %d", dev,
+                   plan->p.prm.device);
+  skvd::LaunchArgs la;
+  skvd::fill_launch_args(plan->p, *args, nullptr, &la);
+  const int e = skvd::launch_prefill(la, stream);
+  return e ? hip_err(e, "prefill kernel launch") : SKVD_OK;
 }
 
 skvd_status skvd_append_check(const skvd_plan *plan, const skvd_append_args *args) {

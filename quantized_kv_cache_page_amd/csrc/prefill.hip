@@ -1,0 +1,299 @@
+// Prefill / multi-token route: T > 8 query tokens per sequence against the paged cache, as MFMA
+// tiles with the int8 cache dequantized on its way into LDS (no f16 temporary in memory).
+//
+// llama-cpp-turboquant PR #176 ("HIP: fix turbo KV decode crash under graph capture;
+// batch-aware VEC/TILE FA routing", section "Changes") keeps the vector decode path for at most
+// 8 query tokens and sends larger batches to the tiled matrix-core kernel; its tiled path
+// dequantized the whole cache into K_f16/V_f16 buffers first. Here the tile kernel reads the
+// pages itself and widens int8 in registers.
+//
+// Work unit: one workgroup of 4 waves per (sequence b, KV head, tile of query tokens). Its 64
+// query rows are (token, head-of-group) pairs r = token * G + g, so every wave reads the same
+// KV head: K and V tiles of KT tokens are gathered through the page table into LDS once and
+// shared by the 4 waves (16 rows each). Per KV tile a wave computes S^T = K Q^T with the
+// 16x16x32 f16 MFMA (A = 16 K rows from LDS, B = the wave's 16 query rows, held in registers),
+// so each lane holds one query row's scores (column lane % 16) for 4 tokens per 16-token
+// sub-tile; the online softmax (base 2) needs only per-lane work plus two cross-lane steps for
+// the max; the probabilities are already the B operand of O^T = V^T P^T, whose A operand (16
+// head_dim rows x 32 tokens of V) comes from LDS through transposing reads
+// (ds_read_b64_tr_b16). The token order inside the contraction is the one the score layout
+// gives (tokens 4g..4g+3 and 16+4g..16+4g+3 for lane group g); both operands use it.
+//
+// Causal reading (the decode's): the T query tokens are the last T cached positions, token t
+// sees positions j <= kv_len - T + t. A workgroup walks positions [0, kv_len - T + t_last] in
+// tiles; the next tile's rows are loaded into registers while the current one is computed.
+// Workgroups run heaviest (latest query tiles) first.
+#include <hip/hip_runtime.h>
+
+#include "skvd_internal.h"
+
+namespace skvd {
+namespace {
+
+typedef _Float16 ph8 __attribute__((ext_vector_type(8)));
+typedef _Float16 ph4 __attribute__((ext_vector_type(4)));
+typedef float pf4 __attribute__((ext_vector_type(4)));
+typedef short ps4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) ps4 *lds_ps4;
+typedef unsigned pu4 __attribute__((ext_vector_type(4)));
+
+constexpr float kPNegInf = -__builtin_huge_valf();
+constexpr float kPLn2 = 0.6931471805599453f;
+constexpr float kMFloor = -1e30f;  // running max before any visible score (keeps exp2 finite)
+
+// Byte offset of 16-byte chunk c of row r in an LDS tile with rows of ROWB bytes; the chunk is
+// XOR-swizzled by the row so that 16 rows read at one column hit different banks.
+template <int ROWB>
+__device__ __forceinline__ int pswz(int r, int c) {
+  return r * ROWB + ((c ^ (r & 15)) << 4);
+}
+
+template <int D>
+constexpr int kv_tile() { return D == 128 ? 64 : 32; }
+
+// One KV tile's rows held in registers between the global load and the LDS store.
+template <int D, bool I8>
+struct TileRegs {
+  static constexpr int KT = kv_tile<D>();
+  // f16: 16-byte chunks of 8 elements; int8: 16-byte chunks of 16 elements (+ their scale)
+  static constexpr int CPR = I8 ? D / 16 : D / 8;  // chunks per row
+  static constexpr int N = KT * CPR / 256;         // chunks per thread per tensor
+  pu4 k[N], v[N];
+  _Float16 ks[I8 ? N : 1], vs[I8 ? N : 1];
+};
+
+template <int D, bool I8>
+__device__ __forceinline__ void load_tile(const LaunchArgs &a, int b, int kvh, int kv0, int kv_last,
+                                          TileRegs<D, I8> &r) {
+  using TR = TileRegs<D, I8>;
+  const int P1 = (1 << a.page_shift) - 1;
+#pragma unroll
+  for (int n = 0; n < TR::N; ++n) {
+    const int i = threadIdx.x + 256 * n;
+    const int tok = min(kv0 + i / TR::CPR, kv_last);  // the tail re-reads the last row (masked)
+    const int part = i % TR::CPR;
+    int64_t pg = a.table[(int64_t)b * a.table_stride + (tok >> a.page_shift)];
+    const int64_t pk = pg < 0 ? 0 : (pg >= a.num_k_pages ? a.num_k_pages - 1 : pg);
+    const int64_t pv = pg < 0 ? 0 : (pg >= a.num_v_pages ? a.num_v_pages - 1 : pg);
+    const int64_t rk = pk * a.page_stride + (int64_t)(tok & P1) * a.tok_stride +
+                       (int64_t)kvh * a.head_stride;
+    const int64_t rv = pv * a.page_stride + (int64_t)(tok & P1) * a.tok_stride +
+                       (int64_t)kvh * a.head_stride;
+    if constexpr (!I8) {
+      r.k[n] = __builtin_nontemporal_load((const pu4 *)((const _Float16 *)a.k + rk + 8 * part));
+      r.v[n] = __builtin_nontemporal_load((const pu4 *)((const _Float16 *)a.v + rv + 8 * part));
+    } else {
+      r.k[n] = __builtin_nontemporal_load((const pu4 *)((const int8_t *)a.k + rk + 16 * part));
+      r.v[n] = __builtin_nontemporal_load((const pu4 *)((const int8_t *)a.v + rv + 16 * part));
+      const int64_t sk = pk * a.s_page_stride + (int64_t)(tok & P1) * a.s_tok_stride +
+                         (int64_t)kvh * a.s_head_stride + (part >> 1);
+      const int64_t sv = pv * a.s_page_stride + (int64_t)(tok & P1) * a.s_tok_stride +
+                         (int64_t)kvh * a.s_head_stride + (part >> 1);
+      r.ks[n] = ((const _Float16 *)a.ks)[sk];
+      r.vs[n] = ((const _Float16 *)a.vs)[sv];
+    }
+  }
+}
+
+// 16 signed bytes -> two groups of 8 f16, each times the f16 scale (one rounding, as the
+// decode's K path).
+__device__ __forceinline__ void widen16(pu4 w, _Float16 s, ph8 *lo, ph8 *hi) {
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int byte = (int)(signed char)(w[e >> 2] >> (8 * (e & 3)));
+    const _Float16 x = (_Float16)byte * s;
+    if (e < 8) (*lo)[e] = x;
+    else (*hi)[e - 8] = x;
+  }
+}
+
+template <int D, bool I8>
+__device__ __forceinline__ void store_tile(char *k_lds, char *v_lds, const TileRegs<D, I8> &r) {
+  using TR = TileRegs<D, I8>;
+  constexpr int ROWB = D * 2;
+#pragma unroll
+  for (int n = 0; n < TR::N; ++n) {
+    const int i = threadIdx.x + 256 * n;
+    const int tok = i / TR::CPR, part = i % TR::CPR;
+    if constexpr (!I8) {
+      *(pu4 *)(k_lds + pswz<ROWB>(tok, part)) = r.k[n];
+      *(pu4 *)(v_lds + pswz<ROWB>(tok, part)) = r.v[n];
+    } else {
+      ph8 lo, hi;
+      widen16(r.k[n], r.ks[n], &lo, &hi);
+      *(ph8 *)(k_lds + pswz<ROWB>(tok, 2 * part)) = lo;
+      *(ph8 *)(k_lds + pswz<ROWB>(tok, 2 * part + 1)) = hi;
+      widen16(r.v[n], r.vs[n], &lo, &hi);
+      *(ph8 *)(v_lds + pswz<ROWB>(tok, 2 * part)) = lo;
+      *(ph8 *)(v_lds + pswz<ROWB>(tok, 2 * part + 1)) = hi;
+    }
+  }
+}
+
+template <int D, bool I8>
+__global__ __launch_bounds__(256) void prefill_kernel(LaunchArgs a, int tpw) {
+  constexpr int KT = kv_tile<D>();
+  constexpr int NST = KT / 16;   // 16-token score sub-tiles per KV tile
+  constexpr int NCH = KT / 32;   // 32-token P.V chunks per KV tile
+  constexpr int NKS = D / 32;    // contraction steps over head_dim
+  constexpr int NDT = D / 16;    // 16-wide head_dim tiles of the output
+  constexpr int ROWB = D * 2;
+  __shared__ __attribute__((aligned(16))) char k_lds[KT * ROWB];
+  __shared__ __attribute__((aligned(16))) char v_lds[KT * ROWB];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c16 = lane & 15, g4 = lane >> 4;
+  const int b = blockIdx.z, kvh = blockIdx.y;
+  const int qt = gridDim.x - 1 - blockIdx.x;  // heaviest query tiles first
+  const int G = a.G, T = a.T;
+  int L = a.kv_len[b];
+  L = L < 0 ? 0 : (L > a.max_kv_len ? a.max_kv_len : L);
+  const int t0 = qt * tpw;
+  const int t_last = min(t0 + tpw, T) - 1;
+  const int kv_end = min(L, L - T + t_last + 1);  // positions [0, kv_end) are visited
+
+  // this lane's query row: column c16 of the wave's 16 (rows r = token * G + head)
+  const int r = 16 * w + c16;
+  const int tl = r / G;
+  const int gh = r - tl * G;
+  const bool row_ok = tl < tpw && t0 + tl < T;
+  const int t = row_ok ? t0 + tl : t_last;
+  const int h = kvh * G + gh;
+  const int limit = L - T + t;  // last visible position of the row
+
+  ph8 qv[NKS];
+  {
+    const _Float16 *qp = (const _Float16 *)a.q + ((int64_t)b * T + t) * a.q_tok_stride +
+                         (int64_t)h * a.q_head_stride + 8 * g4;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qv[ks] = *(const ph8 *)(qp + 32 * ks);
+  }
+
+  pf4 acc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) acc[dt] = pf4{0.f, 0.f, 0.f, 0.f};
+  float m = kMFloor, l = 0.f;
+
+  const int ntiles = kv_end > 0 ? (kv_end + KT - 1) / KT : 0;
+  TileRegs<D, I8> regs;
+  if (ntiles > 0) {
+    load_tile<D, I8>(a, b, kvh, 0, kv_end - 1, regs);
+    store_tile<D, I8>(k_lds, v_lds, regs);
+  }
+  __syncthreads();
+  for (int it = 0; it < ntiles; ++it) {
+    const int kv0 = it * KT;
+    const bool more = it + 1 < ntiles;
+    if (more) load_tile<D, I8>(a, b, kvh, kv0 + KT, kv_end - 1, regs);
+
+    // ---- S^T = K Q^T: lane holds row c16's scores for tokens 16 st + 4 g4 + e
+    pf4 s[NST];
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      s[st] = pf4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const ph8 kf = *(const ph8 *)(k_lds + pswz<ROWB>(16 * st + c16, 4 * ks + g4));
+        s[st] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qv[ks], s[st], 0, 0, 0);
+      }
+    }
+    // ---- mask, scale (base 2), online softmax
+    float mx = kPNegInf;
+#pragma unroll
+    for (int st = 0; st < NST; ++st)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int pos = kv0 + 16 * st + 4 * g4 + e;
+        const float v = pos <= limit ? s[st][e] * a.scale_log2 : kPNegInf;
+        s[st][e] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+    m = m_new;
+    float ls = 0.f;
+#pragma unroll
+    for (int st = 0; st < NST; ++st)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p = __builtin_amdgcn_exp2f(s[st][e] - m_new);
+        s[st][e] = p;
+        ls += p;
+      }
+    l = l * alpha + ls;
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[dt][e] *= alpha;
+    }
+    // ---- O^T += V^T P^T, 32 tokens per MFMA
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      ph8 pb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pb[e] = (_Float16)s[2 * c][e];
+        pb[4 + e] = (_Float16)s[2 * c + 1][e];
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        ph8 va;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          // lane (g4, c16) receives column 16 dt + c16 of tokens 32 c + 16 hh + 4 g4 + 0..3
+          const int row = 32 * c + 16 * hh + 4 * g4 + (c16 >> 2);
+          const int col = 16 * dt + 4 * (c16 & 3);
+          const ps4 r4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_ps4)(v_lds + pswz<ROWB>(row, col >> 3) + ((col & 7) << 1)));
+          const ph4 hv = __builtin_bit_cast(ph4, r4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) va[4 * hh + e] = hv[e];
+        }
+        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, acc[dt], 0, 0, 0);
+      }
+    }
+    __syncthreads();  // every wave is done with this tile's LDS
+    if (more) store_tile<D, I8>(k_lds, v_lds, regs);
+    __syncthreads();
+  }
+
+  // ---- epilogue: row sums across the four lane groups, normalize, write o and lse
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (!row_ok) return;
+  const int64_t orow = ((int64_t)b * T + t) * a.Hq + h;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  _Float16 *op = (_Float16 *)a.o + orow * D + 4 * g4;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    ph4 ov;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ov[e] = (_Float16)(acc[dt][e] * inv);
+    *(ph4 *)(op + 16 * dt) = ov;
+  }
+  if (g4 == 0 && a.lse) a.lse[orow] = l > 0.f ? (m + __log2f(l)) * kPLn2 : kPNegInf;
+}
+
+template <int D>
+void launch_pd(const LaunchArgs &a, int tpw, hipStream_t st) {
+  const dim3 grid((a.T + tpw - 1) / tpw, a.Hkv, a.batch);
+  if (a.int8) prefill_kernel<D, true><<<grid, 256, 0, st>>>(a, tpw);
+  else prefill_kernel<D, false><<<grid, 256, 0, st>>>(a, tpw);
+}
+
+}  // namespace
+
+int launch_prefill(const LaunchArgs &a, void *stream) {
+  if (a.batch == 0) return 0;
+  const int tpw = 64 / a.G;  // query tokens per workgroup: 64 rows of (token, head) pairs
+  hipStream_t st = (hipStream_t)stream;
+  if (a.D == 128) launch_pd<128>(a, tpw, st);
+  else launch_pd<256>(a, tpw, st);
+  return (int)hipGetLastError();
+}
+
+}  // namespace skvd

@@ -102,6 +102,9 @@ struct AppendLaunch {
   unsigned blocks;      // 256-lane workgroups launched
 };
 
+// prefill.hip: the multi-token route (T > 8) over the decode's LaunchArgs; no workspace.
+int launch_prefill(const LaunchArgs &la, void *stream);
+
 // append.hip
 constexpr int kAppendTokensPerLane = 4;  // tokens one append lane serves per round
 int launch_append(const AppendLaunch &a, void *stream);

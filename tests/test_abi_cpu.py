@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol():
     for s in syms:
         assert hasattr(L, s), s
     assert set(syms) == set(bd.SIGNATURES), set(syms) ^ set(bd.SIGNATURES)
-    assert L.skvd_abi_version() == bd.ABI_VERSION == 5
+    assert L.skvd_abi_version() == bd.ABI_VERSION == 6
 
 
 def plan(**kw):
@@ -273,3 +273,15 @@ def test_append_check_int8(over, status):
 
 def test_append_check_null_plan():
     assert bd.skvd_append_check(None, good_append_args()) == 1
+
+
+@pytest.mark.parametrize("over,status", [
+    ({}, 0), (dict(q_per_seq=8), 0), (dict(q_per_seq=4096), 0), (dict(q_per_seq=1), 0),
+    (dict(q_per_seq=0), 2), (dict(q_per_seq=4097), 2), (dict(batch=33), 2),
+    (dict(q=None), 1), (dict(q_head_stride=100), 3), (dict(k_scales=FAKE), 4),
+])
+def test_prefill_check(over, status):
+    """The prefill route takes any token count up to max_kv_len and needs no workspace."""
+    p = plan()
+    a = good_args(p, **dict(dict(q_per_seq=512), **over))
+    assert bd.skvd_prefill_check(p.handle, a) == status

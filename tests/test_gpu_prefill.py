@@ -1,0 +1,137 @@
+"""GPU parity of the multi-token (prefill) route: the MFMA tile kernel through the C ABI against
+the fp64 oracle, whose causal reading (token t of T sees positions j <= kv_len - T + t) is the
+decode's and is pinned at long T against torch's SDPA. Tolerances as for the decode: max|do| <=
+2e-3, max|dlse| <= 1e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.gpu_util import compare, make_plan, run, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import quantized_kv_cache_page_amd as skvd
+    skvd.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def prefill(plan, prob, dev, out=None, lse=None):
+    return plan.prefill(dev["q"], dev["k_pages"], dev["v_pages"], dev["page_table"],
+                        dev["kv_len"], prob["sm_scale"], dev["k_scales"], dev["v_scales"],
+                        out=out, lse=lse, q_per_seq=int(prob["q_per_seq"]))
+
+
+def check(s, seed, rows=None):
+    prob = workloads.generate(s, seed)
+    say(f"case {s.name}: B={s.batch} T={s.q_per_seq} Hq={s.num_qo_heads} Hkv={s.num_kv_heads} "
+        f"D={s.head_dim} P={s.page_size} kv={s.kv_dtype} L={list(prob['kv_len'])[:8]}")
+    dev = to_dev(prob)
+    plan = make_plan(prob, max_q_per_seq=1)  # the prefill route is not bounded by max_q_per_seq
+    o, lse = prefill(plan, prob, dev)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode(prob, rows=rows)
+    compare(o, lse, ro, rl, rows=rows, what=s.name)
+    return prob, dev, plan, o, lse
+
+
+CASES = [
+    # (name, B, T, Hq, Hkv, D, P, kv, lens)
+    ("gqa4_full_causal", 2, 37, 8, 2, 128, 16, "f16", (37, 300)),
+    ("gqa4_i8", 1, 100, 32, 8, 128, 16, "i8", (1000,)),
+    ("mha_p1", 3, 9, 4, 4, 128, 1, "f16", (9, 64, 129)),
+    ("gqa8_d256", 2, 64, 16, 2, 256, 16, "f16", (64, 500)),
+    ("mha_d256_i8_p4", 2, 50, 8, 8, 256, 4, "i8", (50, 777)),
+    ("gqa16", 1, 20, 32, 2, 128, 16, "f16", (700,)),
+    ("gqa4_t1", 2, 1, 8, 2, 128, 16, "f16", (1, 200)),
+    ("gqa4_i8_p64_ragged", 4, 70, 16, 4, 128, 64, "i8", (70, 71, 135, 2049)),
+    ("gqa2_many_tiles", 1, 300, 8, 4, 128, 16, "f16", (4100,)),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_prefill_matches_oracle(case):
+    name, B, T, Hq, Hkv, D, P, kv, lens = case
+    s = workloads.spec(name=name, batch=B, q_per_seq=T, num_qo_heads=Hq, num_kv_heads=Hkv,
+                       head_dim=D, page_size=P, kv_dtype=kv, lens=("list", lens))
+    check(s, 61)
+
+
+def test_prefill_rows_without_positions():
+    """kv_len below T (a contract violation): rows that see no position get o = 0, lse = -inf."""
+    s = workloads.spec(name="short", batch=2, q_per_seq=8, num_qo_heads=8, num_kv_heads=2,
+                       head_dim=128, page_size=16, kv_dtype="f16", lens=("list", (5, 40)))
+    prob, dev, plan, o, lse = check(s, 62)
+    ls = lse.cpu().numpy().reshape(2, 8, 8)
+    assert np.isneginf(ls[0, :3]).all() and np.isfinite(ls[0, 3:]).all()
+    assert (o.reshape(2, 8, 8, 128)[0, :3] == 0).all()
+
+
+def test_prefill_equals_decode_route():
+    """For T <= 8 both routes compute the same attention: each matches the oracle, and they agree
+    with each other within the tolerance."""
+    s = workloads.spec(name="routes", batch=3, q_per_seq=4, num_qo_heads=16, num_kv_heads=4,
+                       head_dim=128, page_size=16, kv_dtype="i8", lens=("list", (4, 900, 3000)))
+    prob, dev, plan, o1, l1 = check(s, 63)
+    plan2 = make_plan(prob)
+    o2, l2 = run(plan2, prob, dev)
+    torch.cuda.synchronize()
+    assert float((o1.float() - o2.float()).abs().max()) <= 2e-3
+    assert float((l1 - l2).abs().max()) <= 1e-3
+
+
+def test_prefill_deterministic():
+    s = workloads.spec(name="det", batch=2, q_per_seq=33, num_qo_heads=8, num_kv_heads=2,
+                       head_dim=128, page_size=16, kv_dtype="f16", lens=("list", (33, 500)))
+    prob, dev, plan, o1, l1 = check(s, 64)
+    o2, l2 = prefill(plan, prob, dev)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_prefill_graph_capture_replay():
+    s = workloads.spec(name="graph_prefill", batch=2, q_per_seq=40, num_qo_heads=8,
+                       num_kv_heads=2, head_dim=128, page_size=16, kv_dtype="i8",
+                       lens=("list", (40, 1000)))
+    prob = workloads.generate(s, 65)
+    dev = to_dev(prob)
+    plan = make_plan(prob, max_q_per_seq=1)
+    out = torch.empty(dev["q"].shape, dtype=torch.float16, device="cuda")
+    lse = torch.empty(dev["q"].shape[:2], dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        prefill(plan, prob, dev, out=out, lse=lse)
+    ro, rl = oracle.decode(prob)
+    ref = None
+    for i in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        compare(out, lse, ro, rl, what=f"replay {i}")
+        if ref is None:
+            ref = (out.clone(), lse.clone())
+        else:
+            assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1])
+        torch.ones(1 << 20, device="cuda").sum()
+
+
+@pytest.mark.parametrize("name", sorted(workloads.PREFILL_CONFIGS))
+def test_prefill_workloads_sampled(name):
+    """The benchmark's prefill workloads at full size, in its launch configuration, on 256
+    sampled rows (spread over sequences, tokens and heads, incl. the first and last token)."""
+    s = workloads.PREFILL_CONFIGS[name]
+    rng = np.random.default_rng(66)
+    total = s.batch * s.q_per_seq * s.num_qo_heads
+    rows = np.unique(np.concatenate([rng.integers(0, total, 250),
+                                     [0, s.num_qo_heads - 1, total - 1,
+                                      (s.q_per_seq - 1) * s.num_qo_heads]]))
+    check(s, 67, rows=rows)

@@ -40,6 +40,8 @@ CASES = [
     (1, 2, 6, 3, 32, 16, (150,), False),
     (2, 1, 4, 2, 64, 4, (37, 90), True),
     (2, 4, 8, 2, 128, 16, (100, 33), True),
+    (2, 37, 4, 2, 64, 16, (37, 120), False),   # many query tokens (the prefill route's reading)
+    (1, 20, 8, 2, 64, 4, (90,), True),
 ]
 
 

@@ -269,6 +269,28 @@ APPEND_CONFIGS = {
 }
 
 
+# Prefill workloads (the multi-token route): 4 prompts of 2048 tokens each processed at once
+# against their own 2048 cached positions (full causal), the GQA batch's head shape; int8 and
+# f16 caches. T = 2048 query tokens per sequence.
+PREFILL_CONFIGS = {
+    "prompt_i8": Spec("prefill_prompt_i8", 4, 2048, 32, 8, 128, 16, "i8", ("fixed", 2048)),
+    "prompt_f16": Spec("prefill_prompt_f16", 4, 2048, 32, 8, 128, 16, "f16", ("fixed", 2048)),
+}
+
+
+def attention_flops(prob: dict) -> int:
+    """Algorithmic FLOPs of one attention call: 4*D per (query row, visible position) pair
+    (2*D for q.k, 2*D for p*v), visible positions per the causal reading."""
+    k = prob["k_pages"]
+    D = k.shape[3]
+    Hq = prob["q"].shape[1]
+    T = int(prob["q_per_seq"])
+    L = np.asarray(prob["kv_len"], np.int64)
+    t = np.arange(T, dtype=np.int64)
+    vis = np.clip(L[:, None] - T + t[None, :] + 1, 0, None).sum()
+    return int(4 * D * Hq * vis)
+
+
 def append_bytes(prob: dict, new: dict) -> int:
     """Algorithmic bytes of one append: the new K and V rows read (2*D*2 bytes per token-head)
     plus the cache written (2*D*2 bytes for f16; 2*(D + 2*D/32) for int8 with f16 scales)."""
