@@ -7,10 +7,10 @@
 // dequantized the whole cache into K_f16/V_f16 buffers first. Here the tile kernel reads the
 // pages itself and widens int8 in registers.
 //
-// Work unit: one workgroup of 4 waves per (sequence b, KV head, tile of query tokens). Its 64
-// query rows are (token, head-of-group) pairs r = token * G + g, so every wave reads the same
-// KV head: K and V tiles of KT tokens are gathered through the page table into LDS once and
-// shared by the 4 waves (16 rows each). Per KV tile a wave computes S^T = K Q^T with the
+// Work unit: one workgroup of 4 waves per (sequence b, KV head, tile of query tokens). Its
+// query rows (128 at head_dim 128, 64 at 256) are (token, head-of-group) pairs r = token * G +
+// g, so every wave reads the same KV head: K and V tiles of KT tokens are gathered through the
+// page table into LDS once and shared by the 4 waves (one or two sets of 16 rows each). Per KV tile a wave computes S^T = K Q^T with the
 // 16x16x32 f16 MFMA (A = 16 K rows from LDS, B = the wave's 16 query rows, held in registers),
 // so each lane holds one query row's scores (column lane % 16) for 4 tokens per 16-token
 // sub-tile; the online softmax (base 2) needs only per-lane work plus two cross-lane steps for
@@ -21,8 +21,10 @@
 //
 // Causal reading (the decode's): the T query tokens are the last T cached positions, token t
 // sees positions j <= kv_len - T + t. A workgroup walks positions [0, kv_len - T + t_last] in
-// tiles; the next tile's rows are loaded into registers while the current one is computed.
-// Workgroups run heaviest (latest query tiles) first.
+// tiles; the next tile's rows are loaded into registers while the current one is computed and
+// stored into the second of two LDS tile buffers, so one barrier per tile suffices. Two
+// workgroups share a CU (256 registers per lane each). Workgroups run heaviest (latest query
+// tiles) first.
 #include <hip/hip_runtime.h>
 
 #include "skvd_internal.h"
@@ -130,16 +132,22 @@ __device__ __forceinline__ void store_tile(char *k_lds, char *v_lds, const TileR
   }
 }
 
+// Row sets per wave: each wave serves RS sets of 16 query rows, so every K fragment and every
+// transposed V fragment it reads from LDS feeds RS MFMAs (LDS traffic per FLOP / RS).
+template <int D>
+constexpr int row_sets() { return D == 128 ? 2 : 1; }
+
 template <int D, bool I8>
-__global__ __launch_bounds__(256) void prefill_kernel(LaunchArgs a, int tpw) {
+__global__ __launch_bounds__(256, 2) void prefill_kernel(LaunchArgs a, int tpw) {
   constexpr int KT = kv_tile<D>();
+  constexpr int RS = row_sets<D>();
   constexpr int NST = KT / 16;   // 16-token score sub-tiles per KV tile
   constexpr int NCH = KT / 32;   // 32-token P.V chunks per KV tile
   constexpr int NKS = D / 32;    // contraction steps over head_dim
   constexpr int NDT = D / 16;    // 16-wide head_dim tiles of the output
   constexpr int ROWB = D * 2;
-  __shared__ __attribute__((aligned(16))) char k_lds[KT * ROWB];
-  __shared__ __attribute__((aligned(16))) char v_lds[KT * ROWB];
+  // two K/V tile buffers: tile i+1 is stored into one while tile i is read from the other
+  __shared__ __attribute__((aligned(16))) char kv_lds[2][2][KT * ROWB];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -153,92 +161,109 @@ __global__ __launch_bounds__(256) void prefill_kernel(LaunchArgs a, int tpw) {
   const int t_last = min(t0 + tpw, T) - 1;
   const int kv_end = min(L, L - T + t_last + 1);  // positions [0, kv_end) are visited
 
-  // this lane's query row: column c16 of the wave's 16 (rows r = token * G + head)
-  const int r = 16 * w + c16;
-  const int tl = r / G;
-  const int gh = r - tl * G;
-  const bool row_ok = tl < tpw && t0 + tl < T;
-  const int t = row_ok ? t0 + tl : t_last;
-  const int h = kvh * G + gh;
-  const int limit = L - T + t;  // last visible position of the row
-
-  ph8 qv[NKS];
-  {
-    const _Float16 *qp = (const _Float16 *)a.q + ((int64_t)b * T + t) * a.q_tok_stride +
-                         (int64_t)h * a.q_head_stride + 8 * g4;
+  // this lane's query rows: column c16 of each of the wave's row sets (r = token * G + head)
+  bool row_ok[RS];
+  int trow[RS], hrow[RS], limit[RS];
+  ph8 qv[RS][NKS];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qv[ks] = *(const ph8 *)(qp + 32 * ks);
+  for (int rs = 0; rs < RS; ++rs) {
+    const int r = 16 * (RS * w + rs) + c16;
+    const int tl = r / G;
+    const int gh = r - tl * G;
+    row_ok[rs] = tl < tpw && t0 + tl < T;
+    trow[rs] = row_ok[rs] ? t0 + tl : t_last;
+    hrow[rs] = kvh * G + gh;
+    limit[rs] = L - T + trow[rs];  // last visible position of the row
+    const _Float16 *qp = (const _Float16 *)a.q + ((int64_t)b * T + trow[rs]) * a.q_tok_stride +
+                         (int64_t)hrow[rs] * a.q_head_stride + 8 * g4;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qv[rs][ks] = *(const ph8 *)(qp + 32 * ks);
   }
 
-  pf4 acc[NDT];
+  pf4 acc[RS][NDT];
+  float m[RS], l[RS];
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) acc[dt] = pf4{0.f, 0.f, 0.f, 0.f};
-  float m = kMFloor, l = 0.f;
+  for (int rs = 0; rs < RS; ++rs) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc[rs][dt] = pf4{0.f, 0.f, 0.f, 0.f};
+    m[rs] = kMFloor;
+    l[rs] = 0.f;
+  }
 
   const int ntiles = kv_end > 0 ? (kv_end + KT - 1) / KT : 0;
   TileRegs<D, I8> regs;
   if (ntiles > 0) {
     load_tile<D, I8>(a, b, kvh, 0, kv_end - 1, regs);
-    store_tile<D, I8>(k_lds, v_lds, regs);
+    store_tile<D, I8>(kv_lds[0][0], kv_lds[0][1], regs);
   }
   __syncthreads();
   for (int it = 0; it < ntiles; ++it) {
     const int kv0 = it * KT;
     const bool more = it + 1 < ntiles;
+    const char *k_lds = kv_lds[it & 1][0];
+    const char *v_lds = kv_lds[it & 1][1];
     if (more) load_tile<D, I8>(a, b, kvh, kv0 + KT, kv_end - 1, regs);
 
     // ---- S^T = K Q^T: lane holds row c16's scores for tokens 16 st + 4 g4 + e
-    pf4 s[NST];
+    pf4 s[RS][NST];
 #pragma unroll
     for (int st = 0; st < NST; ++st) {
-      s[st] = pf4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int rs = 0; rs < RS; ++rs) s[rs][st] = pf4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const ph8 kf = *(const ph8 *)(k_lds + pswz<ROWB>(16 * st + c16, 4 * ks + g4));
-        s[st] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qv[ks], s[st], 0, 0, 0);
+#pragma unroll
+        for (int rs = 0; rs < RS; ++rs)
+          s[rs][st] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qv[rs][ks], s[rs][st], 0, 0, 0);
       }
     }
-    // ---- mask, scale (base 2), online softmax
-    float mx = kPNegInf;
+    // ---- mask, scale (base 2), online softmax per row set
+    ph8 pb[RS][NCH];
 #pragma unroll
-    for (int st = 0; st < NST; ++st)
+    for (int rs = 0; rs < RS; ++rs) {
+      float mx = kPNegInf;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int pos = kv0 + 16 * st + 4 * g4 + e;
-        const float v = pos <= limit ? s[st][e] * a.scale_log2 : kPNegInf;
-        s[st][e] = v;
-        mx = fmaxf(mx, v);
+      for (int st = 0; st < NST; ++st)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int pos = kv0 + 16 * st + 4 * g4 + e;
+          const float v = pos <= limit[rs] ? s[rs][st][e] * a.scale_log2 : kPNegInf;
+          s[rs][st][e] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m[rs], mx);
+      const float alpha = __builtin_amdgcn_exp2f(m[rs] - m_new);
+      m[rs] = m_new;
+      float ls = 0.f;
+#pragma unroll
+      for (int st = 0; st < NST; ++st)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p = __builtin_amdgcn_exp2f(s[rs][st][e] - m_new);
+          s[rs][st][e] = p;
+          ls += p;
+        }
+      l[rs] = l[rs] * alpha + ls;
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[rs][dt][e] *= alpha;
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-    m = m_new;
-    float ls = 0.f;
 #pragma unroll
-    for (int st = 0; st < NST; ++st)
+      for (int c = 0; c < NCH; ++c)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p = __builtin_amdgcn_exp2f(s[st][e] - m_new);
-        s[st][e] = p;
-        ls += p;
-      }
-    l = l * alpha + ls;
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[dt][e] *= alpha;
+        for (int e = 0; e < 4; ++e) {
+          pb[rs][c][e] = (_Float16)s[rs][2 * c][e];
+          pb[rs][c][4 + e] = (_Float16)s[rs][2 * c + 1][e];
+        }
     }
     // ---- O^T += V^T P^T, 32 tokens per MFMA
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      ph8 pb;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pb[e] = (_Float16)s[2 * c][e];
-        pb[4 + e] = (_Float16)s[2 * c + 1][e];
-      }
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         ph8 va;
@@ -248,38 +273,45 @@ __global__ __launch_bounds__(256) void prefill_kernel(LaunchArgs a, int tpw) {
           const int row = 32 * c + 16 * hh + 4 * g4 + (c16 >> 2);
           const int col = 16 * dt + 4 * (c16 & 3);
           const ps4 r4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_ps4)(v_lds + pswz<ROWB>(row, col >> 3) + ((col & 7) << 1)));
+              (lds_ps4)(const_cast<char *>(v_lds) + pswz<ROWB>(row, col >> 3) + ((col & 7) << 1)));
           const ph4 hv = __builtin_bit_cast(ph4, r4);
 #pragma unroll
           for (int e = 0; e < 4; ++e) va[4 * hh + e] = hv[e];
         }
-        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, acc[dt], 0, 0, 0);
+#pragma unroll
+        for (int rs = 0; rs < RS; ++rs)
+          acc[rs][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[rs][c], acc[rs][dt], 0, 0, 0);
       }
     }
-    __syncthreads();  // every wave is done with this tile's LDS
-    if (more) store_tile<D, I8>(k_lds, v_lds, regs);
-    __syncthreads();
+    // the other buffer was last read in the previous iteration, which every wave has left
+    if (more) store_tile<D, I8>(kv_lds[(it + 1) & 1][0], kv_lds[(it + 1) & 1][1], regs);
+    __syncthreads();  // tile it+1 is in LDS, and every wave is done reading tile it
   }
 
   // ---- epilogue: row sums across the four lane groups, normalize, write o and lse
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  if (!row_ok) return;
-  const int64_t orow = ((int64_t)b * T + t) * a.Hq + h;
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  _Float16 *op = (_Float16 *)a.o + orow * D + 4 * g4;
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) {
-    ph4 ov;
+  for (int rs = 0; rs < RS; ++rs) {
+    float lt = l[rs];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    if (!row_ok[rs]) continue;
+    const int64_t orow = ((int64_t)b * T + trow[rs]) * a.Hq + hrow[rs];
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    _Float16 *op = (_Float16 *)a.o + orow * D + 4 * g4;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) ov[e] = (_Float16)(acc[dt][e] * inv);
-    *(ph4 *)(op + 16 * dt) = ov;
+    for (int dt = 0; dt < NDT; ++dt) {
+      ph4 ov;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ov[e] = (_Float16)(acc[rs][dt][e] * inv);
+      *(ph4 *)(op + 16 * dt) = ov;
+    }
+    if (g4 == 0 && a.lse) a.lse[orow] = lt > 0.f ? (m[rs] + __log2f(lt)) * kPLn2 : kPNegInf;
   }
-  if (g4 == 0 && a.lse) a.lse[orow] = l > 0.f ? (m + __log2f(l)) * kPLn2 : kPNegInf;
 }
 
 template <int D>
-void launch_pd(const LaunchArgs &a, int tpw, hipStream_t st) {
+void launch_pd(const LaunchArgs &a, hipStream_t st) {
+  const int tpw = 64 * row_sets<D>() / a.G;  // query tokens per workgroup: its rows / G
   const dim3 grid((a.T + tpw - 1) / tpw, a.Hkv, a.batch);
   if (a.int8) prefill_kernel<D, true><<<grid, 256, 0, st>>>(a, tpw);
   else prefill_kernel<D, false><<<grid, 256, 0, st>>>(a, tpw);
@@ -289,10 +321,9 @@ void launch_pd(const LaunchArgs &a, int tpw, hipStream_t st) {
 
 int launch_prefill(const LaunchArgs &a, void *stream) {
   if (a.batch == 0) return 0;
-  const int tpw = 64 / a.G;  // query tokens per workgroup: 64 rows of (token, head) pairs
   hipStream_t st = (hipStream_t)stream;
-  if (a.D == 128) launch_pd<128>(a, tpw, st);
-  else launch_pd<256>(a, tpw, st);
+  if (a.D == 128) launch_pd<128>(a, st);
+  else launch_pd<256>(a, st);
   return (int)hipGetLastError();
 }
 
