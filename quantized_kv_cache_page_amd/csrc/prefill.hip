@@ -53,13 +53,18 @@ __device__ __forceinline__ int pswz(int r, int c) {
 template <int D>
 constexpr int kv_tile() { return D == 128 ? 64 : 32; }
 
-// One KV tile's rows held in registers between the global load and the LDS store.
+// One KV tile's rows held in registers between the global load and the LDS store. Each thread
+// serves one token of the tile (TPT threads per token) and N consecutive 16-byte chunks of its K
+// and V rows, so it reads one page-table entry and forms one row address per tile. The loads
+// are ordinary (cached): every query tile of the sequence reads the same K/V tiles, so they
+// should stay in L2 and the Infinity Cache (non-temporal loads here cost 12-37 %).
 template <int D, bool I8>
 struct TileRegs {
   static constexpr int KT = kv_tile<D>();
   // f16: 16-byte chunks of 8 elements; int8: 16-byte chunks of 16 elements (+ their scale)
   static constexpr int CPR = I8 ? D / 16 : D / 8;  // chunks per row
-  static constexpr int N = KT * CPR / 256;         // chunks per thread per tensor
+  static constexpr int TPT = 256 / KT;             // threads per token
+  static constexpr int N = CPR / TPT;              // chunks per thread per tensor
   pu4 k[N], v[N];
   _Float16 ks[I8 ? N : 1], vs[I8 ? N : 1];
 };
@@ -69,30 +74,34 @@ __device__ __forceinline__ void load_tile(const LaunchArgs &a, int b, int kvh, i
                                           TileRegs<D, I8> &r) {
   using TR = TileRegs<D, I8>;
   const int P1 = (1 << a.page_shift) - 1;
+  const int tok = min(kv0 + (int)threadIdx.x / TR::TPT, kv_last);  // tail re-reads (masked)
+  const int part0 = ((int)threadIdx.x % TR::TPT) * TR::N;
+  const int64_t pg = a.table[(int64_t)b * a.table_stride + (tok >> a.page_shift)];
+  const int64_t pk = pg < 0 ? 0 : (pg >= a.num_k_pages ? a.num_k_pages - 1 : pg);
+  const int64_t pv = pg < 0 ? 0 : (pg >= a.num_v_pages ? a.num_v_pages - 1 : pg);
+  const int64_t in_page = (int64_t)(tok & P1) * a.tok_stride + (int64_t)kvh * a.head_stride;
+  const int64_t rk = pk * a.page_stride + in_page;
+  const int64_t rv = pv * a.page_stride + in_page;
+  if constexpr (!I8) {
+    const pu4 *kp = (const pu4 *)((const _Float16 *)a.k + rk) + part0;
+    const pu4 *vp = (const pu4 *)((const _Float16 *)a.v + rv) + part0;
 #pragma unroll
-  for (int n = 0; n < TR::N; ++n) {
-    const int i = threadIdx.x + 256 * n;
-    const int tok = min(kv0 + i / TR::CPR, kv_last);  // the tail re-reads the last row (masked)
-    const int part = i % TR::CPR;
-    int64_t pg = a.table[(int64_t)b * a.table_stride + (tok >> a.page_shift)];
-    const int64_t pk = pg < 0 ? 0 : (pg >= a.num_k_pages ? a.num_k_pages - 1 : pg);
-    const int64_t pv = pg < 0 ? 0 : (pg >= a.num_v_pages ? a.num_v_pages - 1 : pg);
-    const int64_t rk = pk * a.page_stride + (int64_t)(tok & P1) * a.tok_stride +
-                       (int64_t)kvh * a.head_stride;
-    const int64_t rv = pv * a.page_stride + (int64_t)(tok & P1) * a.tok_stride +
-                       (int64_t)kvh * a.head_stride;
-    if constexpr (!I8) {
-      r.k[n] = __builtin_nontemporal_load((const pu4 *)((const _Float16 *)a.k + rk + 8 * part));
-      r.v[n] = __builtin_nontemporal_load((const pu4 *)((const _Float16 *)a.v + rv + 8 * part));
-    } else {
-      r.k[n] = __builtin_nontemporal_load((const pu4 *)((const int8_t *)a.k + rk + 16 * part));
-      r.v[n] = __builtin_nontemporal_load((const pu4 *)((const int8_t *)a.v + rv + 16 * part));
-      const int64_t sk = pk * a.s_page_stride + (int64_t)(tok & P1) * a.s_tok_stride +
-                         (int64_t)kvh * a.s_head_stride + (part >> 1);
-      const int64_t sv = pv * a.s_page_stride + (int64_t)(tok & P1) * a.s_tok_stride +
-                         (int64_t)kvh * a.s_head_stride + (part >> 1);
-      r.ks[n] = ((const _Float16 *)a.ks)[sk];
-      r.vs[n] = ((const _Float16 *)a.vs)[sv];
+    for (int n = 0; n < TR::N; ++n) {
+      r.k[n] = kp[n];
+      r.v[n] = vp[n];
+    }
+  } else {
+    const pu4 *kp = (const pu4 *)((const int8_t *)a.k + rk) + part0;
+    const pu4 *vp = (const pu4 *)((const int8_t *)a.v + rv) + part0;
+    const int64_t s_in_page = (int64_t)(tok & P1) * a.s_tok_stride + (int64_t)kvh * a.s_head_stride;
+    const _Float16 *ksp = (const _Float16 *)a.ks + pk * a.s_page_stride + s_in_page;
+    const _Float16 *vsp = (const _Float16 *)a.vs + pv * a.s_page_stride + s_in_page;
+#pragma unroll
+    for (int n = 0; n < TR::N; ++n) {
+      r.k[n] = kp[n];
+      r.v[n] = vp[n];
+      r.ks[n] = ksp[(part0 + n) >> 1];  // a 16-element chunk lies in scale group chunk / 2
+      r.vs[n] = vsp[(part0 + n) >> 1];
     }
   }
 }
@@ -113,10 +122,10 @@ template <int D, bool I8>
 __device__ __forceinline__ void store_tile(char *k_lds, char *v_lds, const TileRegs<D, I8> &r) {
   using TR = TileRegs<D, I8>;
   constexpr int ROWB = D * 2;
+  const int tok = (int)threadIdx.x / TR::TPT;
 #pragma unroll
   for (int n = 0; n < TR::N; ++n) {
-    const int i = threadIdx.x + 256 * n;
-    const int tok = i / TR::CPR, part = i % TR::CPR;
+    const int part = ((int)threadIdx.x % TR::TPT) * TR::N + n;
     if constexpr (!I8) {
       *(pu4 *)(k_lds + pswz<ROWB>(tok, part)) = r.k[n];
       *(pu4 *)(v_lds + pswz<ROWB>(tok, part)) = r.v[n];
@@ -218,41 +227,59 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(LaunchArgs a, int tpw) 
           s[rs][st] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qv[rs][ks], s[rs][st], 0, 0, 0);
       }
     }
-    // ---- mask, scale (base 2), online softmax per row set
+    // ---- mask (only tiles that reach past the first row's limit), scale (base 2), online
+    // softmax per row set. The reference max m is raised only when a score exceeds it by more
+    // than 2^8 in weight (then the accumulators are rescaled); otherwise probabilities up to 2^8
+    // are taken against the old reference, which the final o = acc / l and lse = m + log2 l
+    // absorb exactly.
+    const bool need_mask = kv0 + KT - 1 > L - T + t0;  // workgroup-uniform
     ph8 pb[RS][NCH];
 #pragma unroll
     for (int rs = 0; rs < RS; ++rs) {
       float mx = kPNegInf;
+      if (need_mask) {
 #pragma unroll
-      for (int st = 0; st < NST; ++st)
+        for (int st = 0; st < NST; ++st)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int pos = kv0 + 16 * st + 4 * g4 + e;
-          const float v = pos <= limit[rs] ? s[rs][st][e] * a.scale_log2 : kPNegInf;
-          s[rs][st][e] = v;
-          mx = fmaxf(mx, v);
-        }
+          for (int e = 0; e < 4; ++e) {
+            const int pos = kv0 + 16 * st + 4 * g4 + e;
+            const float v = pos <= limit[rs] ? s[rs][st][e] * a.scale_log2 : kPNegInf;
+            s[rs][st][e] = v;
+            mx = fmaxf(mx, v);
+          }
+      } else {
+#pragma unroll
+        for (int st = 0; st < NST; ++st)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float v = s[rs][st][e] * a.scale_log2;
+            s[rs][st][e] = v;
+            mx = fmaxf(mx, v);
+          }
+      }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m[rs], mx);
-      const float alpha = __builtin_amdgcn_exp2f(m[rs] - m_new);
-      m[rs] = m_new;
-      float ls = 0.f;
-#pragma unroll
-      for (int st = 0; st < NST; ++st)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p = __builtin_amdgcn_exp2f(s[rs][st][e] - m_new);
-          s[rs][st][e] = p;
-          ls += p;
-        }
-      l[rs] = l[rs] * alpha + ls;
-      if (__any(alpha != 1.f)) {
+      const bool raise = mx > m[rs] + 8.f;
+      if (__any(raise)) {
+        const float m_new = raise ? mx : m[rs];
+        const float alpha = __builtin_amdgcn_exp2f(m[rs] - m_new);
+        m[rs] = m_new;
+        l[rs] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
           for (int e = 0; e < 4; ++e) acc[rs][dt][e] *= alpha;
       }
+      float ls = 0.f;
+#pragma unroll
+      for (int st = 0; st < NST; ++st)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p = __builtin_amdgcn_exp2f(s[rs][st][e] - m[rs]);
+          s[rs][st][e] = p;
+          ls += p;
+        }
+      l[rs] += ls;
 #pragma unroll
       for (int c = 0; c < NCH; ++c)
 #pragma unroll
