@@ -9,7 +9,7 @@ that file with gcc and marshals numpy arrays into it.
 The decode functions take the problem as the dict that ``workloads.generate`` returns (numpy
 arrays: q, k_pages, v_pages, k_scales, v_scales, page_table, kv_len; ints: q_per_seq; float:
 sm_scale). ``append`` takes new K/V rows and their (sequence, position) pairs and returns
-written copies of the pools. Strides are read from the arrays themselves, in elements.
+written copies of the pools; ``merge_states`` merges attention states over disjoint key sets. Strides are read from the arrays themselves, in elements.
 """
 from __future__ import annotations
 
@@ -99,6 +99,10 @@ def load(path: str | None = None):
     lib.oracle_quantize_group.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
                                           ctypes.c_void_p]
     lib.oracle_quantize_group.restype = None
+    lib.oracle_merge_states.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    lib.oracle_merge_states.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -255,3 +259,20 @@ def quantize_group(x, lib=None):
     sb = np.empty(1, np.uint16)
     lib.oracle_quantize_group(xb.ctypes.data, xb.shape[0], codes.ctypes.data, sb.ctypes.data)
     return codes, sb.view(np.float16)[0]
+
+
+def merge_states(o_states, lse_states, lib=None):
+    """Merge S attention states per row: o_states [S, rows, D] (any float dtype, widened to
+    fp64 exactly), lse_states [S, rows] (natural log). Returns fp64 (o [rows, D], lse [rows])."""
+    lib = lib or load()
+    o_s = np.ascontiguousarray(o_states, dtype=np.float64)
+    l_s = np.ascontiguousarray(lse_states, dtype=np.float64)
+    S, rows, D = o_s.shape
+    assert l_s.shape == (S, rows)
+    o = np.empty((rows, D), np.float64)
+    lse = np.empty((rows,), np.float64)
+    rc = lib.oracle_merge_states(S, rows, D, o_s.ctypes.data, l_s.ctypes.data, o.ctypes.data,
+                                 lse.ctypes.data)
+    if rc != 0:
+        raise RuntimeError("oracle_merge_states failed")
+    return o, lse

@@ -468,3 +468,54 @@ int64_t oracle_append(const oracle_append_problem *p) {
   }
   return skipped;
 }
+
+/* ============================================================================ merge states
+ * Merging attention states: the shared-prefix (cascade) use of the log-sum-exp reduction that
+ * merges the split-KV partials (1bit-MONSTER/engine issue #115, comments "Root-caused" and
+ * "Closing the remaining half of this issue": partials merged by reduce_fused; AMD-Ecosystem/
+ * flashinfer PR #397 names a cascade test under "Test plan"). A state of one row over a set of
+ * keys is (o, lse) with o the softmax-weighted mean of V over the set and lse = ln sum exp of
+ * the set's scaled logits. States over disjoint key sets merge to the state over their union:
+ *   M = max_s lse_s, w_s = exp(lse_s - M), W = sum_s w_s,
+ *   o = sum_s w_s o_s / W, lse = M + ln W;
+ * a state with lse = -inf (an empty key set) contributes nothing; if every state is empty,
+ * o = 0 and lse = -inf. fp64 throughout.
+ * ============================================================================ */
+
+/* o_states: fp64 [S][rows][D]; lse_states: fp64 [S][rows]; outputs fp64 o [rows][D], lse [rows]. */
+int oracle_merge_states(int32_t num_states, int64_t rows, int32_t head_dim,
+                        const double *o_states, const double *lse_states, double *o,
+                        double *lse) {
+  if (num_states < 1 || rows < 0 || head_dim < 1) return -1;
+  int D = head_dim;
+  for (int64_t r = 0; r < rows; ++r) {
+    double M = -INFINITY;
+    for (int s = 0; s < num_states; ++s) {
+      double x = lse_states[(int64_t)s * rows + r];
+      if (x > M) M = x;
+    }
+    double *orow = o + r * D;
+    for (int d = 0; d < D; ++d) orow[d] = 0.0;
+    if (M == -INFINITY) { lse[r] = -INFINITY; continue; }
+    double W = 0.0;
+    for (int s = 0; s < num_states; ++s) {
+      double x = lse_states[(int64_t)s * rows + r];
+      if (x == -INFINITY) continue;
+#if ORACLE_MUTANT == 15
+      double w = exp(M - x); /* planted: weight sign flipped */
+#else
+      double w = exp(x - M);
+#endif
+      W += w;
+      const double *os = o_states + ((int64_t)s * rows + r) * D;
+      for (int d = 0; d < D; ++d) orow[d] += w * os[d];
+    }
+    for (int d = 0; d < D; ++d) orow[d] /= W;
+#if ORACLE_MUTANT == 16
+    lse[r] = log(W); /* planted: max dropped */
+#else
+    lse[r] = M + log(W);
+#endif
+  }
+  return 0;
+}
