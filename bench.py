@@ -4,6 +4,7 @@
     python bench.py [--steps K] [--warmup W] [--config 2] [--gpus 1] [--no-cpu]
     python bench.py --op append [--append prefill_i8|prefill_f16|decode_i8]
     python bench.py --op prefill [--prefill prompt_i8|prompt_f16]
+    python bench.py --op merge
 
 A step is one decode call (partial kernel + reducer) over one batch of the workload, with
 all inputs resident in HBM. The default workload is the GQA batch decode (B=32, 32 query /
@@ -386,6 +387,69 @@ def bench_prefill(args):
     print(json.dumps(res), flush=True)
 
 
+MERGE_METRIC = "merge-states µs/call and achieved HBM GB/s (states read + merged state written) vs roofline"
+
+
+def bench_merge(args):
+    """skvd_merge_states on the cascade workload: 2 states of 262144 rows (4 x 2048 query
+    tokens x 32 heads, a prefill batch's outputs) at head_dim 128, inputs resident in HBM."""
+    import numpy as np
+    import torch
+    import quantized_kv_cache_page_amd as skvd
+    S, rows, D = 2, 4 * 2048 * 32, 128
+    seed = 80 if args.seed is None else args.seed
+    rng = np.random.default_rng(seed)
+    dev = torch.device("cuda:0")
+    o_s = torch.from_numpy(rng.standard_normal((S, rows, D), dtype=np.float32).astype(np.float16)).to(dev)
+    l_s = torch.from_numpy((5 * rng.standard_normal((S, rows))).astype(np.float32)).to(dev)
+    nbytes = S * rows * (2 * D + 4) + rows * (2 * D + 4)
+    copies = max(1, math.ceil(2 * MALL_BYTES / nbytes) + 1)
+    sets = [(o_s, l_s)] + [(o_s.clone(), l_s.clone()) for _ in range(copies - 1)]
+    out = torch.empty((rows, D), dtype=torch.float16, device=dev)
+    lse = torch.empty((rows,), dtype=torch.float32, device=dev)
+    for i in range(args.warmup):
+        skvd.merge_states(*sets[i % copies], out=out, lse=lse)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        skvd.merge_states(*sets[i % copies], out=out, lse=lse)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / args.steps * 1e3
+    gbs = nbytes / (us * 1e-6) / 1e9
+    res = {
+        "metric": MERGE_METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(us / 1e3, 5),
+        "us_per_call": round(us, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": f"cascade merge: {S} states x {rows} rows (4 x 2048 tokens x 32 "
+                               f"heads), head_dim {D}", "seed": seed, "bytes_per_call": nbytes,
+                   "copies_rotated": copies},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "merge_states_kernel", "kernel_avg_us": round(us, 3),
+                     "algorithmic_bytes_per_launch": nbytes},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        import oracle
+        n = 8192
+        o64 = o_s[:, :n].float().cpu().numpy().astype(np.float64)
+        l64 = l_s[:, :n].cpu().numpy().astype(np.float64)
+        times = []
+        t_end = time.time() + 5.0
+        while time.time() < t_end and len(times) < 20:
+            t0 = time.time()
+            oracle.merge_states(o64, l64)
+            times.append(time.time() - t0)
+        t = float(np.median(times))
+        res["cpu_baseline"] = {"value": round(nbytes * n / rows / t / 1e9, 3), "unit": "GB/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"{n} of the {rows} rows, median {t:.4f} s, fp64"}
+    print(json.dumps(res), flush=True)
+
+
 def bench_append(args):
     import workloads
     seed = 40 if args.seed is None else args.seed
@@ -416,7 +480,7 @@ def bench_append(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--op", choices=["decode", "append", "prefill"], default="decode")
+    ap.add_argument("--op", choices=["decode", "append", "prefill", "merge"], default="decode")
     ap.add_argument("--prefill", default="prompt_i8",
                     help="prefill workload for --op prefill: prompt_i8, prompt_f16")
     ap.add_argument("--append", default="prefill_i8",
@@ -468,6 +532,8 @@ def main():
         return bench_append(args)
     if args.op == "prefill":
         return bench_prefill(args)
+    if args.op == "merge":
+        return bench_merge(args)
 
     import numpy as np
     import torch

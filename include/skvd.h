@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define SKVD_ABI_VERSION 6
+#define SKVD_ABI_VERSION 7
 
 typedef enum {
   SKVD_OK = 0,
@@ -276,6 +276,32 @@ skvd_status skvd_prefill_check(const skvd_plan *plan, const skvd_decode_args *ar
 /* Prefill: one kernel on `stream` (a hipStream_t; NULL is the null stream), asynchronous. The
  * current HIP device must be the plan's device. Errors as for skvd_decode. */
 skvd_status skvd_prefill(const skvd_plan *plan, const skvd_decode_args *args, void *stream);
+
+/* ---------------------------------------------------------------------- merge states
+ * Cascade (shared-prefix) attention: merge S attention states of each row, computed over
+ * disjoint key sets (e.g. the pages of a prefix shared by many sequences, and each sequence's
+ * own suffix), into the state over their union, with the log-sum-exp reduction that merges the
+ * split-KV partials (1bit-MONSTER/engine issue #115, comments "Root-caused" and "Closing the
+ * remaining half of this issue"; AMD-Ecosystem/flashinfer PR #397 lists a cascade test under
+ * "Test plan"):
+ *     M = max_s lse_s,  w_s = exp(lse_s - M),  o = sum_s w_s o_s / sum_s w_s,
+ *     lse = M + ln sum_s w_s     (natural log, as skvd_decode writes it)
+ * A state with lse = -inf (an empty key set) contributes nothing; a row whose states are all
+ * empty gets o = 0 and lse = -inf. The states are exactly what skvd_decode / skvd_prefill write
+ * (o f16, lse f32), so a cascade is: decode the prefix, decode the suffixes, merge.
+ *
+ * - o_states: f16, state s of row r at o_states + s * o_state_stride + r * o_row_stride
+ *   (elements), head_dim dense; lse_states: f32 at s * lse_state_stride + r. Read only.
+ * - o: f16 [rows, head_dim] dense, written; lse: f32 [rows], written, may be NULL. They must not
+ *   overlap the states.
+ * - head_dim in {64, 128, 256, 512}; num_states >= 1; 0 <= rows <= 2^31 (0 launches nothing).
+ *   o_states and o 16-byte aligned with strides multiples of 8 elements; lse arrays 4-byte
+ *   aligned. Device pointers; one kernel on `stream`, asynchronous,
+ *   no allocation (graph-capture safe). Errors as for skvd_decode. */
+skvd_status skvd_merge_states(const void *o_states, int64_t o_state_stride, int64_t o_row_stride,
+                              const float *lse_states, int64_t lse_state_stride,
+                              int32_t num_states, int64_t rows, int32_t head_dim, void *o,
+                              float *lse, void *stream);
 
 /* ---------------------------------------------------------------------------- append
  * Writing new tokens into the paged cache: the step right before a decode, and the one

@@ -21,7 +21,7 @@ REDUCERS = {"auto": 0, "direct": 1, "cooperative": 2, "multipass": 3, "hierarchi
 REDUCER_NAMES = {v: k for k, v in REDUCERS.items()}
 SCHEDULES = {"auto": 0, "static": 1, "balanced": 2}
 SCHEDULE_NAMES = {v: k for k, v in SCHEDULES.items()}
-ABI_VERSION = 6
+ABI_VERSION = 7
 STATUS_KV_LEN_CLAMPED = 0x1
 STATUS_PAGE_CLAMPED = 0x2
 
@@ -108,6 +108,10 @@ SIGNATURES = {
                                          ctypes.c_void_p, ctypes.c_void_p]),
     "skvd_stream_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                         ctypes.c_void_p]),
+    "skvd_merge_states": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                         ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                         ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_void_p]),
     "skvd_prefill_check": (ctypes.c_int, [_PLAN_P, ctypes.POINTER(skvd_decode_args)]),
     "skvd_prefill": (ctypes.c_int, [_PLAN_P, ctypes.POINTER(skvd_decode_args), ctypes.c_void_p]),
     "skvd_append_check": (ctypes.c_int, [_PLAN_P, ctypes.POINTER(skvd_append_args)]),
@@ -216,6 +220,36 @@ def skvd_decode_merge(plan, args, workspace, workspace_bytes, stream) -> int:
 def skvd_gather_debug(plan, args, max_len, dk, dv, dks, dvs, stream) -> int:
     return int(lib().skvd_gather_debug(plan, ctypes.byref(args), max_len, dk, dv, dks, dvs,
                                        stream))
+
+
+def skvd_merge_states(o_states, o_state_stride, o_row_stride, lse_states, lse_state_stride,
+                      num_states, rows, head_dim, o, lse, stream) -> int:
+    return int(lib().skvd_merge_states(o_states, o_state_stride, o_row_stride, lse_states,
+                                       lse_state_stride, num_states, rows, head_dim, o, lse,
+                                       stream))
+
+
+def merge_states(o_states, lse_states, out=None, lse=None, stream=None):
+    """skvd_merge_states on torch tensors: o_states [S, rows, D] f16 (D dense), lse_states
+    [S, rows] f32 (row stride 1). Returns (o [rows, D] f16, lse [rows] f32)."""
+    if o_states.dtype != torch.float16 or lse_states.dtype != torch.float32:
+        raise TypeError("o_states must be float16 and lse_states float32")
+    if o_states.dim() != 3 or lse_states.dim() != 2 or o_states.shape[:2] != lse_states.shape:
+        raise SkvdError(2, "merge_states", "o_states [S, rows, D] and lse_states [S, rows]")
+    if o_states.stride(2) != 1 or lse_states.stride(1) != 1:
+        raise SkvdError(3, "merge_states", "head_dim and rows must be dense")
+    S, rows, D = o_states.shape
+    if out is None:
+        out = torch.empty((rows, D), dtype=torch.float16, device=o_states.device)
+    if lse is None:
+        lse = torch.empty((rows,), dtype=torch.float32, device=o_states.device)
+    if not out.is_contiguous() or not lse.is_contiguous():
+        raise SkvdError(3, "merge_states", "outputs are written densely")
+    st = (stream if stream is not None else torch.cuda.current_stream(o_states.device)).cuda_stream
+    _check(skvd_merge_states(o_states.data_ptr(), o_states.stride(0), o_states.stride(1),
+                             lse_states.data_ptr(), lse_states.stride(0), S, rows, D,
+                             out.data_ptr(), lse.data_ptr(), st), "skvd_merge_states")
+    return out, lse
 
 
 def skvd_prefill_check(plan, args) -> int:

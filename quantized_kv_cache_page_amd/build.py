@@ -16,7 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libskvd.so")
-SOURCES = ["api.cpp", "plan.cpp", "kernels.hip", "append.hip", "prefill.hip"]
+SOURCES = ["api.cpp", "plan.cpp", "kernels.hip", "append.hip", "prefill.hip", "cascade.hip"]
 ARCH = "gfx950"
 
 

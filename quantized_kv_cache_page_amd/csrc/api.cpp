@@ -378,6 +378,40 @@ skvd_status skvd_append(const skvd_plan *plan, const skvd_append_args *a, void *
   return e ? hip_err(e, "append kernel launch") : SKVD_OK;
 }
 
+skvd_status skvd_merge_states(const void *o_states, int64_t o_state_stride, int64_t o_row_stride,
+                              const float *lse_states, int64_t lse_state_stride,
+                              int32_t num_states, int64_t rows, int32_t head_dim, void *o,
+                              float *lse, void *stream) {
+  g_err[0] = 0;
+  if (!o_states || !lse_states || !o)
+    return set_err(SKVD_ERR_NULL, "o_states, lse_states and o must be non-NULL");
+  if (num_states < 1 || rows < 0 || rows > (int64_t(1) << 31))
+    return set_err(SKVD_ERR_SHAPE, "num_states=%d must be >= 1 and rows=%lld in 0..2^31",
+                   num_states, (long long)rows);
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256 && head_dim != 512)
+    return set_err(SKVD_ERR_SHAPE, "head_dim=%d not in {64, 128, 256, 512}", head_dim);
+  const int64_t vec = 8;  // f16 elements one lane reads (16 bytes)
+  if ((uintptr_t)o_states % (2 * vec) || (uintptr_t)o % (2 * vec) || o_state_stride < 0 ||
+      o_row_stride < 0 || o_state_stride % vec || o_row_stride % vec ||
+      (uintptr_t)lse_states % 4 || (lse && (uintptr_t)lse % 4) || lse_state_stride < 0)
+    return set_err(SKVD_ERR_LAYOUT, "o_states and o must be %lld-byte aligned with "
+                   "non-negative strides that are multiples of %lld elements; lse arrays "
+                   "4-byte aligned", (long long)(2 * vec), (long long)vec);
+  skvd::MergeStatesArgs m{};
+  m.o_states = o_states;
+  m.o_state_stride = o_state_stride;
+  m.o_row_stride = o_row_stride;
+  m.lse_states = lse_states;
+  m.lse_state_stride = lse_state_stride;
+  m.num_states = num_states;
+  m.head_dim = head_dim;
+  m.rows = rows;
+  m.o = o;
+  m.lse = lse;
+  const int e = skvd::launch_merge_states(m, stream);
+  return e ? hip_err(e, "merge-states kernel launch") : SKVD_OK;
+}
+
 skvd_status skvd_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *stream) {
   g_err[0] = 0;
   if (!buf || !sink) return set_err(SKVD_ERR_NULL, "buf and sink must be non-NULL");

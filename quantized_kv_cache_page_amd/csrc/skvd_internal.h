@@ -105,6 +105,19 @@ struct AppendLaunch {
 // prefill.hip: the multi-token route (T > 8) over the decode's LaunchArgs; no workspace.
 int launch_prefill(const LaunchArgs &la, void *stream);
 
+// cascade.hip: merge of attention states (validated in api.cpp)
+struct MergeStatesArgs {
+  const void *o_states;  // f16, state s row r at s * o_state_stride + r * o_row_stride
+  int64_t o_state_stride, o_row_stride;
+  const float *lse_states;  // state s row r at s * lse_state_stride + r
+  int64_t lse_state_stride;
+  int num_states, head_dim;
+  int64_t rows;
+  void *o;     // f16 [rows, head_dim] dense
+  float *lse;  // [rows] or NULL
+};
+int launch_merge_states(const MergeStatesArgs &a, void *stream);
+
 // append.hip
 constexpr int kAppendTokensPerLane = 4;  // tokens one append lane serves per round
 int launch_append(const AppendLaunch &a, void *stream);

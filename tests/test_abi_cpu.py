@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol():
     for s in syms:
         assert hasattr(L, s), s
     assert set(syms) == set(bd.SIGNATURES), set(syms) ^ set(bd.SIGNATURES)
-    assert L.skvd_abi_version() == bd.ABI_VERSION == 6
+    assert L.skvd_abi_version() == bd.ABI_VERSION == 7
 
 
 def plan(**kw):
@@ -285,3 +285,19 @@ def test_prefill_check(over, status):
     p = plan()
     a = good_args(p, **dict(dict(q_per_seq=512), **over))
     assert bd.skvd_prefill_check(p.handle, a) == status
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(o_states=None), 1), (dict(lse_states=None), 1), (dict(o=None), 1),
+    (dict(num_states=0), 2), (dict(rows=-1), 2), (dict(head_dim=96), 2),
+    (dict(o_states=FAKE + 8), 3), (dict(o_row_stride=132), 3), (dict(o=FAKE + 8), 3),
+    (dict(lse_states=FAKE + 2), 3), (dict(o_state_stride=-128), 3),
+])
+def test_merge_states_errors(over, status):
+    """Invalid merges are refused before any launch (the error paths need no GPU)."""
+    a = dict(o_states=FAKE, o_state_stride=1024 * 128, o_row_stride=128, lse_states=FAKE,
+             lse_state_stride=1024, num_states=2, rows=1024, head_dim=128, o=FAKE, lse=FAKE,
+             stream=None)
+    a.update(over)
+    assert bd.skvd_merge_states(*a.values()) == status
+    assert skvd.last_error()
