@@ -32,6 +32,12 @@
  * routing", section "Changes") does; that PR's routing threshold (Q->ne[1] <= 8) is why this
  * decode call accepts at most 8 query tokens per sequence.
  *
+ * Besides the decode, the library holds the operations around it on the same cache: the
+ * multi-token route (skvd_prefill: any number of query tokens, MFMA tiles), the append that
+ * writes new tokens into the pages (skvd_append: int8 quantized on write), and the merge of
+ * attention states over disjoint key sets (skvd_merge_states: cascade / shared prefix). Each is
+ * declared below with the passage that defines it.
+ *
  * Conventions
  * -----------
  * - Ownership: every pointer in skvd_decode_args is caller-owned device memory on the plan's

@@ -33,6 +33,20 @@ skvd_status hip_err(int e, const char *what) {
   return set_err(SKVD_ERR_HIP, "%s: %s", what, hipGetErrorString((hipError_t)e));
 }
 
+// The current HIP device must be the plan's (launches go to the current device).
+skvd_status check_device(const skvd::Plan &p) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return set_err(SKVD_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  }
+  if (dev != p.prm.device)
+    return set_err(SKVD_ERR_DEVICE, "current device %d is not the plan's device %d", dev,
+                   p.prm.device);
+  return SKVD_OK;
+}
+
 skvd_status common_checks(const skvd_plan *plan, const skvd_decode_args *args, void *ws,
                           size_t ws_bytes) {
   g_err[0] = 0;
@@ -42,16 +56,7 @@ skvd_status common_checks(const skvd_plan *plan, const skvd_decode_args *args, v
   if (!ws) return set_err(SKVD_ERR_WORKSPACE, "workspace is NULL");
   if ((uintptr_t)ws % skvd::kAlign)
     return set_err(SKVD_ERR_WORKSPACE, "workspace must be %zu-byte aligned", skvd::kAlign);
-  int dev = -1;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) {
-    (void)hipGetLastError();
-    return set_err(SKVD_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
-  }
-  if (dev != plan->p.prm.device)
-    return set_err(SKVD_ERR_DEVICE, "current device %d is not the plan's device %d", dev,
-                   plan->p.prm.device);
-  return SKVD_OK;
+  return check_device(plan->p);
 }
 
 // skvd_append's host checks (shapes and layout the append kernel addresses; no HIP call).
@@ -292,16 +297,8 @@ skvd_status skvd_prefill_check(const skvd_plan *plan, const skvd_decode_args *ar
 
 skvd_status skvd_prefill(const skvd_plan *plan, const skvd_decode_args *args, void *stream) {
   skvd_status st = check_prefill(plan, args);
+  if (st == SKVD_OK) st = check_device(plan->p);
   if (st != SKVD_OK) return st;
-  int dev = -1;
-  hipError_t he = hipGetDevice(&dev);
-  if (he != hipSuccess) {
-    (void)hipGetLastError();
-    return set_err(SKVD_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(he));
-  }
-  if (dev != plan->p.prm.device)
-    return set_err(SKVD_ERR_DEVICE, "current device %d is not the plan's device %d", dev,
-                   plan->p.prm.device);
   skvd::LaunchArgs la;
   skvd::fill_launch_args(plan->p, *args, nullptr, &la);
   const int e = skvd::launch_prefill(la, stream);
@@ -314,17 +311,9 @@ skvd_status skvd_append_check(const skvd_plan *plan, const skvd_append_args *arg
 
 skvd_status skvd_append(const skvd_plan *plan, const skvd_append_args *a, void *stream) {
   skvd_status st = check_append(plan, a);
+  if (st == SKVD_OK) st = check_device(plan->p);
   if (st != SKVD_OK) return st;
   const skvd::Plan &p = plan->p;
-  int dev = -1;
-  hipError_t he = hipGetDevice(&dev);
-  if (he != hipSuccess) {
-    (void)hipGetLastError();
-    return set_err(SKVD_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(he));
-  }
-  if (dev != p.prm.device)
-    return set_err(SKVD_ERR_DEVICE, "current device %d is not the plan's device %d", dev,
-                   p.prm.device);
   skvd::AppendLaunch l{};
   l.k_new = a->k_new;
   l.v_new = a->v_new;
