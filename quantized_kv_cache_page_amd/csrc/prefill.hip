@@ -13,8 +13,8 @@
 // page table into LDS once and shared by the 4 waves (one or two sets of 16 rows each). Per KV tile a wave computes S^T = K Q^T with the
 // 16x16x32 f16 MFMA (A = 16 K rows from LDS, B = the wave's 16 query rows, held in registers),
 // so each lane holds one query row's scores (column lane % 16) for 4 tokens per 16-token
-// sub-tile; the online softmax (base 2) needs only per-lane work plus two cross-lane steps for
-// the max; the probabilities are already the B operand of O^T = V^T P^T, whose A operand (16
+// sub-tile; the online softmax (base 2) needs only per-lane work plus two cross-row lane swaps
+// (v_permlane32_swap, v_permlane16_swap) for the max; the probabilities are already the B operand of O^T = V^T P^T, whose A operand (16
 // head_dim rows x 32 tokens of V) comes from LDS through transposing reads
 // (ds_read_b64_tr_b16). The token order inside the contraction is the one the score layout
 // gives (tokens 4g..4g+3 and 16+4g..16+4g+3 for lane group g); both operands use it.
@@ -52,6 +52,22 @@ __device__ __forceinline__ int pswz(int r, int c) {
 
 template <int D>
 constexpr int kv_tile() { return D == 128 ? 64 : 32; }
+
+// Max / sum over the four lanes l, l^16, l^32, l^48 (the four lane groups holding one query
+// row's scores) with the cross-row swaps of the vector ALU: each swap exchanges halves between
+// two copies of x, so combining the two results combines lane pairs, whichever copy got which.
+__device__ __forceinline__ float rows4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 // One KV tile's rows held in registers between the global load and the LDS store. Each thread
 // serves one token of the tile (TPT threads per token) and N consecutive 16-byte chunks of its K
@@ -257,8 +273,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(LaunchArgs a, int tpw) 
             mx = fmaxf(mx, v);
           }
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = rows4_max(mx);
       const bool raise = mx > m[rs] + 8.f;
       if (__any(raise)) {
         const float m_new = raise ? mx : m[rs];
@@ -318,9 +333,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(LaunchArgs a, int tpw) 
   // ---- epilogue: row sums across the four lane groups, normalize, write o and lse
 #pragma unroll
   for (int rs = 0; rs < RS; ++rs) {
-    float lt = l[rs];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
+    const float lt = rows4_sum(l[rs]);
     if (!row_ok[rs]) continue;
     const int64_t orow = ((int64_t)b * T + trow[rs]) * a.Hq + hrow[rs];
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
