@@ -163,7 +163,7 @@ template <int D>
 constexpr int row_sets() { return D == 128 ? 2 : 1; }
 
 template <int D, bool I8>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(LaunchArgs a, int tpw) {
+__global__ __launch_bounds__(256, 2) void prefill_kernel(LaunchArgs a, int tpw, int qtiles) {
   constexpr int KT = kv_tile<D>();
   constexpr int RS = row_sets<D>();
   constexpr int NST = KT / 16;   // 16-token score sub-tiles per KV tile
@@ -177,8 +177,23 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(LaunchArgs a, int tpw) 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c16 = lane & 15, g4 = lane >> 4;
-  const int b = blockIdx.z, kvh = blockIdx.y;
-  const int qt = gridDim.x - 1 - blockIdx.x;  // heaviest query tiles first
+  // Work item of this workgroup: (sequence b, KV head, query tile). Workgroups are handed to
+  // the 8 XCDs in turn (linear id mod 8), and every query tile of one (sequence, KV head) pair
+  // re-reads that pair's K/V tiles, so when the pairs divide evenly the pairs p = x, x+8, ...
+  // all go to XCD x: their tiles then stay in one L2 instead of being fetched into all eight.
+  // Within an XCD the latest (heaviest) query tiles start first.
+  const int pairs = a.Hkv * a.batch;
+  const int id = blockIdx.x;
+  int pair, qt;
+  if (pairs % 8 == 0) {
+    const int per_xcd = pairs / 8, k = id / 8;
+    qt = qtiles - 1 - k / per_xcd;
+    pair = (id % 8) + 8 * (k % per_xcd);
+  } else {
+    qt = qtiles - 1 - id % qtiles;
+    pair = id / qtiles;
+  }
+  const int kvh = pair % a.Hkv, b = pair / a.Hkv;
   const int G = a.G, T = a.T;
   int L = a.kv_len[b];
   L = L < 0 ? 0 : (L > a.max_kv_len ? a.max_kv_len : L);
@@ -352,9 +367,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(LaunchArgs a, int tpw) 
 template <int D>
 void launch_pd(const LaunchArgs &a, hipStream_t st) {
   const int tpw = 64 * row_sets<D>() / a.G;  // query tokens per workgroup: its rows / G
-  const dim3 grid((a.T + tpw - 1) / tpw, a.Hkv, a.batch);
-  if (a.int8) prefill_kernel<D, true><<<grid, 256, 0, st>>>(a, tpw);
-  else prefill_kernel<D, false><<<grid, 256, 0, st>>>(a, tpw);
+  const int qtiles = (a.T + tpw - 1) / tpw;
+  const unsigned grid = (unsigned)qtiles * a.Hkv * a.batch;
+  if (a.int8) prefill_kernel<D, true><<<grid, 256, 0, st>>>(a, tpw, qtiles);
+  else prefill_kernel<D, false><<<grid, 256, 0, st>>>(a, tpw, qtiles);
 }
 
 }  // namespace
