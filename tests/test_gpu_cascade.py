@@ -93,3 +93,39 @@ def test_cascade_prefix_suffix(kv):
     o, lse = skvd.merge_states(o_s, l_s)
     torch.cuda.synchronize()
     compare(o.reshape(o_pre.shape), lse.reshape(l_pre.shape), ro, rl, what=f"cascade {kv}")
+
+
+def test_merge_states_graph_capture_replay():
+    import quantized_kv_cache_page_amd as skvd
+    rng = np.random.default_rng(74)
+    o_s, l_s = random_states(rng, 3, 2000, 128)
+    od, ld = torch.from_numpy(o_s).cuda(), torch.from_numpy(l_s).cuda()
+    out = torch.empty((2000, 128), dtype=torch.float16, device="cuda")
+    lse = torch.empty((2000,), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        skvd.merge_states(od, ld, out=out, lse=lse)
+    ro, rl = oracle.merge_states(o_s.astype(np.float64), l_s.astype(np.float64))
+    ref = None
+    for i in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        compare(out.reshape(2000, 1, 128), lse.reshape(2000, 1), ro, rl, what=f"replay {i}")
+        if ref is None:
+            ref = (out.clone(), lse.clone())
+        else:
+            assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1])
+        torch.ones(1 << 20, device="cuda").sum()
+
+
+def test_merge_many_states():
+    """Nine states (rounds of four loads plus a partial one)."""
+    import quantized_kv_cache_page_amd as skvd
+    rng = np.random.default_rng(75)
+    o_s, l_s = random_states(rng, 9, 777, 256)
+    o, lse = skvd.merge_states(torch.from_numpy(o_s).cuda(), torch.from_numpy(l_s).cuda())
+    torch.cuda.synchronize()
+    ro, rl = oracle.merge_states(o_s.astype(np.float64), l_s.astype(np.float64))
+    compare(o.reshape(777, 1, 256), lse.reshape(777, 1), ro, rl, what="merge S=9")

@@ -135,3 +135,18 @@ def test_prefill_workloads_sampled(name):
                                      [0, s.num_qo_heads - 1, total - 1,
                                       (s.q_per_seq - 1) * s.num_qo_heads]]))
     check(s, 67, rows=rows)
+
+
+def test_prefill_long_prompt_sampled():
+    """One 8192-token prompt over its own 8192 positions (128 KV tiles for the last query tile),
+    and a ragged batch whose pair count is not a multiple of 8 (the other work order)."""
+    s = workloads.spec(name="long_prompt", batch=1, q_per_seq=8192, num_qo_heads=32,
+                       num_kv_heads=8, head_dim=128, page_size=16, kv_dtype="f16",
+                       lens=("list", (8192,)))
+    rng = np.random.default_rng(68)
+    total = 8192 * 32
+    rows = np.unique(np.concatenate([rng.integers(0, total, 200), [0, total - 1]]))
+    check(s, 69, rows=rows)
+    s = workloads.spec(name="odd_pairs", batch=3, q_per_seq=300, num_qo_heads=6, num_kv_heads=3,
+                       head_dim=128, page_size=16, kv_dtype="i8", lens=("list", (300, 1000, 700)))
+    check(s, 70)
