@@ -182,10 +182,14 @@ def sweep(args):
         if args.sweep == "cliff":
             s = workloads.spec(name=f"cliff_{L}", batch=32, q_per_seq=1, num_qo_heads=32,
                                num_kv_heads=8, head_dim=128, page_size=16, lens=("fixed", L))
-        else:
+        elif args.sweep == "long":
             s = workloads.spec(name=f"long_{L}", batch=1, q_per_seq=1, num_qo_heads=32,
                                num_kv_heads=8, head_dim=128, page_size=64, lens=("fixed", L),
                                q_mult=2.0)
+        else:  # long_i8: the int8 batch's head shape at fixed long lengths, 8 sequences
+            s = workloads.spec(name=f"long_i8_{L}", batch=8, q_per_seq=1, num_qo_heads=32,
+                               num_kv_heads=8, head_dim=128, page_size=16, kv_dtype="i8",
+                               lens=("fixed", L))
         us, part_us, kvb, plan = time_decode(s, 100 + L % 97, args.steps, args.warmup,
                                              args.bps, args.reducer, args.schedule,
                                              args.wgs_per_cu)
@@ -504,7 +508,7 @@ def main():
                     help="pool layout: nhd = [pages, P, Hkv, D] (the workload's); hnd = each KV "
                          "head's page rows contiguous, passed through the same strides")
     ap.add_argument("--no-stream-ref", action="store_true")
-    ap.add_argument("--sweep", choices=["cliff", "long"], default=None,
+    ap.add_argument("--sweep", choices=["cliff", "long", "long_i8"], default=None,
                     help="instead of the bench line: cliff = B=32, 32/8 heads, D=128, P=16 at "
                          "uniform kv_len across the 2048-token boundary; long = B=1, the long-"
                          "context shape, kv_len 8192..131072. One JSON line per point.")
