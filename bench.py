@@ -55,12 +55,10 @@ def kernel_source_hash() -> str:
 
 
 def append_source_hash() -> str:
-    """Hash of the append kernel's source and of api.cpp (its launch shape)."""
-    csrc = os.path.join(ROOT, "quantized_kv_cache_page_amd", "csrc")
+    """Hash of the append kernel's source (append.hip holds the kernel and its launch shape)."""
     h = hashlib.sha256()
-    for f in ("append.hip", "api.cpp"):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
+    with open(os.path.join(ROOT, "quantized_kv_cache_page_amd", "csrc", "append.hip"), "rb") as fh:
+        h.update(fh.read())
     return h.hexdigest()[:16]
 
 

@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define SKVD_ABI_VERSION 7
+#define SKVD_ABI_VERSION 8
 
 typedef enum {
   SKVD_OK = 0,
@@ -282,6 +282,14 @@ skvd_status skvd_prefill_check(const skvd_plan *plan, const skvd_decode_args *ar
 /* Prefill: one kernel on `stream` (a hipStream_t; NULL is the null stream), asynchronous. The
  * current HIP device must be the plan's device. Errors as for skvd_decode. */
 skvd_status skvd_prefill(const skvd_plan *plan, const skvd_decode_args *args, void *stream);
+
+/* Batch-aware routing (llama-cpp-turboquant PR #176, section "Changes": at most 8 query
+ * tokens per sequence stay on the decode path, larger batches go to the tiled matrix-core
+ * kernel): skvd_decode when args->q_per_seq <= the plan's max_q_per_seq (itself <= 8), else
+ * skvd_prefill. Same arguments, result and errors as the route taken; the workspace is used
+ * only by the decode route. */
+skvd_status skvd_attention(const skvd_plan *plan, const skvd_decode_args *args, void *workspace,
+                           size_t workspace_bytes, void *stream);
 
 /* ---------------------------------------------------------------------- merge states
  * Cascade (shared-prefix) attention: merge S attention states of each row, computed over

@@ -12,6 +12,6 @@ from ._binding import (  # noqa: F401
     skvd_plan_create, skvd_plan_describe, skvd_plan_destroy, skvd_plan_get_info,
     skvd_plan_params, skvd_plan_workspace_bytes, skvd_decode_args, status_string,
     skvd_stream_read, stream_read, skvd_append, skvd_append_check, skvd_append_args,
-    skvd_prefill, skvd_prefill_check, skvd_merge_states, merge_states,
+    skvd_prefill, skvd_prefill_check, skvd_merge_states, merge_states, skvd_attention,
     STATUS_KV_LEN_CLAMPED, STATUS_PAGE_CLAMPED,
 )

@@ -21,7 +21,7 @@ REDUCERS = {"auto": 0, "direct": 1, "cooperative": 2, "multipass": 3, "hierarchi
 REDUCER_NAMES = {v: k for k, v in REDUCERS.items()}
 SCHEDULES = {"auto": 0, "static": 1, "balanced": 2}
 SCHEDULE_NAMES = {v: k for k, v in SCHEDULES.items()}
-ABI_VERSION = 7
+ABI_VERSION = 8
 STATUS_KV_LEN_CLAMPED = 0x1
 STATUS_PAGE_CLAMPED = 0x2
 
@@ -108,6 +108,8 @@ SIGNATURES = {
                                          ctypes.c_void_p, ctypes.c_void_p]),
     "skvd_stream_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                         ctypes.c_void_p]),
+    "skvd_attention": (ctypes.c_int, [_PLAN_P, ctypes.POINTER(skvd_decode_args), ctypes.c_void_p,
+                                      ctypes.c_size_t, ctypes.c_void_p]),
     "skvd_merge_states": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                          ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
                                          ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
@@ -220,6 +222,10 @@ def skvd_decode_merge(plan, args, workspace, workspace_bytes, stream) -> int:
 def skvd_gather_debug(plan, args, max_len, dk, dv, dks, dvs, stream) -> int:
     return int(lib().skvd_gather_debug(plan, ctypes.byref(args), max_len, dk, dv, dks, dvs,
                                        stream))
+
+
+def skvd_attention(plan, args, workspace, workspace_bytes, stream) -> int:
+    return int(lib().skvd_attention(plan, ctypes.byref(args), workspace, workspace_bytes, stream))
 
 
 def skvd_merge_states(o_states, o_state_stride, o_row_stride, lse_states, lse_state_stride,
@@ -443,6 +449,18 @@ class Plan:
                            out, lse, q_per_seq)
         return skvd_decode_check(self.handle, a, self.workspace_bytes if workspace_bytes is None
                                  else workspace_bytes)
+
+    def attend(self, q, k_pages, v_pages, page_table, kv_len, sm_scale, k_scales=None,
+               v_scales=None, out=None, lse=None, q_per_seq=1, stream=None):
+        """skvd_attention: the decode for q_per_seq <= max_q_per_seq, the tiled route beyond
+        (the pages' batch-aware routing). Returns (o, lse) as run()."""
+        out, lse = self._outputs(q, out, lse)
+        ws = self.ensure_workspace()
+        a = self.make_args(q, k_pages, v_pages, page_table, kv_len, sm_scale, k_scales, v_scales,
+                           out, lse, q_per_seq)
+        _check(skvd_attention(self.handle, a, ws.data_ptr(), self.workspace_bytes,
+                              self._stream(stream)), "skvd_attention")
+        return out, lse
 
     def prefill(self, q, k_pages, v_pages, page_table, kv_len, sm_scale, k_scales=None,
                 v_scales=None, out=None, lse=None, q_per_seq=1, stream=None):

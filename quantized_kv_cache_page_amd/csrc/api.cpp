@@ -270,6 +270,18 @@ skvd_status skvd_decode(const skvd_plan *plan, const skvd_decode_args *args, voi
   return e ? hip_err(e, "merge kernel launch") : SKVD_OK;
 }
 
+skvd_status skvd_attention(const skvd_plan *plan, const skvd_decode_args *args, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+  g_err[0] = 0;
+  if (!plan) return set_err(SKVD_ERR_NULL, "plan is NULL");
+  if (!args) return set_err(SKVD_ERR_NULL, "args is NULL");
+  // the routing threshold of the pages: at most 8 query tokens (and the plan's bound) on the
+  // split-KV decode, more on the tiled route
+  if (args->q_per_seq <= plan->p.prm.max_q_per_seq)
+    return skvd_decode(plan, args, workspace, workspace_bytes, stream);
+  return skvd_prefill(plan, args, stream);
+}
+
 skvd_status skvd_gather_debug(const skvd_plan *plan, const skvd_decode_args *args,
                               int32_t max_len, void *dense_k, void *dense_v, void *dense_ks,
                               void *dense_vs, void *stream) {
@@ -345,24 +357,7 @@ skvd_status skvd_append(const skvd_plan *plan, const skvd_append_args *a, void *
   l.page_shift = sh;
   l.max_len = p.prm.max_kv_len;
   l.int8 = p.prm.kv_dtype == SKVD_KV_I8_F16SCALE32;
-  // Grid: a whole number of tokens' lanes (so a lane keeps its head and part while it strides),
-  // each lane serving up to skvd::kAppendTokensPerLane tokens per round; at most one round of
-  // resident 256-lane workgroups, fewer for a small append.
-  l.lanes_per_token = l.Hkv * l.D / 8;
-  int64_t g0 = 1;
-  {
-    int64_t x = l.lanes_per_token, y = 256;
-    while (y) { const int64_t t = x % y; x = y; y = t; }
-    g0 = l.lanes_per_token / x;  // workgroups per whole number of tokens
-  }
-  const int64_t toks = (a->num_tokens + skvd::kAppendTokensPerLane - 1) / skvd::kAppendTokensPerLane;
-  const int64_t want = (toks * l.lanes_per_token + 255) / 256;
-  // resident workgroups per CU: int8 77 VGPRs -> 6 waves per SIMD; f16 58 -> 8
-  const int64_t cap = (l.int8 ? 6LL : 8LL) * p.num_cus;
-  int64_t blocks = want < cap ? want : cap;
-  blocks = (blocks + g0 - 1) / g0 * g0;
-  l.blocks = (unsigned)blocks;
-  l.tok_step = (int)(blocks * 256 / l.lanes_per_token);
+  l.num_cus = p.num_cus;
   int e = skvd::launch_append(l, stream);
   return e ? hip_err(e, "append kernel launch") : SKVD_OK;
 }

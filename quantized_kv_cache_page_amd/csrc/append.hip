@@ -169,8 +169,27 @@ void launch_d(const AppendLaunch &a, hipStream_t st) {
 
 }  // namespace
 
-int launch_append(const AppendLaunch &a, void *stream) {
+int launch_append(AppendLaunch a, void *stream) {
   if (a.rows == 0 || a.batch == 0) return 0;  // nothing to write (and no table row to read)
+  // Grid: a whole number of tokens' lanes (so a lane keeps its head and part while it strides),
+  // each lane serving up to kTokensPerLane tokens per round; at most one round of resident
+  // 256-lane workgroups (int8: 77 registers -> 6 waves per SIMD; f16: 58 -> 8), fewer for a
+  // small append.
+  a.lanes_per_token = a.Hkv * a.D / 8;
+  int64_t x = a.lanes_per_token, y = 256;
+  while (y) {
+    const int64_t t = x % y;
+    x = y;
+    y = t;
+  }
+  const int64_t g0 = a.lanes_per_token / x;  // workgroups per whole number of tokens
+  const int64_t toks = (a.num_tokens + kTokensPerLane - 1) / kTokensPerLane;
+  const int64_t want = (toks * a.lanes_per_token + 255) / 256;
+  const int64_t cap = (a.int8 ? 6LL : 8LL) * a.num_cus;
+  int64_t blocks = want < cap ? want : cap;
+  blocks = (blocks + g0 - 1) / g0 * g0;
+  a.blocks = (unsigned)blocks;
+  a.tok_step = (int)(blocks * 256 / a.lanes_per_token);
   hipStream_t st = (hipStream_t)stream;
   if (a.D == 128) launch_d<128>(a, st);
   else launch_d<256>(a, st);

@@ -97,9 +97,10 @@ struct AppendLaunch {
   int64_t table_stride;
   int64_t rows;        // num_tokens * Hkv
   int num_tokens, batch, Hkv, D, page_shift, max_len, int8;
-  int lanes_per_token;  // Hkv * D / 8: one lane per 8 elements of a row, K and V together
-  int tok_step;         // tokens the whole grid covers per step (grid lanes / lanes_per_token)
-  unsigned blocks;      // 256-lane workgroups launched
+  int num_cus;          // compute units of the plan's device
+  int lanes_per_token;  // set by launch_append: Hkv * D / 8 (one lane per 8 elements of a row)
+  int tok_step;         // set by launch_append: tokens the whole grid covers per step
+  unsigned blocks;      // set by launch_append: 256-lane workgroups launched
 };
 
 // prefill.hip: the multi-token route (T > 8) over the decode's LaunchArgs; no workspace.
@@ -120,6 +121,6 @@ int launch_merge_states(const MergeStatesArgs &a, void *stream);
 
 // append.hip
 constexpr int kAppendTokensPerLane = 4;  // tokens one append lane serves per round
-int launch_append(const AppendLaunch &a, void *stream);
+int launch_append(AppendLaunch a, void *stream);
 
 }  // namespace skvd

@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol():
     for s in syms:
         assert hasattr(L, s), s
     assert set(syms) == set(bd.SIGNATURES), set(syms) ^ set(bd.SIGNATURES)
-    assert L.skvd_abi_version() == bd.ABI_VERSION == 7
+    assert L.skvd_abi_version() == bd.ABI_VERSION == 8
 
 
 def plan(**kw):
@@ -301,3 +301,14 @@ def test_merge_states_errors(over, status):
     a.update(over)
     assert bd.skvd_merge_states(*a.values()) == status
     assert skvd.last_error()
+
+
+def test_attention_routes_errors():
+    """skvd_attention reports the errors of the route it takes (no launch on the CPU)."""
+    p = plan()
+    assert bd.skvd_attention(None, good_args(p), None, 0, None) == 1
+    # T <= max_q_per_seq: the decode route, which wants its workspace
+    assert bd.skvd_attention(p.handle, good_args(p), None, p.workspace_bytes, None) == 5
+    # T above the plan's bound: the tiled route; its checks (here a bad q stride) apply
+    assert bd.skvd_attention(p.handle, good_args(p, q_per_seq=64, q_head_stride=100), None, 0,
+                             None) == 3

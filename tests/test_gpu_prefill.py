@@ -150,3 +150,23 @@ def test_prefill_long_prompt_sampled():
     s = workloads.spec(name="odd_pairs", batch=3, q_per_seq=300, num_qo_heads=6, num_kv_heads=3,
                        head_dim=128, page_size=16, kv_dtype="i8", lens=("list", (300, 1000, 700)))
     check(s, 70)
+
+
+def test_attention_routing():
+    """skvd_attention: T = 4 takes the decode (bit-identical to run()), T = 40 the tiled route
+    (bit-identical to prefill())."""
+    for T, lens in ((4, (4, 900, 3000)), (40, (40, 900, 3000))):
+        s = workloads.spec(name=f"route_T{T}", batch=3, q_per_seq=T, num_qo_heads=16,
+                           num_kv_heads=4, head_dim=128, page_size=16, kv_dtype="i8",
+                           lens=("list", lens))
+        prob = workloads.generate(s, 76)
+        dev = to_dev(prob)
+        plan = make_plan(prob, max_q_per_seq=min(T, 4))
+        args = (dev["q"], dev["k_pages"], dev["v_pages"], dev["page_table"], dev["kv_len"],
+                prob["sm_scale"], dev["k_scales"], dev["v_scales"])
+        o1, l1 = plan.attend(*args, q_per_seq=T)
+        o2, l2 = (plan.run if T <= 4 else plan.prefill)(*args, q_per_seq=T)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), T
+        ro, rl = oracle.decode(prob)
+        compare(o1, l1, ro, rl, what=f"attend T={T}")
