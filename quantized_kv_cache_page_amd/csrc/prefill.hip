@@ -123,14 +123,30 @@ __device__ __forceinline__ void load_tile(const LaunchArgs &a, int b, int kvh, i
 }
 
 // 16 signed bytes -> two groups of 8 f16, each times the f16 scale (one rounding, as the
-// decode's K path).
+// decode's K path). Exact widening without per-element conversions: flipping each byte's sign
+// bit gives u = x + 128 as an unsigned byte; a byte permute places u under the f16 exponent
+// byte of 1024 (the f16 with bits 0x64uu is 1024 + u, exactly); one packed subtract of 1152
+// leaves x exactly; one packed multiply applies the scale.
+typedef _Float16 ph2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ ph2 magic_pair16(unsigned flipped, unsigned sel) {
+  return __builtin_bit_cast(ph2, __builtin_amdgcn_perm(0x64646464u, flipped, sel)) -
+         (ph2)(_Float16)1152;
+}
+
 __device__ __forceinline__ void widen16(pu4 w, _Float16 s, ph8 *lo, ph8 *hi) {
+  const ph2 s2 = {s, s};
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const int byte = (int)(signed char)(w[e >> 2] >> (8 * (e & 3)));
-    const _Float16 x = (_Float16)byte * s;
-    if (e < 8) (*lo)[e] = x;
-    else (*hi)[e - 8] = x;
+  for (int k = 0; k < 4; ++k) {
+    const unsigned x = w[k] ^ 0x80808080u;
+    const ph2 a = magic_pair16(x, 0x04010400u) * s2;  // bytes 0, 1
+    const ph2 b = magic_pair16(x, 0x04030402u) * s2;  // bytes 2, 3
+    ph8 &dst = k < 2 ? *lo : *hi;
+    const int e0 = 4 * (k & 1);
+    dst[e0 + 0] = a[0];
+    dst[e0 + 1] = a[1];
+    dst[e0 + 2] = b[0];
+    dst[e0 + 3] = b[1];
   }
 }
 
