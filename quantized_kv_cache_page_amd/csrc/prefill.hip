@@ -195,19 +195,25 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(LaunchArgs a, int tpw, 
   const int c16 = lane & 15, g4 = lane >> 4;
   // Work item of this workgroup: (sequence b, KV head, query tile). Workgroups are handed to
   // the 8 XCDs in turn (linear id mod 8), and every query tile of one (sequence, KV head) pair
-  // re-reads that pair's K/V tiles, so when the pairs divide evenly the pairs p = x, x+8, ...
-  // all go to XCD x: their tiles then stay in one L2 instead of being fetched into all eight.
-  // Within an XCD the latest (heaviest) query tiles start first.
+  // re-reads that pair's K/V tiles, so the items of a pair go to one XCD: their tiles then stay
+  // in one L2 instead of being fetched into all eight. When the pairs divide evenly, pairs
+  // x, x+8, ... go to XCD x, latest (heaviest) query tiles of all of them first. Otherwise XCD x
+  // takes a contiguous run of the (pair, query tile) list -- as many items as ids = x mod 8 --
+  // heaviest tile of each pair first; only the pairs cut at a run's ends span two XCDs.
   const int pairs = a.Hkv * a.batch;
   const int id = blockIdx.x;
+  const int x = id % 8, k = id / 8;
   int pair, qt;
   if (pairs % 8 == 0) {
-    const int per_xcd = pairs / 8, k = id / 8;
+    const int per_xcd = pairs / 8;
     qt = qtiles - 1 - k / per_xcd;
-    pair = (id % 8) + 8 * (k % per_xcd);
+    pair = x + 8 * (k % per_xcd);
   } else {
-    qt = qtiles - 1 - id % qtiles;
-    pair = id / qtiles;
+    const int n = qtiles * pairs;  // the grid: ids with id % 8 == y number ceil((n - y) / 8)
+    const int base = n / 8, extra = n % 8;
+    const int item = x * base + min(x, extra) + k;  // runs of XCDs 0..x-1 come first
+    pair = item / qtiles;
+    qt = qtiles - 1 - item % qtiles;
   }
   const int kvh = pair % a.Hkv, b = pair / a.Hkv;
   const int G = a.G, T = a.T;
