@@ -242,6 +242,19 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(LaunchArgs a, int tpw, 
     for (int ks = 0; ks < NKS; ++ks) qv[rs][ks] = *(const ph8 *)(qp + 32 * ks);
   }
 
+  // Scores are scaled inside the exponent, p = 2^(s c - m) with c = sm_scale * log2(e) > 0,
+  // so the max is taken on unscaled scores and scaled once. A negative scale is carried by q
+  // (negating f16 is exact); a zero scale by a tiny c (masked scores stay -inf, others ~0).
+  float c = a.scale_log2;
+  if (c < 0.f) {
+    c = -c;
+#pragma unroll
+    for (int rs = 0; rs < RS; ++rs)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) qv[rs][ks] = -qv[rs][ks];
+  }
+  c = fmaxf(c, 1e-30f);
+
   pf4 acc[RS][NDT];
   float m[RS], l[RS];
 #pragma unroll
@@ -289,6 +302,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(LaunchArgs a, int tpw, 
     ph8 pb[RS][NCH];
 #pragma unroll
     for (int rs = 0; rs < RS; ++rs) {
+      // the max of the unscaled scores (c > 0), scaled once per row
       float mx = kPNegInf;
       if (need_mask) {
 #pragma unroll
@@ -296,7 +310,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(LaunchArgs a, int tpw, 
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int pos = kv0 + 16 * st + 4 * g4 + e;
-            const float v = pos <= limit[rs] ? s[rs][st][e] * a.scale_log2 : kPNegInf;
+            const float v = pos <= limit[rs] ? s[rs][st][e] : kPNegInf;
             s[rs][st][e] = v;
             mx = fmaxf(mx, v);
           }
@@ -304,13 +318,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(LaunchArgs a, int tpw, 
 #pragma unroll
         for (int st = 0; st < NST; ++st)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float v = s[rs][st][e] * a.scale_log2;
-            s[rs][st][e] = v;
-            mx = fmaxf(mx, v);
-          }
+          for (int e = 0; e < 4; ++e) mx = fmaxf(mx, s[rs][st][e]);
       }
-      mx = rows4_max(mx);
+      mx = rows4_max(mx) * c;
       const bool raise = mx > m[rs] + 8.f;
       if (__any(raise)) {
         const float m_new = raise ? mx : m[rs];
@@ -327,7 +337,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(LaunchArgs a, int tpw, 
       for (int st = 0; st < NST; ++st)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p = __builtin_amdgcn_exp2f(s[rs][st][e] - m[rs]);
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[rs][st][e], c, -m[rs]));
           s[rs][st][e] = p;
           ls += p;
         }

@@ -170,3 +170,17 @@ def test_attention_routing():
         assert torch.equal(o1, o2) and torch.equal(l1, l2), T
         ro, rl = oracle.decode(prob)
         compare(o1, l1, ro, rl, what=f"attend T={T}")
+
+
+@pytest.mark.parametrize("scale", [-0.08, 0.0])
+def test_prefill_scale_sign(scale):
+    """A negative softmax scale (carried by q) and a zero scale (uniform weights)."""
+    s = workloads.spec(name="scale", batch=2, q_per_seq=24, num_qo_heads=8, num_kv_heads=2,
+                       head_dim=128, page_size=16, kv_dtype="f16", lens=("list", (24, 300)))
+    prob = dict(workloads.generate(s, 77), sm_scale=float(np.float32(scale)))
+    dev = to_dev(prob)
+    plan = make_plan(prob, max_q_per_seq=1)
+    o, lse = prefill(plan, prob, dev)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode(prob)
+    compare(o, lse, ro, rl, what=f"scale {scale}")
