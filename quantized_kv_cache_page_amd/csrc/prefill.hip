@@ -14,7 +14,8 @@
 // 16x16x32 f16 MFMA (A = 16 K rows from LDS, B = the wave's 16 query rows, held in registers),
 // so each lane holds one query row's scores (column lane % 16) for 4 tokens per 16-token
 // sub-tile; the online softmax (base 2) needs only per-lane work plus two cross-row lane swaps
-// (v_permlane32_swap, v_permlane16_swap) for the max; the probabilities are already the B operand of O^T = V^T P^T, whose A operand (16
+// (v_permlane32_swap, v_permlane16_swap) for the max, and the row sums come from one more MFMA
+// with an all-ones operand; the probabilities are already the B operand of O^T = V^T P^T, whose A operand (16
 // head_dim rows x 32 tokens of V) comes from LDS through transposing reads
 // (ds_read_b64_tr_b16). The token order inside the contraction is the one the score layout
 // gives (tokens 4g..4g+3 and 16+4g..16+4g+3 for lane group g); both operands use it.
@@ -53,20 +54,14 @@ __device__ __forceinline__ int pswz(int r, int c) {
 template <int D>
 constexpr int kv_tile() { return D == 128 ? 64 : 32; }
 
-// Max / sum over the four lanes l, l^16, l^32, l^48 (the four lane groups holding one query
-// row's scores) with the cross-row swaps of the vector ALU: each swap exchanges halves between
-// two copies of x, so combining the two results combines lane pairs, whichever copy got which.
+// Max over the four lanes l, l^16, l^32, l^48 (the four lane groups holding one query row's
+// scores) with the cross-row swaps of the vector ALU: each swap exchanges halves between two
+// copies of x, so combining the two results combines lane pairs, whichever copy got which.
 __device__ __forceinline__ float rows4_max(float x) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float rows4_sum(float x) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // One KV tile's rows held in registers between the global load and the LDS store. Each thread
@@ -255,14 +250,18 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(LaunchArgs a, int tpw, 
   }
   c = fmaxf(c, 1e-30f);
 
-  pf4 acc[RS][NDT];
-  float m[RS], l[RS];
+  // acc: O^T tiles; lacc: the row sums, as one more MFMA tile whose A operand is all ones (every
+  // lane then holds its row's sum of the f16 probabilities that the P.V tiles also use, with no
+  // vector adds or cross-lane sums)
+  pf4 acc[RS][NDT], lacc[RS];
+  float m[RS];
+  const ph8 ones = (ph8)(_Float16)1;
 #pragma unroll
   for (int rs = 0; rs < RS; ++rs) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) acc[rs][dt] = pf4{0.f, 0.f, 0.f, 0.f};
+    lacc[rs] = pf4{0.f, 0.f, 0.f, 0.f};
     m[rs] = kMFloor;
-    l[rs] = 0.f;
   }
 
   const int ntiles = kv_end > 0 ? (kv_end + KT - 1) / KT : 0;
@@ -326,22 +325,18 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(LaunchArgs a, int tpw, 
         const float m_new = raise ? mx : m[rs];
         const float alpha = __builtin_amdgcn_exp2f(m[rs] - m_new);
         m[rs] = m_new;
-        l[rs] *= alpha;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lacc[rs][e] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
           for (int e = 0; e < 4; ++e) acc[rs][dt][e] *= alpha;
       }
-      float ls = 0.f;
 #pragma unroll
       for (int st = 0; st < NST; ++st)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[rs][st][e], c, -m[rs]));
-          s[rs][st][e] = p;
-          ls += p;
-        }
-      l[rs] += ls;
+        for (int e = 0; e < 4; ++e)
+          s[rs][st][e] = __builtin_amdgcn_exp2f(fmaf(s[rs][st][e], c, -m[rs]));
 #pragma unroll
       for (int c = 0; c < NCH; ++c)
 #pragma unroll
@@ -371,6 +366,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(LaunchArgs a, int tpw, 
         for (int rs = 0; rs < RS; ++rs)
           acc[rs][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[rs][c], acc[rs][dt], 0, 0, 0);
       }
+#pragma unroll
+      for (int rs = 0; rs < RS; ++rs)
+        lacc[rs] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[rs][c], lacc[rs], 0, 0, 0);
     }
     // the other buffer was last read in the previous iteration, which every wave has left
     if (more) store_tile<D, I8>(kv_lds[(it + 1) & 1][0], kv_lds[(it + 1) & 1][1], regs);
@@ -380,7 +378,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(LaunchArgs a, int tpw, 
   // ---- epilogue: row sums across the four lane groups, normalize, write o and lse
 #pragma unroll
   for (int rs = 0; rs < RS; ++rs) {
-    const float lt = rows4_sum(l[rs]);
+    const float lt = lacc[rs][0];
     if (!row_ok[rs]) continue;
     const int64_t orow = ((int64_t)b * T + trow[rs]) * a.Hq + hrow[rs];
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
