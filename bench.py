@@ -77,6 +77,27 @@ def measured_append_traffic(workload: str):
     return e.get("bytes_per_launch")
 
 
+def merge_source_hash() -> str:
+    """Hash of the merge-states kernel's source (cascade.hip)."""
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "quantized_kv_cache_page_amd", "csrc", "cascade.hip"), "rb") as fh:
+        h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_merge_traffic():
+    """HBM bytes per merge-states launch from the committed rocprofv3 --pmc summary, if it was
+    taken on the current kernel source; else None."""
+    try:
+        with open(os.path.join(ROOT, "profiles", "merge_states_kernel_traffic.json")) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_hash") != merge_source_hash():
+        return None
+    return d.get("bytes_per_launch")
+
+
 def measured_traffic(workload: str):
     """HBM bytes per partial-kernel launch from the committed rocprofv3 --pmc summary, if it
     was taken on the current kernel sources; else None."""
@@ -429,7 +450,8 @@ def bench_merge(args):
                                f"heads), head_dim {D}", "seed": seed, "bytes_per_call": nbytes,
                    "copies_rotated": copies},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_merge_traffic(),
                      "kernel": "merge_states_kernel", "kernel_avg_us": round(us, 3),
                      "algorithmic_bytes_per_launch": nbytes},
         "cpu_baseline": None,
