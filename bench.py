@@ -643,6 +643,37 @@ def main():
     log(f"[bench] decode {ms_call * 1e3:.2f} us/call (staged {ms_step * 1e3:.2f}), partial "
         f"kernel avg {part_avg * 1e3:.2f} us (min {min(part_ms) * 1e3:.2f})")
 
+    # The same calls replayed from a HIP graph (50 decodes captured once), three interleaved
+    # rounds of eager and graph timing: min and median per call of each.
+    n_graph = 50
+    graph = torch.cuda.CUDAGraph()
+    gstream = torch.cuda.Stream()
+    gstream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(gstream):
+        call(0)  # warm the side stream
+    torch.cuda.current_stream().wait_stream(gstream)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        for i in range(n_graph):
+            call(i)
+    eager_us, graph_us = [], []
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n_graph):
+            call(i)
+        e1.record()
+        torch.cuda.synchronize()
+        eager_us.append(e0.elapsed_time(e1) / n_graph * 1e3)
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        graph_us.append(e0.elapsed_time(e1) / n_graph * 1e3)
+    del graph
+    log(f"[bench] eager {min(eager_us):.2f}/{float(np.median(eager_us)):.2f} us/call, graph "
+        f"replay {min(graph_us):.2f}/{float(np.median(graph_us)):.2f} (min/median of 3)")
+
     stream_gbs = None
     if not args.no_stream_ref:
         # Reference: the library's plain streaming read of 2 GiB on the same GPU.
@@ -673,6 +704,11 @@ def main():
         "vs_baseline": None, "dtype": "f16", "data": "synthetic",
         "config": {"workload": workload, "seed": seed, "kv_bytes_per_call": kvb,
                    "pool_copies_rotated": copies, "plan": plan.describe()},
+        "timing_rounds": {"eager_us_min": round(min(eager_us), 3),
+                          "eager_us_median": round(float(np.median(eager_us)), 3),
+                          "graph_replay_us_min": round(min(graph_us), 3),
+                          "graph_replay_us_median": round(float(np.median(graph_us)), 3),
+                          "calls_per_round": n_graph, "rounds": 3},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "partial_kernel",
