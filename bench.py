@@ -15,8 +15,9 @@ Prints one JSON line: value = K+V bytes read per call / time per call (GB/s), pl
 roofline (the partial kernel's algorithmic K+V bytes per launch over its average launch time,
 timed with HIP events on the launching stream, against 8 TB/s) and cpu_baseline (the fp64
 oracle on the host cores over a bounded sample of the same workload). The default line also
-carries an "append" object: the int8 prefill-chunk append (32 sequences x 1024 new tokens
-quantized into the int8 cache) timed the same way. `--op append` prints the append's own line.
+carries an "append" object (the int8 prefill-chunk append: 32 sequences x 1024 new tokens
+quantized into the int8 cache) and a "prefill" object (the multi-token route on 4 x 2048-token
+prompts over an int8 cache). `--op append|prefill|merge` print those operations' own lines.
 """
 from __future__ import annotations
 
@@ -510,7 +511,7 @@ def main():
     ap.add_argument("--append", default="prefill_i8",
                     help="append workload for --op append: prefill_i8, prefill_f16, decode_i8")
     ap.add_argument("--no-append", action="store_true",
-                    help="leave the append object out of the decode line")
+                    help="leave the append and prefill objects out of the decode line")
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2)
@@ -725,6 +726,13 @@ def main():
                          "roofline_frac": round(r["achieved"] / HBM_PEAK_GBS, 4),
                          "bytes_per_call": r["bytes"]}
         log(f"[bench] append {r['us_per_call']:.2f} us/call, {r['gbs']:.0f} GB/s")
+        # the multi-token route on the int8 prompts (4 x 2048 tokens, full causal)
+        rp, _ = time_prefill("prompt_i8", 50, min(K, 100), min(args.warmup, 10))
+        res["prefill"] = {"workload": rp["workload"], "us_per_call": round(rp["us_per_call"], 3),
+                          "tflops": round(rp["tflops"], 1),
+                          "roofline_frac": round(rp["tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
+                          "bound": "mfma", "flops_per_call": rp["flops"]}
+        log(f"[bench] prefill {rp['us_per_call']:.2f} us/call, {rp['tflops']:.0f} TFLOP/s")
     if not args.no_cpu:
         log("[bench] timing the CPU oracle ...")
         res["cpu_baseline"] = cpu_baseline(prob)
