@@ -39,6 +39,7 @@ class OracleProblem(ctypes.Structure):
         ("s_page_stride", ctypes.c_int64), ("s_tok_stride", ctypes.c_int64), ("s_head_stride", ctypes.c_int64),
         ("table", ctypes.c_void_p), ("table_stride", ctypes.c_int64),
         ("kv_len", ctypes.c_void_p),
+        ("k_fp8_scale", ctypes.c_double), ("v_fp8_scale", ctypes.c_double),
     ]
 
 
@@ -57,6 +58,7 @@ class OracleAppendProblem(ctypes.Structure):
         ("num_k_pages", ctypes.c_int64), ("num_v_pages", ctypes.c_int64),
         ("s_page_stride", ctypes.c_int64), ("s_tok_stride", ctypes.c_int64), ("s_head_stride", ctypes.c_int64),
         ("table", ctypes.c_void_p), ("table_stride", ctypes.c_int64),
+        ("k_fp8_scale", ctypes.c_float), ("v_fp8_scale", ctypes.c_float),
     ]
 
 
@@ -103,6 +105,10 @@ def load(path: str | None = None):
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_void_p]
     lib.oracle_merge_states.restype = ctypes.c_int
+    lib.oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_to_double.restype = ctypes.c_double
+    lib.oracle_e4m3_from_float.argtypes = [ctypes.c_float]
+    lib.oracle_e4m3_from_float.restype = ctypes.c_uint8
     if path is None:
         _lib = lib
     return lib
@@ -116,6 +122,7 @@ def _problem(prob: dict):
     """Build the ctypes problem struct; returns (struct, keep-alive list)."""
     q, k, v = prob["q"], prob["k_pages"], prob["v_pages"]
     int8 = k.dtype == np.int8
+    fp8 = k.dtype == np.uint8  # OCP E4M3 bytes; k_scales / v_scales: one f32 each
     assert q.dtype == np.float16 and q.ndim == 3 and q.strides[2] == 2
     assert k.shape == v.shape and k.strides == v.strides and k.ndim == 4
     table = np.ascontiguousarray(prob["page_table"], dtype=np.int32)
@@ -127,8 +134,11 @@ def _problem(prob: dict):
     s.batch, s.q_per_seq = B, T
     s.num_qo_heads, s.num_kv_heads, s.head_dim = q.shape[1], k.shape[2], k.shape[3]
     s.page_size = k.shape[1]
-    s.kv_int8 = int(int8)
+    s.kv_int8 = 2 if fp8 else int(int8)
     s.sm_scale = float(np.float32(prob["sm_scale"]))
+    if fp8:
+        s.k_fp8_scale = float(np.float32(np.asarray(prob["k_scales"]).reshape(-1)[0]))
+        s.v_fp8_scale = float(np.float32(np.asarray(prob["v_scales"]).reshape(-1)[0]))
     s.q = q.ctypes.data
     s.q_tok_stride, s.q_head_stride = q.strides[0] // 2, q.strides[1] // 2
     s.k, s.v = k.ctypes.data, v.ctypes.data
@@ -193,7 +203,7 @@ def gather(prob: dict, max_len: int, lib=None):
     dk = np.zeros((B, max_len, Hkv, D), dt)
     dv = np.zeros((B, max_len, Hkv, D), dt)
     dks = dvs = None
-    if s.kv_int8:
+    if s.kv_int8 == 1:
         dks = np.zeros((B, max_len, Hkv, D // 32), np.float16)
         dvs = np.zeros((B, max_len, Hkv, D // 32), np.float16)
     rc = lib.oracle_gather(ctypes.byref(s), int(max_len), dk.ctypes.data, dv.ctypes.data,
@@ -211,13 +221,15 @@ def append(k_new, v_new, batch_idx, positions, page_table, max_len, k_pages, v_p
            k_scales=None, v_scales=None, batch=None, lib=None):
     """Write new K/V rows into copies of the pools. k_new, v_new: f16 [N, Hkv, D] (same
     strides); batch_idx, positions: int [N]; page_table [B, stride] int32; pools as in the
-    decode problem (int8 pools take f16 scale pools). Returns (k, v, ks, vs, skipped): the
-    written copies (ks, vs None for f16) and the number of tokens skipped."""
+    decode problem (int8 pools take f16 scale pools; fp8 pools, uint8 E4M3 bytes, take one f32
+    scale each). Returns (k, v, ks, vs, skipped): the written copies (ks, vs None for f16, the
+    scales unchanged for fp8) and the number of tokens skipped."""
     lib = lib or load()
     kn, vn = k_new, v_new
     assert kn.dtype == np.float16 and kn.shape == vn.shape and kn.strides == vn.strides
     assert kn.ndim == 3 and kn.strides[2] == 2
     int8 = k_pages.dtype == np.int8
+    fp8 = k_pages.dtype == np.uint8
     k, v = k_pages.copy(), v_pages.copy()
     bi = np.ascontiguousarray(batch_idx, dtype=np.int32)
     ps = np.ascontiguousarray(positions, dtype=np.int32)
@@ -225,7 +237,7 @@ def append(k_new, v_new, batch_idx, positions, page_table, max_len, k_pages, v_p
     es = k.itemsize
     s = OracleAppendProblem()
     s.num_tokens, s.num_kv_heads, s.head_dim = kn.shape[0], k.shape[2], k.shape[3]
-    s.page_size, s.kv_int8 = k.shape[1], int(int8)
+    s.page_size, s.kv_int8 = k.shape[1], 2 if fp8 else int(int8)
     s.batch = table.shape[0] if batch is None else int(batch)
     s.max_len = int(max_len)
     s.k_new, s.v_new = kn.ctypes.data, vn.ctypes.data
@@ -241,6 +253,10 @@ def append(k_new, v_new, batch_idx, positions, page_table, max_len, k_pages, v_p
         s.k_scale, s.v_scale = ks.ctypes.data, vs.ctypes.data
         s.s_page_stride, s.s_tok_stride, s.s_head_stride = (ks.strides[0] // 2, ks.strides[1] // 2,
                                                             ks.strides[2] // 2)
+    if fp8:
+        ks = np.asarray(k_scales, np.float32).reshape(-1).copy()
+        vs = np.asarray(v_scales, np.float32).reshape(-1).copy()
+        s.k_fp8_scale, s.v_fp8_scale = float(ks[0]), float(vs[0])
     s.table, s.table_stride = table.ctypes.data, table.shape[1]
     skipped = lib.oracle_append(ctypes.byref(s))
     return k, v, ks, vs, int(skipped)
@@ -249,6 +265,22 @@ def append(k_new, v_new, batch_idx, positions, page_table, max_len, k_pages, v_p
 def float_to_half_bits(x: float, lib=None) -> int:
     """f32 -> f16 bits, nearest even (the oracle's own conversion)."""
     return int((lib or load()).oracle_float_to_half(float(np.float32(x))))
+
+
+def e4m3_to_float(codes, lib=None):
+    """OCP E4M3 bytes -> their values (fp64), by the oracle's own decoding."""
+    lib = lib or load()
+    c = np.asarray(codes, np.uint8).reshape(-1)
+    return np.array([lib.oracle_e4m3_to_double(int(x)) for x in c]).reshape(np.shape(codes))
+
+
+def e4m3_from_float(x, lib=None):
+    """f32 values -> E4M3 bytes by the oracle's fp8 append rule (nearest, ties to even,
+    saturating at +-448, NaN -> 0)."""
+    lib = lib or load()
+    a = np.asarray(x, np.float32).reshape(-1)
+    return np.array([lib.oracle_e4m3_from_float(float(v)) for v in a],
+                    np.uint8).reshape(np.shape(x))
 
 
 def quantize_group(x, lib=None):

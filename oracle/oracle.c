@@ -24,7 +24,10 @@
  *              shape and strides; page counts may differ; only indexed pages are read).
  *              An f16 element widens to f64 exactly. An int8 element is value = int8 * scale
  *              with one f16 scale per 32 contiguous head_dim elements; the product is exact
- *              in f64.
+ *              in f64. An fp8 element is an OCP E4M3 byte (the AMD-Ecosystem/flashinfer PR
+ *              #397 commit messages name fp8 caches read with per-tensor k_scale and v_scale
+ *              values) times the tensor's f32 scale: value = e4m3(byte) * k_scale for K and
+ *              * v_scale for V, exact in f64.
  *   O2 heads   Query head h reads KV head floor(h / G), G = Hq / Hkv (consecutive grouping;
  *              the pages give only the head counts).
  *   O3 length  Query token t of a sequence with T query tokens and kv_len L sees positions
@@ -67,7 +70,9 @@ typedef struct {
   int32_t num_kv_heads; /* Hkv */
   int32_t head_dim;     /* D */
   int32_t page_size;    /* P */
-  int32_t kv_int8;      /* 0: f16 K/V; 1: int8 K/V with f16 scales per 32 elements */
+  int32_t kv_int8;      /* 0: f16 K/V; 1: int8 K/V with f16 scales per 32 elements;
+                           2: fp8 E4M3 K/V with one f32 scale per tensor (k_fp8_scale,
+                           v_fp8_scale) */
   int32_t pad0;
   double sm_scale;      /* the f32 scale the caller passes, widened */
   const uint16_t *q;    /* f16 bits */
@@ -79,6 +84,7 @@ typedef struct {
   const int32_t *table;
   int64_t table_stride;
   const int32_t *kv_len;
+  double k_fp8_scale, v_fp8_scale; /* fp8 cache: the per-tensor f32 scales, widened */
 } oracle_problem;
 
 /* IEEE-754 binary16 -> binary64, exact. */
@@ -91,6 +97,25 @@ double oracle_half_to_double(uint16_t h) {
     v = m ? NAN : INFINITY;
   else
     v = ldexp((double)(m + 1024), e - 25); /* (1024 + m) * 2^(e - 15 - 10) */
+  return sign ? -v : v;
+}
+
+/* OCP 8-bit floating point, E4M3 (exponent bias 7, 3 mantissa bits, no infinities):
+ * byte s.eeee.mmm is (-1)^s * 2^(e - 7) * (1 + m/8) for e > 0, (-1)^s * 2^-6 * (m/8) for
+ * e = 0, and NaN for eeee.mmm = 1111.111. Exact in f64. */
+double oracle_e4m3_to_double(uint8_t c) {
+  int sign = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+#if ORACLE_MUTANT == 17
+  if (e == 0)
+    v = ldexp((double)m, -10); /* planted: subnormal exponent off by one */
+#else
+  if (e == 0)
+    v = ldexp((double)m, -9); /* 2^-6 * m / 8 */
+#endif
+  else
+    v = ldexp((double)(8 + m), e - 10); /* 2^(e - 7) * (8 + m) / 8 */
   return sign ? -v : v;
 }
 
@@ -107,10 +132,16 @@ static int64_t row_offset(const oracle_problem *p, int b, int64_t j, int g, int6
   return page * p->page_stride + slot * p->tok_stride + (int64_t)g * p->head_stride;
 }
 
-/* O1: dequantized element d of a gathered row, in fp64. */
+/* O1: dequantized element d of a gathered row, in fp64 (tscale: the fp8 tensor scale). */
 static double kv_elem(const oracle_problem *p, const void *base, const uint16_t *scales,
-                      int64_t off, int64_t soff, int d) {
+                      double tscale, int64_t off, int64_t soff, int d) {
   if (!p->kv_int8) return oracle_half_to_double(((const uint16_t *)base)[off + d]);
+  if (p->kv_int8 == 2) {
+#if ORACLE_MUTANT == 18
+    tscale = 1.0; /* planted: tensor scale dropped */
+#endif
+    return oracle_e4m3_to_double(((const uint8_t *)base)[off + d]) * tscale;
+  }
   int group = d / 32;
 #if ORACLE_MUTANT == 5
   group = d / 16; /* planted: wrong scale group */
@@ -146,12 +177,14 @@ static double logit(const oracle_problem *p, const uint16_t *qrow, int b, int64_
   int64_t off = row_offset(p, b, j, g, &soff);
 #if ORACLE_MUTANT == 8
   const void *kb = p->v; const uint16_t *ks = p->v_scale; /* planted: V used as K */
+  double ts = p->v_fp8_scale;
 #else
   const void *kb = p->k; const uint16_t *ks = p->k_scale;
+  double ts = p->k_fp8_scale;
 #endif
   double dot = 0.0;
   for (int d = 0; d < p->head_dim; ++d)
-    dot += oracle_half_to_double(qrow[d]) * kv_elem(p, kb, ks, off, soff, d);
+    dot += oracle_half_to_double(qrow[d]) * kv_elem(p, kb, ks, ts, off, soff, d);
 #if ORACLE_MUTANT == 2
   return dot; /* planted: scale dropped */
 #else
@@ -199,7 +232,7 @@ static void decode_row(const oracle_problem *p, int64_t r, double *o, double *ls
     S += w;
     int64_t soff = 0;
     int64_t off = row_offset(p, b, j, g, &soff);
-    for (int d = 0; d < D; ++d) o[d] += w * kv_elem(p, p->v, p->v_scale, off, soff, d);
+    for (int d = 0; d < D; ++d) o[d] += w * kv_elem(p, p->v, p->v_scale, p->v_fp8_scale, off, soff, d);
   }
 #if ORACLE_MUTANT != 7
   for (int d = 0; d < D; ++d) o[d] /= S;
@@ -280,7 +313,7 @@ int oracle_decode_blocked(const oracle_problem *p, const int64_t *rows, int64_t 
         Si += w;
         int64_t soff = 0;
         int64_t off = row_offset(p, b, j, g, &soff);
-        for (int d = 0; d < D; ++d) oi[d] += w * kv_elem(p, p->v, p->v_scale, off, soff, d);
+        for (int d = 0; d < D; ++d) oi[d] += w * kv_elem(p, p->v, p->v_scale, p->v_fp8_scale, off, soff, d);
       }
       /* merge block i into the running state */
       double Mn = mi > M ? mi : M;
@@ -297,7 +330,8 @@ int oracle_decode_blocked(const oracle_problem *p, const int64_t *rows, int64_t 
   return 0;
 }
 
-/* O1 alone: copy the raw elements (and, for int8, the raw f16 scale bits) of every visible
+/* O1 alone: copy the raw elements (and, for int8, the raw f16 scale bits; fp8 has none per
+ * row) of every visible
  * position j < kv_len[b] into dense [B, max_len, Hkv, D] (and [B, max_len, Hkv, D/32])
  * arrays. Positions at or beyond kv_len are left untouched. */
 int oracle_gather(const oracle_problem *p, int64_t max_len, void *dense_k, void *dense_v,
@@ -313,7 +347,7 @@ int oracle_gather(const oracle_problem *p, int64_t max_len, void *dense_k, void 
         int64_t dst = (((int64_t)b * max_len + j) * Hkv + g);
         memcpy((char *)dense_k + dst * D * es, (const char *)p->k + off * es, (size_t)D * es);
         memcpy((char *)dense_v + dst * D * es, (const char *)p->v + off * es, (size_t)D * es);
-        if (p->kv_int8) {
+        if (p->kv_int8 == 1) {
           memcpy(dense_ks + dst * ng, p->k_scale + soff, sizeof(uint16_t) * ng);
           memcpy(dense_vs + dst * ng, p->v_scale + soff, sizeof(uint16_t) * ng);
         }
@@ -353,6 +387,12 @@ int oracle_num_threads(void) {
  *                c = clip(rint(x / s), -127, 127), x / s in f32, rint to nearest even;
  *                s = 0 (an all-zero group, or a below f16's range) gives c = 0.
  *              The pages fix no precision for these decisions; f32 is the kernel's.
+ *   W4 fp8     An fp8 cache (OCP E4M3 bytes times a per-tensor f32 scale s: k_scale for K,
+ *              v_scale for V) stores for each element the E4M3 value nearest to
+ *              clip(x / s, -448, 448), x / s the f32 quotient, ties to the even mantissa;
+ *              a NaN quotient (0 / 0) stores 0. 448 is E4M3's largest finite value, so the
+ *              clip saturates rather than overflowing. The pages name the format and its
+ *              per-tensor scales only; the rule is the plainest one with the kernel's f32.
  * ============================================================================ */
 
 typedef struct {
@@ -360,7 +400,8 @@ typedef struct {
   int32_t num_kv_heads; /* Hkv */
   int32_t head_dim;     /* D */
   int32_t page_size;    /* P */
-  int32_t kv_int8;      /* 0: f16 cache; 1: int8 cache with f16 scales per 32 elements */
+  int32_t kv_int8;      /* 0: f16 cache; 1: int8 cache with f16 scales per 32 elements;
+                           2: fp8 E4M3 cache with per-tensor f32 scales */
   int32_t batch;        /* rows of the page table */
   int32_t max_len;      /* positions are < max_len */
   int32_t pad0;
@@ -374,6 +415,7 @@ typedef struct {
   int64_t s_page_stride, s_tok_stride, s_head_stride;
   const int32_t *table;
   int64_t table_stride;
+  float k_fp8_scale, v_fp8_scale; /* fp8 cache: the per-tensor scales */
 } oracle_append_problem;
 
 /* IEEE-754 binary32 -> binary16, rounded to nearest, ties to even (the default IEEE rounding).
@@ -426,13 +468,44 @@ void oracle_quantize_group(const uint16_t *x, int n, int8_t *codes, uint16_t *sc
   }
 }
 
-/* W1-W3 for one row of one pool. */
+/* W4 for one f32 value: the byte of the nearest E4M3 value to clip(q, -448, 448), ties to
+ * the even mantissa, found by comparing against every finite non-negative E4M3 magnitude
+ * (bytes 0x00 .. 0x7E, in increasing order of value). */
+uint8_t oracle_e4m3_from_float(float q) {
+  if (isnan(q)) return 0;
+  uint8_t sign = signbit(q) ? 0x80 : 0;
+  double a = fabs((double)q);
+  if (a > 448.0) a = 448.0;
+  int best = 0;
+  double best_d = INFINITY;
+  for (int c = 0; c <= 0x7E; ++c) {
+    double d = fabs(oracle_e4m3_to_double((uint8_t)c) - a);
+#if ORACLE_MUTANT == 19
+    if (d < best_d) { /* planted: ties go to the smaller magnitude */
+#else
+    if (d < best_d || (d == best_d && (c & 1) == 0)) {
+#endif
+      best = c;
+      best_d = d;
+    }
+  }
+  return (uint8_t)(sign | best);
+}
+
+/* W1-W4 for one row of one pool. */
 static void append_row(const oracle_append_problem *p, const uint16_t *src, void *pool,
-                       uint16_t *scales, int64_t page, int64_t slot, int g) {
+                       uint16_t *scales, float tscale, int64_t page, int64_t slot, int g) {
   int D = p->head_dim;
   int64_t off = page * p->page_stride + slot * p->tok_stride + (int64_t)g * p->head_stride;
   if (!p->kv_int8) {
     memcpy((uint16_t *)pool + off, src, sizeof(uint16_t) * (size_t)D);
+    return;
+  }
+  if (p->kv_int8 == 2) {
+    for (int d = 0; d < D; ++d) {
+      float x = (float)oracle_half_to_double(src[d]);
+      ((uint8_t *)pool)[off + d] = oracle_e4m3_from_float(x / tscale);
+    }
     return;
   }
   int64_t soff = page * p->s_page_stride + slot * p->s_tok_stride + (int64_t)g * p->s_head_stride;
@@ -462,8 +535,10 @@ int64_t oracle_append(const oracle_append_problem *p) {
 #endif
       const uint16_t *kr = p->k_new + i * p->new_tok_stride + (int64_t)g * p->new_head_stride;
       const uint16_t *vr = p->v_new + i * p->new_tok_stride + (int64_t)g * p->new_head_stride;
-      if (page >= 0 && page < p->num_k_pages) append_row(p, kr, p->k, p->k_scale, page, slot, gg);
-      if (page >= 0 && page < p->num_v_pages) append_row(p, vr, p->v, p->v_scale, page, slot, gg);
+      if (page >= 0 && page < p->num_k_pages)
+        append_row(p, kr, p->k, p->k_scale, p->k_fp8_scale, page, slot, gg);
+      if (page >= 0 && page < p->num_v_pages)
+        append_row(p, vr, p->v, p->v_scale, p->v_fp8_scale, page, slot, gg);
     }
   }
   return skipped;

@@ -17,8 +17,8 @@ import torch.nn.functional as F
 
 def paged_from_dense(rng, q, Kd, Vd, L, P, *, T=1, spare=3, extra_heads=0, Ks=None, Vs=None,
                      sm_scale=None, table_pad=2):
-    """q [B*T, Hq, D] f16; Kd, Vd [B, Lmax, Hkv, D] (f16 or int8); Ks, Vs [B, Lmax, Hkv, D/32]
-    f16 scales for int8. Returns a problem dict whose pools hold position j of sequence b at
+    """q [B*T, Hq, D] f16; Kd, Vd [B, Lmax, Hkv, D] (f16, int8, or uint8 E4M3 bytes); Ks, Vs
+    [B, Lmax, Hkv, D/32] f16 scales for int8, or the [1] f32 tensor scales for E4M3. Returns a problem dict whose pools hold position j of sequence b at
     page table[b, j // P], slot j % P, with pages randomly permuted among spare NaN pages."""
     B, Lmax, Hkv, D = Kd.shape
     L = np.asarray(L, np.int32)
@@ -28,7 +28,10 @@ def paged_from_dense(rng, q, Kd, Vd, L, P, *, T=1, spare=3, extra_heads=0, Ks=No
     perm = rng.permutation(N)
     Hs = Hkv + extra_heads
     int8 = Kd.dtype == np.int8
-    if int8:
+    if Kd.dtype == np.uint8:
+        kbig = np.full((N, P, Hs, D), 0x7F, np.uint8)  # the E4M3 NaN byte
+        vbig = np.full((N, P, Hs, D), 0x7F, np.uint8)
+    elif int8:
         kbig = np.full((N, P, Hs, D), 127, np.int8)
         vbig = np.full((N, P, Hs, D), 127, np.int8)
         ksb = np.full((N, P, Hs, D // 32), np.nan, np.float16)
@@ -56,11 +59,23 @@ def paged_from_dense(rng, q, Kd, Vd, L, P, *, T=1, spare=3, extra_heads=0, Ks=No
     if int8:
         prob["k_scales"] = ksb[:, :, :Hkv]
         prob["v_scales"] = vsb[:, :, :Hkv]
+    if Kd.dtype == np.uint8:
+        prob["k_scales"] = np.asarray(Ks, np.float32).reshape(1)
+        prob["v_scales"] = np.asarray(Vs, np.float32).reshape(1)
     return prob
 
 
+def e4m3_values(x):
+    """OCP E4M3 bytes -> fp64 values by torch's float8_e4m3fn decoding (a library routine)."""
+    t = torch.from_numpy(np.ascontiguousarray(x, np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
 def dequant(x, s):
-    """Stored int8 values times their f16 scale (one per 32 elements), in fp64."""
+    """Stored int8 values times their f16 scale (one per 32 elements), or E4M3 bytes times the
+    tensor's f32 scale, in fp64."""
+    if x.dtype == np.uint8:
+        return e4m3_values(x) * float(np.asarray(s, np.float32).reshape(-1)[0])
     if s is None:
         return x.astype(np.float64)
     return x.astype(np.float64) * np.repeat(s.astype(np.float64), 32, axis=-1)

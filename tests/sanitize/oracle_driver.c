@@ -21,6 +21,7 @@ typedef struct {
   const int32_t *table;
   int64_t table_stride;
   const int32_t *kv_len;
+  double k_fp8_scale, v_fp8_scale;
 } oracle_problem;
 
 typedef struct {
@@ -34,6 +35,7 @@ typedef struct {
   int64_t s_page_stride, s_tok_stride, s_head_stride;
   const int32_t *table;
   int64_t table_stride;
+  float k_fp8_scale, v_fp8_scale;
 } oracle_append_problem;
 
 int oracle_decode(const oracle_problem *, const int64_t *, int64_t, double *, double *, int);
@@ -76,7 +78,13 @@ static int run(int int8, int T) {
   void *k = xmalloc(elems * es), *v = xmalloc(elems * es);
   uint16_t *ks = NULL, *vs = NULL;
   const size_t sel = (size_t)total_pages * P * Hkv * (D / 32);
-  if (int8) {
+  if (int8 == 2) { /* fp8 E4M3 bytes, no NaN byte; per-tensor scales in the problem */
+    for (size_t i = 0; i < elems; ++i) {
+      uint8_t a = (uint8_t)((frand() + 1.0f) * 127.5f), c = (uint8_t)((frand() + 1.0f) * 127.5f);
+      ((uint8_t *)k)[i] = (a & 0x7F) == 0x7F ? a ^ 1 : a;
+      ((uint8_t *)v)[i] = (c & 0x7F) == 0x7F ? c ^ 1 : c;
+    }
+  } else if (int8) {
     ks = xmalloc(sizeof(uint16_t) * sel);
     vs = xmalloc(sizeof(uint16_t) * sel);
     for (size_t i = 0; i < elems; ++i) {
@@ -101,7 +109,7 @@ static int run(int int8, int T) {
   oracle_problem p = {B, T, Hq, Hkv, D, P, int8, 0, 0.125, q, (int64_t)Hq * D, D, k, v, ks, vs,
                       (int64_t)P * Hkv * D, (int64_t)Hkv * D, D,
                       (int64_t)P * Hkv * (D / 32), (int64_t)Hkv * (D / 32), D / 32,
-                      table, max_pages, kv_len};
+                      table, max_pages, kv_len, 0.05, 0.07};
   const int64_t rows = (int64_t)B * T * Hq;
   double *o = xmalloc(sizeof(double) * rows * D), *lse = xmalloc(sizeof(double) * rows);
   double *o2 = xmalloc(sizeof(double) * rows * D), *lse2 = xmalloc(sizeof(double) * rows);
@@ -111,8 +119,8 @@ static int run(int int8, int T) {
   /* gather */
   const int max_len = 37;
   void *dk = xmalloc((size_t)B * max_len * Hkv * D * es), *dv = xmalloc((size_t)B * max_len * Hkv * D * es);
-  uint16_t *dks = int8 ? xmalloc(sizeof(uint16_t) * B * max_len * Hkv * (D / 32)) : NULL;
-  uint16_t *dvs = int8 ? xmalloc(sizeof(uint16_t) * B * max_len * Hkv * (D / 32)) : NULL;
+  uint16_t *dks = int8 == 1 ? xmalloc(sizeof(uint16_t) * B * max_len * Hkv * (D / 32)) : NULL;
+  uint16_t *dvs = int8 == 1 ? xmalloc(sizeof(uint16_t) * B * max_len * Hkv * (D / 32)) : NULL;
   bad |= oracle_gather(&p, max_len, dk, dv, dks, dvs) != 0;
   /* append: tokens of sequences 1 and 2, plus skipped ones (bad sequence, bad position) */
   const int N = 8;
@@ -127,7 +135,7 @@ static int run(int int8, int T) {
   oracle_append_problem ap = {N, Hkv, D, P, int8, B, max_pages * P, 0, kn, vn, (int64_t)Hkv * D, D,
                               bi, pos, k, v, ks, vs, (int64_t)P * Hkv * D, (int64_t)Hkv * D, D,
                               total_pages, total_pages, (int64_t)P * Hkv * (D / 32),
-                              (int64_t)Hkv * (D / 32), D / 32, table, max_pages};
+                              (int64_t)Hkv * (D / 32), D / 32, table, max_pages, 0.05f, 0.07f};
   const int64_t skipped = oracle_append(&ap);
   bad |= skipped != 3;
   /* merge two states of every row, one of them empty for the first rows */
@@ -145,7 +153,7 @@ static int run(int int8, int T) {
 
 int main(void) {
   int bad = 0;
-  for (int int8 = 0; int8 < 2; ++int8)
+  for (int int8 = 0; int8 < 3; ++int8) /* f16, int8, fp8 */
     for (int T = 1; T <= 3; T += 2) bad |= run(int8, T);
   printf(bad ? "oracle driver: FAILED\n" : "oracle driver: ok\n");
   return bad;

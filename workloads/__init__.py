@@ -1,7 +1,8 @@
 """Seeded synthetic inputs for paged decode attention.
 
 This module only builds inputs: it draws lengths, page permutations and N(0,1) values, and
-for the int8 cache it builds the stored int8 values and f16 scales from N(0,1) data. It holds
+for the int8 cache it builds the stored int8 values and f16 scales from N(0,1) data; for the
+fp8 cache it draws E4M3 bytes and per-tensor f32 scales directly. It holds
 none of the decode's arithmetic, so both the HIP path and the CPU oracle consume its arrays.
 
 Workloads (synthetic stand-ins; the pages measure whole models whose weights are absent):
@@ -20,8 +21,13 @@ comes from PCG64(SeedSequence(seed, spawn_key=(k, c))), so the values do not dep
 thread count. For the int8 cache the same float32 draws are quantized, which draws nothing.
 Pools hold sum_b ceil(L_b/P) live pages plus ceil(live/16) spare pages; page ids are a random
 permutation consumed in sequence order.
+fp8 cache (kv_dtype "f8", uint8 OCP E4M3 bytes): each byte has a uniform sign bit, an exponent
+field rint(N(7, 1.5)) clipped to [0, 15] and a uniform mantissa (the NaN byte's mantissa 7 at
+exponent 15 becomes 6), drawn per chunk like the normals; k_scale and v_scale (one f32 each,
+arrays of shape [1]) are uniform in [0.1, 0.5] from default_rng((seed, 8)).
 Spare pages and the tail slots past kv_len of each sequence's last page are NaN-poisoned
-(for int8: their scales are NaN), so any read of them shows up in the output.
+(for int8: their scales are NaN; fp8: the NaN byte 0x7F), so any read of them shows up in the
+output.
 """
 from __future__ import annotations
 
@@ -40,7 +46,7 @@ class Spec:
     num_kv_heads: int
     head_dim: int
     page_size: int
-    kv_dtype: str = "f16"           # "f16" or "i8"
+    kv_dtype: str = "f16"           # "f16", "i8" or "f8"
     lens: tuple = ("fixed", 256)     # ("fixed", L) | ("uniform", lo, hi) | ("zipf", s, lo, hi) | ("list", (..))
     q_mult: float = 1.0
     identity_table: bool = False
@@ -169,10 +175,36 @@ def _normal_int8(seed, stream, shape):
     return q, sc
 
 
+def _random_e4m3(seed, stream, shape):
+    """E4M3 bytes: uniform sign, exponent field rint(N(7, 1.5)) clipped to [0, 15], uniform
+    mantissa; the NaN pattern (exponent 15, mantissa 7) is replaced by mantissa 6."""
+    out = np.empty(shape, np.uint8)
+    flat = out.reshape(-1)
+    n = flat.shape[0]
+
+    def fill(c):
+        a, b = c * _CHUNK, min(n, (c + 1) * _CHUNK)
+        r = _chunk_rng(seed, stream, c)
+        sign = r.integers(0, 2, b - a, dtype=np.uint8)
+        e = np.clip(np.rint(r.normal(7.0, 1.5, b - a)), 0, 15).astype(np.uint8)
+        m = r.integers(0, 8, b - a, dtype=np.uint8)
+        m = np.where((e == 15) & (m == 7), 6, m).astype(np.uint8)
+        flat[a:b] = (sign << 7) | (e << 3) | m
+
+    _parallel(fill, -(-n // _CHUNK))
+    return out
+
+
+def fp8_scales(seed):
+    """(k_scale, v_scale): one f32 each, arrays of shape [1], uniform in [0.1, 0.5]."""
+    r = np.random.default_rng((seed, 8)).uniform(0.1, 0.5, 2).astype(np.float32)
+    return r[:1].copy(), r[1:].copy()
+
+
 def generate(s: Spec, seed: int) -> dict:
     """Build one problem. Returns a dict of numpy arrays and ints:
-    q [B*T, Hq, D] f16; k_pages, v_pages [N, P, Hkv, D] f16 or int8; k_scales, v_scales
-    [N, P, Hkv, D/32] f16 or None; page_table [B, ceil(max_kv_len/P)] int32 (-1 past each
+    q [B*T, Hq, D] f16; k_pages, v_pages [N, P, Hkv, D] f16, int8 or uint8 (E4M3); k_scales,
+    v_scales [N, P, Hkv, D/32] f16 (int8), [1] f32 (fp8) or None; page_table [B, ceil(max_kv_len/P)] int32 (-1 past each
     sequence's pages); kv_len [B] int32; q_per_seq; sm_scale (f32 value 1/sqrt(D)); spec."""
     rng = np.random.default_rng(seed)
     B, T, Hq, Hkv, D, P = (s.batch, s.q_per_seq, s.num_qo_heads, s.num_kv_heads, s.head_dim,
@@ -206,6 +238,10 @@ def generate(s: Spec, seed: int) -> dict:
     elif s.kv_dtype == "i8":
         k, ks = _normal_int8(seed, 4, (N, P, Hkv, D))
         v, vs = _normal_int8(seed, 5, (N, P, Hkv, D))
+    elif s.kv_dtype == "f8":
+        k = _random_e4m3(seed, 4, (N, P, Hkv, D))
+        v = _random_e4m3(seed, 5, (N, P, Hkv, D))
+        ks, vs = fp8_scales(seed)
     else:
         raise ValueError(s.kv_dtype)
     if s.poison:
@@ -217,7 +253,17 @@ def generate(s: Spec, seed: int) -> dict:
 def poison_unread(k, v, ks, vs, table, L, P, spare_pages):
     """NaN-poison what a correct decode never reads: spare pages and tail slots."""
     spare = np.asarray(spare_pages, np.int64)
-    if ks is None:
+    if k.dtype == np.uint8:
+        nan = np.uint8(0x7F)  # the E4M3 NaN byte
+        if spare.size:
+            k[spare] = nan
+            v[spare] = nan
+        for b in range(L.shape[0]):
+            if L[b] % P:
+                last = table[b, (L[b] - 1) // P]
+                k[last, L[b] % P:] = nan
+                v[last, L[b] % P:] = nan
+    elif ks is None:
         nan = np.float16(np.nan)
         if spare.size:
             k[spare] = nan
@@ -291,21 +337,32 @@ def attention_flops(prob: dict) -> int:
     return int(4 * D * Hq * vis)
 
 
+def _row_pair_bytes(k) -> int:
+    D = k.shape[3]
+    if k.dtype == np.float16:
+        return 4 * D
+    if k.dtype == np.uint8:
+        return 2 * D
+    return 2 * (D + 2 * (D // 32))
+
+
 def append_bytes(prob: dict, new: dict) -> int:
     """Algorithmic bytes of one append: the new K and V rows read (2*D*2 bytes per token-head)
-    plus the cache written (2*D*2 bytes for f16; 2*(D + 2*D/32) for int8 with f16 scales)."""
+    plus the cache written (2*D*2 bytes for f16; 2*(D + 2*D/32) for int8 with f16 scales; 2*D
+    for fp8)."""
     k = prob["k_pages"]
     Hkv, D = k.shape[2], k.shape[3]
-    written = 4 * D if k.dtype == np.float16 else 2 * (D + 2 * (D // 32))
+    written = _row_pair_bytes(k)
     return int(new["k_new"].shape[0]) * Hkv * (4 * D + written)
 
 
 def kv_bytes(prob: dict) -> int:
     """Algorithmic K+V bytes one decode reads: sum_b kv_len_b * Hkv * row bytes, where a row
-    pair is 2*D*2 bytes for f16 and 2*(D + 2*D/32) bytes for int8 with f16 scales."""
+    pair is 2*D*2 bytes for f16, 2*(D + 2*D/32) bytes for int8 with f16 scales and 2*D bytes
+    for fp8 (its two per-tensor scales are not per row)."""
     k = prob["k_pages"]
     Hkv, D = k.shape[2], k.shape[3]
-    row = 4 * D if k.dtype == np.float16 else 2 * (D + 2 * (D // 32))
+    row = _row_pair_bytes(k)
     return int(np.asarray(prob["kv_len"], np.int64).sum()) * Hkv * row
 
 
