@@ -16,12 +16,13 @@ LIB_PATH = os.path.join(_PKG, "libskvd.so")
 
 SKVD_KV_F16 = 0
 SKVD_KV_I8_F16SCALE32 = 1
+SKVD_KV_FP8_E4M3 = 2
 REDUCERS = {"auto": 0, "direct": 1, "cooperative": 2, "multipass": 3, "hierarchical": 4,
             "none": 5}
 REDUCER_NAMES = {v: k for k, v in REDUCERS.items()}
 SCHEDULES = {"auto": 0, "static": 1, "balanced": 2}
 SCHEDULE_NAMES = {v: k for k, v in SCHEDULES.items()}
-ABI_VERSION = 8
+ABI_VERSION = 9
 STATUS_KV_LEN_CLAMPED = 0x1
 STATUS_PAGE_CLAMPED = 0x2
 
@@ -290,13 +291,50 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _kv_dtype_code(kv_dtype) -> int:
+    if kv_dtype in ("f16", torch.float16):
+        return SKVD_KV_F16
+    if kv_dtype in ("i8", torch.int8):
+        return SKVD_KV_I8_F16SCALE32
+    if kv_dtype in ("f8", "fp8", "e4m3", torch.uint8, torch.float8_e4m3fn):
+        return SKVD_KV_FP8_E4M3
+    raise ValueError(f"unknown kv_dtype {kv_dtype!r}")
+
+
+_POOL_DTYPES = {"f16": (torch.float16,), "i8": (torch.int8,),
+                "f8": (torch.uint8, torch.float8_e4m3fn)}
+
+
+def _set_scales(a, k_scales, v_scales, kv_dtype, where):
+    """Scale pointers (and, for int8, strides) of a decode or append argument struct."""
+    if k_scales is None:
+        if v_scales is not None:
+            raise SkvdError(4, where, "v_scales given without k_scales")
+        return
+    if v_scales is None:
+        raise SkvdError(4, where, "k_scales given without v_scales")
+    if kv_dtype == "f8":
+        if k_scales.dtype != torch.float32 or v_scales.dtype != torch.float32 or \
+                k_scales.numel() != 1 or v_scales.numel() != 1:
+            raise SkvdError(4, where, "fp8 k_scales/v_scales must be one-element float32 tensors")
+        a.k_scales, a.v_scales = k_scales.data_ptr(), v_scales.data_ptr()
+        return
+    if k_scales.dtype != torch.float16 or v_scales.stride() != k_scales.stride():
+        raise SkvdError(4, where, "k_scales/v_scales must be f16 with equal strides")
+    a.k_scales, a.v_scales = k_scales.data_ptr(), v_scales.data_ptr()
+    a.scale_page_stride, a.scale_tok_stride, a.scale_head_stride = (
+        k_scales.stride(0), k_scales.stride(1), k_scales.stride(2))
+
+
 class Plan:
     """A decode plan and its workspace.
 
     Plan(num_qo_heads, num_kv_heads, head_dim, page_size, kv_dtype, max_batch, max_q_per_seq,
          max_kv_len, device) sizes everything once, outside any capture; run() then launches
     the decode on the current stream with no allocation other than the default outputs.
-    kv_dtype is "f16" or "i8" (int8 with one f16 scale per 32 elements)."""
+    kv_dtype is "f16", "i8" (int8 with one f16 scale per 32 elements) or "f8" (OCP E4M3
+    bytes, held in uint8 tensors, with one f32 scale per tensor passed as k_scales / v_scales:
+    one-element float32 device tensors)."""
 
     def __init__(self, num_qo_heads, num_kv_heads, head_dim, page_size, kv_dtype="f16",
                  max_batch=1, max_q_per_seq=1, max_kv_len=1, device=0, num_cus=0,
@@ -310,10 +348,11 @@ class Plan:
         self.params = skvd_plan_params(
             int(num_qo_heads), int(num_kv_heads), int(head_dim), int(page_size), int(max_batch),
             int(max_q_per_seq), int(max_kv_len),
-            SKVD_KV_F16 if kv_dtype in ("f16", torch.float16) else SKVD_KV_I8_F16SCALE32,
+            _kv_dtype_code(kv_dtype),
             int(idx), int(num_cus), int(force_blocks_per_split), red, int(bool(debug)), sch,
             int(wgs_per_cu), int(heads_per_wg))
-        self.kv_dtype = "f16" if self.params.kv_dtype == SKVD_KV_F16 else "i8"
+        self.kv_dtype = {SKVD_KV_F16: "f16", SKVD_KV_I8_F16SCALE32: "i8",
+                         SKVD_KV_FP8_E4M3: "f8"}[self.params.kv_dtype]
         self.handle = skvd_plan_create(self.params)
         self.info = skvd_plan_get_info(self.handle)
         self.workspace_bytes = int(self.info.workspace_bytes)
@@ -363,9 +402,9 @@ class Plan:
                   v_scales=None, out=None, lse=None, q_per_seq=1) -> skvd_decode_args:
         if q.dtype != torch.float16:
             raise TypeError("q must be float16")
-        want = torch.float16 if self.kv_dtype == "f16" else torch.int8
-        if k_pages.dtype != want or v_pages.dtype != want:
-            raise TypeError(f"k_pages and v_pages must be {want}")
+        want = _POOL_DTYPES[self.kv_dtype]
+        if k_pages.dtype not in want or v_pages.dtype not in want:
+            raise TypeError(f"k_pages and v_pages must be {want[0]}")
         if k_pages.stride() != v_pages.stride() or k_pages.shape[1:] != v_pages.shape[1:]:
             raise SkvdError(3, "Plan.run", "K and V must share page shape and strides")
         if page_table.dtype != torch.int32 or kv_len.dtype != torch.int32:
@@ -383,14 +422,7 @@ class Plan:
         a.k_pages, a.v_pages = k_pages.data_ptr(), v_pages.data_ptr()
         a.page_stride, a.tok_stride, a.head_stride = k_pages.stride(0), k_pages.stride(1), k_pages.stride(2)
         a.num_k_pages, a.num_v_pages = k_pages.shape[0], v_pages.shape[0]
-        if k_scales is not None:
-            if k_scales.dtype != torch.float16 or v_scales is None or v_scales.stride() != k_scales.stride():
-                raise SkvdError(4, "Plan.run", "k_scales/v_scales must be f16 with equal strides")
-            a.k_scales, a.v_scales = k_scales.data_ptr(), v_scales.data_ptr()
-            a.scale_page_stride, a.scale_tok_stride, a.scale_head_stride = (
-                k_scales.stride(0), k_scales.stride(1), k_scales.stride(2))
-        elif v_scales is not None:
-            raise SkvdError(4, "Plan.run", "v_scales given without k_scales")
+        _set_scales(a, k_scales, v_scales, self.kv_dtype, "Plan.run")
         a.page_table = page_table.data_ptr()
         a.table_stride = page_table.stride(0)
         a.kv_len = kv_len.data_ptr()
@@ -488,9 +520,9 @@ class Plan:
         empty = k_new.shape[0] == 0  # torch may give an empty tensor any strides
         if (not empty and k_new.stride(2) != 1) or k_pages.stride(3) != 1:
             raise SkvdError(3, "Plan.append", "head_dim must be dense in the new rows and the pools")
-        want = torch.float16 if self.kv_dtype == "f16" else torch.int8
-        if k_pages.dtype != want or v_pages.dtype != want:
-            raise TypeError(f"k_pages and v_pages must be {want}")
+        want = _POOL_DTYPES[self.kv_dtype]
+        if k_pages.dtype not in want or v_pages.dtype not in want:
+            raise TypeError(f"k_pages and v_pages must be {want[0]}")
         if k_pages.stride() != v_pages.stride() or k_pages.shape[1:] != v_pages.shape[1:]:
             raise SkvdError(3, "Plan.append", "K and V must share page shape and strides")
         if batch_idx.dtype != torch.int32 or positions.dtype != torch.int32 or \
@@ -513,14 +545,7 @@ class Plan:
         a.k_pages, a.v_pages = k_pages.data_ptr(), v_pages.data_ptr()
         a.page_stride, a.tok_stride, a.head_stride = k_pages.stride(0), k_pages.stride(1), k_pages.stride(2)
         a.num_k_pages, a.num_v_pages = k_pages.shape[0], v_pages.shape[0]
-        if k_scales is not None:
-            if k_scales.dtype != torch.float16 or v_scales is None or v_scales.stride() != k_scales.stride():
-                raise SkvdError(4, "Plan.append", "k_scales/v_scales must be f16 with equal strides")
-            a.k_scales, a.v_scales = k_scales.data_ptr(), v_scales.data_ptr()
-            a.scale_page_stride, a.scale_tok_stride, a.scale_head_stride = (
-                k_scales.stride(0), k_scales.stride(1), k_scales.stride(2))
-        elif v_scales is not None:
-            raise SkvdError(4, "Plan.append", "v_scales given without k_scales")
+        _set_scales(a, k_scales, v_scales, self.kv_dtype, "Plan.append")
         a.page_table = page_table.data_ptr()
         a.table_stride = page_table.stride(0)
         return a
@@ -546,7 +571,7 @@ class Plan:
         dk = torch.zeros((B, max_len, Hkv, D), dtype=k_pages.dtype, device=k_pages.device)
         dv = torch.zeros_like(dk)
         dks = dvs = None
-        if k_scales is not None:
+        if k_scales is not None and self.kv_dtype == "i8":
             dks = torch.zeros((B, max_len, Hkv, D // 32), dtype=torch.float16, device=k_pages.device)
             dvs = torch.zeros_like(dks)
         o = torch.empty(q.shape, dtype=torch.float16, device=q.device)

@@ -66,6 +66,8 @@ skvd_status check_append(const skvd_plan *plan, const skvd_append_args *a) {
   if (!a) return set_err(SKVD_ERR_NULL, "args is NULL");
   const skvd::Plan &p = plan->p;
   const bool i8 = p.prm.kv_dtype == SKVD_KV_I8_F16SCALE32;
+  if (p.prm.kv_dtype == SKVD_KV_FP8_E4M3)
+    return set_err(SKVD_ERR_DTYPE, "append into an fp8 cache is not supported");
   const auto al = [](const void *ptr, uintptr_t n) { return (uintptr_t)ptr % n == 0; };
   if (a->num_tokens < 0 || a->batch < 0)
     return set_err(SKVD_ERR_SHAPE, "num_tokens=%d and batch=%d must be >= 0", a->num_tokens,
@@ -119,6 +121,8 @@ skvd_status check_prefill(const skvd_plan *plan, const skvd_decode_args *a) {
                    p.prm.max_kv_len);
   if (p.group > 64)
     return set_err(SKVD_ERR_SHAPE, "prefill needs Hq/Hkv <= 64 (got %d)", p.group);
+  if (p.prm.kv_dtype == SKVD_KV_FP8_E4M3)
+    return set_err(SKVD_ERR_DTYPE, "the multi-token route does not read fp8 caches");
   skvd_decode_args one = *a;
   one.q_per_seq = 1;  // the remaining checks do not depend on the token count
   return skvd::check_args(p, &one, p.ws_bytes, g_err, sizeof g_err);

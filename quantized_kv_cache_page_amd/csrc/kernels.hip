@@ -191,6 +191,42 @@ __device__ __forceinline__ void h16_pairs(const half8 &a, const half8 &b, half2v
   }
 }
 
+// ----------------------------------------------------------------------------- fp8 (E4M3) -> f16
+// An OCP E4M3 byte s.eeee.mmm rewritten as the f16 bits s.0eeee.mmm0000000 is the f16 of its
+// value times 2^-8, exactly: the 4-bit exponent field under f16's bias 15 instead of E4M3's 7
+// is the factor 2^-8, and E4M3's subnormals (field 0: 2^-6 * m/8) become f16 subnormals
+// (2^-14 * m/8) with the same factor. The 2^8 comes back with the per-tensor scales, folded
+// into the score scale (K) and the output (V). (The NaN byte turns into a finite f16; a cache
+// holds none.) A byte permute puts two bytes into the high bytes of the two f16 halves; the
+// sign bits stay, the other seven bits of each shift down by one.
+__device__ __forceinline__ unsigned f8_place(unsigned s0, unsigned s1, unsigned sel) {
+  const unsigned t = __builtin_amdgcn_perm(s0, s1, sel);
+  return (t & 0x80008000u) | ((t >> 1) & 0x3F803F80u);
+}
+
+// 8 E4M3 bytes (elements 0..7 in byte order) -> 8 f16 (value * 2^-8).
+__device__ __forceinline__ half8 f8x8_to_h8(uint2v w) {
+  uint4v r;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    r[2 * k] = f8_place(w[k], w[k], 0x010C000Cu);      // bytes 0, 1 -> halves 0, 1
+    r[2 * k + 1] = f8_place(w[k], w[k], 0x030C020Cu);  // bytes 2, 3 -> halves 0, 1
+  }
+  return __builtin_bit_cast(half8, r);
+}
+
+// Two E4M3 rows a (token t) and b (token t + 16), 8 elements each -> the 8 f16 pairs
+// (a_i, b_i) (values * 2^-8): byte i of a into the low half, byte i of b into the high half.
+__device__ __forceinline__ void f8_pairs(uint2v a, uint2v b, half2v *out) {
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      out[4 * w + i] = __builtin_bit_cast(
+          half2v, f8_place(b[w], a[w], ((4u + i) << 24) | 0x0C0000u | ((unsigned)i << 8) | 0x0Cu));
+  }
+}
+
 // ----------------------------------------------------------------------------- balanced schedule
 // The batch's 64-token blocks in (sequence, KV head, block) order, cut into n_shares equal
 // contiguous shares: share w covers [w N / W, (w + 1) N / W). One sequence per lane (the plan
@@ -255,7 +291,9 @@ __device__ __forceinline__ int swz(int r, int c) {
 }
 
 // D: head_dim (128/256). RB: 4-row quarters of the 16 MFMA rows in use (rows = G*T <= 4*RB).
-// I8: int8 cache with f16 scales per 32 elements. FAST: page_size >= 16, so each 16-token
+// KV: cache format, 0 f16, 1 int8 with f16 scales per 32 elements, 2 fp8 E4M3 with one f32
+// scale per tensor; the two one-byte formats share the load layout (I8 below), and only int8
+// reads per-row scales (SC). FAST: page_size >= 16, so each 16-token
 // tile lies in one page and its page id is wave-uniform. CH: tokens per chunk (16, 32 or
 // 64): the K and V registers of a chunk bound how many waves fit on a SIMD.
 // PVM: P.V on the MFMA through an LDS copy of the chunk's V (dense when several query rows
@@ -271,9 +309,12 @@ constexpr int partial_waves() {
   return D == 128 ? (RB == 1 ? (I8 ? 3 : 1) : 2) : 1;
 }
 
-template <int D, int RB, bool I8, bool FAST, int CH, bool PVM, int HW>
+template <int D, int RB, int KV, bool FAST, int CH, bool PVM, int HW>
 __global__ __launch_bounds__(64 * HW)
-__attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_kernel(LaunchArgs a) {
+__attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void partial_kernel(LaunchArgs a) {
+  constexpr bool I8 = KV != 0;  // one-byte elements
+  constexpr bool SC = KV == 1;  // int8: f16 scales per 32 elements of each row
+  constexpr bool F8 = KV == 2;  // fp8 E4M3: one f32 scale per tensor
   static_assert(CH == 16 || CH == 32 || (CH == 64 && !PVM), "chunk");
   static_assert(PVM || CH % 32 == 0, "the vector P.V pairs 16-token tiles 2h and 2h + 1");
   constexpr int NT = CH / 16;    // 16-token score tiles per chunk
@@ -292,7 +333,7 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
   // LDS, one slice per wave (each wave serves its own KV head):
   constexpr int VL = PVM ? CH * ROWB : 16;          // chunk V rows, f16
   constexpr int PL = PVM ? RM * PSTR : 4;           // probabilities [row][token]
-  constexpr int SL = I8 ? CH * (D / 128) : 1;       // int8 V scales [token][group], f16
+  constexpr int SL = SC ? CH * (D / 128) : 1;       // int8 V scales [token][group], f16
   constexpr int QL = PVM ? 4 : (CH / 2) * RM;       // vector P.V: f16 pairs (tp, tp+16) [tp][row]
   __shared__ __attribute__((aligned(16))) char v_lds_all[HW * VL];
   __shared__ __attribute__((aligned(16))) float p_lds_all[HW * PL];
@@ -310,6 +351,10 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
   const int lane = threadIdx.x & 63;
   const int Hkv = a.Hkv;
   const int Hg = Hkv / HW;  // head groups: the rows of the schedule
+  // fp8: the per-tensor scales (one f32 each in device memory) times the widening's 2^8, on
+  // the scores' scale (K) and on the output (V); 1 for the other formats
+  const float scale_log2 = F8 ? a.scale_log2 * (*(const float *)a.ks * 256.f) : a.scale_log2;
+  const float vfac = F8 ? *(const float *)a.vs * 256.f : 1.f;
   const int T = a.T, G = a.G, R = G * T;
   const int P1 = (1 << a.page_shift) - 1;
 
@@ -503,12 +548,14 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
 #pragma unroll
             for (int h = 0; h < 2; ++h)
               kq[t][m][h] = kv_load<true, uint4v>(base + off + 128 * m + 16 * h);
-          const _Float16 *sb = ksc + row_offset(pg, jte & P1, kvh, a.s_page_stride,
-                                                a.s_tok_stride, a.s_head_stride);
-          const unsigned so = 2u * (min(c16_stok, (unsigned)(lim * (int)a.s_tok_stride)) + g4);
+          if constexpr (SC) {
+            const _Float16 *sb = ksc + row_offset(pg, jte & P1, kvh, a.s_page_stride,
+                                                  a.s_tok_stride, a.s_head_stride);
+            const unsigned so = 2u * (min(c16_stok, (unsigned)(lim * (int)a.s_tok_stride)) + g4);
 #pragma unroll
-          for (int m = 0; m < KS / 4; ++m)
-            ksh[t][m] = *(const _Float16 *)((const char *)sb + so + 8 * m);
+            for (int m = 0; m < KS / 4; ++m)
+              ksh[t][m] = *(const _Float16 *)((const char *)sb + so + 8 * m);
+          }
         } else {
           const unsigned off = (min(c16_tok, (unsigned)(lim * (int)a.tok_stride)) + 8 * g4) * ES;
 #pragma unroll
@@ -528,10 +575,12 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
           for (int m = 0; m < KS / 4; ++m)
 #pragma unroll
             for (int h = 0; h < 2; ++h) kq[t][m][h] = kv_load<true, uint4v>(kp + 128 * m + 16 * h);
-          const int64_t so = row_offset(pg, j & P1, kvh, a.s_page_stride, a.s_tok_stride,
-                                        a.s_head_stride) + g4;
+          if constexpr (SC) {
+            const int64_t so = row_offset(pg, j & P1, kvh, a.s_page_stride, a.s_tok_stride,
+                                          a.s_head_stride) + g4;
 #pragma unroll
-          for (int m = 0; m < KS / 4; ++m) ksh[t][m] = ksc[so + 4 * m];
+            for (int m = 0; m < KS / 4; ++m) ksh[t][m] = ksc[so + 4 * m];
+          }
         } else {
           const char *kp = kbase + (off + 8 * g4) * ES;
 #pragma unroll
@@ -568,7 +617,7 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
         vb[s2] = kv_load<true, Vec>(vbase + (off + vlane_el) * ES);
       }
     }
-    if constexpr (I8) {
+    if constexpr (SC) {
       // scales of chunk token (lane % CH); a token past the split reads the last one's
       const int jl = min(c0 + lane % CH, tok_end - 1);
       int64_t pg;
@@ -623,7 +672,9 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
         for (int k = 0; k < KS; ++k) {
           const uint4v &q4 = kq[t][k >> 2][(k & 3) >> 1];
           const unsigned w0 = q4[2 * (k & 1)], w1 = q4[2 * (k & 1) + 1];
-          const half8 kh = i8x8_to_h8(uint2v{w0, w1}) * (half8)ksh[t][k >> 2];
+          half8 kh;
+          if constexpr (SC) kh = i8x8_to_h8(uint2v{w0, w1}) * (half8)ksh[t][k >> 2];
+          else kh = f8x8_to_h8(uint2v{w0, w1});  // fp8: k_scale * 2^8 is in the score scale
           S[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[k], kh, S[t], 0, 0, 0);
         }
       } else {
@@ -646,7 +697,7 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const int j = c0 + 16 * t + c16;
-        const float sc = j < nvis[e] ? S[t][e] * a.scale_log2 : kNegInf;
+        const float sc = j < nvis[e] ? S[t][e] * scale_log2 : kNegInf;
         S[t][e] = sc;
         cmax = fmaxf(cmax, sc);
       }
@@ -678,14 +729,16 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
       for (int s2 = 0; s2 < NS; ++s2) {
         const int row = TPS * s2 + vlane_tok;
         half8 h;
-        if constexpr (I8) {
+        if constexpr (SC) {
           h = i8x8_to_h8(vb[s2]);
+        } else if constexpr (F8) {
+          h = f8x8_to_h8(vb[s2]);
         } else {
           h = vb[s2];
         }
         *(half8 *)(v_lds + swz<ROWB>(row, lane % LPR)) = h;
       }
-      if constexpr (I8) {
+      if constexpr (SC) {
         if (lane < CH) {
 #pragma unroll
           for (int k4 = 0; k4 < D / 128; ++k4) vsc_lds[lane * (D / 128) + k4] = vsr[k4];
@@ -707,8 +760,8 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
       float pv[KPL];
 #pragma unroll
       for (int i = 0; i < KPL; ++i) pv[i] = c16 < RM ? p_lds[c16 * PSTR + KPL * g4 + i] : 0.f;
-      PvOp pa[I8 ? D / 32 : 1];
-      if constexpr (I8) {
+      PvOp pa[SC ? D / 32 : 1];
+      if constexpr (SC) {
 #pragma unroll
         for (int gg = 0; gg < D / 32; ++gg)
 #pragma unroll
@@ -732,7 +785,7 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
 #pragma unroll
           for (int i = 0; i < 4; ++i) vt[4 * h + i] = hv[i];
         }
-        const PvOp &pop = pa[I8 ? dt / 2 : 0];
+        const PvOp &pop = pa[SC ? dt / 2 : 0];
         if constexpr (CH == 32)
           acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pop, vt, acc[dt], 0, 0, 0);
         else
@@ -755,7 +808,7 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
       float al[RM];
 #pragma unroll
       for (int r = 0; r < RM; ++r) al[r] = readlane_f(alpha[r & 3], 16 * (r >> 2));
-      if constexpr (I8) {
+      if constexpr (SC) {
         if (lane < CH) {
 #pragma unroll
           for (int k4 = 0; k4 < D / 128; ++k4) vsc_lds[lane * (D / 128) + k4] = vsr[k4];
@@ -790,7 +843,9 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
           }
         }
         half2v vp[8];
-        if constexpr (I8) {
+        if constexpr (F8) {
+          f8_pairs(vb[s2], vb[s3], vp);  // fp8: v_scale * 2^8 is applied to the output
+        } else if constexpr (SC) {
           // int8 V: the pair's per-32 scales fold into the probabilities
           const int ta = TPS * s2 + vlane_tok, g = vlane_el / 32;
           const half2v sc = {vsh[ta * (D / 32) + g], vsh[(ta + 16) * (D / 32) + g]};
@@ -854,7 +909,7 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
       const int64_t row = ((int64_t)b * T + t) * Hq + kvh * G + hg;
       if (a.single) {
         const float l = lsum[e];
-        const float inv = l > 0.f ? 1.f / l : 0.f;
+        const float inv = (l > 0.f ? 1.f / l : 0.f) * vfac;
         _Float16 *o = (_Float16 *)a.o + row * D + c16;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) o[16 * dt] = (_Float16)(acc[dt][e] * inv);
@@ -862,7 +917,7 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
       } else {
         float *dst = a.ws_o + part_index(row, hg + G * t) * D + c16;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) dst[16 * dt] = acc[dt][e];
+        for (int dt = 0; dt < NDT; ++dt) dst[16 * dt] = acc[dt][e] * vfac;
         if (c16 == 0) {
           float *ml = a.ws_ml + part_index(row, hg + G * t) * 2;
           ml[0] = m[e];
@@ -894,7 +949,7 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
       const int64_t row = ((int64_t)b * T + t) * Hq + kvh * G + hg;
       if (a.single) {
         const float l = lr[r];
-        const float inv = l > 0.f ? 1.f / l : 0.f;
+        const float inv = (l > 0.f ? 1.f / l : 0.f) * vfac;
         half8 out;
 #pragma unroll
         for (int i = 0; i < 8; ++i) out[i] = (_Float16)(accv[r][i] * inv);
@@ -902,8 +957,8 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, I8>()))) void partial_ke
         if (a.lse && lane == 0) a.lse[row] = l > 0.f ? (mr[r] + __log2f(l)) * kLn2 : kNegInf;
       } else {
         float *dst = a.ws_o + part_index(row, hg + G * t) * D + vlane_el;
-        *(float4v *)dst = float4v{accv[r][0], accv[r][1], accv[r][2], accv[r][3]};
-        *(float4v *)(dst + 4) = float4v{accv[r][4], accv[r][5], accv[r][6], accv[r][7]};
+        *(float4v *)dst = float4v{accv[r][0], accv[r][1], accv[r][2], accv[r][3]} * vfac;
+        *(float4v *)(dst + 4) = float4v{accv[r][4], accv[r][5], accv[r][6], accv[r][7]} * vfac;
         if (lane == 0) {
           float *ml = a.ws_ml + part_index(row, hg + G * t) * 2;
           ml[0] = mr[r];
@@ -1175,7 +1230,7 @@ __global__ __launch_bounds__(64) void gather_kernel(LaunchArgs a, int max_len, c
     *(unsigned *)(dk + dst * D * ES + i) = *(const unsigned *)(ks + i);
     *(unsigned *)(dv + dst * D * ES + i) = *(const unsigned *)(vs + i);
   }
-  if constexpr (I8) {
+  if (I8 && !a.fp8) {  // int8: the row's f16 scales (fp8 has one per tensor)
     const int64_t sk = row_offset(pk, j & P1, kvh, a.s_page_stride, a.s_tok_stride, a.s_head_stride);
     const int64_t sv = row_offset(pv, j & P1, kvh, a.s_page_stride, a.s_tok_stride, a.s_head_stride);
     for (int g = 0; g < D / 32; ++g) {
@@ -1233,39 +1288,39 @@ static void launch_one(K kernel, dim3 grid, unsigned threads, hipStream_t st,
     kernel<<<grid, threads, 0, st>>>(la);
 }
 
-template <int D, int RB, bool I8, int HW>
+template <int D, int RB, int KV, int HW>
 static void launch_partial_hw(const LaunchArgs &la, dim3 grid, hipStream_t st, bool fast,
                               const KernelEvents &ev) {
-  constexpr int CH = chunk_tokens<D, RB, I8>();
+  constexpr int CH = chunk_tokens<D, RB, KV != 0>();
   constexpr bool PVM = pv_on_mfma<D, RB>();
   if (fast)
-    launch_one(partial_kernel<D, RB, I8, true, CH, PVM, HW>, grid, 64 * HW, st, ev, la);
+    launch_one(partial_kernel<D, RB, KV, true, CH, PVM, HW>, grid, 64 * HW, st, ev, la);
   else
-    launch_one(partial_kernel<D, RB, I8, false, CH, PVM, HW>, grid, 64 * HW, st, ev, la);
+    launch_one(partial_kernel<D, RB, KV, false, CH, PVM, HW>, grid, 64 * HW, st, ev, la);
 }
 
 // KV heads per workgroup (one wave each): the D=128 single-quarter variants read each token's
 // rows of 4 (or 2) KV heads from one CU together (int8: and share the token's scale line);
 // every other variant serves one head.
-template <int D, int RB, bool I8>
+template <int D, int RB, int KV>
 static void launch_partial_t(const LaunchArgs &la, dim3 grid, hipStream_t st, bool fast,
                              const KernelEvents &ev) {
   if constexpr (D == 128 && RB == 1) {
-    if (la.heads_per_wg == 8) return launch_partial_hw<D, RB, I8, 8>(la, grid, st, fast, ev);
-    if (la.heads_per_wg == 4) return launch_partial_hw<D, RB, I8, 4>(la, grid, st, fast, ev);
-    if (la.heads_per_wg == 2) return launch_partial_hw<D, RB, I8, 2>(la, grid, st, fast, ev);
+    if (la.heads_per_wg == 8) return launch_partial_hw<D, RB, KV, 8>(la, grid, st, fast, ev);
+    if (la.heads_per_wg == 4) return launch_partial_hw<D, RB, KV, 4>(la, grid, st, fast, ev);
+    if (la.heads_per_wg == 2) return launch_partial_hw<D, RB, KV, 2>(la, grid, st, fast, ev);
   }
-  launch_partial_hw<D, RB, I8, 1>(la, grid, st, fast, ev);
+  launch_partial_hw<D, RB, KV, 1>(la, grid, st, fast, ev);
 }
 
-template <int D, bool I8>
+template <int D, int KV>
 static void launch_partial_rb(const Plan &p, const LaunchArgs &la, dim3 grid, hipStream_t st,
                               const KernelEvents &ev) {
   const bool fast = p.prm.page_size >= 16;
   switch (p.row_blocks) {
-    case 1: launch_partial_t<D, 1, I8>(la, grid, st, fast, ev); break;
-    case 2: launch_partial_t<D, 2, I8>(la, grid, st, fast, ev); break;
-    default: launch_partial_t<D, 4, I8>(la, grid, st, fast, ev); break;
+    case 1: launch_partial_t<D, 1, KV>(la, grid, st, fast, ev); break;
+    case 2: launch_partial_t<D, 2, KV>(la, grid, st, fast, ev); break;
+    default: launch_partial_t<D, 4, KV>(la, grid, st, fast, ev); break;
   }
 }
 
@@ -1280,13 +1335,15 @@ int launch_partial(const Plan &p, const LaunchArgs &la, void *stream, void *star
   dim3 grid(la.balanced ? (unsigned)la.grid_wgs
                         : (unsigned)((int64_t)la.split_stride * (la.Hkv / la.heads_per_wg) *
                                      la.batch));
-  const bool i8 = la.int8;
+  const int kv = la.fp8 ? 2 : la.int8 ? 1 : 0;
   if (la.D == 128) {
-    if (i8) launch_partial_rb<128, true>(p, la, grid, st, ev);
-    else launch_partial_rb<128, false>(p, la, grid, st, ev);
+    if (kv == 2) launch_partial_rb<128, 2>(p, la, grid, st, ev);
+    else if (kv == 1) launch_partial_rb<128, 1>(p, la, grid, st, ev);
+    else launch_partial_rb<128, 0>(p, la, grid, st, ev);
   } else {
-    if (i8) launch_partial_rb<256, true>(p, la, grid, st, ev);
-    else launch_partial_rb<256, false>(p, la, grid, st, ev);
+    if (kv == 2) launch_partial_rb<256, 2>(p, la, grid, st, ev);
+    else if (kv == 1) launch_partial_rb<256, 1>(p, la, grid, st, ev);
+    else launch_partial_rb<256, 0>(p, la, grid, st, ev);
   }
   return (int)hipGetLastError();
 }

@@ -67,7 +67,8 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
   const int R = G * prm.max_q_per_seq;
   if (R > 16)
     return fail(err, errn, SKVD_ERR_SHAPE, "group*max_q_per_seq=%d exceeds 16 rows", R);
-  if (prm.kv_dtype != SKVD_KV_F16 && prm.kv_dtype != SKVD_KV_I8_F16SCALE32)
+  if (prm.kv_dtype != SKVD_KV_F16 && prm.kv_dtype != SKVD_KV_I8_F16SCALE32 &&
+      prm.kv_dtype != SKVD_KV_FP8_E4M3)
     return fail(err, errn, SKVD_ERR_DTYPE, "kv_dtype=%d unknown", prm.kv_dtype);
   if (num_cus < 1) return fail(err, errn, SKVD_ERR_DEVICE, "num_cus=%d", num_cus);
   if (prm.force_reducer < 0 || prm.force_reducer > SKVD_REDUCER_NONE)
@@ -81,7 +82,7 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
     return fail(err, errn, SKVD_ERR_PLAN, "wgs_per_cu=%d outside 0..64", prm.wgs_per_cu);
   // KV heads per workgroup: the single-quarter variants at D=128 come in 1, 2, 4 and 8.
   const bool multi_head_ok = D == 128 && G * prm.max_q_per_seq <= 4;
-  const bool i8_kv = prm.kv_dtype == SKVD_KV_I8_F16SCALE32;
+  const bool i8_kv = prm.kv_dtype != SKVD_KV_F16;  // one-byte elements (int8 or fp8)
   int hw = prm.heads_per_wg;
   // A decode with no more (sequence, KV head, block) units than CUs is latency-bound: one
   // head per workgroup spreads it over the most CUs (measured: B=1, 1024 tokens, 12.5 vs 13.8
@@ -110,7 +111,9 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
   // Blocks per split. Two pressures: enough workgroups to fill the chip (about 16 per CU
   // when every sequence is at max_kv_len), and partial traffic (one (m, l, D floats) per row
   // and split, written then read back) at most ~3% of the split's K+V bytes.
-  const double row_bytes = prm.kv_dtype == SKVD_KV_F16 ? 4.0 * D : 2.0 * (D + 2 * (D / 32));
+  const double row_bytes = prm.kv_dtype == SKVD_KV_F16 ? 4.0 * D
+                           : prm.kv_dtype == SKVD_KV_FP8_E4M3 ? 2.0 * D
+                                                              : 2.0 * (D + 2 * (D / 32));
   const double partial_bytes = 2.0 * R * (D + 2) * 4.0;
   int bps_min = (int)std::ceil(partial_bytes / (0.03 * kBlockTokens * row_bytes));
   if (bps_min < 1) bps_min = 1;
@@ -164,7 +167,7 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
     // workgroup of 8 KV heads at a time, two per CU in two rounds (the registers hold one), so
     // that the dispatcher hands each CU its second share when it frees up; D=256 workgroups
     // are the largest (3 per CU measured best).
-    const bool i8 = prm.kv_dtype == SKVD_KV_I8_F16SCALE32;
+    const bool i8 = prm.kv_dtype != SKVD_KV_F16;  // one-byte elements
     const int auto_wpc = D == 256 ? 3
                          : p.row_blocks == 1 ? (i8 ? (hw == 8 ? 2 : 8 / hw)
                                                    : std::max(1, kDefaultWgsPerCu / hw))
@@ -232,6 +235,8 @@ skvd_status check_args(const Plan &p, const skvd_decode_args *a, size_t ws_bytes
   if (!a) return fail(err, errn, SKVD_ERR_NULL, "args is NULL");
   const int D = p.prm.head_dim;
   const bool i8 = p.prm.kv_dtype == SKVD_KV_I8_F16SCALE32;
+  const bool f8 = p.prm.kv_dtype == SKVD_KV_FP8_E4M3;
+  const bool byte = i8 || f8;  // one-byte elements
   if (a->reserved != 0) return fail(err, errn, SKVD_ERR_SHAPE, "reserved must be 0");
   if (a->batch < 0 || a->batch > p.prm.max_batch)
     return fail(err, errn, SKVD_ERR_SHAPE, "batch=%d outside 0..max_batch=%d", a->batch,
@@ -242,14 +247,17 @@ skvd_status check_args(const Plan &p, const skvd_decode_args *a, size_t ws_bytes
   if (!a->q || !a->k_pages || !a->v_pages || !a->page_table || !a->kv_len || !a->o)
     return fail(err, errn, SKVD_ERR_NULL, "q, k_pages, v_pages, page_table, kv_len and o "
                 "must be non-NULL");
-  if (i8 && (!a->k_scales || !a->v_scales))
-    return fail(err, errn, SKVD_ERR_DTYPE, "int8 cache needs k_scales and v_scales");
-  if (!i8 && (a->k_scales || a->v_scales))
+  if (byte && (!a->k_scales || !a->v_scales))
+    return fail(err, errn, SKVD_ERR_DTYPE, "%s cache needs k_scales and v_scales",
+                i8 ? "int8" : "fp8");
+  if (!byte && (a->k_scales || a->v_scales))
     return fail(err, errn, SKVD_ERR_DTYPE, "f16 cache takes no scales");
+  if (f8 && (!aligned(a->k_scales, 4) || !aligned(a->v_scales, 4)))
+    return fail(err, errn, SKVD_ERR_LAYOUT, "fp8 k_scale / v_scale must be 4-byte aligned");
   if (!std::isfinite(a->sm_scale))
     return fail(err, errn, SKVD_ERR_SHAPE, "sm_scale is not finite");
-  // Vector loads: 16 bytes of q, o, K and f16 V rows; 8 bytes of int8 V rows.
-  const int64_t kv_vec = i8 ? 16 : 8;  // elements per 16-byte load
+  // Vector loads: 16 bytes of q, o, K and f16 V rows; 8 bytes of int8 / fp8 V rows.
+  const int64_t kv_vec = byte ? 16 : 8;  // elements per 16-byte load
   if (!aligned(a->q, 16) || a->q_tok_stride % 8 || a->q_head_stride % 8 || a->q_tok_stride < 0 ||
       a->q_head_stride < 0)
     return fail(err, errn, SKVD_ERR_LAYOUT, "q must be 16-byte aligned with token/head "
@@ -267,7 +275,7 @@ skvd_status check_args(const Plan &p, const skvd_decode_args *a, size_t ws_bytes
     return fail(err, errn, SKVD_ERR_LAYOUT, "scale pools must be 8-byte aligned with "
                 "non-negative strides that are multiples of 4 elements");
   // Within a 16-token tile the kernels address rows with 32-bit byte offsets.
-  const int64_t es = i8 ? 1 : 2;
+  const int64_t es = byte ? 1 : 2;
   if ((16 * a->tok_stride + D) * es >= (int64_t(1) << 31) ||
       (i8 && 16 * a->scale_tok_stride + D / 32 >= (int64_t(1) << 30)))
     return fail(err, errn, SKVD_ERR_LAYOUT, "token stride too large for 32-bit in-tile offsets");
@@ -326,7 +334,8 @@ void fill_launch_args(const Plan &p, const skvd_decode_args &a, void *ws, Launch
   l.piece_min = p.piece_min;
   l.max_kv_len = p.prm.max_kv_len;
   l.hier_groups_cap = p.hier_groups_cap;
-  l.int8 = p.prm.kv_dtype == SKVD_KV_I8_F16SCALE32;
+  l.int8 = p.prm.kv_dtype != SKVD_KV_F16;  // one-byte elements
+  l.fp8 = p.prm.kv_dtype == SKVD_KV_FP8_E4M3;
   l.debug = p.prm.debug;
   char *w = (char *)ws;
   l.status = w ? (unsigned *)(w + p.off_status) : nullptr;

@@ -54,7 +54,9 @@ struct LaunchArgs {
   int bps, splits_cap, split_stride, max_kv_len, hier_groups_cap;  // stride: odd, >= cap
   int balanced, grid_wgs, part_stride, piece_min;
   int heads_per_wg;  // KV heads (waves) per partial-kernel workgroup; divides Hkv
-  int int8, debug;
+  int int8;         // one-byte elements (int8 with f16 group scales, or fp8)
+  int fp8;          // fp8 E4M3: ks / vs each point to one f32 tensor scale
+  int debug;
   // partials (static: [rows_cap][part_stride]; balanced: [slots][heads_per_wg][G*T]):
   float *ws_ml;      // [..][2]  (max in log2 units, sum)
   float *ws_o;       // [..][D]  unnormalized f32 output

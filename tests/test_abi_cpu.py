@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol():
     for s in syms:
         assert hasattr(L, s), s
     assert set(syms) == set(bd.SIGNATURES), set(syms) ^ set(bd.SIGNATURES)
-    assert L.skvd_abi_version() == bd.ABI_VERSION == 8
+    assert L.skvd_abi_version() == bd.ABI_VERSION == 9
 
 
 def plan(**kw):
@@ -214,6 +214,33 @@ def test_decode_check_f16(over, status):
 def test_decode_check_int8(over, status):
     p = plan(kv_dtype="i8")
     assert bd.skvd_decode_check(p.handle, good_args(p, i8=True, **over), p.workspace_bytes) == status
+
+
+@pytest.mark.parametrize("over,status", [
+    ({}, 0), (dict(k_scales=None), 4), (dict(v_scales=None), 4), (dict(k_scales=FAKE + 2), 3),
+    (dict(v_scales=FAKE + 4), 0), (dict(k_pages=FAKE + 8), 3),
+    (dict(tok_stride=8 * 128 + 8), 3), (dict(tok_stride=8 * 128 + 16), 0),
+    (dict(scale_tok_stride=3, scale_head_stride=1), 0),  # fp8 has no per-row scale strides
+])
+def test_decode_check_fp8(over, status):
+    """fp8 E4M3 cache: one-byte elements like int8, and one f32 scale per tensor (4-byte
+    aligned pointers; the scale strides are ignored)."""
+    p = plan(kv_dtype="f8")
+    a = good_args(p, **dict(dict(k_scales=FAKE + (2 << 30), v_scales=FAKE + (3 << 30)), **over))
+    assert bd.skvd_decode_check(p.handle, a, p.workspace_bytes) == status
+
+
+def test_fp8_plan_and_unsupported_routes():
+    """fp8 plans share the one-byte layout's choices; append and the multi-token route refuse
+    an fp8 cache with SKVD_ERR_DTYPE before any launch."""
+    p8, pi = plan(kv_dtype="f8"), plan(kv_dtype="i8")
+    assert p8.kv_dtype == "f8" and p8.info.heads_per_wg == pi.info.heads_per_wg
+    a = good_append_args(k_scales=FAKE + (2 << 32), v_scales=FAKE + (3 << 32))
+    assert bd.skvd_append_check(p8.handle, a) == 4
+    d = good_args(p8, q_per_seq=512, k_scales=FAKE + (2 << 30), v_scales=FAKE + (3 << 30))
+    assert bd.skvd_prefill_check(p8.handle, d) == 4
+    with pytest.raises(ValueError):
+        plan(kv_dtype="q4")
 
 
 def test_workspace_too_small():

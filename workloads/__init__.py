@@ -1,8 +1,8 @@
 """Seeded synthetic inputs for paged decode attention.
 
 This module only builds inputs: it draws lengths, page permutations and N(0,1) values, and
-for the int8 cache it builds the stored int8 values and f16 scales from N(0,1) data; for the
-fp8 cache it draws E4M3 bytes and per-tensor f32 scales directly. It holds
+for the int8 cache it builds the stored int8 values and f16 scales from N(0,1) data, and for
+the fp8 cache the E4M3 bytes of N(0,1) data under a drawn per-tensor scale. It holds
 none of the decode's arithmetic, so both the HIP path and the CPU oracle consume its arrays.
 
 Workloads (synthetic stand-ins; the pages measure whole models whose weights are absent):
@@ -21,10 +21,10 @@ comes from PCG64(SeedSequence(seed, spawn_key=(k, c))), so the values do not dep
 thread count. For the int8 cache the same float32 draws are quantized, which draws nothing.
 Pools hold sum_b ceil(L_b/P) live pages plus ceil(live/16) spare pages; page ids are a random
 permutation consumed in sequence order.
-fp8 cache (kv_dtype "f8", uint8 OCP E4M3 bytes): each byte has a uniform sign bit, an exponent
-field rint(N(7, 1.5)) clipped to [0, 15] and a uniform mantissa (the NaN byte's mantissa 7 at
-exponent 15 becomes 6), drawn per chunk like the normals; k_scale and v_scale (one f32 each,
-arrays of shape [1]) are uniform in [0.1, 0.5] from default_rng((seed, 8)).
+fp8 cache (kv_dtype "f8", uint8 OCP E4M3 bytes): k_scale and v_scale (one f32 each, arrays of
+shape [1]) are uniform in [1/80, 1/64] from default_rng((seed, 8)); the pools' N(0,1) draws
+(streams 4 and 5, as for f16) divided by the scale, clipped to +-448, become E4M3 bytes by
+torch's float8_e4m3fn cast (nearest even), which draws nothing.
 Spare pages and the tail slots past kv_len of each sequence's last page are NaN-poisoned
 (for int8: their scales are NaN; fp8: the NaN byte 0x7F), so any read of them shows up in the
 output.
@@ -175,29 +175,28 @@ def _normal_int8(seed, stream, shape):
     return q, sc
 
 
-def _random_e4m3(seed, stream, shape):
-    """E4M3 bytes: uniform sign, exponent field rint(N(7, 1.5)) clipped to [0, 15], uniform
-    mantissa; the NaN pattern (exponent 15, mantissa 7) is replaced by mantissa 6."""
+def _normal_e4m3(seed, stream, shape, scale):
+    """N(0,1) data (drawn as in _normal_f16) over a per-tensor scale, as E4M3 bytes: x / scale
+    in f32, clipped to +-448, cast by torch to float8_e4m3fn (nearest even)."""
+    import torch
     out = np.empty(shape, np.uint8)
     flat = out.reshape(-1)
     n = flat.shape[0]
+    sc = np.float32(scale)
 
     def fill(c):
         a, b = c * _CHUNK, min(n, (c + 1) * _CHUNK)
-        r = _chunk_rng(seed, stream, c)
-        sign = r.integers(0, 2, b - a, dtype=np.uint8)
-        e = np.clip(np.rint(r.normal(7.0, 1.5, b - a)), 0, 15).astype(np.uint8)
-        m = r.integers(0, 8, b - a, dtype=np.uint8)
-        m = np.where((e == 15) & (m == 7), 6, m).astype(np.uint8)
-        flat[a:b] = (sign << 7) | (e << 3) | m
+        x = _chunk_rng(seed, stream, c).standard_normal(b - a, dtype=np.float32)
+        y = np.clip(x / sc, np.float32(-448), np.float32(448))
+        flat[a:b] = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
     _parallel(fill, -(-n // _CHUNK))
     return out
 
 
 def fp8_scales(seed):
-    """(k_scale, v_scale): one f32 each, arrays of shape [1], uniform in [0.1, 0.5]."""
-    r = np.random.default_rng((seed, 8)).uniform(0.1, 0.5, 2).astype(np.float32)
+    """(k_scale, v_scale): one f32 each, arrays of shape [1], uniform in [1/80, 1/64]."""
+    r = np.random.default_rng((seed, 8)).uniform(1 / 80, 1 / 64, 2).astype(np.float32)
     return r[:1].copy(), r[1:].copy()
 
 
@@ -239,9 +238,9 @@ def generate(s: Spec, seed: int) -> dict:
         k, ks = _normal_int8(seed, 4, (N, P, Hkv, D))
         v, vs = _normal_int8(seed, 5, (N, P, Hkv, D))
     elif s.kv_dtype == "f8":
-        k = _random_e4m3(seed, 4, (N, P, Hkv, D))
-        v = _random_e4m3(seed, 5, (N, P, Hkv, D))
         ks, vs = fp8_scales(seed)
+        k = _normal_e4m3(seed, 4, (N, P, Hkv, D), ks[0])
+        v = _normal_e4m3(seed, 5, (N, P, Hkv, D), vs[0])
     else:
         raise ValueError(s.kv_dtype)
     if s.poison:
