@@ -22,6 +22,7 @@ prompts over an int8 cache). `--op append|prefill|merge` print those operations'
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -206,9 +207,10 @@ def sweep(args):
             s = workloads.spec(name=f"long_{L}", batch=1, q_per_seq=1, num_qo_heads=32,
                                num_kv_heads=8, head_dim=128, page_size=64, lens=("fixed", L),
                                q_mult=2.0)
-        else:  # long_i8: the int8 batch's head shape at fixed long lengths, 8 sequences
-            s = workloads.spec(name=f"long_i8_{L}", batch=8, q_per_seq=1, num_qo_heads=32,
-                               num_kv_heads=8, head_dim=128, page_size=16, kv_dtype="i8",
+        else:  # long_i8 / long_f8: the int8 batch's head shape at long lengths, 8 sequences
+            kv = args.sweep[-2:]
+            s = workloads.spec(name=f"long_{kv}_{L}", batch=8, q_per_seq=1, num_qo_heads=32,
+                               num_kv_heads=8, head_dim=128, page_size=16, kv_dtype=kv,
                                lens=("fixed", L))
         us, part_us, kvb, plan = time_decode(s, 100 + L % 97, args.steps, args.warmup,
                                              args.bps, args.reducer, args.schedule,
@@ -515,6 +517,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--kv", choices=["f16", "i8", "f8"], default=None,
+                    help="cache format in place of the config's own (f8: OCP E4M3 with one f32 "
+                         "scale per tensor)")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--bps", type=int, default=0, help="force 64-token blocks per split")
@@ -529,7 +534,7 @@ def main():
                     help="pool layout: nhd = [pages, P, Hkv, D] (the workload's); hnd = each KV "
                          "head's page rows contiguous, passed through the same strides")
     ap.add_argument("--no-stream-ref", action="store_true")
-    ap.add_argument("--sweep", choices=["cliff", "long", "long_i8"], default=None,
+    ap.add_argument("--sweep", choices=["cliff", "long", "long_i8", "long_f8"], default=None,
                     help="instead of the bench line: cliff = B=32, 32/8 heads, D=128, P=16 at "
                          "uniform kv_len across the 2048-token boundary; long = B=1, the long-"
                          "context shape, kv_len 8192..131072. One JSON line per point.")
@@ -566,6 +571,8 @@ def main():
     import workloads
 
     spec = workloads.config(args.config)
+    if args.kv and args.kv != spec.kv_dtype:
+        spec = dataclasses.replace(spec, kv_dtype=args.kv, name=f"{spec.name}_{args.kv}")
     seed = args.config if args.seed is None else args.seed
     t0 = time.time()
     prob = workloads.generate(spec, seed)

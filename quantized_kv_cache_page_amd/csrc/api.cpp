@@ -215,7 +215,7 @@ skvd_status skvd_plan_describe(const skvd_plan *plan, char *buf, size_t n) {
            "blocks_per_split=%d splits=%d schedule=%s grid=%d heads_per_wg=%d reducer=%s "
            "hier_groups=%d rows_per_wg=%d workspace=%zu B",
            p.prm.num_qo_heads, p.prm.num_kv_heads, p.prm.head_dim, p.prm.page_size,
-           p.prm.kv_dtype == SKVD_KV_F16 ? "f16" : "int8", p.prm.max_batch, p.prm.max_q_per_seq,
+           p.prm.kv_dtype == SKVD_KV_F16 ? "f16" : p.prm.kv_dtype == SKVD_KV_FP8_E4M3 ? "fp8" : "int8", p.prm.max_batch, p.prm.max_q_per_seq,
            p.prm.max_kv_len, p.num_cus, p.bps, p.splits_cap,
            p.schedule == SKVD_SCHEDULE_BALANCED ? "balanced" : "static", p.grid_wgs,
            p.heads_per_wg,

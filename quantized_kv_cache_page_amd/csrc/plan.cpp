@@ -167,10 +167,15 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
     // workgroup of 8 KV heads at a time, two per CU in two rounds (the registers hold one), so
     // that the dispatcher hands each CU its second share when it frees up; D=256 workgroups
     // are the largest (3 per CU measured best).
-    const bool i8 = prm.kv_dtype != SKVD_KV_F16;  // one-byte elements
+    // fp8 (no per-element scale work) does best with eight waves per CU whatever the head
+    // count per workgroup (measured: GQA batch 45.9 us with 8 heads x 1 workgroup, 55.7 with
+    // int8's 8 x 2; the int8 batch shape 541 vs 546 us).
+    const bool i8 = prm.kv_dtype == SKVD_KV_I8_F16SCALE32;
+    const bool f8 = prm.kv_dtype == SKVD_KV_FP8_E4M3;
     const int auto_wpc = D == 256 ? 3
-                         : p.row_blocks == 1 ? (i8 ? (hw == 8 ? 2 : 8 / hw)
-                                                   : std::max(1, kDefaultWgsPerCu / hw))
+                         : p.row_blocks == 1 ? (f8   ? 8 / hw
+                                                : i8 ? (hw == 8 ? 2 : 8 / hw)
+                                                     : std::max(1, kDefaultWgsPerCu / hw))
                                              : kDefaultWgsPerCu;
     p.grid_wgs = (prm.wgs_per_cu ? prm.wgs_per_cu : auto_wpc) * num_cus;
     // a forced split size becomes the balanced shares' minimum
