@@ -511,7 +511,7 @@ def main():
     ap.add_argument("--prefill", default="prompt_i8",
                     help="prefill workload for --op prefill: prompt_i8, prompt_f16")
     ap.add_argument("--append", default="prefill_i8",
-                    help="append workload for --op append: prefill_i8, prefill_f16, decode_i8")
+                    help="append workload for --op append: prefill_i8, prefill_f16, prefill_f8, decode_i8")
     ap.add_argument("--no-append", action="store_true",
                     help="leave the append and prefill objects out of the decode line")
     ap.add_argument("--steps", type=int, default=200)

@@ -93,7 +93,9 @@ typedef enum {
                                 tensor: element value = e4m3(byte) * k_scale for K and
                                 * v_scale for V (AMD-Ecosystem/flashinfer PR #397, the two
                                 commit messages: fp8 caches are read with per-tensor k_scale
-                                and v_scale values passed by pointer). Decode and gather only. */
+                                and v_scale values passed by pointer). Decode, gather and append
+                                (nearest-even E4M3 of x / scale, saturating at 448); the
+                                multi-token route refuses it. */
 } skvd_kv_dtype;
 
 typedef enum {
@@ -341,7 +343,10 @@ skvd_status skvd_merge_states(const void *o_states, int64_t o_state_stride, int6
  * write, symmetric, the largest magnitude of each group of 32 mapped to 127:
  *     s = f16(max|x| / 127)             (quotient in f32, rounded once to f16, nearest even)
  *     c = clip(rint(x / s), -127, 127)  (quotient in f32, rint to nearest even; s = 0 -> c = 0)
- * with no f16 temporary: each row is read once and written once.
+ * with no f16 temporary: each row is read once and written once. An fp8 cache (OCP E4M3 bytes
+ * with one f32 scale s per tensor, AMD-Ecosystem/flashinfer PR #397 commit messages) stores for
+ * each element the E4M3 value nearest to clip(x / s, -448, 448) (the quotient in f32, correctly
+ * rounded; ties to the even mantissa; a NaN quotient stores 0); its scales are only read.
  *
  * - Written: exactly the K/V elements (and, int8, the scales) of the slots the tokens name.
  *   Nothing else; no workspace. k_new, v_new, batch_idx, positions and the table are read only.
@@ -364,7 +369,7 @@ typedef struct {
   const int32_t *positions;   /* [N] device: logical position of each new token */
   int32_t num_tokens;         /* N >= 0 (0 launches nothing) */
   int32_t batch;              /* rows of page_table, >= 0 */
-  void *k_pages;              /* [num_k_pages, P, Hkv, D] f16 or int8, written; layout rules
+  void *k_pages;              /* [num_k_pages, P, Hkv, D] f16, int8 or E4M3, written; layout rules
                                  as in skvd_decode_args */
   void *v_pages;              /* [num_v_pages, P, Hkv, D], same strides as K, written */
   int64_t page_stride;        /* elements; shared by K and V */
@@ -372,8 +377,10 @@ typedef struct {
   int64_t head_stride;
   int64_t num_k_pages;        /* >= 1 */
   int64_t num_v_pages;        /* >= 1 */
-  void *k_scales;             /* int8 only: f16 [num_k_pages, P, Hkv, D/32], written; else NULL */
-  void *v_scales;             /* int8 only: f16 [num_v_pages, P, Hkv, D/32], written; else NULL */
+  void *k_scales;             /* int8: f16 [num_k_pages, P, Hkv, D/32], written; fp8: one f32
+                                 (k_scale, device memory, 4-byte aligned), read; f16: NULL */
+  void *v_scales;             /* int8: f16 [num_v_pages, P, Hkv, D/32], written; fp8: one f32
+                                 (v_scale), read; f16: NULL */
   int64_t scale_page_stride;  /* elements; layout rules as in skvd_decode_args */
   int64_t scale_tok_stride;
   int64_t scale_head_stride;

@@ -66,8 +66,7 @@ skvd_status check_append(const skvd_plan *plan, const skvd_append_args *a) {
   if (!a) return set_err(SKVD_ERR_NULL, "args is NULL");
   const skvd::Plan &p = plan->p;
   const bool i8 = p.prm.kv_dtype == SKVD_KV_I8_F16SCALE32;
-  if (p.prm.kv_dtype == SKVD_KV_FP8_E4M3)
-    return set_err(SKVD_ERR_DTYPE, "append into an fp8 cache is not supported");
+  const bool f8 = p.prm.kv_dtype == SKVD_KV_FP8_E4M3;
   const auto al = [](const void *ptr, uintptr_t n) { return (uintptr_t)ptr % n == 0; };
   if (a->num_tokens < 0 || a->batch < 0)
     return set_err(SKVD_ERR_SHAPE, "num_tokens=%d and batch=%d must be >= 0", a->num_tokens,
@@ -77,15 +76,17 @@ skvd_status check_append(const skvd_plan *plan, const skvd_append_args *a) {
                    "when num_tokens > 0");
   if (!a->k_pages || !a->v_pages || !a->page_table)
     return set_err(SKVD_ERR_NULL, "k_pages, v_pages and page_table must be non-NULL");
-  if (i8 && (!a->k_scales || !a->v_scales))
-    return set_err(SKVD_ERR_DTYPE, "int8 cache needs k_scales and v_scales");
-  if (!i8 && (a->k_scales || a->v_scales))
+  if ((i8 || f8) && (!a->k_scales || !a->v_scales))
+    return set_err(SKVD_ERR_DTYPE, "%s cache needs k_scales and v_scales", i8 ? "int8" : "fp8");
+  if (!i8 && !f8 && (a->k_scales || a->v_scales))
     return set_err(SKVD_ERR_DTYPE, "f16 cache takes no scales");
+  if (f8 && (!al(a->k_scales, 4) || !al(a->v_scales, 4)))
+    return set_err(SKVD_ERR_LAYOUT, "fp8 k_scale / v_scale must be 4-byte aligned");
   if (!al(a->k_new, 16) || !al(a->v_new, 16) || a->new_tok_stride < 0 || a->new_head_stride < 0 ||
       a->new_tok_stride % 8 || a->new_head_stride % 8)
     return set_err(SKVD_ERR_LAYOUT, "k_new/v_new must be 16-byte aligned with token/head strides "
                    "that are non-negative multiples of 8 elements");
-  const int64_t kv_vec = i8 ? 16 : 8;  // the decode's rule: 16-byte rows in both cache types
+  const int64_t kv_vec = i8 || f8 ? 16 : 8;  // the decode's rule: strides of 16 bytes
   if (!al(a->k_pages, 16) || !al(a->v_pages, 16) || a->page_stride < 0 || a->tok_stride < 0 ||
       a->head_stride < 0 || a->page_stride % kv_vec || a->tok_stride % kv_vec ||
       a->head_stride % kv_vec)
@@ -361,6 +362,7 @@ skvd_status skvd_append(const skvd_plan *plan, const skvd_append_args *a, void *
   l.page_shift = sh;
   l.max_len = p.prm.max_kv_len;
   l.int8 = p.prm.kv_dtype == SKVD_KV_I8_F16SCALE32;
+  l.fp8 = p.prm.kv_dtype == SKVD_KV_FP8_E4M3;
   l.num_cus = p.num_cus;
   int e = skvd::launch_append(l, stream);
   return e ? hip_err(e, "append kernel launch") : SKVD_OK;

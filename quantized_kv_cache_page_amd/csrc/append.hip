@@ -1,4 +1,5 @@
-// Append kernel: new K/V rows into the paged cache, f16 verbatim or int8 quantized on write.
+// Append kernel: new K/V rows into the paged cache, f16 verbatim, or int8 or fp8 quantized on
+// write.
 //
 // The slot of new token i is (page_table[b][j / P], j % P) for b = batch_idx[i], j =
 // positions[i]: the address the decode reads. Each lane owns 8 consecutive head_dim elements of
@@ -20,6 +21,11 @@
 // division; the codes take the correctly rounded quotient's decision through a reciprocal
 // multiply checked against the rounding boundary (code_of), so they are those of any correctly
 // rounded f32 evaluation of the same rule.
+//
+// fp8 (OCP E4M3 bytes with one f32 scale s per tensor, read from device memory; the
+// AMD-Ecosystem/flashinfer PR #397 commit messages name fp8 caches with per-tensor k_scale and
+// v_scale): each element stores the E4M3 value nearest to clip(x / s, -448, 448), x / s the
+// correctly rounded f32 quotient, ties to the even mantissa; a NaN quotient stores 0.
 #include <hip/hip_runtime.h>
 
 #include "skvd_internal.h"
@@ -86,14 +92,75 @@ __device__ __forceinline__ uint2a quantize8(half8a x, _Float16 *scale) {
   return r;
 }
 
-template <int D, bool I8>
+// E4M3 byte of one f32 value q (see above). Below 2^-6 the E4M3 grid is 2^-9 (subnormals, and
+// 2^-6 itself as 8 steps), so the code is rint(|q| * 512); above, the f32 bits are rounded to
+// three mantissa bits (nearest, ties to even, by adding 0x7FFFF plus the kept lowest bit) and
+// the exponent is rebased from f32's bias 127 to E4M3's 7. |q| <= 448 keeps the code <= 0x7E.
+__device__ __forceinline__ unsigned e4m3_of(float q) {
+  const unsigned sign = (__float_as_uint(q) >> 24) & 0x80u;
+  const float m = fminf(fabsf(q), 448.0f);
+  unsigned code;
+  if (m < 0x1p-6f) {
+    code = (unsigned)rintf(m * 512.0f);
+  } else {
+    const unsigned b = __float_as_uint(m);
+    code = ((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - (120u << 3);
+  }
+  return q != q ? 0u : (sign | code);
+}
+
+// True when q lies within 4 ulps of a point where the E4M3 rounding changes (a midpoint
+// between neighbouring values): above 2^-6 the 20 f32 mantissa bits below the kept three are
+// within 4 of 0x80000; below, q * 512 is within 2^-16 of a half-integer. Binade edges are E4M3
+// values themselves, and 448 is one, so the clip adds no other decision point.
+__device__ __forceinline__ bool e4m3_near_tie(float q) {
+  const float m = fminf(fabsf(q), 448.0f);
+  if (m < 0x1p-6f) {
+    const float t = m * 512.0f;
+    return fabsf(fabsf(t - rintf(t)) - 0.5f) <= 0x1p-16f;
+  }
+  return (__float_as_uint(m) & 0xFFFFFu) - 0x7FFFCu <= 8u;
+}
+
+// The 8 E4M3 codes of one lane's elements over the tensor scale s, as if from the correctly
+// rounded quotients x / s: the product q = x * rcp(s) (rcp to 1 ulp) is within 2 ulps of x / s,
+// so the code of q is the quotient's unless q is near a rounding midpoint; those elements (and
+// every element when s or its reciprocal is outside the normal range) take the division.
+__device__ __forceinline__ uint2a quantize_fp8(half8a x, float s) {
+  const float r = __builtin_amdgcn_rcpf(s);
+  const bool normal = s >= 0x1p-125f && s <= 0x1p125f;
+  float f[8];
+  unsigned c[8];
+  bool near = !normal;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    f[e] = (float)x[e];
+    const float q = f[e] * r;
+    c[e] = e4m3_of(q);
+    near |= e4m3_near_tie(q);
+  }
+  if (near) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (!normal || e4m3_near_tie(f[e] * r)) c[e] = e4m3_of(f[e] / s);
+  }
+  uint2a w;
+  w[0] = c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24;
+  w[1] = c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24;
+  return w;
+}
+
+// KV: 0 f16, 1 int8 with per-32 f16 scales, 2 fp8 with the tensor scale tscale.
+template <int D, int KV>
 __device__ __forceinline__ void store_row(const AppendLaunch &a, half8a x, void *pool,
-                                          void *scales, int64_t page, int slot, int kvh,
-                                          int part) {
+                                          void *scales, float tscale, int64_t page, int slot,
+                                          int kvh, int part) {
   const int64_t off = page * a.page_stride + (int64_t)slot * a.tok_stride +
                       (int64_t)kvh * a.head_stride + part * 8;
-  if constexpr (!I8) {
+  if constexpr (KV == 0) {
     __builtin_nontemporal_store(x, (half8a *)((_Float16 *)pool + off));
+  } else if constexpr (KV == 2) {
+    __builtin_nontemporal_store(quantize_fp8(x, tscale), (uint2a *)((int8_t *)pool + off));
   } else {
     _Float16 sh;
     const uint2a codes = quantize8(x, &sh);
@@ -114,7 +181,7 @@ __device__ __forceinline__ void store_row(const AppendLaunch &a, half8a x, void 
 // (token indices clamped into the batch, invalid tokens masked), so nothing waits early.
 constexpr int kTokensPerLane = kAppendTokensPerLane;
 
-template <int D, bool I8>
+template <int D, int KV>
 __global__ __launch_bounds__(256) void append_kernel(AppendLaunch a) {
   constexpr int kLanesPerRow = D / 8;
   constexpr int U = kTokensPerLane;
@@ -130,6 +197,9 @@ __global__ __launch_bounds__(256) void append_kernel(AppendLaunch a) {
   const _Float16 *vn = (const _Float16 *)a.v_new;
   const int slot_mask = (1 << a.page_shift) - 1;
   const int last = a.num_tokens - 1;
+  // fp8: the tensor scales (scalar loads, once)
+  const float ksc = KV == 2 ? *(const float *)a.ks : 0.0f;
+  const float vsc = KV == 2 ? *(const float *)a.vs : 0.0f;
   for (int base = tok0; base < a.num_tokens; base += U * a.tok_step) {
     half8a xk[U], xv[U];
     int b[U], j[U];
@@ -155,16 +225,19 @@ __global__ __launch_bounds__(256) void append_kernel(AppendLaunch a) {
     for (int u = 0; u < U; ++u) {
       if (page[u] < 0) continue;
       const int slot = j[u] & slot_mask;
-      if (page[u] < a.num_k_pages) store_row<D, I8>(a, xk[u], a.k, a.ks, page[u], slot, kvh, part);
-      if (page[u] < a.num_v_pages) store_row<D, I8>(a, xv[u], a.v, a.vs, page[u], slot, kvh, part);
+      if (page[u] < a.num_k_pages)
+        store_row<D, KV>(a, xk[u], a.k, a.ks, ksc, page[u], slot, kvh, part);
+      if (page[u] < a.num_v_pages)
+        store_row<D, KV>(a, xv[u], a.v, a.vs, vsc, page[u], slot, kvh, part);
     }
   }
 }
 
 template <int D>
 void launch_d(const AppendLaunch &a, hipStream_t st) {
-  if (a.int8) append_kernel<D, true><<<a.blocks, 256, 0, st>>>(a);
-  else append_kernel<D, false><<<a.blocks, 256, 0, st>>>(a);
+  if (a.fp8) append_kernel<D, 2><<<a.blocks, 256, 0, st>>>(a);
+  else if (a.int8) append_kernel<D, 1><<<a.blocks, 256, 0, st>>>(a);
+  else append_kernel<D, 0><<<a.blocks, 256, 0, st>>>(a);
 }
 
 }  // namespace
@@ -173,8 +246,8 @@ int launch_append(AppendLaunch a, void *stream) {
   if (a.rows == 0 || a.batch == 0) return 0;  // nothing to write (and no table row to read)
   // Grid: a whole number of tokens' lanes (so a lane keeps its head and part while it strides),
   // each lane serving up to kTokensPerLane tokens per round; at most one round of resident
-  // 256-lane workgroups (int8: 77 registers -> 6 waves per SIMD; f16: 58 -> 8), fewer for a
-  // small append.
+  // 256-lane workgroups (int8: 77 registers -> 6 waves per SIMD; fp8: 82 -> 5; f16: 58 -> 8),
+  // fewer for a small append.
   a.lanes_per_token = a.Hkv * a.D / 8;
   int64_t x = a.lanes_per_token, y = 256;
   while (y) {
@@ -185,7 +258,7 @@ int launch_append(AppendLaunch a, void *stream) {
   const int64_t g0 = a.lanes_per_token / x;  // workgroups per whole number of tokens
   const int64_t toks = (a.num_tokens + kTokensPerLane - 1) / kTokensPerLane;
   const int64_t want = (toks * a.lanes_per_token + 255) / 256;
-  const int64_t cap = (a.int8 ? 6LL : 8LL) * a.num_cus;
+  const int64_t cap = (a.fp8 ? 5LL : a.int8 ? 6LL : 8LL) * a.num_cus;
   int64_t blocks = want < cap ? want : cap;
   blocks = (blocks + g0 - 1) / g0 * g0;
   a.blocks = (unsigned)blocks;

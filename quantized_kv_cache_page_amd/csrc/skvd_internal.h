@@ -99,6 +99,7 @@ struct AppendLaunch {
   int64_t table_stride;
   int64_t rows;        // num_tokens * Hkv
   int num_tokens, batch, Hkv, D, page_shift, max_len, int8;
+  int fp8;              // fp8 E4M3 cache: ks / vs each point to one f32 tensor scale
   int num_cus;          // compute units of the plan's device
   int lanes_per_token;  // set by launch_append: Hkv * D / 8 (one lane per 8 elements of a row)
   int tok_step;         // set by launch_append: tokens the whole grid covers per step

@@ -231,12 +231,17 @@ def test_decode_check_fp8(over, status):
 
 
 def test_fp8_plan_and_unsupported_routes():
-    """fp8 plans share the one-byte layout's choices; append and the multi-token route refuse
-    an fp8 cache with SKVD_ERR_DTYPE before any launch."""
+    """fp8 plans share the one-byte layout's head grouping; the multi-token route refuses an
+    fp8 cache with SKVD_ERR_DTYPE before any launch; appends take the two tensor scales."""
     p8, pi = plan(kv_dtype="f8"), plan(kv_dtype="i8")
     assert p8.kv_dtype == "f8" and p8.info.heads_per_wg == pi.info.heads_per_wg
     a = good_append_args(k_scales=FAKE + (2 << 32), v_scales=FAKE + (3 << 32))
-    assert bd.skvd_append_check(p8.handle, a) == 4
+    assert bd.skvd_append_check(p8.handle, a) == 0
+    for over, st in ((dict(k_scales=None), 4), (dict(v_scales=FAKE + 2), 3),
+                     (dict(tok_stride=8 * 128 + 8), 3), (dict(scale_tok_stride=3), 0)):
+        a = good_append_args(**dict(dict(k_scales=FAKE + (2 << 32), v_scales=FAKE + (3 << 32)),
+                                    **over))
+        assert bd.skvd_append_check(p8.handle, a) == st, over
     d = good_args(p8, q_per_seq=512, k_scales=FAKE + (2 << 30), v_scales=FAKE + (3 << 30))
     assert bd.skvd_prefill_check(p8.handle, d) == 4
     with pytest.raises(ValueError):

@@ -35,7 +35,7 @@ def _pool_dev(x, layout):
     logical view over [N, Hkv, P, X] storage)."""
     if x is None:
         return None
-    if layout == "nhd":
+    if layout == "nhd" or x.ndim != 4:  # (fp8 scales: one f32 per tensor)
         return torch.from_numpy(x).cuda()
     return torch.from_numpy(np.ascontiguousarray(x.transpose(0, 2, 1, 3))).cuda().permute(0, 2, 1, 3)
 
@@ -82,6 +82,9 @@ CASES = [
     ("i8_d256_p4", 2, 2, 256, 4, "i8", (7, 300), 300, "nhd"),
     ("i8_d128_p1_mha", 2, 1, 128, 1, "i8", (50, 3), 50, "nhd"),
     ("i8_d128_p16_hnd", 3, 8, 128, 16, "i8", (40, 16, 100), 25, "hnd"),
+    ("f8_d128_p16", 3, 8, 128, 16, "f8", (17, 300, 64), 40, "nhd"),
+    ("f8_d256_p1", 2, 2, 256, 1, "f8", (9, 130), 130, "nhd"),
+    ("f8_d128_p64_hnd", 3, 4, 128, 64, "f8", (1, 200, 129), 70, "hnd"),
 ]
 
 
@@ -142,6 +145,38 @@ def test_append_special_values():
     assert_pools_equal(got, want, "special values")
 
 
+@pytest.mark.parametrize("scale", [2.0 ** -6, 3.0 / 16])
+def test_append_fp8_special_values(scale):
+    """The fp8 rule at its edges: every E4M3 magnitude and every midpoint between neighbours
+    (exact ties when the scale is a power of two), one f16 step either side, values past 448 *
+    scale (saturation), zeros of both signs and f16 subnormals."""
+    B, Hkv, D, P = 1, 2, 128, 16
+    s = workloads.spec(name="special_f8", batch=B, num_qo_heads=4, num_kv_heads=Hkv, head_dim=D,
+                       page_size=P, kv_dtype="f8", lens=("list", (64,)))
+    prob = workloads.generate(s, 37)
+    prob = dict(prob, k_scales=np.array([scale], np.float32),
+                v_scales=np.array([scale * 1.25], np.float32))
+    mags = oracle.e4m3_to_float(np.arange(0x7F, dtype=np.uint8))
+    mid = (mags[:-1] + mags[1:]) / 2
+    base = np.concatenate([mags, mid]) * scale
+    h = base.astype(np.float16)
+    vals = np.concatenate([h, -h, np.nextafter(h, np.float16(np.inf)),
+                           np.nextafter(h, np.float16(0)),
+                           np.array([0.0, -0.0, 500 * scale, -600 * scale, 65504, -65504,
+                                     2.0 ** -24, -3 * 2.0 ** -24, 2.0 ** -14], np.float16)])
+    rng = np.random.default_rng(37)
+    N = 64
+    x = np.resize(rng.permutation(vals), 2 * N * Hkv * D).astype(np.float16)
+    kn = x[:N * Hkv * D].reshape(N, Hkv, D)
+    vn = x[N * Hkv * D:].reshape(N, Hkv, D)
+    new = dict(k_new=kn, v_new=vn, batch_idx=np.zeros(N, np.int32),
+               positions=rng.permutation(64).astype(np.int32))
+    plan = make_plan(prob)
+    got = gpu_append(plan, prob, new)
+    want = oracle_append(prob, new, plan.params.max_kv_len)
+    assert_pools_equal(got, want, f"fp8 special values, scale {scale}")
+
+
 def test_append_skips_invalid_tokens():
     """Tokens naming a sequence outside [0, batch), a position outside [0, max_kv_len), or a page
     id outside the pool write nothing (the kernel's own bounds checks); the rest are written."""
@@ -187,7 +222,7 @@ def test_append_workloads_full_size(name):
     assert_pools_equal(got, want, name)
 
 
-@pytest.mark.parametrize("kv", ["f16", "i8"])
+@pytest.mark.parametrize("kv", ["f16", "i8", "f8"])
 def test_append_then_decode(kv):
     """A decode step: append T new tokens per sequence at the end of each cache, then decode
     over the result on the GPU; the pools match the oracle's append bit for bit and the decode
