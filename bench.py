@@ -2,8 +2,8 @@
 """Benchmark: split-KV paged decode on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--config 2] [--gpus 1] [--no-cpu]
-    python bench.py --op append [--append prefill_i8|prefill_f16|decode_i8]
-    python bench.py --op prefill [--prefill prompt_i8|prompt_f16]
+    python bench.py --op append [--append prefill_i8|prefill_f16|prefill_f8|decode_i8]
+    python bench.py --op prefill [--prefill prompt_i8|prompt_f16|prompt_f8]
     python bench.py --op merge
 
 A step is one decode call (partial kernel + reducer) over one batch of the workload, with
@@ -509,7 +509,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--op", choices=["decode", "append", "prefill", "merge"], default="decode")
     ap.add_argument("--prefill", default="prompt_i8",
-                    help="prefill workload for --op prefill: prompt_i8, prompt_f16")
+                    help="prefill workload for --op prefill: prompt_i8, prompt_f16, prompt_f8")
     ap.add_argument("--append", default="prefill_i8",
                     help="append workload for --op append: prefill_i8, prefill_f16, prefill_f8, decode_i8")
     ap.add_argument("--no-append", action="store_true",

@@ -93,9 +93,9 @@ typedef enum {
                                 tensor: element value = e4m3(byte) * k_scale for K and
                                 * v_scale for V (AMD-Ecosystem/flashinfer PR #397, the two
                                 commit messages: fp8 caches are read with per-tensor k_scale
-                                and v_scale values passed by pointer). Decode, gather and append
-                                (nearest-even E4M3 of x / scale, saturating at 448); the
-                                multi-token route refuses it. */
+                                and v_scale values passed by pointer). Decode, multi-token
+                                route, gather and append (nearest-even E4M3 of x / scale,
+                                saturating at 448). */
 } skvd_kv_dtype;
 
 typedef enum {

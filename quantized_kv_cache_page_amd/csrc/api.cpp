@@ -122,8 +122,6 @@ skvd_status check_prefill(const skvd_plan *plan, const skvd_decode_args *a) {
                    p.prm.max_kv_len);
   if (p.group > 64)
     return set_err(SKVD_ERR_SHAPE, "prefill needs Hq/Hkv <= 64 (got %d)", p.group);
-  if (p.prm.kv_dtype == SKVD_KV_FP8_E4M3)
-    return set_err(SKVD_ERR_DTYPE, "the multi-token route does not read fp8 caches");
   skvd_decode_args one = *a;
   one.q_per_seq = 1;  // the remaining checks do not depend on the token count
   return skvd::check_args(p, &one, p.ws_bytes, g_err, sizeof g_err);

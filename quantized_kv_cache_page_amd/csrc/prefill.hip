@@ -1,11 +1,11 @@
 // Prefill / multi-token route: T > 8 query tokens per sequence against the paged cache, as MFMA
-// tiles with the int8 cache dequantized on its way into LDS (no f16 temporary in memory).
+// tiles with int8 and fp8 caches widened on their way into LDS (no f16 temporary in memory).
 //
 // llama-cpp-turboquant PR #176 ("HIP: fix turbo KV decode crash under graph capture;
 // batch-aware VEC/TILE FA routing", section "Changes") keeps the vector decode path for at most
 // 8 query tokens and sends larger batches to the tiled matrix-core kernel; its tiled path
 // dequantized the whole cache into K_f16/V_f16 buffers first. Here the tile kernel reads the
-// pages itself and widens int8 in registers.
+// pages itself and widens int8 and fp8 bytes in registers.
 //
 // Work unit: one workgroup of 4 waves per (sequence b, KV head, tile of query tokens). Its
 // query rows (128 at head_dim 128, 64 at 256) are (token, head-of-group) pairs r = token * G +
@@ -80,9 +80,12 @@ struct TileRegs {
   _Float16 ks[I8 ? N : 1], vs[I8 ? N : 1];
 };
 
-template <int D, bool I8>
+// KV: 0 f16, 1 int8 with per-32 f16 scales, 2 fp8 E4M3 with one f32 scale per tensor (the
+// one-byte formats share the int8 tile layout; only int8 loads per-row scales).
+template <int D, int KV>
 __device__ __forceinline__ void load_tile(const LaunchArgs &a, int b, int kvh, int kv0, int kv_last,
-                                          TileRegs<D, I8> &r) {
+                                          TileRegs<D, KV != 0> &r) {
+  constexpr bool I8 = KV != 0;
   using TR = TileRegs<D, I8>;
   const int P1 = (1 << a.page_shift) - 1;
   const int tok = min(kv0 + (int)threadIdx.x / TR::TPT, kv_last);  // tail re-reads (masked)
@@ -104,6 +107,14 @@ __device__ __forceinline__ void load_tile(const LaunchArgs &a, int b, int kvh, i
   } else {
     const pu4 *kp = (const pu4 *)((const int8_t *)a.k + rk) + part0;
     const pu4 *vp = (const pu4 *)((const int8_t *)a.v + rv) + part0;
+    if constexpr (KV == 2) {
+#pragma unroll
+      for (int n = 0; n < TR::N; ++n) {
+        r.k[n] = kp[n];
+        r.v[n] = vp[n];
+      }
+      return;
+    }
     const int64_t s_in_page = (int64_t)(tok & P1) * a.s_tok_stride + (int64_t)kvh * a.s_head_stride;
     const _Float16 *ksp = (const _Float16 *)a.ks + pk * a.s_page_stride + s_in_page;
     const _Float16 *vsp = (const _Float16 *)a.vs + pv * a.s_page_stride + s_in_page;
@@ -145,8 +156,33 @@ __device__ __forceinline__ void widen16(pu4 w, _Float16 s, ph8 *lo, ph8 *hi) {
   }
 }
 
-template <int D, bool I8>
-__device__ __forceinline__ void store_tile(char *k_lds, char *v_lds, const TileRegs<D, I8> &r) {
+// 16 E4M3 bytes -> two groups of 8 f16 holding value * 2^-8 exactly: the byte s.eeee.mmm
+// becomes the f16 bits s.0eeee.mmm0000000 (the exponent field under f16's bias 15 instead of
+// E4M3's 7 is the factor 2^-8; E4M3 subnormals map onto f16 subnormals). A byte permute puts two
+// bytes into the high bytes of an f16 pair; the sign bits stay and the rest shift down by one.
+// The 2^8 and the tensor scales are applied to the score scale (K) and the output (V).
+__device__ __forceinline__ unsigned f8_pair16(unsigned w, unsigned sel) {
+  const unsigned t = __builtin_amdgcn_perm(w, w, sel);
+  return (t & 0x80008000u) | ((t >> 1) & 0x3F803F80u);
+}
+
+__device__ __forceinline__ void widen16_f8(pu4 w, ph8 *lo, ph8 *hi) {
+  pu4 l, h;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const unsigned a = f8_pair16(w[k], 0x010C000Cu);  // bytes 0, 1
+    const unsigned b = f8_pair16(w[k], 0x030C020Cu);  // bytes 2, 3
+    pu4 &dst = k < 2 ? l : h;
+    dst[2 * (k & 1)] = a;
+    dst[2 * (k & 1) + 1] = b;
+  }
+  *lo = __builtin_bit_cast(ph8, l);
+  *hi = __builtin_bit_cast(ph8, h);
+}
+
+template <int D, int KV>
+__device__ __forceinline__ void store_tile(char *k_lds, char *v_lds, const TileRegs<D, KV != 0> &r) {
+  constexpr bool I8 = KV != 0;
   using TR = TileRegs<D, I8>;
   constexpr int ROWB = D * 2;
   const int tok = (int)threadIdx.x / TR::TPT;
@@ -158,10 +194,12 @@ __device__ __forceinline__ void store_tile(char *k_lds, char *v_lds, const TileR
       *(pu4 *)(v_lds + pswz<ROWB>(tok, part)) = r.v[n];
     } else {
       ph8 lo, hi;
-      widen16(r.k[n], r.ks[n], &lo, &hi);
+      if constexpr (KV == 2) widen16_f8(r.k[n], &lo, &hi);
+      else widen16(r.k[n], r.ks[n], &lo, &hi);
       *(ph8 *)(k_lds + pswz<ROWB>(tok, 2 * part)) = lo;
       *(ph8 *)(k_lds + pswz<ROWB>(tok, 2 * part + 1)) = hi;
-      widen16(r.v[n], r.vs[n], &lo, &hi);
+      if constexpr (KV == 2) widen16_f8(r.v[n], &lo, &hi);
+      else widen16(r.v[n], r.vs[n], &lo, &hi);
       *(ph8 *)(v_lds + pswz<ROWB>(tok, 2 * part)) = lo;
       *(ph8 *)(v_lds + pswz<ROWB>(tok, 2 * part + 1)) = hi;
     }
@@ -173,8 +211,9 @@ __device__ __forceinline__ void store_tile(char *k_lds, char *v_lds, const TileR
 template <int D>
 constexpr int row_sets() { return D == 128 ? 2 : 1; }
 
-template <int D, bool I8>
+template <int D, int KV>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(LaunchArgs a, int tpw, int qtiles) {
+  constexpr bool I8 = KV != 0;
   constexpr int KT = kv_tile<D>();
   constexpr int RS = row_sets<D>();
   constexpr int NST = KT / 16;   // 16-token score sub-tiles per KV tile
@@ -241,6 +280,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(LaunchArgs a, int tpw, 
   // so the max is taken on unscaled scores and scaled once. A negative scale is carried by q
   // (negating f16 is exact); a zero scale by a tiny c (masked scores stay -inf, others ~0).
   float c = a.scale_log2;
+  if constexpr (KV == 2) c *= *(const float *)a.ks * 256.0f;  // fp8: k_scale and the 2^8
   if (c < 0.f) {
     c = -c;
 #pragma unroll
@@ -265,10 +305,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(LaunchArgs a, int tpw, 
   }
 
   const int ntiles = kv_end > 0 ? (kv_end + KT - 1) / KT : 0;
-  TileRegs<D, I8> regs;
+  TileRegs<D, I8> regs;  // (I8: the one-byte layout)
   if (ntiles > 0) {
-    load_tile<D, I8>(a, b, kvh, 0, kv_end - 1, regs);
-    store_tile<D, I8>(kv_lds[0][0], kv_lds[0][1], regs);
+    load_tile<D, KV>(a, b, kvh, 0, kv_end - 1, regs);
+    store_tile<D, KV>(kv_lds[0][0], kv_lds[0][1], regs);
   }
   __syncthreads();
   for (int it = 0; it < ntiles; ++it) {
@@ -276,7 +316,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(LaunchArgs a, int tpw, 
     const bool more = it + 1 < ntiles;
     const char *k_lds = kv_lds[it & 1][0];
     const char *v_lds = kv_lds[it & 1][1];
-    if (more) load_tile<D, I8>(a, b, kvh, kv0 + KT, kv_end - 1, regs);
+    if (more) load_tile<D, KV>(a, b, kvh, kv0 + KT, kv_end - 1, regs);
 
     // ---- S^T = K Q^T: lane holds row c16's scores for tokens 16 st + 4 g4 + e
     pf4 s[RS][NST];
@@ -371,7 +411,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(LaunchArgs a, int tpw, 
         lacc[rs] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[rs][c], lacc[rs], 0, 0, 0);
     }
     // the other buffer was last read in the previous iteration, which every wave has left
-    if (more) store_tile<D, I8>(kv_lds[(it + 1) & 1][0], kv_lds[(it + 1) & 1][1], regs);
+    if (more) store_tile<D, KV>(kv_lds[(it + 1) & 1][0], kv_lds[(it + 1) & 1][1], regs);
     __syncthreads();  // tile it+1 is in LDS, and every wave is done reading tile it
   }
 
@@ -381,7 +421,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(LaunchArgs a, int tpw, 
     const float lt = lacc[rs][0];
     if (!row_ok[rs]) continue;
     const int64_t orow = ((int64_t)b * T + trow[rs]) * a.Hq + hrow[rs];
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    float inv = lt > 0.f ? 1.f / lt : 0.f;
+    if constexpr (KV == 2) inv *= *(const float *)a.vs * 256.0f;  // fp8: v_scale and the 2^8
     _Float16 *op = (_Float16 *)a.o + orow * D + 4 * g4;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
@@ -399,8 +440,9 @@ void launch_pd(const LaunchArgs &a, hipStream_t st) {
   const int tpw = 64 * row_sets<D>() / a.G;  // query tokens per workgroup: its rows / G
   const int qtiles = (a.T + tpw - 1) / tpw;
   const unsigned grid = (unsigned)qtiles * a.Hkv * a.batch;
-  if (a.int8) prefill_kernel<D, true><<<grid, 256, 0, st>>>(a, tpw, qtiles);
-  else prefill_kernel<D, false><<<grid, 256, 0, st>>>(a, tpw, qtiles);
+  if (a.fp8) prefill_kernel<D, 2><<<grid, 256, 0, st>>>(a, tpw, qtiles);
+  else if (a.int8) prefill_kernel<D, 1><<<grid, 256, 0, st>>>(a, tpw, qtiles);
+  else prefill_kernel<D, 0><<<grid, 256, 0, st>>>(a, tpw, qtiles);
 }
 
 }  // namespace

@@ -106,7 +106,8 @@ struct AppendLaunch {
   unsigned blocks;      // set by launch_append: 256-lane workgroups launched
 };
 
-// prefill.hip: the multi-token route (T > 8) over the decode's LaunchArgs; no workspace.
+// prefill.hip: the multi-token route (T > 8) over the decode's LaunchArgs (f16, int8 or fp8
+// cache); no workspace.
 int launch_prefill(const LaunchArgs &la, void *stream);
 
 // cascade.hip: merge of attention states (validated in api.cpp)

@@ -231,8 +231,8 @@ def test_decode_check_fp8(over, status):
 
 
 def test_fp8_plan_and_unsupported_routes():
-    """fp8 plans share the one-byte layout's head grouping; the multi-token route refuses an
-    fp8 cache with SKVD_ERR_DTYPE before any launch; appends take the two tensor scales."""
+    """fp8 plans share the one-byte layout's head grouping; appends and the multi-token route
+    take the two tensor scales."""
     p8, pi = plan(kv_dtype="f8"), plan(kv_dtype="i8")
     assert p8.kv_dtype == "f8" and p8.info.heads_per_wg == pi.info.heads_per_wg
     a = good_append_args(k_scales=FAKE + (2 << 32), v_scales=FAKE + (3 << 32))
@@ -243,7 +243,8 @@ def test_fp8_plan_and_unsupported_routes():
                                     **over))
         assert bd.skvd_append_check(p8.handle, a) == st, over
     d = good_args(p8, q_per_seq=512, k_scales=FAKE + (2 << 30), v_scales=FAKE + (3 << 30))
-    assert bd.skvd_prefill_check(p8.handle, d) == 4
+    assert bd.skvd_prefill_check(p8.handle, d) == 0
+    assert bd.skvd_prefill_check(p8.handle, good_args(p8, q_per_seq=512)) == 4  # no scales
     with pytest.raises(ValueError):
         plan(kv_dtype="q4")
 

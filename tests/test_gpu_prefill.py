@@ -54,6 +54,9 @@ CASES = [
     ("gqa4_t1", 2, 1, 8, 2, 128, 16, "f16", (1, 200)),
     ("gqa4_i8_p64_ragged", 4, 70, 16, 4, 128, 64, "i8", (70, 71, 135, 2049)),
     ("gqa2_many_tiles", 1, 300, 8, 4, 128, 16, "f16", (4100,)),
+    ("gqa4_f8", 2, 100, 32, 8, 128, 16, "f8", (100, 1000)),
+    ("gqa8_d256_f8_p4", 2, 50, 16, 2, 256, 4, "f8", (50, 777)),
+    ("mha_f8_p1_ragged", 3, 40, 4, 4, 128, 1, "f8", (40, 41, 300)),
 ]
 
 
@@ -75,11 +78,12 @@ def test_prefill_rows_without_positions():
     assert (o.reshape(2, 8, 8, 128)[0, :3] == 0).all()
 
 
-def test_prefill_equals_decode_route():
+@pytest.mark.parametrize("kv", ["i8", "f8"])
+def test_prefill_equals_decode_route(kv):
     """For T <= 8 both routes compute the same attention: each matches the oracle, and they agree
     with each other within the tolerance."""
-    s = workloads.spec(name="routes", batch=3, q_per_seq=4, num_qo_heads=16, num_kv_heads=4,
-                       head_dim=128, page_size=16, kv_dtype="i8", lens=("list", (4, 900, 3000)))
+    s = workloads.spec(name=f"routes_{kv}", batch=3, q_per_seq=4, num_qo_heads=16, num_kv_heads=4,
+                       head_dim=128, page_size=16, kv_dtype=kv, lens=("list", (4, 900, 3000)))
     prob, dev, plan, o1, l1 = check(s, 63)
     plan2 = make_plan(prob)
     o2, l2 = run(plan2, prob, dev)

@@ -321,6 +321,7 @@ APPEND_CONFIGS = {
 PREFILL_CONFIGS = {
     "prompt_i8": Spec("prefill_prompt_i8", 4, 2048, 32, 8, 128, 16, "i8", ("fixed", 2048)),
     "prompt_f16": Spec("prefill_prompt_f16", 4, 2048, 32, 8, 128, 16, "f16", ("fixed", 2048)),
+    "prompt_f8": Spec("prefill_prompt_f8", 4, 2048, 32, 8, 128, 16, "f8", ("fixed", 2048)),
 }
 
 
