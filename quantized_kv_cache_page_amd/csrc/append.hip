@@ -111,42 +111,50 @@ __device__ __forceinline__ unsigned e4m3_of(float q) {
 
 // True when q lies within 4 ulps of a point where the E4M3 rounding changes (a midpoint
 // between neighbouring values): above 2^-6 the 20 f32 mantissa bits below the kept three are
-// within 4 of 0x80000; below, q * 512 is within 2^-16 of a half-integer. Binade edges are E4M3
-// values themselves, and 448 is one, so the clip adds no other decision point.
+// within 4 of 0x80000 (the bits of q itself: sign and exponent are masked off; a q beyond 448
+// that tests near only costs the slow path). Below 2^-6, where the grid is 2^-9, every nonzero q
+// counts as near. Binade edges are E4M3 values themselves, and 448 is one, so the clip adds no
+// other decision point.
 __device__ __forceinline__ bool e4m3_near_tie(float q) {
-  const float m = fminf(fabsf(q), 448.0f);
-  if (m < 0x1p-6f) {
-    const float t = m * 512.0f;
-    return fabsf(fabsf(t - rintf(t)) - 0.5f) <= 0x1p-16f;
-  }
-  return (__float_as_uint(m) & 0xFFFFFu) - 0x7FFFCu <= 8u;
+  return (fabsf(q) < 0x1p-6f && q != 0.0f) || (__float_as_uint(q) & 0xFFFFFu) - 0x7FFFCu <= 8u;
 }
 
 // The 8 E4M3 codes of one lane's elements over the tensor scale s, as if from the correctly
-// rounded quotients x / s: the product q = x * rcp(s) (rcp to 1 ulp) is within 2 ulps of x / s,
-// so the code of q is the quotient's unless q is near a rounding midpoint; those elements (and
-// every element when s or its reciprocal is outside the normal range) take the division.
+// rounded quotients x / s. The product q = x * rcp(s) (rcp to 1 ulp) is within 2 ulps of x / s,
+// so away from the rounding midpoints its code is the quotient's: the hardware conversion
+// (v_cvt_pk_fp8_f32, OCP E4M3 on gfx950, nearest even) of q clamped to +-448 gives it, four
+// bytes per two instructions. A lane with an element near a midpoint (or with s or 1/s outside
+// the normal range) recomputes its codes in software from the division for those elements.
 __device__ __forceinline__ uint2a quantize_fp8(half8a x, float s) {
   const float r = __builtin_amdgcn_rcpf(s);
   const bool normal = s >= 0x1p-125f && s <= 0x1p125f;
-  float f[8];
-  unsigned c[8];
+  float f[8], q[8];
   bool near = !normal;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     f[e] = (float)x[e];
-    const float q = f[e] * r;
-    c[e] = e4m3_of(q);
-    near |= e4m3_near_tie(q);
-  }
-  if (near) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (!normal || e4m3_near_tie(f[e] * r)) c[e] = e4m3_of(f[e] / s);
+    q[e] = f[e] * r;
+    near |= e4m3_near_tie(q[e]);
   }
   uint2a w;
-  w[0] = c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24;
-  w[1] = c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const float *qk = q + 4 * k;
+    int v = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(qk[0], -448.0f, 448.0f),
+                                            __builtin_amdgcn_fmed3f(qk[1], -448.0f, 448.0f), 0,
+                                            false);
+    v = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(qk[2], -448.0f, 448.0f),
+                                        __builtin_amdgcn_fmed3f(qk[3], -448.0f, 448.0f), v, true);
+    w[k] = (unsigned)v;
+  }
+  if (near) {
+    unsigned c[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      c[e] = e4m3_of(!normal || e4m3_near_tie(q[e]) ? f[e] / s : q[e]);
+    w[0] = c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24;
+    w[1] = c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24;
+  }
   return w;
 }
 
@@ -246,7 +254,7 @@ int launch_append(AppendLaunch a, void *stream) {
   if (a.rows == 0 || a.batch == 0) return 0;  // nothing to write (and no table row to read)
   // Grid: a whole number of tokens' lanes (so a lane keeps its head and part while it strides),
   // each lane serving up to kTokensPerLane tokens per round; at most one round of resident
-  // 256-lane workgroups (int8: 77 registers -> 6 waves per SIMD; fp8: 82 -> 5; f16: 58 -> 8),
+  // 256-lane workgroups (int8: 77 registers -> 6 waves per SIMD; fp8: 69 -> 7; f16: 58 -> 8),
   // fewer for a small append.
   a.lanes_per_token = a.Hkv * a.D / 8;
   int64_t x = a.lanes_per_token, y = 256;
@@ -258,7 +266,7 @@ int launch_append(AppendLaunch a, void *stream) {
   const int64_t g0 = a.lanes_per_token / x;  // workgroups per whole number of tokens
   const int64_t toks = (a.num_tokens + kTokensPerLane - 1) / kTokensPerLane;
   const int64_t want = (toks * a.lanes_per_token + 255) / 256;
-  const int64_t cap = (a.fp8 ? 5LL : a.int8 ? 6LL : 8LL) * a.num_cus;
+  const int64_t cap = (a.fp8 ? 7LL : a.int8 ? 6LL : 8LL) * a.num_cus;
   int64_t blocks = want < cap ? want : cap;
   blocks = (blocks + g0 - 1) / g0 * g0;
   a.blocks = (unsigned)blocks;
