@@ -286,7 +286,7 @@ def test_append_graph_capture_replay():
         torch.ones(1 << 20, device="cuda").sum()  # eager work between replays
 
 
-@pytest.mark.parametrize("kv", ["f16", "i8"])
+@pytest.mark.parametrize("kv", ["f16", "i8", "f8"])
 @pytest.mark.parametrize("form", ["halves", "interleaved", "layer"])
 def test_cache_views(kv, form):
     """K and V as views of one tensor -- the two halves of [2, pages, ...], the interleaved
