@@ -23,7 +23,7 @@ int main() {
         for (int B : batches)
           for (int L : lens)
             for (int T = 1; T <= 9; T += 4)
-              for (int dt = 0; dt < 3; ++dt)
+              for (int dt = 0; dt < 4; ++dt)  // f16, int8, fp8, and one unknown value
                 for (int sched = 0; sched < 3; ++sched) {
                   skvd_plan_params prm{};
                   prm.num_qo_heads = hh[0];
@@ -51,6 +51,7 @@ int main() {
                   a.tok_stride = (int64_t)hh[1] * D;
                   a.head_stride = D;
                   a.num_k_pages = a.num_v_pages = 1000;
+                  if (dt == SKVD_KV_FP8_E4M3) a.k_scales = a.v_scales = fake;  // one f32 each
                   if (dt == SKVD_KV_I8_F16SCALE32) {
                     a.k_scales = a.v_scales = fake;
                     a.scale_page_stride = (int64_t)P * hh[1] * (D / 32);
