@@ -333,7 +333,13 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
   // LDS, one slice per wave (each wave serves its own KV head):
   constexpr int VL = PVM ? CH * ROWB : 16;          // chunk V rows, f16
   constexpr int PL = PVM ? RM * PSTR : 4;           // probabilities [row][token]
-  constexpr int SL = SC ? CH * (D / 128) : 1;       // int8 V scales [token][group], f16
+  // int8 at D=128 (32-token chunks): a chunk's K and V scales come in one 8-byte load per lane
+  // (lanes 0..31: the K scales of chunk token lane; 32..63: the V scales of token lane - 32),
+  // issued with the chunk's K rows and handed over through LDS, instead of a two-byte load per
+  // token tile for K and an 8-byte load for V (one vector-memory instruction per chunk instead
+  // of three).
+  constexpr bool SCL = SC && D == 128 && CH == 32;
+  constexpr int SL = SCL ? 64 : SC ? CH * (D / 128) : 1;  // int8 scales [token][group], f16
   constexpr int QL = PVM ? 4 : (CH / 2) * RM;       // vector P.V: f16 pairs (tp, tp+16) [tp][row]
   __shared__ __attribute__((aligned(16))) char v_lds_all[HW * VL];
   __shared__ __attribute__((aligned(16))) float p_lds_all[HW * PL];
@@ -345,7 +351,8 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
   char *const v_lds = v_lds_all + wave * VL;
   float *const p_lds = p_lds_all + wave * PL;
   uint2v *const vsc_lds = vsc_lds_all + wave * SL;
-  const _Float16 *vsh = (const _Float16 *)vsc_lds;
+  const _Float16 *vsh = (const _Float16 *)(vsc_lds + (SCL ? CH : 0));  // V scales
+  const _Float16 *ksl = (const _Float16 *)vsc_lds;                        // K scales (SCL)
   unsigned *const p2_lds = p2_lds_all + wave * QL;
 
   const int lane = threadIdx.x & 63;
@@ -527,6 +534,7 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
   // int8 V scales: the D/32 scales of chunk token (lane % CH), one 8-byte load per lane (a
   // token-head's scales are contiguous), handed to the P.V lanes through LDS.
   uint2v vsr[D / 128];
+  uint2v scr;  // SCL: this lane's K (lane < 32) or V scales of one chunk token
 
   // K rows of chunk c0 in the score MFMA B-operand layout: tile t, lane (g4, c16) holds
   // elements 32k + 8*g4 .. +7 of token 16t + c16.
@@ -548,7 +556,7 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
 #pragma unroll
             for (int h = 0; h < 2; ++h)
               kq[t][m][h] = kv_load<true, uint4v>(base + off + 128 * m + 16 * h);
-          if constexpr (SC) {
+          if constexpr (SC && !SCL) {
             const _Float16 *sb = ksc + row_offset(pg, jte & P1, kvh, a.s_page_stride,
                                                   a.s_tok_stride, a.s_head_stride);
             const unsigned so = 2u * (min(c16_stok, (unsigned)(lim * (int)a.s_tok_stride)) + g4);
@@ -575,7 +583,7 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
           for (int m = 0; m < KS / 4; ++m)
 #pragma unroll
             for (int h = 0; h < 2; ++h) kq[t][m][h] = kv_load<true, uint4v>(kp + 128 * m + 16 * h);
-          if constexpr (SC) {
+          if constexpr (SC && !SCL) {
             const int64_t so = row_offset(pg, j & P1, kvh, a.s_page_stride, a.s_tok_stride,
                                           a.s_head_stride) + g4;
 #pragma unroll
@@ -587,6 +595,28 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
           for (int k = 0; k < KS; ++k) kb[t][k] = kv_load<true, Vec>(kp + 32 * k * ES);
         }
       }
+    }
+    if constexpr (SCL) {
+      // K scales (lanes 0..31) or V scales (32..63) of chunk token lane % 32; a token past the
+      // split reads the last one's
+      const bool isk = lane < CH;
+      const int jl = min(c0 + (lane & (CH - 1)), tok_end - 1);
+      const int64_t np = isk ? a.num_k_pages : a.num_v_pages;
+      int64_t pg;
+      if constexpr (FAST) {
+        const int tl = (jl - c0) >> 4;  // the token's 16-token tile (its page is wave-uniform)
+        int pgl = pgs[0];
+#pragma unroll
+        for (int t = 1; t < NT; ++t) pgl = tl == t ? pgs[t] : pgl;
+        pg = clamp_page(pgl, np);
+      } else {
+        bool cl;
+        pg = lookup_page(a.table, a.table_stride, b, jl, a.page_shift, np, &cl);
+        clamped_any |= cl;
+      }
+      const _Float16 *sp = (isk ? ksc : vsc) + row_offset(pg, jl & P1, kvh, a.s_page_stride,
+                                                          a.s_tok_stride, a.s_head_stride);
+      scr = *(const uint2v *)sp;
     }
   };
   // V rows of chunk c0 in the load layout: step s, lane holds elements vlane_el .. +7 of
@@ -617,7 +647,7 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
         vb[s2] = kv_load<true, Vec>(vbase + (off + vlane_el) * ES);
       }
     }
-    if constexpr (SC) {
+    if constexpr (SC && !SCL) {
       // scales of chunk token (lane % CH); a token past the split reads the last one's
       const int jl = min(c0 + lane % CH, tok_end - 1);
       int64_t pg;
@@ -656,6 +686,10 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
   // the in-order load counter is then waited on for K alone at the loop top.
   auto chunk = [&](int c0) __attribute__((always_inline)) {
     const int c1 = c0 + CH;
+    if constexpr (SCL) {  // this chunk's K and V scales to LDS (the previous chunk's reads of
+      vsc_lds[lane] = scr;  // them ended at its closing wave_sync)
+      wave_sync();
+    }
     if constexpr (FAST) chunk_pages(c1, pg_next);
     // ---- scores: S[t] = rows x 16 tokens of tile t (lane: token c16, rows 4*g4 + e)
     // The MFMA chains run for every tile, also the ones past the split (their K is a clamped
@@ -673,7 +707,10 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
           const uint4v &q4 = kq[t][k >> 2][(k & 3) >> 1];
           const unsigned w0 = q4[2 * (k & 1)], w1 = q4[2 * (k & 1) + 1];
           half8 kh;
-          if constexpr (SC) kh = i8x8_to_h8(uint2v{w0, w1}) * (half8)ksh[t][k >> 2];
+          if constexpr (SCL)
+            kh = i8x8_to_h8(uint2v{w0, w1}) *
+                 (half8)ksl[(16 * t + c16) * (D / 32) + g4 + 4 * (k >> 2)];
+          else if constexpr (SC) kh = i8x8_to_h8(uint2v{w0, w1}) * (half8)ksh[t][k >> 2];
           else kh = f8x8_to_h8(uint2v{w0, w1});  // fp8: k_scale * 2^8 is in the score scale
           S[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[k], kh, S[t], 0, 0, 0);
         }
@@ -738,7 +775,7 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
         }
         *(half8 *)(v_lds + swz<ROWB>(row, lane % LPR)) = h;
       }
-      if constexpr (SC) {
+      if constexpr (SC && !SCL) {
         if (lane < CH) {
 #pragma unroll
           for (int k4 = 0; k4 < D / 128; ++k4) vsc_lds[lane * (D / 128) + k4] = vsr[k4];
@@ -808,7 +845,7 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
       float al[RM];
 #pragma unroll
       for (int r = 0; r < RM; ++r) al[r] = readlane_f(alpha[r & 3], 16 * (r >> 2));
-      if constexpr (SC) {
+      if constexpr (SC && !SCL) {
         if (lane < CH) {
 #pragma unroll
           for (int k4 = 0; k4 < D / 128; ++k4) vsc_lds[lane * (D / 128) + k4] = vsr[k4];
