@@ -61,6 +61,9 @@ SMALL = [
     ("int8_p1", 2, 1, 8, 2, 128, 1, "i8", ("list", (33, 200))),
     ("int8_t4_d256", 2, 4, 8, 4, 256, 16, "i8", ("list", (4, 600))),
     ("int8_t3_g2", 2, 3, 4, 2, 128, 8, "i8", ("list", (3, 400))),
+    ("int8_t4_g4", 2, 4, 16, 4, 128, 16, "i8", ("list", (4, 900))),     # 16 rows: 4 quarters
+    ("int8_t4_g4_p4", 3, 4, 8, 2, 128, 4, "i8", ("list", (5, 64, 333))),
+    ("int8_t2_g4", 2, 2, 8, 2, 128, 16, "i8", ("list", (2, 1500))),     # 8 rows: 2 quarters
 ]
 
 
