@@ -27,6 +27,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -42,6 +43,14 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def _code_only(src: bytes) -> bytes:
+    """Source text without comments and with whitespace runs collapsed, so that the hashes
+    below change when the compiled code can change, not when a comment does."""
+    src = re.sub(rb"/\*.*?\*/", b" ", src, flags=re.S)
+    src = re.sub(rb"//[^\n]*", b" ", src)
+    return b" ".join(src.split())
+
+
 def kernel_source_hash() -> str:
     """Hash of the partial kernel's source (kernels.hip up to the merge kernels, which holds
     the addressing helpers and the partial kernel) and of plan.cpp (its launch shape)."""
@@ -49,10 +58,10 @@ def kernel_source_hash() -> str:
     h = hashlib.sha256()
     with open(os.path.join(csrc, "kernels.hip"), "rb") as fh:
         src = fh.read()
-    h.update(src[:src.index(b"// ---------------------------------------------------------------"
-                             b"-------------- merge kernels")])
+    h.update(_code_only(src[:src.index(b"// ---------------------------------------------------------"
+                                       b"-------------------- merge kernels")]))
     with open(os.path.join(csrc, "plan.cpp"), "rb") as fh:
-        h.update(fh.read())
+        h.update(_code_only(fh.read()))
     return h.hexdigest()[:16]
 
 
@@ -60,7 +69,7 @@ def append_source_hash() -> str:
     """Hash of the append kernel's source (append.hip holds the kernel and its launch shape)."""
     h = hashlib.sha256()
     with open(os.path.join(ROOT, "quantized_kv_cache_page_amd", "csrc", "append.hip"), "rb") as fh:
-        h.update(fh.read())
+        h.update(_code_only(fh.read()))
     return h.hexdigest()[:16]
 
 
@@ -83,7 +92,7 @@ def merge_source_hash() -> str:
     """Hash of the merge-states kernel's source (cascade.hip)."""
     h = hashlib.sha256()
     with open(os.path.join(ROOT, "quantized_kv_cache_page_amd", "csrc", "cascade.hip"), "rb") as fh:
-        h.update(fh.read())
+        h.update(_code_only(fh.read()))
     return h.hexdigest()[:16]
 
 

@@ -255,8 +255,9 @@ skvd_status skvd_decode_partial_timed(const skvd_plan *plan, const skvd_decode_a
                                       void *start_event, void *stop_event);
 
 /* Test aid: copy the raw elements of every visible K/V row (position j < kv_len[b]) into
- * dense [B, max_len, Hkv, D] arrays (element size 2 for f16, 1 for int8), and for int8 the
- * raw f16 scales into dense [B, max_len, Hkv, D/32] arrays (dense_ks/dense_vs; NULL for f16).
+ * dense [B, max_len, Hkv, D] arrays (element size 2 for f16, 1 for int8 and fp8), and for int8
+ * the raw f16 scales into dense [B, max_len, Hkv, D/32] arrays (dense_ks/dense_vs; NULL for f16
+ * and fp8, whose scales are per tensor).
  * The row address comes from the same device function the decode kernels use. Rows at or
  * beyond kv_len[b] are not written. max_len >= every kv_len[b]. o, lse are ignored. */
 skvd_status skvd_gather_debug(const skvd_plan *plan, const skvd_decode_args *args,

@@ -553,7 +553,8 @@ class Plan:
     def append(self, k_new, v_new, batch_idx, positions, k_pages, v_pages, page_table,
                k_scales=None, v_scales=None, batch=None, stream=None):
         """skvd_append: write new rows k_new, v_new [N, Hkv, D] f16 of tokens (batch_idx[i],
-        positions[i]) into the pools in place (int8 pools: quantized, scales written). Only the
+        positions[i]) into the pools in place (int8 pools: quantized, scales written; fp8 pools:
+        quantized with the given tensor scales, which are only read). Only the
         named slots are written; nothing is allocated."""
         a = self.make_append_args(k_new, v_new, batch_idx, positions, k_pages, v_pages,
                                   page_table, k_scales, v_scales, batch)

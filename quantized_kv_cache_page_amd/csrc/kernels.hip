@@ -1,18 +1,21 @@
 // HIP kernels for split-KV paged decode attention on gfx950 (CDNA4, wave64).
 //
-// Partial kernel: one wave64 workgroup per (split, KV head, sequence). A split is a run of
-// 64-token blocks (1bit-MONSTER/engine issue #115, "Closing the remaining half of this
-// issue": one producer partial per 64-token block; here a workgroup covers `bps` blocks).
-// For each chunk of tokens it
+// Partial kernel: workgroups of one wave per KV head served (1, 2, 4 or 8), each covering a
+// run of 64-token blocks of one or more (sequence, KV head group) rows (1bit-MONSTER/engine
+// issue #115, "Closing the remaining half of this issue": one producer partial per 64-token
+// block; here a workgroup covers a split of `bps` blocks, or an equal share of the batch's
+// blocks under the balanced schedule). For each chunk of tokens it
 //   1. gathers K and V rows through the page table straight into registers (16-byte loads;
 //      the page id of a 16-token tile is wave-uniform when P >= 16),
 //   2. computes the scores of the G*T query rows against 16-token tiles with the 16x16x32
 //      f16 MFMA (query rows x tokens, contraction over head_dim; int8 K is widened to f16
-//      exactly and its per-32 scale applied to each 32-element partial dot product in f32),
+//      exactly and multiplied by its per-32 scale in f16, one rounding; fp8 K is widened
+//      exactly to value * 2^-8, its tensor scale and the 2^8 going into the score scale),
 //   3. masks positions past the split, the sequence and (T > 1) the causal limit, and updates
 //      the running max and sum in base 2 (online softmax),
-//   4. accumulates P.V on the vector ALU in f32, lanes owning 8 head_dim elements of a V
-//      row and reading the probabilities from LDS (int8 V: the scale is folded into p).
+//   4. accumulates P.V in f32: for one query-row quarter as f16 pair dot products from the V
+//      registers (int8 V: the scale is folded into the probabilities; fp8 V: the tensor scale
+//      is applied to the output), otherwise on the MFMA from an LDS copy of V.
 // It writes one partial (max, sum, f32 output) per query row, or o and lse directly when
 // the plan has a single split.
 //
