@@ -157,3 +157,27 @@ def test_fp8_deterministic_and_read_only():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     for b, k in zip(before, ("k_pages", "v_pages", "k_scales", "v_scales")):
         assert torch.equal(b, dev[k]), k
+
+
+@pytest.mark.parametrize("route", ["decode", "prefill"])
+def test_fp8_scale_edges(route):
+    """Tensor scales that are negative (the scores change sign: on the multi-token route the
+    sign is carried by q) or zero (k_scale 0: uniform weights; v_scale 0: o = 0)."""
+    T = 2 if route == "decode" else 24
+    s = workloads.spec(name=f"f8_edges_{route}", batch=2, q_per_seq=T, num_qo_heads=8,
+                       num_kv_heads=2, head_dim=128, page_size=16, kv_dtype="f8",
+                       lens=("list", (T, 700)))
+    prob = workloads.generate(s, 41)
+    k0, v0 = float(prob["k_scales"][0]), float(prob["v_scales"][0])
+    for ks, vs in ((-k0, v0), (0.0, v0), (k0, 0.0), (-2 * k0, -v0)):
+        p = dict(prob, k_scales=np.array([ks], np.float32), v_scales=np.array([vs], np.float32))
+        dev = to_dev(p)
+        plan = make_plan(p, max_q_per_seq=T if route == "decode" else 1)
+        args = (dev["q"], dev["k_pages"], dev["v_pages"], dev["page_table"], dev["kv_len"],
+                p["sm_scale"], dev["k_scales"], dev["v_scales"])
+        o, lse = (plan.run if route == "decode" else plan.prefill)(*args, q_per_seq=T)
+        torch.cuda.synchronize()
+        ro, rl = oracle.decode(p)
+        compare(o, lse, ro, rl, what=f"{route} k_scale={ks:.4f} v_scale={vs:.4f}")
+        if vs == 0.0:
+            assert not o.float().abs().max().item()
