@@ -82,7 +82,7 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
     return fail(err, errn, SKVD_ERR_PLAN, "wgs_per_cu=%d outside 0..64", prm.wgs_per_cu);
   // KV heads per workgroup: the single-quarter variants at D=128 come in 1, 2, 4 and 8.
   const bool multi_head_ok = D == 128 && G * prm.max_q_per_seq <= 4;
-  const bool i8_kv = prm.kv_dtype != SKVD_KV_F16;  // one-byte elements (int8 or fp8)
+  const bool i8_kv = prm.kv_dtype == SKVD_KV_I8_F16SCALE32;
   int hw = prm.heads_per_wg;
   // A decode with no more (sequence, KV head, block) units than CUs is latency-bound: one
   // head per workgroup spreads it over the most CUs (measured: B=1, 1024 tokens, 12.5 vs 13.8
@@ -167,13 +167,14 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
     // workgroup of 8 KV heads at a time, two per CU in two rounds (the registers hold one), so
     // that the dispatcher hands each CU its second share when it frees up; D=256 workgroups
     // are the largest (3 per CU measured best).
-    // fp8 (no per-element scale work) does best with eight waves per CU whatever the head
-    // count per workgroup (measured: GQA batch 45.9 us with 8 heads x 1 workgroup, 55.7 with
-    // int8's 8 x 2; the int8 batch shape 541 vs 546 us).
+    // fp8 (no per-row scale loads) does best with twelve waves per CU, as three workgroups of
+    // 4 KV heads (measured, two interleaved rounds: GQA batch 44.6 us/call against 46.4 with
+    // 8 heads x 1 and 45.1 with 4 x 2; the int8 batch's shape 521.9 against 530.5 and 530.2;
+    // int8's 8 x 2 ran the GQA batch at 55.7).
     const bool i8 = prm.kv_dtype == SKVD_KV_I8_F16SCALE32;
     const bool f8 = prm.kv_dtype == SKVD_KV_FP8_E4M3;
     const int auto_wpc = D == 256 ? 3
-                         : p.row_blocks == 1 ? (f8   ? 8 / hw
+                         : p.row_blocks == 1 ? (f8   ? std::max(1, 12 / hw)
                                                 : i8 ? (hw == 8 ? 2 : 8 / hw)
                                                      : std::max(1, kDefaultWgsPerCu / hw))
                                              : kDefaultWgsPerCu;

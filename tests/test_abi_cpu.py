@@ -231,10 +231,11 @@ def test_decode_check_fp8(over, status):
 
 
 def test_fp8_plan_and_unsupported_routes():
-    """fp8 plans share the one-byte layout's head grouping; appends and the multi-token route
-    take the two tensor scales."""
+    """fp8 plans: 4 KV heads per workgroup, three workgroups per CU (int8: 8 heads); appends
+    and the multi-token route take the two tensor scales."""
     p8, pi = plan(kv_dtype="f8"), plan(kv_dtype="i8")
-    assert p8.kv_dtype == "f8" and p8.info.heads_per_wg == pi.info.heads_per_wg
+    assert p8.kv_dtype == "f8" and p8.info.heads_per_wg == 4 and pi.info.heads_per_wg == 8
+    assert "grid=768" in p8.describe()
     a = good_append_args(k_scales=FAKE + (2 << 32), v_scales=FAKE + (3 << 32))
     assert bd.skvd_append_check(p8.handle, a) == 0
     for over, st in ((dict(k_scales=None), 4), (dict(v_scales=FAKE + 2), 3),
