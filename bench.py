@@ -749,6 +749,17 @@ def main():
                           "roofline_frac": round(rp["tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
                           "bound": "mfma", "flops_per_call": rp["flops"]}
         log(f"[bench] prefill {rp['us_per_call']:.2f} us/call, {rp['tflops']:.0f} TFLOP/s")
+        # the decode over an fp8 (E4M3, per-tensor scales) cache of the int8 batch's shape
+        s8 = workloads.config(5)
+        s8 = dataclasses.replace(s8, kv_dtype="f8", name=f"{s8.name}_f8")
+        us8, part8, kvb8, plan8 = time_decode(s8, 5, min(K, 100), args.warmup)
+        res["fp8"] = {"workload": f"{s8.name}: int8 batch's shape (B=64, Zipf lengths) over OCP "
+                                  f"E4M3 pools with one f32 scale per tensor",
+                      "us_per_call": round(us8, 3), "partial_us": round(part8, 3),
+                      "gbs": round(kvb8 / (us8 * 1e-6) / 1e9, 1),
+                      "roofline_frac": round(kvb8 / (part8 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                      "kv_bytes_per_call": kvb8, "plan": plan8}
+        log(f"[bench] fp8 decode {us8:.2f} us/call, partial {part8:.2f} us")
     if not args.no_cpu:
         log("[bench] timing the CPU oracle ...")
         res["cpu_baseline"] = cpu_baseline(prob)
