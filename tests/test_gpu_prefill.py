@@ -156,12 +156,13 @@ def test_prefill_long_prompt_sampled():
     check(s, 70)
 
 
-def test_attention_routing():
+@pytest.mark.parametrize("kv", ["i8", "f8"])
+def test_attention_routing(kv):
     """skvd_attention: T = 4 takes the decode (bit-identical to run()), T = 40 the tiled route
     (bit-identical to prefill())."""
     for T, lens in ((4, (4, 900, 3000)), (40, (40, 900, 3000))):
-        s = workloads.spec(name=f"route_T{T}", batch=3, q_per_seq=T, num_qo_heads=16,
-                           num_kv_heads=4, head_dim=128, page_size=16, kv_dtype="i8",
+        s = workloads.spec(name=f"route_T{T}_{kv}", batch=3, q_per_seq=T, num_qo_heads=16,
+                           num_kv_heads=4, head_dim=128, page_size=16, kv_dtype=kv,
                            lens=("list", lens))
         prob = workloads.generate(s, 76)
         dev = to_dev(prob)
