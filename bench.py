@@ -495,7 +495,7 @@ def bench_append(args):
         "metric": APPEND_METRIC, "value": round(r["gbs"], 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["us_per_call"] / 1e3, 5),
         "us_per_call": round(r["us_per_call"], 3), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "i8" if spec.kv_dtype == "i8" else "f16",
+        "vs_baseline": None, "dtype": {"i8": "i8", "f8": "f8"}.get(spec.kv_dtype, "f16"),
         "data": "synthetic",
         "config": {"workload": r["workload"], "seed": seed, "bytes_per_call": r["bytes"],
                    "copies_rotated": r["copies"]},
