@@ -52,6 +52,9 @@ __device__ __forceinline__ float quad_dpp(float x) {
 // nearly every element costs one multiply.
 __device__ __forceinline__ uint2a quantize8(half8a x, _Float16 *scale) {
   constexpr float kNear = 0.5f - 0x1p-12f;
+  // 1.5 * 2^23: adding it to a value of magnitude below 2^22 rounds that value to an integer
+  // (nearest even) held in the low mantissa bits, two's complement in the low byte
+  constexpr float kMagic = 12582912.0f;
   float f[8];
   float amax = 0.0f;
 #pragma unroll
@@ -64,31 +67,30 @@ __device__ __forceinline__ uint2a quantize8(half8a x, _Float16 *scale) {
   const _Float16 sh = (_Float16)(amax / 127.0f);
   const float s = (float)sh;
   const float rs = __builtin_amdgcn_rcpf(s);
-  float c[8];
+  // clip(rint(q), -127, 127) = rint(clip(q, -127, 127)): clamp, then one add rounds and the low
+  // byte is the code; q - rint(q) from the same add flags the elements near a half-integer
+  unsigned c[8];
   bool near = false;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const float q = f[e] * rs;
-    c[e] = rintf(q);
-    near |= fabsf(q - c[e]) > kNear;
+    const float qc = __builtin_amdgcn_fmed3f(f[e] * rs, -127.0f, 127.0f);
+    const float t = qc + kMagic;
+    c[e] = __float_as_uint(t) & 0xFFu;
+    near |= fabsf(qc - (t - kMagic)) > kNear;
   }
   if (near && s > 0.0f) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float q = f[e] * rs;
-      if (fabsf(q - rintf(q)) > kNear) c[e] = rintf(f[e] / s);
+      const float qc = __builtin_amdgcn_fmed3f(f[e] * rs, -127.0f, 127.0f);
+      if (fabsf(qc - rintf(qc)) > kNear)
+        c[e] = (unsigned)(int)__builtin_amdgcn_fmed3f(rintf(f[e] / s), -127.0f, 127.0f) & 0xFFu;
     }
   }
-  unsigned w[2] = {0u, 0u};
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float cc = s > 0.0f ? __builtin_amdgcn_fmed3f(c[e], -127.0f, 127.0f) : 0.0f;
-    w[e >> 2] |= ((unsigned)(int)cc & 0xFFu) << (8 * (e & 3));
-  }
+  const unsigned keep = s > 0.0f ? 0xFFFFFFFFu : 0u;  // s = 0: every code 0
   *scale = sh;
   uint2a r;
-  r[0] = w[0];
-  r[1] = w[1];
+  r[0] = (c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24) & keep;
+  r[1] = (c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24) & keep;
   return r;
 }
 
