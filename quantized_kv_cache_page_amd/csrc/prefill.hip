@@ -78,6 +78,10 @@ struct TileRegs {
   static constexpr int N = CPR / TPT;              // chunks per thread per tensor
   pu4 k[N], v[N];
   _Float16 ks[I8 ? N : 1], vs[I8 ? N : 1];
+  // int8 with four threads per token (D = 128): the token's K scales (thread 0 of the quad) or
+  // V scales (thread 1), all four groups in one 8-byte load, shared over the quad by DPP
+  static constexpr bool kQuadScales = I8 && TPT == 4 && N == 2;
+  unsigned sq[2];
 };
 
 // KV: 0 f16, 1 int8 with per-32 f16 scales, 2 fp8 E4M3 with one f32 scale per tensor (the
@@ -122,8 +126,18 @@ __device__ __forceinline__ void load_tile(const LaunchArgs &a, int b, int kvh, i
     for (int n = 0; n < TR::N; ++n) {
       r.k[n] = kp[n];
       r.v[n] = vp[n];
-      r.ks[n] = ksp[(part0 + n) >> 1];  // a 16-element chunk lies in scale group chunk / 2
-      r.vs[n] = vsp[(part0 + n) >> 1];
+      if constexpr (!TR::kQuadScales) {
+        r.ks[n] = ksp[(part0 + n) >> 1];  // a 16-element chunk lies in scale group chunk / 2
+        r.vs[n] = vsp[(part0 + n) >> 1];
+      }
+    }
+    if constexpr (TR::kQuadScales) {
+      const unsigned q = threadIdx.x & 3u;
+      const _Float16 *sp = q == 0 ? ksp : vsp;  // threads 2 and 3 re-read V's line (unused)
+      typedef unsigned su2 __attribute__((ext_vector_type(2)));
+      const su2 sv = *(const su2 *)sp;
+      r.sq[0] = sv[0];
+      r.sq[1] = sv[1];
     }
   }
 }
@@ -180,10 +194,26 @@ __device__ __forceinline__ void widen16_f8(pu4 w, ph8 *lo, ph8 *hi) {
   *hi = __builtin_bit_cast(ph8, h);
 }
 
+// Broadcast of a quad's lane L (quad_perm [L, L, L, L]).
+template <int L>
+__device__ __forceinline__ unsigned quad_bcast(unsigned x) {
+  return (unsigned)__builtin_amdgcn_mov_dpp((int)x, L * 0x55, 0xF, 0xF, false);
+}
+
 template <int D, int KV>
 __device__ __forceinline__ void store_tile(char *k_lds, char *v_lds, const TileRegs<D, KV != 0> &r) {
   constexpr bool I8 = KV != 0;
   using TR = TileRegs<D, I8>;
+  _Float16 qks = 0, qvs = 0;  // kQuadScales: this thread's group (its quad index) of K and V
+  if constexpr (TR::kQuadScales) {
+    const unsigned q = threadIdx.x & 3u;
+    const unsigned k0 = quad_bcast<0>(r.sq[0]), k1 = quad_bcast<0>(r.sq[1]);
+    const unsigned v0 = quad_bcast<1>(r.sq[0]), v1 = quad_bcast<1>(r.sq[1]);
+    const unsigned kw = q < 2 ? k0 : k1, vw = q < 2 ? v0 : v1;
+    const unsigned sh = (q & 1u) * 16u;
+    qks = __builtin_bit_cast(_Float16, (unsigned short)(kw >> sh));
+    qvs = __builtin_bit_cast(_Float16, (unsigned short)(vw >> sh));
+  }
   constexpr int ROWB = D * 2;
   const int tok = (int)threadIdx.x / TR::TPT;
 #pragma unroll
@@ -195,11 +225,11 @@ __device__ __forceinline__ void store_tile(char *k_lds, char *v_lds, const TileR
     } else {
       ph8 lo, hi;
       if constexpr (KV == 2) widen16_f8(r.k[n], &lo, &hi);
-      else widen16(r.k[n], r.ks[n], &lo, &hi);
+      else widen16(r.k[n], TR::kQuadScales ? qks : r.ks[n], &lo, &hi);
       *(ph8 *)(k_lds + pswz<ROWB>(tok, 2 * part)) = lo;
       *(ph8 *)(k_lds + pswz<ROWB>(tok, 2 * part + 1)) = hi;
       if constexpr (KV == 2) widen16_f8(r.v[n], &lo, &hi);
-      else widen16(r.v[n], r.vs[n], &lo, &hi);
+      else widen16(r.v[n], TR::kQuadScales ? qvs : r.vs[n], &lo, &hi);
       *(ph8 *)(v_lds + pswz<ROWB>(tok, 2 * part)) = lo;
       *(ph8 *)(v_lds + pswz<ROWB>(tok, 2 * part + 1)) = hi;
     }
