@@ -152,3 +152,24 @@ def test_fp8_pins_catch_planted_mistake(mutant):
         lib = oracle.load(oracle.build(os.path.join(d, f"liboracle_m{mutant}.so"), mutant=mutant))
         failed = [n for n, fn in ALL_PINS if not fn(lib)]
         assert failed, f"no pin catches mutant {mutant} ({MUTANTS[mutant]})"
+
+
+def test_fp8_generator_recipe():
+    """The fp8 inputs follow their recipe: scales in [1/80, 1/64]; every byte a decode reads is a
+    finite E4M3 value and every slot it must not read holds the NaN byte; dequantized values are
+    N(0,1) draws to within E4M3's rounding."""
+    import workloads
+    s = workloads.spec(name="f8_recipe", batch=3, q_per_seq=1, num_qo_heads=8, num_kv_heads=2,
+                       head_dim=128, page_size=16, kv_dtype="f8", lens=("list", (5, 300, 64)))
+    prob = workloads.generate(s, 9)
+    ks, vs = float(prob["k_scales"][0]), float(prob["v_scales"][0])
+    assert 1 / 80 <= ks <= 1 / 64 and 1 / 80 <= vs <= 1 / 64
+    k, table, L, P = prob["k_pages"], prob["page_table"], prob["kv_len"], 16
+    live = np.zeros(k.shape[:2], bool)
+    for b in range(3):
+        for j in range(int(L[b])):
+            live[table[b, j // P], j % P] = True
+    assert not ((k[live] & 0x7F) == 0x7F).any()
+    assert ((k[~live] & 0x7F) == 0x7F).all()
+    x = e4m3_values(k[live]) * ks
+    assert abs(x.mean()) < 0.05 and 0.93 < x.std() < 1.07
