@@ -173,7 +173,11 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
     // int8's 8 x 2 ran the GQA batch at 55.7).
     const bool i8 = prm.kv_dtype == SKVD_KV_I8_F16SCALE32;
     const bool f8 = prm.kv_dtype == SKVD_KV_FP8_E4M3;
-    const int auto_wpc = D == 256 ? 3
+    // D = 256 variants hold one wave per SIMD (over 256 registers with the accumulators): f16,
+    // a pure stream, does best with three workgroups per CU (the wide multi-token workload 527
+    // us against 537 with four); the one-byte formats widen every element and need all four
+    // SIMDs (fp8: 604.7 -> 460.9 us with four)
+    const int auto_wpc = D == 256 ? (prm.kv_dtype == SKVD_KV_F16 ? 3 : 4)
                          : p.row_blocks == 1 ? (f8   ? std::max(1, 12 / hw)
                                                 : i8 ? (hw == 8 ? 2 : 8 / hw)
                                                      : std::max(1, kDefaultWgsPerCu / hw))
