@@ -346,3 +346,20 @@ def test_attention_routes_errors():
     # T above the plan's bound: the tiled route; its checks (here a bad q stride) apply
     assert bd.skvd_attention(p.handle, good_args(p, q_per_seq=64, q_head_stride=100), None, 0,
                              None) == 3
+
+
+def test_plan_waves_per_cu_by_format():
+    """Workgroups per CU chosen per format (256 CUs): at head_dim 128 with one query-row quarter,
+    f16 4 KV heads x 1 workgroup, int8 8 x 2, fp8 4 x 3; at head_dim 256 (one wave per SIMD),
+    f16 three workgroups per CU, the one-byte formats four."""
+    def grid(**kw):
+        d = plan(**kw).describe()
+        return int(d.split("grid=")[1].split()[0]), int(d.split("heads_per_wg=")[1].split()[0])
+    assert grid(kv_dtype="f16") == (256, 4)
+    assert grid(kv_dtype="i8") == (512, 8)
+    assert grid(kv_dtype="f8") == (768, 4)
+    wide = dict(num_qo_heads=32, num_kv_heads=16, head_dim=256, max_batch=8, max_q_per_seq=4,
+                max_kv_len=32768)
+    assert grid(kv_dtype="f16", **wide) == (768, 1)
+    assert grid(kv_dtype="i8", **wide) == (1024, 1)
+    assert grid(kv_dtype="f8", **wide) == (1024, 1)
