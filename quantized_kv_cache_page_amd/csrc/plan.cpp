@@ -165,8 +165,7 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
     // an f16 stream, best as one workgroup of 4 KV heads reading each token row's heads
     // together; int8 at D=128 also needs vector-ALU throughput, so two waves per SIMD: one
     // workgroup of 8 KV heads at a time, two per CU in two rounds (the registers hold one), so
-    // that the dispatcher hands each CU its second share when it frees up; D=256 workgroups
-    // are the largest (3 per CU measured best).
+    // that the dispatcher hands each CU its second share when it frees up.
     // fp8 (no per-row scale loads) does best with twelve waves per CU, as three workgroups of
     // 4 KV heads (measured, two interleaved rounds: GQA batch 44.6 us/call against 46.4 with
     // 8 heads x 1 and 45.1 with 4 x 2; the int8 batch's shape 521.9 against 530.5 and 530.2;
@@ -176,7 +175,7 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
     // D = 256 variants hold one wave per SIMD (over 256 registers with the accumulators): f16,
     // a pure stream, does best with three workgroups per CU (the wide multi-token workload 527
     // us against 537 with four); the one-byte formats widen every element and need all four
-    // SIMDs (fp8: 604.7 -> 460.9 us with four)
+    // SIMDs (fp8: 604.7 -> 460.9 us with four, int8: 640.5 -> 484.2)
     const int auto_wpc = D == 256 ? (prm.kv_dtype == SKVD_KV_F16 ? 3 : 4)
                          : p.row_blocks == 1 ? (f8   ? std::max(1, 12 / hw)
                                                 : i8 ? (hw == 8 ? 2 : 8 / hw)
