@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define SKVD_ABI_VERSION 9
+#define SKVD_ABI_VERSION 10
 
 typedef enum {
   SKVD_OK = 0,
@@ -109,14 +109,14 @@ typedef enum {
 
 /* How the partial kernel's workgroups divide the batch's 64-token blocks. */
 typedef enum {
-  SKVD_SCHEDULE_AUTO = 0,     /* balanced when the plan splits and max_batch <= 64, else static */
+  SKVD_SCHEDULE_AUTO = 0,     /* balanced when the plan splits and max_batch <= 1024, else static */
   SKVD_SCHEDULE_STATIC = 1,   /* one workgroup per (split of blocks_per_split blocks, KV head,
                                  sequence); splits past a sequence's length exit at once */
   SKVD_SCHEDULE_BALANCED = 2  /* the launch's blocks, in (sequence, KV head, block) order, cut
                                  on the device into W equal contiguous shares, W = min(grid,
                                  blocks / blocks_per_split); a share may cover parts of several
                                  (sequence, KV head) rows and writes one partial per part.
-                                 Needs max_batch <= 64 and more than one split. */
+                                 Needs max_batch <= 1024 and more than one split. */
 } skvd_schedule;
 
 /* Static shape of a plan. All sizes are upper bounds of what skvd_decode may be given. */
@@ -126,7 +126,9 @@ typedef struct {
   int32_t head_dim;       /* D: 128 or 256 */
   int32_t page_size;      /* P: power of two, 1..1024 */
   int32_t max_batch;      /* B upper bound, >= 1 */
-  int32_t max_q_per_seq;  /* T upper bound: 1..8, and G * T <= 16 */
+  int32_t max_q_per_seq;  /* T upper bound: 1..8 (G * T <= 1024 query rows per KV head: up to 16
+                             per wave, up to 4 waves of one KV head per workgroup, and groups of
+                             64 rows beyond that) */
   int32_t max_kv_len;     /* kv_len upper bound, >= 1 */
   int32_t kv_dtype;       /* skvd_kv_dtype */
   int32_t device;         /* HIP device ordinal the calls run on */
@@ -258,8 +260,13 @@ skvd_status skvd_decode_partial_timed(const skvd_plan *plan, const skvd_decode_a
  * dense [B, max_len, Hkv, D] arrays (element size 2 for f16, 1 for int8 and fp8), and for int8
  * the raw f16 scales into dense [B, max_len, Hkv, D/32] arrays (dense_ks/dense_vs; NULL for f16
  * and fp8, whose scales are per tensor).
- * The row address comes from the same device function the decode kernels use. Rows at or
- * beyond kv_len[b] are not written. max_len >= every kv_len[b]. o, lse are ignored. */
+ * It runs the plan's own partial-kernel variant -- the same schedule, page lookups, lane
+ * offsets, loads and (int8) register transposes as skvd_decode -- in a debug form that stores
+ * each K/V element and scale it holds at the point where the decode consumes it, at the
+ * position the decode attributes it to, and computes nothing else; a wrong address or lane
+ * mapping in the decode shows up as a wrong element here. Rows at or beyond kv_len[b] are not
+ * written. max_len >= every kv_len[b]; dense_k / dense_v 16-byte aligned, dense_ks / dense_vs
+ * 2-byte aligned. o, lse and the workspace are not used. */
 skvd_status skvd_gather_debug(const skvd_plan *plan, const skvd_decode_args *args,
                               int32_t max_len, void *dense_k, void *dense_v, void *dense_ks,
                               void *dense_vs, void *stream);

@@ -22,7 +22,7 @@ REDUCERS = {"auto": 0, "direct": 1, "cooperative": 2, "multipass": 3, "hierarchi
 REDUCER_NAMES = {v: k for k, v in REDUCERS.items()}
 SCHEDULES = {"auto": 0, "static": 1, "balanced": 2}
 SCHEDULE_NAMES = {v: k for k, v in SCHEDULES.items()}
-ABI_VERSION = 9
+ABI_VERSION = 10
 STATUS_KV_LEN_CLAMPED = 0x1
 STATUS_PAGE_CLAMPED = 0x2
 

@@ -16,7 +16,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libskvd.so")
-SOURCES = ["api.cpp", "plan.cpp", "kernels.hip", "append.hip", "prefill.hip", "cascade.hip"]
+SOURCES = ["api.cpp", "plan.cpp", "kernels.hip", "partial_128_f16.hip", "partial_128_i8.hip",
+           "partial_128_f8.hip", "partial_256_f16.hip", "partial_256_i8.hip", "partial_256_f8.hip",
+           "append.hip", "prefill.hip", "cascade.hip"]
 ARCH = "gfx950"
 
 

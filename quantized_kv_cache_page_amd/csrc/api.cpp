@@ -297,12 +297,23 @@ skvd_status skvd_gather_debug(const skvd_plan *plan, const skvd_decode_args *arg
     return set_err(SKVD_ERR_NULL, "dense outputs must be non-NULL");
   if (max_len < 0 || max_len > plan->p.prm.max_kv_len)
     return set_err(SKVD_ERR_SHAPE, "max_len=%d outside 0..max_kv_len", max_len);
-  if (((uintptr_t)dense_k | (uintptr_t)dense_v) % 4)
-    return set_err(SKVD_ERR_LAYOUT, "dense_k and dense_v must be 4-byte aligned");
+  // the partial kernel's stores: 16 bytes of f16 / 8 bytes of one-byte K and V rows, 2-byte
+  // scales
+  if (((uintptr_t)dense_k | (uintptr_t)dense_v) % 16 ||
+      (i8 && ((uintptr_t)dense_ks | (uintptr_t)dense_vs) % 2))
+    return set_err(SKVD_ERR_LAYOUT, "dense_k and dense_v must be 16-byte aligned, dense_ks and "
+                   "dense_vs 2-byte aligned");
+  st = check_device(plan->p);
+  if (st != SKVD_OK) return st;
   skvd::LaunchArgs la;
   skvd::fill_launch_args(plan->p, *args, nullptr, &la);
   la.debug = 0;
-  int e = skvd::launch_gather(plan->p, la, max_len, dense_k, dense_v, dense_ks, dense_vs, stream);
+  la.dbg_k = (char *)dense_k;
+  la.dbg_v = (char *)dense_v;
+  la.dbg_ks = (uint16_t *)dense_ks;
+  la.dbg_vs = (uint16_t *)dense_vs;
+  la.dbg_max_len = max_len;
+  int e = skvd::launch_gather(plan->p, la, stream);
   return e ? hip_err(e, "gather kernel launch") : SKVD_OK;
 }
 

@@ -1,23 +1,6 @@
-// HIP kernels for split-KV paged decode attention on gfx950 (CDNA4, wave64).
-//
-// Partial kernel: workgroups of one wave per KV head served (1, 2, 4 or 8), each covering a
-// run of 64-token blocks of one or more (sequence, KV head group) rows (1bit-MONSTER/engine
-// issue #115, "Closing the remaining half of this issue": one producer partial per 64-token
-// block; here a workgroup covers a split of `bps` blocks, or an equal share of the batch's
-// blocks under the balanced schedule). For each chunk of tokens it
-//   1. gathers K and V rows through the page table straight into registers (16-byte loads;
-//      the page id of a 16-token tile is wave-uniform when P >= 16),
-//   2. computes the scores of the G*T query rows against 16-token tiles with the 16x16x32
-//      f16 MFMA (query rows x tokens, contraction over head_dim; int8 K is widened to f16
-//      exactly and multiplied by its per-32 scale in f16, one rounding; fp8 K is widened
-//      exactly to value * 2^-8, its tensor scale and the 2^8 going into the score scale),
-//   3. masks positions past the split, the sequence and (T > 1) the causal limit, and updates
-//      the running max and sum in base 2 (online softmax),
-//   4. accumulates P.V in f32: for one query-row quarter as f16 pair dot products from the V
-//      registers (int8 V: the scale is folded into the probabilities; fp8 V: the tensor scale
-//      is applied to the output), otherwise on the MFMA from an LDS copy of V.
-// It writes one partial (max, sum, f32 output) per query row, or o and lse directly when
-// the plan has a single split.
+// HIP kernels for split-KV paged decode attention on gfx950 (CDNA4, wave64): the merge of the
+// partial kernel's partials (partial.h holds the partial kernel), the launch sequence, and a
+// streaming-read reference kernel.
 //
 // Merge kernels: the log-sum-exp reduction of the partials of one row,
 //   M = max m_s, S = sum_s l_s 2^(m_s - M), o = sum_s 2^(m_s - M) o_s / S,
@@ -25,997 +8,18 @@
 // as direct (serial), cooperative (one lane per partial, <= 64), multipass (lane-strided,
 // any count) and hierarchical (64 partials per workgroup, then a multipass over groups).
 // Loop bounds come from kv_len on the device; the partial stride is the plan's capacity.
-#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
-#include <type_traits>
-
-#include "skvd_internal.h"
+#include "device_common.h"
 
 namespace skvd {
-
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef float float4v __attribute__((ext_vector_type(4)));
-typedef unsigned uint2v __attribute__((ext_vector_type(2)));
-typedef unsigned uint4v __attribute__((ext_vector_type(4)));
-
-constexpr float kNegInf = -__builtin_huge_valf();
-constexpr float kLn2 = 0.6931471805599453f;
-
-// ----------------------------------------------------------------------------- addressing
-// The one address function of the cache: the page holding logical position j of sequence b
-// (clamped into [0, num_pages) so that a bad table entry cannot read out of range), and the
-// element offset of (page, slot, KV head) in a pool.
-__device__ __forceinline__ int64_t lookup_page(const int32_t *table, int64_t table_stride, int b,
-                                               int j, int page_shift, int64_t num_pages,
-                                               bool *clamped) {
-  int64_t pg = table[(int64_t)b * table_stride + (j >> page_shift)];
-  const bool bad = pg < 0 || pg >= num_pages;
-  *clamped = bad;
-  return bad ? (pg < 0 ? 0 : num_pages - 1) : pg;
-}
-
-__device__ __forceinline__ int64_t row_offset(int64_t page, int slot, int kvh, int64_t page_stride,
-                                              int64_t tok_stride, int64_t head_stride) {
-  return page * page_stride + (int64_t)slot * tok_stride + (int64_t)kvh * head_stride;
-}
-
-__device__ __forceinline__ int clamp_len(int L, int max_len, unsigned *status, int debug) {
-  if (L < 0 || L > max_len) {
-    if (debug) atomicOr(status, (unsigned)SKVD_STATUS_KV_LEN_CLAMPED);
-    L = L < 0 ? 0 : max_len;
-  }
-  return L;
-}
-
-// ----------------------------------------------------------------------------- wave helpers
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-
-// max / sum over the 16 lanes of a DPP row (xor 1, xor 2, half-mirror, mirror)
-__device__ __forceinline__ float row16_max(float x) {
-  x = fmaxf(x, dpp<0xB1>(x));
-  x = fmaxf(x, dpp<0x4E>(x));
-  x = fmaxf(x, dpp<0x141>(x));
-  x = fmaxf(x, dpp<0x140>(x));
-  return x;
-}
-__device__ __forceinline__ float row16_sum(float x) {
-  x += dpp<0xB1>(x);
-  x += dpp<0x4E>(x);
-  x += dpp<0x141>(x);
-  x += dpp<0x140>(x);
-  return x;
-}
-__device__ __forceinline__ float wave_max(float x) {
-  x = row16_max(x);
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-  x = row16_sum(x);
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
-}
-__device__ __forceinline__ float readlane_f(float x, int lane) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
-}
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// LDS hand-off between the lanes of a one-wave workgroup: a wavefront-scope fence and wave
-// barrier order the LDS accesses without waiting on outstanding global loads.
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// ----------------------------------------------------------------------------- int8 -> f16
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-
-// K operand (feeds the score MFMA, so compiler-visible code only: the MFMA's operand hazards are
-// tracked for the compiler's own instructions): flip the sign bit of each byte (x + 128 as an
-// unsigned byte u), put u under the f16 exponent of 1024 with a byte permute (the f16 with bits
-// 0x64uu is 1024 + u, exact) and subtract 1152 with one packed f16 add per pair.
-constexpr unsigned kExp1024 = 0x64646464u;  // every byte 0x64: f16 high byte of 1024
-
-__device__ __forceinline__ half2v magic_pair(unsigned flipped, unsigned sel) {
-  return __builtin_bit_cast(half2v, __builtin_amdgcn_perm(kExp1024, flipped, sel)) -
-         (half2v)(_Float16)1152;
-}
-
-// 8 signed bytes (elements 0..7 in byte order) -> 8 f16.
-__device__ __forceinline__ half8 i8x8_to_h8(uint2v w) {
-  half8 r;
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const unsigned x = w[k] ^ 0x80808080u;
-    const half2v lo = magic_pair(x, 0x04010400u), hi = magic_pair(x, 0x04030402u);
-    r[4 * k + 0] = lo[0];
-    r[4 * k + 1] = lo[1];
-    r[4 * k + 2] = hi[0];
-    r[4 * k + 3] = hi[1];
-  }
-  return r;
-}
-
-// V pairs (feed v_dot2, vector ALU only): v_cvt_f16_i16 with SDWA operand selection takes byte
-// k of a dword sign-extended and writes either the low half of the result (clearing the high
-// half) or the high half (keeping the low half) -- a packed f16 pair in two instructions, one
-// per element, with no shifts, permutes or packs.
-template <int B>
-__device__ __forceinline__ unsigned cvt_i8_lo(unsigned src);
-template <int B>
-__device__ __forceinline__ unsigned cvt_i8_hi(unsigned dst, unsigned src);
-#define SKVD_CVT_I8(B)                                                                         \
-  template <>                                                                                  \
-  __device__ __forceinline__ unsigned cvt_i8_lo<B>(unsigned src) {                             \
-    unsigned r;                                                                                \
-    asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_" \
-        #B : "=v"(r) : "v"(src));                                                              \
-    return r;                                                                                  \
-  }                                                                                            \
-  template <>                                                                                  \
-  __device__ __forceinline__ unsigned cvt_i8_hi<B>(unsigned dst, unsigned src) {               \
-    asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE "           \
-        "src0_sel:BYTE_" #B : "+v"(dst) : "v"(src));                                           \
-    return dst;                                                                                \
-  }
-SKVD_CVT_I8(0)
-SKVD_CVT_I8(1)
-SKVD_CVT_I8(2)
-SKVD_CVT_I8(3)
-#undef SKVD_CVT_I8
-
-// Two int8 rows a (token t) and b (token t + 16), 8 elements each -> the 8 f16 pairs
-// (a_i, b_i).
-__device__ __forceinline__ void i8_pairs(uint2v a, uint2v b, half2v *out) {
-#pragma unroll
-  for (int w = 0; w < 2; ++w) {
-    const unsigned x = a[w], y = b[w];
-    out[4 * w + 0] = __builtin_bit_cast(half2v, cvt_i8_hi<0>(cvt_i8_lo<0>(x), y));
-    out[4 * w + 1] = __builtin_bit_cast(half2v, cvt_i8_hi<1>(cvt_i8_lo<1>(x), y));
-    out[4 * w + 2] = __builtin_bit_cast(half2v, cvt_i8_hi<2>(cvt_i8_lo<2>(x), y));
-    out[4 * w + 3] = __builtin_bit_cast(half2v, cvt_i8_hi<3>(cvt_i8_lo<3>(x), y));
-  }
-}
-
-// Two f16 rows a (token t) and b (token t + 16) -> the 8 pairs (a_i, b_i).
-__device__ __forceinline__ void h16_pairs(const half8 &a, const half8 &b, half2v *out) {
-  const uint4v aw = __builtin_bit_cast(uint4v, a), bw = __builtin_bit_cast(uint4v, b);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    out[2 * k] = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(bw[k], aw[k], 0x05040100u));
-    out[2 * k + 1] = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(bw[k], aw[k], 0x07060302u));
-  }
-}
-
-// ----------------------------------------------------------------------------- fp8 (E4M3) -> f16
-// An OCP E4M3 byte s.eeee.mmm rewritten as the f16 bits s.0eeee.mmm0000000 is the f16 of its
-// value times 2^-8, exactly: the 4-bit exponent field under f16's bias 15 instead of E4M3's 7
-// is the factor 2^-8, and E4M3's subnormals (field 0: 2^-6 * m/8) become f16 subnormals
-// (2^-14 * m/8) with the same factor. The 2^8 comes back with the per-tensor scales, folded
-// into the score scale (K) and the output (V). (The NaN byte turns into a finite f16; a cache
-// holds none.) A byte permute puts two bytes into the high bytes of the two f16 halves; the
-// sign bits stay, the other seven bits of each shift down by one.
-__device__ __forceinline__ unsigned f8_place(unsigned s0, unsigned s1, unsigned sel) {
-  const unsigned t = __builtin_amdgcn_perm(s0, s1, sel);
-  return (t & 0x80008000u) | ((t >> 1) & 0x3F803F80u);
-}
-
-// 8 E4M3 bytes (elements 0..7 in byte order) -> 8 f16 (value * 2^-8).
-__device__ __forceinline__ half8 f8x8_to_h8(uint2v w) {
-  uint4v r;
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    r[2 * k] = f8_place(w[k], w[k], 0x010C000Cu);      // bytes 0, 1 -> halves 0, 1
-    r[2 * k + 1] = f8_place(w[k], w[k], 0x030C020Cu);  // bytes 2, 3 -> halves 0, 1
-  }
-  return __builtin_bit_cast(half8, r);
-}
-
-// Two E4M3 rows a (token t) and b (token t + 16), 8 elements each -> the 8 f16 pairs
-// (a_i, b_i) (values * 2^-8): byte i of a into the low half, byte i of b into the high half.
-__device__ __forceinline__ void f8_pairs(uint2v a, uint2v b, half2v *out) {
-#pragma unroll
-  for (int w = 0; w < 2; ++w) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      out[4 * w + i] = __builtin_bit_cast(
-          half2v, f8_place(b[w], a[w], ((4u + i) << 24) | 0x0C0000u | ((unsigned)i << 8) | 0x0Cu));
-  }
-}
-
-// ----------------------------------------------------------------------------- balanced schedule
-// The batch's 64-token blocks in (sequence, KV head, block) order, cut into n_shares equal
-// contiguous shares: share w covers [w N / W, (w + 1) N / W). One sequence per lane (the plan
-// limits the batch to 64); every lane of the wave must be active. Per lane: the sequence's
-// clamped length, its block count and the blocks of all earlier sequences.
-struct Shares {
-  int len_l;
-  unsigned nb_l, pre_l;
-  int64_t n_blocks;  // N = (Hkv / heads per workgroup) * sum of block counts
-  int n_shares;      // W = min(grid, N / piece_min), at least 1 when N > 0
-};
-
-__device__ __forceinline__ Shares balanced_shares(const LaunchArgs &a, int debug) {
-  const int lane = threadIdx.x & 63;
-  Shares sh;
-  sh.len_l = lane < a.batch ? clamp_len(a.kv_len[lane], a.max_kv_len, a.status, debug) : 0;
-  sh.nb_l = (unsigned)(sh.len_l + 63) >> 6;
-  unsigned inc = sh.nb_l;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const unsigned up = __shfl_up(inc, d);
-    if (lane >= d) inc += up;
-  }
-  sh.pre_l = inc - sh.nb_l;
-  // (readlane: the total is wave-uniform, so it and everything derived from it stay scalar)
-  sh.n_blocks = (int64_t)(unsigned)__builtin_amdgcn_readlane((int)inc, 63) *
-                (a.Hkv / a.heads_per_wg);
-  sh.n_shares = sh.n_blocks == 0
-                    ? 0
-                    : (int)max((int64_t)1, min((int64_t)a.grid_wgs, sh.n_blocks / a.piece_min));
-  return sh;
-}
-
-// The share holding global block x (0 <= x < N): the largest w with floor(w N / W) <= x.
-__device__ __forceinline__ int share_of(int64_t x, int64_t n_blocks, int n_shares) {
-  return (int)(((x + 1) * n_shares - 1) / n_blocks);
-}
-
-// ----------------------------------------------------------------------------- partial kernel
-// K and V rows are read once: non-temporal loads (evict-first in L2, no Infinity Cache
-// allocation) when each load instruction covers whole 128-byte lines between the lanes that
-// share them (f16 K: half lines, consumed by the next instruction; f16 and int8 V: whole
-// lines). int8 K instructions cover a quarter of each line, whose other quarters are read by
-// the next three instructions: cached loads (measured: evict-first loses them).
-template <bool STREAM, class T>
-__device__ __forceinline__ T kv_load(const char *p) {
-  if constexpr (STREAM) return __builtin_nontemporal_load((const T *)p);
-  else return *(const T *)p;
-}
-
-// ----------------------------------------------------------------------------- partial kernel (body)
-typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-typedef short short4v __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) short4v *lds_s4_ptr;
-
-// Byte offset of 16-byte chunk c of row r in a row-major LDS tile with rows of RB bytes: the
-// chunk index is XOR-swizzled by the row so that the transposed reads of 16 consecutive rows
-// at one column fall in different banks.
-template <int ROWB>
-__device__ __forceinline__ int swz(int r, int c) {
-  return r * ROWB + ((c ^ (r & 15)) << 4);
-}
-
-// D: head_dim (128/256). RB: 4-row quarters of the 16 MFMA rows in use (rows = G*T <= 4*RB).
-// KV: cache format, 0 f16, 1 int8 with f16 scales per 32 elements, 2 fp8 E4M3 with one f32
-// scale per tensor; the two one-byte formats share the load layout (I8 below), and only int8
-// reads per-row scales (SC). FAST: page_size >= 16, so each 16-token
-// tile lies in one page and its page id is wave-uniform. CH: tokens per chunk (16, 32 or
-// 64): the K and V registers of a chunk bound how many waves fit on a SIMD.
-// PVM: P.V on the MFMA through an LDS copy of the chunk's V (dense when several query rows
-// share the KV head); otherwise P.V on the vector ALU as f16 pair dot products
-// (v_dot2_f32_f16) from the V registers, pairing token t with token t + 16.
-// Minimum waves per SIMD the register allocator must leave room for. int8 at D=128 is vector-
-// ALU heavy and runs several waves per SIMD (the plan launches 8 workgroups per CU): three,
-// at the cost of three values spilled and reloaded once per segment. f16 single-quarter
-// variants run one wave per SIMD under the balanced schedule and gain more from registers
-// spent on instruction-level parallelism than from occupancy: no floor.
-template <int D, int RB, bool I8>
-constexpr int partial_waves() {
-  return D == 128 ? (RB == 1 ? (I8 ? 3 : 1) : 2) : 1;
-}
-
-template <int D, int RB, int KV, bool FAST, int CH, bool PVM, int HW>
-__global__ __launch_bounds__(64 * HW)
-__attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void partial_kernel(LaunchArgs a) {
-  constexpr bool I8 = KV != 0;  // one-byte elements
-  constexpr bool SC = KV == 1;  // int8: f16 scales per 32 elements of each row
-  constexpr bool F8 = KV == 2;  // fp8 E4M3: one f32 scale per tensor
-  static_assert(CH == 16 || CH == 32 || (CH == 64 && !PVM), "chunk");
-  static_assert(PVM || CH % 32 == 0, "the vector P.V pairs 16-token tiles 2h and 2h + 1");
-  constexpr int NT = CH / 16;    // 16-token score tiles per chunk
-  constexpr int KS = D / 32;     // score MFMA steps of 32 head_dim elements
-  constexpr int LPR = D / 8;     // lanes per V row in the load layout, 8 elements each
-  constexpr int TPS = 64 / LPR;  // V rows per load step
-  constexpr int NS = CH / TPS;   // V load steps per chunk
-  constexpr int NDT = D / 16;    // 16-wide head_dim tiles of the P.V MFMA
-  constexpr int KPL = CH / 4;    // P.V contraction elements per lane (8: 16x16x32, 4: 16x16x16)
-  constexpr int RM = 4 * RB;     // query rows held (padded)
-  constexpr int PSTR = CH + 4;   // row stride of the probability tile, floats
-  constexpr int ROWB = 2 * D;    // bytes per V row in LDS (f16)
-  using Vec = std::conditional_t<I8, uint2v, half8>;  // one lane's 8 elements of a row
-  using PvOp = std::conditional_t<CH == 32, half8, half4>;
-
-  // LDS, one slice per wave (each wave serves its own KV head):
-  constexpr int VL = PVM ? CH * ROWB : 16;          // chunk V rows, f16
-  constexpr int PL = PVM ? RM * PSTR : 4;           // probabilities [row][token]
-  // int8 at D=128 (32-token chunks): a chunk's K and V scales come in one 8-byte load per lane
-  // (lanes 0..31: the K scales of chunk token lane; 32..63: the V scales of token lane - 32),
-  // issued with the chunk's K rows and handed over through LDS, instead of a two-byte load per
-  // token tile for K and an 8-byte load for V (one vector-memory instruction per chunk instead
-  // of three).
-  constexpr bool SCL = SC && D == 128 && CH == 32;
-  constexpr int SL = SCL ? 64 : SC ? CH * (D / 128) : 1;  // int8 scales [token][group], f16
-  constexpr int QL = PVM ? 4 : (CH / 2) * RM;       // vector P.V: f16 pairs (tp, tp+16) [tp][row]
-  __shared__ __attribute__((aligned(16))) char v_lds_all[HW * VL];
-  __shared__ __attribute__((aligned(16))) float p_lds_all[HW * PL];
-  __shared__ __attribute__((aligned(16))) uint2v vsc_lds_all[HW * SL];
-  __shared__ __attribute__((aligned(16))) unsigned p2_lds_all[HW * QL];
-  // (readfirstlane: the wave index is uniform in the wave, and saying so keeps the KV head and
-  // every row base derived from it in SGPRs, so loads take a scalar base + 32-bit lane offset)
-  const int wave = HW > 1 ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) : 0;
-  char *const v_lds = v_lds_all + wave * VL;
-  float *const p_lds = p_lds_all + wave * PL;
-  uint2v *const vsc_lds = vsc_lds_all + wave * SL;
-  const _Float16 *vsh = (const _Float16 *)(vsc_lds + (SCL ? CH : 0));  // V scales
-  const _Float16 *ksl = (const _Float16 *)vsc_lds;                        // K scales (SCL)
-  unsigned *const p2_lds = p2_lds_all + wave * QL;
-
-  const int lane = threadIdx.x & 63;
-  const int Hkv = a.Hkv;
-  const int Hg = Hkv / HW;  // head groups: the rows of the schedule
-  // fp8: the per-tensor scales (one f32 each in device memory) times the widening's 2^8, on
-  // the scores' scale (K) and on the output (V); 1 for the other formats
-  const float scale_log2 = F8 ? a.scale_log2 * (*(const float *)a.ks * 256.f) : a.scale_log2;
-  const float vfac = F8 ? *(const float *)a.vs * 256.f : 1.f;
-  const int T = a.T, G = a.G, R = G * T;
-  const int P1 = (1 << a.page_shift) - 1;
-
-  // ---- this workgroup's segments: (sequence, KV head group, block range, partial slot); wave
-  // w of the workgroup serves KV head HW * group + w over the same block range
-  // Static: workgroup order split fastest, then KV head, then sequence, with an odd split
-  // stride. Consecutive workgroups go to the eight XCDs in turn; with an even stride split s
-  // of every (head, sequence) would land on the same XCD, and the live splits of a ragged
-  // batch would pile onto the XCDs of the low split indices. The odd stride rotates each
-  // row's start over all eight. Indices past splits_cap are padding. One segment.
-  // Balanced: the batch's blocks in (sequence, KV head, block) order are cut into W equal
-  // contiguous shares; workgroup w takes share w, which may cover the end of one row and the
-  // start of the next ones: one segment per row, its partial in slot w - (first share of the
-  // row). Sequence lengths, one per lane, come from kv_len on the device.
-  int st_b = 0, st_grp = 0, st_split = 0;
-  Shares sh{};
-  int64_t x_cur = 0, x_end = 0;  // balanced: this workgroup's share
-  // Progress priority (int8, whose waves share SIMDs): waves of a SIMD are served oldest
-  // first, so a co-resident workgroup started later falls behind and finishes alone, with fewer
-  // loads in flight. Each wave instead sets its issue priority from the fraction of its work
-  // done (3 in the first quarter down to 0 in the last), so the waves of a SIMD advance
-  // together. Blocks done so far: done_base (earlier segments) + the segment's own; quarters
-  // at pq1, pq2, pq3.
-  int done_base = 0, pq1 = 0, pq2 = 0, pq3 = 0;
-  const int share = blockIdx.x;
-  if (a.balanced) {
-    sh = balanced_shares(a, a.debug);
-    if (share >= sh.n_shares) return;
-    x_cur = share * sh.n_blocks / sh.n_shares;
-    x_end = (share + 1) * sh.n_blocks / sh.n_shares;
-    const int total = (int)(x_end - x_cur);
-    pq1 = total / 4;
-    pq2 = total / 2;
-    pq3 = 3 * total / 4;
-  } else {
-    const int wg = blockIdx.x;
-    st_split = wg % a.split_stride;
-    const int head_seq = wg / a.split_stride;
-    st_grp = head_seq % Hg;
-    st_b = head_seq / Hg;
-    if (st_split >= a.splits_cap) return;
-  }
-  bool pending = true;
-  for (;;) {
-  int b, grp, slot, L, blk_lo, blk_hi;
-  if (a.balanced) {
-    if (x_cur >= x_end) break;
-    // the sequence holding global block x_cur: Hg*pre <= x_cur < Hg*(pre + nb), that is
-    // pre <= x_cur / Hg < pre + nb (one scalar division, 32-bit lane compares)
-    const unsigned xq = (unsigned)(x_cur / Hg);
-    const bool mine = sh.pre_l <= xq && xq < sh.pre_l + sh.nb_l;
-    b = __builtin_ctzll(__ballot(mine));
-    const unsigned pre_b = (unsigned)__builtin_amdgcn_readlane((int)sh.pre_l, b);
-    const int nb_b = __builtin_amdgcn_readlane((int)sh.nb_l, b);
-    L = __builtin_amdgcn_readlane(sh.len_l, b);
-    const int64_t off = x_cur - (int64_t)Hg * pre_b;
-    grp = (int)(off / nb_b);
-    blk_lo = (int)(off - (int64_t)grp * nb_b);
-    const int64_t row0 = (int64_t)Hg * pre_b + (int64_t)grp * nb_b;  // the row's first block
-    const int64_t seg_end = min(x_end, row0 + nb_b);
-    blk_hi = blk_lo + (int)(seg_end - x_cur);
-    // compact slot of (schedule row b*Hg + grp, share): unique, below rows + shares
-    slot = b * Hg + grp + share;
-    x_cur = seg_end;
-  } else {
-    if (!pending) break;
-    pending = false;
-    b = st_b;
-    grp = st_grp;
-    slot = st_split;
-    L = clamp_len(a.kv_len[b], a.max_kv_len, a.status, a.debug);
-    const int nblk = (L + 63) >> 6;
-    blk_lo = st_split * a.bps;
-    if (!a.single && blk_lo >= nblk) break;  // beyond this sequence: no partial is read
-    blk_hi = min(blk_lo + a.bps, nblk);
-    const int total = blk_hi - blk_lo;
-    pq1 = total / 4;
-    pq2 = total / 2;
-    pq3 = 3 * total / 4;
-  }
-  const int kvh = HW * grp + wave;
-  const int tok0 = blk_lo * 64;
-  const int tok_end = min(blk_hi * 64, L);
-
-  const char *kbase = (const char *)a.k;
-  const char *vbase = (const char *)a.v;
-  constexpr int ES = I8 ? 1 : 2;  // element bytes
-  const _Float16 *ksc = (const _Float16 *)a.ks;
-  const _Float16 *vsc = (const _Float16 *)a.vs;
-
-  // Query rows as the score MFMA A operand: lane holds row (lane & 15), elements
-  // 8*(lane>>4)..+7 of each 32-element contraction step.
-  const int g4 = lane >> 4, c16 = lane & 15;
-  // head_dim element of step k's first lane element (the contraction order is free as long as
-  // q and K agree): f16, 32k + 8*g4; int8, group g4 + 4*(k/4) at offset 8*(k%4), so that each
-  // lane's elements of a group are 32 contiguous bytes under one scale
-  auto kelem = [&](int k) __attribute__((always_inline)) {
-    return I8 ? 32 * (g4 + 4 * (k >> 2)) + 8 * (k & 3) : 32 * k + 8 * g4;
-  };
-  half8 qa[KS];
-  {
-    const int r = c16;
-    if (r < R) {
-      const int t = r / G, hg = r - (r / G) * G;
-      const _Float16 *qp = (const _Float16 *)a.q + ((int64_t)b * T + t) * a.q_tok_stride +
-                           (int64_t)(kvh * G + hg) * a.q_head_stride + 8 * g4;
-#pragma unroll
-      for (int k = 0; k < KS; ++k) qa[k] = *(const half8 *)(qp + kelem(k) - 8 * g4);
-    } else {
-#pragma unroll
-      for (int k = 0; k < KS; ++k) qa[k] = (half8)(_Float16)0;
-    }
-  }
-  // This lane's MFMA output rows: 4*g4 + e. Row r sees positions j < L - T + t + 1.
-  int nvis[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int r = 4 * g4 + e;
-    const int n = r < R ? L - T + r / G + 1 : 0;
-    nvis[e] = min(n, tok_end);
-  }
-
-  float m[4], lsum[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) { m[e] = kNegInf; lsum[e] = 0.f; }
-  // MFMA P.V output: lane holds head_dim column 16*dt + c16 of rows 4*g4 + e.
-  float4v acc[PVM ? NDT : 1];
-#pragma unroll
-  for (int dt = 0; dt < (PVM ? NDT : 1); ++dt) acc[dt] = (float4v)0.f;
-  // Vector P.V output: lane holds elements vlane_el .. +7 of every row, summed over the
-  // tokens of its load slot (reduced across slots at the end).
-  float accv[PVM ? 1 : RM][8];
-#pragma unroll
-  for (int r = 0; r < (PVM ? 1 : RM); ++r)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) accv[r][i] = 0.f;
-
-  bool clamped_any = false;
-  const int vlane_tok = lane / LPR, vlane_el = 8 * (lane % LPR);
-
-  // Loads are branch-free: a token past the split is clamped to the split's last token
-  // (a re-read of lines already fetched, masked out of the softmax), so every load of a chunk
-  // is issued unconditionally and the in-order load counter can be waited on precisely.
-  // FAST: the page of each 16-token tile is wave-uniform; a chunk's page ids are read from the
-  // table through the constant address space (scalar loads, counted apart from the vector
-  // loads) one chunk ahead of their use.
-  const int last_tile = (tok_end - 1) & ~15;
-  typedef const __attribute__((address_space(4))) int32_t *ctable_t;
-  const ctable_t trow = (ctable_t)(a.table + (int64_t)b * a.table_stride);
-  auto chunk_pages = [&](int c0, int *pg) __attribute__((always_inline)) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t) pg[t] = trow[min(c0 + 16 * t, last_tile) >> a.page_shift];
-  };
-  auto clamp_page = [&](int pg, int64_t npages) __attribute__((always_inline)) -> int64_t {
-    const bool bad = pg < 0 || pg >= npages;
-    clamped_any |= bad;
-    return bad ? (pg < 0 ? 0 : npages - 1) : (int64_t)pg;
-  };
-
-  // Per-lane token offsets within a 16-token tile, hoisted: with a non-negative stride,
-  // min(token, limit) * stride = min(token * stride, limit * stride), the limit being scalar.
-  const unsigned c16_tok = (unsigned)(c16 * (int)a.tok_stride);
-  const unsigned c16_stok = I8 ? (unsigned)(c16 * (int)a.s_tok_stride) : 0u;
-  const unsigned vt_tok = (unsigned)(vlane_tok * (int)a.tok_stride);
-
-  Vec kb[NT][I8 ? 1 : KS];                   // f16 K: step k's 8 elements
-  uint4v kq[NT][I8 ? KS / 4 : 1][2];         // int8 K: the lane's 32 bytes of group g4 + 4m
-  _Float16 ksh[NT][I8 ? KS / 4 : 1];         // int8 K: the token's scale of group g4 + 4m
-  Vec vb[NS];
-  // int8 V scales: the D/32 scales of chunk token (lane % CH), one 8-byte load per lane (a
-  // token-head's scales are contiguous), handed to the P.V lanes through LDS.
-  uint2v vsr[D / 128];
-  uint2v scr;  // SCL: this lane's K (lane < 32) or V scales of one chunk token
-
-  // K rows of chunk c0 in the score MFMA B-operand layout: tile t, lane (g4, c16) holds
-  // elements 32k + 8*g4 .. +7 of token 16t + c16.
-  auto load_k = [&](int c0, const int *pgs) __attribute__((always_inline)) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int jt = c0 + 16 * t;
-      if constexpr (FAST) {
-        // wave-uniform base of the (clamped) tile on the scalar unit + 32-bit lane offset
-        const int jte = min(jt, last_tile);
-        const int64_t pg = clamp_page(pgs[t], a.num_k_pages);
-        const char *base = kbase + row_offset(pg, jte & P1, kvh, a.page_stride, a.tok_stride,
-                                              a.head_stride) * ES;
-        const int lim = min(tok_end - 1 - jte, 15);  // last valid token of the tile
-        if constexpr (I8) {
-          const unsigned off = min(c16_tok, (unsigned)(lim * (int)a.tok_stride)) + 32 * g4;
-#pragma unroll
-          for (int m = 0; m < KS / 4; ++m)
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-              kq[t][m][h] = kv_load<true, uint4v>(base + off + 128 * m + 16 * h);
-          if constexpr (SC && !SCL) {
-            const _Float16 *sb = ksc + row_offset(pg, jte & P1, kvh, a.s_page_stride,
-                                                  a.s_tok_stride, a.s_head_stride);
-            const unsigned so = 2u * (min(c16_stok, (unsigned)(lim * (int)a.s_tok_stride)) + g4);
-#pragma unroll
-            for (int m = 0; m < KS / 4; ++m)
-              ksh[t][m] = *(const _Float16 *)((const char *)sb + so + 8 * m);
-          }
-        } else {
-          const unsigned off = (min(c16_tok, (unsigned)(lim * (int)a.tok_stride)) + 8 * g4) * ES;
-#pragma unroll
-          for (int k = 0; k < KS; ++k) kb[t][k] = kv_load<true, Vec>(base + off + 32 * k * ES);
-        }
-      } else {
-        const int j = min(jt + c16, tok_end - 1);
-        bool cl;
-        const int64_t pg = lookup_page(a.table, a.table_stride, b, j, a.page_shift,
-                                       a.num_k_pages, &cl);
-        clamped_any |= cl;
-        const int64_t off = row_offset(pg, j & P1, kvh, a.page_stride, a.tok_stride,
-                                       a.head_stride);
-        if constexpr (I8) {
-          const char *kp = kbase + off + 32 * g4;
-#pragma unroll
-          for (int m = 0; m < KS / 4; ++m)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) kq[t][m][h] = kv_load<true, uint4v>(kp + 128 * m + 16 * h);
-          if constexpr (SC && !SCL) {
-            const int64_t so = row_offset(pg, j & P1, kvh, a.s_page_stride, a.s_tok_stride,
-                                          a.s_head_stride) + g4;
-#pragma unroll
-            for (int m = 0; m < KS / 4; ++m) ksh[t][m] = ksc[so + 4 * m];
-          }
-        } else {
-          const char *kp = kbase + (off + 8 * g4) * ES;
-#pragma unroll
-          for (int k = 0; k < KS; ++k) kb[t][k] = kv_load<true, Vec>(kp + 32 * k * ES);
-        }
-      }
-    }
-    if constexpr (SCL) {
-      // K scales (lanes 0..31) or V scales (32..63) of chunk token lane % 32; a token past the
-      // split reads the last one's
-      const bool isk = lane < CH;
-      const int jl = min(c0 + (lane & (CH - 1)), tok_end - 1);
-      const int64_t np = isk ? a.num_k_pages : a.num_v_pages;
-      int64_t pg;
-      if constexpr (FAST) {
-        const int tl = (jl - c0) >> 4;  // the token's 16-token tile (its page is wave-uniform)
-        int pgl = pgs[0];
-#pragma unroll
-        for (int t = 1; t < NT; ++t) pgl = tl == t ? pgs[t] : pgl;
-        pg = clamp_page(pgl, np);
-      } else {
-        bool cl;
-        pg = lookup_page(a.table, a.table_stride, b, jl, a.page_shift, np, &cl);
-        clamped_any |= cl;
-      }
-      const _Float16 *sp = (isk ? ksc : vsc) + row_offset(pg, jl & P1, kvh, a.s_page_stride,
-                                                          a.s_tok_stride, a.s_head_stride);
-      scr = *(const uint2v *)sp;
-    }
-  };
-  // V rows of chunk c0 in the load layout: step s, lane holds elements vlane_el .. +7 of
-  // token TPS*s + vlane_tok.
-  auto load_v = [&](int c0, const int *pgs) __attribute__((always_inline)) {
-#pragma unroll
-    for (int s2 = 0; s2 < NS; ++s2) {
-      const int js = c0 + TPS * s2;
-      if constexpr (FAST) {
-        const int jte = min(js & ~15, last_tile);
-        const int64_t pg = clamp_page(pgs[(TPS * s2) >> 4], a.num_v_pages);
-        const char *base = vbase + row_offset(pg, jte & P1, kvh, a.page_stride, a.tok_stride,
-                                              a.head_stride) * ES;
-        // token (js & 15) + vlane_tok of the tile, clamped to its last valid token
-        const int ts = (int)a.tok_stride;
-        const unsigned tko = min(vt_tok + (unsigned)((js & 15) * ts),
-                                 (unsigned)(min(tok_end - 1 - jte, 15) * ts));
-        const unsigned off = (tko + vlane_el) * ES;
-        vb[s2] = kv_load<true, Vec>(base + off);
-      } else {
-        const int j = min(js + vlane_tok, tok_end - 1);
-        bool cl;
-        const int64_t pg = lookup_page(a.table, a.table_stride, b, j, a.page_shift,
-                                       a.num_v_pages, &cl);
-        clamped_any |= cl;
-        const int64_t off = row_offset(pg, j & P1, kvh, a.page_stride, a.tok_stride,
-                                       a.head_stride);
-        vb[s2] = kv_load<true, Vec>(vbase + (off + vlane_el) * ES);
-      }
-    }
-    if constexpr (SC && !SCL) {
-      // scales of chunk token (lane % CH); a token past the split reads the last one's
-      const int jl = min(c0 + lane % CH, tok_end - 1);
-      int64_t pg;
-      if constexpr (FAST) {
-        const int tl = (jl - c0) >> 4;  // the lane's 16-token tile (its page is wave-uniform)
-        int pgl = pgs[0];
-#pragma unroll
-        for (int t = 1; t < NT; ++t) pgl = tl == t ? pgs[t] : pgl;
-        pg = clamp_page(pgl, a.num_v_pages);
-      } else {
-        bool cl;
-        pg = lookup_page(a.table, a.table_stride, b, jl, a.page_shift, a.num_v_pages, &cl);
-        clamped_any |= cl;
-      }
-      const _Float16 *sp = vsc + row_offset(pg, jl & P1, kvh, a.s_page_stride, a.s_tok_stride,
-                                            a.s_head_stride);
-#pragma unroll
-      for (int k4 = 0; k4 < D / 128; ++k4) vsr[k4] = *(const uint2v *)(sp + 4 * k4);
-    }
-  };
-
-  int pg_cur[NT], pg_next[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) pg_cur[t] = pg_next[t] = 0;
-  if (tok0 < tok_end) {
-    if constexpr (FAST) chunk_pages(tok0, pg_cur);
-    load_k(tok0, pg_cur);
-    __builtin_amdgcn_sched_barrier(0);
-    load_v(tok0, pg_cur);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-
-  // One chunk: scores of the chunk's K (loaded one step ahead), prefetch of the next K,
-  // softmax, P.V with the chunk's V, prefetch of the next V. The first call is peeled off the
-  // loop so that the loop is entered with the same load order as its back edge (K before V):
-  // the in-order load counter is then waited on for K alone at the loop top.
-  auto chunk = [&](int c0) __attribute__((always_inline)) {
-    const int c1 = c0 + CH;
-    if constexpr (SCL) {  // this chunk's K and V scales to LDS (the previous chunk's reads of
-      vsc_lds[lane] = scr;  // them ended at its closing wave_sync)
-      wave_sync();
-    }
-    if constexpr (FAST) chunk_pages(c1, pg_next);
-    // ---- scores: S[t] = rows x 16 tokens of tile t (lane: token c16, rows 4*g4 + e)
-    // The MFMA chains run for every tile, also the ones past the split (their K is a clamped
-    // re-read and their scores are masked): a branch between an MFMA and the reads of its
-    // result let the compiler's wait-state insertion miss the taken path.
-    float4v S[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      S[t] = (float4v)0.f;
-      if constexpr (I8) {
-        // int8: step k's 8 elements are bytes 8(k%4) .. +7 of the lane's 32-byte group slice,
-        // widened exactly and scaled in f16 (one rounding of int8 * scale)
-#pragma unroll
-        for (int k = 0; k < KS; ++k) {
-          const uint4v &q4 = kq[t][k >> 2][(k & 3) >> 1];
-          const unsigned w0 = q4[2 * (k & 1)], w1 = q4[2 * (k & 1) + 1];
-          half8 kh;
-          if constexpr (SCL)
-            kh = i8x8_to_h8(uint2v{w0, w1}) *
-                 (half8)ksl[(16 * t + c16) * (D / 32) + g4 + 4 * (k >> 2)];
-          else if constexpr (SC) kh = i8x8_to_h8(uint2v{w0, w1}) * (half8)ksh[t][k >> 2];
-          else kh = f8x8_to_h8(uint2v{w0, w1});  // fp8: k_scale * 2^8 is in the score scale
-          S[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[k], kh, S[t], 0, 0, 0);
-        }
-      } else {
-#pragma unroll
-        for (int k = 0; k < KS; ++k)
-          S[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[k], kb[t][k], S[t], 0, 0, 0);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // ---- prefetch the next chunk's K while this chunk's softmax and P.V run (past the end
-    // of the split this re-reads the last token: cached, and never used)
-    load_k(c1, pg_next);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // ---- mask, online softmax (base 2)
-    float alpha[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float cmax = kNegInf;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int j = c0 + 16 * t + c16;
-        const float sc = j < nvis[e] ? S[t][e] * scale_log2 : kNegInf;
-        S[t][e] = sc;
-        cmax = fmaxf(cmax, sc);
-      }
-      cmax = row16_max(cmax);
-      const float mnew = fmaxf(m[e], cmax);
-      const bool dead = mnew == kNegInf;
-      alpha[e] = dead ? 1.f : fast_exp2(m[e] - mnew);
-      float ps = 0.f;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const float p = dead ? 0.f : fast_exp2(S[t][e] - mnew);
-        S[t][e] = p;
-        ps += p;
-      }
-      lsum[e] = lsum[e] * alpha[e] + ps;
-      m[e] = mnew;
-    }
-
-    if constexpr (PVM) {
-      // ---- probabilities to LDS as [row][token]; the chunk's V rows to LDS (int8 widened
-      // exactly to f16; int8 V scales to vsc_lds)
-      if (g4 < RB) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) p_lds[(4 * g4 + e) * PSTR + 16 * t + c16] = S[t][e];
-      }
-#pragma unroll
-      for (int s2 = 0; s2 < NS; ++s2) {
-        const int row = TPS * s2 + vlane_tok;
-        half8 h;
-        if constexpr (SC) {
-          h = i8x8_to_h8(vb[s2]);
-        } else if constexpr (F8) {
-          h = f8x8_to_h8(vb[s2]);
-        } else {
-          h = vb[s2];
-        }
-        *(half8 *)(v_lds + swz<ROWB>(row, lane % LPR)) = h;
-      }
-      if constexpr (SC && !SCL) {
-        if (lane < CH) {
-#pragma unroll
-          for (int k4 = 0; k4 < D / 128; ++k4) vsc_lds[lane * (D / 128) + k4] = vsr[k4];
-        }
-      }
-      wave_sync();
-
-      // ---- P.V on the MFMA: A = probabilities (row c16, tokens KPL*g4 ..), B = V^T tiles
-      // read transposed from LDS (column 16*dt + c16, the same tokens)
-      bool rescale = false;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) rescale |= alpha[e] != 1.f;
-      if (__builtin_amdgcn_read_exec() && rescale) {
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[dt][e] *= alpha[e];
-      }
-      float pv[KPL];
-#pragma unroll
-      for (int i = 0; i < KPL; ++i) pv[i] = c16 < RM ? p_lds[c16 * PSTR + KPL * g4 + i] : 0.f;
-      PvOp pa[SC ? D / 32 : 1];
-      if constexpr (SC) {
-#pragma unroll
-        for (int gg = 0; gg < D / 32; ++gg)
-#pragma unroll
-          for (int i = 0; i < KPL; ++i)
-            pa[gg][i] = (_Float16)(pv[i] * (float)vsh[(KPL * g4 + i) * (D / 32) + gg]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < KPL; ++i) pa[0][i] = (_Float16)pv[i];
-      }
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        // lane (g4, c16) of read h receives column 16*dt + c16 of tokens KPL*g4 + 4h + 0..3
-        PvOp vt;
-#pragma unroll
-        for (int h = 0; h < KPL / 4; ++h) {
-          const int row = KPL * g4 + 4 * h + (c16 >> 2);
-          const int col = 16 * dt + 4 * (c16 & 3);
-          const short4v r4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s4_ptr)(v_lds + swz<ROWB>(row, col >> 3) + ((col & 7) << 1)));
-          const half4 hv = __builtin_bit_cast(half4, r4);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) vt[4 * h + i] = hv[i];
-        }
-        const PvOp &pop = pa[SC ? dt / 2 : 0];
-        if constexpr (CH == 32)
-          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pop, vt, acc[dt], 0, 0, 0);
-        else
-          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(pop, vt, acc[dt], 0, 0, 0);
-      }
-    } else {
-      // ---- probabilities to LDS as f16 pairs (token 32h + c16, token 32h + 16 + c16) per row
-      if (g4 < RB) {
-#pragma unroll
-        for (int h = 0; h < NT / 2; ++h) {
-          uint4v w;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            w[e] = __builtin_bit_cast(unsigned,
-                                      half2v{(_Float16)S[2 * h][e], (_Float16)S[2 * h + 1][e]});
-          *(uint4v *)&p2_lds[(16 * h + c16) * RM + 4 * g4] = w;
-        }
-      }
-      // per-row rescale factors (row-uniform within the 16 lanes of a DPP row)
-      float al[RM];
-#pragma unroll
-      for (int r = 0; r < RM; ++r) al[r] = readlane_f(alpha[r & 3], 16 * (r >> 2));
-      if constexpr (SC && !SCL) {
-        if (lane < CH) {
-#pragma unroll
-          for (int k4 = 0; k4 < D / 128; ++k4) vsc_lds[lane * (D / 128) + k4] = vsr[k4];
-        }
-      }
-      wave_sync();
-      bool rescale = false;
-#pragma unroll
-      for (int r = 0; r < RM; ++r) rescale |= al[r] != 1.f;
-      if (rescale) {
-#pragma unroll
-        for (int r = 0; r < RM; ++r)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) accv[r][i] *= al[r];
-      }
-      // ---- P.V: in the 32 tokens from 32h, load steps s and s + SPT hold tokens tp and
-      // tp + 16 of the lane's slot (SPT load steps per 16-token tile)
-      constexpr int SPT = 16 / TPS;
-#pragma unroll
-      for (int ps = 0; ps < NS / 2; ++ps) {
-        const int h = ps / SPT, s2 = 2 * SPT * h + ps % SPT, s3 = s2 + SPT;
-        const int tp = 16 * h + TPS * (ps % SPT) + vlane_tok;
-        half2v pp[RM];
-#pragma unroll
-        for (int q = 0; q < RB; ++q) {
-          const uint4v w = *(const uint4v *)&p2_lds[tp * RM + 4 * q];
-          // (bit_cast of a vector element would cast element 0: copy the element out first)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const unsigned we = w[e];
-            pp[4 * q + e] = __builtin_bit_cast(half2v, we);
-          }
-        }
-        half2v vp[8];
-        if constexpr (F8) {
-          f8_pairs(vb[s2], vb[s3], vp);  // fp8: v_scale * 2^8 is applied to the output
-        } else if constexpr (SC) {
-          // int8 V: the pair's per-32 scales fold into the probabilities
-          const int ta = TPS * s2 + vlane_tok, g = vlane_el / 32;
-          const half2v sc = {vsh[ta * (D / 32) + g], vsh[(ta + 16) * (D / 32) + g]};
-#pragma unroll
-          for (int r = 0; r < RM; ++r) pp[r] *= sc;
-          i8_pairs(vb[s2], vb[s3], vp);
-        } else {
-          h16_pairs(vb[s2], vb[s3], vp);
-        }
-#pragma unroll
-        for (int r = 0; r < RM; ++r)
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            accv[r][i] = __builtin_amdgcn_fdot2(pp[r], vp[i], accv[r][i], false);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // ---- prefetch the next chunk's V while the next chunk's scores run
-    load_v(c1, pg_next);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) pg_cur[t] = pg_next[t];
-    wave_sync();
-  };
-  auto set_priority = [&](int c0) __attribute__((always_inline)) {
-    if constexpr (!I8) return;  // f16 runs one wave per SIMD: nothing to arbitrate
-    const int done = done_base + ((c0 - tok0) >> 6);
-    if (done < pq1) __builtin_amdgcn_s_setprio(3);
-    else if (done < pq2) __builtin_amdgcn_s_setprio(2);
-    else if (done < pq3) __builtin_amdgcn_s_setprio(1);
-    else __builtin_amdgcn_s_setprio(0);
-  };
-  if (tok0 < tok_end) {
-    set_priority(tok0);
-    chunk(tok0);
-    for (int c0 = tok0 + CH; c0 < tok_end; c0 += CH) {
-      set_priority(c0);
-      chunk(c0);
-    }
-  }
-  done_base += blk_hi - blk_lo;
-  if (a.debug && clamped_any) atomicOr(a.status, (unsigned)SKVD_STATUS_PAGE_CLAMPED);
-
-  // ---- per-row sum over the tokens of the lane's DPP row; max is already row-uniform
-#pragma unroll
-  for (int e = 0; e < 4; ++e) lsum[e] = row16_sum(lsum[e]);
-  const int Hq = a.Hq;
-  // Partial index of output row `orow` (query row rr of this wave's KV head): static, the
-  // split slot of the row; balanced, the compact slot's entry for this head and row.
-  auto part_index = [&](int64_t orow, int rr) __attribute__((always_inline)) -> int64_t {
-    return a.balanced ? ((int64_t)slot * HW + wave) * R + rr : orow * a.part_stride + slot;
-  };
-
-  if constexpr (PVM) {
-    // ---- output: lanes of group g4 hold rows 4*g4 + e, column 16*dt + c16
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 4 * g4 + e;
-      if (g4 >= RB || r >= R) continue;
-      const int t = r / G, hg = r - (r / G) * G;
-      const int64_t row = ((int64_t)b * T + t) * Hq + kvh * G + hg;
-      if (a.single) {
-        const float l = lsum[e];
-        const float inv = (l > 0.f ? 1.f / l : 0.f) * vfac;
-        _Float16 *o = (_Float16 *)a.o + row * D + c16;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[16 * dt] = (_Float16)(acc[dt][e] * inv);
-        if (a.lse && c16 == 0) a.lse[row] = l > 0.f ? (m[e] + __log2f(l)) * kLn2 : kNegInf;
-      } else {
-        float *dst = a.ws_o + part_index(row, hg + G * t) * D + c16;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) dst[16 * dt] = acc[dt][e] * vfac;
-        if (c16 == 0) {
-          float *ml = a.ws_ml + part_index(row, hg + G * t) * 2;
-          ml[0] = m[e];
-          ml[1] = lsum[e];
-        }
-      }
-    }
-  } else {
-    // ---- sum the load slots: lanes l, l ^ LPR, ... hold the same head_dim elements
-#pragma unroll
-    for (int r = 0; r < RM; ++r)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float x = accv[r][i];
-#pragma unroll
-        for (int sh = LPR; sh < 64; sh <<= 1) x += __shfl_xor(x, sh);
-        accv[r][i] = x;
-      }
-    float mr[RM], lr[RM];
-#pragma unroll
-    for (int r = 0; r < RM; ++r) {
-      mr[r] = readlane_f(m[r & 3], 16 * (r >> 2));
-      lr[r] = readlane_f(lsum[r & 3], 16 * (r >> 2));
-    }
-#pragma unroll
-    for (int r = 0; r < RM; ++r) {
-      if (lane >= LPR || r >= R) continue;
-      const int t = r / G, hg = r - (r / G) * G;
-      const int64_t row = ((int64_t)b * T + t) * Hq + kvh * G + hg;
-      if (a.single) {
-        const float l = lr[r];
-        const float inv = (l > 0.f ? 1.f / l : 0.f) * vfac;
-        half8 out;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) out[i] = (_Float16)(accv[r][i] * inv);
-        *(half8 *)((_Float16 *)a.o + row * D + vlane_el) = out;
-        if (a.lse && lane == 0) a.lse[row] = l > 0.f ? (mr[r] + __log2f(l)) * kLn2 : kNegInf;
-      } else {
-        float *dst = a.ws_o + part_index(row, hg + G * t) * D + vlane_el;
-        *(float4v *)dst = float4v{accv[r][0], accv[r][1], accv[r][2], accv[r][3]} * vfac;
-        *(float4v *)(dst + 4) = float4v{accv[r][4], accv[r][5], accv[r][6], accv[r][7]} * vfac;
-        if (lane == 0) {
-          float *ml = a.ws_ml + part_index(row, hg + G * t) * 2;
-          ml[0] = mr[r];
-          ml[1] = lr[r];
-        }
-      }
-    }
-  }
-  }  // segments
-}
 
 // ----------------------------------------------------------------------------- merge kernels
 // The partials of output row `row` (sequence b, query head -> KV head): their count, the
 // index of the first and the index step between consecutive ones. Static: the splits covering
 // the sequence's blocks, contiguous at row * part_stride. Balanced: the shares the (sequence,
-// head group) schedule row r meets, w_first .. w_last, in compact slots r + w, by the partial
-// kernel's own integer arithmetic. Called by the whole wave.
+// schedule head) schedule row r meets, w_first .. w_last, in compact slots r + w, by the
+// partial kernel's own integer arithmetic. Called by the whole wave.
 struct RowParts {
   int64_t first;
   int64_t stride;
@@ -1033,18 +37,21 @@ __device__ __forceinline__ RowParts row_parts(const LaunchArgs &a, int64_t row) 
   const int rem = (int)(row - b * per_seq);
   const int t = rem / a.Hq, qh = rem - t * a.Hq;
   const int kvh = qh / a.G, hg = qh - kvh * a.G;
-  const int HW = a.heads_per_wg, Hg = a.Hkv / HW;
-  const int grp = kvh / HW, wave = kvh - grp * HW;
-  const int RT = a.G * a.T;
+  const int r = hg + a.G * t;  // query row within the KV head
+  const int RPG = a.rows_per_group, NRG = a.row_groups;
+  const int rg = r / RPG;      // its row group
+  const int HW = a.heads_per_wg, Hg = a.sched_heads;
+  const int kgrp = kvh / HW, head_w = kvh - kgrp * HW;
+  const int grp = kgrp * NRG + rg;  // the schedule head
   const Shares sh = balanced_shares(a, 0);
-  const int64_t pre_b = (unsigned)__builtin_amdgcn_readlane((int)sh.pre_l, b);
-  const int64_t nb_b = __builtin_amdgcn_readlane((int)sh.nb_l, b);
+  const SeqRef s = seq_info(a, sh, b);
+  const int64_t pre_b = s.pre, nb_b = s.nb;
   if (nb_b == 0) return {0, 1, 0};
-  const int64_t row0 = Hg * pre_b + grp * nb_b;
-  const int w0 = share_of(row0, sh.n_blocks, sh.n_shares);
-  const int w1 = share_of(row0 + nb_b - 1, sh.n_blocks, sh.n_shares);
-  const int64_t r = (int64_t)b * Hg + grp;
-  return {((r + w0) * HW + wave) * RT + hg + a.G * t, (int64_t)HW * RT, w1 - w0 + 1};
+  const int64_t x0 = Hg * pre_b + grp * nb_b;  // the schedule row's first block
+  const int w0 = share_of(x0, sh.n_blocks, sh.n_shares);
+  const int w1 = share_of(x0 + nb_b - 1, sh.n_blocks, sh.n_shares);
+  const int64_t sr = (int64_t)b * Hg + grp;
+  return {((sr + w0) * HW + head_w) * RPG + (r - rg * RPG), (int64_t)HW * RPG, w1 - w0 + 1};
 }
 
 // Final write of one row from an unnormalized accumulator (wave 0's lanes hold D/64 each).
@@ -1247,39 +254,6 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_hier2(LaunchArgs a) {
   if (threadIdx.x < 64) write_row<D>(a, row, r.acc, r.M, r.S);
 }
 
-// ----------------------------------------------------------------------------- gather (test aid)
-template <int D, bool I8>
-__global__ __launch_bounds__(64) void gather_kernel(LaunchArgs a, int max_len, char *dk, char *dv,
-                                                    _Float16 *dks, _Float16 *dvs) {
-  constexpr int ES = I8 ? 1 : 2;
-  const int j = blockIdx.x * 64 + threadIdx.x;
-  const int kvh = blockIdx.y, b = blockIdx.z;
-  const int L = clamp_len(a.kv_len[b], a.max_kv_len, a.status, a.debug);
-  if (j >= L || j >= max_len) return;
-  const int P1 = (1 << a.page_shift) - 1;
-  bool ck, cv;
-  const int64_t pk = lookup_page(a.table, a.table_stride, b, j, a.page_shift, a.num_k_pages, &ck);
-  const int64_t pv = lookup_page(a.table, a.table_stride, b, j, a.page_shift, a.num_v_pages, &cv);
-  if (a.debug && (ck || cv)) atomicOr(a.status, (unsigned)SKVD_STATUS_PAGE_CLAMPED);
-  const int64_t ok = row_offset(pk, j & P1, kvh, a.page_stride, a.tok_stride, a.head_stride);
-  const int64_t ov = row_offset(pv, j & P1, kvh, a.page_stride, a.tok_stride, a.head_stride);
-  const int64_t dst = (((int64_t)b * max_len + j) * a.Hkv + kvh);
-  const char *ks = (const char *)a.k + ok * ES;
-  const char *vs = (const char *)a.v + ov * ES;
-  for (int i = 0; i < D * ES; i += 4) {
-    *(unsigned *)(dk + dst * D * ES + i) = *(const unsigned *)(ks + i);
-    *(unsigned *)(dv + dst * D * ES + i) = *(const unsigned *)(vs + i);
-  }
-  if (I8 && !a.fp8) {  // int8: the row's f16 scales (fp8 has one per tensor)
-    const int64_t sk = row_offset(pk, j & P1, kvh, a.s_page_stride, a.s_tok_stride, a.s_head_stride);
-    const int64_t sv = row_offset(pv, j & P1, kvh, a.s_page_stride, a.s_tok_stride, a.s_head_stride);
-    for (int g = 0; g < D / 32; ++g) {
-      dks[dst * (D / 32) + g] = ((const _Float16 *)a.ks)[sk + g];
-      dvs[dst * (D / 32) + g] = ((const _Float16 *)a.vs)[sv + g];
-    }
-  }
-}
-
 // ----------------------------------------------------------------------------- stream read (measurement aid)
 // Every thread reads one 16-byte word per step with a grid-wide stride, so at any moment the
 // chip sweeps one contiguous window: the plainest way to run HBM at its sustainable rate.
@@ -1301,91 +275,38 @@ int launch_stream_read(const void *buf, size_t n16, uint32_t *sink, void *stream
 }
 
 // ----------------------------------------------------------------------------- launchers
-// Tokens per chunk and P.V unit per variant. D=128 chunks hold 32 tokens, D=256 chunks 16
-// (register bound; 64 int8 tokens at D=128 measured slower: two waves per SIMD). One query
-// row quarter at D=128 takes the vector P.V (pair dot products from registers, no LDS copy
-// of V); more rows, or D=256, make P.V a dense tile for the MFMA.
-template <int D, int RB>
-constexpr bool pv_on_mfma() {
-  return !(D == 128 && RB == 1);
-}
-template <int D, int RB, bool I8>
-constexpr int chunk_tokens() {
-  return D == 128 ? 32 : 16;
+// Partial-kernel grid: balanced, the plan's share count bound; static, split fastest over
+// (split, schedule head, sequence) (the plan keeps the count below 2^31).
+static unsigned partial_grid(const LaunchArgs &la) {
+  return la.balanced ? (unsigned)la.grid_wgs
+                     : (unsigned)((int64_t)la.split_stride * la.sched_heads * la.batch);
 }
 
-// Events: optional pair that the dispatch itself stamps with the kernel's begin and end.
-struct KernelEvents {
-  hipEvent_t start = nullptr, stop = nullptr;
-};
-
-template <typename K>
-static void launch_one(K kernel, dim3 grid, unsigned threads, hipStream_t st,
-                       const KernelEvents &ev, const LaunchArgs &la) {
-  if (ev.start || ev.stop)
-    hipExtLaunchKernelGGL(kernel, grid, dim3(threads), 0, st, ev.start, ev.stop, 0, la);
-  else
-    kernel<<<grid, threads, 0, st>>>(la);
-}
-
-template <int D, int RB, int KV, int HW>
-static void launch_partial_hw(const LaunchArgs &la, dim3 grid, hipStream_t st, bool fast,
-                              const KernelEvents &ev) {
-  constexpr int CH = chunk_tokens<D, RB, KV != 0>();
-  constexpr bool PVM = pv_on_mfma<D, RB>();
-  if (fast)
-    launch_one(partial_kernel<D, RB, KV, true, CH, PVM, HW>, grid, 64 * HW, st, ev, la);
-  else
-    launch_one(partial_kernel<D, RB, KV, false, CH, PVM, HW>, grid, 64 * HW, st, ev, la);
-}
-
-// KV heads per workgroup (one wave each): the D=128 single-quarter variants read each token's
-// rows of 4 (or 2) KV heads from one CU together (int8: and share the token's scale line);
-// every other variant serves one head.
-template <int D, int RB, int KV>
-static void launch_partial_t(const LaunchArgs &la, dim3 grid, hipStream_t st, bool fast,
-                             const KernelEvents &ev) {
-  if constexpr (D == 128 && RB == 1) {
-    if (la.heads_per_wg == 8) return launch_partial_hw<D, RB, KV, 8>(la, grid, st, fast, ev);
-    if (la.heads_per_wg == 4) return launch_partial_hw<D, RB, KV, 4>(la, grid, st, fast, ev);
-    if (la.heads_per_wg == 2) return launch_partial_hw<D, RB, KV, 2>(la, grid, st, fast, ev);
+static int launch_partial_any(const Plan &p, const LaunchArgs &la, void *stream,
+                              const KernelEvents &ev, bool dbg) {
+  const unsigned grid = partial_grid(la);
+  const int kv = la.fp8 ? 2 : la.int8 ? 1 : 0;
+  if (la.D == 128) {
+    if (kv == 2) return launch_partial_128_2(p, la, grid, stream, ev, dbg);
+    if (kv == 1) return launch_partial_128_1(p, la, grid, stream, ev, dbg);
+    return launch_partial_128_0(p, la, grid, stream, ev, dbg);
   }
-  launch_partial_hw<D, RB, KV, 1>(la, grid, st, fast, ev);
-}
-
-template <int D, int KV>
-static void launch_partial_rb(const Plan &p, const LaunchArgs &la, dim3 grid, hipStream_t st,
-                              const KernelEvents &ev) {
-  const bool fast = p.prm.page_size >= 16;
-  switch (p.row_blocks) {
-    case 1: launch_partial_t<D, 1, KV>(la, grid, st, fast, ev); break;
-    case 2: launch_partial_t<D, 2, KV>(la, grid, st, fast, ev); break;
-    default: launch_partial_t<D, 4, KV>(la, grid, st, fast, ev); break;
-  }
+  if (kv == 2) return launch_partial_256_2(p, la, grid, stream, ev, dbg);
+  if (kv == 1) return launch_partial_256_1(p, la, grid, stream, ev, dbg);
+  return launch_partial_256_0(p, la, grid, stream, ev, dbg);
 }
 
 int launch_partial(const Plan &p, const LaunchArgs &la, void *stream, void *start_event,
                    void *stop_event) {
-  hipStream_t st = (hipStream_t)stream;
   KernelEvents ev;
-  ev.start = (hipEvent_t)start_event;
-  ev.stop = (hipEvent_t)stop_event;
-  // one-dimensional grid: balanced, the plan's share count bound; static, split fastest over
-  // (split, KV head, sequence) (the plan keeps the count below 2^31)
-  dim3 grid(la.balanced ? (unsigned)la.grid_wgs
-                        : (unsigned)((int64_t)la.split_stride * (la.Hkv / la.heads_per_wg) *
-                                     la.batch));
-  const int kv = la.fp8 ? 2 : la.int8 ? 1 : 0;
-  if (la.D == 128) {
-    if (kv == 2) launch_partial_rb<128, 2>(p, la, grid, st, ev);
-    else if (kv == 1) launch_partial_rb<128, 1>(p, la, grid, st, ev);
-    else launch_partial_rb<128, 0>(p, la, grid, st, ev);
-  } else {
-    if (kv == 2) launch_partial_rb<256, 2>(p, la, grid, st, ev);
-    else if (kv == 1) launch_partial_rb<256, 1>(p, la, grid, st, ev);
-    else launch_partial_rb<256, 0>(p, la, grid, st, ev);
-  }
-  return (int)hipGetLastError();
+  ev.start = start_event;
+  ev.stop = stop_event;
+  return launch_partial_any(p, la, stream, ev, false);
+}
+
+int launch_gather(const Plan &p, const LaunchArgs &la, void *stream) {
+  if (la.batch == 0) return 0;
+  return launch_partial_any(p, la, stream, KernelEvents{}, true);
 }
 
 template <int D>
@@ -1395,10 +316,10 @@ static void launch_merge_t(const Plan &p, const LaunchArgs &la, hipStream_t st) 
     case SKVD_REDUCER_DIRECT: merge_direct<D><<<rows, 64, 0, st>>>(la); break;
     case SKVD_REDUCER_COOPERATIVE: merge_rows<D, 1><<<rows, 64, 0, st>>>(la); break;
     case SKVD_REDUCER_MULTIPASS: {
-      // Balanced: a schedule row (sequence, head group) meets on average at most
+      // Balanced: a schedule row (sequence, schedule head) meets on average at most
       // shares / rows + 1 partials; while that fits one wave's lanes, one wave per output row
       // (rounds of 64 cover the outliers) beats four.
-      const int64_t sched_rows = (int64_t)la.batch * (la.Hkv / la.heads_per_wg);
+      const int64_t sched_rows = (int64_t)la.batch * la.sched_heads;
       if (la.balanced && la.grid_wgs / sched_rows + 1 <= 64)
         merge_rows<D, 1><<<rows, 64, 0, st>>>(la);
       else
@@ -1418,24 +339,6 @@ int launch_merge(const Plan &p, const LaunchArgs &la, void *stream) {
   hipStream_t st = (hipStream_t)stream;
   if (la.D == 128) launch_merge_t<128>(p, la, st);
   else launch_merge_t<256>(p, la, st);
-  return (int)hipGetLastError();
-}
-
-int launch_gather(const Plan &p, const LaunchArgs &la, int max_len, void *dk, void *dv, void *dks,
-                  void *dvs, void *stream) {
-  hipStream_t st = (hipStream_t)stream;
-  dim3 grid((max_len + 63) / 64, la.Hkv, la.batch);
-  if (grid.x == 0 || la.batch == 0) return 0;
-  char *k = (char *)dk, *v = (char *)dv;
-  _Float16 *ks = (_Float16 *)dks, *vs = (_Float16 *)dvs;
-  if (la.D == 128) {
-    if (la.int8) gather_kernel<128, true><<<grid, 64, 0, st>>>(la, max_len, k, v, ks, vs);
-    else gather_kernel<128, false><<<grid, 64, 0, st>>>(la, max_len, k, v, ks, vs);
-  } else {
-    if (la.int8) gather_kernel<256, true><<<grid, 64, 0, st>>>(la, max_len, k, v, ks, vs);
-    else gather_kernel<256, false><<<grid, 64, 0, st>>>(la, max_len, k, v, ks, vs);
-  }
-  (void)p;
   return (int)hipGetLastError();
 }
 

@@ -65,8 +65,10 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
                 prm.max_q_per_seq);
   const int G = Hq / Hkv;
   const int R = G * prm.max_q_per_seq;
-  if (R > 16)
-    return fail(err, errn, SKVD_ERR_SHAPE, "group*max_q_per_seq=%d exceeds 16 rows", R);
+  // Query rows of one KV head: up to 16 per wave (the 16x16 MFMA's rows), up to 4 such waves
+  // per workgroup, and row groups of 64 beyond that.
+  if (R > 1024)
+    return fail(err, errn, SKVD_ERR_SHAPE, "group*max_q_per_seq=%d exceeds 1024 rows", R);
   if (prm.kv_dtype != SKVD_KV_F16 && prm.kv_dtype != SKVD_KV_I8_F16SCALE32 &&
       prm.kv_dtype != SKVD_KV_FP8_E4M3)
     return fail(err, errn, SKVD_ERR_DTYPE, "kv_dtype=%d unknown", prm.kv_dtype);
@@ -103,10 +105,14 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
   p.group = G;
   p.rows_per_wg = R;
   p.row_blocks = R <= 4 ? 1 : (R <= 8 ? 2 : 4);
+  p.row_tiles = R <= kRowTile ? 1 : (R <= 2 * kRowTile ? 2 : 4);
+  p.rows_per_group = std::min(R, kRowTile * p.row_tiles);
+  p.row_groups = (R + p.rows_per_group - 1) / p.rows_per_group;
   p.num_cus = num_cus;
   p.max_blocks = (prm.max_kv_len + kBlockTokens - 1) / kBlockTokens;
   p.rows_cap = (int64_t)prm.max_batch * prm.max_q_per_seq * Hq;
   p.heads_per_wg = hw;
+  p.sched_heads = (Hkv / hw) * p.row_groups;
 
   // Blocks per split. Two pressures: enough workgroups to fill the chip (about 16 per CU
   // when every sequence is at max_kv_len), and partial traffic (one (m, l, D floats) per row
@@ -127,12 +133,12 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
   if (prm.force_blocks_per_split > 0) bps = prm.force_blocks_per_split;
   if (bps > p.max_blocks) bps = p.max_blocks;
   if (bps < 1) bps = 1;
-  // The partial kernel's one-dimensional grid holds split_stride x KV heads x sequences
+  // The partial kernel's one-dimensional grid holds split_stride x schedule heads x sequences
   // < 2^31 workgroups, split_stride being splits_cap rounded up to odd.
-  const int64_t per_split = (int64_t)(Hkv / hw) * prm.max_batch;
+  const int64_t per_split = (int64_t)p.sched_heads * prm.max_batch;
   const int64_t max_splits = INT32_MAX / per_split - 1;
   if (max_splits < 1)
-    return fail(err, errn, SKVD_ERR_SHAPE, "num_kv_heads x max_batch = %lld exceeds the grid",
+    return fail(err, errn, SKVD_ERR_SHAPE, "schedule heads x max_batch = %lld exceeds the grid",
                 (long long)per_split);
   const int64_t bps_grid = (p.max_blocks + max_splits - 1) / max_splits;
   if (bps < bps_grid) {
@@ -147,7 +153,8 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
   // Schedule. Static: workgroups are (split, KV head, sequence) at fixed block offsets, so a
   // ragged batch leaves some compute units with more work than others once the grid fits the
   // chip in one round. Balanced: equal shares of the blocks actually present, cut on the device
-  // from kv_len (one sequence per lane, hence the batch limit); partials go to compact slots,
+  // from kv_len (up to 16 sequences per lane of one wave, hence the batch limit); partials go to
+  // compact slots,
   // one per (schedule row, share) pair that meet — at most rows + shares — so the workspace does
   // not grow with the context and shares can be as small as one block.
   int sched = prm.schedule;
@@ -181,13 +188,16 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
                                                 : i8 ? (hw == 8 ? 2 : 8 / hw)
                                                      : std::max(1, kDefaultWgsPerCu / hw))
                                              : kDefaultWgsPerCu;
-    p.grid_wgs = (prm.wgs_per_cu ? prm.wgs_per_cu : auto_wpc) * num_cus;
+    // several row-tile waves per workgroup (more than 16 query rows per KV head): the same
+    // waves per CU as one-wave workgroups
+    const int auto_wgs = std::max(1, auto_wpc / p.row_tiles);
+    p.grid_wgs = (prm.wgs_per_cu ? prm.wgs_per_cu : auto_wgs) * num_cus;
     // a forced split size becomes the balanced shares' minimum
     p.piece_min = prm.force_blocks_per_split > 0 ? p.bps : 1;
     const int64_t per_row = std::min<int64_t>(p.grid_wgs,
                                               (p.max_blocks + p.piece_min - 1) / p.piece_min + 1);
     p.part_stride = (int)per_row;
-    p.slots_cap = (int64_t)prm.max_batch * (Hkv / hw) + p.grid_wgs;
+    p.slots_cap = (int64_t)prm.max_batch * p.sched_heads + p.grid_wgs;
   } else {
     p.part_stride = p.splits_cap;
     p.piece_min = p.bps;
@@ -221,7 +231,7 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
   off = align_up(off + sizeof(uint32_t));
   const size_t parts = red == SKVD_REDUCER_NONE ? 0
                        : sched == SKVD_SCHEDULE_BALANCED
-                           ? (size_t)p.slots_cap * hw * R
+                           ? (size_t)p.slots_cap * hw * p.rows_per_group
                            : (size_t)p.rows_cap * p.part_stride;
   p.off_ml = off;
   off = align_up(off + parts * 2 * sizeof(float));
@@ -339,6 +349,11 @@ void fill_launch_args(const Plan &p, const skvd_decode_args &a, void *ws, Launch
   l.balanced = p.schedule == SKVD_SCHEDULE_BALANCED;
   l.grid_wgs = p.grid_wgs;
   l.heads_per_wg = p.heads_per_wg;
+  l.row_tiles = p.row_tiles;
+  l.row_groups = p.row_groups;
+  l.rows_per_group = p.rows_per_group;
+  l.sched_heads = p.sched_heads;
+  l.seqs_per_lane = std::max(1, (a.batch + 63) / 64);
   l.part_stride = p.part_stride;
   l.piece_min = p.piece_min;
   l.max_kv_len = p.prm.max_kv_len;

@@ -12,14 +12,19 @@ namespace skvd {
 constexpr int kBlockTokens = 64;  // one partial block: 64 consecutive KV positions
 constexpr int kHierGroup = 64;    // partials merged by one first-level hierarchical workgroup
 constexpr size_t kAlign = 256;
-constexpr int kBalancedMaxBatch = 64;  // balanced schedule: one sequence per lane of a wave
+constexpr int kBalancedMaxBatch = 1024;  // balanced schedule: up to 16 sequences per lane of a wave
+constexpr int kRowTile = 16;             // query rows of one wave (the 16x16 MFMA's rows)
 constexpr int kDefaultWgsPerCu = 4;
 
 struct Plan {
   skvd_plan_params prm;
   int group;          // G = Hq / Hkv
-  int rows_per_wg;    // G * max_q_per_seq
-  int row_blocks;     // ceil(rows_per_wg / 4): 16x16 MFMA row quarters in use (1, 2 or 4)
+  int rows_per_wg;    // R = G * max_q_per_seq: query rows of one KV head
+  int row_blocks;     // 16x16 MFMA row quarters in use per wave (1, 2 or 4; 4 when R > 16)
+  int row_tiles;      // RT: waves per KV head in a workgroup, 16 rows each (1, 2 or 4)
+  int row_groups;     // NRG = ceil(R / (16 RT)): workgroups per KV head (rows 16 RT each)
+  int rows_per_group; // RPG = min(R, 16 RT): query rows one schedule head covers
+  int sched_heads;    // Hg = (Hkv / heads_per_wg) * row_groups: schedule heads per sequence
   int num_cus;
   int max_blocks;     // ceil(max_kv_len / 64)
   int bps;            // 64-token blocks per split
@@ -54,6 +59,8 @@ struct LaunchArgs {
   int bps, splits_cap, split_stride, max_kv_len, hier_groups_cap;  // stride: odd, >= cap
   int balanced, grid_wgs, part_stride, piece_min;
   int heads_per_wg;  // KV heads (waves) per partial-kernel workgroup; divides Hkv
+  int row_tiles, row_groups, rows_per_group, sched_heads;  // as in Plan
+  int seqs_per_lane;  // balanced schedule: sequences per lane of the share computation
   int int8;         // one-byte elements (int8 with f16 group scales, or fp8)
   int fp8;          // fp8 E4M3: ks / vs each point to one f32 tensor scale
   int debug;
@@ -66,6 +73,12 @@ struct LaunchArgs {
   void *o;
   float *lse;
   int single;        // the partial kernel writes o/lse (reducer NONE)
+  // gather-debug launches only (the partial kernel's debug variant): raw K/V elements and
+  // int8 scales as the kernel holds them at their point of use, into dense
+  // [B, dbg_max_len, Hkv, D] / [B, dbg_max_len, Hkv, D/32] arrays
+  char *dbg_k, *dbg_v;
+  uint16_t *dbg_ks, *dbg_vs;  // f16 bits
+  int dbg_max_len;
 };
 
 // plan.cpp (pure host)
@@ -82,8 +95,24 @@ int launch_partial(const Plan &p, const LaunchArgs &la, void *stream, void *star
                    void *stop_event = nullptr);
 int launch_merge(const Plan &p, const LaunchArgs &la, void *stream);
 int launch_stream_read(const void *buf, size_t n16, uint32_t *sink, void *stream);
-int launch_gather(const Plan &p, const LaunchArgs &la, int max_len, void *dk, void *dv, void *dks,
-                  void *dvs, void *stream);
+// The partial kernel's debug variant (the plan's own schedule and lane layout) writing the raw
+// K/V rows and int8 scales it uses into la.dbg_* instead of any partial or output.
+int launch_gather(const Plan &p, const LaunchArgs &la, void *stream);
+
+// Per-format partial launchers (partial_<D>_<fmt>.hip), dispatched by launch_partial.
+struct KernelEvents {
+  void *start = nullptr, *stop = nullptr;  // hipEvent_t stamped by the dispatch, or NULL
+};
+#define SKVD_DECLARE_PARTIAL(D, KV)                                                            \
+  int launch_partial_##D##_##KV(const Plan &p, const LaunchArgs &la, unsigned grid,            \
+                                void *stream, const KernelEvents &ev, bool dbg);
+SKVD_DECLARE_PARTIAL(128, 0)
+SKVD_DECLARE_PARTIAL(128, 1)
+SKVD_DECLARE_PARTIAL(128, 2)
+SKVD_DECLARE_PARTIAL(256, 0)
+SKVD_DECLARE_PARTIAL(256, 1)
+SKVD_DECLARE_PARTIAL(256, 2)
+#undef SKVD_DECLARE_PARTIAL
 
 // Append launch (append.hip): resolved on the host from the plan and skvd_append_args.
 struct AppendLaunch {

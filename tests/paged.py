@@ -118,3 +118,82 @@ def random_dense(rng, B, Lmax, Hkv, D, int8=False):
     Ks = (rng.uniform(0.005, 0.05, size=(B, Lmax, Hkv, D // 32))).astype(np.float16)
     Vs = (rng.uniform(0.005, 0.05, size=(B, Lmax, Hkv, D // 32))).astype(np.float16)
     return K, V, Ks, Vs
+
+
+def quantize_dense(x, kv, rng_scale=None):
+    """f32 dense rows -> the stored form of cache format kv: f16 values; int8 codes and f16
+    scales (the workload generator's quantizer); or E4M3 bytes (torch's nearest-even cast of
+    x / scale, clipped to +-448) with a [1] f32 tensor scale. Returns (stored, scales)."""
+    import workloads
+    if kv == "f16":
+        return x.astype(np.float16), None
+    if kv == "i8":
+        return workloads.quantize_int8(x.astype(np.float32))
+    scale = np.float32(1 / 64 if rng_scale is None else rng_scale)
+    y = np.clip(x.astype(np.float32) / scale, np.float32(-448), np.float32(448))
+    b = torch.from_numpy(np.ascontiguousarray(y)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return b, np.array([scale], np.float32)
+
+
+def dominant_problem(rng, B, T, Hq, Hkv, D, P, L, kv, positions, *, beta=32.0, noise=0.25,
+                     spare=3):
+    """A problem whose every (sequence b, KV head g) has one dominant key: K rows are
+    noise * N(0,1) except row positions[b][g] = alpha * u[b,g], and every query row of the
+    group is beta * u[b,g] plus 0.3 * N(0,1), u a random unit vector. alpha is set so that the
+    dominant logit exceeds every other visible one by >= 40 (checked on the stored values), so
+    o is that position's V row to within e^-40 * L. positions[b][g] <= L[b] - T. Returns the
+    problem dict and the dequantized dominant V rows [B, Hkv, D] (fp64)."""
+    L = np.asarray(L, np.int32)
+    G = Hq // Hkv
+    Lmax = int(L.max())
+    sm = 1.0 / math.sqrt(D)
+    u = rng.standard_normal((B, Hkv, D))
+    u /= np.linalg.norm(u, axis=-1, keepdims=True)
+    K = (noise * rng.standard_normal((B, Lmax, Hkv, D))).astype(np.float32)
+    V = rng.standard_normal((B, Lmax, Hkv, D)).astype(np.float32)
+    # the noise keys' largest logit is about sm * beta * noise * 4.5; the dominant one
+    # sm * beta * alpha
+    alpha = (44.0 + sm * beta * noise * 5.0) / (sm * beta)
+    for b in range(B):
+        for g in range(Hkv):
+            p = int(positions[b][g])
+            assert 0 <= p <= L[b] - T, (b, g, p, L[b])
+            K[b, p, g] = alpha * u[b, g]
+    q = np.empty((B * T, Hq, D), np.float32)
+    for b in range(B):
+        for h in range(Hq):
+            q[b * T:(b + 1) * T, h] = beta * u[b, h // G] + 0.3 * rng.standard_normal((T, D))
+    q = q.astype(np.float16)
+    Kd, Ks = quantize_dense(K, kv)
+    Vd, Vs = quantize_dense(V, kv)
+    prob = paged_from_dense(rng, q, Kd, Vd, L, P, T=T, spare=spare, Ks=Ks, Vs=Vs, sm_scale=sm)
+    Kf, Vf = dequant(Kd, Ks), dequant(Vd, Vs)
+    dom = np.empty((B, Hkv, D))
+    q64 = q.astype(np.float64)
+    for b in range(B):
+        for g in range(Hkv):
+            p = int(positions[b][g])
+            dom[b, g] = Vf[b, p, g]
+            for t in range(T):
+                n = int(L[b]) - T + t + 1
+                s = sm * (Kf[b, :n, g] @ q64[b * T + t, g * G:(g + 1) * G].T)  # [n, G]
+                gap = s[p] - np.delete(s, p, axis=0).max(axis=0) if n > 1 else np.full(G, 99.0)
+                assert gap.min() >= 40.0, (b, g, t, gap.min())
+    return prob, dom
+
+
+def identical_key_problem(rng, B, T, Hq, Hkv, D, P, L, kv, spare=3):
+    """Every visible K row of (sequence b, KV head g) is the same vector; V rows random. The
+    softmax is then uniform over a row's n visible positions: o = mean of its n V rows and
+    lse = s + ln n with s the one logit. Returns the problem and the dequantized dense K, V."""
+    L = np.asarray(L, np.int32)
+    Lmax = int(L.max())
+    k0 = rng.standard_normal((B, 1, Hkv, D)).astype(np.float32)
+    K = np.repeat(k0, Lmax, axis=1)
+    V = rng.standard_normal((B, Lmax, Hkv, D)).astype(np.float32)
+    q = (2.0 * rng.standard_normal((B * T, Hq, D))).astype(np.float16)
+    Kd, Ks = quantize_dense(K, kv)
+    Vd, Vs = quantize_dense(V, kv)
+    prob = paged_from_dense(rng, q, Kd, Vd, L, P, T=T, spare=spare, Ks=Ks, Vs=Vs,
+                            sm_scale=1.0 / math.sqrt(D))
+    return prob, dequant(Kd, Ks), dequant(Vd, Vs)

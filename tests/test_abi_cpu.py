@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol():
     for s in syms:
         assert hasattr(L, s), s
     assert set(syms) == set(bd.SIGNATURES), set(syms) ^ set(bd.SIGNATURES)
-    assert L.skvd_abi_version() == bd.ABI_VERSION == 9
+    assert L.skvd_abi_version() == bd.ABI_VERSION == 10
 
 
 def plan(**kw):
@@ -85,10 +85,11 @@ def test_plan_splits_and_total_reducer(maxlen, bps):
 
 
 def test_schedule_choice():
-    assert plan(max_batch=64).schedule == "balanced"
-    p = plan(max_batch=65)
+    for b in (64, 65, 256, 1024):
+        assert plan(max_batch=b).schedule == "balanced"
+    p = plan(max_batch=1025)
     assert p.schedule == "static" and p.info.part_stride == p.info.splits_cap
-    assert p.info.grid_wgs == (p.info.splits_cap | 1) * (8 // p.info.heads_per_wg) * 65
+    assert p.info.grid_wgs == (p.info.splits_cap | 1) * (8 // p.info.heads_per_wg) * 1025
     s = plan(schedule="static")
     assert s.schedule == "static" and s.info.part_stride == s.info.splits_cap
     w = plan(wgs_per_cu=7, num_cus=100)
@@ -145,11 +146,11 @@ def test_heuristic_configs():
 
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=64), 2), (dict(num_qo_heads=30), 2), (dict(page_size=24), 2),
-    (dict(max_q_per_seq=9), 2), (dict(max_q_per_seq=8, num_qo_heads=32, num_kv_heads=8), 2),
+    (dict(max_q_per_seq=9), 2), (dict(max_q_per_seq=1, num_qo_heads=2048, num_kv_heads=1), 2),
     (dict(max_batch=0), 2), (dict(max_kv_len=0), 2), (dict(kv_dtype=7), 4),
     (dict(force_reducer="cooperative", max_kv_len=131072, max_batch=1, force_blocks_per_split=1), 7),
     (dict(force_reducer="none", max_kv_len=4096), 7),
-    (dict(schedule="balanced", max_batch=65), 7), (dict(schedule="balanced", max_kv_len=256), 7),
+    (dict(schedule="balanced", max_batch=1025), 7), (dict(schedule="balanced", max_kv_len=256), 7),
     (dict(schedule="balanced", force_reducer="none", max_kv_len=200), 7),
     (dict(schedule=3), 7), (dict(wgs_per_cu=65), 7), (dict(wgs_per_cu=-1), 7),
     (dict(heads_per_wg=2, max_q_per_seq=2), 7), (dict(kv_dtype="i8", heads_per_wg=3), 7),
