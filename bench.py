@@ -52,16 +52,13 @@ def _code_only(src: bytes) -> bytes:
 
 
 def kernel_source_hash() -> str:
-    """Hash of the partial kernel's source (kernels.hip up to the merge kernels, which holds
-    the addressing helpers and the partial kernel) and of plan.cpp (its launch shape)."""
+    """Hash of the partial kernel's source (partial.h, the device helpers it uses in
+    device_common.h) and of plan.cpp (its launch shape)."""
     csrc = os.path.join(ROOT, "quantized_kv_cache_page_amd", "csrc")
     h = hashlib.sha256()
-    with open(os.path.join(csrc, "kernels.hip"), "rb") as fh:
-        src = fh.read()
-    h.update(_code_only(src[:src.index(b"// ---------------------------------------------------------"
-                                       b"-------------------- merge kernels")]))
-    with open(os.path.join(csrc, "plan.cpp"), "rb") as fh:
-        h.update(_code_only(fh.read()))
+    for name in ("partial.h", "device_common.h", "plan.cpp"):
+        with open(os.path.join(csrc, name), "rb") as fh:
+            h.update(_code_only(fh.read()))
     return h.hexdigest()[:16]
 
 

@@ -127,6 +127,12 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
   int64_t bps = units / (16LL * num_cus);
   if (bps < bps_min) bps = bps_min;
   if (bps > 4LL * bps_min) bps = 4LL * bps_min;
+  // ... but at least one workgroup per CU when the work allows it: with many query rows per KV
+  // head (a large group times a multi-token draft) the traffic rule alone would leave a small
+  // batch a handful of workgroups walking whole sequences
+  const int64_t bps_fill = std::max<int64_t>(
+      1, (int64_t)prm.max_batch * p.sched_heads * p.max_blocks / num_cus);
+  if (bps > bps_fill) bps = bps_fill;
   // very short contexts: one split, one launch (up to 128 tokens; beyond, a second launch for
   // the merge costs less than one workgroup walking the chunks: 256 tokens 16.4 vs 12-13 us)
   if (p.max_blocks <= 2) bps = p.max_blocks;

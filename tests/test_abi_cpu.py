@@ -131,7 +131,14 @@ def test_heuristic_configs():
     assert plan(num_qo_heads=8, num_kv_heads=8, max_batch=1, max_kv_len=128).reducer == "none"
     c1 = plan(num_qo_heads=8, num_kv_heads=8, max_batch=1, max_kv_len=256)
     assert c1.reducer in ("direct", "cooperative") and c1.schedule == "balanced"
-    assert c1.info.heads_per_wg == 1 and c1.info.blocks_per_split == 2
+    # 32 (sequence, KV head, block) units on 256 CUs: one block per split fills the most CUs
+    assert c1.info.heads_per_wg == 1 and c1.info.blocks_per_split == 1
+    # many query rows per KV head (32 query / 4 KV heads, 8-token drafts, 64 rows): the partial
+    # traffic rule alone would give one split per row; the plan still fills the CUs
+    mtp = plan(num_qo_heads=32, num_kv_heads=4, max_batch=2, max_q_per_seq=8, max_kv_len=2544,
+               kv_dtype="i8")
+    assert mtp.schedule == "balanced" and mtp.info.splits_cap >= 32
+    assert "rows_per_wg=64" in mtp.describe()
     # (sequence, KV head, block) units <= CUs: one head per workgroup; beyond, four
     assert plan(max_batch=1, max_kv_len=1024).info.heads_per_wg == 1
     assert plan(max_batch=1, max_kv_len=8192).info.heads_per_wg == 4
@@ -150,7 +157,7 @@ def test_heuristic_configs():
     (dict(max_batch=0), 2), (dict(max_kv_len=0), 2), (dict(kv_dtype=7), 4),
     (dict(force_reducer="cooperative", max_kv_len=131072, max_batch=1, force_blocks_per_split=1), 7),
     (dict(force_reducer="none", max_kv_len=4096), 7),
-    (dict(schedule="balanced", max_batch=1025), 7), (dict(schedule="balanced", max_kv_len=256), 7),
+    (dict(schedule="balanced", max_batch=1025), 7), (dict(schedule="balanced", max_kv_len=128), 7),
     (dict(schedule="balanced", force_reducer="none", max_kv_len=200), 7),
     (dict(schedule=3), 7), (dict(wgs_per_cu=65), 7), (dict(wgs_per_cu=-1), 7),
     (dict(heads_per_wg=2, max_q_per_seq=2), 7), (dict(kv_dtype="i8", heads_per_wg=3), 7),
