@@ -236,6 +236,20 @@ skvd_status skvd_decode_check(const skvd_plan *plan, const skvd_decode_args *arg
 skvd_status skvd_decode(const skvd_plan *plan, const skvd_decode_args *args, void *workspace,
                         size_t workspace_bytes, void *stream);
 
+/* Allocation-free decode, for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation. Same arguments, result and errors as skvd_decode, but the workspace is a
+ * device array inside the library of SKVD_NOALLOC_WORKSPACE_MAX bytes per GPU (held until
+ * the process ends); plans whose skvd_plan_workspace_bytes() exceed it return
+ * SKVD_ERR_WORKSPACE, and debug plans (whose status word the caller reads from its own
+ * workspace) return SKVD_ERR_PLAN. No hipMalloc, hipFree or allocating call. The array's
+ * device address is looked up on the first call on each device (do that first call outside
+ * graph capture). Every call on a GPU shares that GPU's array: calls that overlap on one GPU
+ * (other streams, other threads, other plans) race and must be ordered by the caller. */
+#define SKVD_NOALLOC_WORKSPACE_MAX (((size_t)32) << 20)
+skvd_status skvd_decode_noalloc(const skvd_plan *plan, const skvd_decode_args *args,
+                                void *stream);
+
 /* The two stages of skvd_decode, for callers that time or compose them. The partial stage
  * writes one (max, sum, f32 output) partial per split into the workspace, or o and lse
  * directly when the plan's reducer is SKVD_REDUCER_NONE; the merge stage reads those

@@ -96,6 +96,8 @@ SIGNATURES = {
     "skvd_decode_check": (ctypes.c_int, [_PLAN_P, ctypes.POINTER(skvd_decode_args), ctypes.c_size_t]),
     "skvd_decode": (ctypes.c_int, [_PLAN_P, ctypes.POINTER(skvd_decode_args), ctypes.c_void_p,
                                    ctypes.c_size_t, ctypes.c_void_p]),
+    "skvd_decode_noalloc": (ctypes.c_int, [_PLAN_P, ctypes.POINTER(skvd_decode_args),
+                                           ctypes.c_void_p]),
     "skvd_decode_partial": (ctypes.c_int, [_PLAN_P, ctypes.POINTER(skvd_decode_args),
                                            ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "skvd_decode_merge": (ctypes.c_int, [_PLAN_P, ctypes.POINTER(skvd_decode_args),
@@ -202,6 +204,10 @@ def skvd_decode_check(plan: int, args: skvd_decode_args, workspace_bytes: int) -
 
 def skvd_decode(plan, args, workspace, workspace_bytes, stream) -> int:
     return int(lib().skvd_decode(plan, ctypes.byref(args), workspace, workspace_bytes, stream))
+
+
+def skvd_decode_noalloc(plan, args, stream) -> int:
+    return int(lib().skvd_decode_noalloc(plan, ctypes.byref(args), stream))
 
 
 def skvd_decode_partial(plan, args, workspace, workspace_bytes, stream) -> int:
@@ -472,6 +478,17 @@ class Plan:
         fn = {"all": skvd_decode, "partial": skvd_decode_partial, "merge": skvd_decode_merge}[stage]
         _check(fn(self.handle, a, ws.data_ptr(), self.workspace_bytes, self._stream(stream)),
                f"skvd_decode[{stage}]")
+        return out, lse
+
+    def run_noalloc(self, q, k_pages, v_pages, page_table, kv_len, sm_scale, k_scales=None,
+                    v_scales=None, out=None, lse=None, q_per_seq=1, stream=None):
+        """skvd_decode_noalloc: the decode with the library's own device workspace (no plan
+        workspace is allocated). out and lse must be passed by callers that cannot allocate
+        (the defaults allocate them). Returns (o, lse) as run()."""
+        out, lse = self._outputs(q, out, lse)
+        a = self.make_args(q, k_pages, v_pages, page_table, kv_len, sm_scale, k_scales, v_scales,
+                           out, lse, q_per_seq)
+        _check(skvd_decode_noalloc(self.handle, a, self._stream(stream)), "skvd_decode_noalloc")
         return out, lse
 
     def check(self, q, k_pages, v_pages, page_table, kv_len, sm_scale, k_scales=None,

@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "skvd_internal.h"
@@ -125,6 +126,35 @@ skvd_status check_prefill(const skvd_plan *plan, const skvd_decode_args *a) {
   skvd_decode_args one = *a;
   one.q_per_seq = 1;  // the remaining checks do not depend on the token count
   return skvd::check_args(p, &one, p.ws_bytes, g_err, sizeof g_err);
+}
+
+// ---- the allocation-free decode's workspace: one file-scope device array per GPU. In host code
+// `scratch` names a host-side stand-in, not device memory: every use goes through the device
+// address hipGetSymbolAddress returns for the current device, kept per device.
+constexpr size_t kScratchBytes = size_t(32) << 20;  // SKVD_NOALLOC_WORKSPACE_MAX
+static_assert(kScratchBytes == SKVD_NOALLOC_WORKSPACE_MAX, "header and library agree");
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// The current device's scratch address (looked up once per device, with that device current).
+skvd_status device_scratch(int dev, void **out) {
+  if (dev < 0 || dev >= kMaxDevices)
+    return set_err(SKVD_ERR_DEVICE, "device %d outside 0..%d", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return set_err(SKVD_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                     hipGetErrorString(e));
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SKVD_OK;
 }
 
 }  // namespace
@@ -267,6 +297,33 @@ skvd_status skvd_decode(const skvd_plan *plan, const skvd_decode_args *args, voi
   if (st != SKVD_OK || args->batch == 0) return st;
   skvd::LaunchArgs la;
   skvd::fill_launch_args(plan->p, *args, workspace, &la);
+  int e = skvd::launch_partial(plan->p, la, stream);
+  if (e) return hip_err(e, "partial kernel launch");
+  e = skvd::launch_merge(plan->p, la, stream);
+  return e ? hip_err(e, "merge kernel launch") : SKVD_OK;
+}
+
+skvd_status skvd_decode_noalloc(const skvd_plan *plan, const skvd_decode_args *args,
+                                void *stream) {
+  g_err[0] = 0;
+  if (!plan) return set_err(SKVD_ERR_NULL, "plan is NULL");
+  if (plan->p.ws_bytes > kScratchBytes)
+    return set_err(SKVD_ERR_WORKSPACE, "the plan's workspace of %zu bytes exceeds the %zu bytes "
+                   "of the allocation-free decode's device array (use skvd_decode with a "
+                   "workspace)", plan->p.ws_bytes, kScratchBytes);
+  if (plan->p.prm.debug)
+    return set_err(SKVD_ERR_PLAN, "debug plans record their status word in a caller workspace: "
+                   "use skvd_decode");
+  skvd_status st = skvd::check_args(plan->p, args, plan->p.ws_bytes, g_err, sizeof g_err);
+  if (st == SKVD_OK) st = check_device(plan->p);
+  if (st != SKVD_OK || args->batch == 0) return st;
+  void *ws = nullptr;
+  st = device_scratch(plan->p.prm.device, &ws);
+  if (st != SKVD_OK) return st;
+  // every partial the merge reads is written by the same call's partial kernel, so nothing in
+  // the array needs clearing (the status word is only written by debug plans)
+  skvd::LaunchArgs la;
+  skvd::fill_launch_args(plan->p, *args, ws, &la);
   int e = skvd::launch_partial(plan->p, la, stream);
   if (e) return hip_err(e, "partial kernel launch");
   e = skvd::launch_merge(plan->p, la, stream);
