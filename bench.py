@@ -1,23 +1,27 @@
 #!/usr/bin/env python3
 """Benchmark: split-KV paged decode on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config 2] [--gpus 1] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--config 5] [--gpus 1] [--no-cpu] [--no-append]
     python bench.py --op append [--append prefill_i8|prefill_f16|prefill_f8|decode_i8]
     python bench.py --op prefill [--prefill prompt_i8|prompt_f16|prompt_f8]
     python bench.py --op merge
+    python bench.py --sweep cliff|long|long_i8|long_f8
 
-A step is one decode call (partial kernel + reducer) over one batch of the workload, with
-all inputs resident in HBM. The default workload is the GQA batch decode (B=32, 32 query /
-8 KV heads, head_dim 128, page 16, kv_len uniform in [1024, 4096], f16 cache). Enough copies
-of the pools and tables rotate that the working set exceeds twice the 256 MB Infinity Cache.
+A step is one decode call (partial kernel + reducer) over one batch of the workload, with all
+inputs resident in HBM. The default workload is the largest one, the int8 batch (workload 5:
+B=64, 32 query / 8 KV heads, head_dim 128, page 16, kv_len Zipf(1.1) clipped to [512, 65536],
+int8 K/V with one f16 scale per 32 elements). Enough copies of the pools rotate that the
+working set exceeds twice the 256 MB Infinity Cache.
 
-Prints one JSON line: value = K+V bytes read per call / time per call (GB/s), plus
-roofline (the partial kernel's algorithmic K+V bytes per launch over its average launch time,
-timed with HIP events on the launching stream, against 8 TB/s) and cpu_baseline (the fp64
-oracle on the host cores over a bounded sample of the same workload). The default line also
-carries an "append" object (the int8 prefill-chunk append: 32 sequences x 1024 new tokens
-quantized into the int8 cache) and a "prefill" object (the multi-token route on 4 x 2048-token
-prompts over an int8 cache). `--op append|prefill|merge` print those operations' own lines.
+Prints one JSON line: value = K+V bytes read per call / time per call (GB/s) over exactly K
+timed calls; roofline = the partial kernel's algorithmic K+V bytes per launch over its time per
+launch (back-to-back launches between one HIP event pair on the launching stream) against
+8 TB/s; cpu_baseline = the fp64 oracle on the host cores over whole decodes of the same batch.
+The default line also carries, each as min / median of three interleaved rounds of a fixed
+launch count: the other workloads (2, 3, 4), the pages' depth points (B=32 at 2000 / 2048 /
+2100 / 8192 tokens, with the largest GB/s dip across the 2048-token boundary; B=1 at 8192 /
+32768 / 131072), the int8 batch's shape over an fp8 cache, the int8 prefill-chunk append and
+the multi-token route on 4 x 2048-token prompts.
 """
 from __future__ import annotations
 
@@ -139,67 +143,187 @@ def cpu_baseline(prob, budget_s=12.0):
     t = float(np.median(times))
     gbs = workloads.kv_bytes(prob) / t / 1e9
     return {"value": round(gbs, 3), "unit": "GB/s", "cores": nthreads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{len(times)} whole decodes of the same batch (all {prob['q'].shape[0]} "
                       f"query tokens x {prob['q'].shape[1]} heads), median {t:.3f} s each, fp64"}
 
 
 CLIFF_LENS = [1024, 1470, 1900, 2000, 2047, 2048, 2049, 2100, 3000, 4096, 4097, 4800, 8192,
-              16384, 32768]
+             16384, 32768]
 LONG_LENS = [8192, 16384, 32768, 65536, 131072]
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+class DecodeBench:
+    """One decode workload resident on the GPU: the problem's q, table and lengths, and enough
+    copies of the pools (rotated call by call) that the working set exceeds twice the 256 MB
+    Infinity Cache. Timing helpers run on torch's current stream (the one the calls launch on)
+    and bracket back-to-back launches with one event pair."""
+
+    def __init__(self, spec, seed, bps=0, reducer="auto", schedule="auto", wgs_per_cu=0,
+                 heads_per_wg=0, layout="nhd", copies=0):
+        import numpy as np
+        import torch
+        import quantized_kv_cache_page_amd as skvd
+        import workloads
+        t0 = time.time()
+        self.spec = spec
+        self.prob = workloads.generate(spec, seed)
+        self.kvb = workloads.kv_bytes(self.prob)
+        dev = torch.device("cuda:0")
+
+        def up(x):
+            return None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+        self.q, self.table, self.kv_len = (up(self.prob[k]) for k in ("q", "page_table", "kv_len"))
+        pools = [up(self.prob[k]) for k in ("k_pages", "v_pages", "k_scales", "v_scales")]
+        if layout == "hnd":
+            pools = [None if p is None else p.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+                     if p.dim() == 4 else p for p in pools]
+        self.copies = copies or max(1, math.ceil(2 * MALL_BYTES / max(self.kvb, 1)) + 1)
+        self.sets = [pools] + [[None if p is None else p.clone() for p in pools]
+                               for _ in range(self.copies - 1)]
+        self.plan = skvd.Plan(spec.num_qo_heads, spec.num_kv_heads, spec.head_dim,
+                              spec.page_size, spec.kv_dtype, spec.batch, spec.q_per_seq,
+                              spec.max_kv_len, device=0, force_blocks_per_split=bps,
+                              force_reducer=reducer, schedule=schedule, wgs_per_cu=wgs_per_cu,
+                              heads_per_wg=heads_per_wg)
+        self.plan.ensure_workspace()
+        self.out = torch.empty(self.q.shape, dtype=torch.float16, device=dev)
+        self.lse = torch.empty(self.q.shape[:2], dtype=torch.float32, device=dev)
+        self.i = 0
+        self.setup_s = time.time() - t0
+
+    def call(self, stage="all", events=None):
+        k, v, ks, vs = self.sets[self.i % self.copies]
+        self.i += 1
+        self.plan.run(self.q, k, v, self.table, self.kv_len, self.prob["sm_scale"], ks, vs,
+                      out=self.out, lse=self.lse, q_per_seq=self.spec.q_per_seq, stage=stage,
+                      events=events)
+
+    def timed(self, n, stage="all"):
+        """Microseconds per launch over n back-to-back launches of `stage`."""
+        import torch
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n):
+            self.call(stage)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3
+
+    def stamped(self, n):
+        """Per-launch durations (us) of n partial-kernel launches back to back, each stamped by
+        its own dispatch (start and end events that the launch records itself)."""
+        import numpy as np
+        import torch
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        for a, b in ev:  # recording once creates the HIP events the dispatch stamps
+            a.record()
+            b.record()
+        torch.cuda.synchronize()
+        for e in ev:
+            self.call("partial", events=e)
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+
+    def graph_replay(self, n):
+        """Microseconds per decode replaying n decodes captured in one HIP graph."""
+        import torch
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            self.call()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for _ in range(n):
+                self.call()
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        del g
+        return e0.elapsed_time(e1) / n * 1e3
+
+    def rounds(self, rounds=3, n=30, graph=False):
+        """rounds interleaved rounds of: n whole decodes, n partial-kernel launches (and n
+        decodes replayed from a graph). Min and median per launch of each."""
+        import numpy as np
+        calls, parts, graphs = [], [], []
+        for _ in range(rounds):
+            calls.append(self.timed(n, "all"))
+            parts.append(self.timed(n, "partial"))
+            if graph:
+                graphs.append(self.graph_replay(n))
+        r = {"us_per_call_min": round(min(calls), 3),
+             "us_per_call_median": round(float(np.median(calls)), 3),
+             "partial_us_min": round(min(parts), 3),
+             "partial_us_median": round(float(np.median(parts)), 3),
+             "rounds": rounds, "launches_per_round": n}
+        if graph:
+            r["graph_replay_us_min"] = round(min(graphs), 3)
+            r["graph_replay_us_median"] = round(float(np.median(graphs)), 3)
+        return r
+
+    def release(self):
+        import torch
+        self.sets = None
+        self.plan = None
+        torch.cuda.empty_cache()
+
+
+def decode_object(spec, seed, what, rounds=3, n=30, warmup=5, **kw):
+    """One extra decode measurement for the bench line: min / median of `rounds` interleaved
+    rounds of n launches each (a fixed count, independent of --steps), GB/s of K+V bytes per
+    whole call and per partial-kernel launch, and the partial kernel's fraction of 8 TB/s
+    (from the median round)."""
+    b = DecodeBench(spec, seed, **kw)
+    for _ in range(warmup):
+        b.call()
+    r = b.rounds(rounds, n)
+    res = {"workload": what, "kv_bytes_per_call": b.kvb, "seed": seed,
+           "pool_copies_rotated": b.copies, **r,
+           "gbs": round(b.kvb / (r["us_per_call_median"] * 1e-6) / 1e9, 1),
+           "partial_gbs": round(b.kvb / (r["partial_us_median"] * 1e-6) / 1e9, 1),
+           "roofline_frac": round(b.kvb / (r["partial_us_median"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+           "plan": b.plan.describe()}
+    log(f"[bench] {what}: {r['us_per_call_median']:.2f} us/call, partial "
+        f"{r['partial_us_median']:.2f} us, frac {res['roofline_frac']:.3f}")
+    b.release()
+    return res
 
 
 def time_decode(spec, seed, steps, warmup, bps=0, reducer="auto", schedule="auto",
                 wgs_per_cu=0):
-    """Generate one problem, rotate pool copies past the Infinity Cache, and return
-    (us per decode call, us per partial kernel, K+V bytes, plan description)."""
-    import numpy as np
-    import torch
-    import quantized_kv_cache_page_amd as skvd
-    import workloads
-    prob = workloads.generate(spec, seed)
-    kvb = workloads.kv_bytes(prob)
-    dev = torch.device("cuda:0")
-
-    def up(x):
-        return None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(dev)
-
-    q, table, kv_len = up(prob["q"]), up(prob["page_table"]), up(prob["kv_len"])
-    pools = [up(prob[k]) for k in ("k_pages", "v_pages", "k_scales", "v_scales")]
-    copies = max(1, math.ceil(2 * MALL_BYTES / max(kvb, 1)) + 1)
-    sets = [pools] + [[None if p is None else p.clone() for p in pools] for _ in range(copies - 1)]
-    plan = skvd.Plan(spec.num_qo_heads, spec.num_kv_heads, spec.head_dim, spec.page_size,
-                     spec.kv_dtype, spec.batch, spec.q_per_seq, spec.max_kv_len, device=0,
-                     force_blocks_per_split=bps, force_reducer=reducer, schedule=schedule,
-                     wgs_per_cu=wgs_per_cu)
-    plan.ensure_workspace()
-    out = torch.empty(q.shape, dtype=torch.float16, device=dev)
-    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
-
-    def call(i, stage="all", events=None):
-        k, v, ks, vs = sets[i % copies]
-        plan.run(q, k, v, table, kv_len, prob["sm_scale"], ks, vs, out=out, lse=lse,
-                 q_per_seq=spec.q_per_seq, stage=stage, events=events)
-
-    for i in range(warmup):
-        call(i)
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    for a, b in ev:  # recording once creates the HIP events the partial dispatch stamps
-        a.record()
-        b.record()
-    for i in range(steps):
-        call(i, "partial", events=ev[i])
-        call(i, "merge")
-    torch.cuda.synchronize()
-    part_us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(steps):
-        call(i)
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps * 1e3, part_us, kvb, plan.describe()
+    """(us per decode call, us per partial kernel launch, K+V bytes, plan description): steps
+    back-to-back launches of each."""
+    b = DecodeBench(spec, seed, bps=bps, reducer=reducer, schedule=schedule,
+                    wgs_per_cu=wgs_per_cu)
+    for _ in range(warmup):
+        b.call()
+    us = b.timed(steps, "all")
+    part = b.timed(steps, "partial")
+    kvb, plan = b.kvb, b.plan.describe()
+    b.release()
+    return us, part, kvb, plan
 
 
 def sweep(args):
@@ -231,9 +355,10 @@ def sweep(args):
 APPEND_METRIC = "append µs/call and achieved HBM GB/s (new K/V rows read + cache written) vs roofline"
 
 
-def time_append(name, seed, steps, warmup):
+def time_append(name, seed, steps, warmup, rounds=1):
     """Time skvd_append on one append workload: pools and new rows resident in HBM, copies
-    rotated past the Infinity Cache. Returns a dict of measurements and the problem."""
+    rotated past the Infinity Cache; `rounds` timed rounds of `steps` calls (us_per_call is the
+    median round, us_min the fastest). Returns a dict of measurements and the problem."""
     import numpy as np
     import torch
     import quantized_kv_cache_page_amd as skvd
@@ -267,13 +392,16 @@ def time_append(name, seed, steps, warmup):
     # calls: the append is one kernel and the only work in the region, so the average is its
     # launch duration plus the dispatch gap (within 0.1 us of rocprofv3's kernel trace; marker
     # pairs around each launch would add ~4 us of their own).
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(steps):
-        call(i)
-    e1.record()
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) / steps * 1e3
+    per_round = []
+    for _ in range(rounds):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            call(i)
+        e1.record()
+        torch.cuda.synchronize()
+        per_round.append(e0.elapsed_time(e1) / steps * 1e3)
+    us = float(np.median(per_round))
     k_us = us
     # reference: a plain device-to-device copy of 256 MiB (read + write bytes) on the same GPU
     src = torch.ones(2 ** 28, dtype=torch.uint8, device=dev)
@@ -291,7 +419,8 @@ def time_append(name, seed, steps, warmup):
     workload = (f"{spec.name}: {new['k_new'].shape[0]} new tokens ({n} per sequence x "
                 f"{spec.batch}) Hkv={spec.num_kv_heads} D={spec.head_dim} P={spec.page_size} "
                 f"kv={spec.kv_dtype}, random order, permuted pages")
-    return dict(workload=workload, us_per_call=us, kernel_avg_us=k_us, bytes=nbytes,
+    return dict(workload=workload, us_per_call=us, us_min=min(per_round), kernel_avg_us=k_us,
+                bytes=nbytes, rounds=rounds,
                 gbs=nbytes / (us * 1e-6) / 1e9, achieved=nbytes / (k_us * 1e-6) / 1e9,
                 copies=copies, seed=seed, copy_ref_gbs=copy_gbs), prob, new
 
@@ -339,9 +468,10 @@ PREFILL_METRIC = ("prefill µs/call and achieved TFLOP/s (causal attention FLOPs
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense f16 matrix peak
 
 
-def time_prefill(name, seed, steps, warmup):
+def time_prefill(name, seed, steps, warmup, rounds=1):
     """Time skvd_prefill on one prefill workload (inputs resident in HBM; compute-bound, so no
-    copies rotate). Returns measurements and the problem."""
+    copies rotate); `rounds` timed rounds of `steps` calls (us_per_call is the median round).
+    Returns measurements and the problem."""
     import numpy as np
     import torch
     import quantized_kv_cache_page_amd as skvd
@@ -370,18 +500,21 @@ def time_prefill(name, seed, steps, warmup):
         call()
     torch.cuda.synchronize()
     # one event pair on the launching stream around back-to-back calls (one kernel each)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        call()
-    e1.record()
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) / steps * 1e3
+    per_round = []
+    for _ in range(rounds):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        per_round.append(e0.elapsed_time(e1) / steps * 1e3)
+    us = float(np.median(per_round))
     workload = (f"{spec.name}: B={spec.batch} prompts of T={spec.q_per_seq} tokens over "
                 f"kv_len={spec.lens[1]} (full causal), Hq={spec.num_qo_heads} "
                 f"Hkv={spec.num_kv_heads} D={spec.head_dim} P={spec.page_size} kv={spec.kv_dtype}")
-    return dict(workload=workload, us_per_call=us, flops=flops,
-                tflops=flops / (us * 1e-6) / 1e12, seed=seed), prob
+    return dict(workload=workload, us_per_call=us, us_min=min(per_round), flops=flops,
+                rounds=rounds, tflops=flops / (us * 1e-6) / 1e12, seed=seed), prob
 
 
 def cpu_baseline_prefill(prob, budget_s=10.0, nrows=256):
@@ -534,10 +667,11 @@ def main():
     ap.add_argument("--append", default="prefill_i8",
                     help="append workload for --op append: prefill_i8, prefill_f16, prefill_f8, decode_i8")
     ap.add_argument("--no-append", action="store_true",
-                    help="leave the append and prefill objects out of the decode line")
+                    help="leave the extra objects (other workloads, depth points, fp8, append, "
+                         "prefill) out of the decode line")
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--config", type=int, default=5)
     ap.add_argument("--kv", choices=["f16", "i8", "f8"], default=None,
                     help="cache format in place of the config's own (f8: OCP E4M3 with one f32 "
                          "scale per tensor)")
@@ -595,119 +729,52 @@ def main():
     if args.kv and args.kv != spec.kv_dtype:
         spec = dataclasses.replace(spec, kv_dtype=args.kv, name=f"{spec.name}_{args.kv}")
     seed = args.config if args.seed is None else args.seed
-    t0 = time.time()
-    prob = workloads.generate(spec, seed)
-    log(f"[bench] generated config {args.config} ({spec.name}) in {time.time() - t0:.1f}s")
-    kvb = workloads.kv_bytes(prob)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-
-    def up(x):
-        return None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(dev)
-
-    q = up(prob["q"])
-    table = up(prob["page_table"])
-    kv_len = up(prob["kv_len"])
-    pools = [up(prob[k]) for k in ("k_pages", "v_pages", "k_scales", "v_scales")]
-    if args.layout == "hnd":
-        pools = [None if p is None else p.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
-                 for p in pools]
-    pool_bytes = sum(p.numel() * p.element_size() for p in pools if p is not None)
-    copies = args.copies or max(1, math.ceil(2 * MALL_BYTES / max(kvb, 1)) + 1)
-    sets = [pools] + [[None if p is None else p.clone() for p in pools] for _ in range(copies - 1)]
-    log(f"[bench] K+V bytes/call {kvb / 2**20:.1f} MiB, pools {pool_bytes / 2**20:.1f} MiB x "
-        f"{copies} copies")
-
-    plan = skvd.Plan(spec.num_qo_heads, spec.num_kv_heads, spec.head_dim, spec.page_size,
-                     spec.kv_dtype, spec.batch, spec.q_per_seq, spec.max_kv_len, device=0,
-                     force_blocks_per_split=args.bps, force_reducer=args.reducer,
-                     schedule=args.schedule, wgs_per_cu=args.wgs_per_cu,
-                     heads_per_wg=args.heads_per_wg)
-    plan.ensure_workspace()
-    log(f"[bench] {plan.describe()}")
-    out = torch.empty(q.shape, dtype=torch.float16, device=dev)
-    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
-
-    def call(i, stage="all", events=None):
-        k, v, ks, vs = sets[i % copies]
-        plan.run(q, k, v, table, kv_len, prob["sm_scale"], ks, vs, out=out, lse=lse,
-                 q_per_seq=spec.q_per_seq, stage=stage, events=events)
-
-    for i in range(args.warmup):
-        call(i)
+    torch.cuda.set_device(0)
+    b = DecodeBench(spec, seed, bps=args.bps, reducer=args.reducer, schedule=args.schedule,
+                    wgs_per_cu=args.wgs_per_cu, heads_per_wg=args.heads_per_wg,
+                    layout=args.layout, copies=args.copies)
+    kvb = b.kvb
+    log(f"[bench] config {args.config} ({spec.name}) set up in {b.setup_s:.1f}s: K+V bytes/call "
+        f"{kvb / 2**20:.1f} MiB, {b.copies} pool copies rotated")
+    log(f"[bench] {b.plan.describe()}")
+    # Three interleaved rounds of 50 whole calls, 50 partial launches and 50 graph-replayed
+    # calls (min / median of each); they also bring the GPU to its steady clocks and the pools'
+    # translations into the caches before the timed steps (the first ~25 calls after the
+    # upload run up to 15 % slower).
+    rr = b.rounds(3, 50, graph=True)
+    log(f"[bench] rounds: call {rr['us_per_call_min']:.2f}/{rr['us_per_call_median']:.2f}, "
+        f"partial {rr['partial_us_min']:.2f}/{rr['partial_us_median']:.2f}, graph "
+        f"{rr['graph_replay_us_min']:.2f}/{rr['graph_replay_us_median']:.2f} us (min/median)")
+    for _ in range(args.warmup):
+        b.call()
     torch.cuda.synchronize()
 
-    # Timed region: K steps, each one decode = partial stage + merge stage on the current
-    # stream. Each partial launch stamps its own begin and end into an event pair (the
-    # dispatch's timestamps, skvd_decode_partial_timed), so no marker packet sits between the
-    # kernels; the pairs are recorded once beforehand, which creates them.
+    # Timed region: exactly K whole decode calls (partial kernel + reducer) back to back on the
+    # current stream, bracketed by synchronizations and one event pair.
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
-    for e0, e1 in ev:
-        e0.record()
-        e1.record()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
-    for i in range(K):
-        call(i, "partial", events=ev[i])
-        call(i, "merge")
+    for _ in range(K):
+        b.call()
     stop.record()
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    ms_step = total_ms / K
-    part_ms = [a.elapsed_time(b) for a, b in ev]
-    part_avg = float(np.mean(part_ms))
-
-    # A second timed pass of whole skvd_decode calls (no events in between) for µs/call.
-    start2, stop2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start2.record()
-    for i in range(K):
-        call(i)
-    stop2.record()
-    torch.cuda.synchronize()
-    ms_call = start2.elapsed_time(stop2) / K
-    log(f"[bench] decode {ms_call * 1e3:.2f} us/call (staged {ms_step * 1e3:.2f}), partial "
-        f"kernel avg {part_avg * 1e3:.2f} us (min {min(part_ms) * 1e3:.2f})")
-
-    # The same calls replayed from a HIP graph (50 decodes captured once), three interleaved
-    # rounds of eager and graph timing: min and median per call of each.
-    n_graph = 50
-    graph = torch.cuda.CUDAGraph()
-    gstream = torch.cuda.Stream()
-    gstream.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(gstream):
-        call(0)  # warm the side stream
-    torch.cuda.current_stream().wait_stream(gstream)
-    torch.cuda.synchronize()
-    with torch.cuda.graph(graph):
-        for i in range(n_graph):
-            call(i)
-    eager_us, graph_us = [], []
-    for _ in range(3):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(n_graph):
-            call(i)
-        e1.record()
-        torch.cuda.synchronize()
-        eager_us.append(e0.elapsed_time(e1) / n_graph * 1e3)
-        e0.record()
-        graph.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        graph_us.append(e0.elapsed_time(e1) / n_graph * 1e3)
-    del graph
-    log(f"[bench] eager {min(eager_us):.2f}/{float(np.median(eager_us)):.2f} us/call, graph "
-        f"replay {min(graph_us):.2f}/{float(np.median(graph_us)):.2f} (min/median of 3)")
+    ms_call = start.elapsed_time(stop) / K
+    # The dominant kernel: max(K, 50) partial-kernel launches back to back (each launch's time
+    # includes the dispatch gap to the next, so this is an upper bound of the kernel duration;
+    # it agrees with rocprofv3's kernel trace within 1-2 %).
+    nk = max(K, 50)
+    part_us = b.timed(nk, "partial")
+    log(f"[bench] decode {ms_call * 1e3:.2f} us/call over {K} calls; partial kernel "
+        f"{part_us:.2f} us per launch over {nk} launches")
+    plan_desc = b.plan.describe()
+    b.release()
 
     stream_gbs = None
     if not args.no_stream_ref:
         # Reference: the library's plain streaming read of 2 GiB on the same GPU.
-        buf = torch.ones(2 ** 31, dtype=torch.uint8, device=dev)
-        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        buf = torch.ones(2 ** 31, dtype=torch.uint8, device="cuda:0")
+        sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
         for _ in range(3):
             skvd.stream_read(buf, sink)
         torch.cuda.synchronize()
@@ -719,62 +786,89 @@ def main():
         torch.cuda.synchronize()
         stream_gbs = buf.numel() / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9
         del buf
+        torch.cuda.empty_cache()
         log(f"[bench] streaming-read reference: {stream_gbs:.0f} GB/s")
     gbs = kvb / (ms_call * 1e-3) / 1e9
-    achieved = kvb / (part_avg * 1e-3) / 1e9
-    workload = (f"{spec.name} (config {args.config}, {args.layout.upper()} pools): B={spec.batch} T={spec.q_per_seq} "
-                f"Hq={spec.num_qo_heads} Hkv={spec.num_kv_heads} D={spec.head_dim} "
-                f"P={spec.page_size} kv={spec.kv_dtype} lens={spec.lens}")
-    traffic = measured_traffic(spec.name)
+    achieved = kvb / (part_us * 1e-6) / 1e9
+    workload = (f"{spec.name} (workload {args.config}, {args.layout.upper()} pools): "
+                f"B={spec.batch} T={spec.q_per_seq} Hq={spec.num_qo_heads} "
+                f"Hkv={spec.num_kv_heads} D={spec.head_dim} P={spec.page_size} "
+                f"kv={spec.kv_dtype} lens={spec.lens}")
     res = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms_call, 5),
         "us_per_call": round(ms_call * 1e3, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f16", "data": "synthetic",
         "config": {"workload": workload, "seed": seed, "kv_bytes_per_call": kvb,
-                   "pool_copies_rotated": copies, "plan": plan.describe()},
-        "timing_rounds": {"eager_us_min": round(min(eager_us), 3),
-                          "eager_us_median": round(float(np.median(eager_us)), 3),
-                          "graph_replay_us_min": round(min(graph_us), 3),
-                          "graph_replay_us_median": round(float(np.median(graph_us)), 3),
-                          "calls_per_round": n_graph, "rounds": 3},
+                   "pool_copies_rotated": b.copies, "plan": plan_desc,
+                   "arithmetic": "f16 MFMA / dot products with f32 accumulation over K/V "
+                                 "widened exactly to f16 (int8: per-group scales applied in "
+                                 "f32)"},
+        "timing_rounds": rr,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "partial_kernel",
-                     "kernel_avg_us": round(part_avg * 1e3, 3),
+                     "traffic": measured_traffic(spec.name), "kernel": "partial_kernel",
+                     "kernel_avg_us": round(part_us, 3),
+                     "kernel_timing": f"{nk} back-to-back launches, one HIP event pair on the "
+                                      f"launching stream",
                      "stream_read_ref_gbs": None if stream_gbs is None else round(stream_gbs, 1),
-                     "frac_of_stream_read": None if stream_gbs is None else round(achieved / stream_gbs, 4),
+                     "frac_of_stream_read": None if stream_gbs is None
+                     else round(achieved / stream_gbs, 4),
                      "algorithmic_bytes_per_launch": kvb},
         "cpu_baseline": None,
     }
     if not args.no_append:
-        r, _, _ = time_append("prefill_i8", 40, min(K, 100), min(args.warmup, 10))
+        # the other workloads and the pages' depth points, each as min / median of three
+        # interleaved rounds of a fixed launch count
+        objs = {}
+        for c in (2, 3, 4):
+            if c != args.config:
+                sp = workloads.config(c)
+                objs[f"workload{c}"] = decode_object(
+                    sp, c, f"{sp.name}: B={sp.batch} T={sp.q_per_seq} Hq={sp.num_qo_heads} "
+                           f"Hkv={sp.num_kv_heads} D={sp.head_dim} P={sp.page_size} "
+                           f"kv={sp.kv_dtype} lens={sp.lens}")
+        res["workloads"] = objs
+        cliff = {}
+        for L in (2000, 2048, 2100, 8192):
+            sp = workloads.spec(name=f"cliff_{L}", batch=32, q_per_seq=1, num_qo_heads=32,
+                                num_kv_heads=8, head_dim=128, page_size=16, lens=("fixed", L))
+            cliff[str(L)] = decode_object(sp, 100 + L % 97, f"B=32 32/8 heads D=128 P=16 f16, "
+                                                             f"kv_len {L}")
+        g = [cliff[str(L)]["gbs"] for L in (2000, 2048, 2100)]
+        res["cliff"] = {"points": cliff, "gbs_2000_2048_2100": g,
+                        "max_dip_between_adjacent": round(max(0.0, 1 - g[1] / g[0],
+                                                              1 - g[2] / g[1]), 4)}
+        longp = {}
+        for L in (8192, 32768, 131072):
+            sp = workloads.spec(name=f"long_{L}", batch=1, q_per_seq=1, num_qo_heads=32,
+                                num_kv_heads=8, head_dim=128, page_size=64, lens=("fixed", L),
+                                q_mult=2.0)
+            longp[str(L)] = decode_object(sp, 100 + L % 97, f"B=1 32/8 heads D=128 P=64 f16, "
+                                                             f"kv_len {L}, q x2")
+        res["long_context"] = longp
+        # the int8 batch's shape over an fp8 (E4M3, per-tensor scales) cache
+        s8 = workloads.config(5)
+        s8 = dataclasses.replace(s8, kv_dtype="f8", name=f"{s8.name}_f8")
+        res["fp8"] = decode_object(s8, 5, f"{s8.name}: the int8 batch's shape over OCP E4M3 "
+                                          f"pools with one f32 scale per tensor")
+        r, _, _ = time_append("prefill_i8", 40, 50, 10, rounds=3)
         res["append"] = {"workload": r["workload"], "us_per_call": round(r["us_per_call"], 3),
-                         "gbs": round(r["gbs"], 1), "kernel_avg_us": round(r["kernel_avg_us"], 3),
+                         "us_min": round(r["us_min"], 3), "rounds": 3, "launches_per_round": 50,
+                         "gbs": round(r["gbs"], 1),
                          "roofline_frac": round(r["achieved"] / HBM_PEAK_GBS, 4),
                          "bytes_per_call": r["bytes"]}
         log(f"[bench] append {r['us_per_call']:.2f} us/call, {r['gbs']:.0f} GB/s")
-        # the multi-token route on the int8 prompts (4 x 2048 tokens, full causal)
-        rp, _ = time_prefill("prompt_i8", 50, min(K, 100), min(args.warmup, 10))
+        rp, _ = time_prefill("prompt_i8", 50, 50, 10, rounds=3)
         res["prefill"] = {"workload": rp["workload"], "us_per_call": round(rp["us_per_call"], 3),
-                          "tflops": round(rp["tflops"], 1),
+                          "us_min": round(rp["us_min"], 3), "rounds": 3,
+                          "launches_per_round": 50, "tflops": round(rp["tflops"], 1),
                           "roofline_frac": round(rp["tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
                           "bound": "mfma", "flops_per_call": rp["flops"]}
         log(f"[bench] prefill {rp['us_per_call']:.2f} us/call, {rp['tflops']:.0f} TFLOP/s")
-        # the decode over an fp8 (E4M3, per-tensor scales) cache of the int8 batch's shape
-        s8 = workloads.config(5)
-        s8 = dataclasses.replace(s8, kv_dtype="f8", name=f"{s8.name}_f8")
-        us8, part8, kvb8, plan8 = time_decode(s8, 5, min(K, 100), args.warmup)
-        res["fp8"] = {"workload": f"{s8.name}: int8 batch's shape (B=64, Zipf lengths) over OCP "
-                                  f"E4M3 pools with one f32 scale per tensor",
-                      "us_per_call": round(us8, 3), "partial_us": round(part8, 3),
-                      "gbs": round(kvb8 / (us8 * 1e-6) / 1e9, 1),
-                      "roofline_frac": round(kvb8 / (part8 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                      "kv_bytes_per_call": kvb8, "plan": plan8}
-        log(f"[bench] fp8 decode {us8:.2f} us/call, partial {part8:.2f} us")
     if not args.no_cpu:
         log("[bench] timing the CPU oracle ...")
-        res["cpu_baseline"] = cpu_baseline(prob)
+        res["cpu_baseline"] = cpu_baseline(b.prob)
     print(json.dumps(res), flush=True)
 
 
