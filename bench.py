@@ -183,13 +183,16 @@ class DecodeBench:
         dev = torch.device("cuda:0")
 
         def up(x):
-            return None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+            return None if x is None else torch.from_numpy(x).to(dev)  # (keeps the strides)
 
         self.q, self.table, self.kv_len = (up(self.prob[k]) for k in ("q", "page_table", "kv_len"))
         pools = [up(self.prob[k]) for k in ("k_pages", "v_pages", "k_scales", "v_scales")]
-        if layout == "hnd":
+        if layout in ("hnd", "hnd_scales"):
+            # HND: each KV head's page rows contiguous, passed through the same strides;
+            # hnd_scales: only the int8 scale pools so
             pools = [None if p is None else p.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
-                     if p.dim() == 4 else p for p in pools]
+                     if p.dim() == 4 and (layout == "hnd" or i >= 2) else p
+                     for i, p in enumerate(pools)]
         self.copies = copies or max(1, math.ceil(2 * MALL_BYTES / max(self.kvb, 1)) + 1)
         self.sets = [pools] + [[None if p is None else p.clone() for p in pools]
                                for _ in range(self.copies - 1)]
@@ -370,7 +373,7 @@ def time_append(name, seed, steps, warmup, rounds=1):
     dev = torch.device("cuda:0")
 
     def up(x):
-        return None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+        return None if x is None else torch.from_numpy(x).to(dev)  # (keeps the strides)
 
     table = up(prob["page_table"])
     base = [up(new[k]) for k in ("k_new", "v_new")] + \
@@ -482,7 +485,7 @@ def time_prefill(name, seed, steps, warmup, rounds=1):
     dev = torch.device("cuda:0")
 
     def up(x):
-        return None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+        return None if x is None else torch.from_numpy(x).to(dev)  # (keeps the strides)
 
     t = {k: up(prob[k]) for k in ("q", "k_pages", "v_pages", "k_scales", "v_scales",
                                   "page_table", "kv_len")}
@@ -685,7 +688,7 @@ def main():
     ap.add_argument("--wgs-per-cu", type=int, default=0,
                     help="balanced schedule: partial-kernel workgroups per CU (0: plan default)")
     ap.add_argument("--copies", type=int, default=0, help="pool copies to rotate (0: auto)")
-    ap.add_argument("--layout", choices=["nhd", "hnd"], default="nhd",
+    ap.add_argument("--layout", choices=["nhd", "hnd", "hnd_scales"], default="nhd",
                     help="pool layout: nhd = [pages, P, Hkv, D] (the workload's); hnd = each KV "
                          "head's page rows contiguous, passed through the same strides")
     ap.add_argument("--no-stream-ref", action="store_true")
@@ -737,14 +740,12 @@ def main():
     log(f"[bench] config {args.config} ({spec.name}) set up in {b.setup_s:.1f}s: K+V bytes/call "
         f"{kvb / 2**20:.1f} MiB, {b.copies} pool copies rotated")
     log(f"[bench] {b.plan.describe()}")
-    # Three interleaved rounds of 50 whole calls, 50 partial launches and 50 graph-replayed
-    # calls (min / median of each); they also bring the GPU to its steady clocks and the pools'
-    # translations into the caches before the timed steps (the first ~25 calls after the
-    # upload run up to 15 % slower).
-    rr = b.rounds(3, 50, graph=True)
+    # Three interleaved rounds of 50 whole calls and 50 partial launches (min / median of each);
+    # they also bring the GPU to steady state before the timed steps: the first ~20 calls after
+    # the upload, and the first calls after a HIP graph is torn down, run up to 15 % slower.
+    rr = b.rounds(3, 50)
     log(f"[bench] rounds: call {rr['us_per_call_min']:.2f}/{rr['us_per_call_median']:.2f}, "
-        f"partial {rr['partial_us_min']:.2f}/{rr['partial_us_median']:.2f}, graph "
-        f"{rr['graph_replay_us_min']:.2f}/{rr['graph_replay_us_median']:.2f} us (min/median)")
+        f"partial {rr['partial_us_min']:.2f}/{rr['partial_us_median']:.2f} us (min/median)")
     for _ in range(args.warmup):
         b.call()
     torch.cuda.synchronize()
@@ -767,6 +768,11 @@ def main():
     part_us = b.timed(nk, "partial")
     log(f"[bench] decode {ms_call * 1e3:.2f} us/call over {K} calls; partial kernel "
         f"{part_us:.2f} us per launch over {nk} launches")
+    # Graph replay last: 50 decodes captured in one HIP graph, replayed in three rounds.
+    gr = [b.graph_replay(50) for _ in range(3)]
+    rr["graph_replay_us_min"] = round(min(gr), 3)
+    rr["graph_replay_us_median"] = round(float(np.median(gr)), 3)
+    log(f"[bench] graph replay {min(gr):.2f}/{float(np.median(gr)):.2f} us (min/median)")
     plan_desc = b.plan.describe()
     b.release()
 

@@ -84,7 +84,6 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
     return fail(err, errn, SKVD_ERR_PLAN, "wgs_per_cu=%d outside 0..64", prm.wgs_per_cu);
   // KV heads per workgroup: the single-quarter variants at D=128 come in 1, 2, 4 and 8.
   const bool multi_head_ok = D == 128 && G * prm.max_q_per_seq <= 4;
-  const bool i8_kv = prm.kv_dtype == SKVD_KV_I8_F16SCALE32;
   int hw = prm.heads_per_wg;
   // A decode with no more (sequence, KV head, block) units than CUs is latency-bound: one
   // head per workgroup spreads it over the most CUs (measured: B=1, 1024 tokens, 12.5 vs 13.8
@@ -92,7 +91,6 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
   const int64_t units_all = (int64_t)prm.max_batch * Hkv * ((prm.max_kv_len + 63) / 64);
   if (hw == 0)
     hw = !multi_head_ok || units_all <= num_cus ? 1
-         : (i8_kv && Hkv % 8 == 0) ? 8
          : Hkv % 4 == 0 ? 4
          : Hkv % 2 == 0 ? 2
          : 1;
@@ -176,22 +174,21 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
   if (sched == SKVD_SCHEDULE_BALANCED) {
     // Workgroups per CU (measured on MI355X): one wave per SIMD saturates the memory pipes of
     // an f16 stream, best as one workgroup of 4 KV heads reading each token row's heads
-    // together; int8 at D=128 also needs vector-ALU throughput, so two waves per SIMD: one
-    // workgroup of 8 KV heads at a time, two per CU in two rounds (the registers hold one), so
-    // that the dispatcher hands each CU its second share when it frees up.
-    // fp8 (no per-row scale loads) does best with twelve waves per CU, as three workgroups of
-    // 4 KV heads (measured, two interleaved rounds: GQA batch 44.6 us/call against 46.4 with
-    // 8 heads x 1 and 45.1 with 4 x 2; the int8 batch's shape 521.9 against 530.5 and 530.2;
-    // int8's 8 x 2 ran the GQA batch at 55.7).
-    const bool i8 = prm.kv_dtype == SKVD_KV_I8_F16SCALE32;
-    const bool f8 = prm.kv_dtype == SKVD_KV_FP8_E4M3;
+    // together. The one-byte formats widen every element on the vector ALU and do best with
+    // three waves per SIMD, as three workgroups of 4 KV heads: fp8 on the GQA batch 44.6
+    // us/call against 46.4 with 8 heads x 1 and 45.1 with 4 x 2, on the int8 batch's shape
+    // 521.9 against 530.5 and 530.2; int8 on the int8 batch with head-major scale pools
+    // (each head's scales of a page contiguous, so a 16-token tile's scales are one 128-byte
+    // line) 560.7 us against 586.6 with 8 heads x 1, 592.7 with 8 x 2 (two rounds), 585.1 with
+    // 4 x 2 and 580.8 with 2 x 6 (token-major scale pools: 617 with 4 x 3, whose twelve waves
+    // per CU each touch 32 lines for a chunk's 256 bytes of scales).
+    const bool byte = prm.kv_dtype != SKVD_KV_F16;
     // D = 256 variants hold one wave per SIMD (over 256 registers with the accumulators): f16,
     // a pure stream, does best with three workgroups per CU (the wide multi-token workload 527
     // us against 537 with four); the one-byte formats widen every element and need all four
     // SIMDs (fp8: 604.7 -> 460.9 us with four, int8: 640.5 -> 484.2)
     const int auto_wpc = D == 256 ? (prm.kv_dtype == SKVD_KV_F16 ? 3 : 4)
-                         : p.row_blocks == 1 ? (f8   ? std::max(1, 12 / hw)
-                                                : i8 ? (hw == 8 ? 2 : 8 / hw)
+                         : p.row_blocks == 1 ? (byte ? std::max(1, 12 / hw)
                                                      : std::max(1, kDefaultWgsPerCu / hw))
                                              : kDefaultWgsPerCu;
     // several row-tile waves per workgroup (more than 16 query rows per KV head): the same

@@ -95,18 +95,18 @@ def test_schedule_choice():
     w = plan(wgs_per_cu=7, num_cus=100)
     assert w.schedule == "balanced" and w.info.grid_wgs == 700 and w.info.heads_per_wg == 4
     assert "schedule=balanced" in w.describe()
-    # defaults per variant: 4 per CU, 3 at head_dim 256; int8 single-quarter tiles: workgroups
-    # of 8 KV heads, two per CU (else 4 or 2 heads, 8 waves per CU)
+    # defaults per variant: 4 per CU, 3 at head_dim 256; one-byte single-quarter tiles:
+    # workgroups of 4 KV heads, three per CU (else 2 or 1 heads, 12 waves per CU)
     assert plan(head_dim=256, num_kv_heads=16).info.grid_wgs == 3 * 256
     i8 = plan(kv_dtype="i8")
-    assert i8.info.heads_per_wg == 8 and i8.info.grid_wgs == 2 * 256
+    assert i8.info.heads_per_wg == 4 and i8.info.grid_wgs == 3 * 256
     i8_4 = plan(kv_dtype="i8", num_kv_heads=4, num_qo_heads=16)
-    assert i8_4.info.heads_per_wg == 4 and i8_4.info.grid_wgs == 2 * 256
-    assert plan(kv_dtype="i8", heads_per_wg=4).info.grid_wgs == 2 * 256
+    assert i8_4.info.heads_per_wg == 4 and i8_4.info.grid_wgs == 3 * 256
+    assert plan(kv_dtype="i8", heads_per_wg=8).info.grid_wgs == 1 * 256
     assert plan(kv_dtype="i8", num_kv_heads=2, num_qo_heads=8).info.heads_per_wg == 2
     assert plan(heads_per_wg=8).info.grid_wgs == 256
     assert plan(kv_dtype="i8", num_kv_heads=3, num_qo_heads=12).info.heads_per_wg == 1
-    assert plan(kv_dtype="i8", heads_per_wg=1).info.grid_wgs == 8 * 256
+    assert plan(kv_dtype="i8", heads_per_wg=1).info.grid_wgs == 12 * 256
     assert plan(kv_dtype="i8", max_q_per_seq=2).info.grid_wgs == 4 * 256
     assert plan(kv_dtype="i8", max_q_per_seq=2).info.heads_per_wg == 1
     assert plan().info.heads_per_wg == 4 and plan().info.grid_wgs == 256
@@ -239,11 +239,11 @@ def test_decode_check_fp8(over, status):
 
 
 def test_fp8_plan_and_unsupported_routes():
-    """fp8 plans: 4 KV heads per workgroup, three workgroups per CU (int8: 8 heads); appends
-    and the multi-token route take the two tensor scales."""
+    """fp8 plans: 4 KV heads per workgroup, three workgroups per CU (as int8); appends and the
+    multi-token route take the two tensor scales."""
     p8, pi = plan(kv_dtype="f8"), plan(kv_dtype="i8")
-    assert p8.kv_dtype == "f8" and p8.info.heads_per_wg == 4 and pi.info.heads_per_wg == 8
-    assert "grid=768" in p8.describe()
+    assert p8.kv_dtype == "f8" and p8.info.heads_per_wg == 4 and pi.info.heads_per_wg == 4
+    assert "grid=768" in p8.describe() and "grid=768" in pi.describe()
     a = good_append_args(k_scales=FAKE + (2 << 32), v_scales=FAKE + (3 << 32))
     assert bd.skvd_append_check(p8.handle, a) == 0
     for over, st in ((dict(k_scales=None), 4), (dict(v_scales=FAKE + 2), 3),
@@ -358,13 +358,13 @@ def test_attention_routes_errors():
 
 def test_plan_waves_per_cu_by_format():
     """Workgroups per CU chosen per format (256 CUs): at head_dim 128 with one query-row quarter,
-    f16 4 KV heads x 1 workgroup, int8 8 x 2, fp8 4 x 3; at head_dim 256 (one wave per SIMD),
+    f16 4 KV heads x 1 workgroup, int8 and fp8 4 x 3; at head_dim 256 (one wave per SIMD),
     f16 three workgroups per CU, the one-byte formats four."""
     def grid(**kw):
         d = plan(**kw).describe()
         return int(d.split("grid=")[1].split()[0]), int(d.split("heads_per_wg=")[1].split()[0])
     assert grid(kv_dtype="f16") == (256, 4)
-    assert grid(kv_dtype="i8") == (512, 8)
+    assert grid(kv_dtype="i8") == (768, 4)
     assert grid(kv_dtype="f8") == (768, 4)
     wide = dict(num_qo_heads=32, num_kv_heads=16, head_dim=256, max_batch=8, max_q_per_seq=4,
                 max_kv_len=32768)

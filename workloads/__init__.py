@@ -1,7 +1,8 @@
 """Seeded synthetic inputs for paged decode attention.
 
 This module only builds inputs: it draws lengths, page permutations and N(0,1) values, and
-for the int8 cache it builds the stored int8 values and f16 scales from N(0,1) data, and for
+for the int8 cache it builds the stored int8 values and f16 scales from N(0,1) data (the
+scale pools stored head-major within each page, see head_major), and for
 the fp8 cache the E4M3 bytes of N(0,1) data under a drawn per-tensor scale. It holds
 none of the decode's arithmetic, so both the HIP path and the CPU oracle consume its arrays.
 
@@ -175,6 +176,13 @@ def _normal_int8(seed, stream, shape):
     return q, sc
 
 
+def head_major(sc: np.ndarray) -> np.ndarray:
+    """The same [pages, P, Hkv, D/32] scales stored head-major within each page (memory order
+    [pages, Hkv, P, D/32]): the int8 cache's scale layout, in which one KV head's scales of a
+    16-token tile are 128 contiguous bytes. Returns a strided view; the values are unchanged."""
+    return np.ascontiguousarray(sc.transpose(0, 2, 1, 3)).transpose(0, 2, 1, 3)
+
+
 def _normal_e4m3(seed, stream, shape, scale):
     """N(0,1) data (drawn as in _normal_f16) over a per-tensor scale, as E4M3 bytes: x / scale
     in f32, clipped to +-448, cast by torch to float8_e4m3fn (nearest even)."""
@@ -237,6 +245,7 @@ def generate(s: Spec, seed: int) -> dict:
     elif s.kv_dtype == "i8":
         k, ks = _normal_int8(seed, 4, (N, P, Hkv, D))
         v, vs = _normal_int8(seed, 5, (N, P, Hkv, D))
+        ks, vs = head_major(ks), head_major(vs)
     elif s.kv_dtype == "f8":
         ks, vs = fp8_scales(seed)
         k = _normal_e4m3(seed, 4, (N, P, Hkv, D), ks[0])
