@@ -369,13 +369,16 @@ skvd_status skvd_merge_states(const void *o_states, int64_t o_state_stride, int6
  * with one f32 scale s per tensor, AMD-Ecosystem/flashinfer PR #397 commit messages) stores for
  * each element the E4M3 value nearest to clip(x / s, -448, 448) (the quotient in f32, correctly
  * rounded; ties to the even mantissa; a NaN quotient stores 0); its scales are only read.
+ * Non-finite inputs: int8 -- a NaN element stores code 0 and is left out of its group's maximum;
+ * an infinite element gives its group the scale f16(inf) = inf and every code 0. fp8 -- NaN
+ * stores 0, +-inf saturates to +-448.
  *
  * - Written: exactly the K/V elements (and, int8, the scales) of the slots the tokens name.
  *   Nothing else; no workspace. k_new, v_new, batch_idx, positions and the table are read only.
  * - Skips (device-data contract, not checked with a synchronization): a token whose batch_idx is
  *   outside [0, batch) or whose position is outside [0, the plan's max_kv_len) writes nothing; a
  *   page id outside [0, num_k_pages) (or num_v_pages) skips that pool's write. Two tokens naming
- *   the same slot leave it undefined (no ordering between them). Inputs must be finite.
+ *   the same slot leave it undefined (no ordering between them).
  * - The pools may be any views the strides describe (K and V share page shape and strides, as
  *   for the decode), but must not overlap each other or the inputs.
  * - Graph capture: no allocation, synchronization or device-to-host read; one kernel launch.

@@ -387,11 +387,17 @@ int oracle_num_threads(void) {
  *                c = clip(rint(x / s), -127, 127), x / s in f32, rint to nearest even;
  *                s = 0 (an all-zero group, or a below f16's range) gives c = 0.
  *              The pages fix no precision for these decisions; f32 is the kernel's.
+ *              Non-finite inputs (the pages do not cover them; the plainest reading of the
+ *              formulas): a NaN element is not larger than any magnitude, so it leaves the
+ *              maximum alone, and its quotient is NaN, stored as code 0; an infinite element
+ *              makes a infinite, s = f16(inf) = inf, and every code 0 (finite / inf = 0,
+ *              inf / inf = NaN).
  *   W4 fp8     An fp8 cache (OCP E4M3 bytes times a per-tensor f32 scale s: k_scale for K,
  *              v_scale for V) stores for each element the E4M3 value nearest to
  *              clip(x / s, -448, 448), x / s the f32 quotient, ties to the even mantissa;
- *              a NaN quotient (0 / 0) stores 0. 448 is E4M3's largest finite value, so the
- *              clip saturates rather than overflowing. The pages name the format and its
+ *              a NaN quotient (0 / 0, or a NaN element) stores 0; an infinite one saturates
+ *              at +-448. 448 is E4M3's largest finite value, so the clip saturates rather
+ *              than overflowing. The pages name the format and its
  *              per-tensor scales only; the rule is the plainest one with the kernel's f32.
  * ============================================================================ */
 
@@ -425,6 +431,7 @@ uint16_t oracle_float_to_half(float x) {
   uint16_t sign = signbit(x) ? 0x8000 : 0;
   double a = fabs((double)x);
   if (isnan(x)) return (uint16_t)(sign | 0x7e00);
+  if (isinf(x)) return (uint16_t)(sign | 0x7c00);
   if (a == 0.0) return sign;
   int e2;
   frexp(a, &e2);          /* a = f * 2^e2, f in [0.5, 1): the binade is [2^(e2-1), 2^e2) */
@@ -463,6 +470,7 @@ void oracle_quantize_group(const uint16_t *x, int n, int8_t *codes, uint16_t *sc
 #endif
       if (c > 127.0f) c = 127.0f;
       if (c < -127.0f) c = -127.0f;
+      if (isnan(c)) c = 0.0f; /* NaN element, or an infinite one over an infinite scale */
     }
     codes[d] = (int8_t)c;
   }

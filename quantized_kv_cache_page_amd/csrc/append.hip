@@ -73,16 +73,18 @@ __device__ __forceinline__ uint2a quantize8(half8a x, _Float16 *scale) {
   bool near = false;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const float qc = __builtin_amdgcn_fmed3f(f[e] * rs, -127.0f, 127.0f);
+    const float q = f[e] * rs;
+    const float qc = __builtin_amdgcn_fmed3f(q, -127.0f, 127.0f);
     const float t = qc + kMagic;
-    c[e] = __float_as_uint(t) & 0xFFu;
+    // a NaN quotient (a NaN element, or an infinite one over an infinite scale) stores 0
+    c[e] = q != q ? 0u : __float_as_uint(t) & 0xFFu;
     near |= fabsf(qc - (t - kMagic)) > kNear;
   }
   if (near && s > 0.0f) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float qc = __builtin_amdgcn_fmed3f(f[e] * rs, -127.0f, 127.0f);
-      if (fabsf(qc - rintf(qc)) > kNear)
+      if (fabsf(qc - rintf(qc)) > kNear && f[e] == f[e])
         c[e] = (unsigned)(int)__builtin_amdgcn_fmed3f(rintf(f[e] / s), -127.0f, 127.0f) & 0xFFu;
     }
   }
@@ -136,7 +138,8 @@ __device__ __forceinline__ uint2a quantize_fp8(half8a x, float s) {
   for (int e = 0; e < 8; ++e) {
     f[e] = (float)x[e];
     q[e] = f[e] * r;
-    near |= e4m3_near_tie(q[e]);
+    // (a NaN quotient takes the software path, which stores 0: the hardware clamp would not)
+    near |= e4m3_near_tie(q[e]) || q[e] != q[e];
   }
   uint2a w;
 #pragma unroll

@@ -249,7 +249,35 @@ def check_skips(lib, seed=7, int8=True):
     return same and skipped == 5
 
 
+def check_non_finite(lib, seed=12):
+    """Non-finite inputs follow the formulas: f16 infinity converts like numpy's; a NaN element
+    is left out of the group maximum (the scale and the other codes are those of the group
+    without it) and stores code 0; an infinite element gives the scale f16(inf) and all codes
+    0."""
+    ok = lib.oracle_float_to_half(float("inf")) == np.float16(np.inf).view(np.uint16)
+    ok &= lib.oracle_float_to_half(float("-inf")) == np.float16(-np.inf).view(np.uint16)
+    rng = np.random.default_rng(seed)
+    x, c, sc = exact_groups(rng, (40, 32))
+    for i in range(x.shape[0]):
+        g = x[i].astype(np.float16)
+        j = int(rng.integers(32))
+        if int(np.abs(c[i, j])) == 127:
+            continue  # the maximum itself: removing it changes the scale
+        gn = g.copy()
+        gn[j] = np.float16(np.nan)
+        codes, s = _quant(lib, gn)
+        ref_codes, ref_s = _quant(lib, g)
+        ok &= codes[j] == 0 and s.view(np.uint16) == ref_s.view(np.uint16)
+        ok &= np.array_equal(np.delete(codes, j), np.delete(ref_codes, j))
+        gi = g.copy()
+        gi[j] = np.float16(np.inf if i % 2 else -np.inf)
+        codes, s = _quant(lib, gi)
+        ok &= bool(np.isinf(s)) and not codes.any()
+    return bool(ok)
+
+
 ALL_PINS = [
+    ("non_finite", check_non_finite),
     ("half_conversion", check_half_conversion),
     ("exact_groups", check_exact_groups),
     ("half_step_bound", check_half_step_bound),

@@ -128,7 +128,17 @@ def check_append_fp8(lib, seed=3):
     return bool(ok)
 
 
+def check_non_finite(lib):
+    """The rule's clip at +-448 makes an infinite quotient the nearest value to +-448 (the
+    largest finite E4M3 magnitude), and a NaN quotient stores 0."""
+    b = oracle.e4m3_from_float(np.array([np.inf, -np.inf, np.nan, 448.0, -448.0], np.float32),
+                               lib=lib)
+    v = oracle.e4m3_to_float(b[:2], lib=lib)
+    return bool(b[0] == b[3] and b[1] == b[4] and b[2] == 0 and v[0] == 448.0 and v[1] == -448.0)
+
+
 ALL_PINS = [
+    ("non_finite", check_non_finite),
     ("decode_all_bytes", check_decode_all_bytes),
     ("encode_against_torch", check_encode_against_torch),
     ("encode_special", check_encode_special),

@@ -104,8 +104,8 @@ def test_append_matches_oracle(case):
 
 def test_append_special_values():
     """Groups that stress the int8 rule: exact multiples of powers of two, quotients halfway
-    between integers, all-zero groups, groups whose scale underflows f16, f16 subnormals and
-    values near f16's maximum."""
+    between integers, all-zero groups, groups whose scale underflows f16, f16 subnormals,
+    values near f16's maximum, and NaN and infinite elements."""
     B, Hkv, D, P = 1, 2, 128, 16
     s = workloads.spec(name="special", batch=B, num_qo_heads=4, num_kv_heads=Hkv, head_dim=D,
                        page_size=P, kv_dtype="i8", lens=("list", (64,)))
@@ -133,8 +133,13 @@ def test_append_special_values():
                     x[i, h, g] = c * 2.0 ** -24
                 elif kind == 5:  # near f16's maximum
                     x[i, h, g] = rng.uniform(-65504, 65504, 32)
-                else:            # wide dynamic range in one group
+                elif kind == 6:  # wide dynamic range in one group
                     x[i, h, g] = rng.standard_normal(32) * 10.0 ** rng.uniform(-4, 4, 32)
+                else:            # non-finite elements: NaN (left out of the maximum, code 0),
+                    x[i, h, g] = c  # and on odd tokens an infinity (scale inf, codes 0)
+                    x[i, h, g, int(rng.integers(32))] = np.nan
+                    if i % 2:
+                        x[i, h, g, int(rng.integers(32))] = np.inf * (1 if h else -1)
     kn = x.reshape(N, Hkv, D).astype(np.float16)
     vn = (-x[:, ::-1]).reshape(N, Hkv, D).astype(np.float16)
     new = dict(k_new=kn, v_new=np.ascontiguousarray(vn), batch_idx=np.zeros(N, np.int32),
@@ -149,7 +154,8 @@ def test_append_special_values():
 def test_append_fp8_special_values(scale):
     """The fp8 rule at its edges: every E4M3 magnitude and every midpoint between neighbours
     (exact ties when the scale is a power of two), one f16 step either side, values past 448 *
-    scale (saturation), zeros of both signs and f16 subnormals."""
+    scale (saturation), zeros of both signs, f16 subnormals, NaN (stores 0) and infinities
+    (saturate)."""
     B, Hkv, D, P = 1, 2, 128, 16
     s = workloads.spec(name="special_f8", batch=B, num_qo_heads=4, num_kv_heads=Hkv, head_dim=D,
                        page_size=P, kv_dtype="f8", lens=("list", (64,)))
@@ -163,7 +169,8 @@ def test_append_fp8_special_values(scale):
     vals = np.concatenate([h, -h, np.nextafter(h, np.float16(np.inf)),
                            np.nextafter(h, np.float16(0)),
                            np.array([0.0, -0.0, 500 * scale, -600 * scale, 65504, -65504,
-                                     2.0 ** -24, -3 * 2.0 ** -24, 2.0 ** -14], np.float16)])
+                                     2.0 ** -24, -3 * 2.0 ** -24, 2.0 ** -14, np.nan, np.inf,
+                                     -np.inf, -np.nan], np.float16)])
     rng = np.random.default_rng(37)
     N = 64
     x = np.resize(rng.permutation(vals), 2 * N * Hkv * D).astype(np.float16)
