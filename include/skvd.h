@@ -123,7 +123,8 @@ typedef enum {
 typedef struct {
   int32_t num_qo_heads;   /* Hq; Hq % Hkv == 0 */
   int32_t num_kv_heads;   /* Hkv >= 1 */
-  int32_t head_dim;       /* D: 128 or 256 */
+  int32_t head_dim;       /* D: 128, 192, 256 or 512 (int8 caches: 128, 256 or 512; the
+                             multi-token route: 128 or 256) */
   int32_t page_size;      /* P: power of two, 1..1024 */
   int32_t max_batch;      /* B upper bound, >= 1 */
   int32_t max_q_per_seq;  /* T upper bound: 1..8 (G * T <= 1024 query rows per KV head: up to 16

@@ -16,9 +16,10 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libskvd.so")
-SOURCES = ["api.cpp", "plan.cpp", "kernels.hip", "partial_128_f16.hip", "partial_128_i8.hip",
-           "partial_128_f8.hip", "partial_256_f16.hip", "partial_256_i8.hip", "partial_256_f8.hip",
-           "append.hip", "prefill.hip", "cascade.hip"]
+PARTIAL = [f"partial_{d}_{f}.hip" for d in (128, 256, 512) for f in ("f16", "i8", "f8")] + \
+    ["partial_192_f16.hip", "partial_192_f8.hip"]
+SOURCES = ["api.cpp", "plan.cpp", "kernels.hip", *PARTIAL, "append.hip", "prefill.hip",
+           "cascade.hip"]
 ARCH = "gfx950"
 
 

@@ -123,6 +123,9 @@ skvd_status check_prefill(const skvd_plan *plan, const skvd_decode_args *a) {
                    p.prm.max_kv_len);
   if (p.group > 64)
     return set_err(SKVD_ERR_SHAPE, "prefill needs Hq/Hkv <= 64 (got %d)", p.group);
+  if (p.prm.head_dim != 128 && p.prm.head_dim != 256)
+    return set_err(SKVD_ERR_SHAPE, "the multi-token route supports head_dim 128 and 256 (plan "
+                   "has %d)", p.prm.head_dim);
   skvd_decode_args one = *a;
   one.q_per_seq = 1;  // the remaining checks do not depend on the token count
   return skvd::check_args(p, &one, p.ws_bytes, g_err, sizeof g_err);

@@ -277,8 +277,12 @@ int launch_append(AppendLaunch a, void *stream) {
   a.blocks = (unsigned)blocks;
   a.tok_step = (int)(blocks * 256 / a.lanes_per_token);
   hipStream_t st = (hipStream_t)stream;
-  if (a.D == 128) launch_d<128>(a, st);
-  else launch_d<256>(a, st);
+  switch (a.D) {
+    case 128: launch_d<128>(a, st); break;
+    case 192: launch_d<192>(a, st); break;
+    case 256: launch_d<256>(a, st); break;
+    default: launch_d<512>(a, st); break;
+  }
   return (int)hipGetLastError();
 }
 

@@ -90,16 +90,30 @@ struct MergeAcc {
   }
 };
 
+// One lane's slice of PER consecutive floats of a partial's output row (PER = D / 64: 2, 3, 4
+// or 8), with the widest loads its alignment allows.
 template <int PER>
-struct PerVecT;
-template <>
-struct PerVecT<2> {
-  typedef float __attribute__((ext_vector_type(2))) type;
-};
-template <>
-struct PerVecT<4> {
-  typedef float4v type;
-};
+__device__ __forceinline__ void load_slice(const float *p, float (&v)[PER]) {
+  if constexpr (PER % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < PER; i += 4) {
+      const float4v x = *(const float4v *)(p + i);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[i + k] = x[k];
+    }
+  } else if constexpr (PER % 2 == 0) {
+    typedef float float2v __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int i = 0; i < PER; i += 2) {
+      const float2v x = *(const float2v *)(p + i);
+      v[i] = x[0];
+      v[i + 1] = x[1];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) v[i] = p[i];
+  }
+}
 
 // Cooperative step: up to 64 partials (indices first, first + stride, ...) one per lane of this
 // wave. Each lane's (m, l) gives the wave max and sum; the lanes then walk the partials' output
@@ -109,7 +123,6 @@ template <int D>
 __device__ __forceinline__ void merge_lanes(const float *ml, const float *po, int64_t first,
                                             int64_t stride, int cnt, MergeAcc<D / 64> *out) {
   constexpr int PER = D / 64;
-  using PerVec = typename PerVecT<PER>::type;
   typedef float float2v __attribute__((ext_vector_type(2)));
   const int lane = threadIdx.x & 63;
   float2v mlv = {kNegInf, 0.f};
@@ -119,11 +132,16 @@ __device__ __forceinline__ void merge_lanes(const float *ml, const float *po, in
   const float S = wave_sum(w * mlv[1]);
   float acc[PER] = {};
   for (int k0 = 0; k0 < cnt; k0 += 8) {
-    PerVec ov[8];
+    float ov[8][PER];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      ov[j] = k0 + j < cnt ? *(const PerVec *)(po + (first + stride * (k0 + j)) * D + PER * lane)
-                           : (PerVec)0.f;
+    for (int j = 0; j < 8; ++j) {
+      if (k0 + j < cnt) {
+        load_slice<PER>(po + (first + stride * (k0 + j)) * D + PER * lane, ov[j]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) ov[j][i] = 0.f;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float wj = k0 + j < cnt ? readlane_f(w, k0 + j) : 0.f;
@@ -174,7 +192,6 @@ constexpr int kMergeWaves = 4;
 template <int D>
 __global__ __launch_bounds__(64) void merge_direct(LaunchArgs a) {
   constexpr int PER = D / 64;
-  using PerVec = typename PerVecT<PER>::type;
   const int64_t row = blockIdx.x;
   const RowParts rp = row_parts(a, row);
   const int n = rp.count;
@@ -182,12 +199,17 @@ __global__ __launch_bounds__(64) void merge_direct(LaunchArgs a) {
   for (int s = 0; s < n; ++s) M = fmaxf(M, a.ws_ml[2 * (rp.first + rp.stride * s)]);
   float S = 0.f, acc[PER] = {};
   for (int s0 = 0; s0 < n; s0 += 4) {
-    PerVec ov[4];
+    float ov[4][PER];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      ov[j] = s0 + j < n ? *(const PerVec *)(a.ws_o + (rp.first + rp.stride * (s0 + j)) * D +
-                                             PER * threadIdx.x)
-                         : (PerVec)0.f;
+    for (int j = 0; j < 4; ++j) {
+      if (s0 + j < n) {
+        load_slice<PER>(a.ws_o + (rp.first + rp.stride * (s0 + j)) * D + PER * threadIdx.x,
+                        ov[j]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) ov[j][i] = 0.f;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if (s0 + j >= n) continue;
@@ -286,14 +308,23 @@ static int launch_partial_any(const Plan &p, const LaunchArgs &la, void *stream,
                               const KernelEvents &ev, bool dbg) {
   const unsigned grid = partial_grid(la);
   const int kv = la.fp8 ? 2 : la.int8 ? 1 : 0;
-  if (la.D == 128) {
-    if (kv == 2) return launch_partial_128_2(p, la, grid, stream, ev, dbg);
-    if (kv == 1) return launch_partial_128_1(p, la, grid, stream, ev, dbg);
-    return launch_partial_128_0(p, la, grid, stream, ev, dbg);
+  switch (la.D) {
+    case 128:
+      if (kv == 2) return launch_partial_128_2(p, la, grid, stream, ev, dbg);
+      if (kv == 1) return launch_partial_128_1(p, la, grid, stream, ev, dbg);
+      return launch_partial_128_0(p, la, grid, stream, ev, dbg);
+    case 256:
+      if (kv == 2) return launch_partial_256_2(p, la, grid, stream, ev, dbg);
+      if (kv == 1) return launch_partial_256_1(p, la, grid, stream, ev, dbg);
+      return launch_partial_256_0(p, la, grid, stream, ev, dbg);
+    case 192:  // f16 and fp8 (the plan refuses int8 at head_dim 192)
+      if (kv == 2) return launch_partial_192_2(p, la, grid, stream, ev, dbg);
+      return launch_partial_192_0(p, la, grid, stream, ev, dbg);
+    default:
+      if (kv == 2) return launch_partial_512_2(p, la, grid, stream, ev, dbg);
+      if (kv == 1) return launch_partial_512_1(p, la, grid, stream, ev, dbg);
+      return launch_partial_512_0(p, la, grid, stream, ev, dbg);
   }
-  if (kv == 2) return launch_partial_256_2(p, la, grid, stream, ev, dbg);
-  if (kv == 1) return launch_partial_256_1(p, la, grid, stream, ev, dbg);
-  return launch_partial_256_0(p, la, grid, stream, ev, dbg);
 }
 
 int launch_partial(const Plan &p, const LaunchArgs &la, void *stream, void *start_event,
@@ -337,8 +368,12 @@ static void launch_merge_t(const Plan &p, const LaunchArgs &la, hipStream_t st) 
 int launch_merge(const Plan &p, const LaunchArgs &la, void *stream) {
   if (p.reducer == SKVD_REDUCER_NONE || la.batch == 0) return 0;
   hipStream_t st = (hipStream_t)stream;
-  if (la.D == 128) launch_merge_t<128>(p, la, st);
-  else launch_merge_t<256>(p, la, st);
+  switch (la.D) {
+    case 128: launch_merge_t<128>(p, la, st); break;
+    case 192: launch_merge_t<192>(p, la, st); break;
+    case 256: launch_merge_t<256>(p, la, st); break;
+    default: launch_merge_t<512>(p, la, st); break;
+  }
   return (int)hipGetLastError();
 }
 

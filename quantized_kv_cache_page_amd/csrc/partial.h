@@ -196,12 +196,16 @@ __device__ __forceinline__ T kv_load(const char *p) {
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4v *lds_s4_ptr;
 
-// Byte offset of 16-byte chunk c of row r in a row-major LDS tile with rows of RB bytes: the
+// Byte offset of 16-byte chunk c of row r in a row-major LDS tile with rows of ROWB bytes: the
 // chunk index is XOR-swizzled by the row so that the transposed reads of 16 consecutive rows
-// at one column fall in different banks.
+// at one column fall in different banks (by the row's low 4 bits when a row holds 16 or more
+// chunks in powers of two; rows of 24 chunks, head_dim 192, by its low 3 bits, which keeps the
+// chunk inside its aligned run of 8).
 template <int ROWB>
 __device__ __forceinline__ int swz(int r, int c) {
-  return r * ROWB + ((c ^ (r & 15)) << 4);
+  constexpr int CPR = ROWB / 16;
+  constexpr int XM = (CPR & (CPR - 1)) == 0 ? 15 : 7;
+  return r * ROWB + ((c ^ (r & XM)) << 4);
 }
 
 // D: head_dim (128/256). RB: 4-row quarters of the 16 MFMA rows in use per wave (R = G*T
@@ -234,15 +238,23 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
   constexpr bool SC = KV == 1;  // int8: f16 scales per 32 elements of each row
   constexpr bool F8 = KV == 2;  // fp8 E4M3: one f32 scale per tensor
   static_assert(RT == 1 || (HW == 1 && RB == 4 && PVM), "row tiles: one KV head per workgroup");
+  static_assert(!SC || D % 128 == 0, "int8 scale rows are read four groups at a time");
   constexpr int NW = HW * RT;        // waves per workgroup
   constexpr bool STREAM = RT == 1;   // row tiles re-read the same K/V rows: cached loads
   static_assert(CH == 16 || CH == 32 || (CH == 64 && !PVM), "chunk");
   static_assert(PVM || CH % 32 == 0, "the vector P.V pairs 16-token tiles 2h and 2h + 1");
   constexpr int NT = CH / 16;    // 16-token score tiles per chunk
-  constexpr int KS = D / 32;     // score MFMA steps of 32 head_dim elements
+  constexpr int KS = D / 32;     // 32-element head_dim groups (int8 scale groups)
+  // one-byte K: a lane loads 32 bytes of group g4 + 4m for each block m of four groups (the
+  // last block partly empty at head_dim 192: its missing groups hold zeros)
+  constexpr int KB = (KS + 3) / 4;
+  // score MFMA steps: one per group for f16 and int8 (after the int8 lane transpose); fp8 keeps
+  // the load layout, four steps per block
+  constexpr int KSTEPS = F8 ? 4 * KB : KS;
   constexpr int LPR = D / 8;     // lanes per V row in the load layout, 8 elements each
-  constexpr int TPS = 64 / LPR;  // V rows per load step
+  constexpr int TPS = 64 / LPR;  // V rows per load step (lanes past TPS * LPR idle: D = 192)
   constexpr int NS = CH / TPS;   // V load steps per chunk
+  static_assert(CH % TPS == 0, "V load steps");
   constexpr int NDT = D / 16;    // 16-wide head_dim tiles of the P.V MFMA
   constexpr int KPL = CH / 4;    // P.V contraction elements per lane (8: 16x16x32, 4: 16x16x16)
   constexpr int RM = 4 * RB;     // query rows held (padded)
@@ -393,7 +405,7 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
   auto kelem = [&](int k) __attribute__((always_inline)) {
     return F8 ? 32 * (g4 + 4 * (k >> 2)) + 8 * (k & 3) : 32 * k + 8 * g4;
   };
-  half8 qa[KS];
+  half8 qa[KSTEPS];
   {
     const int r = row0 + c16;
     if (r < R) {
@@ -401,10 +413,11 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
       const _Float16 *qp = (const _Float16 *)a.q + ((int64_t)b * T + t) * a.q_tok_stride +
                            (int64_t)(kvh * G + hg) * a.q_head_stride + 8 * g4;
 #pragma unroll
-      for (int k = 0; k < KS; ++k) qa[k] = *(const half8 *)(qp + kelem(k) - 8 * g4);
+      for (int k = 0; k < KSTEPS; ++k)  // (fp8 steps of a missing group: zeros)
+        qa[k] = kelem(k) < D ? *(const half8 *)(qp + kelem(k) - 8 * g4) : (half8)(_Float16)0;
     } else {
 #pragma unroll
-      for (int k = 0; k < KS; ++k) qa[k] = (half8)(_Float16)0;
+      for (int k = 0; k < KSTEPS; ++k) qa[k] = (half8)(_Float16)0;
     }
   }
   // This lane's MFMA output rows: row0 + 4*g4 + e. Row r sees positions j < L - T + t + 1.
@@ -433,6 +446,7 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
 
   bool clamped_any = false;
   const int vlane_tok = lane / LPR, vlane_el = 8 * (lane % LPR);
+  const bool vlane_ok = lane < TPS * LPR;  // (loads of the idle lanes re-read valid rows)
   // gather-debug variant: dense row (sequence b, position j, KV head kvh)
   auto dbg_row = [&](int j) __attribute__((always_inline)) -> int64_t {
     return ((int64_t)b * a.dbg_max_len + j) * Hkv + kvh;
@@ -465,7 +479,7 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
   const unsigned vt_tok = (unsigned)(vlane_tok * (int)a.tok_stride);
 
   Vec kb[NT][I8 ? 1 : KS];                   // f16 K: step k's 8 elements
-  uint4v kq[NT][I8 ? KS / 4 : 1][2];         // int8 K: the lane's 32 bytes of group g4 + 4m
+  uint4v kq[NT][I8 ? KB : 1][2];             // one-byte K: the lane's 32 bytes of group g4 + 4m
   uint2v ksr[NT][SC && !SCL ? KS / 4 : 1];   // int8 K (no shared scale load): the D/32 scales
                                              // of the lane's token, four per 8-byte load
   Vec vb[NS];
@@ -490,10 +504,12 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
         if constexpr (I8) {
           const unsigned off = min(c16_tok, (unsigned)(lim * (int)a.tok_stride)) + 32 * g4;
 #pragma unroll
-          for (int m = 0; m < KS / 4; ++m)
+          for (int m = 0; m < KB; ++m)
 #pragma unroll
             for (int h = 0; h < 2; ++h)
-              kq[t][m][h] = kv_load<STREAM, uint4v>(base + off + 128 * m + 16 * h);
+              kq[t][m][h] = KS % 4 == 0 || g4 + 4 * m < KS
+                                ? kv_load<STREAM, uint4v>(base + off + 128 * m + 16 * h)
+                                : (uint4v)0u;
           if constexpr (SC && !SCL) {
             const _Float16 *sb = ksc + row_offset(pg, jte & P1, kvh, a.s_page_stride,
                                                   a.s_tok_stride, a.s_head_stride);
@@ -518,9 +534,12 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
         if constexpr (I8) {
           const char *kp = kbase + off + 32 * g4;
 #pragma unroll
-          for (int m = 0; m < KS / 4; ++m)
+          for (int m = 0; m < KB; ++m)
 #pragma unroll
-            for (int h = 0; h < 2; ++h) kq[t][m][h] = kv_load<STREAM, uint4v>(kp + 128 * m + 16 * h);
+            for (int h = 0; h < 2; ++h)
+              kq[t][m][h] = KS % 4 == 0 || g4 + 4 * m < KS
+                                ? kv_load<STREAM, uint4v>(kp + 128 * m + 16 * h)
+                                : (uint4v)0u;
           if constexpr (SC && !SCL) {
             const int64_t so = row_offset(pg, j & P1, kvh, a.s_page_stride, a.s_tok_stride,
                                           a.s_head_stride);
@@ -638,7 +657,7 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int m = 0; m < KS / 4; ++m) group_transpose(kq[t][m][0], kq[t][m][1]);
+        for (int m = 0; m < KB; ++m) group_transpose(kq[t][m][0], kq[t][m][1]);
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -682,14 +701,15 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
         }
       } else if constexpr (F8) {
 #pragma unroll
-        for (int k = 0; k < KS; ++k) {
+        for (int k = 0; k < KSTEPS; ++k) {
           const uint4v &q4 = kq[t][k >> 2][(k & 3) >> 1];
           const unsigned w0 = q4[2 * (k & 1)], w1 = q4[2 * (k & 1) + 1];
           // fp8: k_scale * 2^8 is in the score scale
           S[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[k], f8x8_to_h8(uint2v{w0, w1}), S[t],
                                                         0, 0, 0);
           if constexpr (DBG) {
-            if (jk < tok_end) *(uint2v *)(a.dbg_k + dbg_row(jk) * D + kelem(k)) = uint2v{w0, w1};
+            if (jk < tok_end && kelem(k) < D)
+              *(uint2v *)(a.dbg_k + dbg_row(jk) * D + kelem(k)) = uint2v{w0, w1};
           }
         }
       } else {
@@ -739,7 +759,8 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
 #pragma unroll
       for (int s2 = 0; s2 < NS; ++s2) {
         const int jv = c0 + TPS * s2 + vlane_tok;
-        if (jv < tok_end) *(Vec *)(a.dbg_v + (dbg_row(jv) * D + vlane_el) * ES) = vb[s2];
+        if (jv < tok_end && vlane_ok)
+          *(Vec *)(a.dbg_v + (dbg_row(jv) * D + vlane_el) * ES) = vb[s2];
       }
     }
     if constexpr (PVM) {
@@ -762,7 +783,7 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
         } else {
           h = vb[s2];
         }
-        *(half8 *)(v_lds + swz<ROWB>(row, lane % LPR)) = h;
+        if (vlane_ok) *(half8 *)(v_lds + swz<ROWB>(row, lane % LPR)) = h;
       }
       if constexpr (SC && !SCL) {
         if (lane < CH) {

@@ -49,8 +49,11 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
   if (Hkv < 1 || Hq < 1 || Hq % Hkv != 0)
     return fail(err, errn, SKVD_ERR_SHAPE, "num_qo_heads=%d must be a positive multiple of "
                 "num_kv_heads=%d", Hq, Hkv);
-  if (D != 128 && D != 256)
-    return fail(err, errn, SKVD_ERR_SHAPE, "head_dim=%d unsupported (128 or 256)", D);
+  if (D != 128 && D != 192 && D != 256 && D != 512)
+    return fail(err, errn, SKVD_ERR_SHAPE, "head_dim=%d unsupported (128, 192, 256 or 512)", D);
+  if (D == 192 && prm.kv_dtype == SKVD_KV_I8_F16SCALE32)
+    return fail(err, errn, SKVD_ERR_SHAPE, "int8 cache at head_dim 192 unsupported (its six "
+                "group scales per row are not a whole number of the decode's 8-byte scale loads)");
   if (!is_pow2(prm.page_size) || prm.page_size > 1024)
     return fail(err, errn, SKVD_ERR_SHAPE, "page_size=%d must be a power of two <= 1024",
                 prm.page_size);
@@ -187,7 +190,8 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
     // a pure stream, does best with three workgroups per CU (the wide multi-token workload 527
     // us against 537 with four); the one-byte formats widen every element and need all four
     // SIMDs (fp8: 604.7 -> 460.9 us with four, int8: 640.5 -> 484.2)
-    const int auto_wpc = D == 256 ? (prm.kv_dtype == SKVD_KV_F16 ? 3 : 4)
+    // head_dim 192 and 512 take head_dim 256's counts (one wave per SIMD)
+    const int auto_wpc = D != 128 ? (prm.kv_dtype == SKVD_KV_F16 ? 3 : 4)
                          : p.row_blocks == 1 ? (byte ? std::max(1, 12 / hw)
                                                      : std::max(1, kDefaultWgsPerCu / hw))
                                              : kDefaultWgsPerCu;

@@ -112,6 +112,11 @@ SKVD_DECLARE_PARTIAL(128, 2)
 SKVD_DECLARE_PARTIAL(256, 0)
 SKVD_DECLARE_PARTIAL(256, 1)
 SKVD_DECLARE_PARTIAL(256, 2)
+SKVD_DECLARE_PARTIAL(192, 0)
+SKVD_DECLARE_PARTIAL(192, 2)
+SKVD_DECLARE_PARTIAL(512, 0)
+SKVD_DECLARE_PARTIAL(512, 1)
+SKVD_DECLARE_PARTIAL(512, 2)
 #undef SKVD_DECLARE_PARTIAL
 
 // Append launch (append.hip): resolved on the host from the plan and skvd_append_args.

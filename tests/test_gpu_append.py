@@ -85,6 +85,11 @@ CASES = [
     ("f8_d128_p16", 3, 8, 128, 16, "f8", (17, 300, 64), 40, "nhd"),
     ("f8_d256_p1", 2, 2, 256, 1, "f8", (9, 130), 130, "nhd"),
     ("f8_d128_p64_hnd", 3, 4, 128, 64, "f8", (1, 200, 129), 70, "hnd"),
+    ("f16_d192_p16", 2, 4, 192, 16, "f16", (17, 300), 40, "nhd"),
+    ("f8_d192_p4", 2, 2, 192, 4, "f8", (9, 130), 60, "nhd"),
+    ("f16_d512_p16", 2, 2, 512, 16, "f16", (17, 300), 40, "nhd"),
+    ("i8_d512_p16", 2, 4, 512, 16, "i8", (1, 65, 200)[:2], 64, "nhd"),
+    ("f8_d512_p1", 2, 2, 512, 1, "f8", (9, 130), 130, "nhd"),
 ]
 
 

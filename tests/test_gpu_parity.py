@@ -64,6 +64,14 @@ SMALL = [
     ("int8_t4_g4", 2, 4, 16, 4, 128, 16, "i8", ("list", (4, 900))),     # 16 rows: 4 quarters
     ("int8_t4_g4_p4", 3, 4, 8, 2, 128, 4, "i8", ("list", (5, 64, 333))),
     ("int8_t2_g4", 2, 2, 8, 2, 128, 16, "i8", ("list", (2, 1500))),     # 8 rows: 2 quarters
+    ("d192_gqa4", 3, 1, 16, 4, 192, 16, "f16", ("list", (1, 700, 2100))),  # head_dim 192
+    ("d192_t4_p2", 2, 4, 8, 4, 192, 2, "f16", ("list", (4, 333))),
+    ("d192_f8", 3, 1, 16, 4, 192, 16, "f8", ("list", (65, 700, 1500))),
+    ("d512_gqa4", 3, 1, 16, 4, 512, 16, "f16", ("list", (1, 700, 2100))),  # head_dim 512
+    ("d512_t2_p4", 2, 2, 8, 4, 512, 4, "f16", ("list", (2, 400))),
+    ("d512_i8", 3, 1, 16, 4, 512, 16, "i8", ("list", (64, 900, 1700))),
+    ("d512_i8_t4_p1", 2, 4, 8, 2, 512, 1, "i8", ("list", (5, 300))),
+    ("d512_f8", 3, 1, 16, 4, 512, 16, "f8", ("list", (129, 800, 1300))),
 ]
 
 
@@ -385,6 +393,8 @@ ROWTILES = [
     ("g8_t8_d256", 2, 8, 16, 2, 256, 16, "f16", (8, 1200)),
     ("g8_t8_d256_i8", 2, 8, 16, 2, 256, 16, "i8", (8, 1200)),
     ("g4_t8_d256_f8", 2, 8, 8, 2, 256, 4, "f8", (8, 800)),          # 32 rows at head_dim 256
+    ("g8_t8_d192", 2, 8, 16, 2, 192, 16, "f16", (8, 900)),          # 64 rows at head_dim 192
+    ("g8_t8_d512_i8", 2, 8, 16, 2, 512, 16, "i8", (8, 700)),        # 64 rows at head_dim 512
     ("g32_t1", 2, 1, 64, 2, 128, 16, "f16", (1, 3000)),             # 32 rows from a large group
 ]
 

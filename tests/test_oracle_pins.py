@@ -42,6 +42,9 @@ CASES = [
     (2, 4, 8, 2, 128, 16, (100, 33), True),
     (2, 37, 4, 2, 64, 16, (37, 120), False),   # many query tokens (the prefill route's reading)
     (1, 20, 8, 2, 64, 4, (90,), True),
+    (2, 2, 8, 2, 192, 16, (70, 33), False),    # head_dim 192
+    (2, 1, 4, 2, 512, 4, (41, 66), False),     # head_dim 512
+    (2, 3, 4, 1, 512, 16, (80, 17), True),     # head_dim 512, int8 (16 scale groups per row)
 ]
 
 
