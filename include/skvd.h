@@ -139,17 +139,17 @@ typedef struct {
   int32_t force_reducer;  /* skvd_reducer; 0 = choose by partial count */
   int32_t debug;          /* != 0: kernels record contract violations in the status word */
   int32_t schedule;       /* skvd_schedule; 0 = auto */
-  int32_t wgs_per_cu;     /* balanced schedule: workgroups launched per compute unit (0: 4;
-                             3 at head_dim 256; at head_dim 128 with G*T <= 4: f16,
-                             max(1, 4 / heads_per_wg); int8, 2 with 8 heads per workgroup (two
-                             rounds: the second workgroup of a CU starts when a CU frees up),
-                             else 8 / heads_per_wg) */
+  int32_t wgs_per_cu;     /* balanced schedule: workgroups launched per compute unit (0: at
+                             head_dim 128 with G*T <= 4, f16 max(1, 4 / heads_per_wg) and the
+                             one-byte formats max(1, 12 / heads_per_wg); other head_dims, f16 3
+                             and one-byte 4; 4 for more query rows at head_dim 128; divided by
+                             the row tiles of a workgroup) */
   int32_t heads_per_wg;   /* KV heads one partial-kernel workgroup serves, one wave each
-                             (0 at head_dim 128 with G*T <= 4: int8, 8 if it divides Hkv; then
-                             4, else 2, else 1 -- whichever divides Hkv --, where the waves of
-                             a CU read each token's rows of those heads together (int8: and
-                             share its scale cache line); 1 otherwise). Values 2, 4, 8 only for
-                             that variant and must divide Hkv (else SKVD_ERR_PLAN). */
+                             (0 at head_dim 128 with G*T <= 4: 4, else 2, else 1 -- whichever
+                             divides Hkv --, where the waves of a CU read each token's rows of
+                             those heads together; 1 otherwise, and 1 when the plan has no more
+                             (sequence, KV head, block) units than CUs). Values 2, 4, 8 only
+                             for that variant and must divide Hkv (else SKVD_ERR_PLAN). */
 } skvd_plan_params;
 
 /* What a plan resolved to (for logs and tests). */
