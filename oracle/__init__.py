@@ -101,6 +101,8 @@ def load(path: str | None = None):
     lib.oracle_quantize_group.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
                                           ctypes.c_void_p]
     lib.oracle_quantize_group.restype = None
+    lib.oracle_quantize_q4_group.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.oracle_quantize_q4_group.restype = None
     lib.oracle_merge_states.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_void_p]
@@ -118,11 +120,25 @@ def _ptr(a):
     return None if a is None else a.ctypes.data
 
 
+def kv_format(k_pages, head_dim: int) -> int:
+    """Cache format code of a pool: 0 f16, 1 int8 (int8 elements), 2 fp8 E4M3 (uint8, one
+    byte per element), 3 q4_0 (uint8 rows of head_dim / 2 bytes: two 4-bit codes per byte)."""
+    if k_pages.dtype == np.float16:
+        return 0
+    if k_pages.dtype == np.int8:
+        return 1
+    assert k_pages.dtype == np.uint8
+    if k_pages.shape[3] * 2 == head_dim:
+        return 3
+    assert k_pages.shape[3] == head_dim
+    return 2
+
+
 def _problem(prob: dict):
     """Build the ctypes problem struct; returns (struct, keep-alive list)."""
     q, k, v = prob["q"], prob["k_pages"], prob["v_pages"]
-    int8 = k.dtype == np.int8
-    fp8 = k.dtype == np.uint8  # OCP E4M3 bytes; k_scales / v_scales: one f32 each
+    fmt = kv_format(k, q.shape[2])
+    int8, fp8, q4 = fmt == 1, fmt == 2, fmt == 3
     assert q.dtype == np.float16 and q.ndim == 3 and q.strides[2] == 2
     assert k.shape == v.shape and k.strides == v.strides and k.ndim == 4
     table = np.ascontiguousarray(prob["page_table"], dtype=np.int32)
@@ -132,9 +148,9 @@ def _problem(prob: dict):
     T = int(prob["q_per_seq"])
     s = OracleProblem()
     s.batch, s.q_per_seq = B, T
-    s.num_qo_heads, s.num_kv_heads, s.head_dim = q.shape[1], k.shape[2], k.shape[3]
+    s.num_qo_heads, s.num_kv_heads, s.head_dim = q.shape[1], k.shape[2], q.shape[2]
     s.page_size = k.shape[1]
-    s.kv_int8 = 2 if fp8 else int(int8)
+    s.kv_int8 = fmt
     s.sm_scale = float(np.float32(prob["sm_scale"]))
     if fp8:
         s.k_fp8_scale = float(np.float32(np.asarray(prob["k_scales"]).reshape(-1)[0]))
@@ -145,7 +161,7 @@ def _problem(prob: dict):
     s.page_stride, s.tok_stride, s.head_stride = (k.strides[0] // es, k.strides[1] // es,
                                                   k.strides[2] // es)
     keep = [q, k, v, table, kv_len]
-    if int8:
+    if int8 or q4:
         ks, vs = prob["k_scales"], prob["v_scales"]
         assert ks.dtype == np.float16 and ks.strides == vs.strides
         s.k_scale, s.v_scale = ks.ctypes.data, vs.ctypes.data
@@ -194,16 +210,17 @@ def decode_blocked(prob: dict, block: int, rows=None, lib=None):
 
 def gather(prob: dict, max_len: int, lib=None):
     """Raw dense copies of every visible K/V row: (dense_k, dense_v, dense_ks, dense_vs) of
-    shape [B, max_len, Hkv, D] (and [B, max_len, Hkv, D/32] scales for int8); positions at or
-    beyond kv_len are zero."""
+    shape [B, max_len, Hkv, D] (q4_0: D/2 code bytes; and [B, max_len, Hkv, D/32] scales for
+    int8 and q4_0); positions at or beyond kv_len are zero."""
     lib = lib or load()
     s, keep = _problem(prob)
     B, Hkv, D = s.batch, s.num_kv_heads, s.head_dim
     dt = prob["k_pages"].dtype
-    dk = np.zeros((B, max_len, Hkv, D), dt)
-    dv = np.zeros((B, max_len, Hkv, D), dt)
+    row = D // 2 if s.kv_int8 == 3 else D
+    dk = np.zeros((B, max_len, Hkv, row), dt)
+    dv = np.zeros((B, max_len, Hkv, row), dt)
     dks = dvs = None
-    if s.kv_int8 == 1:
+    if s.kv_int8 in (1, 3):
         dks = np.zeros((B, max_len, Hkv, D // 32), np.float16)
         dvs = np.zeros((B, max_len, Hkv, D // 32), np.float16)
     rc = lib.oracle_gather(ctypes.byref(s), int(max_len), dk.ctypes.data, dv.ctypes.data,
@@ -221,23 +238,24 @@ def append(k_new, v_new, batch_idx, positions, page_table, max_len, k_pages, v_p
            k_scales=None, v_scales=None, batch=None, lib=None):
     """Write new K/V rows into copies of the pools. k_new, v_new: f16 [N, Hkv, D] (same
     strides); batch_idx, positions: int [N]; page_table [B, stride] int32; pools as in the
-    decode problem (int8 pools take f16 scale pools; fp8 pools, uint8 E4M3 bytes, take one f32
-    scale each). Returns (k, v, ks, vs, skipped): the written copies (ks, vs None for f16, the
-    scales unchanged for fp8) and the number of tokens skipped."""
+    decode problem (int8 and q4_0 pools take f16 scale pools; fp8 pools, uint8 E4M3 bytes, take
+    one f32 scale each; q4_0 pools are uint8 rows of D/2 bytes). Returns (k, v, ks, vs,
+    skipped): the written copies (ks, vs None for f16, the scales unchanged for fp8) and the
+    number of tokens skipped."""
     lib = lib or load()
     kn, vn = k_new, v_new
     assert kn.dtype == np.float16 and kn.shape == vn.shape and kn.strides == vn.strides
     assert kn.ndim == 3 and kn.strides[2] == 2
-    int8 = k_pages.dtype == np.int8
-    fp8 = k_pages.dtype == np.uint8
+    fmt = kv_format(k_pages, kn.shape[2])
+    int8, fp8, q4 = fmt == 1, fmt == 2, fmt == 3
     k, v = k_pages.copy(), v_pages.copy()
     bi = np.ascontiguousarray(batch_idx, dtype=np.int32)
     ps = np.ascontiguousarray(positions, dtype=np.int32)
     table = np.ascontiguousarray(page_table, dtype=np.int32)
     es = k.itemsize
     s = OracleAppendProblem()
-    s.num_tokens, s.num_kv_heads, s.head_dim = kn.shape[0], k.shape[2], k.shape[3]
-    s.page_size, s.kv_int8 = k.shape[1], 2 if fp8 else int(int8)
+    s.num_tokens, s.num_kv_heads, s.head_dim = kn.shape[0], k.shape[2], kn.shape[2]
+    s.page_size, s.kv_int8 = k.shape[1], fmt
     s.batch = table.shape[0] if batch is None else int(batch)
     s.max_len = int(max_len)
     s.k_new, s.v_new = kn.ctypes.data, vn.ctypes.data
@@ -248,7 +266,7 @@ def append(k_new, v_new, batch_idx, positions, page_table, max_len, k_pages, v_p
                                                   k.strides[2] // es)
     s.num_k_pages, s.num_v_pages = k.shape[0], v.shape[0]
     ks = vs = None
-    if int8:
+    if int8 or q4:
         ks, vs = k_scales.copy(), v_scales.copy()
         s.k_scale, s.v_scale = ks.ctypes.data, vs.ctypes.data
         s.s_page_stride, s.s_tok_stride, s.s_head_stride = (ks.strides[0] // 2, ks.strides[1] // 2,
@@ -290,6 +308,18 @@ def quantize_group(x, lib=None):
     codes = np.empty(xb.shape[0], np.int8)
     sb = np.empty(1, np.uint16)
     lib.oracle_quantize_group(xb.ctypes.data, xb.shape[0], codes.ctypes.data, sb.ctypes.data)
+    return codes, sb.view(np.float16)[0]
+
+
+def quantize_q4_group(x, lib=None):
+    """One group of 32 f16 elements -> (16 code bytes, f16 scale) by the oracle's q4_0 append
+    rule (byte i: element i in the low nibble, element i + 16 in the high nibble)."""
+    lib = lib or load()
+    xb = np.ascontiguousarray(x, dtype=np.float16)
+    assert xb.shape == (32,)
+    codes = np.empty(16, np.uint8)
+    sb = np.empty(1, np.uint16)
+    lib.oracle_quantize_q4_group(xb.ctypes.data, codes.ctypes.data, sb.ctypes.data)
     return codes, sb.view(np.float16)[0]
 
 

@@ -28,6 +28,14 @@
  *              #397 commit messages name fp8 caches read with per-tensor k_scale and v_scale
  *              values) times the tensor's f32 scale: value = e4m3(byte) * k_scale for K and
  *              * v_scale for V, exact in f64.
+ *              A q4_0 element (the 4-bit cache type that 1bit-MONSTER/engine issue #115,
+ *              comment "Closing the remaining half of this issue", names beside q8_0 among the
+ *              KV cache types not yet exercised; the pages do not define it, so it is read here
+ *              as the published ggml q4_0 block) is a 4-bit code c in 0..15 with one f16 scale
+ *              per 32 contiguous head_dim elements: value = (c - 8) * scale, exact in f64. The
+ *              codes of a row are D/2 bytes: group k (elements 32k .. 32k+31) in bytes
+ *              16k .. 16k+15, byte i of a group holding element i of the group in its low nibble
+ *              and element i + 16 in its high nibble. Scales are laid out as int8's.
  *   O2 heads   Query head h reads KV head floor(h / G), G = Hq / Hkv (consecutive grouping;
  *              the pages give only the head counts).
  *   O3 length  Query token t of a sequence with T query tokens and kv_len L sees positions
@@ -72,7 +80,8 @@ typedef struct {
   int32_t page_size;    /* P */
   int32_t kv_int8;      /* 0: f16 K/V; 1: int8 K/V with f16 scales per 32 elements;
                            2: fp8 E4M3 K/V with one f32 scale per tensor (k_fp8_scale,
-                           v_fp8_scale) */
+                           v_fp8_scale); 3: q4_0 codes (D/2 bytes per row) with f16 scales
+                           per 32 elements */
   int32_t pad0;
   double sm_scale;      /* the f32 scale the caller passes, widened */
   const uint16_t *q;    /* f16 bits */
@@ -141,6 +150,18 @@ static double kv_elem(const oracle_problem *p, const void *base, const uint16_t 
     tscale = 1.0; /* planted: tensor scale dropped */
 #endif
     return oracle_e4m3_to_double(((const uint8_t *)base)[off + d]) * tscale;
+  }
+  if (p->kv_int8 == 3) {
+    int grp = d / 32, i = d % 32;
+    uint8_t byte = ((const uint8_t *)base)[off + 16 * grp + (i % 16)];
+    int c = i < 16 ? (byte & 15) : (byte >> 4);
+#if ORACLE_MUTANT == 20
+    c = i < 16 ? (byte >> 4) : (byte & 15); /* planted: nibble order swapped */
+#endif
+#if ORACLE_MUTANT == 21
+    return (double)(c - 7) * oracle_half_to_double(scales[soff + grp]); /* planted: offset 7 */
+#endif
+    return (double)(c - 8) * oracle_half_to_double(scales[soff + grp]);
   }
   int group = d / 32;
 #if ORACLE_MUTANT == 5
@@ -330,13 +351,14 @@ int oracle_decode_blocked(const oracle_problem *p, const int64_t *rows, int64_t 
   return 0;
 }
 
-/* O1 alone: copy the raw elements (and, for int8, the raw f16 scale bits; fp8 has none per
- * row) of every visible
- * position j < kv_len[b] into dense [B, max_len, Hkv, D] (and [B, max_len, Hkv, D/32])
- * arrays. Positions at or beyond kv_len are left untouched. */
+/* O1 alone: copy the raw elements (and, for int8 and q4_0, the raw f16 scale bits; fp8 has
+ * none per row) of every visible position j < kv_len[b] into dense [B, max_len, Hkv, RB]
+ * (and [B, max_len, Hkv, D/32]) arrays, RB the bytes of a row over the element size (D, or
+ * D/2 bytes for q4_0). Positions at or beyond kv_len are left untouched. */
 int oracle_gather(const oracle_problem *p, int64_t max_len, void *dense_k, void *dense_v,
                   uint16_t *dense_ks, uint16_t *dense_vs) {
-  int D = p->head_dim, Hkv = p->num_kv_heads, es = p->kv_int8 ? 1 : 2, ng = D / 32;
+  int Hkv = p->num_kv_heads, es = p->kv_int8 ? 1 : 2, ng = p->head_dim / 32;
+  int D = p->kv_int8 == 3 ? p->head_dim / 2 : p->head_dim; /* row length in pool elements */
   for (int b = 0; b < p->batch; ++b) {
     int64_t L = p->kv_len[b];
     if (L > max_len) return -1;
@@ -347,7 +369,7 @@ int oracle_gather(const oracle_problem *p, int64_t max_len, void *dense_k, void 
         int64_t dst = (((int64_t)b * max_len + j) * Hkv + g);
         memcpy((char *)dense_k + dst * D * es, (const char *)p->k + off * es, (size_t)D * es);
         memcpy((char *)dense_v + dst * D * es, (const char *)p->v + off * es, (size_t)D * es);
-        if (p->kv_int8 == 1) {
+        if (p->kv_int8 == 1 || p->kv_int8 == 3) {
           memcpy(dense_ks + dst * ng, p->k_scale + soff, sizeof(uint16_t) * ng);
           memcpy(dense_vs + dst * ng, p->v_scale + soff, sizeof(uint16_t) * ng);
         }
@@ -399,6 +421,19 @@ int oracle_num_threads(void) {
  *              at +-448. 448 is E4M3's largest finite value, so the clip saturates rather
  *              than overflowing. The pages name the format and its
  *              per-tensor scales only; the rule is the plainest one with the kernel's f32.
+ *   W5 q4_0    A q4_0 cache (O1's 4-bit codes, value = (c - 8) * d, one f16 d per group of
+ *              32) quantizes each group on write by the published ggml q4_0 rule, all in f32:
+ *                m = the group's element of largest magnitude (the first one in element
+ *                    order on a tie; m = +0 when every magnitude is 0),
+ *                d = m / -8 (so that m itself gets code 0 and value -8d = m),
+ *                r = 1 / d (correctly rounded; r = 0 when d = 0),
+ *                c = min(15, trunc(x * r + 8.5)), the product and the sum each rounded to
+ *                    f32 (x * r lies in [-8, 8] up to rounding, so the sum is positive),
+ *              and the stored scale is f16(d) (nearest even): the codes come from the f32 d,
+ *              not from the rounded scale. Non-finite inputs: a NaN element does not take
+ *              part in the maximum and stores code 8 (value 0); an infinite m makes
+ *              d = -+inf, r = -+0 and every code 8 (an infinite element's x * r is NaN, a
+ *              finite one's 0), with the scale f16(d) = -+inf.
  * ============================================================================ */
 
 typedef struct {
@@ -407,7 +442,8 @@ typedef struct {
   int32_t head_dim;     /* D */
   int32_t page_size;    /* P */
   int32_t kv_int8;      /* 0: f16 cache; 1: int8 cache with f16 scales per 32 elements;
-                           2: fp8 E4M3 cache with per-tensor f32 scales */
+                           2: fp8 E4M3 cache with per-tensor f32 scales; 3: q4_0 codes with
+                           f16 scales per 32 elements */
   int32_t batch;        /* rows of the page table */
   int32_t max_len;      /* positions are < max_len */
   int32_t pad0;
@@ -500,7 +536,42 @@ uint8_t oracle_e4m3_from_float(float q) {
   return (uint8_t)(sign | best);
 }
 
-/* W1-W4 for one row of one pool. */
+/* W5 for one group of 32 f16 elements: 16 code bytes (element i in the low nibble of byte i,
+ * element i + 16 in its high nibble) and the f16 scale. */
+void oracle_quantize_q4_group(const uint16_t *x, uint8_t *codes, uint16_t *scale_bits) {
+  float m = 0.0f, amax = 0.0f;
+  for (int i = 0; i < 32; ++i) {
+    float v = (float)oracle_half_to_double(x[i]);
+#if ORACLE_MUTANT == 22
+    if (amax <= fabsf(v)) { /* planted: the last element of largest magnitude wins a tie */
+#else
+    if (amax < fabsf(v)) { /* false for NaN: a NaN never becomes the maximum */
+#endif
+      amax = fabsf(v);
+      m = v;
+    }
+  }
+  float d = m / -8.0f;
+#if ORACLE_MUTANT == 23
+  d = amax / 8.0f; /* planted: the magnitude instead of the signed extreme */
+#endif
+  float r = d != 0.0f ? 1.0f / d : 0.0f;
+  uint8_t c[32];
+  for (int i = 0; i < 32; ++i) {
+    float v = (float)oracle_half_to_double(x[i]);
+    float xr = v * r;
+    float t = xr + 8.5f;
+#if ORACLE_MUTANT == 24
+    t = rintf(xr) + 8.0f; /* planted: nearest-even rounding instead of the +8.5 truncation */
+#endif
+    int q = isnan(t) ? 8 : (int)t;
+    c[i] = (uint8_t)(q > 15 ? 15 : q);
+  }
+  for (int i = 0; i < 16; ++i) codes[i] = (uint8_t)(c[i] | (c[i + 16] << 4));
+  *scale_bits = oracle_float_to_half(d);
+}
+
+/* W1-W5 for one row of one pool. */
 static void append_row(const oracle_append_problem *p, const uint16_t *src, void *pool,
                        uint16_t *scales, float tscale, int64_t page, int64_t slot, int g) {
   int D = p->head_dim;
@@ -517,6 +588,12 @@ static void append_row(const oracle_append_problem *p, const uint16_t *src, void
     return;
   }
   int64_t soff = page * p->s_page_stride + slot * p->s_tok_stride + (int64_t)g * p->s_head_stride;
+  if (p->kv_int8 == 3) {
+    for (int grp = 0; grp < D / 32; ++grp)
+      oracle_quantize_q4_group(src + grp * 32, (uint8_t *)pool + off + grp * 16,
+                               scales + soff + grp);
+    return;
+  }
   for (int grp = 0; grp < D / 32; ++grp) {
     int sg = grp;
 #if ORACLE_MUTANT == 13

@@ -16,10 +16,12 @@ import torch.nn.functional as F
 
 
 def paged_from_dense(rng, q, Kd, Vd, L, P, *, T=1, spare=3, extra_heads=0, Ks=None, Vs=None,
-                     sm_scale=None, table_pad=2):
-    """q [B*T, Hq, D] f16; Kd, Vd [B, Lmax, Hkv, D] (f16, int8, or uint8 E4M3 bytes); Ks, Vs
-    [B, Lmax, Hkv, D/32] f16 scales for int8, or the [1] f32 tensor scales for E4M3. Returns a problem dict whose pools hold position j of sequence b at
-    page table[b, j // P], slot j % P, with pages randomly permuted among spare NaN pages."""
+                     sm_scale=None, table_pad=2, q4=False):
+    """q [B*T, Hq, D] f16; Kd, Vd [B, Lmax, Hkv, D] (f16, int8, or uint8 E4M3 bytes; with q4,
+    [B, Lmax, Hkv, D/2] uint8 q4_0 code bytes); Ks, Vs [B, Lmax, Hkv, D/32] f16 scales for int8
+    and q4_0, or the [1] f32 tensor scales for E4M3. Returns a problem dict whose pools hold
+    position j of sequence b at page table[b, j // P], slot j % P, with pages randomly permuted
+    among spare NaN pages."""
     B, Lmax, Hkv, D = Kd.shape
     L = np.asarray(L, np.int32)
     npages = (L.astype(np.int64) + P - 1) // P
@@ -27,8 +29,13 @@ def paged_from_dense(rng, q, Kd, Vd, L, P, *, T=1, spare=3, extra_heads=0, Ks=No
     N = live + spare
     perm = rng.permutation(N)
     Hs = Hkv + extra_heads
-    int8 = Kd.dtype == np.int8
-    if Kd.dtype == np.uint8:
+    int8 = Kd.dtype == np.int8 or q4
+    if q4:
+        kbig = np.full((N, P, Hs, D), 0xFF, np.uint8)
+        vbig = np.full((N, P, Hs, D), 0xFF, np.uint8)
+        ksb = np.full((N, P, Hs, 2 * D // 32), np.nan, np.float16)
+        vsb = np.full((N, P, Hs, 2 * D // 32), np.nan, np.float16)
+    elif Kd.dtype == np.uint8:
         kbig = np.full((N, P, Hs, D), 0x7F, np.uint8)  # the E4M3 NaN byte
         vbig = np.full((N, P, Hs, D), 0x7F, np.uint8)
     elif int8:
@@ -53,13 +60,14 @@ def paged_from_dense(rng, q, Kd, Vd, L, P, *, T=1, spare=3, extra_heads=0, Ks=No
                 ksb[pg, :j1 - j0, :Hkv] = Ks[b, j0:j1]
                 vsb[pg, :j1 - j0, :Hkv] = Vs[b, j0:j1]
         off += int(npages[b])
+    Dq = 2 * D if q4 else D
     prob = dict(q=q, k_pages=kbig[:, :, :Hkv], v_pages=vbig[:, :, :Hkv], k_scales=None,
                 v_scales=None, page_table=table, kv_len=L, q_per_seq=T,
-                sm_scale=float(np.float32(sm_scale if sm_scale is not None else 1 / math.sqrt(D))))
+                sm_scale=float(np.float32(sm_scale if sm_scale is not None else 1 / math.sqrt(Dq))))
     if int8:
         prob["k_scales"] = ksb[:, :, :Hkv]
         prob["v_scales"] = vsb[:, :, :Hkv]
-    if Kd.dtype == np.uint8:
+    if Kd.dtype == np.uint8 and not q4:
         prob["k_scales"] = np.asarray(Ks, np.float32).reshape(1)
         prob["v_scales"] = np.asarray(Vs, np.float32).reshape(1)
     return prob
@@ -79,6 +87,23 @@ def dequant(x, s):
     if s is None:
         return x.astype(np.float64)
     return x.astype(np.float64) * np.repeat(s.astype(np.float64), 32, axis=-1)
+
+
+def q4_pack(c):
+    """4-bit codes [..., D] (0..15) -> q4_0 bytes [..., D/2]: in each group of 32, byte i holds
+    code i in its low nibble and code i + 16 in its high nibble."""
+    c = np.asarray(c, np.uint8)
+    g = c.reshape(c.shape[:-1] + (c.shape[-1] // 32, 2, 16))
+    return (g[..., 0, :] | (g[..., 1, :] << 4)).reshape(c.shape[:-1] + (c.shape[-1] // 2,))
+
+
+def q4_values(codes, scales):
+    """q4_0 bytes [..., D/2] and f16 scales [..., D/32] -> fp64 values (c - 8) * scale."""
+    b = np.asarray(codes, np.uint8)
+    g = b.reshape(b.shape[:-1] + (b.shape[-1] // 16, 1, 16))
+    c = np.concatenate([g & 15, g >> 4], axis=-2).reshape(b.shape[:-1] + (2 * b.shape[-1],))
+    return (c.astype(np.float64) - 8) * np.repeat(np.asarray(scales).astype(np.float64), 32,
+                                                  axis=-1)
 
 
 def dense_reference(q, Kd, Vd, L, T, sm_scale, Ks=None, Vs=None):

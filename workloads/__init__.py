@@ -26,9 +26,12 @@ fp8 cache (kv_dtype "f8", uint8 OCP E4M3 bytes): k_scale and v_scale (one f32 ea
 shape [1]) are uniform in [1/80, 1/64] from default_rng((seed, 8)); the pools' N(0,1) draws
 (streams 4 and 5, as for f16) divided by the scale, clipped to +-448, become E4M3 bytes by
 torch's float8_e4m3fn cast (nearest even), which draws nothing.
+q4_0 cache (kv_dtype "q4", uint8 rows of D/2 bytes, two 4-bit codes per byte; value =
+(c - 8) * d, one f16 d per 32 elements, scale pools head-major as int8's): the N(0,1) draws
+(streams 4 and 5) made into codes by quantize_q4, which draws nothing.
 Spare pages and the tail slots past kv_len of each sequence's last page are NaN-poisoned
-(for int8: their scales are NaN; fp8: the NaN byte 0x7F), so any read of them shows up in the
-output.
+(for int8 and q4_0: their scales are NaN; fp8: the NaN byte 0x7F), so any read of them shows
+up in the output.
 """
 from __future__ import annotations
 
@@ -47,7 +50,7 @@ class Spec:
     num_kv_heads: int
     head_dim: int
     page_size: int
-    kv_dtype: str = "f16"           # "f16", "i8" or "f8"
+    kv_dtype: str = "f16"           # "f16", "i8", "f8" or "q4"
     lens: tuple = ("fixed", 256)     # ("fixed", L) | ("uniform", lo, hi) | ("zipf", s, lo, hi) | ("list", (..))
     q_mult: float = 1.0
     identity_table: bool = False
@@ -158,6 +161,43 @@ def quantize_int8(x: np.ndarray):
     return qv.reshape(x.shape), scale
 
 
+def quantize_q4(x: np.ndarray):
+    """4-bit codes with one f16 scale per 32 contiguous elements of the last axis (the q4_0
+    layout: value = (c - 8) * d, codes 0..15): d = f16(max|x| / 8), c = clip(rint(x / d) + 8,
+    0, 15), an all-zero group d = 0 and c = 8 -- a plain input recipe, not the append's rule.
+    Returns (packed uint8 [..., D/2]: byte i of a group holds element i in its low nibble and
+    element i + 16 in its high nibble, scale f16 [..., D/32])."""
+    D = x.shape[-1]
+    g = x.reshape(x.shape[:-1] + (D // 32, 32)).astype(np.float32)
+    amax = np.abs(g).max(axis=-1)
+    scale = (amax / np.float32(8.0)).astype(np.float16)
+    sf = scale.astype(np.float32)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        c = np.where(sf > 0, np.rint(g / np.where(sf > 0, sf, 1)), 0) + 8
+    c = np.clip(c, 0, 15).astype(np.uint8)
+    packed = c[..., :16] | (c[..., 16:] << 4)
+    return packed.reshape(x.shape[:-1] + (D // 2,)), scale
+
+
+def _normal_q4(seed, stream, shape):
+    """N(0,1) data (drawn as in _normal_f16) as q4_0 codes + f16 scales."""
+    D = shape[-1]
+    q = np.empty(tuple(shape[:-1]) + (D // 2,), np.uint8)
+    sc = np.empty(tuple(shape[:-1]) + (D // 32,), np.float16)
+    qf, sf = q.reshape(-1), sc.reshape(-1)
+    n = int(np.prod(shape))
+
+    def fill(c):
+        a, b = c * _CHUNK, min(n, (c + 1) * _CHUNK)
+        x = _chunk_rng(seed, stream, c).standard_normal(b - a, dtype=np.float32)
+        qq, ss = quantize_q4(x.reshape(-1, 32))
+        qf[a // 2:b // 2] = qq.reshape(-1)
+        sf[a // 32:b // 32] = ss.reshape(-1)
+
+    _parallel(fill, -(-n // _CHUNK))
+    return q, sc
+
+
 def _normal_int8(seed, stream, shape):
     """N(0,1) data (drawn as in _normal_f16) quantized to int8 + f16 scales."""
     q = np.empty(shape, np.int8)
@@ -210,8 +250,9 @@ def fp8_scales(seed):
 
 def generate(s: Spec, seed: int) -> dict:
     """Build one problem. Returns a dict of numpy arrays and ints:
-    q [B*T, Hq, D] f16; k_pages, v_pages [N, P, Hkv, D] f16, int8 or uint8 (E4M3); k_scales,
-    v_scales [N, P, Hkv, D/32] f16 (int8), [1] f32 (fp8) or None; page_table [B, ceil(max_kv_len/P)] int32 (-1 past each
+    q [B*T, Hq, D] f16; k_pages, v_pages [N, P, Hkv, D] f16, int8 or uint8 (E4M3), or
+    [N, P, Hkv, D/2] uint8 (q4_0 codes); k_scales, v_scales [N, P, Hkv, D/32] f16 (int8, q4_0),
+    [1] f32 (fp8) or None; page_table [B, ceil(max_kv_len/P)] int32 (-1 past each
     sequence's pages); kv_len [B] int32; q_per_seq; sm_scale (f32 value 1/sqrt(D)); spec."""
     rng = np.random.default_rng(seed)
     B, T, Hq, Hkv, D, P = (s.batch, s.q_per_seq, s.num_qo_heads, s.num_kv_heads, s.head_dim,
@@ -246,6 +287,10 @@ def generate(s: Spec, seed: int) -> dict:
         k, ks = _normal_int8(seed, 4, (N, P, Hkv, D))
         v, vs = _normal_int8(seed, 5, (N, P, Hkv, D))
         ks, vs = head_major(ks), head_major(vs)
+    elif s.kv_dtype == "q4":
+        k, ks = _normal_q4(seed, 4, (N, P, Hkv, D))
+        v, vs = _normal_q4(seed, 5, (N, P, Hkv, D))
+        ks, vs = head_major(ks), head_major(vs)
     elif s.kv_dtype == "f8":
         ks, vs = fp8_scales(seed)
         k = _normal_e4m3(seed, 4, (N, P, Hkv, D), ks[0])
@@ -261,18 +306,20 @@ def generate(s: Spec, seed: int) -> dict:
 def poison_unread(k, v, ks, vs, table, L, P, spare_pages):
     """NaN-poison what a correct decode never reads: spare pages and tail slots."""
     spare = np.asarray(spare_pages, np.int64)
-    if k.dtype == np.uint8:
-        nan = np.uint8(0x7F)  # the E4M3 NaN byte
+    if ks is not None and ks.dtype == np.float16:  # int8 and q4_0: NaN scales
+        nan = np.float16(np.nan)
         if spare.size:
-            k[spare] = nan
-            v[spare] = nan
+            ks[spare] = nan
+            vs[spare] = nan
+            k[spare] = 127 if k.dtype == np.int8 else 0xFF
+            v[spare] = 127 if k.dtype == np.int8 else 0xFF
         for b in range(L.shape[0]):
             if L[b] % P:
                 last = table[b, (L[b] - 1) // P]
-                k[last, L[b] % P:] = nan
-                v[last, L[b] % P:] = nan
-    elif ks is None:
-        nan = np.float16(np.nan)
+                ks[last, L[b] % P:] = nan
+                vs[last, L[b] % P:] = nan
+    elif k.dtype == np.uint8:
+        nan = np.uint8(0x7F)  # the E4M3 NaN byte
         if spare.size:
             k[spare] = nan
             v[spare] = nan
@@ -284,15 +331,13 @@ def poison_unread(k, v, ks, vs, table, L, P, spare_pages):
     else:
         nan = np.float16(np.nan)
         if spare.size:
-            ks[spare] = nan
-            vs[spare] = nan
-            k[spare] = 127
-            v[spare] = 127
+            k[spare] = nan
+            v[spare] = nan
         for b in range(L.shape[0]):
             if L[b] % P:
                 last = table[b, (L[b] - 1) // P]
-                ks[last, L[b] % P:] = nan
-                vs[last, L[b] % P:] = nan
+                k[last, L[b] % P:] = nan
+                v[last, L[b] % P:] = nan
 
 
 def append_tokens(prob: dict, seed: int, new_per_seq: int):
@@ -302,7 +347,7 @@ def append_tokens(prob: dict, seed: int, new_per_seq: int):
     default_rng((seed, 7)). Returns dict(k_new, v_new [N, Hkv, D] f16, batch_idx, positions
     [N] int32)."""
     k = prob["k_pages"]
-    Hkv, D = k.shape[2], k.shape[3]
+    Hkv, D = k.shape[2], prob["q"].shape[2]
     L = np.asarray(prob["kv_len"], np.int64)
     n = np.minimum(L, int(new_per_seq))
     bi = np.concatenate([np.full(int(n[b]), b) for b in range(L.shape[0])] + [np.zeros(0)])
@@ -337,8 +382,7 @@ PREFILL_CONFIGS = {
 def attention_flops(prob: dict) -> int:
     """Algorithmic FLOPs of one attention call: 4*D per (query row, visible position) pair
     (2*D for q.k, 2*D for p*v), visible positions per the causal reading."""
-    k = prob["k_pages"]
-    D = k.shape[3]
+    D = prob["q"].shape[2]
     Hq = prob["q"].shape[1]
     T = int(prob["q_per_seq"])
     L = np.asarray(prob["kv_len"], np.int64)
@@ -347,10 +391,11 @@ def attention_flops(prob: dict) -> int:
     return int(4 * D * Hq * vis)
 
 
-def _row_pair_bytes(k) -> int:
-    D = k.shape[3]
+def _row_pair_bytes(k, D: int) -> int:
     if k.dtype == np.float16:
         return 4 * D
+    if k.dtype == np.uint8 and k.shape[3] * 2 == D:  # q4_0: D/2 code bytes + D/32 f16 scales
+        return 2 * (D // 2 + 2 * (D // 32))
     if k.dtype == np.uint8:
         return 2 * D
     return 2 * (D + 2 * (D // 32))
@@ -359,20 +404,20 @@ def _row_pair_bytes(k) -> int:
 def append_bytes(prob: dict, new: dict) -> int:
     """Algorithmic bytes of one append: the new K and V rows read (2*D*2 bytes per token-head)
     plus the cache written (2*D*2 bytes for f16; 2*(D + 2*D/32) for int8 with f16 scales; 2*D
-    for fp8)."""
+    for fp8; 2*(D/2 + 2*D/32) for q4_0)."""
     k = prob["k_pages"]
-    Hkv, D = k.shape[2], k.shape[3]
-    written = _row_pair_bytes(k)
+    Hkv, D = k.shape[2], new["k_new"].shape[2]
+    written = _row_pair_bytes(k, D)
     return int(new["k_new"].shape[0]) * Hkv * (4 * D + written)
 
 
 def kv_bytes(prob: dict) -> int:
     """Algorithmic K+V bytes one decode reads: sum_b kv_len_b * Hkv * row bytes, where a row
-    pair is 2*D*2 bytes for f16, 2*(D + 2*D/32) bytes for int8 with f16 scales and 2*D bytes
-    for fp8 (its two per-tensor scales are not per row)."""
+    pair is 2*D*2 bytes for f16, 2*(D + 2*D/32) bytes for int8 with f16 scales, 2*D bytes
+    for fp8 (its two per-tensor scales are not per row) and 2*(D/2 + 2*D/32) for q4_0."""
     k = prob["k_pages"]
-    Hkv, D = k.shape[2], k.shape[3]
-    row = _row_pair_bytes(k)
+    Hkv, D = k.shape[2], prob["q"].shape[2]
+    row = _row_pair_bytes(k, D)
     return int(np.asarray(prob["kv_len"], np.int64).sum()) * Hkv * row
 
 
