@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define SKVD_ABI_VERSION 10
+#define SKVD_ABI_VERSION 11
 
 typedef enum {
   SKVD_OK = 0,
@@ -88,7 +88,7 @@ typedef enum {
 typedef enum {
   SKVD_KV_F16 = 0,           /* K/V pools hold f16 */
   SKVD_KV_I8_F16SCALE32 = 1, /* K/V pools hold int8; scale pools hold one f16 per 32 elements */
-  SKVD_KV_FP8_E4M3 = 2       /* K/V pools hold OCP E4M3 bytes (exponent bias 7, no infinities,
+  SKVD_KV_FP8_E4M3 = 2,      /* K/V pools hold OCP E4M3 bytes (exponent bias 7, no infinities,
                                 0x7F / 0xFF NaN); each pool has one f32 scale for the whole
                                 tensor: element value = e4m3(byte) * k_scale for K and
                                 * v_scale for V (AMD-Ecosystem/flashinfer PR #397, the two
@@ -96,6 +96,16 @@ typedef enum {
                                 and v_scale values passed by pointer). Decode, multi-token
                                 route, gather and append (nearest-even E4M3 of x / scale,
                                 saturating at 448). */
+  SKVD_KV_Q4_0 = 3           /* q4_0 (named beside q8_0 among the KV cache types of
+                                1bit-MONSTER/engine issue #115, comment "Closing the remaining
+                                half of this issue"; read as the published ggml q4_0 block):
+                                K/V pools hold uint8 rows of D/2 bytes, two 4-bit codes c per
+                                byte -- in each group of 32 elements (bytes 16k .. 16k+15 of a
+                                row for group k), byte i holds element i in its low nibble and
+                                element i + 16 in its high nibble --, scale pools one f16 d per
+                                32 elements laid out as int8's: value = (c - 8) * d. Pool
+                                strides are in bytes. head_dim 128, 256 or 512; decode, gather
+                                and append (see skvd_append); not the multi-token route. */
 } skvd_kv_dtype;
 
 typedef enum {
@@ -123,8 +133,8 @@ typedef enum {
 typedef struct {
   int32_t num_qo_heads;   /* Hq; Hq % Hkv == 0 */
   int32_t num_kv_heads;   /* Hkv >= 1 */
-  int32_t head_dim;       /* D: 128, 192, 256 or 512 (int8 caches: 128, 256 or 512; the
-                             multi-token route: 128 or 256) */
+  int32_t head_dim;       /* D: 128, 192, 256 or 512 (int8 and q4_0 caches: 128, 256 or 512;
+                             the multi-token route: 128 or 256) */
   int32_t page_size;      /* P: power of two, 1..1024 */
   int32_t max_batch;      /* B upper bound, >= 1 */
   int32_t max_q_per_seq;  /* T upper bound: 1..8 (G * T <= 1024 query rows per KV head: up to 16
@@ -181,22 +191,23 @@ typedef struct {
   const void *q;             /* f16 [B*T, Hq, D]; row b*T + t; D dense; 16-byte aligned */
   int64_t q_tok_stride;      /* elements between rows b*T + t and b*T + t + 1 (multiple of 8) */
   int64_t q_head_stride;     /* elements between heads (multiple of 8) */
-  const void *k_pages;       /* [num_k_pages, P, Hkv, D] f16, int8 or E4M3 bytes; 16-byte
-                                aligned */
-  const void *v_pages;       /* [num_v_pages, P, Hkv, D], same strides as K */
-  int64_t page_stride;       /* elements between pages (shared by K and V); the three strides
-                                are non-negative multiples of 16 bytes (8 f16 / 16 int8 or
-                                fp8 elements), else SKVD_ERR_LAYOUT */
+  const void *k_pages;       /* [num_k_pages, P, Hkv, D] f16, int8 or E4M3 bytes, or
+                                [num_k_pages, P, Hkv, D/2] q4_0 code bytes; 16-byte aligned */
+  const void *v_pages;       /* [num_v_pages, P, Hkv, D] (q4_0: D/2), same strides as K */
+  int64_t page_stride;       /* elements between pages (shared by K and V; bytes for the
+                                one-byte formats and q4_0); the three strides are non-negative
+                                multiples of 16 bytes, else SKVD_ERR_LAYOUT */
   int64_t tok_stride;        /* elements between slots of a page */
   int64_t head_stride;       /* elements between KV heads */
   int64_t num_k_pages;       /* pages in the K pool (>= 1); ids are clamped below it */
   int64_t num_v_pages;       /* pages in the V pool (>= 1) */
-  const void *k_scales;      /* int8: f16 [num_k_pages, P, Hkv, D/32]; fp8: one f32 (k_scale,
-                                device memory, 4-byte aligned, read by the kernels at each
-                                call, so a captured graph sees its current value); f16: NULL */
-  const void *v_scales;      /* int8: f16 [num_v_pages, P, Hkv, D/32]; fp8: one f32 (v_scale);
-                                f16: NULL */
-  int64_t scale_page_stride; /* int8 only (ignored otherwise): elements; shared by both scale
+  const void *k_scales;      /* int8, q4_0: f16 [num_k_pages, P, Hkv, D/32]; fp8: one f32
+                                (k_scale, device memory, 4-byte aligned, read by the kernels at
+                                each call, so a captured graph sees its current value); f16:
+                                NULL */
+  const void *v_scales;      /* int8, q4_0: f16 [num_v_pages, P, Hkv, D/32]; fp8: one f32
+                                (v_scale); f16: NULL */
+  int64_t scale_page_stride; /* int8, q4_0 (ignored otherwise): elements; shared by both scale
                                 pools; the D/32 scales of a token-head are contiguous; pools
                                 8-byte aligned and all three strides multiples of 4 elements
                                 (else SKVD_ERR_LAYOUT) */
@@ -272,11 +283,11 @@ skvd_status skvd_decode_partial_timed(const skvd_plan *plan, const skvd_decode_a
                                       void *start_event, void *stop_event);
 
 /* Test aid: copy the raw elements of every visible K/V row (position j < kv_len[b]) into
- * dense [B, max_len, Hkv, D] arrays (element size 2 for f16, 1 for int8 and fp8), and for int8
- * the raw f16 scales into dense [B, max_len, Hkv, D/32] arrays (dense_ks/dense_vs; NULL for f16
- * and fp8, whose scales are per tensor).
+ * dense [B, max_len, Hkv, D] arrays (element size 2 for f16, 1 for int8 and fp8; q4_0 rows are
+ * D/2 code bytes), and for int8 and q4_0 the raw f16 scales into dense [B, max_len, Hkv, D/32]
+ * arrays (dense_ks/dense_vs; NULL for f16 and fp8, whose scales are per tensor).
  * It runs the plan's own partial-kernel variant -- the same schedule, page lookups, lane
- * offsets, loads and (int8) register transposes as skvd_decode -- in a debug form that stores
+ * offsets, loads and (int8, q4_0) register transposes as skvd_decode -- in a debug form that stores
  * each K/V element and scale it holds at the point where the decode consumes it, at the
  * position the decode attributes it to, and computes nothing else; a wrong address or lane
  * mapping in the decode shows up as a wrong element here. Rows at or beyond kv_len[b] are not
@@ -370,11 +381,17 @@ skvd_status skvd_merge_states(const void *o_states, int64_t o_state_stride, int6
  * with one f32 scale s per tensor, AMD-Ecosystem/flashinfer PR #397 commit messages) stores for
  * each element the E4M3 value nearest to clip(x / s, -448, 448) (the quotient in f32, correctly
  * rounded; ties to the even mantissa; a NaN quotient stores 0); its scales are only read.
+ * A q4_0 cache (SKVD_KV_Q4_0) takes the published ggml q4_0 rule per group of 32, in f32:
+ *     m = the element of largest magnitude (the first on a tie; +0 if all are 0),
+ *     d = m / -8,  r = 1 / d (0 if d = 0),  c = min(15, trunc(x * r + 8.5)),
+ * the product and the sum each rounded to f32, and stores f16(d) (nearest even) as the scale.
  * Non-finite inputs: int8 -- a NaN element stores code 0 and is left out of its group's maximum;
  * an infinite element gives its group the scale f16(inf) = inf and every code 0. fp8 -- NaN
- * stores 0, +-inf saturates to +-448.
+ * stores 0, +-inf saturates to +-448. q4_0 -- a NaN element stores code 8 and is left out of the
+ * maximum; an infinite m gives the scale f16(-m / 8) = -+inf and every code 8.
  *
- * - Written: exactly the K/V elements (and, int8, the scales) of the slots the tokens name.
+ * - Written: exactly the K/V elements (and, int8 and q4_0, the scales) of the slots the tokens
+ *   name.
  *   Nothing else; no workspace. k_new, v_new, batch_idx, positions and the table are read only.
  * - Skips (device-data contract, not checked with a synchronization): a token whose batch_idx is
  *   outside [0, batch) or whose position is outside [0, the plan's max_kv_len) writes nothing; a
@@ -395,18 +412,19 @@ typedef struct {
   const int32_t *positions;   /* [N] device: logical position of each new token */
   int32_t num_tokens;         /* N >= 0 (0 launches nothing) */
   int32_t batch;              /* rows of page_table, >= 0 */
-  void *k_pages;              /* [num_k_pages, P, Hkv, D] f16, int8 or E4M3, written; layout rules
-                                 as in skvd_decode_args */
+  void *k_pages;              /* [num_k_pages, P, Hkv, D] f16, int8 or E4M3 (q4_0: D/2 code
+                                 bytes), written; layout rules as in skvd_decode_args */
   void *v_pages;              /* [num_v_pages, P, Hkv, D], same strides as K, written */
   int64_t page_stride;        /* elements; shared by K and V */
   int64_t tok_stride;
   int64_t head_stride;
   int64_t num_k_pages;        /* >= 1 */
   int64_t num_v_pages;        /* >= 1 */
-  void *k_scales;             /* int8: f16 [num_k_pages, P, Hkv, D/32], written; fp8: one f32
-                                 (k_scale, device memory, 4-byte aligned), read; f16: NULL */
-  void *v_scales;             /* int8: f16 [num_v_pages, P, Hkv, D/32], written; fp8: one f32
-                                 (v_scale), read; f16: NULL */
+  void *k_scales;             /* int8, q4_0: f16 [num_k_pages, P, Hkv, D/32], written; fp8:
+                                 one f32 (k_scale, device memory, 4-byte aligned), read; f16:
+                                 NULL */
+  void *v_scales;             /* int8, q4_0: f16 [num_v_pages, P, Hkv, D/32], written; fp8:
+                                 one f32 (v_scale), read; f16: NULL */
   int64_t scale_page_stride;  /* elements; layout rules as in skvd_decode_args */
   int64_t scale_tok_stride;
   int64_t scale_head_stride;

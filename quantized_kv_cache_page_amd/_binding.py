@@ -17,12 +17,13 @@ LIB_PATH = os.path.join(_PKG, "libskvd.so")
 SKVD_KV_F16 = 0
 SKVD_KV_I8_F16SCALE32 = 1
 SKVD_KV_FP8_E4M3 = 2
+SKVD_KV_Q4_0 = 3
 REDUCERS = {"auto": 0, "direct": 1, "cooperative": 2, "multipass": 3, "hierarchical": 4,
             "none": 5}
 REDUCER_NAMES = {v: k for k, v in REDUCERS.items()}
 SCHEDULES = {"auto": 0, "static": 1, "balanced": 2}
 SCHEDULE_NAMES = {v: k for k, v in SCHEDULES.items()}
-ABI_VERSION = 10
+ABI_VERSION = 11
 STATUS_KV_LEN_CLAMPED = 0x1
 STATUS_PAGE_CLAMPED = 0x2
 
@@ -304,15 +305,17 @@ def _kv_dtype_code(kv_dtype) -> int:
         return SKVD_KV_I8_F16SCALE32
     if kv_dtype in ("f8", "fp8", "e4m3", torch.uint8, torch.float8_e4m3fn):
         return SKVD_KV_FP8_E4M3
+    if kv_dtype in ("q4", "q4_0"):
+        return SKVD_KV_Q4_0
     raise ValueError(f"unknown kv_dtype {kv_dtype!r}")
 
 
 _POOL_DTYPES = {"f16": (torch.float16,), "i8": (torch.int8,),
-                "f8": (torch.uint8, torch.float8_e4m3fn)}
+                "f8": (torch.uint8, torch.float8_e4m3fn), "q4": (torch.uint8,)}
 
 
 def _set_scales(a, k_scales, v_scales, kv_dtype, where):
-    """Scale pointers (and, for int8, strides) of a decode or append argument struct."""
+    """Scale pointers (and, for int8 and q4_0, strides) of a decode or append argument struct."""
     if k_scales is None:
         if v_scales is not None:
             raise SkvdError(4, where, "v_scales given without k_scales")
@@ -338,9 +341,10 @@ class Plan:
     Plan(num_qo_heads, num_kv_heads, head_dim, page_size, kv_dtype, max_batch, max_q_per_seq,
          max_kv_len, device) sizes everything once, outside any capture; run() then launches
     the decode on the current stream with no allocation other than the default outputs.
-    kv_dtype is "f16", "i8" (int8 with one f16 scale per 32 elements) or "f8" (OCP E4M3
+    kv_dtype is "f16", "i8" (int8 with one f16 scale per 32 elements), "f8" (OCP E4M3
     bytes, held in uint8 tensors, with one f32 scale per tensor passed as k_scales / v_scales:
-    one-element float32 device tensors)."""
+    one-element float32 device tensors) or "q4" (q4_0: uint8 pools [pages, P, Hkv, D/2], two
+    4-bit codes per byte, with f16 scale pools [pages, P, Hkv, D/32])."""
 
     def __init__(self, num_qo_heads, num_kv_heads, head_dim, page_size, kv_dtype="f16",
                  max_batch=1, max_q_per_seq=1, max_kv_len=1, device=0, num_cus=0,
@@ -358,7 +362,7 @@ class Plan:
             int(idx), int(num_cus), int(force_blocks_per_split), red, int(bool(debug)), sch,
             int(wgs_per_cu), int(heads_per_wg))
         self.kv_dtype = {SKVD_KV_F16: "f16", SKVD_KV_I8_F16SCALE32: "i8",
-                         SKVD_KV_FP8_E4M3: "f8"}[self.params.kv_dtype]
+                         SKVD_KV_FP8_E4M3: "f8", SKVD_KV_Q4_0: "q4"}[self.params.kv_dtype]
         self.handle = skvd_plan_create(self.params)
         self.info = skvd_plan_get_info(self.handle)
         self.workspace_bytes = int(self.info.workspace_bytes)
@@ -421,6 +425,8 @@ class Plan:
             raise SkvdError(2, "Plan.run", "q must be [B*T, Hq, D] and pools [pages, P, Hkv, D]")
         if q.stride(2) != 1 or k_pages.stride(3) != 1:
             raise SkvdError(3, "Plan.run", "head_dim must be dense in q and the pools")
+        if k_pages.shape[3] != self._row_len():
+            raise SkvdError(2, "Plan.run", f"pool rows must hold {self._row_len()} elements")
         B = int(kv_len.shape[0])
         a = skvd_decode_args()
         a.q = q.data_ptr()
@@ -438,6 +444,11 @@ class Plan:
         a.o = _ptr(out)
         a.lse = _ptr(lse)
         return a
+
+    def _row_len(self) -> int:
+        """Elements of a pool row: head_dim, or head_dim / 2 bytes for q4_0."""
+        D = int(self.params.head_dim)
+        return D // 2 if self.kv_dtype == "q4" else D
 
     def _outputs(self, q, out, lse):
         if out is None:
@@ -542,6 +553,8 @@ class Plan:
             raise TypeError(f"k_pages and v_pages must be {want[0]}")
         if k_pages.stride() != v_pages.stride() or k_pages.shape[1:] != v_pages.shape[1:]:
             raise SkvdError(3, "Plan.append", "K and V must share page shape and strides")
+        if k_pages.dim() != 4 or k_pages.shape[3] != self._row_len():
+            raise SkvdError(2, "Plan.append", f"pool rows must hold {self._row_len()} elements")
         if batch_idx.dtype != torch.int32 or positions.dtype != torch.int32 or \
                 page_table.dtype != torch.int32:
             raise TypeError("batch_idx, positions and page_table must be int32")
@@ -570,8 +583,8 @@ class Plan:
     def append(self, k_new, v_new, batch_idx, positions, k_pages, v_pages, page_table,
                k_scales=None, v_scales=None, batch=None, stream=None):
         """skvd_append: write new rows k_new, v_new [N, Hkv, D] f16 of tokens (batch_idx[i],
-        positions[i]) into the pools in place (int8 pools: quantized, scales written; fp8 pools:
-        quantized with the given tensor scales, which are only read). Only the
+        positions[i]) into the pools in place (int8 and q4_0 pools: quantized, scales written;
+        fp8 pools: quantized with the given tensor scales, which are only read). Only the
         named slots are written; nothing is allocated."""
         a = self.make_append_args(k_new, v_new, batch_idx, positions, k_pages, v_pages,
                                   page_table, k_scales, v_scales, batch)
@@ -583,13 +596,14 @@ class Plan:
 
     def gather_debug(self, q, k_pages, v_pages, page_table, kv_len, max_len, k_scales=None,
                      v_scales=None, q_per_seq=1, stream=None):
-        """skvd_gather_debug: dense raw copies of the visible K/V rows (zeros elsewhere)."""
+        """skvd_gather_debug: dense raw copies of the visible K/V rows (zeros elsewhere; q4_0
+        rows are their D/2 code bytes)."""
         B = int(kv_len.shape[0])
-        Hkv, D = k_pages.shape[2], k_pages.shape[3]
-        dk = torch.zeros((B, max_len, Hkv, D), dtype=k_pages.dtype, device=k_pages.device)
+        Hkv, row, D = k_pages.shape[2], k_pages.shape[3], int(self.params.head_dim)
+        dk = torch.zeros((B, max_len, Hkv, row), dtype=k_pages.dtype, device=k_pages.device)
         dv = torch.zeros_like(dk)
         dks = dvs = None
-        if k_scales is not None and self.kv_dtype == "i8":
+        if k_scales is not None and self.kv_dtype in ("i8", "q4"):
             dks = torch.zeros((B, max_len, Hkv, D // 32), dtype=torch.float16, device=k_pages.device)
             dvs = torch.zeros_like(dks)
         o = torch.empty(q.shape, dtype=torch.float16, device=q.device)

@@ -16,8 +16,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libskvd.so")
-PARTIAL = [f"partial_{d}_{f}.hip" for d in (128, 256, 512) for f in ("f16", "i8", "f8")] + \
-    ["partial_192_f16.hip", "partial_192_f8.hip"]
+PARTIAL = [f"partial_{d}_{f}.hip" for d in (128, 256, 512)
+           for f in ("f16", "i8", "f8", "q4")] + ["partial_192_f16.hip", "partial_192_f8.hip"]
 SOURCES = ["api.cpp", "plan.cpp", "kernels.hip", *PARTIAL, "append.hip", "prefill.hip",
            "cascade.hip"]
 ARCH = "gfx950"

@@ -66,7 +66,8 @@ skvd_status check_append(const skvd_plan *plan, const skvd_append_args *a) {
   if (!plan) return set_err(SKVD_ERR_NULL, "plan is NULL");
   if (!a) return set_err(SKVD_ERR_NULL, "args is NULL");
   const skvd::Plan &p = plan->p;
-  const bool i8 = p.prm.kv_dtype == SKVD_KV_I8_F16SCALE32;
+  const bool q4 = p.prm.kv_dtype == SKVD_KV_Q4_0;
+  const bool i8 = p.prm.kv_dtype == SKVD_KV_I8_F16SCALE32 || q4;  // f16 scales per 32 elements
   const bool f8 = p.prm.kv_dtype == SKVD_KV_FP8_E4M3;
   const auto al = [](const void *ptr, uintptr_t n) { return (uintptr_t)ptr % n == 0; };
   if (a->num_tokens < 0 || a->batch < 0)
@@ -78,7 +79,8 @@ skvd_status check_append(const skvd_plan *plan, const skvd_append_args *a) {
   if (!a->k_pages || !a->v_pages || !a->page_table)
     return set_err(SKVD_ERR_NULL, "k_pages, v_pages and page_table must be non-NULL");
   if ((i8 || f8) && (!a->k_scales || !a->v_scales))
-    return set_err(SKVD_ERR_DTYPE, "%s cache needs k_scales and v_scales", i8 ? "int8" : "fp8");
+    return set_err(SKVD_ERR_DTYPE, "%s cache needs k_scales and v_scales",
+                   q4 ? "q4_0" : i8 ? "int8" : "fp8");
   if (!i8 && !f8 && (a->k_scales || a->v_scales))
     return set_err(SKVD_ERR_DTYPE, "f16 cache takes no scales");
   if (f8 && (!al(a->k_scales, 4) || !al(a->v_scales, 4)))
@@ -126,6 +128,9 @@ skvd_status check_prefill(const skvd_plan *plan, const skvd_decode_args *a) {
   if (p.prm.head_dim != 128 && p.prm.head_dim != 256)
     return set_err(SKVD_ERR_SHAPE, "the multi-token route supports head_dim 128 and 256 (plan "
                    "has %d)", p.prm.head_dim);
+  if (p.prm.kv_dtype == SKVD_KV_Q4_0)
+    return set_err(SKVD_ERR_DTYPE, "the multi-token route reads f16, int8 and fp8 caches, not "
+                   "q4_0");
   skvd_decode_args one = *a;
   one.q_per_seq = 1;  // the remaining checks do not depend on the token count
   return skvd::check_args(p, &one, p.ws_bytes, g_err, sizeof g_err);
@@ -242,12 +247,17 @@ skvd_status skvd_plan_describe(const skvd_plan *plan, char *buf, size_t n) {
   g_err[0] = 0;
   if (!plan || !buf || n == 0) return set_err(SKVD_ERR_NULL, "plan and buf must be non-NULL");
   const skvd::Plan &p = plan->p;
+  const int kv = p.prm.kv_dtype;
+  const char *fmt = kv == SKVD_KV_F16             ? "f16"
+                    : kv == SKVD_KV_FP8_E4M3      ? "fp8"
+                    : kv == SKVD_KV_Q4_0          ? "q4_0"
+                                                  : "int8";
   snprintf(buf, n,
            "plan Hq=%d Hkv=%d D=%d P=%d kv=%s max_batch=%d max_T=%d max_kv_len=%d cus=%d: "
            "blocks_per_split=%d splits=%d schedule=%s grid=%d heads_per_wg=%d reducer=%s "
            "hier_groups=%d rows_per_wg=%d workspace=%zu B",
            p.prm.num_qo_heads, p.prm.num_kv_heads, p.prm.head_dim, p.prm.page_size,
-           p.prm.kv_dtype == SKVD_KV_F16 ? "f16" : p.prm.kv_dtype == SKVD_KV_FP8_E4M3 ? "fp8" : "int8", p.prm.max_batch, p.prm.max_q_per_seq,
+           fmt, p.prm.max_batch, p.prm.max_q_per_seq,
            p.prm.max_kv_len, p.num_cus, p.bps, p.splits_cap,
            p.schedule == SKVD_SCHEDULE_BALANCED ? "balanced" : "static", p.grid_wgs,
            p.heads_per_wg,
@@ -352,7 +362,8 @@ skvd_status skvd_gather_debug(const skvd_plan *plan, const skvd_decode_args *arg
   if (!plan) return set_err(SKVD_ERR_NULL, "plan is NULL");
   skvd_status st = skvd::check_args(plan->p, args, plan->p.ws_bytes, g_err, sizeof g_err);
   if (st != SKVD_OK) return st;
-  const bool i8 = plan->p.prm.kv_dtype == SKVD_KV_I8_F16SCALE32;
+  const bool i8 = plan->p.prm.kv_dtype == SKVD_KV_I8_F16SCALE32 ||
+                  plan->p.prm.kv_dtype == SKVD_KV_Q4_0;  // per-row scales
   if (!dense_k || !dense_v || (i8 && (!dense_ks || !dense_vs)))
     return set_err(SKVD_ERR_NULL, "dense outputs must be non-NULL");
   if (max_len < 0 || max_len > plan->p.prm.max_kv_len)
@@ -432,6 +443,7 @@ skvd_status skvd_append(const skvd_plan *plan, const skvd_append_args *a, void *
   l.max_len = p.prm.max_kv_len;
   l.int8 = p.prm.kv_dtype == SKVD_KV_I8_F16SCALE32;
   l.fp8 = p.prm.kv_dtype == SKVD_KV_FP8_E4M3;
+  l.q4 = p.prm.kv_dtype == SKVD_KV_Q4_0;
   l.num_cus = p.num_cus;
   int e = skvd::launch_append(l, stream);
   return e ? hip_err(e, "append kernel launch") : SKVD_OK;

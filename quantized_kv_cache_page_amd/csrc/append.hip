@@ -1,5 +1,5 @@
-// Append kernel: new K/V rows into the paged cache, f16 verbatim, or int8 or fp8 quantized on
-// write.
+// Append kernel: new K/V rows into the paged cache, f16 verbatim, or int8, fp8 or q4_0
+// quantized on write.
 //
 // The slot of new token i is (page_table[b][j / P], j % P) for b = batch_idx[i], j =
 // positions[i]: the address the decode reads. Each lane owns 8 consecutive head_dim elements of
@@ -163,14 +163,76 @@ __device__ __forceinline__ uint2a quantize_fp8(half8a x, float s) {
   return w;
 }
 
-// KV: 0 f16, 1 int8 with per-32 f16 scales, 2 fp8 with the tensor scale tscale.
+template <int CTRL>
+__device__ __forceinline__ unsigned quad_dpp_u(unsigned x) {
+  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+
+// q4_0 (the published ggml q4_0 rule; the cache type is named beside q8_0 in 1bit-MONSTER/engine
+// issue #115, comment "Closing the remaining half of this issue"): lane r of a group's quad holds
+// its elements 8r .. 8r + 7. The group's extreme m -- largest magnitude, the first in element
+// order on a tie, NaN excluded, +0 when every magnitude is 0 -- comes from a quad max over keys
+// (f16 magnitude bits, then 31 - index, then the sign bit). Then, in f32 with no fused
+// operations (the rule rounds the product and the sum separately):
+//     d = m / -8,  r = 1 / d (0 if d = 0),  c = min(15, trunc(x * r + 8.5))  (NaN -> 8)
+// and the scale stored is f16(d). Lanes 0 and 1 of the quad return the group's code bytes
+// 8r .. 8r + 7 (codes 8r + i in the low nibbles, 16 + 8r + i from lane r + 2 in the high ones).
+__device__ __forceinline__ uint2a quantize_q4(half8a x, int r, _Float16 *scale) {
+#pragma clang fp contract(off)
+  unsigned key = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    // (bit_cast of a vector element would cast element 0: copy the element out first)
+    const _Float16 xe = x[e];
+    const unsigned h = __builtin_bit_cast(unsigned short, xe);
+    const unsigned mag = h & 0x7FFFu;
+    const unsigned k = mag > 0x7C00u ? 0u : (mag << 6) | ((31u - (8u * r + e)) << 1) | (h >> 15);
+    key = max(key, k);
+  }
+  key = max(key, quad_dpp_u<0xB1>(key));  // quad_perm [1,0,3,2]: lane xor 1
+  key = max(key, quad_dpp_u<0x4E>(key));  // quad_perm [2,3,0,1]: lane xor 2
+  const unsigned mag = key >> 6;
+  const float amax = (float)__builtin_bit_cast(_Float16, (unsigned short)mag);
+  const float m = mag == 0 ? 0.0f : (key & 1u ? -amax : amax);
+  const float d = m / -8.0f;
+  const float rd = d != 0.0f ? 1.0f / d : 0.0f;
+  unsigned w[2] = {0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float xr = (float)x[e] * rd;
+    const float t = xr + 8.5f;
+    const unsigned c = t != t ? 8u : (unsigned)min(15, (int)t);
+    w[e >> 2] |= c << (8 * (e & 3));
+  }
+  // lanes 0, 1 take the high nibbles from lanes 2, 3
+  const unsigned h0 = quad_dpp_u<0x4E>(w[0]), h1 = quad_dpp_u<0x4E>(w[1]);
+  *scale = (_Float16)d;
+  uint2a out;
+  out[0] = w[0] | (h0 << 4);
+  out[1] = w[1] | (h1 << 4);
+  return out;
+}
+
+// KV: 0 f16, 1 int8 with per-32 f16 scales, 2 fp8 with the tensor scale tscale, 3 q4_0.
 template <int D, int KV>
 __device__ __forceinline__ void store_row(const AppendLaunch &a, half8a x, void *pool,
                                           void *scales, float tscale, int64_t page, int slot,
                                           int kvh, int part) {
-  const int64_t off = page * a.page_stride + (int64_t)slot * a.tok_stride +
-                      (int64_t)kvh * a.head_stride + part * 8;
-  if constexpr (KV == 0) {
+  const int64_t row = page * a.page_stride + (int64_t)slot * a.tok_stride +
+                      (int64_t)kvh * a.head_stride;
+  const int64_t off = row + part * 8;
+  if constexpr (KV == 3) {
+    _Float16 sh;
+    const uint2a codes = quantize_q4(x, part & 3, &sh);
+    if ((part & 3) < 2)
+      __builtin_nontemporal_store(
+          codes, (uint2a *)((uint8_t *)pool + row + 16 * (part >> 2) + 8 * (part & 3)));
+    if ((part & 3) == 0) {
+      const int64_t soff = page * a.s_page_stride + (int64_t)slot * a.s_tok_stride +
+                           (int64_t)kvh * a.s_head_stride + (part >> 2);
+      ((_Float16 *)scales)[soff] = sh;
+    }
+  } else if constexpr (KV == 0) {
     __builtin_nontemporal_store(x, (half8a *)((_Float16 *)pool + off));
   } else if constexpr (KV == 2) {
     __builtin_nontemporal_store(quantize_fp8(x, tscale), (uint2a *)((int8_t *)pool + off));
@@ -248,7 +310,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendLaunch a) {
 
 template <int D>
 void launch_d(const AppendLaunch &a, hipStream_t st) {
-  if (a.fp8) append_kernel<D, 2><<<a.blocks, 256, 0, st>>>(a);
+  if (a.q4) append_kernel<D, 3><<<a.blocks, 256, 0, st>>>(a);
+  else if (a.fp8) append_kernel<D, 2><<<a.blocks, 256, 0, st>>>(a);
   else if (a.int8) append_kernel<D, 1><<<a.blocks, 256, 0, st>>>(a);
   else append_kernel<D, 0><<<a.blocks, 256, 0, st>>>(a);
 }
@@ -271,7 +334,7 @@ int launch_append(AppendLaunch a, void *stream) {
   const int64_t g0 = a.lanes_per_token / x;  // workgroups per whole number of tokens
   const int64_t toks = (a.num_tokens + kTokensPerLane - 1) / kTokensPerLane;
   const int64_t want = (toks * a.lanes_per_token + 255) / 256;
-  const int64_t cap = (a.fp8 ? 7LL : a.int8 ? 6LL : 8LL) * a.num_cus;
+  const int64_t cap = (a.fp8 ? 7LL : a.int8 || a.q4 ? 6LL : 8LL) * a.num_cus;
   int64_t blocks = want < cap ? want : cap;
   blocks = (blocks + g0 - 1) / g0 * g0;
   a.blocks = (unsigned)blocks;

@@ -307,20 +307,23 @@ static unsigned partial_grid(const LaunchArgs &la) {
 static int launch_partial_any(const Plan &p, const LaunchArgs &la, void *stream,
                               const KernelEvents &ev, bool dbg) {
   const unsigned grid = partial_grid(la);
-  const int kv = la.fp8 ? 2 : la.int8 ? 1 : 0;
+  const int kv = la.q4 ? 3 : la.fp8 ? 2 : la.int8 ? 1 : 0;
   switch (la.D) {
     case 128:
+      if (kv == 3) return launch_partial_128_3(p, la, grid, stream, ev, dbg);
       if (kv == 2) return launch_partial_128_2(p, la, grid, stream, ev, dbg);
       if (kv == 1) return launch_partial_128_1(p, la, grid, stream, ev, dbg);
       return launch_partial_128_0(p, la, grid, stream, ev, dbg);
     case 256:
+      if (kv == 3) return launch_partial_256_3(p, la, grid, stream, ev, dbg);
       if (kv == 2) return launch_partial_256_2(p, la, grid, stream, ev, dbg);
       if (kv == 1) return launch_partial_256_1(p, la, grid, stream, ev, dbg);
       return launch_partial_256_0(p, la, grid, stream, ev, dbg);
-    case 192:  // f16 and fp8 (the plan refuses int8 at head_dim 192)
+    case 192:  // f16 and fp8 (the plan refuses int8 and q4_0 at head_dim 192)
       if (kv == 2) return launch_partial_192_2(p, la, grid, stream, ev, dbg);
       return launch_partial_192_0(p, la, grid, stream, ev, dbg);
     default:
+      if (kv == 3) return launch_partial_512_3(p, la, grid, stream, ev, dbg);
       if (kv == 2) return launch_partial_512_2(p, la, grid, stream, ev, dbg);
       if (kv == 1) return launch_partial_512_1(p, la, grid, stream, ev, dbg);
       return launch_partial_512_0(p, la, grid, stream, ev, dbg);

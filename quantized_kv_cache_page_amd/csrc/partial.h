@@ -44,9 +44,10 @@ namespace skvd {
 // 0x64uu is 1024 + u, exact) and subtract 1152 with one packed f16 add per pair.
 constexpr unsigned kExp1024 = 0x64646464u;  // every byte 0x64: f16 high byte of 1024
 
+template <int BIAS = 1152>
 __device__ __forceinline__ half2v magic_pair(unsigned flipped, unsigned sel) {
   return __builtin_bit_cast(half2v, __builtin_amdgcn_perm(kExp1024, flipped, sel)) -
-         (half2v)(_Float16)1152;
+         (half2v)(_Float16)BIAS;
 }
 
 // 8 signed bytes (elements 0..7 in byte order) -> 8 f16.
@@ -115,6 +116,35 @@ __device__ __forceinline__ void h16_pairs(const half8 &a, const half8 &b, half2v
   }
 }
 
+// ----------------------------------------------------------------------------- q4_0 -> f16
+// A q4_0 dword (four code bytes, byte k holding element k of a run in its low nibble and
+// element k + 16 in its high nibble) gives 8 elements: the low nibbles (elements 0..3 of the
+// run) and the high nibbles (16..19). Each nibble n goes under the f16 exponent of 1024 with a
+// byte permute (1024 + n, exact) and one packed add of -1032 leaves n - 8, exact: the code's
+// value before its scale.
+constexpr unsigned kNib = 0x0F0F0F0Fu;
+
+// One dword -> 8 f16 (c - 8): low nibbles of bytes 0..3, then high nibbles of bytes 0..3.
+__device__ __forceinline__ half8 q4x8_to_h8(unsigned w) {
+  const unsigned lo = w & kNib, hi = (w >> 4) & kNib;
+  const half2v a = magic_pair<1032>(lo, 0x04010400u), b = magic_pair<1032>(lo, 0x04030402u);
+  const half2v c = magic_pair<1032>(hi, 0x04010400u), d = magic_pair<1032>(hi, 0x04030402u);
+  return half8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Two q4_0 dwords a (token t) and b (token t + 16) -> the 8 f16 pairs (a_i - 8, b_i - 8) in
+// q4x8_to_h8's element order: byte k of a and byte k of b side by side in the two halves, then
+// their low nibbles, and (shifted down) their high nibbles, under the exponent of 1024.
+__device__ __forceinline__ void q4_pairs(unsigned a, unsigned b, half2v *out) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const unsigned t = __builtin_amdgcn_perm(b, a, 0x0C000C00u | ((4u + k) << 16) | (unsigned)k);
+    out[k] = __builtin_bit_cast(half2v, (t & 0x000F000Fu) | 0x64006400u) - (half2v)(_Float16)1032;
+    out[4 + k] =
+        __builtin_bit_cast(half2v, ((t >> 4) & 0x000F000Fu) | 0x64006400u) - (half2v)(_Float16)1032;
+  }
+}
+
 // ----------------------------------------------------------------------------- fp8 (E4M3) -> f16
 // An OCP E4M3 byte s.eeee.mmm rewritten as the f16 bits s.0eeee.mmm0000000 is the f16 of its
 // value times 2^-8, exactly: the 4-bit exponent field under f16's bias 15 instead of E4M3's 7
@@ -180,6 +210,25 @@ __device__ __forceinline__ void group_transpose(uint4v &lo, uint4v &hi) {
   }
 }
 
+// q4_0 K: a lane loads the 16 code bytes of group g4 (of a run of four groups) of its token as
+// dwords 0..3. The same two-stage 4 x 4 transpose over dwords leaves dword g4 of group k in
+// slot k of lane group g4: MFMA step k contracts group k alone (elements 4*g4 .. +3 and
+// 16 + 4*g4 .. +3 of it from lane group g4), so its f32 result takes that group's scale.
+__device__ __forceinline__ void nib_transpose(uint4v &x) {
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {  // slot (1, d) of lane groups {0,1} <-> slot (0, d) of {2,3}
+    const auto r = __builtin_amdgcn_permlane32_swap(x[d], x[2 + d], false, false);
+    x[d] = r[0];
+    x[2 + d] = r[1];
+  }
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {  // slot (c, 1) of lane groups {0,2} <-> slot (c, 0) of {1,3}
+    const auto r = __builtin_amdgcn_permlane16_swap(x[2 * c], x[2 * c + 1], false, false);
+    x[2 * c] = r[0];
+    x[2 * c + 1] = r[1];
+  }
+}
+
 // ----------------------------------------------------------------------------- partial kernel
 // K and V rows are read once: non-temporal loads (evict-first in L2, no Infinity Cache
 // allocation) when each load instruction covers whole 128-byte lines between the lanes that
@@ -211,8 +260,9 @@ __device__ __forceinline__ int swz(int r, int c) {
 // D: head_dim (128/256). RB: 4-row quarters of the 16 MFMA rows in use per wave (R = G*T
 // query rows of a KV head; R <= 4*RB with one row tile, RB = 4 with more).
 // KV: cache format, 0 f16, 1 int8 with f16 scales per 32 elements, 2 fp8 E4M3 with one f32
-// scale per tensor; the two one-byte formats share the load layout (I8 below), and only int8
-// reads per-row scales (SC). FAST: page_size >= 16, so each 16-token
+// scale per tensor, 3 q4_0 (two 4-bit codes per byte) with f16 scales per 32 elements; the
+// two one-byte formats share the load layout (I8 below), int8 and q4_0 read per-row scales
+// (SC), and q4_0 loads 16 code bytes per group and 4 per V lane (Q4). FAST: page_size >= 16, so each 16-token
 // tile lies in one page and its page id is wave-uniform. CH: tokens per chunk (16, 32 or
 // 64): the K and V registers of a chunk bound how many waves fit on a SIMD.
 // PVM: P.V on the MFMA through an LDS copy of the chunk's V (dense when several query rows
@@ -234,13 +284,16 @@ constexpr int partial_waves() {
 template <int D, int RB, int KV, bool FAST, int CH, bool PVM, int HW, int RT, bool DBG>
 __global__ __launch_bounds__(64 * HW * RT)
 __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void partial_kernel(LaunchArgs a) {
-  constexpr bool I8 = KV != 0;  // one-byte elements
-  constexpr bool SC = KV == 1;  // int8: f16 scales per 32 elements of each row
+  constexpr bool I8 = KV != 0;  // elements of at most one byte
+  constexpr bool SC = KV == 1 || KV == 3;  // int8, q4_0: f16 scales per 32 elements of a row
   constexpr bool F8 = KV == 2;  // fp8 E4M3: one f32 scale per tensor
+  constexpr bool Q4 = KV == 3;  // q4_0: rows of D/2 bytes
   static_assert(RT == 1 || (HW == 1 && RB == 4 && PVM), "row tiles: one KV head per workgroup");
-  static_assert(!SC || D % 128 == 0, "int8 scale rows are read four groups at a time");
+  static_assert(!SC || D % 128 == 0, "scale rows are read four groups at a time");
   constexpr int NW = HW * RT;        // waves per workgroup
-  constexpr bool STREAM = RT == 1;   // row tiles re-read the same K/V rows: cached loads
+  // row tiles re-read the same K/V rows: cached loads. q4_0 rows (64 bytes at D=128) are half
+  // lines whose other half is the neighbouring KV head's, read by another wave: cached loads.
+  constexpr bool STREAM = RT == 1 && !Q4;
   static_assert(CH == 16 || CH == 32 || (CH == 64 && !PVM), "chunk");
   static_assert(PVM || CH % 32 == 0, "the vector P.V pairs 16-token tiles 2h and 2h + 1");
   constexpr int NT = CH / 16;    // 16-token score tiles per chunk
@@ -260,7 +313,8 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
   constexpr int RM = 4 * RB;     // query rows held (padded)
   constexpr int PSTR = CH + 4;   // row stride of the probability tile, floats
   constexpr int ROWB = 2 * D;    // bytes per V row in LDS (f16)
-  using Vec = std::conditional_t<I8, uint2v, half8>;  // one lane's 8 elements of a row
+  // one lane's 8 elements of a V row (q4_0: one dword, elements vq0 .. +3 and vq1 .. +3 below)
+  using Vec = std::conditional_t<Q4, unsigned, std::conditional_t<I8, uint2v, half8>>;
   using PvOp = std::conditional_t<CH == 32, half8, half4>;
 
   // LDS, one slice per wave:
@@ -413,8 +467,16 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
       const _Float16 *qp = (const _Float16 *)a.q + ((int64_t)b * T + t) * a.q_tok_stride +
                            (int64_t)(kvh * G + hg) * a.q_head_stride + 8 * g4;
 #pragma unroll
-      for (int k = 0; k < KSTEPS; ++k)  // (fp8 steps of a missing group: zeros)
-        qa[k] = kelem(k) < D ? *(const half8 *)(qp + kelem(k) - 8 * g4) : (half8)(_Float16)0;
+      for (int k = 0; k < KSTEPS; ++k) {  // (fp8 steps of a missing group: zeros)
+        if constexpr (Q4) {
+          // q4_0 step k: elements 4*g4 .. +3 and 16 + 4*g4 .. +3 of group k (the K dword's)
+          const half4 lo = *(const half4 *)(qp - 4 * g4 + 32 * k);
+          const half4 hi = *(const half4 *)(qp - 4 * g4 + 32 * k + 16);
+          qa[k] = half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        } else {
+          qa[k] = kelem(k) < D ? *(const half8 *)(qp + kelem(k) - 8 * g4) : (half8)(_Float16)0;
+        }
+      }
     } else {
 #pragma unroll
       for (int k = 0; k < KSTEPS; ++k) qa[k] = (half8)(_Float16)0;
@@ -446,6 +508,11 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
 
   bool clamped_any = false;
   const int vlane_tok = lane / LPR, vlane_el = 8 * (lane % LPR);
+  // head_dim elements of the lane's V slot as two runs of four: vq0 .. +3 and vq1 .. +3
+  // (contiguous for f16 and one-byte elements; q4_0: the low and high nibbles of the lane's
+  // dword, dword w of group g holding elements 32g + 4w .. +3 and 32g + 16 + 4w .. +3)
+  const int vq0 = Q4 ? 32 * (vlane_el >> 5) + ((vlane_el & 31) >> 1) : vlane_el;
+  const int vq1 = Q4 ? vq0 + 16 : vlane_el + 4;
   const bool vlane_ok = lane < TPS * LPR;  // (loads of the idle lanes re-read valid rows)
   // gather-debug variant: dense row (sequence b, position j, KV head kvh)
   auto dbg_row = [&](int j) __attribute__((always_inline)) -> int64_t {
@@ -475,11 +542,12 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
   // Per-lane token offsets within a 16-token tile, hoisted: with a non-negative stride,
   // min(token, limit) * stride = min(token * stride, limit * stride), the limit being scalar.
   const unsigned c16_tok = (unsigned)(c16 * (int)a.tok_stride);
-  const unsigned c16_stok = I8 ? (unsigned)(c16 * (int)a.s_tok_stride) : 0u;
+  const unsigned c16_stok = SC ? (unsigned)(c16 * (int)a.s_tok_stride) : 0u;
   const unsigned vt_tok = (unsigned)(vlane_tok * (int)a.tok_stride);
 
   Vec kb[NT][I8 ? 1 : KS];                   // f16 K: step k's 8 elements
-  uint4v kq[NT][I8 ? KB : 1][2];             // one-byte K: the lane's 32 bytes of group g4 + 4m
+  // one-byte K: the lane's 32 bytes of group g4 + 4m; q4_0: its 16 code bytes
+  uint4v kq[NT][I8 ? KB : 1][Q4 ? 1 : 2];
   uint2v ksr[NT][SC && !SCL ? KS / 4 : 1];   // int8 K (no shared scale load): the D/32 scales
                                              // of the lane's token, four per 8-byte load
   Vec vb[NS];
@@ -501,7 +569,12 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
         const char *base = kbase + row_offset(pg, jte & P1, kvh, a.page_stride, a.tok_stride,
                                               a.head_stride) * ES;
         const int lim = min(tok_end - 1 - jte, 15);  // last valid token of the tile
-        if constexpr (I8) {
+        if constexpr (Q4) {
+          const unsigned off = min(c16_tok, (unsigned)(lim * (int)a.tok_stride)) + 16 * g4;
+#pragma unroll
+          for (int m = 0; m < KB; ++m) kq[t][m][0] = kv_load<STREAM, uint4v>(base + off + 64 * m);
+        }
+        if constexpr (I8 && !Q4) {
           const unsigned off = min(c16_tok, (unsigned)(lim * (int)a.tok_stride)) + 32 * g4;
 #pragma unroll
           for (int m = 0; m < KB; ++m)
@@ -510,6 +583,8 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
               kq[t][m][h] = KS % 4 == 0 || g4 + 4 * m < KS
                                 ? kv_load<STREAM, uint4v>(base + off + 128 * m + 16 * h)
                                 : (uint4v)0u;
+        }
+        if constexpr (I8) {
           if constexpr (SC && !SCL) {
             const _Float16 *sb = ksc + row_offset(pg, jte & P1, kvh, a.s_page_stride,
                                                   a.s_tok_stride, a.s_head_stride);
@@ -531,7 +606,12 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
         clamped_any |= cl;
         const int64_t off = row_offset(pg, j & P1, kvh, a.page_stride, a.tok_stride,
                                        a.head_stride);
-        if constexpr (I8) {
+        if constexpr (Q4) {
+          const char *kp = kbase + off + 16 * g4;
+#pragma unroll
+          for (int m = 0; m < KB; ++m) kq[t][m][0] = kv_load<STREAM, uint4v>(kp + 64 * m);
+        }
+        if constexpr (I8 && !Q4) {
           const char *kp = kbase + off + 32 * g4;
 #pragma unroll
           for (int m = 0; m < KB; ++m)
@@ -540,6 +620,8 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
               kq[t][m][h] = KS % 4 == 0 || g4 + 4 * m < KS
                                 ? kv_load<STREAM, uint4v>(kp + 128 * m + 16 * h)
                                 : (uint4v)0u;
+        }
+        if constexpr (I8) {
           if constexpr (SC && !SCL) {
             const int64_t so = row_offset(pg, j & P1, kvh, a.s_page_stride, a.s_tok_stride,
                                           a.s_head_stride);
@@ -591,7 +673,7 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
         const int ts = (int)a.tok_stride;
         const unsigned tko = min(vt_tok + (unsigned)((js & 15) * ts),
                                  (unsigned)(min(tok_end - 1 - jte, 15) * ts));
-        const unsigned off = (tko + vlane_el) * ES;
+        const unsigned off = Q4 ? tko + vlane_el / 2 : (tko + vlane_el) * ES;
         vb[s2] = kv_load<STREAM, Vec>(base + off);
       } else {
         const int j = min(js + vlane_tok, tok_end - 1);
@@ -601,7 +683,7 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
         clamped_any |= cl;
         const int64_t off = row_offset(pg, j & P1, kvh, a.page_stride, a.tok_stride,
                                        a.head_stride);
-        vb[s2] = kv_load<STREAM, Vec>(vbase + (off + vlane_el) * ES);
+        vb[s2] = kv_load<STREAM, Vec>(vbase + (Q4 ? off + vlane_el / 2 : (off + vlane_el) * ES));
       }
     }
     if constexpr (SC && !SCL) {
@@ -653,7 +735,12 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
     // re-read and their scores are masked): a branch between an MFMA and the reads of its
     // result let the compiler's wait-state insertion miss the taken path.
     float4v S[NT];
-    if constexpr (SC) {
+    if constexpr (Q4) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int m = 0; m < KB; ++m) nib_transpose(kq[t][m][0]);
+    } else if constexpr (SC) {
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -685,18 +772,29 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
         }
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
-          const uint4v &q4 = kq[t][k >> 2][(k & 3) >> 1];
-          const unsigned w0 = q4[2 * (k & 1)], w1 = q4[2 * (k & 1) + 1];
-          const float4v p = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-              qa[k], i8x8_to_h8(uint2v{w0, w1}), (float4v)0.f, 0, 0, 0);
+          float4v p;
+          if constexpr (Q4) {
+            // q4_0: dword g4 of group k, its codes widened to c - 8
+            const unsigned w = kq[t][k >> 2][0][k & 3];
+            p = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[k], q4x8_to_h8(w), (float4v)0.f, 0, 0,
+                                                       0);
+            if constexpr (DBG) {
+              if (jk < tok_end) *(unsigned *)(a.dbg_k + dbg_row(jk) * (D / 2) + 16 * k + 4 * g4) = w;
+            }
+          } else {
+            const uint4v &q4 = kq[t][k >> 2][(k & 3) >> 1];
+            const unsigned w0 = q4[2 * (k & 1)], w1 = q4[2 * (k & 1) + 1];
+            p = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[k], i8x8_to_h8(uint2v{w0, w1}),
+                                                       (float4v)0.f, 0, 0, 0);
+            if constexpr (DBG) {
+              if (jk < tok_end) *(uint2v *)(a.dbg_k + dbg_row(jk) * D + kelem(k)) = uint2v{w0, w1};
+            }
+          }
           const float s = (float)sk[k];
 #pragma unroll
           for (int e = 0; e < 4; ++e) S[t][e] = __builtin_fmaf(s, p[e], S[t][e]);
           if constexpr (DBG) {
-            if (jk < tok_end) {
-              *(uint2v *)(a.dbg_k + dbg_row(jk) * D + kelem(k)) = uint2v{w0, w1};
-              if (g4 == 0) dbg_ks[dbg_row(jk) * (D / 32) + k] = sk[k];
-            }
+            if (jk < tok_end && g4 == 0) dbg_ks[dbg_row(jk) * (D / 32) + k] = sk[k];
           }
         }
       } else if constexpr (F8) {
@@ -760,7 +858,8 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
       for (int s2 = 0; s2 < NS; ++s2) {
         const int jv = c0 + TPS * s2 + vlane_tok;
         if (jv < tok_end && vlane_ok)
-          *(Vec *)(a.dbg_v + (dbg_row(jv) * D + vlane_el) * ES) = vb[s2];
+          *(Vec *)(a.dbg_v + (Q4 ? dbg_row(jv) * (D / 2) + vlane_el / 2
+                                 : (dbg_row(jv) * D + vlane_el) * ES)) = vb[s2];
       }
     }
     if constexpr (PVM) {
@@ -775,15 +874,26 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
 #pragma unroll
       for (int s2 = 0; s2 < NS; ++s2) {
         const int row = TPS * s2 + vlane_tok;
-        half8 h;
-        if constexpr (SC) {
-          h = i8x8_to_h8(vb[s2]);
-        } else if constexpr (F8) {
-          h = f8x8_to_h8(vb[s2]);
+        if constexpr (Q4) {
+          // the two runs of four elements (half chunks) at their columns
+          const half8 h = q4x8_to_h8(vb[s2]);
+          if (vlane_ok) {
+            *(half4 *)(v_lds + swz<ROWB>(row, vq0 >> 3) + ((vq0 & 7) << 1)) =
+                half4{h[0], h[1], h[2], h[3]};
+            *(half4 *)(v_lds + swz<ROWB>(row, vq1 >> 3) + ((vq1 & 7) << 1)) =
+                half4{h[4], h[5], h[6], h[7]};
+          }
         } else {
-          h = vb[s2];
+          half8 h;
+          if constexpr (SC) {
+            h = i8x8_to_h8(vb[s2]);
+          } else if constexpr (F8) {
+            h = f8x8_to_h8(vb[s2]);
+          } else {
+            h = vb[s2];
+          }
+          if (vlane_ok) *(half8 *)(v_lds + swz<ROWB>(row, lane % LPR)) = h;
         }
-        if (vlane_ok) *(half8 *)(v_lds + swz<ROWB>(row, lane % LPR)) = h;
       }
       if constexpr (SC && !SCL) {
         if (lane < CH) {
@@ -917,7 +1027,8 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
           }
 #pragma unroll
           for (int r = 0; r < RM; ++r) pp[r] *= sc;
-          i8_pairs(vb[s2], vb[s3], vp);
+          if constexpr (Q4) q4_pairs(vb[s2], vb[s3], vp);
+          else i8_pairs(vb[s2], vb[s3], vp);
         } else {
           h16_pairs(vb[s2], vb[s3], vp);
         }
@@ -1022,12 +1133,17 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
         half8 out;
 #pragma unroll
         for (int i = 0; i < 8; ++i) out[i] = (_Float16)(accv[r][i] * inv);
-        *(half8 *)((_Float16 *)a.o + row * D + vlane_el) = out;
+        if constexpr (Q4) {
+          *(half4 *)((_Float16 *)a.o + row * D + vq0) = half4{out[0], out[1], out[2], out[3]};
+          *(half4 *)((_Float16 *)a.o + row * D + vq1) = half4{out[4], out[5], out[6], out[7]};
+        } else {
+          *(half8 *)((_Float16 *)a.o + row * D + vlane_el) = out;
+        }
         if (a.lse && lane == 0) a.lse[row] = l > 0.f ? (mr[r] + __log2f(l)) * kLn2 : kNegInf;
       } else {
-        float *dst = a.ws_o + part_index(row, hg + G * t) * D + vlane_el;
-        *(float4v *)dst = float4v{accv[r][0], accv[r][1], accv[r][2], accv[r][3]} * vfac;
-        *(float4v *)(dst + 4) = float4v{accv[r][4], accv[r][5], accv[r][6], accv[r][7]} * vfac;
+        float *dst = a.ws_o + part_index(row, hg + G * t) * D;
+        *(float4v *)(dst + vq0) = float4v{accv[r][0], accv[r][1], accv[r][2], accv[r][3]} * vfac;
+        *(float4v *)(dst + vq1) = float4v{accv[r][4], accv[r][5], accv[r][6], accv[r][7]} * vfac;
         if (lane == 0) {
           float *ml = a.ws_ml + part_index(row, hg + G * t) * 2;
           ml[0] = mr[r];

@@ -51,9 +51,10 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
                 "num_kv_heads=%d", Hq, Hkv);
   if (D != 128 && D != 192 && D != 256 && D != 512)
     return fail(err, errn, SKVD_ERR_SHAPE, "head_dim=%d unsupported (128, 192, 256 or 512)", D);
-  if (D == 192 && prm.kv_dtype == SKVD_KV_I8_F16SCALE32)
-    return fail(err, errn, SKVD_ERR_SHAPE, "int8 cache at head_dim 192 unsupported (its six "
-                "group scales per row are not a whole number of the decode's 8-byte scale loads)");
+  if (D == 192 && (prm.kv_dtype == SKVD_KV_I8_F16SCALE32 || prm.kv_dtype == SKVD_KV_Q4_0))
+    return fail(err, errn, SKVD_ERR_SHAPE, "%s cache at head_dim 192 unsupported (its six "
+                "group scales per row are not a whole number of the decode's 8-byte scale loads)",
+                prm.kv_dtype == SKVD_KV_Q4_0 ? "q4_0" : "int8");
   if (!is_pow2(prm.page_size) || prm.page_size > 1024)
     return fail(err, errn, SKVD_ERR_SHAPE, "page_size=%d must be a power of two <= 1024",
                 prm.page_size);
@@ -73,7 +74,7 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
   if (R > 1024)
     return fail(err, errn, SKVD_ERR_SHAPE, "group*max_q_per_seq=%d exceeds 1024 rows", R);
   if (prm.kv_dtype != SKVD_KV_F16 && prm.kv_dtype != SKVD_KV_I8_F16SCALE32 &&
-      prm.kv_dtype != SKVD_KV_FP8_E4M3)
+      prm.kv_dtype != SKVD_KV_FP8_E4M3 && prm.kv_dtype != SKVD_KV_Q4_0)
     return fail(err, errn, SKVD_ERR_DTYPE, "kv_dtype=%d unknown", prm.kv_dtype);
   if (num_cus < 1) return fail(err, errn, SKVD_ERR_DEVICE, "num_cus=%d", num_cus);
   if (prm.force_reducer < 0 || prm.force_reducer > SKVD_REDUCER_NONE)
@@ -120,7 +121,8 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
   // and split, written then read back) at most ~3% of the split's K+V bytes.
   const double row_bytes = prm.kv_dtype == SKVD_KV_F16 ? 4.0 * D
                            : prm.kv_dtype == SKVD_KV_FP8_E4M3 ? 2.0 * D
-                                                              : 2.0 * (D + 2 * (D / 32));
+                           : prm.kv_dtype == SKVD_KV_Q4_0 ? 2.0 * (D / 2 + 2 * (D / 32))
+                                                          : 2.0 * (D + 2 * (D / 32));
   const double partial_bytes = 2.0 * R * (D + 2) * 4.0;
   int bps_min = (int)std::ceil(partial_bytes / (0.03 * kBlockTokens * row_bytes));
   if (bps_min < 1) bps_min = 1;
@@ -260,9 +262,11 @@ skvd_status check_args(const Plan &p, const skvd_decode_args *a, size_t ws_bytes
                        size_t errn) {
   if (!a) return fail(err, errn, SKVD_ERR_NULL, "args is NULL");
   const int D = p.prm.head_dim;
-  const bool i8 = p.prm.kv_dtype == SKVD_KV_I8_F16SCALE32;
+  const bool q4 = p.prm.kv_dtype == SKVD_KV_Q4_0;
+  const bool i8 = p.prm.kv_dtype == SKVD_KV_I8_F16SCALE32 || q4;  // f16 scales per 32 elements
   const bool f8 = p.prm.kv_dtype == SKVD_KV_FP8_E4M3;
-  const bool byte = i8 || f8;  // one-byte elements
+  const bool byte = i8 || f8;  // pools addressed in bytes
+  const char *fmt = q4 ? "q4_0" : i8 ? "int8" : "fp8";
   if (a->reserved != 0) return fail(err, errn, SKVD_ERR_SHAPE, "reserved must be 0");
   if (a->batch < 0 || a->batch > p.prm.max_batch)
     return fail(err, errn, SKVD_ERR_SHAPE, "batch=%d outside 0..max_batch=%d", a->batch,
@@ -274,15 +278,15 @@ skvd_status check_args(const Plan &p, const skvd_decode_args *a, size_t ws_bytes
     return fail(err, errn, SKVD_ERR_NULL, "q, k_pages, v_pages, page_table, kv_len and o "
                 "must be non-NULL");
   if (byte && (!a->k_scales || !a->v_scales))
-    return fail(err, errn, SKVD_ERR_DTYPE, "%s cache needs k_scales and v_scales",
-                i8 ? "int8" : "fp8");
+    return fail(err, errn, SKVD_ERR_DTYPE, "%s cache needs k_scales and v_scales", fmt);
   if (!byte && (a->k_scales || a->v_scales))
     return fail(err, errn, SKVD_ERR_DTYPE, "f16 cache takes no scales");
   if (f8 && (!aligned(a->k_scales, 4) || !aligned(a->v_scales, 4)))
     return fail(err, errn, SKVD_ERR_LAYOUT, "fp8 k_scale / v_scale must be 4-byte aligned");
   if (!std::isfinite(a->sm_scale))
     return fail(err, errn, SKVD_ERR_SHAPE, "sm_scale is not finite");
-  // Vector loads: 16 bytes of q, o, K and f16 V rows; 8 bytes of int8 / fp8 V rows.
+  // Vector loads: 16 bytes of q, o, K and f16 V rows; 8 bytes of int8 / fp8 V rows, 4 of
+  // q4_0's.
   const int64_t kv_vec = byte ? 16 : 8;  // elements per 16-byte load
   if (!aligned(a->q, 16) || a->q_tok_stride % 8 || a->q_head_stride % 8 || a->q_tok_stride < 0 ||
       a->q_head_stride < 0)
@@ -301,8 +305,8 @@ skvd_status check_args(const Plan &p, const skvd_decode_args *a, size_t ws_bytes
     return fail(err, errn, SKVD_ERR_LAYOUT, "scale pools must be 8-byte aligned with "
                 "non-negative strides that are multiples of 4 elements");
   // Within a 16-token tile the kernels address rows with 32-bit byte offsets.
-  const int64_t es = byte ? 1 : 2;
-  if ((16 * a->tok_stride + D) * es >= (int64_t(1) << 31) ||
+  const int64_t es = byte ? 1 : 2, row = q4 ? D / 2 : D;
+  if ((16 * a->tok_stride + row) * es >= (int64_t(1) << 31) ||
       (i8 && 16 * a->scale_tok_stride + D / 32 >= (int64_t(1) << 30)))
     return fail(err, errn, SKVD_ERR_LAYOUT, "token stride too large for 32-bit in-tile offsets");
   if (a->num_k_pages < 1 || a->num_v_pages < 1)
@@ -365,8 +369,9 @@ void fill_launch_args(const Plan &p, const skvd_decode_args &a, void *ws, Launch
   l.piece_min = p.piece_min;
   l.max_kv_len = p.prm.max_kv_len;
   l.hier_groups_cap = p.hier_groups_cap;
-  l.int8 = p.prm.kv_dtype != SKVD_KV_F16;  // one-byte elements
+  l.int8 = p.prm.kv_dtype != SKVD_KV_F16;  // elements of at most one byte
   l.fp8 = p.prm.kv_dtype == SKVD_KV_FP8_E4M3;
+  l.q4 = p.prm.kv_dtype == SKVD_KV_Q4_0;
   l.debug = p.prm.debug;
   char *w = (char *)ws;
   l.status = w ? (unsigned *)(w + p.off_status) : nullptr;

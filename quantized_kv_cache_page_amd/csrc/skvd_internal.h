@@ -61,8 +61,9 @@ struct LaunchArgs {
   int heads_per_wg;  // KV heads (waves) per partial-kernel workgroup; divides Hkv
   int row_tiles, row_groups, rows_per_group, sched_heads;  // as in Plan
   int seqs_per_lane;  // balanced schedule: sequences per lane of the share computation
-  int int8;         // one-byte elements (int8 with f16 group scales, or fp8)
+  int int8;         // elements of at most one byte (int8, fp8 or q4_0)
   int fp8;          // fp8 E4M3: ks / vs each point to one f32 tensor scale
+  int q4;           // q4_0: rows of D/2 bytes, f16 scales per 32 elements
   int debug;
   // partials (static: [rows_cap][part_stride]; balanced: [slots][heads_per_wg][G*T]):
   float *ws_ml;      // [..][2]  (max in log2 units, sum)
@@ -109,14 +110,17 @@ struct KernelEvents {
 SKVD_DECLARE_PARTIAL(128, 0)
 SKVD_DECLARE_PARTIAL(128, 1)
 SKVD_DECLARE_PARTIAL(128, 2)
+SKVD_DECLARE_PARTIAL(128, 3)
 SKVD_DECLARE_PARTIAL(256, 0)
 SKVD_DECLARE_PARTIAL(256, 1)
 SKVD_DECLARE_PARTIAL(256, 2)
+SKVD_DECLARE_PARTIAL(256, 3)
 SKVD_DECLARE_PARTIAL(192, 0)
 SKVD_DECLARE_PARTIAL(192, 2)
 SKVD_DECLARE_PARTIAL(512, 0)
 SKVD_DECLARE_PARTIAL(512, 1)
 SKVD_DECLARE_PARTIAL(512, 2)
+SKVD_DECLARE_PARTIAL(512, 3)
 #undef SKVD_DECLARE_PARTIAL
 
 // Append launch (append.hip): resolved on the host from the plan and skvd_append_args.
@@ -134,6 +138,7 @@ struct AppendLaunch {
   int64_t rows;        // num_tokens * Hkv
   int num_tokens, batch, Hkv, D, page_shift, max_len, int8;
   int fp8;              // fp8 E4M3 cache: ks / vs each point to one f32 tensor scale
+  int q4;               // q4_0 cache: rows of D/2 code bytes, f16 scales per 32 elements
   int num_cus;          // compute units of the plan's device
   int lanes_per_token;  // set by launch_append: Hkv * D / 8 (one lane per 8 elements of a row)
   int tok_step;         // set by launch_append: tokens the whole grid covers per step

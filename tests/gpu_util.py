@@ -28,10 +28,12 @@ def to_dev(prob, device="cuda:0"):
 def make_plan(prob, **kw):
     import quantized_kv_cache_page_amd as skvd
     k = prob["k_pages"]
-    s = dict(num_qo_heads=prob["q"].shape[1], num_kv_heads=k.shape[2], head_dim=k.shape[3],
+    D = prob["q"].shape[2]
+    s = dict(num_qo_heads=prob["q"].shape[1], num_kv_heads=k.shape[2], head_dim=D,
              page_size=k.shape[1],
-             kv_dtype={np.dtype(np.float16): "f16", np.dtype(np.int8): "i8",
-                       np.dtype(np.uint8): "f8"}[k.dtype],
+             kv_dtype="q4" if k.dtype == np.uint8 and 2 * k.shape[3] == D else
+             {np.dtype(np.float16): "f16", np.dtype(np.int8): "i8",
+              np.dtype(np.uint8): "f8"}[k.dtype],
              max_batch=len(prob["kv_len"]), max_q_per_seq=int(prob["q_per_seq"]),
              max_kv_len=max(int(prob["page_table"].shape[1] * k.shape[1]), 1), device=0)
     s.update(kw)

@@ -29,6 +29,7 @@ def paged_from_dense(rng, q, Kd, Vd, L, P, *, T=1, spare=3, extra_heads=0, Ks=No
     N = live + spare
     perm = rng.permutation(N)
     Hs = Hkv + extra_heads
+    q4 = q4 or (Kd.dtype == np.uint8 and 2 * D == q.shape[2])  # D/2 code bytes per row
     int8 = Kd.dtype == np.int8 or q4
     if q4:
         kbig = np.full((N, P, Hs, D), 0xFF, np.uint8)
@@ -80,8 +81,10 @@ def e4m3_values(x):
 
 
 def dequant(x, s):
-    """Stored int8 values times their f16 scale (one per 32 elements), or E4M3 bytes times the
-    tensor's f32 scale, in fp64."""
+    """Stored int8 values times their f16 scale (one per 32 elements), q4_0 code bytes (uint8
+    with f16 scales) as (c - 8) * scale, or E4M3 bytes times the tensor's f32 scale, in fp64."""
+    if x.dtype == np.uint8 and s is not None and np.asarray(s).dtype == np.float16:
+        return q4_values(x, s)
     if x.dtype == np.uint8:
         return e4m3_values(x) * float(np.asarray(s, np.float32).reshape(-1)[0])
     if s is None:
@@ -147,13 +150,16 @@ def random_dense(rng, B, Lmax, Hkv, D, int8=False):
 
 def quantize_dense(x, kv, rng_scale=None):
     """f32 dense rows -> the stored form of cache format kv: f16 values; int8 codes and f16
-    scales (the workload generator's quantizer); or E4M3 bytes (torch's nearest-even cast of
-    x / scale, clipped to +-448) with a [1] f32 tensor scale. Returns (stored, scales)."""
+    scales (the workload generator's quantizer); q4_0 code bytes and f16 scales (likewise); or
+    E4M3 bytes (torch's nearest-even cast of x / scale, clipped to +-448) with a [1] f32 tensor
+    scale. Returns (stored, scales)."""
     import workloads
     if kv == "f16":
         return x.astype(np.float16), None
     if kv == "i8":
         return workloads.quantize_int8(x.astype(np.float32))
+    if kv == "q4":
+        return workloads.quantize_q4(x.astype(np.float32))
     scale = np.float32(1 / 64 if rng_scale is None else rng_scale)
     y = np.clip(x.astype(np.float32) / scale, np.float32(-448), np.float32(448))
     b = torch.from_numpy(np.ascontiguousarray(y)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()

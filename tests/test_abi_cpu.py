@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol():
     for s in syms:
         assert hasattr(L, s), s
     assert set(syms) == set(bd.SIGNATURES), set(syms) ^ set(bd.SIGNATURES)
-    assert L.skvd_abi_version() == bd.ABI_VERSION == 10
+    assert L.skvd_abi_version() == bd.ABI_VERSION == 11
 
 
 def plan(**kw):
@@ -255,7 +255,7 @@ def test_fp8_plan_and_unsupported_routes():
     assert bd.skvd_prefill_check(p8.handle, d) == 0
     assert bd.skvd_prefill_check(p8.handle, good_args(p8, q_per_seq=512)) == 4  # no scales
     with pytest.raises(ValueError):
-        plan(kv_dtype="q4")
+        plan(kv_dtype="q5")
 
 
 def test_workspace_too_small():
@@ -354,6 +354,40 @@ def test_attention_routes_errors():
     # T above the plan's bound: the tiled route; its checks (here a bad q stride) apply
     assert bd.skvd_attention(p.handle, good_args(p, q_per_seq=64, q_head_stride=100), None, 0,
                              None) == 3
+
+
+@pytest.mark.parametrize("over,status", [
+    ({}, 0), (dict(k_scales=None), 4), (dict(v_scales=None), 4), (dict(k_pages=FAKE + 8), 3),
+    (dict(tok_stride=8 * 64 + 8), 3), (dict(tok_stride=8 * 64 + 16), 0),
+    (dict(head_stride=64 + 4), 3), (dict(scale_tok_stride=34), 3), (dict(k_scales=FAKE + 4), 3),
+])
+def test_decode_check_q4(over, status):
+    """q4_0 cache: pools addressed in bytes (rows of D/2 = 64 code bytes, strides multiples of
+    16 bytes), f16 scale pools laid out as int8's."""
+    p = plan(kv_dtype="q4")
+    a = good_args(p, i8=True, **dict(dict(page_stride=16 * 8 * 64, tok_stride=8 * 64,
+                                          head_stride=64), **over))
+    assert bd.skvd_decode_check(p.handle, a, p.workspace_bytes) == status
+
+
+def test_q4_plan_and_routes():
+    """q4_0 plans at head_dim 128, 256 and 512 (not 192); the append takes the scale pools;
+    the multi-token route refuses the format."""
+    p = plan(kv_dtype="q4")
+    assert p.kv_dtype == "q4" and "kv=q4_0" in p.describe() and p.info.heads_per_wg == 4
+    for D in (256, 512):
+        assert plan(kv_dtype="q4", head_dim=D).kv_dtype == "q4"
+    with pytest.raises(skvd.SkvdError) as e:
+        plan(kv_dtype="q4", head_dim=192)
+    assert e.value.status == 2
+    a = good_append_args(i8=True, page_stride=16 * 8 * 64, tok_stride=8 * 64, head_stride=64)
+    assert bd.skvd_append_check(p.handle, a) == 0
+    assert bd.skvd_append_check(p.handle, good_append_args(page_stride=16 * 8 * 64,
+                                                           tok_stride=8 * 64,
+                                                           head_stride=64)) == 4  # no scales
+    d = good_args(p, i8=True, q_per_seq=512, page_stride=16 * 8 * 64, tok_stride=8 * 64,
+                  head_stride=64)
+    assert bd.skvd_prefill_check(p.handle, d) == 4
 
 
 def test_plan_waves_per_cu_by_format():

@@ -90,6 +90,11 @@ CASES = [
     ("f16_d512_p16", 2, 2, 512, 16, "f16", (17, 300), 40, "nhd"),
     ("i8_d512_p16", 2, 4, 512, 16, "i8", (1, 65, 200)[:2], 64, "nhd"),
     ("f8_d512_p1", 2, 2, 512, 1, "f8", (9, 130), 130, "nhd"),
+    ("q4_d128_p16", 4, 8, 128, 16, "q4", (1, 65, 512, 33), 64, "nhd"),
+    ("q4_d256_p4", 2, 2, 256, 4, "q4", (7, 300), 300, "nhd"),
+    ("q4_d128_p1_mha", 2, 1, 128, 1, "q4", (50, 3), 50, "nhd"),
+    ("q4_d128_p16_hnd", 3, 8, 128, 16, "q4", (40, 16, 100), 25, "hnd"),
+    ("q4_d512_p16", 2, 4, 512, 16, "q4", (1, 65), 64, "nhd"),
 ]
 
 
@@ -153,6 +158,59 @@ def test_append_special_values():
     got = gpu_append(plan, prob, new)
     want = oracle_append(prob, new, plan.params.max_kv_len)
     assert_pools_equal(got, want, "special values")
+
+
+def test_append_q4_special_values():
+    """Groups that stress the q4_0 rule: grids of the rule (k * d with k = -8 at the extreme,
+    either sign of d), quotients x / d exactly halfway between integers (8.5 - x / |d| rounding
+    up), magnitude ties between elements of opposite sign (the first one wins), all-zero
+    groups (scale -0), f16 subnormals, values near f16's maximum, wide dynamic ranges, and NaN
+    and infinite elements."""
+    B, Hkv, D, P = 1, 2, 128, 16
+    s = workloads.spec(name="special_q4", batch=B, num_qo_heads=4, num_kv_heads=Hkv, head_dim=D,
+                       page_size=P, kv_dtype="q4", lens=("list", (64,)))
+    prob = workloads.generate(s, 39)
+    rng = np.random.default_rng(39)
+    N = 64
+    x = np.zeros((N, Hkv, D // 32, 32), np.float64)
+    for i in range(N):
+        for h in range(Hkv):
+            for g in range(D // 32):
+                kind = (i * 7 + h * 3 + g) % 8
+                k = rng.integers(-7, 8, size=32).astype(np.float64)
+                sgn = 1.0 if rng.random() < 0.5 else -1.0
+                if kind == 0:    # on the grid: k * d, the extreme -8 * d
+                    k[rng.integers(32)] = -8
+                    x[i, h, g] = k * sgn * 2.0 ** rng.integers(-12, 3)
+                elif kind == 1:  # halfway quotients: m = 8 (d = -1), x = k + 0.5
+                    x[i, h, g] = np.clip(k, -8, 6) + 0.5
+                    x[i, h, g, int(rng.integers(32))] = 8 * sgn
+                elif kind == 2:  # all zero, or a magnitude tie of opposite signs
+                    x[i, h, g] = 0
+                    if i % 2:
+                        a, b = rng.choice(32, 2, replace=False)
+                        x[i, h, g, a], x[i, h, g, b] = 3.0, -3.0
+                elif kind == 3:  # subnormal inputs
+                    x[i, h, g] = k * 2.0 ** -24
+                elif kind == 4:  # near f16's maximum
+                    x[i, h, g] = rng.uniform(-65504, 65504, 32)
+                elif kind == 5:  # wide dynamic range in one group
+                    x[i, h, g] = rng.standard_normal(32) * 10.0 ** rng.uniform(-4, 4, 32)
+                elif kind == 6:  # N(0, 1)
+                    x[i, h, g] = rng.standard_normal(32)
+                else:            # non-finite: NaN (left out of the maximum, code 8), and on
+                    x[i, h, g] = k  # odd tokens an infinity (scale -+inf, codes 8)
+                    x[i, h, g, int(rng.integers(32))] = np.nan
+                    if i % 2:
+                        x[i, h, g, int(rng.integers(32))] = np.inf * (1 if h else -1)
+    kn = x.reshape(N, Hkv, D).astype(np.float16)
+    vn = (-x[:, ::-1]).reshape(N, Hkv, D).astype(np.float16)
+    new = dict(k_new=kn, v_new=np.ascontiguousarray(vn), batch_idx=np.zeros(N, np.int32),
+               positions=rng.permutation(64).astype(np.int32))
+    plan = make_plan(prob)
+    got = gpu_append(plan, prob, new)
+    want = oracle_append(prob, new, plan.params.max_kv_len)
+    assert_pools_equal(got, want, "q4_0 special values")
 
 
 @pytest.mark.parametrize("scale", [2.0 ** -6, 3.0 / 16])
@@ -234,7 +292,7 @@ def test_append_workloads_full_size(name):
     assert_pools_equal(got, want, name)
 
 
-@pytest.mark.parametrize("kv", ["f16", "i8", "f8"])
+@pytest.mark.parametrize("kv", ["f16", "i8", "f8", "q4"])
 def test_append_then_decode(kv):
     """A decode step: append T new tokens per sequence at the end of each cache, then decode
     over the result on the GPU; the pools match the oracle's append bit for bit and the decode
@@ -298,7 +356,7 @@ def test_append_graph_capture_replay():
         torch.ones(1 << 20, device="cuda").sum()  # eager work between replays
 
 
-@pytest.mark.parametrize("kv", ["f16", "i8", "f8"])
+@pytest.mark.parametrize("kv", ["f16", "i8", "f8", "q4"])
 @pytest.mark.parametrize("form", ["halves", "interleaved", "layer"])
 def test_cache_views(kv, form):
     """K and V as views of one tensor -- the two halves of [2, pages, ...], the interleaved

@@ -72,6 +72,14 @@ SMALL = [
     ("d512_i8", 3, 1, 16, 4, 512, 16, "i8", ("list", (64, 900, 1700))),
     ("d512_i8_t4_p1", 2, 4, 8, 2, 512, 1, "i8", ("list", (5, 300))),
     ("d512_f8", 3, 1, 16, 4, 512, 16, "f8", ("list", (129, 800, 1300))),
+    ("q4_gqa4", 4, 1, 32, 8, 128, 16, "q4", ("list", (1, 65, 512, 2049))),  # q4_0 cache
+    ("q4_p1", 2, 1, 8, 2, 128, 1, "q4", ("list", (33, 200))),
+    ("q4_t4_d256", 2, 4, 8, 4, 256, 16, "q4", ("list", (4, 600))),
+    ("q4_t3_g2", 2, 3, 4, 2, 128, 8, "q4", ("list", (3, 400))),        # 6 rows: MFMA P.V
+    ("q4_t4_g4", 2, 4, 16, 4, 128, 16, "q4", ("list", (4, 900))),
+    ("q4_t2_g4_p4", 3, 2, 8, 2, 128, 4, "q4", ("list", (5, 64, 333))),
+    ("d512_q4", 3, 1, 16, 4, 512, 16, "q4", ("list", (64, 900, 1700))),
+    ("d512_q4_t4_p1", 2, 4, 8, 2, 512, 1, "q4", ("list", (5, 300))),
 ]
 
 
@@ -99,6 +107,8 @@ BALANCED = [
     ("mqa_d256", 9, 1, 4, 1, 256, "f16", (1, 300, 64, 65, 1200, 7, 0, 640, 2),
      dict(force_blocks_per_split=1, wgs_per_cu=2, num_cus=3)),
     ("t4_i8_d256", 5, 4, 8, 4, 256, "i8", (700, 4, 129, 1100, 64), dict(force_blocks_per_split=3)),
+    ("tiny_rows_q4", 64, 1, 8, 2, 128, "q4", tuple(int(x) for x in _rng.integers(0, 140, 64)),
+     dict(force_blocks_per_split=2, wgs_per_cu=1, num_cus=5)),
 ]
 
 
@@ -112,7 +122,7 @@ def test_balanced_schedule_edges(case):
     assert plan.schedule == "balanced"
 
 
-@pytest.mark.parametrize("kv", ["i8", "f16"])
+@pytest.mark.parametrize("kv", ["i8", "f16", "q4"])
 @pytest.mark.parametrize("hw", [1, 2, 4, 8])
 @pytest.mark.parametrize("schedule", ["balanced", "static"])
 @pytest.mark.parametrize("P", [16, 1])
@@ -138,7 +148,7 @@ def test_balanced_all_empty():
     assert (o.float() == 0).all() and torch.isneginf(lse).all()
 
 
-@pytest.mark.parametrize("kv", ["f16", "i8"])
+@pytest.mark.parametrize("kv", ["f16", "i8", "q4"])
 @pytest.mark.parametrize("red,bps", [("direct", 1), ("cooperative", 1), ("multipass", 1),
                                      ("hierarchical", 1), ("direct", 3), ("multipass", 7),
                                      ("hierarchical", 2), ("none", 1000)])
@@ -197,7 +207,7 @@ def test_split_invariance():
 
 
 def test_gather_bit_exact():
-    for kv, P in (("f16", 16), ("f16", 1), ("i8", 4), ("i8", 64)):
+    for kv, P in (("f16", 16), ("f16", 1), ("i8", 4), ("i8", 64), ("q4", 16), ("q4", 2)):
         s = spec(name="gather", batch=3, q_per_seq=1, num_qo_heads=4, num_kv_heads=2,
                  head_dim=128, page_size=P, kv_dtype=kv, lens=("list", (1, 190, 700)))
         prob = workloads.generate(s, 5)
@@ -210,7 +220,7 @@ def test_gather_bit_exact():
         ok, ov, oks, ovs = oracle.gather(prob, maxl)
         assert np.array_equal(dk.cpu().numpy().view(np.uint8), ok.view(np.uint8))
         assert np.array_equal(dv.cpu().numpy().view(np.uint8), ov.view(np.uint8))
-        if kv == "i8":
+        if kv in ("i8", "q4"):
             assert np.array_equal(dks.cpu().numpy().view(np.uint16), oks.view(np.uint16))
             assert np.array_equal(dvs.cpu().numpy().view(np.uint16), ovs.view(np.uint16))
         say(f"  gather {kv} P={P}: bit-exact")
@@ -395,6 +405,8 @@ ROWTILES = [
     ("g4_t8_d256_f8", 2, 8, 8, 2, 256, 4, "f8", (8, 800)),          # 32 rows at head_dim 256
     ("g8_t8_d192", 2, 8, 16, 2, 192, 16, "f16", (8, 900)),          # 64 rows at head_dim 192
     ("g8_t8_d512_i8", 2, 8, 16, 2, 512, 16, "i8", (8, 700)),        # 64 rows at head_dim 512
+    ("g8_t8_q4", 3, 8, 32, 4, 128, 16, "q4", (8, 700, 3000)),
+    ("g8_t8_d256_q4", 2, 8, 16, 2, 256, 16, "q4", (8, 1200)),
     ("g32_t1", 2, 1, 64, 2, 128, 16, "f16", (1, 3000)),             # 32 rows from a large group
 ]
 
@@ -427,7 +439,7 @@ def test_mtp_draft_32q_4kv_t8_all_reducers():
 
 # ------------------------------------------------------------------ more than 64 sequences
 @pytest.mark.parametrize("B", [65, 128, 256, 1000])
-@pytest.mark.parametrize("kv", ["f16", "i8"])
+@pytest.mark.parametrize("kv", ["f16", "i8", "q4"])
 def test_balanced_large_batch(kv, B):
     """Balanced shares over more than 64 sequences: several sequences per lane of the share
     computation, ragged lengths including empty sequences."""
@@ -476,3 +488,24 @@ def test_config_all_rows(cfg, qmult):
     ro, rl = oracle.decode(prob)
     compare(o, lse, ro, rl, what=f"config {cfg} q x{qmult} all {ro.shape[0]} rows")
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+
+
+@pytest.mark.parametrize("qmult", [1, 8])
+def test_q4_batch_all_rows(qmult):
+    """The int8 batch's shape (64 sequences, Zipf lengths 512..65536) over a q4_0 cache: every
+    row, in the benchmark's launch configuration."""
+    key = "q4_batch"
+    if key not in _WORKLOADS:
+        _WORKLOADS[key] = workloads.generate(workloads.VARIANT_CONFIGS[key], 5)
+    prob = dict(_WORKLOADS[key])
+    if qmult != 1:
+        prob["q"] = (prob["q"].astype(np.float32) * qmult).astype(np.float16)
+    s = prob["spec"]
+    say(f"case {key} q x{qmult}: L={list(prob['kv_len'])[:8]}...")
+    dev = to_dev(prob)
+    plan = make_plan(prob, max_kv_len=s.max_kv_len)
+    say(f"  {plan.describe()}")
+    o, lse = run(plan, prob, dev)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode(prob)
+    compare(o, lse, ro, rl, what=f"{key} q x{qmult} all {ro.shape[0]} rows")

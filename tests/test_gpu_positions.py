@@ -1,11 +1,11 @@
 """GPU tests that see which cache position the decode hot path read.
 
 * The hot path's own addressing, bit for bit: skvd_gather_debug runs the plan's partial-kernel
-  variant in a debug form that stores every K/V element and int8 scale at the point where the
-  decode consumes it (after the int8 lane transpose), at the position the kernel attributes it
-  to. Compared with the oracle's gather for every variant: f16 / int8 / fp8, head_dim 128 and
-  256, one to four row quarters, row tiles (more than 16 query rows per KV head) and row groups
-  (more than 64), 1 / 2 / 4 / 8 KV heads per workgroup, page sizes 1, 4, 16 and 64 (per-token
+  variant in a debug form that stores every K/V element and scale at the point where the decode
+  consumes it (after the int8 / q4_0 lane transposes), at the position the kernel attributes it
+  to. Compared with the oracle's gather for every variant: f16 / int8 / fp8 / q4_0, head_dim
+  128, 192, 256 and 512, one to four row quarters, row tiles (more than 16 query rows per KV
+  head) and row groups (more than 64), 1 / 2 / 4 / 8 KV heads per workgroup, page sizes 1, 4, 16 and 64 (per-token
   and per-tile page lookups), static and balanced schedules.
 * A one-hot dominant key (logit gap >= 40 over every other visible key, checked on the stored
   values) at the first and last token of pages, 16-token tiles, 32-token chunks, 64-token
@@ -85,7 +85,7 @@ def _gather_case(kv, D, T, Hq, Hkv, P, schedule, hw=0, lens=(1, 190, 700, 2100))
     tag = f"gather {kv} D={D} T={T} Hq={Hq} Hkv={Hkv} P={P} {schedule} hw={hw}: {plan.describe()}"
     assert np.array_equal(dk.cpu().numpy().view(np.uint8), ok.view(np.uint8)), tag + " K"
     assert np.array_equal(dv.cpu().numpy().view(np.uint8), ov.view(np.uint8)), tag + " V"
-    if kv == "i8":
+    if kv in ("i8", "q4"):
         assert np.array_equal(dks.cpu().numpy().view(np.uint16), oks.view(np.uint16)), tag + " Ks"
         assert np.array_equal(dvs.cpu().numpy().view(np.uint16), ovs.view(np.uint16)), tag + " Vs"
     say(f"  {tag}: bit-exact")
@@ -93,11 +93,11 @@ def _gather_case(kv, D, T, Hq, Hkv, P, schedule, hw=0, lens=(1, 190, 700, 2100))
 
 @pytest.mark.parametrize("schedule", ["balanced", "static"])
 @pytest.mark.parametrize("P", [16, 1, 64, 4])
-@pytest.mark.parametrize("kv", ["f16", "i8", "f8"])
+@pytest.mark.parametrize("kv", ["f16", "i8", "f8", "q4"])
 def test_hot_path_gather_bit_exact(kv, P, schedule):
     for D, T, Hq, Hkv in SHAPES:
-        if D == 192 and kv == "i8":
-            continue  # (the plan refuses int8 at head_dim 192)
+        if D == 192 and kv in ("i8", "q4"):
+            continue  # (the plan refuses int8 and q4_0 at head_dim 192)
         _gather_case(kv, D, T, Hq, Hkv, P, schedule)
     for hw in (1, 2, 8):
         _gather_case(kv, 128, 1, 32, 8, P, schedule, hw=hw)
@@ -109,7 +109,7 @@ def test_hot_path_gather_large_balanced_batch():
     rng = np.random.default_rng(7)
     for B in (65, 130, 300):
         lens = tuple(int(x) for x in rng.integers(0, 300, B))
-        for kv in ("f16", "i8"):
+        for kv in ("f16", "i8", "q4"):
             _gather_case(kv, 128, 1, 32, 8, 16, "balanced", lens=lens)
 
 
@@ -194,6 +194,13 @@ DOM = [
     ("f8_d192_t2", 2, 2, 8, 4, 192, 16, "f8", (3000, 700), {}),
     ("i8_d512", 2, 1, 16, 4, 512, 16, "i8", (3000, 700), {}),
     ("f16_d512_t4", 2, 4, 16, 4, 512, 16, "f16", (2500, 700), {}),
+    ("q4_long", 2, 1, 32, 8, 128, 16, "q4", (65536, 777), {}),
+    ("q4_p1", 2, 1, 8, 2, 128, 1, "q4", (5000, 129), {}),
+    ("q4_hw1", 3, 1, 32, 8, 128, 16, "q4", (5000, 2100, 300), dict(heads_per_wg=1)),
+    ("q4_t2_rb2", 2, 2, 16, 4, 128, 16, "q4", (4000, 600), {}),
+    ("q4_d256_t2", 2, 2, 8, 4, 256, 16, "q4", (3000, 700), {}),
+    ("q4_g8_t8", 2, 8, 32, 4, 128, 16, "q4", (3000, 900), {}),
+    ("q4_d512", 2, 1, 16, 4, 512, 16, "q4", (3000, 700), {}),
 ]
 
 
@@ -206,8 +213,9 @@ def test_dominant_key_position(case, schedule, variant):
     rng = np.random.default_rng(_seed(name, schedule, variant))
     # the plan first (its shape fixes the boundaries), then the problem
     probe = dict(q=np.zeros((B * T, Hq, D), np.float16),
-                 k_pages=np.zeros((1, P, Hkv, D), {"f16": np.float16, "i8": np.int8,
-                                                   "f8": np.uint8}[kv]),
+                 k_pages=np.zeros((1, P, Hkv, D // 2 if kv == "q4" else D),
+                                  {"f16": np.float16, "i8": np.int8, "f8": np.uint8,
+                                   "q4": np.uint8}[kv]),
                  kv_len=np.array(lens, np.int32), q_per_seq=T,
                  page_table=np.zeros((B, -(-max(lens) // P) + 2), np.int32))
     plan = make_plan(probe, schedule=schedule, **kw)
@@ -236,6 +244,8 @@ IDENT = [
     ("i8", 2, 4, 8, 4, 256, 16, (4, 3000)),
     ("f16", 2, 8, 32, 4, 128, 1, (8, 1500)),
     ("i8", 2, 8, 32, 4, 128, 16, (9, 2500)),
+    ("q4", 3, 1, 32, 8, 128, 16, (64, 2049, 5000)),
+    ("q4", 2, 4, 8, 4, 256, 16, (4, 3000)),
 ]
 
 

@@ -82,6 +82,13 @@ CONFIGS = {
 }
 
 
+# The int8 batch's shape over the other quantized cache: q4_0 codes with the same f16 scales
+# per 32 elements (the cache type the pages name beside q8_0).
+VARIANT_CONFIGS = {
+    "q4_batch": Spec("q4_batch", 64, 1, 32, 8, 128, 16, "q4", ("zipf", 1.1, 512, 65536)),
+}
+
+
 def config(i: int) -> Spec:
     return CONFIGS[int(i)]
 
