@@ -846,7 +846,7 @@ def main():
                         "max_dip_between_adjacent": round(max(0.0, 1 - g[1] / g[0],
                                                               1 - g[2] / g[1]), 4)}
         longp = {}
-        for L in (8192, 32768, 131072):
+        for L in (8192, 32768, 65536, 131072):
             sp = workloads.spec(name=f"long_{L}", batch=1, q_per_seq=1, num_qo_heads=32,
                                 num_kv_heads=8, head_dim=128, page_size=64, lens=("fixed", L),
                                 q_mult=2.0)
@@ -858,6 +858,10 @@ def main():
         s8 = dataclasses.replace(s8, kv_dtype="f8", name=f"{s8.name}_f8")
         res["fp8"] = decode_object(s8, 5, f"{s8.name}: the int8 batch's shape over OCP E4M3 "
                                           f"pools with one f32 scale per tensor")
+        # ... and over a q4_0 cache (4-bit codes, one f16 scale per 32 elements)
+        s4 = workloads.VARIANT_CONFIGS["q4_batch"]
+        res["q4_0"] = decode_object(s4, 5, f"{s4.name}: the int8 batch's shape over q4_0 pools "
+                                           f"(two 4-bit codes per byte, f16 scales per 32)")
         r, _, _ = time_append("prefill_i8", 40, 50, 10, rounds=3)
         res["append"] = {"workload": r["workload"], "us_per_call": round(r["us_per_call"], 3),
                          "us_min": round(r["us_min"], 3), "rounds": 3, "launches_per_round": 50,
