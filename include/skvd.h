@@ -227,15 +227,31 @@ typedef struct {
 } skvd_decode_args;
 
 /* Plan: validate the static shape, choose blocks per split and the reducer, and size the
- * workspace. Host only: no device allocation; with num_cus > 0 no HIP call at all. The
- * environment variable SKVD_LOG_DISPATCH=1 prints the resolved plan to stderr here (never
- * in a launch). On success *out owns a plan to free with skvd_plan_destroy. */
+ * workspace. This is the library's form of the selection step of 1bit-MONSTER/engine issue
+ * #115: comment "Root-caused" has a decode-split template chosen by the KV capacity and a
+ * reducer family by the number of 64-token producer blocks, and every candidate rejected
+ * ("all_rejected") past 2048 tokens; comment "Closing the remaining half of this issue" gives
+ * the capacity as ceil(n / 64) * 64 and covers any capacity with a multipass reducer. Here any
+ * max_kv_len >= 1 is planned (no length is rejected), the reducer follows the partial count,
+ * and each call derives its block counts from kv_len on the device, as that issue's comment
+ * "Deep-context decode failures were JIT SGPR exhaustion" derives the producer block count from
+ * the run-time token count rather than the compile-time capacity. Host only: no device
+ * allocation; with num_cus > 0 no HIP call at all. The environment variable
+ * SKVD_LOG_DISPATCH=1 prints the resolved plan to stderr here (never in a launch). On success
+ * *out owns a plan to free with skvd_plan_destroy; on failure *out is NULL and the
+ * status says why (see skvd_last_error). params and out must be non-NULL (SKVD_ERR_NULL). */
 skvd_status skvd_plan_create(const skvd_plan_params *params, skvd_plan **out);
+/* Frees a plan (NULL: no-op). The caller's workspace is the caller's to free. */
 void skvd_plan_destroy(skvd_plan *plan);
 /* Workspace bytes skvd_decode needs for this plan (0 for a NULL plan). */
 size_t skvd_plan_workspace_bytes(const skvd_plan *plan);
+/* What the plan resolved to, into *info (both non-NULL, else SKVD_ERR_NULL). */
 skvd_status skvd_plan_get_info(const skvd_plan *plan, skvd_plan_info *info);
-/* NUL-terminated one-line description (blocks per split, splits, reducer, bytes). */
+/* NUL-terminated one-line description of the resolved plan (blocks per split, splits,
+ * schedule, reducer, workspace bytes), truncated to buf_len - 1 characters: the counterpart of
+ * the dispatch log the pages turn on to confirm which kernel serves a given depth
+ * (GGML_HRX_LOG_DISPATCH=1, 1bit-MONSTER/engine issue #115, comments "Fixed" and "Closing the
+ * remaining half of this issue"). plan and buf non-NULL and buf_len > 0, else SKVD_ERR_NULL. */
 skvd_status skvd_plan_describe(const skvd_plan *plan, char *buf, size_t buf_len);
 
 /* Validation alone: the checks skvd_decode makes before launching, with no HIP call. */
@@ -441,9 +457,18 @@ skvd_status skvd_append_check(const skvd_plan *plan, const skvd_append_args *arg
  * anything is launched; a launch failure returns SKVD_ERR_HIP. */
 skvd_status skvd_append(const skvd_plan *plan, const skvd_append_args *args, void *stream);
 
+/* Errors are statuses returned before anything runs, never a fault, an abort or a silent
+ * fallback: the failures the pages trace were a selection that rejected every candidate
+ * ("all_rejected", 1bit-MONSTER/engine issue #115, comment "Root-caused") and a launch that
+ * returned res = -3 after the kernel's build failed (comment "Deep-context decode failures were
+ * JIT SGPR exhaustion"). skvd_status_string names a status (a static string; "unknown status"
+ * for other values). */
 const char *skvd_status_string(skvd_status status);
-/* Message of the last failed call on this thread ("" if none). */
+/* Message of the last failed call on this thread ("" if none): which argument or limit a
+ * status came from. The string is owned by the library and valid until this thread's next
+ * call. */
 const char *skvd_last_error(void);
+/* SKVD_ABI_VERSION of the built library; the Python binding refuses a mismatch. */
 int32_t skvd_abi_version(void);
 
 #ifdef __cplusplus
