@@ -245,16 +245,22 @@ __device__ __forceinline__ T kv_load(const char *p) {
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4v *lds_s4_ptr;
 
-// Byte offset of 16-byte chunk c of row r in a row-major LDS tile with rows of ROWB bytes: the
-// chunk index is XOR-swizzled by the row so that the transposed reads of 16 consecutive rows
-// at one column fall in different banks (by the row's low 4 bits when a row holds 16 or more
-// chunks in powers of two; rows of 24 chunks, head_dim 192, by its low 3 bits, which keeps the
-// chunk inside its aligned run of 8).
+// Byte offset of 16-byte chunk c of row r in a row-major LDS tile with rows of ROWB bytes (a
+// multiple of 128, so a row starts on bank 0 and a chunk's banks are set by c mod 8). The
+// chunk index is XOR-swizzled by the row so that both read patterns are free of bank
+// conflicts: (1) the transposed reads (ds_read_b64_tr_b16), where each 16-lane phase reads 32
+// contiguous bytes (two chunks 2j, 2j+1) of 4 consecutive rows, need those rows' chunk pairs in
+// 4 different 32-byte bank groups: swizzle bits 1-2 take the row's low 2 bits (bit 2 from row
+// bit 0, so that two consecutive rows written 4 chunks at a time also fill all 8 chunk slots);
+// (2) a 16-byte read of one chunk of 8 consecutive rows (8 lanes a phase) needs 8 different
+// chunks mod 8: bit 0 takes row bit 2 (and bit 3 row bit 3 when a row holds 16 or more chunks in
+// powers of two; rows of 24 chunks, head_dim 192, keep the chunk inside its aligned run of 8).
 template <int ROWB>
 __device__ __forceinline__ int swz(int r, int c) {
   constexpr int CPR = ROWB / 16;
-  constexpr int XM = (CPR & (CPR - 1)) == 0 ? 15 : 7;
-  return r * ROWB + ((c ^ (r & XM)) << 4);
+  constexpr bool P2 = (CPR & (CPR - 1)) == 0;
+  const int x = ((r & 1) << 2) | (r & 2) | ((r >> 2) & 1) | (P2 ? (r & 8) : 0);
+  return r * ROWB + ((c ^ x) << 4);
 }
 
 // D: head_dim (128/256). RB: 4-row quarters of the 16 MFMA rows in use per wave (R = G*T

@@ -44,11 +44,26 @@ constexpr float kPNegInf = -__builtin_huge_valf();
 constexpr float kPLn2 = 0.6931471805599453f;
 constexpr float kMFloor = -1e30f;  // running max before any visible score (keeps exp2 finite)
 
-// Byte offset of 16-byte chunk c of row r in an LDS tile with rows of ROWB bytes; the chunk is
-// XOR-swizzled by the row so that 16 rows read at one column hit different banks.
-template <int ROWB>
+// Byte offset of 16-byte chunk c of row r in an LDS tile with rows of ROWB bytes (256 or 512:
+// a row starts on bank 0, a chunk's banks are set by c mod 8). The chunk is XOR-swizzled so that
+// no access pattern is bank-conflicted:
+//  - transposed V reads fetch 32 contiguous bytes (chunks 2j, 2j+1) of 4 consecutive rows per
+//    16-lane phase: swizzle bits 1-2 take the row's low 2 bits (4 different 32-byte bank groups);
+//  - K reads fetch one chunk of 8 consecutive rows per 8-lane phase: the row swizzle is a
+//    bijection of the row's low 3 bits (8 different chunks mod 8);
+//  - f16 tile stores (head_dim 128) write 4 consecutive chunks of each of two rows per phase:
+//    the two rows' swizzles differ in bit 2 (row bit 0 goes to bit 2);
+//  - one-byte tile stores write chunk 4q + c of a row from its q-th thread (each widened 16-byte
+//    load fills 4 chunks): the column term moves chunk bit 3 to bit 1 and bit 4 to bit 0, so the
+//    threads of a row land on different chunks mod 8, and the two rows of a phase differ in
+//    swizzle bit 0 (row bit 0 goes to bit 0).
+// The reads see a column term that is constant over a read (one chunk, or a 2j / 2j+1 pair).
+template <int ROWB, bool ONEB>
 __device__ __forceinline__ int pswz(int r, int c) {
-  return r * ROWB + ((c ^ (r & 15)) << 4);
+  const int x = ONEB ? (((r & 1) ^ ((r >> 2) & 1)) | ((r & 3) << 1) | (r & 8))
+                     : (((r & 1) << 2) | (r & 2) | ((r >> 2) & 1) | (r & 8));
+  const int col = ONEB ? (((c >> 3) & 1) << 1) | ((c >> 4) & 1) : 0;
+  return r * ROWB + ((c ^ x ^ col) << 4);
 }
 
 template <int D>
@@ -65,8 +80,9 @@ __device__ __forceinline__ float rows4_max(float x) {
 }
 
 // One KV tile's rows held in registers between the global load and the LDS store. Each thread
-// serves one token of the tile (TPT threads per token) and N consecutive 16-byte chunks of its K
-// and V rows, so it reads one page-table entry and forms one row address per tile. The loads
+// serves one token of the tile (TPT threads per token) and N 16-byte chunks of its K and V rows
+// (f16: every TPT-th chunk from its own; one-byte formats: N consecutive chunks, one scale group),
+// so it reads one page-table entry and forms one row address per tile. The loads
 // are ordinary (cached): every query tile of the sequence reads the same K/V tiles, so they
 // should stay in L2 and the Infinity Cache (non-temporal loads here cost 12-37 %).
 template <int D, bool I8>
@@ -93,7 +109,8 @@ __device__ __forceinline__ void load_tile(const LaunchArgs &a, int b, int kvh, i
   using TR = TileRegs<D, I8>;
   const int P1 = (1 << a.page_shift) - 1;
   const int tok = min(kv0 + (int)threadIdx.x / TR::TPT, kv_last);  // tail re-reads (masked)
-  const int part0 = ((int)threadIdx.x % TR::TPT) * TR::N;
+  const int part0 = ((int)threadIdx.x % TR::TPT) * TR::N;  // one-byte: chunks part0 .. + N - 1
+  const int q0 = (int)threadIdx.x % TR::TPT;                 // f16: chunks q0 + TPT * n
   const int64_t pg = a.table[(int64_t)b * a.table_stride + (tok >> a.page_shift)];
   const int64_t pk = pg < 0 ? 0 : (pg >= a.num_k_pages ? a.num_k_pages - 1 : pg);
   const int64_t pv = pg < 0 ? 0 : (pg >= a.num_v_pages ? a.num_v_pages - 1 : pg);
@@ -101,12 +118,12 @@ __device__ __forceinline__ void load_tile(const LaunchArgs &a, int b, int kvh, i
   const int64_t rk = pk * a.page_stride + in_page;
   const int64_t rv = pv * a.page_stride + in_page;
   if constexpr (!I8) {
-    const pu4 *kp = (const pu4 *)((const _Float16 *)a.k + rk) + part0;
-    const pu4 *vp = (const pu4 *)((const _Float16 *)a.v + rv) + part0;
+    const pu4 *kp = (const pu4 *)((const _Float16 *)a.k + rk) + q0;
+    const pu4 *vp = (const pu4 *)((const _Float16 *)a.v + rv) + q0;
 #pragma unroll
     for (int n = 0; n < TR::N; ++n) {
-      r.k[n] = kp[n];
-      r.v[n] = vp[n];
+      r.k[n] = kp[TR::TPT * n];
+      r.v[n] = vp[TR::TPT * n];
     }
   } else {
     const pu4 *kp = (const pu4 *)((const int8_t *)a.k + rk) + part0;
@@ -218,20 +235,22 @@ __device__ __forceinline__ void store_tile(char *k_lds, char *v_lds, const TileR
   const int tok = (int)threadIdx.x / TR::TPT;
 #pragma unroll
   for (int n = 0; n < TR::N; ++n) {
-    const int part = ((int)threadIdx.x % TR::TPT) * TR::N + n;
+    // (f16: chunk q0 + TPT * n, so that the 4 threads of a token store 4 consecutive chunks)
+    const int part = I8 ? ((int)threadIdx.x % TR::TPT) * TR::N + n
+                        : (int)threadIdx.x % TR::TPT + TR::TPT * n;
     if constexpr (!I8) {
-      *(pu4 *)(k_lds + pswz<ROWB>(tok, part)) = r.k[n];
-      *(pu4 *)(v_lds + pswz<ROWB>(tok, part)) = r.v[n];
+      *(pu4 *)(k_lds + pswz<ROWB, false>(tok, part)) = r.k[n];
+      *(pu4 *)(v_lds + pswz<ROWB, false>(tok, part)) = r.v[n];
     } else {
       ph8 lo, hi;
       if constexpr (KV == 2) widen16_f8(r.k[n], &lo, &hi);
       else widen16(r.k[n], TR::kQuadScales ? qks : r.ks[n], &lo, &hi);
-      *(ph8 *)(k_lds + pswz<ROWB>(tok, 2 * part)) = lo;
-      *(ph8 *)(k_lds + pswz<ROWB>(tok, 2 * part + 1)) = hi;
+      *(ph8 *)(k_lds + pswz<ROWB, true>(tok, 2 * part)) = lo;
+      *(ph8 *)(k_lds + pswz<ROWB, true>(tok, 2 * part + 1)) = hi;
       if constexpr (KV == 2) widen16_f8(r.v[n], &lo, &hi);
       else widen16(r.v[n], TR::kQuadScales ? qvs : r.vs[n], &lo, &hi);
-      *(ph8 *)(v_lds + pswz<ROWB>(tok, 2 * part)) = lo;
-      *(ph8 *)(v_lds + pswz<ROWB>(tok, 2 * part + 1)) = hi;
+      *(ph8 *)(v_lds + pswz<ROWB, true>(tok, 2 * part)) = lo;
+      *(ph8 *)(v_lds + pswz<ROWB, true>(tok, 2 * part + 1)) = hi;
     }
   }
 }
@@ -356,7 +375,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(LaunchArgs a, int tpw, 
       for (int rs = 0; rs < RS; ++rs) s[rs][st] = pf4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const ph8 kf = *(const ph8 *)(k_lds + pswz<ROWB>(16 * st + c16, 4 * ks + g4));
+        const ph8 kf = *(const ph8 *)(k_lds + pswz<ROWB, I8>(16 * st + c16, 4 * ks + g4));
 #pragma unroll
         for (int rs = 0; rs < RS; ++rs)
           s[rs][st] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qv[rs][ks], s[rs][st], 0, 0, 0);
@@ -427,7 +446,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(LaunchArgs a, int tpw, 
           const int row = 32 * c + 16 * hh + 4 * g4 + (c16 >> 2);
           const int col = 16 * dt + 4 * (c16 & 3);
           const ps4 r4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_ps4)(const_cast<char *>(v_lds) + pswz<ROWB>(row, col >> 3) + ((col & 7) << 1)));
+              (lds_ps4)(const_cast<char *>(v_lds) + pswz<ROWB, I8>(row, col >> 3) + ((col & 7) << 1)));
           const ph4 hv = __builtin_bit_cast(ph4, r4);
 #pragma unroll
           for (int e = 0; e < 4; ++e) va[4 * hh + e] = hv[e];
