@@ -10,22 +10,23 @@
 // Work unit: one workgroup of 4 waves per (sequence b, KV head, tile of query tokens). Its
 // query rows (128 at head_dim 128, 64 at 256) are (token, head-of-group) pairs r = token * G +
 // g, so every wave reads the same KV head: K and V tiles of KT tokens are gathered through the
-// page table into LDS once and shared by the 4 waves (one or two sets of 16 rows each). Per KV tile a wave computes S^T = K Q^T with the
-// 16x16x32 f16 MFMA (A = 16 K rows from LDS, B = the wave's 16 query rows, held in registers),
-// so each lane holds one query row's scores (column lane % 16) for 4 tokens per 16-token
-// sub-tile; the online softmax (base 2) needs only per-lane work plus two cross-row lane swaps
-// (v_permlane32_swap, v_permlane16_swap) for the max, and the row sums come from one more MFMA
-// with an all-ones operand; the probabilities are already the B operand of O^T = V^T P^T, whose A operand (16
-// head_dim rows x 32 tokens of V) comes from LDS through transposing reads
-// (ds_read_b64_tr_b16). The token order inside the contraction is the one the score layout
-// gives (tokens 4g..4g+3 and 16+4g..16+4g+3 for lane group g); both operands use it.
+// page table into LDS once and shared by the 4 waves (one or two sets of 16 rows each). Per KV
+// tile a wave computes S^T = K Q^T with the 16x16x32 f16 MFMA (A = 16 K rows from LDS, B = the
+// wave's 16 query rows, held in registers), so each lane holds one query row's scores (column
+// lane % 16) for 4 tokens per 16-token sub-tile; the online softmax (base 2) needs only per-lane
+// work plus two cross-row lane swaps (v_permlane32_swap, v_permlane16_swap) for the max, and the
+// row sums come from one more MFMA with an all-ones operand; the probabilities are already the
+// B operand of O^T = V^T P^T, whose A operand (16 head_dim rows x 32 tokens of V) comes from LDS
+// through transposing reads (ds_read_b64_tr_b16). The token order inside the contraction is the
+// one the score layout gives (tokens 4g..4g+3 and 16+4g..16+4g+3 for lane group g); both
+// operands use it.
 //
 // Causal reading (the decode's): the T query tokens are the last T cached positions, token t
 // sees positions j <= kv_len - T + t. A workgroup walks positions [0, kv_len - T + t_last] in
-// tiles; the next tile's rows are loaded into registers while the current one is computed and
-// stored into the second of two LDS tile buffers, so one barrier per tile suffices. Two
-// workgroups share a CU (256 registers per lane each). Workgroups run heaviest (latest query
-// tiles) first.
+// tiles; the next tile's rows (the one-byte formats at head_dim 128: the next two tiles') are
+// loaded into registers while the current one is computed, and stored into the second of two
+// LDS tile buffers, so one barrier per tile suffices. Two workgroups share a CU (256 registers
+// per lane each). Workgroups run heaviest (latest query tiles) first.
 #include <hip/hip_runtime.h>
 
 #include "skvd_internal.h"
@@ -85,12 +86,12 @@ __device__ __forceinline__ float rows4_max(float x) {
 // so it reads one page-table entry and forms one row address per tile. The loads
 // are ordinary (cached): every query tile of the sequence reads the same K/V tiles, so they
 // should stay in L2 and the Infinity Cache (non-temporal loads here cost 12-37 %).
-template <int D, bool I8>
+template <int D, bool I8, int NTH>
 struct TileRegs {
   static constexpr int KT = kv_tile<D>();
   // f16: 16-byte chunks of 8 elements; int8: 16-byte chunks of 16 elements (+ their scale)
   static constexpr int CPR = I8 ? D / 16 : D / 8;  // chunks per row
-  static constexpr int TPT = 256 / KT;             // threads per token
+  static constexpr int TPT = NTH / KT;             // threads per token (NTH: the workgroup's)
   static constexpr int N = CPR / TPT;              // chunks per thread per tensor
   pu4 k[N], v[N];
   _Float16 ks[I8 ? N : 1], vs[I8 ? N : 1];
@@ -100,18 +101,28 @@ struct TileRegs {
   unsigned sq[2];
 };
 
+// The page-table entry of this thread's token in the KV tile at kv0 (a tail token re-reads the
+// tile's last one). Read one tile ahead of the tile's loads, so that its latency is not on the
+// loop's path.
+template <int D, bool I8, int NTH>
+__device__ __forceinline__ int tile_page(const LaunchArgs &a, int b, int kv0, int kv_last) {
+  using TR = TileRegs<D, I8, NTH>;
+  const int tok = min(kv0 + (int)threadIdx.x / TR::TPT, kv_last);
+  return a.table[(int64_t)b * a.table_stride + (tok >> a.page_shift)];
+}
+
 // KV: 0 f16, 1 int8 with per-32 f16 scales, 2 fp8 E4M3 with one f32 scale per tensor (the
-// one-byte formats share the int8 tile layout; only int8 loads per-row scales).
-template <int D, int KV>
-__device__ __forceinline__ void load_tile(const LaunchArgs &a, int b, int kvh, int kv0, int kv_last,
-                                          TileRegs<D, KV != 0> &r) {
+// one-byte formats share the int8 tile layout; only int8 loads per-row scales). pg: the
+// thread's tile_page entry for this tile.
+template <int D, int KV, int NTH>
+__device__ __forceinline__ void load_tile(const LaunchArgs &a, int kvh, int kv0, int kv_last,
+                                          int pg, TileRegs<D, KV != 0, NTH> &r) {
   constexpr bool I8 = KV != 0;
-  using TR = TileRegs<D, I8>;
+  using TR = TileRegs<D, I8, NTH>;
   const int P1 = (1 << a.page_shift) - 1;
   const int tok = min(kv0 + (int)threadIdx.x / TR::TPT, kv_last);  // tail re-reads (masked)
   const int part0 = ((int)threadIdx.x % TR::TPT) * TR::N;  // one-byte: chunks part0 .. + N - 1
   const int q0 = (int)threadIdx.x % TR::TPT;                 // f16: chunks q0 + TPT * n
-  const int64_t pg = a.table[(int64_t)b * a.table_stride + (tok >> a.page_shift)];
   const int64_t pk = pg < 0 ? 0 : (pg >= a.num_k_pages ? a.num_k_pages - 1 : pg);
   const int64_t pv = pg < 0 ? 0 : (pg >= a.num_v_pages ? a.num_v_pages - 1 : pg);
   const int64_t in_page = (int64_t)(tok & P1) * a.tok_stride + (int64_t)kvh * a.head_stride;
@@ -217,10 +228,11 @@ __device__ __forceinline__ unsigned quad_bcast(unsigned x) {
   return (unsigned)__builtin_amdgcn_mov_dpp((int)x, L * 0x55, 0xF, 0xF, false);
 }
 
-template <int D, int KV>
-__device__ __forceinline__ void store_tile(char *k_lds, char *v_lds, const TileRegs<D, KV != 0> &r) {
+template <int D, int KV, int NTH>
+__device__ __forceinline__ void store_tile(char *k_lds, char *v_lds,
+                                           const TileRegs<D, KV != 0, NTH> &r) {
   constexpr bool I8 = KV != 0;
-  using TR = TileRegs<D, I8>;
+  using TR = TileRegs<D, I8, NTH>;
   _Float16 qks = 0, qvs = 0;  // kQuadScales: this thread's group (its quad index) of K and V
   if constexpr (TR::kQuadScales) {
     const unsigned q = threadIdx.x & 3u;
@@ -260,8 +272,21 @@ __device__ __forceinline__ void store_tile(char *k_lds, char *v_lds, const TileR
 template <int D>
 constexpr int row_sets() { return D == 128 ? 2 : 1; }
 
+// Waves per workgroup: 4, two workgroups per CU (8 waves sharing each tile, one workgroup per
+// CU, measured no faster for f16 and slower for the one-byte formats).
+template <int D>
+constexpr int prefill_waves() { return 4; }
+
+// Two tiles of loads in flight for the one-byte formats at head_dim 128 (their register stage is
+// half of f16's); f16 and head_dim 256 keep one (a second stage would not fit in the registers
+// of two workgroups per CU).
 template <int D, int KV>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(LaunchArgs a, int tpw, int qtiles) {
+constexpr bool prefetch_two() { return KV != 0 && D == 128; }
+
+template <int D, int KV, int NW>
+__global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_kernel(LaunchArgs a, int tpw,
+                                                                         int qtiles) {
+  constexpr int NTH = 64 * NW;  // threads per workgroup
   constexpr bool I8 = KV != 0;
   constexpr int KT = kv_tile<D>();
   constexpr int RS = row_sets<D>();
@@ -354,114 +379,138 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(LaunchArgs a, int tpw, 
   }
 
   const int ntiles = kv_end > 0 ? (kv_end + KT - 1) / KT : 0;
-  TileRegs<D, I8> regs;  // (I8: the one-byte layout)
+  // Tile loads run ahead of their use: with PF2 two tiles (the next one waits in registers while
+  // the one after it is being fetched), otherwise one. The page-table entries run one more tile
+  // ahead, so that no load waits on a page lookup.
+  constexpr bool PF2 = prefetch_two<D, KV>();
+  TileRegs<D, I8, NTH> ra, rb;  // (I8: the one-byte layout)
+  int pg_ahead = 0;        // the page entry of the next tile to be loaded
   if (ntiles > 0) {
-    load_tile<D, KV>(a, b, kvh, 0, kv_end - 1, regs);
-    store_tile<D, KV>(kv_lds[0][0], kv_lds[0][1], regs);
+    load_tile<D, KV, NTH>(a, kvh, 0, kv_end - 1, tile_page<D, I8, NTH>(a, b, 0, kv_end - 1), ra);
+    if (ntiles > 1) pg_ahead = tile_page<D, I8, NTH>(a, b, KT, kv_end - 1);
+    store_tile<D, KV, NTH>(kv_lds[0][0], kv_lds[0][1], ra);
+    if (PF2 && ntiles > 1) {
+      load_tile<D, KV, NTH>(a, kvh, KT, kv_end - 1, pg_ahead, ra);
+      if (ntiles > 2) pg_ahead = tile_page<D, I8, NTH>(a, b, 2 * KT, kv_end - 1);
+    }
   }
   __syncthreads();
-  for (int it = 0; it < ntiles; ++it) {
+  // One KV tile: it is read from LDS buffer it & 1; `held` holds the next tile (PF2; loaded in
+  // the previous step) or receives it (one stage), `fetch` receives the tile after it (PF2).
+  auto step = [&](int it, TileRegs<D, I8, NTH> &held, TileRegs<D, I8, NTH> &fetch)
+                  __attribute__((always_inline)) {
     const int kv0 = it * KT;
-    const bool more = it + 1 < ntiles;
     const char *k_lds = kv_lds[it & 1][0];
     const char *v_lds = kv_lds[it & 1][1];
-    if (more) load_tile<D, KV>(a, b, kvh, kv0 + KT, kv_end - 1, regs);
-
-    // ---- S^T = K Q^T: lane holds row c16's scores for tokens 16 st + 4 g4 + e
-    pf4 s[RS][NST];
-#pragma unroll
-    for (int st = 0; st < NST; ++st) {
-#pragma unroll
-      for (int rs = 0; rs < RS; ++rs) s[rs][st] = pf4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const ph8 kf = *(const ph8 *)(k_lds + pswz<ROWB, I8>(16 * st + c16, 4 * ks + g4));
-#pragma unroll
-        for (int rs = 0; rs < RS; ++rs)
-          s[rs][st] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qv[rs][ks], s[rs][st], 0, 0, 0);
-      }
+    const int ahead = PF2 ? it + 2 : it + 1;  // the tile this step starts loading
+    if (ahead < ntiles) {
+      load_tile<D, KV, NTH>(a, kvh, ahead * KT, kv_end - 1, pg_ahead, PF2 ? fetch : held);
+      if (ahead + 1 < ntiles) pg_ahead = tile_page<D, I8, NTH>(a, b, (ahead + 1) * KT, kv_end - 1);
     }
-    // ---- mask (only tiles that reach past the first row's limit), scale (base 2), online
-    // softmax per row set. The reference max m is raised only when a score exceeds it by more
-    // than 2^8 in weight (then the accumulators are rescaled); otherwise probabilities up to 2^8
-    // are taken against the old reference, which the final o = acc / l and lse = m + log2 l
-    // absorb exactly.
-    const bool need_mask = kv0 + KT - 1 > L - T + t0;  // workgroup-uniform
-    ph8 pb[RS][NCH];
+
+      // ---- S^T = K Q^T: lane holds row c16's scores for tokens 16 st + 4 g4 + e
+      pf4 s[RS][NST];
 #pragma unroll
-    for (int rs = 0; rs < RS; ++rs) {
-      // the max of the unscaled scores (c > 0), scaled once per row
-      float mx = kPNegInf;
-      if (need_mask) {
+      for (int st = 0; st < NST; ++st) {
+#pragma unroll
+        for (int rs = 0; rs < RS; ++rs) s[rs][st] = pf4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const ph8 kf = *(const ph8 *)(k_lds + pswz<ROWB, I8>(16 * st + c16, 4 * ks + g4));
+#pragma unroll
+          for (int rs = 0; rs < RS; ++rs)
+            s[rs][st] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qv[rs][ks], s[rs][st], 0, 0, 0);
+        }
+      }
+      // ---- mask (only tiles that reach past the first row's limit), scale (base 2), online
+      // softmax per row set. The reference max m is raised only when a score exceeds it by more
+      // than 2^8 in weight (then the accumulators are rescaled); otherwise probabilities up to 2^8
+      // are taken against the old reference, which the final o = acc / l and lse = m + log2 l
+      // absorb exactly.
+      const bool need_mask = kv0 + KT - 1 > L - T + t0;  // workgroup-uniform
+      ph8 pb[RS][NCH];
+#pragma unroll
+      for (int rs = 0; rs < RS; ++rs) {
+        // the max of the unscaled scores (c > 0), scaled once per row
+        float mx = kPNegInf;
+        if (need_mask) {
+#pragma unroll
+          for (int st = 0; st < NST; ++st)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int pos = kv0 + 16 * st + 4 * g4 + e;
+              const float v = pos <= limit[rs] ? s[rs][st][e] : kPNegInf;
+              s[rs][st][e] = v;
+              mx = fmaxf(mx, v);
+            }
+        } else {
+#pragma unroll
+          for (int st = 0; st < NST; ++st)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mx = fmaxf(mx, s[rs][st][e]);
+        }
+        mx = rows4_max(mx) * c;
+        const bool raise = mx > m[rs] + 8.f;
+        if (__any(raise)) {
+          const float m_new = raise ? mx : m[rs];
+          const float alpha = __builtin_amdgcn_exp2f(m[rs] - m_new);
+          m[rs] = m_new;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) lacc[rs][e] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[rs][dt][e] *= alpha;
+        }
 #pragma unroll
         for (int st = 0; st < NST; ++st)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            s[rs][st][e] = __builtin_amdgcn_exp2f(fmaf(s[rs][st][e], c, -m[rs]));
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int pos = kv0 + 16 * st + 4 * g4 + e;
-            const float v = pos <= limit[rs] ? s[rs][st][e] : kPNegInf;
-            s[rs][st][e] = v;
-            mx = fmaxf(mx, v);
+            pb[rs][c][e] = (_Float16)s[rs][2 * c][e];
+            pb[rs][c][4 + e] = (_Float16)s[rs][2 * c + 1][e];
           }
-      } else {
-#pragma unroll
-        for (int st = 0; st < NST; ++st)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) mx = fmaxf(mx, s[rs][st][e]);
       }
-      mx = rows4_max(mx) * c;
-      const bool raise = mx > m[rs] + 8.f;
-      if (__any(raise)) {
-        const float m_new = raise ? mx : m[rs];
-        const float alpha = __builtin_amdgcn_exp2f(m[rs] - m_new);
-        m[rs] = m_new;
+      // ---- O^T += V^T P^T, 32 tokens per MFMA
 #pragma unroll
-        for (int e = 0; e < 4; ++e) lacc[rs][e] *= alpha;
+      for (int c = 0; c < NCH; ++c) {
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
+        for (int dt = 0; dt < NDT; ++dt) {
+          ph8 va;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[rs][dt][e] *= alpha;
-      }
+          for (int hh = 0; hh < 2; ++hh) {
+            // lane (g4, c16) receives column 16 dt + c16 of tokens 32 c + 16 hh + 4 g4 + 0..3
+            const int row = 32 * c + 16 * hh + 4 * g4 + (c16 >> 2);
+            const int col = 16 * dt + 4 * (c16 & 3);
+            const ps4 r4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_ps4)(const_cast<char *>(v_lds) + pswz<ROWB, I8>(row, col >> 3) + ((col & 7) << 1)));
+            const ph4 hv = __builtin_bit_cast(ph4, r4);
 #pragma unroll
-      for (int st = 0; st < NST; ++st)
+            for (int e = 0; e < 4; ++e) va[4 * hh + e] = hv[e];
+          }
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          s[rs][st][e] = __builtin_amdgcn_exp2f(fmaf(s[rs][st][e], c, -m[rs]));
-#pragma unroll
-      for (int c = 0; c < NCH; ++c)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pb[rs][c][e] = (_Float16)s[rs][2 * c][e];
-          pb[rs][c][4 + e] = (_Float16)s[rs][2 * c + 1][e];
-        }
-    }
-    // ---- O^T += V^T P^T, 32 tokens per MFMA
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        ph8 va;
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          // lane (g4, c16) receives column 16 dt + c16 of tokens 32 c + 16 hh + 4 g4 + 0..3
-          const int row = 32 * c + 16 * hh + 4 * g4 + (c16 >> 2);
-          const int col = 16 * dt + 4 * (c16 & 3);
-          const ps4 r4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_ps4)(const_cast<char *>(v_lds) + pswz<ROWB, I8>(row, col >> 3) + ((col & 7) << 1)));
-          const ph4 hv = __builtin_bit_cast(ph4, r4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) va[4 * hh + e] = hv[e];
+          for (int rs = 0; rs < RS; ++rs)
+            acc[rs][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[rs][c], acc[rs][dt], 0, 0, 0);
         }
 #pragma unroll
         for (int rs = 0; rs < RS; ++rs)
-          acc[rs][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[rs][c], acc[rs][dt], 0, 0, 0);
+          lacc[rs] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[rs][c], lacc[rs], 0, 0, 0);
       }
-#pragma unroll
-      for (int rs = 0; rs < RS; ++rs)
-        lacc[rs] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[rs][c], lacc[rs], 0, 0, 0);
-    }
-    // the other buffer was last read in the previous iteration, which every wave has left
-    if (more) store_tile<D, KV>(kv_lds[(it + 1) & 1][0], kv_lds[(it + 1) & 1][1], regs);
+    // the other buffer was last read in the previous step, which every wave has left
+    if (it + 1 < ntiles) store_tile<D, KV, NTH>(kv_lds[(it + 1) & 1][0], kv_lds[(it + 1) & 1][1], held);
     __syncthreads();  // tile it+1 is in LDS, and every wave is done reading tile it
+  };
+  if constexpr (PF2) {
+    for (int it = 0; it < ntiles; it += 2) {  // (unrolled by two: the stages swap roles)
+      step(it, ra, rb);
+      if (it + 1 < ntiles) step(it + 1, rb, ra);
+    }
+  } else {
+    for (int it = 0; it < ntiles; ++it) step(it, ra, ra);
   }
 
   // ---- epilogue: row sums across the four lane groups, normalize, write o and lse
@@ -486,12 +535,13 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(LaunchArgs a, int tpw, 
 
 template <int D>
 void launch_pd(const LaunchArgs &a, hipStream_t st) {
-  const int tpw = 64 * row_sets<D>() / a.G;  // query tokens per workgroup: its rows / G
+  constexpr int NW = prefill_waves<D>();
+  const int tpw = 16 * NW * row_sets<D>() / a.G;  // query tokens per workgroup: its rows / G
   const int qtiles = (a.T + tpw - 1) / tpw;
   const unsigned grid = (unsigned)qtiles * a.Hkv * a.batch;
-  if (a.fp8) prefill_kernel<D, 2><<<grid, 256, 0, st>>>(a, tpw, qtiles);
-  else if (a.int8) prefill_kernel<D, 1><<<grid, 256, 0, st>>>(a, tpw, qtiles);
-  else prefill_kernel<D, 0><<<grid, 256, 0, st>>>(a, tpw, qtiles);
+  if (a.fp8) prefill_kernel<D, 2, NW><<<grid, 64 * NW, 0, st>>>(a, tpw, qtiles);
+  else if (a.int8) prefill_kernel<D, 1, NW><<<grid, 64 * NW, 0, st>>>(a, tpw, qtiles);
+  else prefill_kernel<D, 0, NW><<<grid, 64 * NW, 0, st>>>(a, tpw, qtiles);
 }
 
 }  // namespace
