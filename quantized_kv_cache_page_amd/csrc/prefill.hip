@@ -23,10 +23,10 @@
 //
 // Causal reading (the decode's): the T query tokens are the last T cached positions, token t
 // sees positions j <= kv_len - T + t. A workgroup walks positions [0, kv_len - T + t_last] in
-// tiles; the next tile's rows (the one-byte formats at head_dim 128: the next two tiles') are
-// loaded into registers while the current one is computed, and stored into the second of two
-// LDS tile buffers, so one barrier per tile suffices. Two workgroups share a CU (256 registers
-// per lane each). Workgroups run heaviest (latest query tiles) first.
+// tiles; the next tile's rows are loaded into registers while the current one is computed (a
+// second register stage does not fit: the allocator then serializes the stages), and stored
+// into the second of two LDS tile buffers, so one barrier per tile suffices. Two workgroups
+// share a CU (256 registers per lane each). Workgroups run heaviest (latest query tiles) first.
 #include <hip/hip_runtime.h>
 
 #include "skvd_internal.h"
@@ -44,6 +44,9 @@ typedef unsigned pu4 __attribute__((ext_vector_type(4)));
 constexpr float kPNegInf = -__builtin_huge_valf();
 constexpr float kPLn2 = 0.6931471805599453f;
 constexpr float kMFloor = -1e30f;  // running max before any visible score (keeps exp2 finite)
+// s_waitcnt operand on gfx9: vector-memory count 0, export and LDS/scalar counts unchanged (at
+// their maxima 7 and 15)
+constexpr int kVmcntZero = 0x0F70;
 
 // Byte offset of 16-byte chunk c of row r in an LDS tile with rows of ROWB bytes (256 or 512:
 // a row starts on bank 0, a chunk's banks are set by c mod 8). The chunk is XOR-swizzled so that
@@ -103,12 +106,22 @@ struct TileRegs {
 
 // The page-table entry of this thread's token in the KV tile at kv0 (a tail token re-reads the
 // tile's last one). Read one tile ahead of the tile's loads, so that its latency is not on the
-// loop's path.
-template <int D, bool I8, int NTH>
+// loop's path. PT (pages of at least 16 tokens): a wave's tokens of a tile (16 at head_dim 128,
+// 8 at 256, aligned) lie in one page, so the entry is wave-uniform and read by a scalar load
+// through the constant address space; the vector-memory count then holds tile loads only and
+// the loop's waits for a page entry do not also wait for the tile loads issued after it.
+template <int D, bool I8, int NTH, bool PT>
 __device__ __forceinline__ int tile_page(const LaunchArgs &a, int b, int kv0, int kv_last) {
   using TR = TileRegs<D, I8, NTH>;
-  const int tok = min(kv0 + (int)threadIdx.x / TR::TPT, kv_last);
-  return a.table[(int64_t)b * a.table_stride + (tok >> a.page_shift)];
+  if constexpr (PT) {
+    typedef const __attribute__((address_space(4))) int32_t *ctab_t;
+    const int wave_tok = (int)(threadIdx.x & ~63u) / TR::TPT;  // the wave's first token
+    const int tok = __builtin_amdgcn_readfirstlane(min(kv0 + wave_tok, kv_last));
+    return ((ctab_t)a.table)[(int64_t)b * a.table_stride + (tok >> a.page_shift)];
+  } else {
+    const int tok = min(kv0 + (int)threadIdx.x / TR::TPT, kv_last);
+    return a.table[(int64_t)b * a.table_stride + (tok >> a.page_shift)];
+  }
 }
 
 // KV: 0 f16, 1 int8 with per-32 f16 scales, 2 fp8 E4M3 with one f32 scale per tensor (the
@@ -277,13 +290,7 @@ constexpr int row_sets() { return D == 128 ? 2 : 1; }
 template <int D>
 constexpr int prefill_waves() { return 4; }
 
-// Two tiles of loads in flight for the one-byte formats at head_dim 128 (their register stage is
-// half of f16's); f16 and head_dim 256 keep one (a second stage would not fit in the registers
-// of two workgroups per CU).
-template <int D, int KV>
-constexpr bool prefetch_two() { return KV != 0 && D == 128; }
-
-template <int D, int KV, int NW>
+template <int D, int KV, int NW, bool PT>
 __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_kernel(LaunchArgs a, int tpw,
                                                                          int qtiles) {
   constexpr int NTH = 64 * NW;  // threads per workgroup
@@ -379,138 +386,128 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_kernel(Launc
   }
 
   const int ntiles = kv_end > 0 ? (kv_end + KT - 1) / KT : 0;
-  // Tile loads run ahead of their use: with PF2 two tiles (the next one waits in registers while
-  // the one after it is being fetched), otherwise one. The page-table entries run one more tile
-  // ahead, so that no load waits on a page lookup.
-  constexpr bool PF2 = prefetch_two<D, KV>();
-  TileRegs<D, I8, NTH> ra, rb;  // (I8: the one-byte layout)
-  int pg_ahead = 0;        // the page entry of the next tile to be loaded
+  // The next tile's loads run one step ahead of its use, its page-table entries one more.
+  TileRegs<D, I8, NTH> regs;  // (I8: the one-byte layout)
+  int pg_ahead = 0;           // the page entry of the next tile to be loaded
   if (ntiles > 0) {
-    load_tile<D, KV, NTH>(a, kvh, 0, kv_end - 1, tile_page<D, I8, NTH>(a, b, 0, kv_end - 1), ra);
-    if (ntiles > 1) pg_ahead = tile_page<D, I8, NTH>(a, b, KT, kv_end - 1);
-    store_tile<D, KV, NTH>(kv_lds[0][0], kv_lds[0][1], ra);
-    if (PF2 && ntiles > 1) {
-      load_tile<D, KV, NTH>(a, kvh, KT, kv_end - 1, pg_ahead, ra);
-      if (ntiles > 2) pg_ahead = tile_page<D, I8, NTH>(a, b, 2 * KT, kv_end - 1);
-    }
+    load_tile<D, KV, NTH>(a, kvh, 0, kv_end - 1, tile_page<D, I8, NTH, PT>(a, b, 0, kv_end - 1),
+                          regs);
+    if (ntiles > 1) pg_ahead = tile_page<D, I8, NTH, PT>(a, b, KT, kv_end - 1);
+    store_tile<D, KV, NTH>(kv_lds[0][0], kv_lds[0][1], regs);
   }
+  // Every load issued so far (q rows, the first tiles, page entries) is complete here. Stated
+  // explicitly: the loop's first use of the q registers otherwise inherits, through the merge
+  // of the loop entry with the back edge, a wait for the vector loads the loop itself issues,
+  // i.e. a wait for the next tile right after its loads are issued.
+  __builtin_amdgcn_s_waitcnt(kVmcntZero);
   __syncthreads();
-  // One KV tile: it is read from LDS buffer it & 1; `held` holds the next tile (PF2; loaded in
-  // the previous step) or receives it (one stage), `fetch` receives the tile after it (PF2).
-  auto step = [&](int it, TileRegs<D, I8, NTH> &held, TileRegs<D, I8, NTH> &fetch)
-                  __attribute__((always_inline)) {
+  for (int it = 0; it < ntiles; ++it) {
     const int kv0 = it * KT;
     const char *k_lds = kv_lds[it & 1][0];
     const char *v_lds = kv_lds[it & 1][1];
-    const int ahead = PF2 ? it + 2 : it + 1;  // the tile this step starts loading
-    if (ahead < ntiles) {
-      load_tile<D, KV, NTH>(a, kvh, ahead * KT, kv_end - 1, pg_ahead, PF2 ? fetch : held);
-      if (ahead + 1 < ntiles) pg_ahead = tile_page<D, I8, NTH>(a, b, (ahead + 1) * KT, kv_end - 1);
-    }
+    // the next tile's loads; its successor's page entry first (requested before the tile loads,
+    // so that the next step waits for the entry alone)
+    const int pg_use = pg_ahead;
+    if (it + 2 < ntiles) pg_ahead = tile_page<D, I8, NTH, PT>(a, b, (it + 2) * KT, kv_end - 1);
+    if (it + 1 < ntiles) load_tile<D, KV, NTH>(a, kvh, (it + 1) * KT, kv_end - 1, pg_use, regs);
 
-      // ---- S^T = K Q^T: lane holds row c16's scores for tokens 16 st + 4 g4 + e
-      pf4 s[RS][NST];
+    // ---- S^T = K Q^T: lane holds row c16's scores for tokens 16 st + 4 g4 + e
+    pf4 s[RS][NST];
 #pragma unroll
-      for (int st = 0; st < NST; ++st) {
+    for (int st = 0; st < NST; ++st) {
 #pragma unroll
-        for (int rs = 0; rs < RS; ++rs) s[rs][st] = pf4{0.f, 0.f, 0.f, 0.f};
+      for (int rs = 0; rs < RS; ++rs) s[rs][st] = pf4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const ph8 kf = *(const ph8 *)(k_lds + pswz<ROWB, I8>(16 * st + c16, 4 * ks + g4));
+      for (int ks = 0; ks < NKS; ++ks) {
+        const ph8 kf = *(const ph8 *)(k_lds + pswz<ROWB, I8>(16 * st + c16, 4 * ks + g4));
 #pragma unroll
-          for (int rs = 0; rs < RS; ++rs)
-            s[rs][st] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qv[rs][ks], s[rs][st], 0, 0, 0);
-        }
+        for (int rs = 0; rs < RS; ++rs)
+          s[rs][st] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qv[rs][ks], s[rs][st], 0, 0, 0);
       }
-      // ---- mask (only tiles that reach past the first row's limit), scale (base 2), online
-      // softmax per row set. The reference max m is raised only when a score exceeds it by more
-      // than 2^8 in weight (then the accumulators are rescaled); otherwise probabilities up to 2^8
-      // are taken against the old reference, which the final o = acc / l and lse = m + log2 l
-      // absorb exactly.
-      const bool need_mask = kv0 + KT - 1 > L - T + t0;  // workgroup-uniform
-      ph8 pb[RS][NCH];
+    }
+    // ---- mask (only tiles that reach past the first row's limit), scale (base 2), online
+    // softmax per row set. The reference max m is raised only when a score exceeds it by more
+    // than 2^8 in weight (then the accumulators are rescaled); otherwise probabilities up to 2^8
+    // are taken against the old reference, which the final o = acc / l and lse = m + log2 l
+    // absorb exactly.
+    const bool need_mask = kv0 + KT - 1 > L - T + t0;  // workgroup-uniform
+    ph8 pb[RS][NCH];
 #pragma unroll
-      for (int rs = 0; rs < RS; ++rs) {
-        // the max of the unscaled scores (c > 0), scaled once per row
-        float mx = kPNegInf;
-        if (need_mask) {
-#pragma unroll
-          for (int st = 0; st < NST; ++st)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int pos = kv0 + 16 * st + 4 * g4 + e;
-              const float v = pos <= limit[rs] ? s[rs][st][e] : kPNegInf;
-              s[rs][st][e] = v;
-              mx = fmaxf(mx, v);
-            }
-        } else {
-#pragma unroll
-          for (int st = 0; st < NST; ++st)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) mx = fmaxf(mx, s[rs][st][e]);
-        }
-        mx = rows4_max(mx) * c;
-        const bool raise = mx > m[rs] + 8.f;
-        if (__any(raise)) {
-          const float m_new = raise ? mx : m[rs];
-          const float alpha = __builtin_amdgcn_exp2f(m[rs] - m_new);
-          m[rs] = m_new;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) lacc[rs][e] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[rs][dt][e] *= alpha;
-        }
+    for (int rs = 0; rs < RS; ++rs) {
+      // the max of the unscaled scores (c > 0), scaled once per row
+      float mx = kPNegInf;
+      if (need_mask) {
 #pragma unroll
         for (int st = 0; st < NST; ++st)
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            s[rs][st][e] = __builtin_amdgcn_exp2f(fmaf(s[rs][st][e], c, -m[rs]));
-#pragma unroll
-        for (int c = 0; c < NCH; ++c)
-#pragma unroll
           for (int e = 0; e < 4; ++e) {
-            pb[rs][c][e] = (_Float16)s[rs][2 * c][e];
-            pb[rs][c][4 + e] = (_Float16)s[rs][2 * c + 1][e];
+            const int pos = kv0 + 16 * st + 4 * g4 + e;
+            const float v = pos <= limit[rs] ? s[rs][st][e] : kPNegInf;
+            s[rs][st][e] = v;
+            mx = fmaxf(mx, v);
           }
+      } else {
+#pragma unroll
+        for (int st = 0; st < NST; ++st)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mx = fmaxf(mx, s[rs][st][e]);
       }
-      // ---- O^T += V^T P^T, 32 tokens per MFMA
+      mx = rows4_max(mx) * c;
+      const bool raise = mx > m[rs] + 8.f;
+      if (__any(raise)) {
+        const float m_new = raise ? mx : m[rs];
+        const float alpha = __builtin_amdgcn_exp2f(m[rs] - m_new);
+        m[rs] = m_new;
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) {
+        for (int e = 0; e < 4; ++e) lacc[rs][e] *= alpha;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          ph8 va;
+        for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            // lane (g4, c16) receives column 16 dt + c16 of tokens 32 c + 16 hh + 4 g4 + 0..3
-            const int row = 32 * c + 16 * hh + 4 * g4 + (c16 >> 2);
-            const int col = 16 * dt + 4 * (c16 & 3);
-            const ps4 r4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_ps4)(const_cast<char *>(v_lds) + pswz<ROWB, I8>(row, col >> 3) + ((col & 7) << 1)));
-            const ph4 hv = __builtin_bit_cast(ph4, r4);
+          for (int e = 0; e < 4; ++e) acc[rs][dt][e] *= alpha;
+      }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) va[4 * hh + e] = hv[e];
-          }
+      for (int st = 0; st < NST; ++st)
 #pragma unroll
-          for (int rs = 0; rs < RS; ++rs)
-            acc[rs][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[rs][c], acc[rs][dt], 0, 0, 0);
+        for (int e = 0; e < 4; ++e)
+          s[rs][st][e] = __builtin_amdgcn_exp2f(fmaf(s[rs][st][e], c, -m[rs]));
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pb[rs][c][e] = (_Float16)s[rs][2 * c][e];
+          pb[rs][c][4 + e] = (_Float16)s[rs][2 * c + 1][e];
+        }
+    }
+    // ---- O^T += V^T P^T, 32 tokens per MFMA
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        ph8 va;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          // lane (g4, c16) receives column 16 dt + c16 of tokens 32 c + 16 hh + 4 g4 + 0..3
+          const int row = 32 * c + 16 * hh + 4 * g4 + (c16 >> 2);
+          const int col = 16 * dt + 4 * (c16 & 3);
+          const ps4 r4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_ps4)(const_cast<char *>(v_lds) + pswz<ROWB, I8>(row, col >> 3) +
+                        ((col & 7) << 1)));
+          const ph4 hv = __builtin_bit_cast(ph4, r4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) va[4 * hh + e] = hv[e];
         }
 #pragma unroll
         for (int rs = 0; rs < RS; ++rs)
-          lacc[rs] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[rs][c], lacc[rs], 0, 0, 0);
+          acc[rs][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[rs][c], acc[rs][dt], 0, 0, 0);
       }
-    // the other buffer was last read in the previous step, which every wave has left
-    if (it + 1 < ntiles) store_tile<D, KV, NTH>(kv_lds[(it + 1) & 1][0], kv_lds[(it + 1) & 1][1], held);
-    __syncthreads();  // tile it+1 is in LDS, and every wave is done reading tile it
-  };
-  if constexpr (PF2) {
-    for (int it = 0; it < ntiles; it += 2) {  // (unrolled by two: the stages swap roles)
-      step(it, ra, rb);
-      if (it + 1 < ntiles) step(it + 1, rb, ra);
+#pragma unroll
+      for (int rs = 0; rs < RS; ++rs)
+        lacc[rs] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[rs][c], lacc[rs], 0, 0, 0);
     }
-  } else {
-    for (int it = 0; it < ntiles; ++it) step(it, ra, ra);
+    // the other buffer was last read in the previous iteration, which every wave has left
+    if (it + 1 < ntiles)
+      store_tile<D, KV, NTH>(kv_lds[(it + 1) & 1][0], kv_lds[(it + 1) & 1][1], regs);
+    __syncthreads();  // tile it+1 is in LDS, and every wave is done reading tile it
   }
 
   // ---- epilogue: row sums across the four lane groups, normalize, write o and lse
@@ -539,9 +536,15 @@ void launch_pd(const LaunchArgs &a, hipStream_t st) {
   const int tpw = 16 * NW * row_sets<D>() / a.G;  // query tokens per workgroup: its rows / G
   const int qtiles = (a.T + tpw - 1) / tpw;
   const unsigned grid = (unsigned)qtiles * a.Hkv * a.batch;
-  if (a.fp8) prefill_kernel<D, 2, NW><<<grid, 64 * NW, 0, st>>>(a, tpw, qtiles);
-  else if (a.int8) prefill_kernel<D, 1, NW><<<grid, 64 * NW, 0, st>>>(a, tpw, qtiles);
-  else prefill_kernel<D, 0, NW><<<grid, 64 * NW, 0, st>>>(a, tpw, qtiles);
+  if (a.page_shift >= 4) {  // pages of 16 tokens or more: wave-uniform page entries
+    if (a.fp8) prefill_kernel<D, 2, NW, true><<<grid, 64 * NW, 0, st>>>(a, tpw, qtiles);
+    else if (a.int8) prefill_kernel<D, 1, NW, true><<<grid, 64 * NW, 0, st>>>(a, tpw, qtiles);
+    else prefill_kernel<D, 0, NW, true><<<grid, 64 * NW, 0, st>>>(a, tpw, qtiles);
+  } else {
+    if (a.fp8) prefill_kernel<D, 2, NW, false><<<grid, 64 * NW, 0, st>>>(a, tpw, qtiles);
+    else if (a.int8) prefill_kernel<D, 1, NW, false><<<grid, 64 * NW, 0, st>>>(a, tpw, qtiles);
+    else prefill_kernel<D, 0, NW, false><<<grid, 64 * NW, 0, st>>>(a, tpw, qtiles);
+  }
 }
 
 }  // namespace
