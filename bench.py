@@ -643,7 +643,7 @@ def bench_append(args):
         "metric": APPEND_METRIC, "value": round(r["gbs"], 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["us_per_call"] / 1e3, 5),
         "us_per_call": round(r["us_per_call"], 3), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": {"i8": "i8", "f8": "f8"}.get(spec.kv_dtype, "f16"),
+        "vs_baseline": None, "dtype": {"i8": "i8", "f8": "f8", "q4": "q4"}.get(spec.kv_dtype, "f16"),
         "data": "synthetic",
         "config": {"workload": r["workload"], "seed": seed, "bytes_per_call": r["bytes"],
                    "copies_rotated": r["copies"]},
@@ -668,16 +668,18 @@ def main():
     ap.add_argument("--prefill", default="prompt_i8",
                     help="prefill workload for --op prefill: prompt_i8, prompt_f16, prompt_f8")
     ap.add_argument("--append", default="prefill_i8",
-                    help="append workload for --op append: prefill_i8, prefill_f16, prefill_f8, decode_i8")
+                    help="append workload for --op append: prefill_i8, prefill_f16, prefill_f8, "
+                         "prefill_q4, decode_i8")
     ap.add_argument("--no-append", action="store_true",
                     help="leave the extra objects (other workloads, depth points, fp8, append, "
                          "prefill) out of the decode line")
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=5)
-    ap.add_argument("--kv", choices=["f16", "i8", "f8"], default=None,
+    ap.add_argument("--kv", choices=["f16", "i8", "f8", "q4"], default=None,
                     help="cache format in place of the config's own (f8: OCP E4M3 with one f32 "
-                         "scale per tensor)")
+                         "scale per tensor; q4: q4_0, two 4-bit codes per byte with an f16 scale "
+                         "per 32 elements)")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--bps", type=int, default=0, help="force 64-token blocks per split")

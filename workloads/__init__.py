@@ -366,13 +366,14 @@ def append_tokens(prob: dict, seed: int, new_per_seq: int):
 
 
 # Append workloads: (cache spec, new tokens per sequence). A prefill chunk of 1024 tokens for
-# each of 32 sequences (the GQA batch's cache shape; int8, f16 and fp8 caches), and one decode
+# each of 32 sequences (the GQA batch's cache shape; int8, f16, fp8 and q4_0 caches), and one decode
 # step (one token for each of 64 sequences, the int8 batch's cache shape).
 APPEND_CONFIGS = {
     "prefill_i8": (Spec("append_prefill_i8", 32, 1, 32, 8, 128, 16, "i8", ("fixed", 1024)), 1024),
     "prefill_f16": (Spec("append_prefill_f16", 32, 1, 32, 8, 128, 16, "f16", ("fixed", 1024)), 1024),
     "decode_i8": (Spec("append_decode_i8", 64, 1, 32, 8, 128, 16, "i8", ("fixed", 1024)), 1),
     "prefill_f8": (Spec("append_prefill_f8", 32, 1, 32, 8, 128, 16, "f8", ("fixed", 1024)), 1024),
+    "prefill_q4": (Spec("append_prefill_q4", 32, 1, 32, 8, 128, 16, "q4", ("fixed", 1024)), 1024),
 }
 
 
