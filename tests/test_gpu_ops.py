@@ -4,7 +4,7 @@ bit-identical after the call under torch.compile over [2, pages] views and a lay
 
 * torch.library.opcheck on skvd::decode_v1 and skvd::decode_out_v1 (schema -- including that
   no input not declared written is changed --, fake implementation, AOT dispatch) over f16,
-  int8 and fp8 caches.
+  int8, fp8 and q4_0 caches.
 * torch.compile(fullgraph=True) with the aot_eager backend and with a backend that keeps the
   functionalized forward graph, over the cache as one half of a [2, pages, ...] tensor, one
   slot of an interleaved [pages, 2, ...] tensor and one layer of a multi-layer pool: outputs
@@ -61,7 +61,7 @@ def _layout(dev, layout):
     return base, kk, vv, ks, vs
 
 
-@pytest.mark.parametrize("kv", ["f16", "i8", "f8"])
+@pytest.mark.parametrize("kv", ["f16", "i8", "f8", "q4"])
 def test_opcheck(kv):
     from quantized_kv_cache_page_amd import ops
     prob = _problem(kv)
@@ -100,7 +100,7 @@ def _capturing_backend(found):
 
 @pytest.mark.parametrize("with_out", [False, True])
 @pytest.mark.parametrize("layout", ["two_halves", "interleaved", "layer_of_pool"])
-@pytest.mark.parametrize("kv", ["f16", "i8"])
+@pytest.mark.parametrize("kv", ["f16", "i8", "q4"])
 def test_compile_over_cache_views(kv, layout, with_out):
     from quantized_kv_cache_page_amd import ops
     prob = _problem(kv, seed=7)

@@ -34,7 +34,7 @@ def _noalloc(plan, prob, dev):
 
 @pytest.mark.parametrize("kv,T,Hq,Hkv,sched", [("f16", 1, 32, 8, "auto"), ("i8", 1, 32, 8, "auto"),
                                                ("i8", 4, 16, 4, "static"),
-                                               ("f8", 8, 32, 4, "auto")])
+                                               ("f8", 8, 32, 4, "auto"), ("q4", 2, 32, 8, "auto")])
 def test_noalloc_matches_decode(kv, T, Hq, Hkv, sched):
     big = workloads.spec(name="na_big", batch=6, q_per_seq=T, num_qo_heads=Hq, num_kv_heads=Hkv,
                          head_dim=128, page_size=16, kv_dtype=kv,
@@ -76,7 +76,11 @@ def test_noalloc_refusals():
     huge = skvd.Plan(64, 64, 256, 16, "f16", max_batch=1024, max_q_per_seq=8, max_kv_len=65536,
                      device=0, schedule="static")
     assert huge.workspace_bytes > (32 << 20)
+    # arguments of the huge plan's shape (one sequence, two pages): refused for the workspace
+    q = torch.zeros((1, 64, 256), dtype=torch.float16, device="cuda")
+    pool = torch.zeros((2, 16, 64, 256), dtype=torch.float16, device="cuda")
+    table = torch.zeros((1, 4096), dtype=torch.int32, device="cuda")
+    kv_len = torch.full((1,), 20, dtype=torch.int32, device="cuda")
     with pytest.raises(skvd.SkvdError) as e:
-        huge.run_noalloc(dev["q"], dev["k_pages"], dev["v_pages"], dev["page_table"],
-                         dev["kv_len"], prob["sm_scale"])
+        huge.run_noalloc(q, pool, pool, table, kv_len, 0.0625)
     assert e.value.status == 5
