@@ -1,8 +1,8 @@
 """The allocation-free decode (skvd_decode_noalloc, the library's own device workspace) through
 the C ABI against skvd_decode with a caller workspace: bit-identical outputs on two calls in a
 row, the second with a smaller batch and shorter sequences (the array keeps the first call's
-contents), over f16 and int8 caches; plans whose workspace exceeds the array's size and debug
-plans are refused."""
+contents), over f16, int8, fp8 and q4_0 caches; plans whose workspace exceeds the array's size
+and debug plans are refused."""
 import numpy as np
 import pytest
 import torch
