@@ -547,6 +547,12 @@ def cpu_baseline_prefill(prob, budget_s=10.0, nrows=256):
                                         f"{t:.3f} s per pass, fp64"}
 
 
+def prefill_kernel_name(spec):
+    """The multi-token route's kernel for a workload: f16 caches with pages of 16+ tokens copy
+    their tiles straight into LDS (prefill_dma_kernel), the rest stage them through registers."""
+    return "prefill_dma_kernel" if spec.kv_dtype == "f16" and spec.page_size >= 16 else "prefill_kernel"
+
+
 def bench_prefill(args):
     seed = 50 if args.seed is None else args.seed
     r, prob = time_prefill(args.prefill, seed, args.steps, args.warmup)
@@ -561,7 +567,7 @@ def bench_prefill(args):
         "roofline": {"bound": "mfma", "achieved": round(r["tflops"], 2),
                      "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(r["tflops"] / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "prefill_kernel", "kernel_avg_us": round(r["us_per_call"], 3),
+                     "kernel": prefill_kernel_name(spec), "kernel_avg_us": round(r["us_per_call"], 3),
                      "algorithmic_flops_per_launch": r["flops"]},
         "cpu_baseline": None,
     }

@@ -23,10 +23,15 @@
 //
 // Causal reading (the decode's): the T query tokens are the last T cached positions, token t
 // sees positions j <= kv_len - T + t. A workgroup walks positions [0, kv_len - T + t_last] in
-// tiles; the next tile's rows are loaded into registers while the current one is computed (a
-// second register stage does not fit: the allocator then serializes the stages), and stored
-// into the second of two LDS tile buffers, so one barrier per tile suffices. Two workgroups
-// share a CU (256 registers per lane each). Workgroups run heaviest (latest query tiles) first.
+// tiles, two LDS tile buffers deep, one barrier per tile. Two workgroups share a CU (256
+// registers per lane each). Workgroups run heaviest (latest query tiles) first.
+//
+// Two ways into LDS. f16 caches with pages of 16+ tokens: copies straight from HBM into LDS
+// (global_load_lds_dwordx4, no registers held), the next tile's copies in flight while the
+// current one is computed. int8 and fp8 caches, and pages of fewer than 16 tokens: the next
+// tile's rows are loaded into registers during the compute, widened (one-byte formats) and
+// stored into the other buffer (a second register stage does not fit: the allocator then
+// serializes the stages).
 #include <hip/hip_runtime.h>
 
 #include "skvd_internal.h"
@@ -530,12 +535,347 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_kernel(Launc
   }
 }
 
+// ---- f16 caches with pages of 16+ tokens: K/V tiles copied from HBM straight into LDS
+// (global_load_lds_dwordx4: each lane's 16 bytes land at the wave's LDS base + 16 * lane, no
+// registers held), NSTG tile buffers deep, so that a tile's loads are issued NSTG - 1 tiles
+// before its use. Each lane loads the global chunk that the tile's swizzle puts at its LDS
+// slot. A wave waits for its own copies of a tile explicitly (vector-memory count, the copies of
+// the later tiles still in flight) before the barrier that publishes the tile; the loop holds no
+// other vector-memory operation, so the count is exact.
+
+// s_waitcnt operand: vector-memory count n (0..63), export and LDS/scalar counts at their maxima
+template <int N>
+constexpr int vmcnt_imm() { return (N & 15) | ((N >> 4) << 14) | 0x0F70; }
+
+template <int D, int KT, int NW>
+struct DmaTile {
+  static constexpr int ROWB = D * 2;             // bytes per K or V row in LDS
+  static constexpr int RPS = 1024 / ROWB;        // rows per wave copy (64 lanes x 16 bytes)
+  static constexpr int CPR = ROWB / 16;          // 16-byte chunks per row
+  static constexpr int SPW = KT * ROWB / 1024 / NW;  // copies per wave per tensor and tile
+  static constexpr int RPW = SPW * RPS;          // rows (tokens) per wave: 8 or 16, one page
+  static constexpr int BYTES = KT * ROWB;        // one tensor's tile
+  static_assert(SPW >= 1 && KT * ROWB == 1024 * NW * SPW, "tile not a whole number of copies");
+  static_assert(RPW <= 16, "a wave's tokens must lie in one 16-token group");
+};
+
+// The page-table entry of wave w's tokens of the tile at kv0 (wave-uniform for pages of 16+
+// tokens, scalar load; a tail token is clamped to the last visited position).
+template <int D, int KT, int NW>
+__device__ __forceinline__ int dma_page(const LaunchArgs &a, int b, int w, int kv0, int kv_last) {
+  using DT = DmaTile<D, KT, NW>;
+  typedef const __attribute__((address_space(4))) int32_t *ctab_t;
+  const int tok = __builtin_amdgcn_readfirstlane(min(kv0 + DT::RPW * w, kv_last));
+  return ((ctab_t)a.table)[(int64_t)b * a.table_stride + (tok >> a.page_shift)];
+}
+
+// Issue the copies of wave w's rows of the K and V tile at kv0 into k_lds / v_lds. The wave's
+// rows lie in one page (pg, the entry of its first visited token tw): a scalar base at token tw
+// of that page plus a 32-bit lane offset (fewer than 16 rows further, within the 32-bit in-tile
+// range the host checks).
+template <int D, int KT, int NW>
+__device__ __forceinline__ void dma_tile(const LaunchArgs &a, int kvh, int w, int kv0,
+                                         int kv_last, int pg, char *k_lds, char *v_lds) {
+  using DT = DmaTile<D, KT, NW>;
+  typedef __attribute__((address_space(3))) void *lds_t;
+  const int lane = threadIdx.x & 63;
+  const int P1 = (1 << a.page_shift) - 1;
+  const int tw = __builtin_amdgcn_readfirstlane(min(kv0 + DT::RPW * w, kv_last));
+  const int64_t pk = pg < 0 ? 0 : (pg >= a.num_k_pages ? a.num_k_pages - 1 : pg);
+  const int64_t pv = pg < 0 ? 0 : (pg >= a.num_v_pages ? a.num_v_pages - 1 : pg);
+  const int64_t in_page = (int64_t)(tw & P1) * a.tok_stride + (int64_t)kvh * a.head_stride;
+  const char *kb = (const char *)((const _Float16 *)a.k + pk * a.page_stride + in_page);
+  const char *vb = (const char *)((const _Float16 *)a.v + pv * a.page_stride + in_page);
+  const unsigned ts = (unsigned)a.tok_stride * 2u;     // bytes per token
+  const int rl = lane / DT::CPR, pc = lane % DT::CPR;  // row within the copy, LDS chunk
+#pragma unroll
+  for (int j = 0; j < DT::SPW; ++j) {
+    const int seg = w * DT::SPW + j;
+    const int row = seg * DT::RPS + rl;
+    const int tok = min(kv0 + row, kv_last);
+    // the chunk whose swizzled place is LDS chunk pc of this row (the swizzle is an XOR)
+    const int c = (pswz<DT::ROWB, false>(row, pc) - row * DT::ROWB) >> 4;
+    const unsigned off = (unsigned)(tok - tw) * ts + 16u * (unsigned)c;
+    __builtin_amdgcn_global_load_lds((const void *)(kb + off), (lds_t)(k_lds + seg * 1024), 16, 0,
+                                     0);
+    __builtin_amdgcn_global_load_lds((const void *)(vb + off), (lds_t)(v_lds + seg * 1024), 16, 0,
+                                     0);
+  }
+}
+
+template <int D, int NW, int KT, int NSTG>
+__global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_dma_kernel(LaunchArgs a,
+                                                                             int tpw, int qtiles) {
+  using DT = DmaTile<D, KT, NW>;
+  static_assert(NSTG >= 2 && NSTG <= 4, "two to four tile buffers");
+  constexpr int RS = row_sets<D>();
+  constexpr int NST = KT / 16;
+  constexpr int NCH = KT / 32;
+  constexpr int NKS = D / 32;
+  constexpr int NDT = D / 16;
+  constexpr int ROWB = D * 2;
+  // NSTG tile buffers (K then V in each)
+  __shared__ __attribute__((aligned(1024))) char stg[NSTG][2 * DT::BYTES];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c16 = lane & 15, g4 = lane >> 4;
+  // work item: as in prefill_kernel (the query tiles of one (sequence, KV head) pair on one XCD,
+  // heaviest first)
+  const int pairs = a.Hkv * a.batch;
+  const int id = blockIdx.x;
+  const int x = id % 8, k = id / 8;
+  int pair, qt;
+  if (pairs % 8 == 0) {
+    const int per_xcd = pairs / 8;
+    qt = qtiles - 1 - k / per_xcd;
+    pair = x + 8 * (k % per_xcd);
+  } else {
+    const int n = qtiles * pairs;
+    const int base = n / 8, extra = n % 8;
+    const int item = x * base + min(x, extra) + k;
+    pair = item / qtiles;
+    qt = qtiles - 1 - item % qtiles;
+  }
+  const int kvh = pair % a.Hkv, b = pair / a.Hkv;
+  const int G = a.G, T = a.T;
+  int L = a.kv_len[b];
+  L = L < 0 ? 0 : (L > a.max_kv_len ? a.max_kv_len : L);
+  const int t0 = qt * tpw;
+  const int t_last = min(t0 + tpw, T) - 1;
+  const int kv_end = min(L, L - T + t_last + 1);
+  const int kv_last = kv_end - 1;
+
+  bool row_ok[RS];
+  int trow[RS], hrow[RS], limit[RS];
+  ph8 qv[RS][NKS];
+#pragma unroll
+  for (int rs = 0; rs < RS; ++rs) {
+    const int r = 16 * (RS * w + rs) + c16;
+    const int tl = r / G;
+    const int gh = r - tl * G;
+    row_ok[rs] = tl < tpw && t0 + tl < T;
+    trow[rs] = row_ok[rs] ? t0 + tl : t_last;
+    hrow[rs] = kvh * G + gh;
+    limit[rs] = L - T + trow[rs];
+    const _Float16 *qp = (const _Float16 *)a.q + ((int64_t)b * T + trow[rs]) * a.q_tok_stride +
+                         (int64_t)hrow[rs] * a.q_head_stride + 8 * g4;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qv[rs][ks] = *(const ph8 *)(qp + 32 * ks);
+  }
+  float c = a.scale_log2;
+  if (c < 0.f) {
+    c = -c;
+#pragma unroll
+    for (int rs = 0; rs < RS; ++rs)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) qv[rs][ks] = -qv[rs][ks];
+  }
+  c = fmaxf(c, 1e-30f);
+
+  pf4 acc[RS][NDT], lacc[RS];
+  float m[RS];
+  const ph8 ones = (ph8)(_Float16)1;
+#pragma unroll
+  for (int rs = 0; rs < RS; ++rs) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc[rs][dt] = pf4{0.f, 0.f, 0.f, 0.f};
+    lacc[rs] = pf4{0.f, 0.f, 0.f, 0.f};
+    m[rs] = kMFloor;
+  }
+
+  const int ntiles = kv_end > 0 ? (kv_end + KT - 1) / KT : 0;
+
+  // Per-lane LDS read offsets within a buffer, the same for every buffer: K fragment of step
+  // ks (16-row sub-tile st adds 16 rows), V fragment of head_dim tile dt (the 32-token chunk and
+  // its 16-token half add whole rows). The swizzle depends on the row's low 4 bits only.
+  int koff[NKS], voff[NDT];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) koff[ks] = pswz<ROWB, false>(c16, 4 * ks + g4);
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    const int row = 4 * g4 + (c16 >> 2), col = 16 * dt + 4 * (c16 & 3);
+    voff[dt] = pswz<ROWB, false>(row, col >> 3) + ((col & 7) << 1);
+  }
+
+  // Scores of one tile, S^T = K Q^T: lane holds row c16's scores for tokens 16 st + 4 g4 + e.
+  auto scores = [&](const char *k_lds, pf4 (&sc)[RS][NST]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+#pragma unroll
+      for (int rs = 0; rs < RS; ++rs) sc[rs][st] = pf4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const ph8 kf = *(const ph8 *)(k_lds + koff[ks] + 16 * st * ROWB);
+#pragma unroll
+        for (int rs = 0; rs < RS; ++rs)
+          sc[rs][st] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qv[rs][ks], sc[rs][st], 0, 0, 0);
+      }
+    }
+  };
+  // Wait until at most n tiles' copies issued after the one needed are outstanding (n <= 2).
+  auto wait_tiles = [&](int n) __attribute__((always_inline)) {
+    if (n >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm<4 * DT::SPW>());
+    else if (n == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm<2 * DT::SPW>());
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
+  };
+
+  // Mask (tiles that reach past the first row's limit) and online softmax statistics of tile
+  // it: the running max m is raised only when a score exceeds it by more than 2^8 in weight
+  // (then the accumulators are rescaled); otherwise probabilities up to 2^8 are taken against
+  // the old reference, which o = acc / l and lse = m + log2 l absorb exactly.
+  auto mask_max = [&](pf4 (&sc)[RS][NST], int it) __attribute__((always_inline)) {
+    const int kv0 = it * KT;
+    const bool need_mask = kv0 + KT - 1 > L - T + t0;  // workgroup-uniform
+    float mrow[RS];
+#pragma unroll
+    for (int rs = 0; rs < RS; ++rs) {
+      float mx = kPNegInf;
+      if (need_mask) {
+#pragma unroll
+        for (int st = 0; st < NST; ++st)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int pos = kv0 + 16 * st + 4 * g4 + e;
+            const float v = pos <= limit[rs] ? sc[rs][st][e] : kPNegInf;
+            sc[rs][st][e] = v;
+            mx = fmaxf(mx, v);
+          }
+      } else {
+#pragma unroll
+        for (int st = 0; st < NST; ++st)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sc[rs][st][e]);
+      }
+      mrow[rs] = rows4_max(mx) * c;
+    }
+#pragma unroll
+    for (int rs = 0; rs < RS; ++rs) {
+      const bool raise = mrow[rs] > m[rs] + 8.f;
+      if (__any(raise)) {
+        const float m_new = raise ? mrow[rs] : m[rs];
+        const float alpha = __builtin_amdgcn_exp2f(m[rs] - m_new);
+        m[rs] = m_new;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lacc[rs][e] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[rs][dt][e] *= alpha;
+      }
+    }
+  };
+  // Probabilities of tile it (base 2, f16) and O^T += V^T P^T over its V rows, 32 tokens per
+  // MFMA; the row sums by the all-ones MFMA.
+  auto exp_pv = [&](const char *buf, pf4 (&sc)[RS][NST]) __attribute__((always_inline)) {
+    ph8 pb[RS][NCH];
+#pragma unroll
+    for (int rs = 0; rs < RS; ++rs) {
+#pragma unroll
+      for (int st = 0; st < NST; ++st)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          sc[rs][st][e] = __builtin_amdgcn_exp2f(fmaf(sc[rs][st][e], c, -m[rs]));
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pb[rs][ch][e] = (_Float16)sc[rs][2 * ch][e];
+          pb[rs][ch][4 + e] = (_Float16)sc[rs][2 * ch + 1][e];
+        }
+    }
+    const char *v_lds = buf + DT::BYTES;
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        ph8 va;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const ps4 r4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_ps4)(const_cast<char *>(v_lds) + voff[dt] + (32 * ch + 16 * hh) * ROWB));
+          const ph4 hv = __builtin_bit_cast(ph4, r4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) va[4 * hh + e] = hv[e];
+        }
+#pragma unroll
+        for (int rs = 0; rs < RS; ++rs)
+          acc[rs][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[rs][ch], acc[rs][dt], 0, 0, 0);
+      }
+#pragma unroll
+      for (int rs = 0; rs < RS; ++rs)
+        lacc[rs] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[rs][ch], lacc[rs], 0, 0, 0);
+    }
+  };
+
+  // One tile per step: wait for its copies (those of up to NSTG - 2 later tiles may stay in
+  // flight), publish it with a barrier (which also says that every wave is done with the
+  // previous tile's buffer), issue the copies of tile it + NSTG - 1 into that buffer, compute.
+  int pg_next = 0;
+#pragma unroll
+  for (int t = 0; t < NSTG - 1; ++t)
+    if (t < ntiles)
+      dma_tile<D, KT, NW>(a, kvh, w, t * KT, kv_last,
+                          dma_page<D, KT, NW>(a, b, w, t * KT, kv_last), stg[t],
+                          stg[t] + DT::BYTES);
+  if (NSTG - 1 < ntiles) pg_next = dma_page<D, KT, NW>(a, b, w, (NSTG - 1) * KT, kv_last);
+  for (int it = 0, bi = 0; it < ntiles; ++it) {
+    const int bn = bi == 0 ? NSTG - 1 : bi - 1;  // buffer of tile it + NSTG - 1
+    wait_tiles(min(NSTG - 2, ntiles - 1 - it));
+    __builtin_amdgcn_s_barrier();
+    if (it + NSTG - 1 < ntiles) {
+      const int pg = pg_next;
+      if (it + NSTG < ntiles) pg_next = dma_page<D, KT, NW>(a, b, w, (it + NSTG) * KT, kv_last);
+      dma_tile<D, KT, NW>(a, kvh, w, (it + NSTG - 1) * KT, kv_last, pg, stg[bn],
+                          stg[bn] + DT::BYTES);
+    }
+    pf4 s[RS][NST];
+    scores(stg[bi], s);
+    mask_max(s, it);
+    exp_pv(stg[bi], s);
+    bi = bi == NSTG - 1 ? 0 : bi + 1;
+  }
+  for (int rs = 0; rs < RS; ++rs) {
+    const float lt = lacc[rs][0];
+    if (!row_ok[rs]) continue;
+    const int64_t orow = ((int64_t)b * T + trow[rs]) * a.Hq + hrow[rs];
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    _Float16 *op = (_Float16 *)a.o + orow * D + 4 * g4;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      ph4 ov;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ov[e] = (_Float16)(acc[rs][dt][e] * inv);
+      *(ph4 *)(op + 16 * dt) = ov;
+    }
+    if (g4 == 0 && a.lse) a.lse[orow] = lt > 0.f ? (m[rs] + __log2f(lt)) * kPLn2 : kPNegInf;
+  }
+}
+
+// The copy-staged kernel's shape: 4 waves per workgroup (two workgroups per CU, so that the two
+// waves on a SIMD belong to different workgroups and do not meet at the same barriers), two
+// tile buffers of the register-staged kernel's tile size. Measured alternatives: 8 waves per
+// workgroup with two or three buffers (as fast, or 1 % slower), 32-token tiles with three to
+// five buffers (7-20 % slower), one workgroup of 4 waves per CU (70 % slower), and a pipeline
+// inside each wave that issues the next tile's score MFMAs among this tile's exponentials
+// (10 % slower: both waves of a SIMD then reach their LDS reads together).
+constexpr int kDmaWaves = 4;
+constexpr int kDmaStages = 2;
+
 template <int D>
 void launch_pd(const LaunchArgs &a, hipStream_t st) {
   constexpr int NW = prefill_waves<D>();
   const int tpw = 16 * NW * row_sets<D>() / a.G;  // query tokens per workgroup: its rows / G
   const int qtiles = (a.T + tpw - 1) / tpw;
   const unsigned grid = (unsigned)qtiles * a.Hkv * a.batch;
+  if (a.page_shift >= 4 && !a.int8 && !a.fp8) {  // f16, pages of 16+ tokens: copies into LDS
+    constexpr int DNW = kDmaWaves, DKT = kv_tile<D>();
+    const int dtpw = 16 * DNW * row_sets<D>() / a.G;
+    const int dq = (a.T + dtpw - 1) / dtpw;
+    prefill_dma_kernel<D, DNW, DKT, kDmaStages>
+        <<<(unsigned)dq * a.Hkv * a.batch, 64 * DNW, 0, st>>>(a, dtpw, dq);
+    return;
+  }
   if (a.page_shift >= 4) {  // pages of 16 tokens or more: wave-uniform page entries
     if (a.fp8) prefill_kernel<D, 2, NW, true><<<grid, 64 * NW, 0, st>>>(a, tpw, qtiles);
     else if (a.int8) prefill_kernel<D, 1, NW, true><<<grid, 64 * NW, 0, st>>>(a, tpw, qtiles);
