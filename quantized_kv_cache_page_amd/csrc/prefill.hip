@@ -835,6 +835,9 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_dma_kernel(L
     exp_pv(stg[bi], s);
     bi = bi == NSTG - 1 ? 0 : bi + 1;
   }
+
+  // ---- epilogue: normalize, write o and lse
+#pragma unroll
   for (int rs = 0; rs < RS; ++rs) {
     const float lt = lacc[rs][0];
     if (!row_ok[rs]) continue;
