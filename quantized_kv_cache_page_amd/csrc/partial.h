@@ -281,10 +281,14 @@ __device__ __forceinline__ int swz(int r, int c) {
 // ALU heavy and runs several waves per SIMD (the plan launches 8 workgroups per CU): three,
 // at the cost of three values spilled and reloaded once per segment. f16 single-quarter
 // variants run one wave per SIMD under the balanced schedule and gain more from registers
-// spent on instruction-level parallelism than from occupancy: no floor.
+// spent on instruction-level parallelism than from occupancy: no floor. The one-byte formats
+// at D = 192 / 256 widen every element: two waves per SIMD (<= 256 registers; int8 spills 16
+// values), so that one wave's widening overlaps the other's loads (the wide multi-token
+// workload's shape: int8 408 -> 290-300 us, fp8 377 -> 244-255, q4_0 393 -> 240-254, with 8
+// workgroups per CU); f16 there, a pure stream, keeps one wave per SIMD (no faster with two).
 template <int D, int RB, bool I8>
 constexpr int partial_waves() {
-  return D == 128 ? (RB == 1 ? (I8 ? 3 : 1) : 2) : 1;
+  return D == 128 ? (RB == 1 ? (I8 ? 3 : 1) : 2) : (D <= 256 && I8 ? 2 : 1);
 }
 
 template <int D, int RB, int KV, bool FAST, int CH, bool PVM, int HW, int RT, bool DBG>

@@ -188,12 +188,15 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
     // 4 x 2 and 580.8 with 2 x 6 (token-major scale pools: 617 with 4 x 3, whose twelve waves
     // per CU each touch 32 lines for a chunk's 256 bytes of scales).
     const bool byte = prm.kv_dtype != SKVD_KV_F16;
-    // D = 256 variants hold one wave per SIMD (over 256 registers with the accumulators): f16,
-    // a pure stream, does best with three workgroups per CU (the wide multi-token workload 527
-    // us against 537 with four); the one-byte formats widen every element and need all four
-    // SIMDs (fp8: 604.7 -> 460.9 us with four, int8: 640.5 -> 484.2)
-    // head_dim 192 and 512 take head_dim 256's counts (one wave per SIMD)
-    const int auto_wpc = D != 128 ? (prm.kv_dtype == SKVD_KV_F16 ? 3 : 4)
+    // D = 256 f16 variants hold one wave per SIMD (over 256 registers with the accumulators)
+    // and, a pure stream, do best with three workgroups per CU (the wide multi-token workload
+    // 527 us against 537 with four; with two waves per SIMD no faster at three, slower at six or
+    // eight). The one-byte formats at D = 192 / 256 widen every element and run two waves per
+    // SIMD: eight workgroups per CU (on the wide multi-token workload's shape, against four
+    // workgroups of one wave: int8 408 -> 290-300 us, fp8 377 -> 244-255, q4_0 393 -> 240-254).
+    // head_dim 192 takes head_dim 256's counts; 512 holds one wave per SIMD: four for the
+    // one-byte formats.
+    const int auto_wpc = D != 128 ? (!byte ? 3 : D <= 256 ? 8 : 4)
                          : p.row_blocks == 1 ? (byte ? std::max(1, 12 / hw)
                                                      : std::max(1, kDefaultWgsPerCu / hw))
                                              : kDefaultWgsPerCu;

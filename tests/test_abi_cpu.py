@@ -95,9 +95,15 @@ def test_schedule_choice():
     w = plan(wgs_per_cu=7, num_cus=100)
     assert w.schedule == "balanced" and w.info.grid_wgs == 700 and w.info.heads_per_wg == 4
     assert "schedule=balanced" in w.describe()
-    # defaults per variant: 4 per CU, 3 at head_dim 256; one-byte single-quarter tiles:
+    # defaults per variant: 4 per CU, 3 at head_dim 256 (f16), 8 for the one-byte formats at
+    # head_dim 192 / 256 (two waves per SIMD), 4 at 512; one-byte single-quarter tiles:
     # workgroups of 4 KV heads, three per CU (else 2 or 1 heads, 12 waves per CU)
     assert plan(head_dim=256, num_kv_heads=16).info.grid_wgs == 3 * 256
+    for kv in ("i8", "f8", "q4"):
+        assert plan(head_dim=256, num_kv_heads=16, kv_dtype=kv).info.grid_wgs == 8 * 256, kv
+        assert plan(head_dim=512, num_kv_heads=16, kv_dtype=kv).info.grid_wgs == 4 * 256, kv
+    assert plan(head_dim=192, num_kv_heads=16, kv_dtype="f8").info.grid_wgs == 8 * 256
+    assert plan(head_dim=192, num_kv_heads=16).info.grid_wgs == 3 * 256
     i8 = plan(kv_dtype="i8")
     assert i8.info.heads_per_wg == 4 and i8.info.grid_wgs == 3 * 256
     i8_4 = plan(kv_dtype="i8", num_kv_heads=4, num_qo_heads=16)
@@ -392,8 +398,8 @@ def test_q4_plan_and_routes():
 
 def test_plan_waves_per_cu_by_format():
     """Workgroups per CU chosen per format (256 CUs): at head_dim 128 with one query-row quarter,
-    f16 4 KV heads x 1 workgroup, int8 and fp8 4 x 3; at head_dim 256 (one wave per SIMD),
-    f16 three workgroups per CU, the one-byte formats four."""
+    f16 4 KV heads x 1 workgroup, int8 and fp8 4 x 3; at head_dim 256, f16 three workgroups
+    per CU (one wave per SIMD), the one-byte formats eight (two waves per SIMD)."""
     def grid(**kw):
         d = plan(**kw).describe()
         return int(d.split("grid=")[1].split()[0]), int(d.split("heads_per_wg=")[1].split()[0])
@@ -403,5 +409,6 @@ def test_plan_waves_per_cu_by_format():
     wide = dict(num_qo_heads=32, num_kv_heads=16, head_dim=256, max_batch=8, max_q_per_seq=4,
                 max_kv_len=32768)
     assert grid(kv_dtype="f16", **wide) == (768, 1)
-    assert grid(kv_dtype="i8", **wide) == (1024, 1)
-    assert grid(kv_dtype="f8", **wide) == (1024, 1)
+    assert grid(kv_dtype="i8", **wide) == (2048, 1)
+    assert grid(kv_dtype="f8", **wide) == (2048, 1)
+    assert grid(kv_dtype="q4", **wide) == (2048, 1)
