@@ -146,38 +146,47 @@ __device__ __forceinline__ void q4_pairs(unsigned a, unsigned b, half2v *out) {
 }
 
 // ----------------------------------------------------------------------------- fp8 (E4M3) -> f16
-// An OCP E4M3 byte s.eeee.mmm rewritten as the f16 bits s.0eeee.mmm0000000 is the f16 of its
-// value times 2^-8, exactly: the 4-bit exponent field under f16's bias 15 instead of E4M3's 7
-// is the factor 2^-8, and E4M3's subnormals (field 0: 2^-6 * m/8) become f16 subnormals
-// (2^-14 * m/8) with the same factor. The 2^8 comes back with the per-tensor scales, folded
-// into the score scale (K) and the output (V). (The NaN byte turns into a finite f16; a cache
-// holds none.) A byte permute puts two bytes into the high bytes of the two f16 halves; the
-// sign bits stay, the other seven bits of each shift down by one.
-__device__ __forceinline__ unsigned f8_place(unsigned s0, unsigned s1, unsigned sel) {
-  const unsigned t = __builtin_amdgcn_perm(s0, s1, sel);
-  return (t & 0x80008000u) | ((t >> 1) & 0x3F803F80u);
+// The conversion instruction turns two OCP E4M3 bytes (the low or the high half-word of a
+// dword) into two f16 values times a power-of-two scale (only the scale's exponent is used):
+// with 2^-8 every E4M3 value, subnormals included, is exact in f16 (|x| 2^-8 <= 1.75, the least
+// subnormal 2^-17) and keeps the f16 products of the score MFMA and the P.V dot products far from
+// overflow. The 2^8 comes back with the per-tensor scales, folded into the score scale (K) and
+// the output (V). The NaN byte stays NaN.
+constexpr float kF8Scale = 0.00390625f;  // 2^-8
+
+template <bool HI>
+__device__ __forceinline__ half2v f8x2_to_h2(unsigned w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, kF8Scale, HI);
 }
 
 // 8 E4M3 bytes (elements 0..7 in byte order) -> 8 f16 (value * 2^-8).
 __device__ __forceinline__ half8 f8x8_to_h8(uint2v w) {
-  uint4v r;
+  half8 r;
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
-    r[2 * k] = f8_place(w[k], w[k], 0x010C000Cu);      // bytes 0, 1 -> halves 0, 1
-    r[2 * k + 1] = f8_place(w[k], w[k], 0x030C020Cu);  // bytes 2, 3 -> halves 0, 1
+    const half2v lo = f8x2_to_h2<false>(w[k]), hi = f8x2_to_h2<true>(w[k]);
+    r[4 * k] = lo[0];
+    r[4 * k + 1] = lo[1];
+    r[4 * k + 2] = hi[0];
+    r[4 * k + 3] = hi[1];
   }
-  return __builtin_bit_cast(half8, r);
+  return r;
 }
 
 // Two E4M3 rows a (token t) and b (token t + 16), 8 elements each -> the 8 f16 pairs
-// (a_i, b_i) (values * 2^-8): byte i of a into the low half, byte i of b into the high half.
+// (a_i, b_i) (values * 2^-8): one byte permute gathers bytes i and i+1 of both rows as
+// (a_i, b_i, a_i+1, b_i+1), the two half-words of which convert to two pairs.
 __device__ __forceinline__ void f8_pairs(uint2v a, uint2v b, half2v *out) {
 #pragma unroll
   for (int w = 0; w < 2; ++w) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      out[4 * w + i] = __builtin_bit_cast(
-          half2v, f8_place(b[w], a[w], ((4u + i) << 24) | 0x0C0000u | ((unsigned)i << 8) | 0x0Cu));
+    for (int i = 0; i < 4; i += 2) {
+      // perm selector bytes: 0-3 pick from the second operand (a), 4-7 from the first (b)
+      const unsigned t = __builtin_amdgcn_perm(
+          b[w], a[w], ((5u + i) << 24) | ((unsigned)(i + 1) << 16) | ((4u + i) << 8) | (unsigned)i);
+      out[4 * w + i] = f8x2_to_h2<false>(t);
+      out[4 * w + i + 1] = f8x2_to_h2<true>(t);
+    }
   }
 }
 

@@ -216,28 +216,21 @@ __device__ __forceinline__ void widen16(pu4 w, _Float16 s, ph8 *lo, ph8 *hi) {
   }
 }
 
-// 16 E4M3 bytes -> two groups of 8 f16 holding value * 2^-8 exactly: the byte s.eeee.mmm
-// becomes the f16 bits s.0eeee.mmm0000000 (the exponent field under f16's bias 15 instead of
-// E4M3's 7 is the factor 2^-8; E4M3 subnormals map onto f16 subnormals). A byte permute puts two
-// bytes into the high bytes of an f16 pair; the sign bits stay and the rest shift down by one.
+// 16 E4M3 bytes -> two groups of 8 f16 holding value * 2^-8 exactly, two bytes per conversion
+// instruction (power-of-two scale 2^-8: every E4M3 value, subnormals included, is exact in f16).
 // The 2^8 and the tensor scales are applied to the score scale (K) and the output (V).
-__device__ __forceinline__ unsigned f8_pair16(unsigned w, unsigned sel) {
-  const unsigned t = __builtin_amdgcn_perm(w, w, sel);
-  return (t & 0x80008000u) | ((t >> 1) & 0x3F803F80u);
-}
-
 __device__ __forceinline__ void widen16_f8(pu4 w, ph8 *lo, ph8 *hi) {
-  pu4 l, h;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const unsigned a = f8_pair16(w[k], 0x010C000Cu);  // bytes 0, 1
-    const unsigned b = f8_pair16(w[k], 0x030C020Cu);  // bytes 2, 3
-    pu4 &dst = k < 2 ? l : h;
-    dst[2 * (k & 1)] = a;
-    dst[2 * (k & 1) + 1] = b;
+    const ph2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[k], 0.00390625f, false);  // bytes 0, 1
+    const ph2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[k], 0.00390625f, true);   // bytes 2, 3
+    ph8 &dst = k < 2 ? *lo : *hi;
+    const int e0 = 4 * (k & 1);
+    dst[e0] = a[0];
+    dst[e0 + 1] = a[1];
+    dst[e0 + 2] = b[0];
+    dst[e0 + 3] = b[1];
   }
-  *lo = __builtin_bit_cast(ph8, l);
-  *hi = __builtin_bit_cast(ph8, h);
 }
 
 // Broadcast of a quad's lane L (quad_perm [L, L, L, L]).
