@@ -877,13 +877,18 @@ def main():
                          "roofline_frac": round(r["achieved"] / HBM_PEAK_GBS, 4),
                          "bytes_per_call": r["bytes"]}
         log(f"[bench] append {r['us_per_call']:.2f} us/call, {r['gbs']:.0f} GB/s")
-        rp, _ = time_prefill("prompt_i8", 50, 50, 10, rounds=3)
-        res["prefill"] = {"workload": rp["workload"], "us_per_call": round(rp["us_per_call"], 3),
-                          "us_min": round(rp["us_min"], 3), "rounds": 3,
-                          "launches_per_round": 50, "tflops": round(rp["tflops"], 1),
-                          "roofline_frac": round(rp["tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
-                          "bound": "mfma", "flops_per_call": rp["flops"]}
-        log(f"[bench] prefill {rp['us_per_call']:.2f} us/call, {rp['tflops']:.0f} TFLOP/s")
+        # the multi-token route on the prompt workloads: int8 ("prefill"), f16 and fp8
+        for key, wname in (("prefill", "prompt_i8"), ("prefill_f16", "prompt_f16"),
+                           ("prefill_f8", "prompt_f8")):
+            rp, _ = time_prefill(wname, 50, 50, 10, rounds=3)
+            res[key] = {"workload": rp["workload"], "us_per_call": round(rp["us_per_call"], 3),
+                        "us_min": round(rp["us_min"], 3), "rounds": 3,
+                        "launches_per_round": 50, "tflops": round(rp["tflops"], 1),
+                        "roofline_frac": round(rp["tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
+                        "bound": "mfma", "flops_per_call": rp["flops"],
+                        "kernel": prefill_kernel_name(workloads.PREFILL_CONFIGS[wname])}
+            log(f"[bench] {key} ({wname}) {rp['us_per_call']:.2f} us/call, "
+                f"{rp['tflops']:.0f} TFLOP/s")
     if not args.no_cpu:
         log("[bench] timing the CPU oracle ...")
         res["cpu_baseline"] = cpu_baseline(b.prob)
