@@ -3,7 +3,7 @@
 
     python bench.py [--steps K] [--warmup W] [--config 5] [--gpus 1] [--no-cpu] [--no-append]
     python bench.py --op append [--append prefill_i8|prefill_f16|prefill_f8|decode_i8]
-    python bench.py --op prefill [--prefill prompt_i8|prompt_f16|prompt_f8]
+    python bench.py --op prefill [--prefill prompt_i8|prompt_f16|prompt_f8|prompt_q4]
     python bench.py --op merge
     python bench.py --sweep cliff|long|long_i8|long_f8
 
@@ -672,7 +672,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--op", choices=["decode", "append", "prefill", "merge"], default="decode")
     ap.add_argument("--prefill", default="prompt_i8",
-                    help="prefill workload for --op prefill: prompt_i8, prompt_f16, prompt_f8")
+                    help="prefill workload for --op prefill: prompt_i8, prompt_f16, prompt_f8, "
+                         "prompt_q4")
     ap.add_argument("--append", default="prefill_i8",
                     help="append workload for --op append: prefill_i8, prefill_f16, prefill_f8, "
                          "prefill_q4, decode_i8")
@@ -877,9 +878,9 @@ def main():
                          "roofline_frac": round(r["achieved"] / HBM_PEAK_GBS, 4),
                          "bytes_per_call": r["bytes"]}
         log(f"[bench] append {r['us_per_call']:.2f} us/call, {r['gbs']:.0f} GB/s")
-        # the multi-token route on the prompt workloads: int8 ("prefill"), f16 and fp8
+        # the multi-token route on the prompt workloads: int8 ("prefill"), f16, fp8 and q4_0
         for key, wname in (("prefill", "prompt_i8"), ("prefill_f16", "prompt_f16"),
-                           ("prefill_f8", "prompt_f8")):
+                           ("prefill_f8", "prompt_f8"), ("prefill_q4", "prompt_q4")):
             rp, _ = time_prefill(wname, 50, 50, 10, rounds=3)
             res[key] = {"workload": rp["workload"], "us_per_call": round(rp["us_per_call"], 3),
                         "us_min": round(rp["us_min"], 3), "rounds": 3,

@@ -105,7 +105,8 @@ typedef enum {
                                 element i + 16 in its high nibble --, scale pools one f16 d per
                                 32 elements laid out as int8's: value = (c - 8) * d. Pool
                                 strides are in bytes. head_dim 128, 256 or 512; decode, gather
-                                and append (see skvd_append); not the multi-token route. */
+                                and append (see skvd_append); the multi-token route at head_dim
+                                128 and 256. */
 } skvd_kv_dtype;
 
 typedef enum {
@@ -328,8 +329,10 @@ skvd_status skvd_stream_read(const void *buf, size_t bytes, uint32_t *sink, void
  * KV decode crash under graph capture; batch-aware VEC/TILE FA routing", section "Changes")
  * keeps the vector decode for at most 8 query tokens and routes larger batches to a tiled
  * matrix-core kernel; its tiled path first dequantized the quantized cache into f16 buffers.
- * This route is one tiled MFMA kernel that reads the pages itself and widens int8 (value =
- * int8 * f16 scale per 32 elements) on the way into LDS: no f16 temporary, no workspace.
+ * This route is one tiled MFMA kernel that reads the pages itself and widens the one-byte
+ * formats (int8: value = int8 * f16 scale per 32 elements; fp8: E4M3 * tensor scale; q4_0:
+ * (c - 8) * f16 scale per 32 elements) on the way into LDS: no f16 temporary, no workspace.
+ * Formats: f16, int8, fp8, q4_0; head_dim 128 or 256.
  *
  * - args: as skvd_decode_args, with q_per_seq = T in 1..max_kv_len (not bounded by the plan's
  *   max_q_per_seq); batch <= max_batch; o [B*T, Hq, D] f16 dense and lse [B*T, Hq] f32 (may be

@@ -128,9 +128,6 @@ skvd_status check_prefill(const skvd_plan *plan, const skvd_decode_args *a) {
   if (p.prm.head_dim != 128 && p.prm.head_dim != 256)
     return set_err(SKVD_ERR_SHAPE, "the multi-token route supports head_dim 128 and 256 (plan "
                    "has %d)", p.prm.head_dim);
-  if (p.prm.kv_dtype == SKVD_KV_Q4_0)
-    return set_err(SKVD_ERR_DTYPE, "the multi-token route reads f16, int8 and fp8 caches, not "
-                   "q4_0");
   skvd_decode_args one = *a;
   one.q_per_seq = 1;  // the remaining checks do not depend on the token count
   return skvd::check_args(p, &one, p.ws_bytes, g_err, sizeof g_err);

@@ -1,5 +1,5 @@
 // Prefill / multi-token route: T > 8 query tokens per sequence against the paged cache, as MFMA
-// tiles with int8 and fp8 caches widened on their way into LDS (no f16 temporary in memory).
+// tiles with int8, fp8 and q4_0 caches widened on their way into LDS (no f16 temporary in memory).
 //
 // llama-cpp-turboquant PR #176 ("HIP: fix turbo KV decode crash under graph capture;
 // batch-aware VEC/TILE FA routing", section "Changes") keeps the vector decode path for at most
@@ -28,9 +28,9 @@
 //
 // Two ways into LDS. f16 caches with pages of 16+ tokens: copies straight from HBM into LDS
 // (global_load_lds_dwordx4, no registers held), the next tile's copies in flight while the
-// current one is computed. int8 and fp8 caches, and pages of fewer than 16 tokens: the next
-// tile's rows are loaded into registers during the compute, widened (one-byte formats) and
-// stored into the other buffer (a second register stage does not fit: the allocator then
+// current one is computed. int8, fp8 and q4_0 caches, and pages of fewer than 16 tokens: the
+// next tile's rows are loaded into registers during the compute, widened (one-byte formats)
+// and stored into the other buffer (a second register stage does not fit: the allocator then
 // serializes the stages).
 #include <hip/hip_runtime.h>
 
@@ -94,18 +94,21 @@ __device__ __forceinline__ float rows4_max(float x) {
 // so it reads one page-table entry and forms one row address per tile. The loads
 // are ordinary (cached): every query tile of the sequence reads the same K/V tiles, so they
 // should stay in L2 and the Infinity Cache (non-temporal loads here cost 12-37 %).
-template <int D, bool I8, int NTH>
+template <int D, int KV, int NTH>
 struct TileRegs {
+  static constexpr bool I8 = KV != 0;  // one-byte layout (int8, fp8, q4_0)
   static constexpr int KT = kv_tile<D>();
-  // f16: 16-byte chunks of 8 elements; int8: 16-byte chunks of 16 elements (+ their scale)
-  static constexpr int CPR = I8 ? D / 16 : D / 8;  // chunks per row
+  // 16-byte chunks of a row: f16 8 elements; int8 and fp8 16 elements (int8: + their scale);
+  // q4_0 one 32-element group of codes (+ its scale)
+  static constexpr int CPR = KV == 3 ? D / 32 : I8 ? D / 16 : D / 8;  // chunks per row
   static constexpr int TPT = NTH / KT;             // threads per token (NTH: the workgroup's)
   static constexpr int N = CPR / TPT;              // chunks per thread per tensor
+  static_assert(N >= 1, "at least one chunk per thread");
   pu4 k[N], v[N];
   _Float16 ks[I8 ? N : 1], vs[I8 ? N : 1];
   // int8 with four threads per token (D = 128): the token's K scales (thread 0 of the quad) or
   // V scales (thread 1), all four groups in one 8-byte load, shared over the quad by DPP
-  static constexpr bool kQuadScales = I8 && TPT == 4 && N == 2;
+  static constexpr bool kQuadScales = KV == 1 && TPT == 4 && N == 2;
   unsigned sq[2];
 };
 
@@ -117,7 +120,7 @@ struct TileRegs {
 // the loop's waits for a page entry do not also wait for the tile loads issued after it.
 template <int D, bool I8, int NTH, bool PT>
 __device__ __forceinline__ int tile_page(const LaunchArgs &a, int b, int kv0, int kv_last) {
-  using TR = TileRegs<D, I8, NTH>;
+  using TR = TileRegs<D, I8 ? 1 : 0, NTH>;  // (threads per token: the same for every format)
   if constexpr (PT) {
     typedef const __attribute__((address_space(4))) int32_t *ctab_t;
     const int wave_tok = (int)(threadIdx.x & ~63u) / TR::TPT;  // the wave's first token
@@ -129,14 +132,14 @@ __device__ __forceinline__ int tile_page(const LaunchArgs &a, int b, int kv0, in
   }
 }
 
-// KV: 0 f16, 1 int8 with per-32 f16 scales, 2 fp8 E4M3 with one f32 scale per tensor (the
-// one-byte formats share the int8 tile layout; only int8 loads per-row scales). pg: the
-// thread's tile_page entry for this tile.
+// KV: 0 f16, 1 int8 with per-32 f16 scales, 2 fp8 E4M3 with one f32 scale per tensor, 3 q4_0
+// (rows of D/2 code bytes, per-32 f16 scales; a thread loads whole groups). The one-byte
+// formats share the int8 tile layout in LDS. pg: the thread's tile_page entry for this tile.
 template <int D, int KV, int NTH>
 __device__ __forceinline__ void load_tile(const LaunchArgs &a, int kvh, int kv0, int kv_last,
-                                          int pg, TileRegs<D, KV != 0, NTH> &r) {
+                                          int pg, TileRegs<D, KV, NTH> &r) {
   constexpr bool I8 = KV != 0;
-  using TR = TileRegs<D, I8, NTH>;
+  using TR = TileRegs<D, KV, NTH>;
   const int P1 = (1 << a.page_shift) - 1;
   const int tok = min(kv0 + (int)threadIdx.x / TR::TPT, kv_last);  // tail re-reads (masked)
   const int part0 = ((int)threadIdx.x % TR::TPT) * TR::N;  // one-byte: chunks part0 .. + N - 1
@@ -173,8 +176,9 @@ __device__ __forceinline__ void load_tile(const LaunchArgs &a, int kvh, int kv0,
       r.k[n] = kp[n];
       r.v[n] = vp[n];
       if constexpr (!TR::kQuadScales) {
-        r.ks[n] = ksp[(part0 + n) >> 1];  // a 16-element chunk lies in scale group chunk / 2
-        r.vs[n] = vsp[(part0 + n) >> 1];
+        // int8: a 16-element chunk lies in scale group chunk / 2; q4_0: chunk = group
+        r.ks[n] = ksp[KV == 3 ? part0 + n : (part0 + n) >> 1];
+        r.vs[n] = vsp[KV == 3 ? part0 + n : (part0 + n) >> 1];
       }
     }
     if constexpr (TR::kQuadScales) {
@@ -233,6 +237,32 @@ __device__ __forceinline__ void widen16_f8(pu4 w, ph8 *lo, ph8 *hi) {
   }
 }
 
+// One q4_0 group (16 code bytes: byte i holds element i in its low nibble and element 16 + i in
+// its high nibble) -> four groups of 8 f16, (c - 8) times the f16 scale (one rounding, as the
+// int8 path): a nibble c placed under the f16 exponent byte of 1024 is 1024 + c exactly; one
+// packed subtract of 1032 leaves c - 8 exactly; one packed multiply applies the scale.
+__device__ __forceinline__ void widen_q4(pu4 w, _Float16 s, ph8 *c) {
+  const ph2 s2 = {s, s};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const unsigned lo = w[k] & 0x0F0F0F0Fu, hi = (w[k] >> 4) & 0x0F0F0F0Fu;
+    const int e0 = 4 * (k & 1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const unsigned nib = h ? hi : lo;
+      const ph2 a = (__builtin_bit_cast(ph2, __builtin_amdgcn_perm(0x64646464u, nib, 0x04010400u)) -
+                     (ph2)(_Float16)1032) * s2;  // bytes 0, 1
+      const ph2 b = (__builtin_bit_cast(ph2, __builtin_amdgcn_perm(0x64646464u, nib, 0x04030402u)) -
+                     (ph2)(_Float16)1032) * s2;  // bytes 2, 3
+      ph8 &dst = c[2 * h + (k >> 1)];  // elements 4k .. 4k+3 (low) or 16 + 4k .. (high)
+      dst[e0] = a[0];
+      dst[e0 + 1] = a[1];
+      dst[e0 + 2] = b[0];
+      dst[e0 + 3] = b[1];
+    }
+  }
+}
+
 // Broadcast of a quad's lane L (quad_perm [L, L, L, L]).
 template <int L>
 __device__ __forceinline__ unsigned quad_bcast(unsigned x) {
@@ -241,9 +271,9 @@ __device__ __forceinline__ unsigned quad_bcast(unsigned x) {
 
 template <int D, int KV, int NTH>
 __device__ __forceinline__ void store_tile(char *k_lds, char *v_lds,
-                                           const TileRegs<D, KV != 0, NTH> &r) {
+                                           const TileRegs<D, KV, NTH> &r) {
   constexpr bool I8 = KV != 0;
-  using TR = TileRegs<D, I8, NTH>;
+  using TR = TileRegs<D, KV, NTH>;
   _Float16 qks = 0, qvs = 0;  // kQuadScales: this thread's group (its quad index) of K and V
   if constexpr (TR::kQuadScales) {
     const unsigned q = threadIdx.x & 3u;
@@ -264,6 +294,15 @@ __device__ __forceinline__ void store_tile(char *k_lds, char *v_lds,
     if constexpr (!I8) {
       *(pu4 *)(k_lds + pswz<ROWB, false>(tok, part)) = r.k[n];
       *(pu4 *)(v_lds + pswz<ROWB, false>(tok, part)) = r.v[n];
+    } else if constexpr (KV == 3) {
+      // one group: f16 chunks 4 part .. + 3 of the row (the int8 layout's chunks of this thread)
+      ph8 c4[4];
+      widen_q4(r.k[n], r.ks[n], c4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *(ph8 *)(k_lds + pswz<ROWB, true>(tok, 4 * part + j)) = c4[j];
+      widen_q4(r.v[n], r.vs[n], c4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *(ph8 *)(v_lds + pswz<ROWB, true>(tok, 4 * part + j)) = c4[j];
     } else {
       ph8 lo, hi;
       if constexpr (KV == 2) widen16_f8(r.k[n], &lo, &hi);
@@ -385,7 +424,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_kernel(Launc
 
   const int ntiles = kv_end > 0 ? (kv_end + KT - 1) / KT : 0;
   // The next tile's loads run one step ahead of its use, its page-table entries one more.
-  TileRegs<D, I8, NTH> regs;  // (I8: the one-byte layout)
+  TileRegs<D, KV, NTH> regs;
   int pg_ahead = 0;           // the page entry of the next tile to be loaded
   if (ntiles > 0) {
     load_tile<D, KV, NTH>(a, kvh, 0, kv_end - 1, tile_page<D, I8, NTH, PT>(a, b, 0, kv_end - 1),
@@ -793,7 +832,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_dma_kernel(L
         }
 #pragma unroll
         for (int rs = 0; rs < RS; ++rs)
-          acc[rs][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[rs][ch], acc[rs][dt], 0, 0, 0);
+          acc[rs][dt] =
+              __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[rs][ch], acc[rs][dt], 0, 0, 0);
       }
 #pragma unroll
       for (int rs = 0; rs < RS; ++rs)
@@ -873,11 +913,13 @@ void launch_pd(const LaunchArgs &a, hipStream_t st) {
     return;
   }
   if (a.page_shift >= 4) {  // pages of 16 tokens or more: wave-uniform page entries
-    if (a.fp8) prefill_kernel<D, 2, NW, true><<<grid, 64 * NW, 0, st>>>(a, tpw, qtiles);
+    if (a.q4) prefill_kernel<D, 3, NW, true><<<grid, 64 * NW, 0, st>>>(a, tpw, qtiles);
+    else if (a.fp8) prefill_kernel<D, 2, NW, true><<<grid, 64 * NW, 0, st>>>(a, tpw, qtiles);
     else if (a.int8) prefill_kernel<D, 1, NW, true><<<grid, 64 * NW, 0, st>>>(a, tpw, qtiles);
     else prefill_kernel<D, 0, NW, true><<<grid, 64 * NW, 0, st>>>(a, tpw, qtiles);
   } else {
-    if (a.fp8) prefill_kernel<D, 2, NW, false><<<grid, 64 * NW, 0, st>>>(a, tpw, qtiles);
+    if (a.q4) prefill_kernel<D, 3, NW, false><<<grid, 64 * NW, 0, st>>>(a, tpw, qtiles);
+    else if (a.fp8) prefill_kernel<D, 2, NW, false><<<grid, 64 * NW, 0, st>>>(a, tpw, qtiles);
     else if (a.int8) prefill_kernel<D, 1, NW, false><<<grid, 64 * NW, 0, st>>>(a, tpw, qtiles);
     else prefill_kernel<D, 0, NW, false><<<grid, 64 * NW, 0, st>>>(a, tpw, qtiles);
   }

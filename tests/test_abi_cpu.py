@@ -378,7 +378,7 @@ def test_decode_check_q4(over, status):
 
 def test_q4_plan_and_routes():
     """q4_0 plans at head_dim 128, 256 and 512 (not 192); the append takes the scale pools;
-    the multi-token route refuses the format."""
+    so does the multi-token route (head_dim 128 and 256)."""
     p = plan(kv_dtype="q4")
     assert p.kv_dtype == "q4" and "kv=q4_0" in p.describe() and p.info.heads_per_wg == 4
     for D in (256, 512):
@@ -393,7 +393,11 @@ def test_q4_plan_and_routes():
                                                            head_stride=64)) == 4  # no scales
     d = good_args(p, i8=True, q_per_seq=512, page_stride=16 * 8 * 64, tok_stride=8 * 64,
                   head_stride=64)
-    assert bd.skvd_prefill_check(p.handle, d) == 4
+    assert bd.skvd_prefill_check(p.handle, d) == 0
+    p512 = plan(kv_dtype="q4", head_dim=512)
+    d512 = good_args(p512, i8=True, q_per_seq=512, page_stride=16 * 8 * 256, tok_stride=8 * 256,
+                     head_stride=256)
+    assert bd.skvd_prefill_check(p512.handle, d512) == 2  # head_dim 512: not on this route
 
 
 def test_plan_waves_per_cu_by_format():

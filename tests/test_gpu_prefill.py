@@ -57,6 +57,9 @@ CASES = [
     ("gqa4_f8", 2, 100, 32, 8, 128, 16, "f8", (100, 1000)),
     ("gqa8_d256_f8_p4", 2, 50, 16, 2, 256, 4, "f8", (50, 777)),
     ("mha_f8_p1_ragged", 3, 40, 4, 4, 128, 1, "f8", (40, 41, 300)),
+    ("gqa4_q4", 2, 100, 32, 8, 128, 16, "q4", (100, 1000)),
+    ("mha_d256_q4_p4", 2, 50, 8, 8, 256, 4, "q4", (50, 777)),
+    ("gqa8_q4_p64_ragged", 3, 70, 32, 4, 128, 64, "q4", (70, 71, 2049)),
 ]
 
 
@@ -78,7 +81,7 @@ def test_prefill_rows_without_positions():
     assert (o.reshape(2, 8, 8, 128)[0, :3] == 0).all()
 
 
-@pytest.mark.parametrize("kv", ["i8", "f8"])
+@pytest.mark.parametrize("kv", ["i8", "f8", "q4"])
 def test_prefill_equals_decode_route(kv):
     """For T <= 8 both routes compute the same attention: each matches the oracle, and they agree
     with each other within the tolerance."""
@@ -156,7 +159,7 @@ def test_prefill_long_prompt_sampled():
     check(s, 70)
 
 
-@pytest.mark.parametrize("kv", ["i8", "f8"])
+@pytest.mark.parametrize("kv", ["i8", "f8", "q4"])
 def test_attention_routing(kv):
     """skvd_attention: T = 4 takes the decode (bit-identical to run()), T = 40 the tiled route
     (bit-identical to prefill())."""

@@ -384,6 +384,7 @@ PREFILL_CONFIGS = {
     "prompt_i8": Spec("prefill_prompt_i8", 4, 2048, 32, 8, 128, 16, "i8", ("fixed", 2048)),
     "prompt_f16": Spec("prefill_prompt_f16", 4, 2048, 32, 8, 128, 16, "f16", ("fixed", 2048)),
     "prompt_f8": Spec("prefill_prompt_f8", 4, 2048, 32, 8, 128, 16, "f8", ("fixed", 2048)),
+    "prompt_q4": Spec("prefill_prompt_q4", 4, 2048, 32, 8, 128, 16, "q4", ("fixed", 2048)),
 }
 
 
