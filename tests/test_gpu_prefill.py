@@ -104,9 +104,13 @@ def test_prefill_deterministic():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-def test_prefill_graph_capture_replay():
-    s = workloads.spec(name="graph_prefill", batch=2, q_per_seq=40, num_qo_heads=8,
-                       num_kv_heads=2, head_dim=128, page_size=16, kv_dtype="i8",
+@pytest.mark.parametrize("kv", ["i8", "f16", "q4"])
+def test_prefill_graph_capture_replay(kv):
+    """Replays of a captured multi-token call (f16: the kernel that copies tiles straight into
+    LDS; int8 / q4_0: the register-staged one) match the oracle and each other bit for bit,
+    with eager work between the replays."""
+    s = workloads.spec(name=f"graph_prefill_{kv}", batch=2, q_per_seq=40, num_qo_heads=8,
+                       num_kv_heads=2, head_dim=128, page_size=16, kv_dtype=kv,
                        lens=("list", (40, 1000)))
     prob = workloads.generate(s, 65)
     dev = to_dev(prob)
