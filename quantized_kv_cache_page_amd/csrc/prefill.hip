@@ -106,9 +106,11 @@ struct TileRegs {
   static_assert(N >= 1, "at least one chunk per thread");
   pu4 k[N], v[N];
   _Float16 ks[I8 ? N : 1], vs[I8 ? N : 1];
-  // int8 with four threads per token (D = 128): the token's K scales (thread 0 of the quad) or
-  // V scales (thread 1), all four groups in one 8-byte load, shared over the quad by DPP
-  static constexpr bool kQuadScales = KV == 1 && TPT == 4 && N == 2;
+  // int8 and q4_0 with four threads per token (D = 128; thread q of the quad serves group q):
+  // the token's K scales (thread 0 of the quad) or V scales (thread 1), all four groups in one
+  // 8-byte load, shared over the quad by DPP
+  static constexpr bool kQuadScales =
+      TPT == 4 && ((KV == 1 && N == 2) || (KV == 3 && N == 1));
   unsigned sq[2];
 };
 
@@ -297,10 +299,10 @@ __device__ __forceinline__ void store_tile(char *k_lds, char *v_lds,
     } else if constexpr (KV == 3) {
       // one group: f16 chunks 4 part .. + 3 of the row (the int8 layout's chunks of this thread)
       ph8 c4[4];
-      widen_q4(r.k[n], r.ks[n], c4);
+      widen_q4(r.k[n], TR::kQuadScales ? qks : r.ks[n], c4);
 #pragma unroll
       for (int j = 0; j < 4; ++j) *(ph8 *)(k_lds + pswz<ROWB, true>(tok, 4 * part + j)) = c4[j];
-      widen_q4(r.v[n], r.vs[n], c4);
+      widen_q4(r.v[n], TR::kQuadScales ? qvs : r.vs[n], c4);
 #pragma unroll
       for (int j = 0; j < 4; ++j) *(ph8 *)(v_lds + pswz<ROWB, true>(tok, 4 * part + j)) = c4[j];
     } else {
