@@ -783,10 +783,14 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_dma_kernel(L
       }
       mrow[rs] = rows4_max(mx) * c;
     }
+    // one rescale branch for both row sets (one fewer basic-block boundary in the tile)
+    bool any_raise = false;
 #pragma unroll
-    for (int rs = 0; rs < RS; ++rs) {
-      const bool raise = mrow[rs] > m[rs] + 8.f;
-      if (__any(raise)) {
+    for (int rs = 0; rs < RS; ++rs) any_raise |= mrow[rs] > m[rs] + 8.f;
+    if (__any(any_raise)) {
+#pragma unroll
+      for (int rs = 0; rs < RS; ++rs) {
+        const bool raise = mrow[rs] > m[rs] + 8.f;
         const float m_new = raise ? mrow[rs] : m[rs];
         const float alpha = __builtin_amdgcn_exp2f(m[rs] - m_new);
         m[rs] = m_new;
