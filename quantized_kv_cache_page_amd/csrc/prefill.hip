@@ -869,9 +869,16 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_dma_kernel(L
                           stg[bn] + DT::BYTES);
     }
     pf4 s[RS][NST];
+    // raised issue priority over the MFMA phases: when the other workgroup's wave on this SIMD
+    // is in its softmax, this wave's MFMAs go first (measured 1 % faster; the softmax raised
+    // instead: 0.5 % slower)
+    __builtin_amdgcn_s_setprio(1);
     scores(stg[bi], s);
+    __builtin_amdgcn_s_setprio(0);
     mask_max(s, it);
+    __builtin_amdgcn_s_setprio(1);
     exp_pv(stg[bi], s);
+    __builtin_amdgcn_s_setprio(0);
     bi = bi == NSTG - 1 ? 0 : bi + 1;
   }
 
