@@ -16,12 +16,21 @@ def say(*a):
     sys.stdout.flush()
 
 
-def to_dev(prob, device="cuda:0"):
+def to_dev(prob, device="cuda:0", layout="nhd"):
+    """The problem's arrays on the device. layout "hnd": the K/V pools and int8 / q4_0 scale
+    pools [N, P, Hkv, X] are stored as [N, Hkv, P, X] (each KV head's page rows contiguous) and
+    passed as the permuted view, so the kernels see the HND strides with the same values."""
     d = {}
     for k in ("q", "k_pages", "v_pages", "k_scales", "v_scales", "page_table", "kv_len"):
         v = prob.get(k)
-        d[k] = None if v is None else torch.from_numpy(np.ascontiguousarray(v) if k in
-                                                       ("page_table", "kv_len") else v).to(device)
+        if v is None:
+            d[k] = None
+        elif layout == "hnd" and k in ("k_pages", "v_pages", "k_scales", "v_scales") and v.ndim == 4:
+            d[k] = torch.from_numpy(np.ascontiguousarray(v.transpose(0, 2, 1, 3))).to(
+                device).permute(0, 2, 1, 3)
+        else:
+            d[k] = torch.from_numpy(np.ascontiguousarray(v) if k in
+                                    ("page_table", "kv_len") else v).to(device)
     return d
 
 

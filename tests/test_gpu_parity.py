@@ -268,6 +268,40 @@ def test_strided_q_and_shorter_v_pool():
     compare(o, lse, ref_o, ref_l, what="strided q, unequal pools")
 
 
+HND_CASES = [
+    # (kv, B, T, Hq, Hkv, D, P, lens)
+    ("f16", 3, 1, 32, 8, 128, 16, (33, 1500, 4100)),
+    ("f16", 2, 4, 32, 16, 256, 16, (700, 3000)),
+    ("i8", 3, 1, 32, 8, 128, 16, (33, 1500, 4100)),
+    ("i8", 2, 2, 16, 8, 256, 64, (129, 2049)),
+    ("f8", 3, 1, 32, 8, 128, 64, (64, 1500, 4100)),
+    ("q4", 3, 1, 32, 8, 128, 16, (33, 1500, 4100)),
+    ("q4", 2, 4, 32, 16, 256, 16, (700, 3000)),
+    ("f16", 2, 1, 8, 2, 128, 4, (5, 300)),
+]
+
+
+@pytest.mark.parametrize("case", HND_CASES, ids=[f"{c[0]}_D{c[5]}_P{c[6]}_T{c[2]}" for c in
+                                                 HND_CASES])
+@pytest.mark.parametrize("sched", ["auto", "static"])
+def test_hnd_pools(case, sched):
+    """K/V pools (and int8 / q4_0 scale pools) in HND memory order: each KV head's page rows
+    contiguous, passed as the permuted [N, P, Hkv, X] view; the decode reads them through the
+    strides alone (the results depend only on the values)."""
+    kv, B, T, Hq, Hkv, D, P, lens = case
+    s = spec(name=f"hnd_{kv}", batch=B, q_per_seq=T, num_qo_heads=Hq, num_kv_heads=Hkv,
+             head_dim=D, page_size=P, kv_dtype=kv, lens=("list", lens))
+    prob = workloads.generate(s, 91)
+    dev = to_dev(prob, layout="hnd")
+    assert dev["k_pages"].stride(1) != dev["k_pages"].shape[2] * dev["k_pages"].shape[3]
+    plan = make_plan(prob, schedule=sched)
+    say(f"case hnd {kv} D={D} P={P} T={T} {sched}: {plan.describe()}")
+    o, lse = run(plan, prob, dev)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.decode(prob)
+    compare(o, lse, ref_o, ref_l, what=f"hnd {kv} {sched}")
+
+
 def test_read_only_and_canaries():
     """Inputs bit-identical after the call; nothing written outside o and lse."""
     s = spec(name="ro", batch=4, q_per_seq=2, num_qo_heads=8, num_kv_heads=4, head_dim=128,

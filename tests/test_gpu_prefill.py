@@ -95,6 +95,24 @@ def test_prefill_equals_decode_route(kv):
     assert float((l1 - l2).abs().max()) <= 1e-3
 
 
+@pytest.mark.parametrize("kv,P", [("f16", 16), ("f16", 64), ("i8", 16), ("f8", 16),
+                                  ("q4", 16)])
+def test_prefill_hnd_pools(kv, P):
+    """The multi-token route over HND pools (each KV head's page rows contiguous, passed as the
+    permuted view): f16 copies tiles into LDS through the HND strides, the one-byte formats load
+    and widen them."""
+    s = workloads.spec(name=f"pf_hnd_{kv}", batch=2, q_per_seq=70, num_qo_heads=32,
+                       num_kv_heads=8, head_dim=128, page_size=P, kv_dtype=kv,
+                       lens=("list", (70, 2100)))
+    prob = workloads.generate(s, 93)
+    dev = to_dev(prob, layout="hnd")
+    plan = make_plan(prob, max_q_per_seq=1)
+    o, lse = prefill(plan, prob, dev)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode(prob)
+    compare(o, lse, ro, rl, what=f"prefill hnd {kv} P={P}")
+
+
 def test_prefill_deterministic():
     s = workloads.spec(name="det", batch=2, q_per_seq=33, num_qo_heads=8, num_kv_heads=2,
                        head_dim=128, page_size=16, kv_dtype="f16", lens=("list", (33, 500)))
