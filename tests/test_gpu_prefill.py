@@ -113,6 +113,52 @@ def test_prefill_hnd_pools(kv, P):
     compare(o, lse, ro, rl, what=f"prefill hnd {kv} P={P}")
 
 
+@pytest.mark.parametrize("kv", ["f16", "i8", "q4"])
+@pytest.mark.parametrize("form", ["halves", "interleaved", "layer"])
+def test_prefill_cache_views(kv, form):
+    """The multi-token route with K and V as views of one tensor (the halves of [2, pages, ...],
+    the interleaved [pages, 2, ...], layer 1 of a [layers, 2, pages, ...] pool): addressed
+    through the views' strides alone (f16: the copies into LDS), the result matches the oracle
+    and the tensor keeps its bytes."""
+    s = workloads.spec(name=f"pf_views_{form}_{kv}", batch=2, q_per_seq=40, num_qo_heads=16,
+                       num_kv_heads=4, head_dim=128, page_size=16, kv_dtype=kv,
+                       lens=("list", (40, 1500)))
+    prob = workloads.generate(s, 95)
+
+    def combined(k, v):
+        if k is None:
+            return None, None, None
+        if form == "halves":
+            big = np.stack([k, v])                       # [2, N, P, H, X]
+            return big, big[0], big[1]
+        if form == "interleaved":
+            big = np.ascontiguousarray(np.stack([k, v], axis=1))  # [N, 2, P, H, X]
+            return big, big[:, 0], big[:, 1]
+        big = np.stack([np.stack([v, k]), np.stack([k, v])])     # [layers=2, 2, N, P, H, X]
+        return big, big[1, 0], big[1, 1]
+
+    def dev_view(t, npview, base):
+        off = (npview.__array_interface__["data"][0] - base.__array_interface__["data"][0])
+        st = [x // npview.itemsize for x in npview.strides]
+        return torch.as_strided(t, npview.shape, st, off // npview.itemsize)
+
+    bkv, kview, vview = combined(prob["k_pages"], prob["v_pages"])
+    bsc, ksview, vsview = combined(prob["k_scales"], prob["v_scales"])
+    tk = torch.from_numpy(bkv).cuda()
+    ts = None if bsc is None else torch.from_numpy(bsc).cuda()
+    dev = to_dev(prob)
+    dev["k_pages"], dev["v_pages"] = dev_view(tk, kview, bkv), dev_view(tk, vview, bkv)
+    if ts is not None:
+        dev["k_scales"], dev["v_scales"] = dev_view(ts, ksview, bsc), dev_view(ts, vsview, bsc)
+    before = tk.clone()
+    plan = make_plan(prob, max_q_per_seq=1)
+    o, lse = prefill(plan, prob, dev)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode(prob)
+    compare(o, lse, ro, rl, what=f"prefill views {form} {kv}")
+    assert torch.equal(tk.view(torch.uint8), before.view(torch.uint8))
+
+
 def test_prefill_deterministic():
     s = workloads.spec(name="det", batch=2, q_per_seq=33, num_qo_heads=8, num_kv_heads=2,
                        head_dim=128, page_size=16, kv_dtype="f16", lens=("list", (33, 500)))
