@@ -159,6 +159,42 @@ def test_prefill_cache_views(kv, form):
     assert torch.equal(tk.view(torch.uint8), before.view(torch.uint8))
 
 
+@pytest.mark.parametrize("kv", ["f16", "i8"])
+def test_prefill_strided_q_unequal_pools_read_only(kv):
+    """q sliced from a fused QKV buffer (token stride > Hq*D), a K pool longer than the V pool
+    (only indexed pages are read), outputs inside larger canary buffers: o and lse match the
+    oracle, every input and every canary keeps its bytes."""
+    s = workloads.spec(name=f"pf_strided_{kv}", batch=3, q_per_seq=24, num_qo_heads=16,
+                       num_kv_heads=4, head_dim=128, page_size=16, kv_dtype=kv,
+                       lens=("list", (24, 500, 1300)), spare_frac=0.0)
+    prob = workloads.generate(s, 97)
+    ro, rl = oracle.decode(prob)
+    dev = to_dev(prob)
+    rows = dev["q"].shape[0]
+    qkv = torch.randn((rows, 16 + 8, 128), device="cuda").to(torch.float16)
+    qkv[:, :16] = dev["q"]
+    dev["q"] = qkv[:, :16]
+    extra = torch.full((5,) + tuple(dev["k_pages"].shape[1:]), 0x7F, dtype=torch.uint8,
+                       device="cuda").view(dev["k_pages"].dtype) if kv != "f16" else \
+        torch.full((5,) + tuple(dev["k_pages"].shape[1:]), float("nan"), dtype=torch.float16,
+                   device="cuda")
+    dev["k_pages"] = torch.cat([dev["k_pages"], extra])  # K pool longer than V pool
+    inputs = {k: v.clone() for k, v in dev.items() if v is not None}
+    qkv_before = qkv.clone()
+    o_buf = torch.full((rows + 2, 16, 128), 7.0, dtype=torch.float16, device="cuda")
+    l_buf = torch.full((rows + 2, 16), 7.0, dtype=torch.float32, device="cuda")
+    o, lse = o_buf[1:-1], l_buf[1:-1]
+    plan = make_plan(prob, max_q_per_seq=1)
+    prefill(plan, prob, dev, out=o, lse=lse)
+    torch.cuda.synchronize()
+    compare(o, lse, ro, rl, what=f"prefill strided {kv}")
+    for k, v in inputs.items():
+        assert torch.equal(dev[k].view(torch.uint8), v.view(torch.uint8)), k
+    assert torch.equal(qkv.view(torch.uint8), qkv_before.view(torch.uint8))
+    assert torch.all(o_buf[0] == 7.0) and torch.all(o_buf[-1] == 7.0)
+    assert torch.all(l_buf[0] == 7.0) and torch.all(l_buf[-1] == 7.0)
+
+
 def test_prefill_deterministic():
     s = workloads.spec(name="det", batch=2, q_per_seq=33, num_qo_heads=8, num_kv_heads=2,
                        head_dim=128, page_size=16, kv_dtype="f16", lens=("list", (33, 500)))
