@@ -60,6 +60,10 @@ CASES = [
     ("gqa4_q4", 2, 100, 32, 8, 128, 16, "q4", (100, 1000)),
     ("mha_d256_q4_p4", 2, 50, 8, 8, 256, 4, "q4", (50, 777)),
     ("gqa8_q4_p64_ragged", 3, 70, 32, 4, 128, 64, "q4", (70, 71, 2049)),
+    ("mha_f16_p16", 2, 150, 8, 8, 128, 16, "f16", (150, 900)),
+    ("g3_f16_p16", 2, 50, 12, 4, 128, 16, "f16", (50, 700)),
+    ("g64_f16_p16", 1, 20, 64, 1, 128, 16, "f16", (300,)),
+    ("g3_d256_f16_p32", 2, 33, 6, 2, 256, 32, "f16", (33, 400)),
 ]
 
 
