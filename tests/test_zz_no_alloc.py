@@ -1,8 +1,8 @@
 """The allocation-free decode (skvd_decode_noalloc, the library's own device workspace) through
 the C ABI against skvd_decode with a caller workspace: bit-identical outputs on two calls in a
 row, the second with a smaller batch and shorter sequences (the array keeps the first call's
-contents), over f16, int8, fp8 and q4_0 caches; plans whose workspace exceeds the array's size
-and debug plans are refused."""
+contents), over f16, int8, fp8 and q4_0 caches at head_dim 128 and the one-byte formats at 256;
+plans whose workspace exceeds the array's size and debug plans are refused."""
 import numpy as np
 import pytest
 import torch
@@ -32,15 +32,19 @@ def _noalloc(plan, prob, dev):
     return out, lse
 
 
-@pytest.mark.parametrize("kv,T,Hq,Hkv,sched", [("f16", 1, 32, 8, "auto"), ("i8", 1, 32, 8, "auto"),
-                                               ("i8", 4, 16, 4, "static"),
-                                               ("f8", 8, 32, 4, "auto"), ("q4", 2, 32, 8, "auto")])
-def test_noalloc_matches_decode(kv, T, Hq, Hkv, sched):
+@pytest.mark.parametrize("kv,T,Hq,Hkv,sched,D", [("f16", 1, 32, 8, "auto", 128),
+                                                 ("i8", 1, 32, 8, "auto", 128),
+                                                 ("i8", 4, 16, 4, "static", 128),
+                                                 ("f8", 8, 32, 4, "auto", 128),
+                                                 ("q4", 2, 32, 8, "auto", 128),
+                                                 ("i8", 4, 32, 16, "auto", 256),
+                                                 ("f8", 2, 16, 8, "auto", 256)])
+def test_noalloc_matches_decode(kv, T, Hq, Hkv, sched, D):
     big = workloads.spec(name="na_big", batch=6, q_per_seq=T, num_qo_heads=Hq, num_kv_heads=Hkv,
-                         head_dim=128, page_size=16, kv_dtype=kv,
+                         head_dim=D, page_size=16, kv_dtype=kv,
                          lens=("list", (9000, 700, 2049, 64, 3000, 8)))
     small = workloads.spec(name="na_small", batch=3, q_per_seq=T, num_qo_heads=Hq,
-                           num_kv_heads=Hkv, head_dim=128, page_size=16, kv_dtype=kv,
+                           num_kv_heads=Hkv, head_dim=D, page_size=16, kv_dtype=kv,
                            lens=("list", (100, 1500, 9)))
     pb = workloads.generate(big, 31)
     ps = workloads.generate(small, 32)
