@@ -4,8 +4,9 @@ The decode, the multi-token (prefill) route and the append that writes new token
 cache run in hand-written HIP kernels behind the C ABI of ``include/skvd.h`` (``libskvd.so``, built in-tree by
 ``python -m quantized_kv_cache_page_amd.build``). This package is its thin Python face: ``Plan`` marshals torch tensors into those calls, and the
 ``skvd_*`` functions are the C-ABI entry points under the same names. ``ops`` registers the
-decode and append as torch operators (``torch.ops.skvd.decode_v1``, ``decode_out_v1``,
-``append_v1``) whose schemas declare exactly what they write.
+decode, the multi-token route and the append as torch operators (``torch.ops.skvd.decode_v1``,
+``decode_out_v1``, ``prefill_v1``, ``prefill_out_v1``, ``append_v1``) whose schemas declare
+exactly what they write.
 """
 from ._binding import (  # noqa: F401
     LIB_PATH, REDUCERS, SIGNATURES, Plan, SkvdError, last_error, lib, skvd_abi_version_py,

@@ -15,6 +15,9 @@ Here:
 * ``skvd::decode_v1`` returns fresh ``(o, lse)`` and declares nothing mutated;
 * ``skvd::decode_out_v1`` writes caller-provided ``out`` and ``lse`` and declares exactly those
   two as mutated;
+* ``skvd::prefill_v1`` and ``skvd::prefill_out_v1`` are the same pair for the multi-token route
+  (a query block of T tokens per sequence, causal over its own last T positions): the page
+  treats its paged prefill op the way it treats the decode ops, declaring only the real outputs;
 * ``skvd::append_v1`` writes new tokens into the cache and declares the pools (and, for an int8
   cache, the scale pools) mutated, because it writes them.
 
@@ -97,6 +100,43 @@ def _decode_out_v1_fake(q, k_pages, v_pages, page_table, kv_len, k_scales, v_sca
     return None
 
 
+# ---------------------------------------------------------------------------- multi-token
+@torch.library.custom_op("skvd::prefill_v1", mutates_args=(), device_types="cuda")
+def prefill_v1(q: Tensor, k_pages: Tensor, v_pages: Tensor, page_table: Tensor, kv_len: Tensor,
+               k_scales: Optional[Tensor], v_scales: Optional[Tensor], sm_scale: float,
+               q_per_seq: int, plan_id: int) -> tuple[Tensor, Tensor]:
+    """Multi-token route; returns (o [B*T, Hq, D] f16 dense, lse [B*T, Hq] f32). Reads every
+    input."""
+    return _plan(plan_id).prefill(q, k_pages, v_pages, page_table, kv_len, sm_scale, k_scales,
+                                  v_scales, q_per_seq=q_per_seq)
+
+
+@prefill_v1.register_fake
+def _prefill_v1_fake(q, k_pages, v_pages, page_table, kv_len, k_scales, v_scales, sm_scale,
+                     q_per_seq, plan_id):
+    o = q.new_empty(q.shape, dtype=torch.float16)
+    lse = q.new_empty(q.shape[:2], dtype=torch.float32)
+    return o, lse
+
+
+@torch.library.custom_op("skvd::prefill_out_v1", mutates_args=("out", "lse"),
+                         device_types="cuda")
+def prefill_out_v1(q: Tensor, k_pages: Tensor, v_pages: Tensor, page_table: Tensor,
+                   kv_len: Tensor, k_scales: Optional[Tensor], v_scales: Optional[Tensor],
+                   sm_scale: float, q_per_seq: int, plan_id: int, out: Tensor,
+                   lse: Tensor) -> None:
+    """Multi-token route into caller-provided out (contiguous f16 [B*T, Hq, D]) and lse
+    (contiguous f32 [B*T, Hq]); declares exactly those two as written."""
+    _plan(plan_id).prefill(q, k_pages, v_pages, page_table, kv_len, sm_scale, k_scales,
+                           v_scales, out=out, lse=lse, q_per_seq=q_per_seq)
+
+
+@prefill_out_v1.register_fake
+def _prefill_out_v1_fake(q, k_pages, v_pages, page_table, kv_len, k_scales, v_scales, sm_scale,
+                         q_per_seq, plan_id, out, lse):
+    return None
+
+
 # ---------------------------------------------------------------------------- append
 @torch.library.custom_op("skvd::append_v1", mutates_args=("k_pages", "v_pages", "k_scales",
                                                            "v_scales"), device_types="cuda")
@@ -127,3 +167,17 @@ def decode(plan_id: int, q, k_pages, v_pages, page_table, kv_len, sm_scale, k_sc
         raise ValueError("pass both out and lse, or neither")
     return torch.ops.skvd.decode_v1(q, k_pages, v_pages, page_table, kv_len, k_scales, v_scales,
                                     float(sm_scale), int(q_per_seq), int(plan_id))
+
+
+def prefill(plan_id: int, q, k_pages, v_pages, page_table, kv_len, sm_scale, k_scales=None,
+            v_scales=None, q_per_seq=1, out=None, lse=None):
+    """Convenience dispatch: ``prefill_out_v1`` when out and lse are given, else ``prefill_v1``."""
+    if out is not None and lse is not None:
+        torch.ops.skvd.prefill_out_v1(q, k_pages, v_pages, page_table, kv_len, k_scales,
+                                      v_scales, float(sm_scale), int(q_per_seq), int(plan_id),
+                                      out, lse)
+        return out, lse
+    if out is not None or lse is not None:
+        raise ValueError("pass both out and lse, or neither")
+    return torch.ops.skvd.prefill_v1(q, k_pages, v_pages, page_table, kv_len, k_scales,
+                                     v_scales, float(sm_scale), int(q_per_seq), int(plan_id))

@@ -1,6 +1,6 @@
 """The torch operators' declarations, checked without a GPU: what each op's schema marks as
 written, and what torch's functionalization (the pass torch.compile and torch.export run) makes
-of a decode over cache views -- one half of a [2, pages, ...] tensor, one slot of an
+of a decode (and of the multi-token route) over cache views -- one half of a [2, pages, ...] tensor, one slot of an
 interleaved [pages, 2, ...] tensor, one layer of a multi-layer pool
 (AMD-Ecosystem/flashinfer PR #397, "What changed" and "Test plan"). The graphs are traced
 with meta tensors through the ops' fake implementations; nothing runs. A planted wrong
@@ -21,6 +21,8 @@ def _mutable(schema):
 def test_schemas_declare_only_real_outputs():
     assert _mutable(torch.ops.skvd.decode_v1.default._schema) == []
     assert _mutable(torch.ops.skvd.decode_out_v1.default._schema) == ["lse", "out"]
+    assert _mutable(torch.ops.skvd.prefill_v1.default._schema) == []
+    assert _mutable(torch.ops.skvd.prefill_out_v1.default._schema) == ["lse", "out"]
     # the append really writes the cache and says so
     assert _mutable(torch.ops.skvd.append_v1.default._schema) == [
         "k_pages", "k_scales", "v_pages", "v_scales"]
@@ -42,9 +44,9 @@ def _views(layout, pages=40, P=16, Hkv=8, D=128, dtype=torch.float16):
 
 
 class _Decode(torch.nn.Module):
-    def __init__(self, layout, with_out):
+    def __init__(self, layout, with_out, route="decode"):
         super().__init__()
-        self.layout, self.with_out = layout, with_out
+        self.layout, self.with_out, self.route = layout, with_out, route
 
     def forward(self, q, base, table, kv_len, out, lse):
         if self.layout == "two_halves":
@@ -53,10 +55,14 @@ class _Decode(torch.nn.Module):
             k, v = base[:, 0], base[:, 1]
         else:
             k, v = base[1, 0], base[1, 1]
+        T = 1 if self.route == "decode" else 2
         if self.with_out:
-            torch.ops.skvd.decode_out_v1(q, k, v, table, kv_len, None, None, 0.1, 1, 1, out, lse)
+            op = torch.ops.skvd.decode_out_v1 if self.route == "decode" else \
+                torch.ops.skvd.prefill_out_v1
+            op(q, k, v, table, kv_len, None, None, 0.1, T, 1, out, lse)
             return out.sum(), lse.sum()
-        return torch.ops.skvd.decode_v1(q, k, v, table, kv_len, None, None, 0.1, 1, 1)
+        op = torch.ops.skvd.decode_v1 if self.route == "decode" else torch.ops.skvd.prefill_v1
+        return op(q, k, v, table, kv_len, None, None, 0.1, T, 1)
 
 
 def _inputs(layout):
@@ -74,10 +80,11 @@ def _functional_graph(mod, args):
     return ep, ep.graph_signature.user_inputs_to_mutate
 
 
+@pytest.mark.parametrize("route", ["decode", "prefill"])
 @pytest.mark.parametrize("with_out", [False, True])
 @pytest.mark.parametrize("layout", ["two_halves", "interleaved", "layer_of_pool"])
-def test_functionalized_decode_writes_no_cache(layout, with_out):
-    ep, mutated = _functional_graph(_Decode(layout, with_out), _inputs(layout))
+def test_functionalized_decode_writes_no_cache(layout, with_out, route):
+    ep, mutated = _functional_graph(_Decode(layout, with_out, route), _inputs(layout))
     assert "base" not in mutated.values(), (layout, mutated)
     assert set(mutated.values()) == ({"out", "lse"} if with_out else set()), mutated
     # no copy of anything back into the cache's base
