@@ -50,6 +50,23 @@ __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
+// Inclusive prefix sum over the 64 lanes on DPP, no LDS: shifts right by 1, 2, 4 and 8 within
+// each 16-lane row (lanes shifted in from outside the row add 0), then lane 15's total into
+// rows 1 and 3 and lane 31's into rows 2 and 3 (the row broadcasts).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ unsigned dpp_u(unsigned x) {
+  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROWS, 0xF, false);
+}
+__device__ __forceinline__ unsigned wave_inclusive_sum(unsigned x) {
+  x += dpp_u<0x111, 0xF>(x);  // row_shr:1
+  x += dpp_u<0x112, 0xF>(x);  // row_shr:2
+  x += dpp_u<0x114, 0xF>(x);  // row_shr:4
+  x += dpp_u<0x118, 0xF>(x);  // row_shr:8
+  x += dpp_u<0x142, 0xA>(x);  // row_bcast:15 into rows 1, 3
+  x += dpp_u<0x143, 0xC>(x);  // row_bcast:31 into rows 2, 3
+  return x;
+}
+
 // max / sum over the 16 lanes of a DPP row (xor 1, xor 2, half-mirror, mirror)
 __device__ __forceinline__ float row16_max(float x) {
   x = fmaxf(x, dpp<0xB1>(x));
@@ -82,6 +99,22 @@ __device__ __forceinline__ float readlane_f(float x, int lane) {
 }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Lane-swap sums (gfx950 v_permlane32_swap / v_permlane16_swap, which trade the upper 32
+// lanes of their first operand with the lower 32 of the second, and the odd 16-lane rows of the
+// first with the even rows of the second). swap_sum32: lanes 0..31 get a(l) + a(l + 32), lanes
+// 32..63 get b(l - 32) + b(l). swap_sum16: rows 0 and 2 (lanes / 16) get a(l) + a(l ^ 16),
+// rows 1 and 3 get b(l ^ 16) + b(l). Vector ALU only, no LDS.
+__device__ __forceinline__ float swap_sum32(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap_sum16(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // LDS hand-off between the lanes of a one-wave workgroup: a wavefront-scope fence and wave
 // barrier order the LDS accesses without waiting on outstanding global loads.
 __device__ __forceinline__ void wave_sync() {
@@ -105,7 +138,7 @@ struct Shares {
   int len_l;         // seqs_per_lane == 1: the clamped length of the lane's sequence
   unsigned nb_l;     // blocks of the lane's sequences
   unsigned pre_l;    // blocks of all earlier lanes' sequences
-  int64_t n_blocks;  // N = schedule heads * sum of block counts
+  int64_t n_blocks;  // N = schedule heads * sum of block counts (below 2^31)
   int n_shares;      // W = min(grid, N / piece_min), at least 1 when N > 0
 };
 
@@ -122,18 +155,15 @@ __device__ __forceinline__ Shares balanced_shares(const LaunchArgs &a, int debug
     nb += (unsigned)(L + 63) >> 6;
   }
   sh.nb_l = nb;
-  unsigned inc = nb;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const unsigned up = __shfl_up(inc, d);
-    if (lane >= d) inc += up;
-  }
+  const unsigned inc = wave_inclusive_sum(nb);
   sh.pre_l = inc - nb;
-  // (readlane: the total is wave-uniform, so it and everything derived from it stay scalar)
-  sh.n_blocks = (int64_t)(unsigned)__builtin_amdgcn_readlane((int)inc, 63) * a.sched_heads;
-  sh.n_shares = sh.n_blocks == 0
-                    ? 0
-                    : (int)max((int64_t)1, min((int64_t)a.grid_wgs, sh.n_blocks / a.piece_min));
+  // (readlane: the total is wave-uniform, so it and everything derived from it stay scalar;
+  // the plan keeps N below 2^31, so 32-bit arithmetic: a 64-bit division is a long scalar
+  // sequence on the launch's critical path)
+  const unsigned n = (unsigned)__builtin_amdgcn_readlane((int)inc, 63) * (unsigned)a.sched_heads;
+  const unsigned pieces = a.piece_min == 1 ? n : n / (unsigned)a.piece_min;
+  sh.n_blocks = n;
+  sh.n_shares = n == 0 ? 0 : (int)max(1u, min((unsigned)a.grid_wgs, pieces));
   return sh;
 }
 

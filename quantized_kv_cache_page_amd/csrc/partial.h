@@ -303,6 +303,11 @@ constexpr int partial_waves() {
 template <int D, int RB, int KV, bool FAST, int CH, bool PVM, int HW, int RT, bool DBG>
 __global__ __launch_bounds__(64 * HW * RT)
 __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void partial_kernel(LaunchArgs a) {
+  // The argument block's first two 64-byte lines (pointers and strides of q and the pools,
+  // the page table) come in with the first batch of argument loads: left to the compiler,
+  // they are loaded after the share arithmetic, one more memory round trip on the launch's
+  // critical path.
+  asm volatile("" ::"s"(a.q), "s"(a.table));
   constexpr bool I8 = KV != 0;  // elements of at most one byte
   constexpr bool SC = KV == 1 || KV == 3;  // int8, q4_0: f16 scales per 32 elements of a row
   constexpr bool F8 = KV == 2;  // fp8 E4M3: one f32 scale per tensor
@@ -390,7 +395,7 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
   // row). Sequence lengths, one per lane, come from kv_len on the device.
   int st_b = 0, st_grp = 0, st_split = 0;
   Shares sh{};
-  int64_t x_cur = 0, x_end = 0;  // balanced: this workgroup's share
+  int x_cur = 0, x_end = 0;  // balanced: this workgroup's share (blocks below 2^31)
   // Progress priority (int8, whose waves share SIMDs): waves of a SIMD are served oldest
   // first, so a co-resident workgroup started later falls behind and finishes alone, with fewer
   // loads in flight. Each wave instead sets its issue priority from the fraction of its work
@@ -402,8 +407,11 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
   if (a.balanced) {
     sh = balanced_shares(a, a.debug);
     if (share >= sh.n_shares) return;
-    x_cur = share * sh.n_blocks / sh.n_shares;
-    x_end = (share + 1) * sh.n_blocks / sh.n_shares;
+    // floor(w N / W) = w q + floor(w r / W) with N = q W + r: 32-bit (N < 2^31, W^2 < 2^30)
+    const unsigned N = (unsigned)sh.n_blocks, W = (unsigned)sh.n_shares;
+    const unsigned q = N / W, r = N - q * W;
+    x_cur = (int)(share * q + (share * r) / W);
+    x_end = (int)((share + 1) * q + ((share + 1) * r) / W);
     const int total = (int)(x_end - x_cur);
     pq1 = total / 4;
     pq2 = total / 2;
@@ -423,18 +431,18 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
     if (x_cur >= x_end) break;
     // the sequence holding global block x_cur: Hg*pre <= x_cur < Hg*(pre + nb), that is
     // pre <= x_cur / Hg < pre + nb (one scalar division, 32-bit lane compares)
-    const unsigned xq = (unsigned)(x_cur / Hg);
+    const unsigned xq = (unsigned)x_cur / (unsigned)Hg;
     const SeqRef sr = seq_at(a, sh, xq);
     b = sr.b;
     const unsigned pre_b = sr.pre;
     const int nb_b = sr.nb;
     L = sr.L;
-    const int64_t off = x_cur - (int64_t)Hg * pre_b;
-    grp = (int)(off / nb_b);
-    blk_lo = (int)(off - (int64_t)grp * nb_b);
-    const int64_t row0 = (int64_t)Hg * pre_b + (int64_t)grp * nb_b;  // the row's first block
-    const int64_t seg_end = min(x_end, row0 + nb_b);
-    blk_hi = blk_lo + (int)(seg_end - x_cur);
+    const unsigned off = (unsigned)x_cur - (unsigned)Hg * pre_b;
+    grp = (int)(off / (unsigned)nb_b);
+    blk_lo = (int)(off - (unsigned)grp * (unsigned)nb_b);
+    const int row0 = (int)((unsigned)Hg * pre_b + (unsigned)grp * (unsigned)nb_b);  // row's 1st block
+    const int seg_end = min(x_end, row0 + nb_b);
+    blk_hi = blk_lo + (seg_end - x_cur);
     // compact slot of (schedule row b*Hg + grp, share): unique, below rows + shares
     slot = b * Hg + grp + share;
     x_cur = seg_end;
@@ -741,14 +749,17 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
   // One chunk: scores of the chunk's K (loaded one step ahead), prefetch of the next K,
   // softmax, P.V with the chunk's V, prefetch of the next V. The first call is peeled off the
   // loop so that the loop is entered with the same load order as its back edge (K before V):
-  // the in-order load counter is then waited on for K alone at the loop top.
-  auto chunk = [&](int c0) __attribute__((always_inline)) {
+  // the in-order load counter is then waited on for K alone at the loop top. A last call with
+  // more = false prefetches nothing: loads of a chunk past the segment are waited on before the
+  // epilogue reuses their registers, an HBM round trip (about 1.5 us) at the end of a segment.
+  auto chunk = [&](int c0, auto more) __attribute__((always_inline)) {
+    constexpr bool PF = decltype(more)::value;
     const int c1 = c0 + CH;
     if constexpr (SCL) {  // this chunk's K and V scales to LDS (the previous chunk's reads of
       vsc_lds[lane] = scr;  // them ended at its closing wave_sync)
       wave_sync();
     }
-    if constexpr (FAST) chunk_pages(c1, pg_next);
+    if constexpr (FAST && PF) chunk_pages(c1, pg_next);
     // ---- scores: S[t] = rows x 16 tokens of tile t (lane: token c16, rows 4*g4 + e)
     // The MFMA chains run for every tile, also the ones past the split (their K is a clamped
     // re-read and their scores are masked): a branch between an MFMA and the reads of its
@@ -841,8 +852,8 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
     }
     __builtin_amdgcn_sched_barrier(0);
     // ---- prefetch the next chunk's K while this chunk's softmax and P.V run (past the end
-    // of the split this re-reads the last token: cached, and never used)
-    load_k(c1, pg_next);
+    // of the split, in a partial last chunk, this re-reads the last token: never used)
+    if constexpr (PF) load_k(c1, pg_next);
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- mask, online softmax (base 2)
@@ -1060,10 +1071,12 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
     }
     __builtin_amdgcn_sched_barrier(0);
     // ---- prefetch the next chunk's V while the next chunk's scores run
-    load_v(c1, pg_next);
+    if constexpr (PF) load_v(c1, pg_next);
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (PF) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) pg_cur[t] = pg_next[t];
+      for (int t = 0; t < NT; ++t) pg_cur[t] = pg_next[t];
+    }
     wave_sync();
   };
   auto set_priority = [&](int c0) __attribute__((always_inline)) {
@@ -1074,12 +1087,29 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
     else if (done < pq3) __builtin_amdgcn_s_setprio(1);
     else __builtin_amdgcn_s_setprio(0);
   };
+  // The last chunk peeled off (a third copy of the chunk's code) where registers allow: at
+  // D = 128, and for f16 at D = 256; elsewhere it would add spills.
+  constexpr bool PEEL = D == 128 || (D == 256 && !I8);
   if (tok0 < tok_end) {
-    set_priority(tok0);
-    chunk(tok0);
-    for (int c0 = tok0 + CH; c0 < tok_end; c0 += CH) {
+    int c0 = tok0;
+    if constexpr (PEEL) {
+      if (c0 + CH < tok_end) {
+        set_priority(c0);
+        chunk(c0, std::true_type{});
+        for (c0 += CH; c0 + CH < tok_end; c0 += CH) {
+          set_priority(c0);
+          chunk(c0, std::true_type{});
+        }
+      }
       set_priority(c0);
-      chunk(c0);
+      chunk(c0, std::false_type{});
+    } else {
+      set_priority(c0);
+      chunk(c0, std::true_type{});
+      for (c0 += CH; c0 < tok_end; c0 += CH) {
+        set_priority(c0);
+        chunk(c0, std::true_type{});
+      }
     }
   }
   done_base += blk_hi - blk_lo;
@@ -1125,48 +1155,50 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<D, RB, KV != 0>()))) void parti
       }
     }
   } else {
-    // ---- sum the load slots: lanes l, l ^ LPR, ... hold the same head_dim elements
+    // ---- sum the four load slots (lanes l, l ^ 16, l ^ 32, l ^ 48 hold the same head_dim
+    // elements of every row) as a reduce-scatter on the lane swaps: the first step leaves rows
+    // 0 and 1 in lanes 0..31 and rows 2 and 3 in lanes 32..63, the second row g = lane / 16 in
+    // lane group g (24 swaps and adds, where a butterfly per value took 64 LDS shuffles)
+    static_assert(LPR == 16 && RM == 4, "the vector P.V holds four rows at head_dim 128");
+    float w[2][8], u[8];
 #pragma unroll
-    for (int r = 0; r < RM; ++r)
+    for (int r = 0; r < 2; ++r)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float x = accv[r][i];
+      for (int i = 0; i < 8; ++i) w[r][i] = swap_sum32(accv[r][i], accv[r + 2][i]);
 #pragma unroll
-        for (int sh = LPR; sh < 64; sh <<= 1) x += __shfl_xor(x, sh);
-        accv[r][i] = x;
-      }
+    for (int i = 0; i < 8; ++i) u[i] = swap_sum16(w[0][i], w[1][i]);
+    const int g = lane >> 4;  // this lane group's row
     float mr[RM], lr[RM];
 #pragma unroll
     for (int r = 0; r < RM; ++r) {
-      mr[r] = readlane_f(m[r & 3], 16 * (r >> 2));
-      lr[r] = readlane_f(lsum[r & 3], 16 * (r >> 2));
+      mr[r] = readlane_f(m[r], 0);
+      lr[r] = readlane_f(lsum[r], 0);
     }
-#pragma unroll
-    for (int r = 0; r < RM; ++r) {
-      if (lane >= LPR || r >= R) continue;
-      const int t = r / G, hg = r - (r / G) * G;
+    const float mg = g == 0 ? mr[0] : g == 1 ? mr[1] : g == 2 ? mr[2] : mr[3];
+    const float lg = g == 0 ? lr[0] : g == 1 ? lr[1] : g == 2 ? lr[2] : lr[3];
+    if (g < R) {
+      const int t = g / G, hg = g - t * G;
       const int64_t row = ((int64_t)b * T + t) * Hq + kvh * G + hg;
       if (a.single) {
-        const float l = lr[r];
-        const float inv = (l > 0.f ? 1.f / l : 0.f) * vfac;
+        const float inv = (lg > 0.f ? 1.f / lg : 0.f) * vfac;
         half8 out;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) out[i] = (_Float16)(accv[r][i] * inv);
+        for (int i = 0; i < 8; ++i) out[i] = (_Float16)(u[i] * inv);
         if constexpr (Q4) {
           *(half4 *)((_Float16 *)a.o + row * D + vq0) = half4{out[0], out[1], out[2], out[3]};
           *(half4 *)((_Float16 *)a.o + row * D + vq1) = half4{out[4], out[5], out[6], out[7]};
         } else {
           *(half8 *)((_Float16 *)a.o + row * D + vlane_el) = out;
         }
-        if (a.lse && lane == 0) a.lse[row] = l > 0.f ? (mr[r] + __log2f(l)) * kLn2 : kNegInf;
+        if (a.lse && (lane & 15) == 0) a.lse[row] = lg > 0.f ? (mg + __log2f(lg)) * kLn2 : kNegInf;
       } else {
         float *dst = a.ws_o + part_index(row, hg + G * t) * D;
-        *(float4v *)(dst + vq0) = float4v{accv[r][0], accv[r][1], accv[r][2], accv[r][3]} * vfac;
-        *(float4v *)(dst + vq1) = float4v{accv[r][4], accv[r][5], accv[r][6], accv[r][7]} * vfac;
-        if (lane == 0) {
+        *(float4v *)(dst + vq0) = float4v{u[0], u[1], u[2], u[3]} * vfac;
+        *(float4v *)(dst + vq1) = float4v{u[4], u[5], u[6], u[7]} * vfac;
+        if ((lane & 15) == 0) {
           float *ml = a.ws_ml + part_index(row, hg + G * t) * 2;
-          ml[0] = mr[r];
-          ml[1] = lr[r];
+          ml[0] = mg;
+          ml[1] = lg;
         }
       }
     }

@@ -167,13 +167,18 @@ skvd_status make_plan(const skvd_plan_params &prm, int num_cus, Plan *out, char 
   // one per (schedule row, share) pair that meet — at most rows + shares — so the workspace does
   // not grow with the context and shares can be as small as one block.
   int sched = prm.schedule;
+  // (the device cuts the shares in 32-bit arithmetic: the batch's blocks times the schedule
+  // heads below 2^31, and the grid's square below 2^30, num_cus <= 512 at 64 per CU)
   const bool can_balance = p.splits_cap > 1 && prm.max_batch <= kBalancedMaxBatch &&
-                           prm.force_reducer != SKVD_REDUCER_NONE;
+                           prm.force_reducer != SKVD_REDUCER_NONE &&
+                           (int64_t)prm.max_batch * p.sched_heads * p.max_blocks < INT32_MAX &&
+                           num_cus <= 512;
   if (sched == SKVD_SCHEDULE_AUTO)
     sched = can_balance ? SKVD_SCHEDULE_BALANCED : SKVD_SCHEDULE_STATIC;
   if (sched == SKVD_SCHEDULE_BALANCED && !can_balance)
     return fail(err, errn, SKVD_ERR_PLAN, "balanced schedule needs more than one split, "
-                "max_batch <= %d and a reducer (plan: %d splits, max_batch %d)",
+                "max_batch <= %d, a reducer, max_batch x schedule heads x blocks < 2^31 and "
+                "num_cus <= 512 (plan: %d splits, max_batch %d)",
                 kBalancedMaxBatch, p.splits_cap, prm.max_batch);
   p.schedule = sched;
   if (sched == SKVD_SCHEDULE_BALANCED) {
