@@ -215,9 +215,13 @@ __device__ __forceinline__ SeqRef seq_info(const LaunchArgs &a, const Shares &sh
   return walk_lane(a, l, pre, 0u, b);
 }
 
-// The share holding global block x (0 <= x < N): the largest w with floor(w N / W) <= x.
+// The share holding global block x (0 <= x < N): the largest w with floor(w N / W) <= x, that
+// is floor(((x + 1) W - 1) / N). In double, exactly: the numerator (below 2^46) and N are
+// exact, the division is correctly rounded, and a quotient that is not an integer lies at least
+// 1/N > 2^-31 below the next integer, far beyond the rounding error at quotients up to W <= 2^15
+// (a 64-bit integer division is a long scalar sequence).
 __device__ __forceinline__ int share_of(int64_t x, int64_t n_blocks, int n_shares) {
-  return (int)(((x + 1) * n_shares - 1) / n_blocks);
+  return (int)__builtin_floor(((double)(x + 1) * (double)n_shares - 1.0) / (double)n_blocks);
 }
 
 }  // namespace skvd
