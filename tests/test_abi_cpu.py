@@ -157,6 +157,15 @@ def test_heuristic_configs():
         assert i.blocks_per_split * 64 * i.splits_cap >= p.params.max_kv_len
 
 
+def test_balanced_limits_fall_back_to_static():
+    """Where the balanced schedule's 32-bit share arithmetic would not hold, the automatic
+    choice is the static schedule; just inside the limits it stays balanced."""
+    assert plan(max_batch=1024, max_kv_len=1 << 27).schedule == "static"
+    assert plan(num_cus=600).schedule == "static"
+    assert plan(max_batch=1024, max_kv_len=1 << 21).schedule == "balanced"  # 2^26 blocks
+    assert plan(num_cus=512).schedule == "balanced"
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=64), 2), (dict(num_qo_heads=30), 2), (dict(page_size=24), 2),
     (dict(max_q_per_seq=9), 2), (dict(max_q_per_seq=1, num_qo_heads=2048, num_kv_heads=1), 2),
@@ -165,6 +174,10 @@ def test_heuristic_configs():
     (dict(force_reducer="none", max_kv_len=4096), 7),
     (dict(schedule="balanced", max_batch=1025), 7), (dict(schedule="balanced", max_kv_len=128), 7),
     (dict(schedule="balanced", force_reducer="none", max_kv_len=200), 7),
+    # the device cuts balanced shares in 32-bit arithmetic: blocks x schedule heads x max_batch
+    # below 2^31 (here 1024 x 2 x 2^21), and the grid's square below 2^30 (num_cus <= 512)
+    (dict(schedule="balanced", max_batch=1024, max_kv_len=1 << 27), 7),
+    (dict(schedule="balanced", num_cus=600), 7),
     (dict(schedule=3), 7), (dict(wgs_per_cu=65), 7), (dict(wgs_per_cu=-1), 7),
     (dict(heads_per_wg=2, max_q_per_seq=2), 7), (dict(kv_dtype="i8", heads_per_wg=3), 7),
     (dict(kv_dtype="i8", heads_per_wg=8, num_kv_heads=4, num_qo_heads=16), 7), (dict(kv_dtype="i8", heads_per_wg=4, num_kv_heads=2,
