@@ -10,6 +10,8 @@
 // Loop bounds come from kv_len on the device; the partial stride is the plan's capacity.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "device_common.h"
 
 namespace skvd {
@@ -122,8 +124,13 @@ __device__ __forceinline__ void load_slice(const float *p, float (&v)[PER]) {
 
 // Cooperative step: up to 64 partials (indices first, first + stride, ...) one per lane of this
 // wave. Each lane's (m, l) gives the wave max and sum; the lanes then walk the partials' output
-// slices (PER elements per lane), eight loads in flight, each weight broadcast from the lane
-// that owns the partial.
+// slices (PER elements per lane) in rounds of U loads, each weight broadcast from the lane that
+// owns the partial: U = 8 for up to 8 partials, else 64 / PER (a wave's 32 partials of a long
+// single sequence at head_dim 128 in one round trip instead of four). The loads are
+// unconditional (an index past the count re-reads the last partial, weighted 0): conditional
+// ones became a branch around each load. Slices are addressed from the first one's row (a
+// uniform base) with 32-bit byte offsets: consecutive partials are at most HW * RPG rows apart
+// (128), so 63 steps stay below 2^25 bytes.
 template <int D>
 __device__ __forceinline__ void merge_lanes(const float *ml, const float *po, int64_t first,
                                             int64_t stride, int cnt, MergeAcc<D / 64> *out) {
@@ -135,25 +142,31 @@ __device__ __forceinline__ void merge_lanes(const float *ml, const float *po, in
   const float M = wave_max(mlv[0]);
   const float w = M == kNegInf ? 0.f : part_weight(mlv[0], M);
   const float S = wave_sum(w * mlv[1]);
+  const char *base = (const char *)(po + first * D);
+  const unsigned step = (unsigned)stride * (unsigned)(D * 4);
+  const unsigned lane_off = (unsigned)(PER * 4 * lane);
   float acc[PER] = {};
-  for (int k0 = 0; k0 < cnt; k0 += 8) {
-    float ov[8][PER];
+  auto rounds = [&](auto uc) __attribute__((always_inline)) {
+    constexpr int U = decltype(uc)::value;
+    for (int k0 = 0; k0 < cnt; k0 += U) {
+      float ov[U][PER];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (k0 + j < cnt) {
-        load_slice<PER>(po + (first + stride * (k0 + j)) * D + PER * lane, ov[j]);
-      } else {
+      for (int j = 0; j < U; ++j) {
+        const unsigned jj = (unsigned)min(k0 + j, cnt - 1);
+        load_slice<PER>((const float *)(base + (lane_off + jj * step)), ov[j]);
+      }
 #pragma unroll
-        for (int i = 0; i < PER; ++i) ov[j][i] = 0.f;
+      for (int j = 0; j < U; ++j) {
+        const float wj = k0 + j < cnt ? readlane_f(w, k0 + j) : 0.f;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) acc[i] = fmaf(wj, ov[j][i], acc[i]);
       }
     }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float wj = k0 + j < cnt ? readlane_f(w, k0 + j) : 0.f;
-#pragma unroll
-      for (int i = 0; i < PER; ++i) acc[i] = fmaf(wj, ov[j][i], acc[i]);
-    }
-  }
+  };
+  if (cnt > 8)
+    rounds(std::integral_constant<int, 64 / PER>{});
+  else
+    rounds(std::integral_constant<int, 8>{});
   out->fold(M, S, acc);
 }
 
