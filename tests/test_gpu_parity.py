@@ -163,6 +163,19 @@ def test_forced_reducers_and_splits(kv, red, bps, schedule):
                                   schedule=schedule))
 
 
+@pytest.mark.parametrize("schedule", ["auto", "static"])
+@pytest.mark.parametrize("red", ["cooperative", "multipass", "hierarchical"])
+@pytest.mark.parametrize("D", [192, 256, 512])
+def test_forced_reducers_wide_heads(D, red, schedule):
+    """The merge's rounds of output-slice loads at every head_dim (64 / PER per round for more
+    than 8 partials: 21, 16 and 8 loads), one block per split so that rows carry from 3 to
+    beyond 64 partials (cooperative: up to 63), under both schedules."""
+    lens = (130, 1100, 4000) if red == "cooperative" else (130, 1100, 5000)
+    s = spec(name=f"wide{D}", batch=3, q_per_seq=1, num_qo_heads=8, num_kv_heads=2, head_dim=D,
+             page_size=16, lens=("list", lens))
+    check(s, seed=D, plan_kw=dict(force_reducer=red, force_blocks_per_split=1, schedule=schedule))
+
+
 @pytest.mark.parametrize("L", [2047, 2048, 2049, 4095, 4096, 4097])
 def test_2048_4096_boundaries(L):
     """Partial counts 32/33/64/65 around the pages' cooperative ceiling, at one block per
