@@ -129,8 +129,8 @@ __device__ __forceinline__ void load_slice(const float *p, float (&v)[PER]) {
 // single sequence at head_dim 128 in one round trip instead of four). The loads are
 // unconditional (an index past the count re-reads the last partial, weighted 0): conditional
 // ones became a branch around each load. Slices are addressed from the first one's row (a
-// uniform base) with 32-bit byte offsets: consecutive partials are at most HW * RPG rows apart
-// (128), so 63 steps stay below 2^25 bytes.
+// uniform base) with 32-bit byte offsets: consecutive partials are at most HW * RPG (128) rows
+// apart, times the multipass waves' NW (4), so 63 steps of D floats stay below 2^26 bytes.
 template <int D>
 __device__ __forceinline__ void merge_lanes(const float *ml, const float *po, int64_t first,
                                             int64_t stride, int cnt, MergeAcc<D / 64> *out) {
