@@ -120,14 +120,17 @@ typedef enum {
 
 /* How the partial kernel's workgroups divide the batch's 64-token blocks. */
 typedef enum {
-  SKVD_SCHEDULE_AUTO = 0,     /* balanced when the plan splits and max_batch <= 1024, else static */
+  SKVD_SCHEDULE_AUTO = 0,     /* balanced where it is allowed (below), else static */
   SKVD_SCHEDULE_STATIC = 1,   /* one workgroup per (split of blocks_per_split blocks, KV head,
                                  sequence); splits past a sequence's length exit at once */
   SKVD_SCHEDULE_BALANCED = 2  /* the launch's blocks, in (sequence, KV head, block) order, cut
                                  on the device into W equal contiguous shares, W = min(grid,
                                  blocks / blocks_per_split); a share may cover parts of several
                                  (sequence, KV head) rows and writes one partial per part.
-                                 Needs max_batch <= 1024 and more than one split. */
+                                 Needs max_batch <= 1024, more than one split, a reducer,
+                                 max_batch * schedule heads * blocks per sequence < 2^31 and
+                                 num_cus <= 512 (the device cuts the shares in 32-bit
+                                 arithmetic). */
 } skvd_schedule;
 
 /* Static shape of a plan. All sizes are upper bounds of what skvd_decode may be given. */
@@ -153,8 +156,9 @@ typedef struct {
   int32_t wgs_per_cu;     /* balanced schedule: workgroups launched per compute unit (0: at
                              head_dim 128 with G*T <= 4, f16 max(1, 4 / heads_per_wg) and the
                              one-byte formats max(1, 12 / heads_per_wg); other head_dims, f16 3
-                             and one-byte 4; 4 for more query rows at head_dim 128; divided by
-                             the row tiles of a workgroup) */
+                             and one-byte 8 (head_dim 192, 256) or 4 (512); 4 for more query
+                             rows at head_dim 128; divided by the row tiles of a workgroup);
+                             1..64 */
   int32_t heads_per_wg;   /* KV heads one partial-kernel workgroup serves, one wave each
                              (0 at head_dim 128 with G*T <= 4: 4, else 2, else 1 -- whichever
                              divides Hkv --, where the waves of a CU read each token's rows of
