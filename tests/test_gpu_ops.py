@@ -14,8 +14,8 @@ only reads is copied on a graph replay).
   pool, for the decode and the multi-token route: outputs equal the eager call bit for bit,
   every cache tensor is bit-identical afterwards, and the graph copies nothing into any cache
   tensor.
-* The compiled decode captured in a CUDA graph and replayed with eager work in between:
-  bit-identical replays, caches untouched.
+* The compiled decode and multi-token route captured in a CUDA graph and replayed with eager
+  work in between: bit-identical replays, caches untouched.
 * skvd::append_v1 under torch.compile writes what the eager append writes; an append of half
   the new rows before each route and of the other half after it, in one compiled graph (over
   separate caches, and over views of one tensor with dynamic shapes), gives what the same
@@ -186,9 +186,11 @@ def test_compile_over_cache_views(kv, layout, with_out, route):
     ops.unregister_plan(pid)
 
 
-def test_compiled_decode_in_cuda_graph():
+@pytest.mark.parametrize("route", ["decode", "prefill"])
+def test_compiled_decode_in_cuda_graph(route):
     from quantized_kv_cache_page_amd import ops
-    prob = _problem("i8", seed=9)
+    _, op_out, T = _route_ops(route)
+    prob = _problem("i8", T=T, seed=9)
     dev = to_dev(prob)
     base, k, v, ks, vs = _layout(dev, "layer_of_pool")
     plan = make_plan(prob)
@@ -198,8 +200,7 @@ def test_compiled_decode_in_cuda_graph():
     lse = torch.empty(dev["q"].shape[:2], dtype=torch.float32, device="cuda")
 
     def fn():
-        torch.ops.skvd.decode_out_v1(dev["q"], k, v, dev["page_table"], dev["kv_len"], ks, vs,
-                                     sm, 1, pid, out, lse)
+        op_out(dev["q"], k, v, dev["page_table"], dev["kv_len"], ks, vs, sm, T, pid, out, lse)
 
     cfn = torch.compile(fn, backend="aot_eager", fullgraph=True)
     s = torch.cuda.Stream()
@@ -221,10 +222,11 @@ def test_compiled_decode_in_cuda_graph():
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), eo.view(torch.int16)), f"replay {i}"
         assert torch.equal(lse, el)
-        plan.run(dev["q"], k, v, dev["page_table"], dev["kv_len"], sm, ks, vs)  # eager work
+        plan.run(dev["q"], k, v, dev["page_table"], dev["kv_len"], sm, ks, vs,
+                 q_per_seq=T)  # eager work
     assert torch.equal(base.view(torch.uint8), before.view(torch.uint8))
     ro, rl = oracle.decode(prob)
-    compare(out, lse, ro, rl, what="graph-replayed compiled decode")
+    compare(out, lse, ro, rl, what=f"graph-replayed compiled {route}")
     ops.unregister_plan(pid)
 
 
